@@ -1,0 +1,343 @@
+// C ABI of the SOCKET decode library: host-side validation, workspace
+// layout and kernel sequencing. Declarations and contracts are in
+// include/socket_lsh.h.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kernels.hpp"
+#include "socket_lsh.h"
+
+namespace {
+
+using namespace socket_lsh;
+
+thread_local std::string g_last_error;
+
+socket_status fail(socket_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+socket_status ok() {
+  g_last_error.clear();
+  return SOCKET_OK;
+}
+
+socket_status from_hip(hipError_t err, const char* what) {
+  if (err == hipSuccess) return ok();
+  return fail(SOCKET_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+constexpr size_t kMaxTableBytes = 160 * 1024;  // LDS of one gfx950 CU
+
+bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+socket_status check_dtype(socket_dtype dt) {
+  if (dt != SOCKET_DTYPE_F32 && dt != SOCKET_DTYPE_BF16)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dt);
+  return SOCKET_OK;
+}
+
+socket_status check_d(int32_t d) {
+  if (d <= 0) return fail(SOCKET_ERR_INVALID_ARGUMENT, "d must be > 0 (got %d)", d);
+  if (d != 64 && d != 128)
+    return fail(SOCKET_ERR_UNSUPPORTED, "d=%d is not supported (64 or 128)", d);
+  return SOCKET_OK;
+}
+
+socket_status check_lp(int32_t L, int32_t P) {
+  if (L < 1) return fail(SOCKET_ERR_INVALID_ARGUMENT, "L must be >= 1 (got %d)", L);
+  if (P < 1 || P > 8)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "P must be in [1, 8] (got %d)", P);
+  if ((int64_t)L * P > 1024)
+    return fail(SOCKET_ERR_UNSUPPORTED, "L*P=%lld exceeds 1024 hyperplanes",
+                (long long)L * P);
+  return SOCKET_OK;
+}
+
+socket_status check_heads(int32_t B, int32_t Hq, int32_t Hkv) {
+  if (B < 1 || Hq < 1 || Hkv < 1)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "B, Hq, Hkv must be >= 1 (got %d, %d, %d)",
+                B, Hq, Hkv);
+  if (Hq % Hkv != 0)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(SOCKET_ERR_UNSUPPORTED, "GQA group size %d is not supported (1, 2, 4, 8)", G);
+  return SOCKET_OK;
+}
+
+socket_status check_table(int32_t L, int32_t P, int32_t G) {
+  const size_t bytes = ((size_t)1 << P) * L * G * sizeof(float);
+  if (bytes > kMaxTableBytes)
+    return fail(SOCKET_ERR_UNSUPPORTED,
+                "probability table of one KV head (%zu bytes = 2^P*L*G*4) exceeds the "
+                "%zu bytes of LDS", bytes, kMaxTableBytes);
+  return SOCKET_OK;
+}
+
+#define SOCKET_TRY(expr)                 \
+  do {                                   \
+    socket_status _st = (expr);          \
+    if (_st != SOCKET_OK) return _st;    \
+  } while (0)
+
+struct DecodeLayout {
+  size_t table_off, scores_off, idx_off, topk_off, attn_off, total;
+  TopkPlan topk;
+  AttnPlan attn;
+};
+
+DecodeLayout decode_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                           int64_t n_keys, int32_t L, int32_t P, int64_t k) {
+  DecodeLayout lay{};
+  const int rows = B * Hq;
+  const int64_t kk = k < n_keys ? k : n_keys;
+  size_t off = 0;
+  lay.table_off = off;
+  off = align256(off + ((size_t)1 << P) * L * Hq * B * sizeof(float));
+  lay.scores_off = off;
+  off = align256(off + (size_t)rows * n_keys * sizeof(float));
+  lay.idx_off = off;
+  off = align256(off + (size_t)rows * kk * sizeof(int32_t));
+  lay.topk = plan_topk(rows, n_keys, k);
+  lay.topk_off = off;
+  off = align256(off + lay.topk.total_bytes);
+  lay.attn = plan_attn(B, Hq, Hkv, d, kk);
+  lay.attn_off = off;
+  off = align256(off + lay.attn.partial_bytes);
+  lay.total = off;
+  return lay;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t socket_version(void) { return (0 << 16) | (1 << 8) | 0; }
+
+const char* socket_status_string(socket_status status) {
+  switch (status) {
+    case SOCKET_OK: return "ok";
+    case SOCKET_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SOCKET_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SOCKET_ERR_WORKSPACE: return "workspace missing or too small";
+    case SOCKET_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* socket_last_error(void) { return g_last_error.c_str(); }
+
+socket_status socket_hash_keys(const void* K, const void* V, const void* R,
+                               socket_dtype dtype, int64_t n_heads,
+                               int64_t n_keys, int64_t head_stride_rows,
+                               int32_t d, int32_t L, int32_t P, uint8_t* ids,
+                               float* vnorm, void* stream) {
+  SOCKET_TRY(check_dtype(dtype));
+  SOCKET_TRY(check_d(d));
+  SOCKET_TRY(check_lp(L, P));
+  if (n_heads < 0 || n_keys < 0)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "n_heads and n_keys must be >= 0");
+  if (head_stride_rows < n_keys)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT,
+                "head_stride_rows (%lld) < n_keys (%lld)", (long long)head_stride_rows,
+                (long long)n_keys);
+  if (dtype == SOCKET_DTYPE_BF16 && (int64_t)L * P > 512)
+    return fail(SOCKET_ERR_UNSUPPORTED,
+                "bf16 hashing supports L*P <= 512 hyperplanes (got %lld)",
+                (long long)L * P);
+  if (n_heads == 0 || n_keys == 0) return ok();
+  if (!K || !V || !R || !ids || !vnorm)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (!aligned16(K) || !aligned16(V))
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "K and V must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (dtype == SOCKET_DTYPE_BF16)
+    err = launch_hash_keys_bf16((const uint16_t*)K, (const uint16_t*)V,
+                                (const uint16_t*)R, n_heads, n_keys,
+                                head_stride_rows, d, L, P, ids, vnorm, s);
+  else
+    err = launch_hash_keys_f32((const float*)K, (const float*)V,
+                               (const float*)R, n_heads, n_keys,
+                               head_stride_rows, d, L, P, ids, vnorm, s);
+  return from_hip(err, "socket_hash_keys launch");
+}
+
+socket_status socket_bucket_probs(const void* Q, const void* R,
+                                  socket_dtype dtype, int32_t B, int32_t Hq,
+                                  int32_t Hkv, int32_t d, int32_t L,
+                                  int32_t P, float tau, float* table,
+                                  void* stream) {
+  SOCKET_TRY(check_dtype(dtype));
+  SOCKET_TRY(check_heads(B, Hq, Hkv));
+  SOCKET_TRY(check_d(d));
+  SOCKET_TRY(check_lp(L, P));
+  if (!(std::isfinite(tau) && tau > 0.f))
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "tau must be finite and > 0");
+  if (!Q || !R || !table)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "null pointer argument");
+  hipError_t err = launch_bucket_probs(Q, R, dtype == SOCKET_DTYPE_BF16, B, Hq,
+                                       Hkv, d, L, P, tau, table, nullptr, 0,
+                                       static_cast<hipStream_t>(stream));
+  return from_hip(err, "socket_bucket_probs launch");
+}
+
+socket_status socket_score(const float* table, const uint8_t* ids,
+                           const float* vnorm, int32_t B, int32_t Hq,
+                           int32_t Hkv, int64_t n_keys,
+                           int64_t head_stride_rows, int32_t L, int32_t P,
+                           float* scores, void* stream) {
+  SOCKET_TRY(check_heads(B, Hq, Hkv));
+  SOCKET_TRY(check_lp(L, P));
+  SOCKET_TRY(check_table(L, P, Hq / Hkv));
+  if (n_keys < 0 || head_stride_rows < n_keys)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "need 0 <= n_keys <= head_stride_rows");
+  if (n_keys == 0) return ok();
+  if (!table || !ids || !vnorm || !scores)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (!aligned16(table))
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "table must be 16-byte aligned");
+  hipError_t err = launch_score(table, ids, vnorm, B, Hq, Hkv, n_keys,
+                                head_stride_rows, L, P, scores, nullptr,
+                                static_cast<hipStream_t>(stream));
+  return from_hip(err, "socket_score launch");
+}
+
+size_t socket_topk_workspace_bytes(int32_t rows, int64_t n, int64_t k) {
+  if (rows < 1 || n < 1 || k < 1) return 0;
+  return plan_topk(rows, n, k).total_bytes;
+}
+
+socket_status socket_topk(const float* scores, int32_t rows, int64_t n,
+                          int64_t k, int32_t* idx, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (rows < 0 || n < 0)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "rows and n must be >= 0");
+  if (k < 1) return fail(SOCKET_ERR_INVALID_ARGUMENT, "k must be >= 1");
+  if (n >= ((int64_t)1 << 31))
+    return fail(SOCKET_ERR_UNSUPPORTED, "n must be < 2^31 (int32 indices)");
+  if (rows == 0 || n == 0) return ok();
+  if (!scores || !idx)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "null pointer argument");
+  const TopkPlan plan = plan_topk(rows, n, k);
+  if (plan.kk < n && (!workspace || workspace_bytes < plan.total_bytes))
+    return fail(SOCKET_ERR_WORKSPACE, "top-k needs %zu workspace bytes, got %zu",
+                plan.total_bytes, workspace ? workspace_bytes : (size_t)0);
+  hipError_t err = launch_topk(scores, plan, idx, workspace, false,
+                               static_cast<hipStream_t>(stream));
+  return from_hip(err, "socket_topk launch");
+}
+
+size_t socket_sparse_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t d,
+                                          int64_t kk) {
+  if (B < 1 || Hq < 1 || d < 1 || kk < 1) return 0;
+  return plan_attn(B, Hq, Hq, d, kk).partial_bytes;
+}
+
+socket_status socket_sparse_attn(const void* Q, const void* K, const void* V,
+                                 socket_dtype dtype, int32_t B, int32_t Hq,
+                                 int32_t Hkv, int32_t d,
+                                 int64_t head_stride_rows, const int32_t* idx,
+                                 int64_t kk, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  SOCKET_TRY(check_dtype(dtype));
+  SOCKET_TRY(check_heads(B, Hq, Hkv));
+  SOCKET_TRY(check_d(d));
+  if (kk < 1) return fail(SOCKET_ERR_INVALID_ARGUMENT, "kk must be >= 1");
+  if (head_stride_rows < 1)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "head_stride_rows must be >= 1");
+  if (head_stride_rows >= ((int64_t)1 << 31))
+    return fail(SOCKET_ERR_UNSUPPORTED, "head_stride_rows must be < 2^31");
+  if (!Q || !K || !V || !idx || !out)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V))
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "Q, K and V must be 16-byte aligned");
+  const AttnPlan plan = plan_attn(B, Hq, Hkv, d, kk);
+  if (!workspace || workspace_bytes < plan.partial_bytes)
+    return fail(SOCKET_ERR_WORKSPACE, "attention needs %zu workspace bytes, got %zu",
+                plan.partial_bytes, workspace ? workspace_bytes : (size_t)0);
+  hipError_t err = launch_sparse_attn(Q, K, V, dtype == SOCKET_DTYPE_BF16, plan,
+                                      head_stride_rows, idx, out,
+                                      static_cast<float*>(workspace),
+                                      static_cast<hipStream_t>(stream));
+  return from_hip(err, "socket_sparse_attn launch");
+}
+
+size_t socket_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv,
+                                     int32_t d, int64_t n_keys, int32_t L,
+                                     int32_t P, int64_t k) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || d < 1 || n_keys < 1 || L < 1 || P < 1 ||
+      P > 8 || k < 1)
+    return 0;
+  return decode_layout(B, Hq, Hkv, d, n_keys, L, P, k).total;
+}
+
+socket_status socket_decode(const void* Q, const void* K, const void* V,
+                            const void* R, const uint8_t* ids,
+                            const float* vnorm, socket_dtype dtype, int32_t B,
+                            int32_t Hq, int32_t Hkv, int32_t d,
+                            int64_t n_keys, int64_t head_stride_rows,
+                            int32_t L, int32_t P, float tau, int64_t k,
+                            void* out, int32_t* idx_out, float* scores_out,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  SOCKET_TRY(check_dtype(dtype));
+  SOCKET_TRY(check_heads(B, Hq, Hkv));
+  SOCKET_TRY(check_d(d));
+  SOCKET_TRY(check_lp(L, P));
+  SOCKET_TRY(check_table(L, P, Hq / Hkv));
+  if (!(std::isfinite(tau) && tau > 0.f))
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "tau must be finite and > 0");
+  if (k < 1) return fail(SOCKET_ERR_INVALID_ARGUMENT, "k must be >= 1");
+  if (n_keys < 1) return fail(SOCKET_ERR_INVALID_ARGUMENT, "n_keys must be >= 1");
+  if (head_stride_rows < n_keys)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "head_stride_rows (%lld) < n_keys (%lld)",
+                (long long)head_stride_rows, (long long)n_keys);
+  if (head_stride_rows >= ((int64_t)1 << 31))
+    return fail(SOCKET_ERR_UNSUPPORTED, "head_stride_rows must be < 2^31");
+  if (!Q || !K || !V || !R || !ids || !vnorm || !out)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V))
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "Q, K and V must be 16-byte aligned");
+  const DecodeLayout lay = decode_layout(B, Hq, Hkv, d, n_keys, L, P, k);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(SOCKET_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu",
+                lay.total, workspace ? workspace_bytes : (size_t)0);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  float* table = reinterpret_cast<float*>(ws + lay.table_off);
+  float* scores = scores_out ? scores_out : reinterpret_cast<float*>(ws + lay.scores_off);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + lay.idx_off);
+  unsigned char* tws = ws + lay.topk_off;
+  float* partial = reinterpret_cast<float*>(ws + lay.attn_off);
+  const bool bf16 = dtype == SOCKET_DTYPE_BF16;
+
+  hipError_t err = launch_bucket_probs(Q, R, bf16, B, Hq, Hkv, d, L, P, tau,
+                                       table, nullptr, 0, s);
+  if (err != hipSuccess) return from_hip(err, "socket_decode: bucket_probs");
+  err = launch_score(table, ids, vnorm, B, Hq, Hkv, n_keys, head_stride_rows,
+                     L, P, scores, nullptr, s);
+  if (err != hipSuccess) return from_hip(err, "socket_decode: score");
+  err = launch_topk(scores, lay.topk, idx, tws, false, s);
+  if (err != hipSuccess) return from_hip(err, "socket_decode: topk");
+  err = launch_sparse_attn(Q, K, V, bf16, lay.attn, head_stride_rows, idx, out,
+                           partial, s);
+  return from_hip(err, "socket_decode: sparse_attn");
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Host-side launchers of the SOCKET kernels. Every launcher assumes its
+// arguments were validated by the C-ABI layer and enqueues on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace socket_lsh {
+
+// ------------------------------------------------------------- prefill hash
+hipError_t launch_hash_keys_bf16(const uint16_t* K, const uint16_t* V,
+                                 const uint16_t* R, int64_t n_heads,
+                                 int64_t n_keys, int64_t stride, int d, int L,
+                                 int P, uint8_t* ids, float* vnorm,
+                                 hipStream_t stream);
+hipError_t launch_hash_keys_f32(const float* K, const float* V, const float* R,
+                                int64_t n_heads, int64_t n_keys,
+                                int64_t stride, int d, int L, int P,
+                                uint8_t* ids, float* vnorm,
+                                hipStream_t stream);
+
+// ------------------------------------------------------ soft bucket table
+// zero_ptr/zero_words: optional device words cleared by the same launch.
+hipError_t launch_bucket_probs(const void* Q, const void* R, bool bf16, int B,
+                               int Hq, int Hkv, int d, int L, int P,
+                               float tau, float* table, uint32_t* zero_ptr,
+                               int64_t zero_words, hipStream_t stream);
+
+// ------------------------------------------------------------------ score
+// hist (optional): [B*Hq, 2048] first-digit histograms, accumulated with
+// atomics; must be zero on entry.
+hipError_t launch_score(const float* table, const uint8_t* ids,
+                        const float* vnorm, int B, int Hq, int Hkv,
+                        int64_t n_keys, int64_t stride, int L, int P,
+                        float* scores, uint32_t* hist, hipStream_t stream);
+
+// ------------------------------------------------------------------ top-k
+struct TopkPlan {
+  int rows;
+  int64_t n, kk;
+  int segs;
+  int64_t seg_len;
+  size_t hist_off, cnt_off, list_off, total_bytes;
+};
+TopkPlan plan_topk(int rows, int64_t n, int64_t k);
+constexpr int kHistBins = 2048;
+hipError_t launch_zero_u32(uint32_t* p, int64_t words, hipStream_t stream);
+// hist_ready: the histogram region of ws already holds the first-digit
+// histogram (filled by the score kernel); otherwise it is built here.
+hipError_t launch_topk(const float* scores, const TopkPlan& plan,
+                       int32_t* idx, void* ws, bool hist_ready,
+                       hipStream_t stream);
+
+// ------------------------------------------------------- sparse attention
+struct AttnPlan {
+  int B, Hq, Hkv, d;
+  int64_t kk;
+  int keys_per_wave, chunk_keys, chunks;
+  size_t partial_bytes;
+};
+AttnPlan plan_attn(int B, int Hq, int Hkv, int d, int64_t kk);
+hipError_t launch_sparse_attn(const void* Q, const void* K, const void* V,
+                              bool bf16, const AttnPlan& plan, int64_t stride,
+                              const int32_t* idx, void* out, float* partial,
+                              hipStream_t stream);
+
+}  // namespace socket_lsh

@@ -1,0 +1,272 @@
+// Exact softmax attention over the selected keys.
+//
+// Last part of step 4 of the soft-LSH mechanism of SOCKET (page "Resumen
+// Técnico: SOCKET - Estimador de Núcleo de Colisión Suave para Atención
+// Escasa", section "Mecanismo Central: LSH Suave", item 4; German page
+// "SOCKET: SOft Collision Kernel EsTimator for Sparse Attention",
+// Kernmechanismus, Auswahl): exact attention is computed over the selected
+// subset only.
+//
+// Split-k flash decoding: each block takes one query row (b, h) and a chunk
+// of its selected keys; each of its 4 waves gathers KPW key rows and the
+// matching value rows with 16-byte loads (one row per LPR lanes, all loads
+// of a wave issued before the first use), computes the scaled dot products,
+// a wave-local softmax (max m, sum l) and the weighted value sum, and the
+// block merges its 4 waves in LDS into one (m, l, acc[d]) partial. A second
+// kernel merges the chunk partials of a row in chunk order (the online
+// softmax merge) and writes the output in the input dtype. Everything runs
+// in float32 in a fixed order, so results are reproducible run to run.
+//
+// Blocks are dealt to the 8 XCDs round-robin; the mapping below keeps all
+// query heads of one KV head on one XCD and issues the G heads of a chunk
+// back to back, so keys chosen by several heads of a group are likely to be
+// served from that XCD's L2.
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+#include <algorithm>
+
+namespace socket_lsh {
+namespace {
+
+constexpr int kAttnThreads = 256;
+constexpr int kAttnWaves = kAttnThreads / 64;
+
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4& w, float* f);
+template <>
+__device__ __forceinline__ void unpack16<BF16>(const uint4& w, float* f) {
+  unpack8_bf16(w, f);
+}
+template <>
+__device__ __forceinline__ void unpack16<F32>(const uint4& w, float* f) {
+  unpack4_f32(w, f);
+}
+
+template <typename T, int D, int KPW>
+__global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
+    const typename T::storage* __restrict__ Q,
+    const typename T::storage* __restrict__ K,
+    const typename T::storage* __restrict__ V, int Hq, int Hkv, int bhkv,
+    int64_t stride, const int32_t* __restrict__ idx, int64_t kk, int chunks,
+    float* __restrict__ partial) {
+  constexpr int EPL = 16 / T::bytes;  // elements per 16-byte load
+  constexpr int LPR = D / EPL;        // lanes per key row
+  constexpr int KPI = 64 / LPR;       // key rows per wave-wide load
+  constexpr int IT = KPW / KPI;       // loads per wave per tensor
+  constexpr int CHUNK = KPW * kAttnWaves;
+  __shared__ float sm_m[kAttnWaves], sm_l[kAttnWaves];
+  __shared__ float sm_acc[kAttnWaves][D];
+
+  const int G = Hq / Hkv;
+  const int per_group = G * chunks;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int gi = xcd + 8 * (slot / per_group);
+  if (gi >= bhkv) return;
+  const int local = slot % per_group;
+  const int chunk = local / G, j = local % G;
+  const int b = gi / Hkv, g = gi % Hkv;
+  const int h = g * G + j;
+  const int64_t row = (int64_t)b * Hq + h;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = lane / LPR, sub = lane % LPR;
+  const float scale = 1.0f / sqrtf((float)D);
+
+  float qf[EPL];
+  {
+    const uint4 w = *reinterpret_cast<const uint4*>(Q + row * D + sub * EPL);
+    unpack16<T>(w, qf);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[e] *= scale;
+  }
+
+  const int64_t kbeg = (int64_t)chunk * CHUNK + wave * KPW;
+  const typename T::storage* Kh = K + (int64_t)gi * stride * D;
+  const typename T::storage* Vh = V + (int64_t)gi * stride * D;
+  const int32_t* irow = idx + row * kk;
+
+  int key[IT];
+  bool valid[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int64_t p = kbeg + it * KPI + grp;
+    valid[it] = p < kk;
+    // indices outside [0, stride) are clamped so no load leaves the head
+    key[it] = valid[it] ? (int)min<int64_t>(max(irow[p], 0), stride - 1) : 0;
+  }
+  uint4 kr[IT], vr[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it)
+    kr[it] = valid[it] ? *reinterpret_cast<const uint4*>(
+                             Kh + (int64_t)key[it] * D + sub * EPL)
+                       : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int it = 0; it < IT; ++it)
+    vr[it] = valid[it] ? *reinterpret_cast<const uint4*>(
+                             Vh + (int64_t)key[it] * D + sub * EPL)
+                       : make_uint4(0, 0, 0, 0);
+
+  float s[IT];
+  float m = -INFINITY;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    float f[EPL];
+    unpack16<T>(kr[it], f);
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], f[e], dot);
+    dot = group_sum<LPR>(dot);
+    s[it] = valid[it] ? dot : -INFINITY;
+    m = fmaxf(m, s[it]);
+  }
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+
+  float l = 0.f;
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const float p = valid[it] ? __expf(s[it] - m) : 0.f;
+    l += p;
+    float f[EPL];
+    unpack16<T>(vr[it], f);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, f[e], acc[e]);
+  }
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1) {
+    l += __shfl_xor(l, o, kWave);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
+  }
+  if (lane == 0) {
+    sm_m[wave] = m;
+    sm_l[wave] = l;
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) sm_acc[wave][sub * EPL + e] = acc[e];
+  }
+  __syncthreads();
+
+  float* out = partial + (row * chunks + chunk) * (D + 2);
+  for (int t = threadIdx.x; t < D; t += kAttnThreads) {
+    float mt = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) mt = fmaxf(mt, sm_m[w]);
+    float lt = 0.f, at = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float c = sm_m[w] == -INFINITY ? 0.f : expf(sm_m[w] - mt);
+      lt = fmaf(c, sm_l[w], lt);
+      at = fmaf(c, sm_acc[w][t], at);
+    }
+    out[t] = at;
+    if (t == 0) {
+      out[D] = mt;
+      out[D + 1] = lt;
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(D) void attn_merge_kernel(
+    const float* __restrict__ partial, int chunks,
+    typename T::storage* __restrict__ out) {
+  const int64_t row = blockIdx.x;
+  const float* p = partial + row * chunks * (D + 2);
+  const int t = threadIdx.x;
+  float mt = -INFINITY;
+  for (int c = 0; c < chunks; ++c) mt = fmaxf(mt, p[c * (D + 2) + D]);
+  float lt = 0.f, at = 0.f;
+  for (int c = 0; c < chunks; ++c) {
+    const float mc = p[c * (D + 2) + D];
+    const float w = mc == -INFINITY ? 0.f : expf(mc - mt);
+    lt = fmaf(w, p[c * (D + 2) + D + 1], lt);
+    at = fmaf(w, p[c * (D + 2) + t], at);
+  }
+  T::store(out, row * D + t, at / lt);
+}
+
+template <typename T, int D, int KPW>
+hipError_t launch_attn_t(const void* Q, const void* K, const void* V,
+                         const AttnPlan& plan, int64_t stride,
+                         const int32_t* idx, void* out, float* partial,
+                         hipStream_t stream) {
+  using S = typename T::storage;
+  const int G = plan.Hq / plan.Hkv;
+  const int bhkv = plan.B * plan.Hkv;
+  const int per_group = G * plan.chunks;
+  const int grid = ((bhkv + 7) / 8) * 8 * per_group;
+  hipLaunchKernelGGL((sparse_attn_kernel<T, D, KPW>), dim3(grid),
+                     dim3(kAttnThreads), 0, stream, (const S*)Q, (const S*)K,
+                     (const S*)V, plan.Hq, plan.Hkv, bhkv, stride, idx,
+                     plan.kk, plan.chunks, partial);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3(plan.B * plan.Hq),
+                     dim3(D), 0, stream, partial, plan.chunks, (S*)out);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_attn_d(const void* Q, const void* K, const void* V,
+                         const AttnPlan& plan, int64_t stride,
+                         const int32_t* idx, void* out, float* partial,
+                         hipStream_t stream) {
+  switch (plan.keys_per_wave) {
+    case 64:
+      return launch_attn_t<T, D, 64>(Q, K, V, plan, stride, idx, out, partial, stream);
+    case 32:
+      return launch_attn_t<T, D, 32>(Q, K, V, plan, stride, idx, out, partial, stream);
+    default:
+      return launch_attn_t<T, D, 16>(Q, K, V, plan, stride, idx, out, partial, stream);
+  }
+}
+
+}  // namespace
+
+AttnPlan plan_attn(int B, int Hq, int Hkv, int d, int64_t kk) {
+  AttnPlan p{};
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.d = d;
+  p.kk = kk;
+  const int64_t rows = (int64_t)B * Hq;
+  int kpw = 16;
+  for (int cand : {64, 32}) {
+    const int64_t chunks = (kk + cand * kAttnWaves - 1) / (cand * kAttnWaves);
+    if (rows * chunks >= 1024) {
+      kpw = cand;
+      break;
+    }
+  }
+  p.keys_per_wave = kpw;
+  p.chunk_keys = kpw * kAttnWaves;
+  p.chunks = (int)((kk + p.chunk_keys - 1) / p.chunk_keys);
+  if (p.chunks < 1) p.chunks = 1;
+  p.partial_bytes = (size_t)rows * p.chunks * (d + 2) * sizeof(float);
+  return p;
+}
+
+hipError_t launch_sparse_attn(const void* Q, const void* K, const void* V,
+                              bool bf16, const AttnPlan& plan, int64_t stride,
+                              const int32_t* idx, void* out, float* partial,
+                              hipStream_t stream) {
+  if (plan.B == 0 || plan.Hq == 0) return hipSuccess;
+  if (bf16) {
+    if (plan.d == 128)
+      return launch_attn_d<BF16, 128>(Q, K, V, plan, stride, idx, out, partial, stream);
+    return launch_attn_d<BF16, 64>(Q, K, V, plan, stride, idx, out, partial, stream);
+  }
+  if (plan.d == 128)
+    return launch_attn_d<F32, 128>(Q, K, V, plan, stride, idx, out, partial, stream);
+  return launch_attn_d<F32, 64>(Q, K, V, plan, stride, idx, out, partial, stream);
+}
+
+}  // namespace socket_lsh

@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/socket_lsh.h, and rejects invalid arguments on the host
+before anything is enqueued (fake non-null pointers are never dereferenced
+because validation fails first)."""
+
+import os
+import re
+
+import pytest
+
+from soft_lsh_sparse_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x1000  # 16-byte aligned, never dereferenced (validation fails first)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "socket_lsh.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(socket_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported_and_typed(lib):
+    names = _declared_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"{name} has no ctypes signature"
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.socket_version() == (0 << 16) | (1 << 8) | 0
+    for st in range(5):
+        assert lib.socket_status_string(st)
+    assert lib.socket_status_string(99) == b"unknown status"
+
+
+def _decode(lib, **over):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, R=FAKE, ids=FAKE, vnorm=FAKE, dt=1, B=1,
+             Hq=32, Hkv=8, d=128, n=1024, stride=1024, L=32, P=8, tau=0.3,
+             k=64, out=FAKE, idx=None, scores=None, ws=FAKE, ws_bytes=0)
+    a.update(over)
+    return lib.socket_decode(a["Q"], a["K"], a["V"], a["R"], a["ids"], a["vnorm"],
+                             a["dt"], a["B"], a["Hq"], a["Hkv"], a["d"], a["n"],
+                             a["stride"], a["L"], a["P"], a["tau"], a["k"],
+                             a["out"], a["idx"], a["scores"], a["ws"],
+                             a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dt=7), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(Hq=30), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(Hq=48, Hkv=8), _lib.SOCKET_ERR_UNSUPPORTED),       # G = 6
+    (dict(d=96), _lib.SOCKET_ERR_UNSUPPORTED),
+    (dict(d=0), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(P=0), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(P=9), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(L=0), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(L=200, P=8), _lib.SOCKET_ERR_UNSUPPORTED),         # L*P > 1024
+    (dict(L=64, P=8), _lib.SOCKET_ERR_UNSUPPORTED),          # 256 KB table
+    (dict(tau=0.0), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(tau=-1.0), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(tau=float("inf")), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(tau=float("nan")), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(k=0), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(n=0), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(stride=100), _lib.SOCKET_ERR_INVALID_ARGUMENT),    # stride < n
+    (dict(Q=None), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(ids=None), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(out=None), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(K=FAKE + 2), _lib.SOCKET_ERR_INVALID_ARGUMENT),    # misaligned
+    (dict(ws=None), _lib.SOCKET_ERR_WORKSPACE),
+    (dict(ws_bytes=1000), _lib.SOCKET_ERR_WORKSPACE),
+])
+def test_decode_rejects_bad_arguments(lib, over, status):
+    assert _decode(lib, **over) == status
+    assert lib.socket_last_error()
+
+
+def test_hash_keys_validation(lib):
+    f = lib.socket_hash_keys
+    ok_args = [FAKE, FAKE, FAKE, 1, 8, 1024, 1024, 128, 64, 8, FAKE, FAKE, None]
+    bad = list(ok_args); bad[7] = 80
+    assert f(*bad) == _lib.SOCKET_ERR_UNSUPPORTED
+    bad = list(ok_args); bad[9] = 9
+    assert f(*bad) == _lib.SOCKET_ERR_INVALID_ARGUMENT
+    bad = list(ok_args); bad[8] = 128          # L*P = 1024 > 512 for bf16
+    assert f(*bad) == _lib.SOCKET_ERR_UNSUPPORTED
+    bad = list(ok_args); bad[6] = 10           # stride < n_keys
+    assert f(*bad) == _lib.SOCKET_ERR_INVALID_ARGUMENT
+    bad = list(ok_args); bad[10] = None
+    assert f(*bad) == _lib.SOCKET_ERR_INVALID_ARGUMENT
+    bad = list(ok_args); bad[0] = FAKE + 4
+    assert f(*bad) == _lib.SOCKET_ERR_INVALID_ARGUMENT
+    # nothing to hash: OK without touching any pointer or the GPU
+    empty = list(ok_args); empty[5] = 0
+    assert f(*empty) == _lib.SOCKET_OK
+    empty = [None, None, None, 1, 0, 5, 5, 128, 64, 8, None, None, None]
+    assert f(*empty) == _lib.SOCKET_OK
+
+
+def test_stage_validation(lib):
+    assert lib.socket_bucket_probs(FAKE, FAKE, 1, 1, 32, 8, 128, 32, 8, 0.0,
+                                   FAKE, None) == _lib.SOCKET_ERR_INVALID_ARGUMENT
+    assert lib.socket_score(FAKE, FAKE, FAKE, 1, 32, 8, 10, 5, 32, 8, FAKE,
+                            None) == _lib.SOCKET_ERR_INVALID_ARGUMENT
+    assert lib.socket_topk(FAKE, 4, 100, 0, FAKE, FAKE, 1 << 30,
+                           None) == _lib.SOCKET_ERR_INVALID_ARGUMENT
+    assert lib.socket_topk(FAKE, 4, 100, 10, FAKE, None, 0,
+                           None) == _lib.SOCKET_ERR_WORKSPACE
+    assert lib.socket_topk(None, 0, 100, 10, None, None, 0, None) == _lib.SOCKET_OK
+    assert lib.socket_sparse_attn(FAKE, FAKE, FAKE, 1, 1, 32, 8, 128, 1024, FAKE,
+                                  0, FAKE, FAKE, 1 << 30,
+                                  None) == _lib.SOCKET_ERR_INVALID_ARGUMENT
+    assert lib.socket_sparse_attn(FAKE, FAKE, FAKE, 1, 1, 32, 8, 128, 1024, FAKE,
+                                  16, FAKE, FAKE, 4,
+                                  None) == _lib.SOCKET_ERR_WORKSPACE
+
+
+def test_workspace_sizes_are_sane(lib):
+    # 128K-key decode, batch 4, 32/8 heads, L=32, P=8, k=4096
+    ws = lib.socket_decode_workspace_bytes(4, 32, 8, 128, 131072, 32, 8, 4096)
+    rows, n = 4 * 32, 131072
+    assert ws >= rows * n * 4          # scores
+    assert ws < 512 * 1024 * 1024
+    assert lib.socket_decode_workspace_bytes(0, 32, 8, 128, 1, 32, 8, 1) == 0
+    assert lib.socket_topk_workspace_bytes(128, 131072, 4096) >= 128 * 2048 * 4
+    assert lib.socket_sparse_attn_workspace_bytes(4, 32, 128, 4096) >= 4 * 32 * 130 * 4

@@ -1,0 +1,429 @@
+"""GPU parity: every HIP stage and the whole decode path against the CPU oracle.
+
+Gates (tolerances follow from the arithmetic of each step):
+  * bucket ids and selected index sets: bit-exact;
+  * value norms: 1e-5 relative;
+  * soft probabilities: 1e-6 relative (float32 rounding of float64 values)
+    plus an absolute floor of 1e-37 for float32 underflow;
+  * scores: 1e-5 relative plus an absolute floor of 1e-30 (float32 scores of
+    keys whose probabilities underflow where float64 keeps tiny values);
+  * top-k: bit-exact against the oracle's selection on the GPU's own scores;
+    against the oracle's float64 scores, differences are allowed only for
+    keys whose score lies within the score tolerance of the k-th score;
+  * attention output: 2e-2 absolute for bf16 (output rounding), 1e-4 for
+    float32, with the oracle attending over the GPU's selection.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import soft_lsh_sparse_amd as S
+import synthetic as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def f64(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def tau32(tau):
+    return float(np.float32(tau))
+
+
+def assert_close_rel(got, ref, rel, floor, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref)
+    lim = rel * np.abs(ref) + floor
+    bad = err > lim
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(
+            f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; first at "
+            f"{tuple(i)}: got {got[tuple(i)]!r} ref {ref[tuple(i)]!r}")
+
+
+def table_to_oracle_layout(table, G):
+    """[B, Hkv, 2^P, L, G] -> [B, Hq, L, 2^P]."""
+    B, Hkv, nb, L, _ = table.shape
+    t = table.permute(0, 1, 4, 3, 2).reshape(B, Hkv * G, L, nb)
+    return f64(t)
+
+
+# --------------------------------------------------------------------- hash
+
+HASH_CASES = [
+    # (n_heads, N, stride, d, L, P, dtype)
+    (1, 1024, 1024, 64, 8, 4, "f32"),
+    (2, 1000, 1000, 128, 32, 8, "bf16"),
+    (3, 77, 80, 64, 16, 4, "bf16"),
+    (1, 33, 33, 128, 64, 6, "bf16"),
+    (2, 513, 513, 128, 7, 3, "bf16"),
+    (1, 1, 1, 128, 64, 8, "bf16"),
+    (2, 300, 310, 128, 11, 8, "f32"),
+    (1, 500, 500, 128, 8, 1, "bf16"),
+    (1, 257, 257, 64, 40, 5, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", HASH_CASES)
+def test_hash_keys_bit_exact(case):
+    n_heads, N, stride, d, L, P, dt = case
+    log(f"hash case {case}")
+    w = W.custom_workload(B=1, Hq=n_heads, Hkv=n_heads, d=d, N=stride, dtype=dt, L=L, P=P)
+    K, V = W.make_keys_values(w, DEV, seed=11)
+    R = W.make_hyperplanes(w, DEV, seed=11)
+    K, V = K[0], V[0]
+    ids, vn = S.hash_keys(K, V, R, L, P, n_keys=N)
+    torch.cuda.synchronize()
+    ref_ids = O.hash_keys(f64(K[:, :N]), f64(R), L, P)
+    ref_vn = O.value_norms(f64(V[:, :N]))
+    got = ids[:, :N].cpu().numpy()
+    assert np.array_equal(got, ref_ids), f"{int((got != ref_ids).sum())} ids differ"
+    assert_close_rel(vn[:, :N].cpu().numpy(), ref_vn, 1e-5, 0.0, "vnorm")
+
+
+def test_hash_near_zero_projections_are_exact():
+    """Keys built so that some projections are exactly 0 or cancel far below
+    float32 resolution: the certified-sign fix-up must get every bit right."""
+    log("hash near-zero")
+    d, L, P = 128, 16, 8
+    g = torch.Generator().manual_seed(5)
+    R = torch.randn(d, L * P, generator=g).to(torch.bfloat16)
+    R[0:3, :] = 1.0
+    Rf = R.float()
+    rows = []
+    for c in range(L * P):
+        # exact zero: k_i = r_jc, k_j = -r_ic on two rows with nonzero r
+        k = torch.zeros(d)
+        i, j = 5 + (c % 50), 60 + (c % 60)
+        k[i], k[j] = Rf[j, c], -Rf[i, c]
+        rows.append(k)
+    for s in (1.0, -1.0):
+        # big + small - big along rows 0..2 (R = 1 there): exact sign of small
+        k = torch.randn(d, generator=g) * 1e-3
+        k[0], k[1], k[2] = 2.0 ** 20, s * 2.0 ** -10, -(2.0 ** 20)
+        k[3:] = 0.0
+        rows.append(k)
+    rows.append(torch.zeros(d))
+    K = torch.stack(rows)[None].to(torch.bfloat16)
+    n = K.shape[1]
+    K = K.to(DEV).contiguous()
+    V = torch.randn(1, n, d, generator=g).to(torch.bfloat16).to(DEV)
+    R = R.to(DEV).contiguous()
+    ids, _ = S.hash_keys(K, V, R, L, P)
+    torch.cuda.synchronize()
+    ref = O.hash_keys(f64(K), f64(R), L, P)
+    assert np.array_equal(ids.cpu().numpy(), ref)
+    bits = O.hash_bits(f64(K), f64(R))
+    assert bits[0, L * P].all() and not bits[0, L * P + 1].any()
+
+
+def test_hash_append_with_row_offset():
+    log("hash append")
+    w = W.custom_workload(B=1, Hq=2, Hkv=2, d=128, N=700, dtype="bf16", L=32, P=8)
+    K, V = W.make_keys_values(w, DEV, seed=3)
+    R = W.make_hyperplanes(w, DEV, seed=3)
+    K, V = K[0], V[0]
+    full_ids, full_vn = S.hash_keys(K, V, R, 32, 8)
+    ids = torch.zeros_like(full_ids)
+    vn = torch.zeros_like(full_vn)
+    S.hash_keys(K, V, R, 32, 8, n_keys=500, ids=ids, vnorm=vn)
+    S.hash_keys(K, V, R, 32, 8, n_keys=1, ids=ids, vnorm=vn, row_offset=500)
+    S.hash_keys(K, V, R, 32, 8, ids=ids, vnorm=vn, row_offset=501)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, full_ids)
+    assert torch.equal(vn, full_vn)
+
+
+def test_hash_prefill_128k_sampled():
+    """Full 8 x 131072 x 128 prefill (64 tables of 8 bits); ids checked
+    bit-exactly on a seeded sample of 12288 keys, norms on the same keys."""
+    w = W.WORKLOADS["prefill_hash_128k"]
+    log(f"hash {w.name}")
+    K, V = W.make_keys_values(w, DEV, seed=0)
+    R = W.make_hyperplanes(w, DEV, seed=0)
+    K, V = K[0], V[0]
+    ids, vn = S.hash_keys(K, V, R, w.L, w.P)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    heads = rng.integers(0, w.Hkv, 12288)
+    rows = rng.integers(0, w.N, 12288)
+    rows[:64] = np.arange(64)                 # first tile
+    rows[64:128] = w.N - 1 - np.arange(64)    # last tile
+    hi = torch.from_numpy(heads).to(DEV)
+    ri = torch.from_numpy(rows).to(DEV)
+    Ks = f64(K[hi, ri])
+    ref = O.hash_keys(Ks, f64(R), w.L, w.P)
+    got = ids[hi, ri].cpu().numpy()
+    assert np.array_equal(got, ref), f"{int((got != ref).sum())} ids differ"
+    assert_close_rel(vn[hi, ri].cpu().numpy(), O.value_norms(f64(V[hi, ri])), 1e-5, 0.0,
+                     "vnorm")
+
+
+# ----------------------------------------------------------- bucket probs
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,L,P,tau,dt", [
+    (1, 1, 1, 64, 8, 4, 0.5, "f32"),
+    (2, 8, 2, 128, 32, 8, 0.3, "bf16"),
+    (1, 32, 8, 128, 64, 6, 0.2, "bf16"),
+    (1, 4, 4, 64, 5, 1, 0.05, "bf16"),
+    (3, 16, 2, 128, 9, 7, 2.0, "f32"),
+])
+def test_bucket_probs(B, Hq, Hkv, d, L, P, tau, dt):
+    log(f"bucket_probs {(B, Hq, Hkv, d, L, P, tau, dt)}")
+    w = W.custom_workload(B=B, Hq=Hq, Hkv=Hkv, d=d, N=8, dtype=dt, L=L, P=P, tau=tau)
+    Q = W.make_query(w, DEV, seed=2)
+    R = W.make_hyperplanes(w, DEV, seed=2)
+    table = S.bucket_probs(Q, R, Hkv, L, P, tau)
+    torch.cuda.synchronize()
+    got = table_to_oracle_layout(table, Hq // Hkv)
+    ref = O.soft_bucket_probs(f64(Q), f64(R), L, P, tau32(tau))
+    assert_close_rel(got, ref, 1e-6, 1e-37, "probs")
+    assert np.allclose(got.sum(-1), 1.0, atol=1e-5, rtol=0)
+
+
+# ------------------------------------------------------------------ score
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,L,P", [
+    (1, 1, 1, 1024, 8, 4),
+    (2, 8, 2, 5000, 32, 8),
+    (1, 8, 2, 3001, 64, 6),
+    (1, 4, 1, 777, 16, 5),
+    (1, 16, 2, 1500, 13, 3),
+    (2, 4, 2, 100, 1, 8),
+    (1, 2, 1, 65, 24, 2),
+])
+def test_score_stage(B, Hq, Hkv, N, L, P):
+    """Score kernel against the oracle fed the same table, ids and norms."""
+    log(f"score {(B, Hq, Hkv, N, L, P)}")
+    w = W.custom_workload(B=B, Hq=Hq, Hkv=Hkv, d=128, N=N, dtype="bf16", L=L, P=P,
+                          tau=0.3, lognormal_v=True)
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=4)
+    ids, vn = S.hash_keys(K, V, R, L, P)
+    table = S.bucket_probs(Q, R, Hkv, L, P, 0.3)
+    sc = S.score(table, ids, vn, Hq)
+    torch.cuda.synchronize()
+    ref = O.soft_scores(table_to_oracle_layout(table, Hq // Hkv), ids.cpu().numpy(),
+                        f64(vn), Hq // Hkv)
+    assert_close_rel(sc.cpu().numpy(), ref, 1e-5, 1e-30, "scores")
+
+
+# ------------------------------------------------------------------ top-k
+
+@pytest.mark.parametrize("rows,n,k,kind", [
+    (1, 1024, 64, "rand"),
+    (7, 5000, 300, "ties"),
+    (3, 70000, 1, "rand"),
+    (2, 70000, 4096, "ties"),
+    (4, 129, 128, "rand"),
+    (4, 129, 129, "rand"),
+    (4, 129, 1000, "rand"),
+    (2, 1, 1, "rand"),
+    (3, 4096, 100, "const"),
+    (2, 20000, 1000, "zeros"),
+    (32, 32768, 1024, "lognormal"),
+    (5, 300001, 7777, "ties"),
+])
+def test_topk_stage(rows, n, k, kind):
+    log(f"topk {(rows, n, k, kind)}")
+    g = torch.Generator().manual_seed(rows * 1000003 + n + k)
+    if kind == "rand":
+        s = torch.rand(rows, n, generator=g)
+    elif kind == "ties":
+        s = torch.randint(0, 50, (rows, n), generator=g).float() * 0.125
+    elif kind == "const":
+        s = torch.full((rows, n), 2.5)
+    elif kind == "zeros":
+        s = torch.zeros(rows, n)
+        s[:, ::7] = torch.rand(rows, (n + 6) // 7, generator=g)
+    else:
+        s = torch.exp(torch.randn(rows, n, generator=g) * 3.0)
+    idx = S.topk(s.to(DEV), k)
+    torch.cuda.synchronize()
+    ref = O.topk_indices(s.numpy(), k)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+# --------------------------------------------------------------- attention
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,N,kk,dt", [
+    (1, 1, 1, 64, 1024, 64, "f32"),
+    (2, 8, 2, 128, 3000, 1000, "bf16"),
+    (1, 32, 8, 128, 20000, 4096, "bf16"),
+    (1, 4, 4, 64, 50, 50, "bf16"),
+    (1, 2, 1, 128, 10, 1, "f32"),
+    (2, 8, 1, 128, 700, 333, "f32"),
+])
+def test_sparse_attn_stage(B, Hq, Hkv, d, N, kk, dt):
+    log(f"attn {(B, Hq, Hkv, d, N, kk, dt)}")
+    w = W.custom_workload(B=B, Hq=Hq, Hkv=Hkv, d=d, N=N, dtype=dt, lognormal_v=True)
+    Q, K, V, _ = W.make_decode_inputs(w, DEV, seed=6)
+    g = torch.Generator().manual_seed(9)
+    idx = torch.stack([torch.stack([torch.sort(torch.randperm(N, generator=g)[:kk]).values
+                                    for _ in range(Hq)]) for _ in range(B)])
+    idx = idx.to(torch.int32).to(DEV)
+    out = S.sparse_attn(Q, K, V, idx)
+    torch.cuda.synchronize()
+    ref = O.subset_attention(f64(Q), f64(K), f64(V), idx.cpu().numpy(), Hq // Hkv)
+    tol = 2e-2 if dt == "bf16" else 1e-4
+    assert np.max(np.abs(f64(out) - ref)) <= tol
+
+
+# ----------------------------------------------------------- decode end to end
+
+def _check_decode(w, seed=0, step=0, sample_rows=None):
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=seed, step=step)
+    ids, vn = S.hash_keys(K, V, R, w.L, w.P)
+    kk = w.kk
+    idx = torch.empty((w.B, w.Hq, kk), dtype=torch.int32, device=DEV)
+    sc = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=DEV)
+    out, _, _ = S.decode(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, idx_out=idx,
+                         scores_out=sc)
+    torch.cuda.synchronize()
+    G = w.G
+    rows = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    if sample_rows is not None:
+        rng = np.random.default_rng(seed + step)
+        pick = rng.choice(len(rows), size=min(sample_rows, len(rows)), replace=False)
+        rows = [rows[i] for i in sorted(pick)]
+    p_ref = O.soft_bucket_probs(f64(Q), f64(R), w.L, w.P, tau32(w.tau))
+    ids_np = ids.cpu().numpy()
+    vn64 = f64(vn)
+    sc_np = sc.cpu().numpy()
+    idx_np = idx.cpu().numpy()
+    out64 = f64(out)
+    Q64 = f64(Q)
+    swaps = 0
+    for (b, h) in rows:
+        g = h // G
+        s_ref = O.soft_scores(p_ref[b:b + 1, h:h + 1], ids_np[b:b + 1, g:g + 1],
+                              vn64[b:b + 1, g:g + 1], 1)[0, 0]
+        assert_close_rel(sc_np[b, h], s_ref, 1e-5, 1e-30, f"scores row {(b, h)}")
+        # (i) selection is exact on the GPU's own scores
+        sel = O.topk_indices(sc_np[b, h], w.k)
+        assert np.array_equal(idx_np[b, h], sel), f"top-k row {(b, h)}"
+        # (ii) against float64 scores: differences only inside the band
+        sel_ref = O.topk_indices(s_ref, w.k)
+        diff = np.setxor1d(sel, sel_ref)
+        if diff.size:
+            kth = np.sort(s_ref)[::-1][kk - 1]
+            band = np.abs(s_ref[diff] - kth) <= 1e-5 * kth + 1e-30
+            assert band.all(), f"selection differs outside the band in row {(b, h)}"
+            swaps += diff.size // 2
+        Kg = f64(K[b, g][torch.from_numpy(idx_np[b, h]).long().to(DEV)])
+        Vg = f64(V[b, g][torch.from_numpy(idx_np[b, h]).long().to(DEV)])
+        a = Kg @ Q64[b, h] / math.sqrt(w.d)
+        a = np.exp(a - a.max())
+        ref_out = (a / a.sum()) @ Vg
+        tol = 2e-2 if w.dtype == "bf16" else 1e-4
+        assert np.max(np.abs(out64[b, h] - ref_out)) <= tol, f"out row {(b, h)}"
+    log(f"{w.name}: {len(rows)} rows checked, {swaps} tolerance-band swaps")
+    return ids, vn, out, idx, sc
+
+
+def test_decode_tiny_fp32_full_oracle():
+    w = W.WORKLOADS["tiny_fp32_1k"]
+    log(f"decode {w.name}")
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=0)
+    ids, vn = S.hash_keys(K, V, R, w.L, w.P)
+    idx = torch.empty((1, 1, w.kk), dtype=torch.int32, device=DEV)
+    sc = torch.empty((1, 1, w.N), dtype=torch.float32, device=DEV)
+    out, _, _ = S.decode(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, idx_out=idx,
+                         scores_out=sc)
+    torch.cuda.synchronize()
+    ref_ids = O.hash_keys(f64(K), f64(R), w.L, w.P)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    r_out, r_idx, r_s, _ = O.decode(f64(Q), f64(K), f64(V), f64(R), ref_ids,
+                                    O.value_norms(f64(V)), w.L, w.P, tau32(w.tau), w.k)
+    assert_close_rel(sc.cpu().numpy(), r_s, 1e-5, 1e-30, "scores")
+    assert np.array_equal(idx.cpu().numpy(), O.topk_indices(sc.cpu().numpy(), w.k))
+    assert np.array_equal(idx.cpu().numpy(), r_idx)
+    assert np.max(np.abs(f64(out) - r_out)) <= 1e-4
+
+
+def test_decode_small_gqa_full():
+    w = W.custom_workload(B=2, Hq=8, Hkv=2, d=128, N=5000, dtype="bf16", L=32, P=8,
+                          tau=0.3, k=300, outlier_channels=4, outlier_scale=8.0,
+                          lognormal_v=True, planted=16, name="small_gqa")
+    log("decode small_gqa")
+    _check_decode(w)
+
+
+def test_decode_llama3_8b_32k():
+    w = W.WORKLOADS["llama3_8b_32k"]
+    log(f"decode {w.name}")
+    _check_decode(w, sample_rows=12)
+
+
+@pytest.mark.parametrize("step", [0, 1, 255])
+def test_decode_llama3_8b_128k_b4(step):
+    w = W.WORKLOADS["llama3_8b_128k_b4"]
+    log(f"decode {w.name} step {step}")
+    _check_decode(w, step=step, sample_rows=6)
+
+
+def test_decode_llama3_8b_1m():
+    w = W.WORKLOADS["llama3_8b_1m"]
+    log(f"decode {w.name}")
+    _check_decode(w, sample_rows=3)
+
+
+def test_decode_is_deterministic():
+    w = W.WORKLOADS["llama3_8b_32k"]
+    log("decode determinism")
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=1)
+    ids, vn = S.hash_keys(K, V, R, w.L, w.P)
+    ids2, vn2 = S.hash_keys(K, V, R, w.L, w.P)
+    assert torch.equal(ids, ids2) and torch.equal(vn, vn2)
+    res = []
+    for _ in range(2):
+        idx = torch.empty((w.B, w.Hq, w.kk), dtype=torch.int32, device=DEV)
+        sc = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=DEV)
+        out, _, _ = S.decode(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, idx_out=idx,
+                             scores_out=sc)
+        res.append((out, idx, sc))
+    torch.cuda.synchronize()
+    for a, b in zip(res[0], res[1]):
+        assert torch.equal(a, b)
+
+
+def test_decode_identical_group_queries_give_identical_outputs():
+    w = W.custom_workload(B=1, Hq=8, Hkv=2, d=128, N=4000, dtype="bf16", L=32, P=8,
+                          tau=0.3, k=256, lognormal_v=True)
+    log("decode GQA identical")
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=8)
+    Q = Q[:, ::4].repeat_interleave(4, dim=1).contiguous()
+    ids, vn = S.hash_keys(K, V, R, w.L, w.P)
+    idx = torch.empty((1, 8, 256), dtype=torch.int32, device=DEV)
+    out, _, _ = S.decode(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, idx_out=idx)
+    torch.cuda.synchronize()
+    for h in range(8):
+        assert torch.equal(out[0, h], out[0, (h // 4) * 4])
+        assert torch.equal(idx[0, h], idx[0, (h // 4) * 4])
+
+
+@pytest.mark.parametrize("N,k", [(1, 1), (5, 3), (5, 5), (64, 1000), (1000, 1)])
+def test_decode_edge_sizes(N, k):
+    w = W.custom_workload(B=1, Hq=4, Hkv=2, d=128, N=N, dtype="bf16", L=32, P=8,
+                          tau=0.3, k=k, lognormal_v=True, name=f"edge_{N}_{k}")
+    log(f"decode edge N={N} k={k}")
+    _, _, out, idx, _ = _check_decode(w)
+    if N == 1:
+        _, _, V, _ = W.make_decode_inputs(w, DEV)
+        for h in range(4):
+            assert torch.equal(out[0, h], V[0, h // 2, 0])
+    if k >= N:
+        assert torch.equal(idx.cpu(), torch.arange(N, dtype=torch.int32).expand(1, 4, N))
