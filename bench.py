@@ -18,6 +18,7 @@ CPU baseline (the float64 oracle on a bounded sample of the same workload).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -43,29 +44,74 @@ def parse():
                     help="approximate budget of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-stage-timing", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 1 GiB buffer 4 times (reference for HBM "
+                         "byte counters) and exit")
     return ap.parse_args()
 
 
 def algorithmic_bytes(w):
-    """Compulsory bytes per step, whole step and per stage."""
+    """Compulsory bytes of one whole decode step: bucket ids and value norms
+    of every key, the selected K and V rows of every query head, queries and
+    outputs (intermediates such as tables and scores are not counted)."""
+    e = w.elem_bytes
+    rows = w.B * w.Hq
+    keys = w.B * w.Hkv * w.N
+    return keys * w.L + keys * 4 + rows * w.kk * 2 * w.d * e + 2 * rows * w.d * e
+
+
+def decode_kernel_names(w):
+    """Kernels socket_decode enqueues for this workload, in order. The score
+    kernel builds the first top-k histogram itself when the table plus the
+    packed histogram fit the 160 KB of LDS (true for every workload here)."""
+    names = ["bucket_probs_kernel", "score_kernel"]
+    if w.kk >= w.N:
+        names += ["iota_rows_kernel"]
+    else:
+        lds = (2 ** w.P) * w.L * w.G * 4 + w.G * 1024 * 4
+        if lds > 160 * 1024:
+            names += ["zero_u32_kernel", "topk_hist_kernel"]
+        names += ["topk_filter_kernel", "topk_refine_kernel"]
+    return names + ["sparse_attn_kernel", "attn_merge_kernel"]
+
+
+def kernel_bytes(w):
+    """Compulsory HBM bytes of one launch of each decode kernel."""
     e = w.elem_bytes
     rows = w.B * w.Hq
     keys = w.B * w.Hkv * w.N
     kk = w.kk
-    q_out = 2 * rows * w.d * e
-    ids = keys * w.L
-    norms = keys * 4
-    gather = rows * kk * 2 * w.d * e
-    scores = rows * w.N * 4
     table = w.B * w.Hkv * (2 ** w.P) * w.L * w.G * 4
-    step = ids + norms + gather + q_out
-    stages = {
-        "bucket_probs": rows * w.d * e + w.d * w.C * e + table,
-        "score": ids + norms + table + scores,
-        "topk": scores + rows * kk * 4,
-        "sparse_attn": gather + q_out + rows * kk * 4,
+    scores = rows * w.N * 4
+    partial = 0  # intermediates between two kernels are not counted
+    return {
+        "bucket_probs_kernel": rows * w.d * e + w.d * w.C * e + table,
+        "score_kernel": keys * w.L + keys * 4 + table + scores,
+        "zero_u32_kernel": rows * 2048 * 4,
+        "topk_hist_kernel": scores,
+        "topk_filter_kernel": scores,
+        "topk_refine_kernel": rows * kk * 4,
+        "iota_rows_kernel": rows * kk * 4,
+        "sparse_attn_kernel": rows * kk * (2 * w.d * e + 4) + rows * w.d * e + partial,
+        "attn_merge_kernel": rows * w.d * e,
     }
-    return step, stages
+
+
+def _hip_runtime():
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                        ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+def _hip_event(hip):
+    ev = ctypes.c_void_p()
+    rc = hip.hipEventCreate(ctypes.byref(ev))
+    if rc != 0:
+        raise RuntimeError(f"hipEventCreate failed ({rc})")
+    return ev.value
 
 
 def cpu_baseline(w, budget_s):
@@ -77,33 +123,36 @@ def cpu_baseline(w, budget_s):
     import oracle as O
     import synthetic as W
 
-    Q, K, V, R = W.make_decode_inputs(w, "cpu", seed=0, step=0, layer=0)
-    Q64 = Q.double().numpy()
-    R64 = R.double().numpy()
+    K, V = W.make_keys_values(w, "cpu", seed=0, layer=0)
+    R64 = W.make_hyperplanes(w, "cpu", seed=0, layer=0).double().numpy()
     tau = float(np.float32(w.tau))
     done = 0
+    steps = 0
     elapsed = 0.0
     with threadpool_limits(limits=1):
-        for b in range(w.B):
+        cache = []
+        for b in range(w.B):                         # prefill, not timed
             K64 = K[b:b + 1].double().numpy()
             V64 = V[b:b + 1].double().numpy()
-            ids = O.hash_keys(K64, R64, w.L, w.P)      # prefill, not timed
-            vn = O.value_norms(V64)
+            cache.append((K64, V64, O.hash_keys(K64, R64, w.L, w.P), O.value_norms(V64)))
+        while elapsed < budget_s and steps < w.steps:
+            Q64 = W.make_query(w, "cpu", seed=0, step=steps, layer=0).double().numpy()
             t0 = time.perf_counter()
-            O.decode(Q64[b:b + 1], K64, V64, R64, ids, vn, w.L, w.P, tau, w.k)
+            for b in range(w.B):
+                K64, V64, ids, vn = cache[b]
+                O.decode(Q64[b:b + 1], K64, V64, R64, ids, vn, w.L, w.P, tau, w.k)
             elapsed += time.perf_counter() - t0
-            done += 1
-            if elapsed >= budget_s:
-                break
+            done += w.B
+            steps += 1
     return {
         "value": done / elapsed,
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"{w.name}: decode step 0 for batch elements 0..{done - 1} "
+        "sample": (f"{w.name}: decode steps 0..{steps - 1} of the whole batch "
                    f"({done} tokens, {w.Hq} heads x {w.N} keys each), numpy float64 "
-                   f"oracle, single thread, {elapsed:.1f} s timed (prefill hashing "
-                   f"not timed)"),
+                   f"oracle on one host thread, {elapsed:.1f} s timed (prefill "
+                   f"hashing not timed)"),
     }
 
 
@@ -117,6 +166,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_copy": src.numel() * 4,
+                          "copies": 4}), flush=True)
+        return
 
     import soft_lsh_sparse_amd as S
     import synthetic as W
@@ -180,65 +239,53 @@ def main():
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
     tokens_per_s = w.B / (ms_per_step * 1e-3)
 
-    step_bytes, stage_bytes = algorithmic_bytes(w)
+    step_bytes = algorithmic_bytes(w)
     hbm_frac = step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9)
 
-    # ---- per-stage kernel times: the same kernels through the stage calls,
-    # bracketed by HIP events on the launch stream
-    stage_ms = {}
+    # ---- per-kernel times of the same decode: socket_decode_profiled records
+    # a HIP event on the launch stream before the first kernel and after
+    # every kernel (same kernels, same order, same workspace)
+    kernel_ms = {}
     roofline = None
     if not args.skip_stage_timing:
-        table = torch.empty(w.B * w.Hkv * (2 ** w.P) * w.L * w.G, dtype=torch.float32,
-                            device=dev)
-        scores = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
-        tws_b = lib.socket_topk_workspace_bytes(w.B * w.Hq, w.N, w.k)
-        tws = torch.empty(max(tws_b, 1), dtype=torch.uint8, device=dev)
-        aws_b = lib.socket_sparse_attn_workspace_bytes(w.B, w.Hq, w.d, w.kk)
-        aws = torch.empty(aws_b, dtype=torch.uint8, device=dev)
-        names = ["bucket_probs", "score", "topk", "sparse_attn"]
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
-               for _ in range(args.steps)]
+        names = decode_kernel_names(w)
+        hip = _hip_runtime()
+        n_ev = len(names) + 1
+        events = [[_hip_event(hip) for _ in range(n_ev)] for _ in range(args.steps)]
+        ev_arrays = [(ctypes.c_void_p * n_ev)(*ev) for ev in events]
+        prof = lib.socket_decode_profiled
         torch.cuda.synchronize()
         for i, s in enumerate(range(args.warmup, total)):
-            layer = s % args.layers
-            K, V, R, ids, vn = layers[layer]
-            Q = queries[layer][s % n_q]
-            e = evs[i]
-            e[0].record()
-            lib.socket_bucket_probs(Q.data_ptr(), R.data_ptr(), dt_code, w.B, w.Hq,
-                                    w.Hkv, w.d, w.L, w.P, w.tau, table.data_ptr(),
-                                    stream)
-            e[1].record()
-            lib.socket_score(table.data_ptr(), ids.data_ptr(), vn.data_ptr(), w.B,
-                             w.Hq, w.Hkv, w.N, w.N, w.L, w.P, scores.data_ptr(),
-                             stream)
-            e[2].record()
-            lib.socket_topk(scores.data_ptr(), w.B * w.Hq, w.N, w.k, idx.data_ptr(),
-                            tws.data_ptr(), tws_b, stream)
-            e[3].record()
-            lib.socket_sparse_attn(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dt_code,
-                                   w.B, w.Hq, w.Hkv, w.d, w.N, idx.data_ptr(), w.kk,
-                                   out.data_ptr(), aws.data_ptr(), aws_b, stream)
-            e[4].record()
+            st = prof(*arglist[s], ev_arrays[i], n_ev)
+            if st:
+                _lib.check(st, "socket_decode_profiled")
         torch.cuda.synchronize()
         for j, name in enumerate(names):
-            stage_ms[name] = sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
-        # dominant single-kernel stage for the roofline (score is one kernel)
-        dom = max(stage_ms, key=stage_ms.get)
-        kernel = {"score": "score_kernel_rot", "bucket_probs": "bucket_probs_kernel",
-                  "topk": "topk (zero+hist+filter+refine)",
-                  "sparse_attn": "sparse_attn_kernel+attn_merge_kernel"}[dom]
-        achieved = stage_bytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
+            tot = 0.0
+            for ev in events:
+                ms = ctypes.c_float()
+                rc = hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(ev[j]),
+                                             ctypes.c_void_p(ev[j + 1]))
+                if rc != 0:
+                    raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+                tot += ms.value
+            kernel_ms[name] = tot / args.steps
+        for ev in events:
+            for e in ev:
+                hip.hipEventDestroy(ctypes.c_void_p(e))
+        kbytes = kernel_bytes(w)
+        dom = max(kernel_ms, key=kernel_ms.get)
+        achieved = kbytes[dom] / (kernel_ms[dom] * 1e-3) / 1e9
         roofline = {
             "bound": "hbm",
-            "kernel": kernel,
+            "kernel": dom,
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "algorithmic_bytes_per_launch": stage_bytes[dom],
-            "avg_launch_ms": round(stage_ms[dom], 5),
+            "algorithmic_bytes_per_launch": kbytes[dom],
+            "avg_launch_ms": round(kernel_ms[dom], 5),
         }
 
     cpu = None
@@ -265,7 +312,7 @@ def main():
         },
         "hbm_peak_frac": round(hbm_frac, 4),
         "algorithmic_bytes_per_step": step_bytes,
-        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "kernel_ms": {k: round(v, 5) for k, v in kernel_ms.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),

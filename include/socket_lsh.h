@@ -208,6 +208,25 @@ socket_status socket_decode(const void* Q, const void* K, const void* V,
                             void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/*
+ * socket_decode with per-kernel timing: identical work and results, and in
+ * addition events[0] (a hipEvent_t) is recorded on `stream` before the first
+ * kernel and events[i] right after the i-th kernel it enqueues, for at most
+ * n_events events. Kernel order: bucket table, scores, then the top-k
+ * kernels (clear + histogram, unless the score kernel built the histogram
+ * itself, then filter and refine; a single index fill when k >= n_keys),
+ * then the attention gather and its merge. Unused events are not touched.
+ * For profiling tools; events must not be NULL.
+ */
+socket_status socket_decode_profiled(
+    const void* Q, const void* K, const void* V, const void* R,
+    const uint8_t* ids, const float* vnorm, socket_dtype dtype, int32_t B,
+    int32_t Hq, int32_t Hkv, int32_t d, int64_t n_keys,
+    int64_t head_stride_rows, int32_t L, int32_t P, float tau, int64_t k,
+    void* out, int32_t* idx_out, float* scores_out, void* workspace,
+    size_t workspace_bytes, void* stream, void* const* events,
+    int32_t n_events);
+
 #ifdef __cplusplus
 }
 #endif

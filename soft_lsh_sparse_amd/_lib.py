@@ -56,6 +56,8 @@ SIGNATURES = {
                               c_float, c_int64, c_void_p, c_void_p, c_void_p,
                               c_void_p, c_size_t, c_void_p]),
 }
+SIGNATURES["socket_decode_profiled"] = (
+    c_int, SIGNATURES["socket_decode"][1] + [c_void_p, c_int32])
 
 _lock = threading.Lock()
 _lib = None

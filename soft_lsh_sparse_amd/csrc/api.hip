@@ -258,6 +258,9 @@ socket_status socket_sparse_attn(const void* Q, const void* K, const void* V,
   SOCKET_TRY(check_heads(B, Hq, Hkv));
   SOCKET_TRY(check_d(d));
   if (kk < 1) return fail(SOCKET_ERR_INVALID_ARGUMENT, "kk must be >= 1");
+  if (kk > kMaxSelected)
+    return fail(SOCKET_ERR_UNSUPPORTED, "at most %lld selected keys per row",
+                (long long)kMaxSelected);
   if (head_stride_rows < 1)
     return fail(SOCKET_ERR_INVALID_ARGUMENT, "head_stride_rows must be >= 1");
   if (head_stride_rows >= ((int64_t)1 << 31))
@@ -286,15 +289,19 @@ size_t socket_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv,
   return decode_layout(B, Hq, Hkv, d, n_keys, L, P, k).total;
 }
 
-socket_status socket_decode(const void* Q, const void* K, const void* V,
-                            const void* R, const uint8_t* ids,
-                            const float* vnorm, socket_dtype dtype, int32_t B,
-                            int32_t Hq, int32_t Hkv, int32_t d,
-                            int64_t n_keys, int64_t head_stride_rows,
-                            int32_t L, int32_t P, float tau, int64_t k,
-                            void* out, int32_t* idx_out, float* scores_out,
-                            void* workspace, size_t workspace_bytes,
-                            void* stream) {
+}  // extern "C"
+
+namespace {
+
+socket_status decode_impl(const void* Q, const void* K, const void* V,
+                          const void* R, const uint8_t* ids,
+                          const float* vnorm, socket_dtype dtype, int32_t B,
+                          int32_t Hq, int32_t Hkv, int32_t d, int64_t n_keys,
+                          int64_t head_stride_rows, int32_t L, int32_t P,
+                          float tau, int64_t k, void* out, int32_t* idx_out,
+                          float* scores_out, void* workspace,
+                          size_t workspace_bytes, void* stream,
+                          void* const* events, int32_t n_events) {
   SOCKET_TRY(check_dtype(dtype));
   SOCKET_TRY(check_heads(B, Hq, Hkv));
   SOCKET_TRY(check_d(d));
@@ -304,6 +311,9 @@ socket_status socket_decode(const void* Q, const void* K, const void* V,
     return fail(SOCKET_ERR_INVALID_ARGUMENT, "tau must be finite and > 0");
   if (k < 1) return fail(SOCKET_ERR_INVALID_ARGUMENT, "k must be >= 1");
   if (n_keys < 1) return fail(SOCKET_ERR_INVALID_ARGUMENT, "n_keys must be >= 1");
+  if ((k < n_keys ? k : n_keys) > kMaxSelected)
+    return fail(SOCKET_ERR_UNSUPPORTED, "at most %lld selected keys per row",
+                (long long)kMaxSelected);
   if (head_stride_rows < n_keys)
     return fail(SOCKET_ERR_INVALID_ARGUMENT, "head_stride_rows (%lld) < n_keys (%lld)",
                 (long long)head_stride_rows, (long long)n_keys);
@@ -319,6 +329,15 @@ socket_status socket_decode(const void* Q, const void* K, const void* V,
                 lay.total, workspace ? workspace_bytes : (size_t)0);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (events != nullptr && n_events < 1)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "n_events must be >= 1 with events");
+  LaunchTrace trace{reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)),
+                    events ? n_events : 0, 0};
+  struct TraceScope {
+    explicit TraceScope(LaunchTrace* t) { g_trace = t; }
+    ~TraceScope() { g_trace = nullptr; }
+  } scope(events ? &trace : nullptr);
+  trace_mark(s);  // first event: before the first kernel
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   float* table = reinterpret_cast<float*>(ws + lay.table_off);
   float* scores = scores_out ? scores_out : reinterpret_cast<float*>(ws + lay.scores_off);
@@ -327,17 +346,61 @@ socket_status socket_decode(const void* Q, const void* K, const void* V,
   float* partial = reinterpret_cast<float*>(ws + lay.attn_off);
   const bool bf16 = dtype == SOCKET_DTYPE_BF16;
 
-  hipError_t err = launch_bucket_probs(Q, R, bf16, B, Hq, Hkv, d, L, P, tau,
-                                       table, nullptr, 0, s);
+  // The score kernel builds the first radix histogram of the top-k when its
+  // LDS has room next to the table; the bucket kernel clears it beforehand.
+  const int64_t kk = k < n_keys ? k : n_keys;
+  const bool fused_hist = kk < n_keys &&
+                          score_lds_bytes(L, P, Hq / Hkv, true) <= kLdsBytesPerCU;
+  uint32_t* hist = reinterpret_cast<uint32_t*>(tws + lay.topk.hist_off);
+  hipError_t err = launch_bucket_probs(
+      Q, R, bf16, B, Hq, Hkv, d, L, P, tau, table, fused_hist ? hist : nullptr,
+      fused_hist ? (int64_t)B * Hq * kHistBins : 0, s);
   if (err != hipSuccess) return from_hip(err, "socket_decode: bucket_probs");
   err = launch_score(table, ids, vnorm, B, Hq, Hkv, n_keys, head_stride_rows,
-                     L, P, scores, nullptr, s);
+                     L, P, scores, fused_hist ? hist : nullptr, s);
   if (err != hipSuccess) return from_hip(err, "socket_decode: score");
-  err = launch_topk(scores, lay.topk, idx, tws, false, s);
+  err = launch_topk(scores, lay.topk, idx, tws, fused_hist, s);
   if (err != hipSuccess) return from_hip(err, "socket_decode: topk");
   err = launch_sparse_attn(Q, K, V, bf16, lay.attn, head_stride_rows, idx, out,
                            partial, s);
   return from_hip(err, "socket_decode: sparse_attn");
 }
 
+}  // namespace
+
+extern "C" {
+
+socket_status socket_decode(const void* Q, const void* K, const void* V,
+                            const void* R, const uint8_t* ids,
+                            const float* vnorm, socket_dtype dtype, int32_t B,
+                            int32_t Hq, int32_t Hkv, int32_t d,
+                            int64_t n_keys, int64_t head_stride_rows,
+                            int32_t L, int32_t P, float tau, int64_t k,
+                            void* out, int32_t* idx_out, float* scores_out,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return decode_impl(Q, K, V, R, ids, vnorm, dtype, B, Hq, Hkv, d, n_keys,
+                     head_stride_rows, L, P, tau, k, out, idx_out, scores_out,
+                     workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+socket_status socket_decode_profiled(
+    const void* Q, const void* K, const void* V, const void* R,
+    const uint8_t* ids, const float* vnorm, socket_dtype dtype, int32_t B,
+    int32_t Hq, int32_t Hkv, int32_t d, int64_t n_keys,
+    int64_t head_stride_rows, int32_t L, int32_t P, float tau, int64_t k,
+    void* out, int32_t* idx_out, float* scores_out, void* workspace,
+    size_t workspace_bytes, void* stream, void* const* events,
+    int32_t n_events) {
+  if (events == nullptr)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "events must not be NULL");
+  return decode_impl(Q, K, V, R, ids, vnorm, dtype, B, Hq, Hkv, d, n_keys,
+                     head_stride_rows, L, P, tau, k, out, idx_out, scores_out,
+                     workspace, workspace_bytes, stream, events, n_events);
+}
+
 }  // extern "C"
+
+namespace socket_lsh {
+thread_local LaunchTrace* g_trace = nullptr;
+}  // namespace socket_lsh

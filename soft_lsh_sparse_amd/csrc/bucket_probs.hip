@@ -47,8 +47,10 @@ __global__ __launch_bounds__(256) void bucket_probs_kernel(
   const int C = L * P;
   const int ncols = nl * P;
   const int npairs = G * ncols;
-  double* w1 = smem;             // weight of bit value 1, [G][ncols]
-  double* w0 = smem + npairs;    // weight of bit value 0
+  double* w1 = smem;                    // weight of bit value 1, [G][ncols]
+  double* w0 = w1 + npairs;             // weight of bit value 0
+  float* qs = reinterpret_cast<float*>(w0 + npairs);  // [G][d]
+  float* rs = qs + G * d;                             // [d][ncols]
 
   // Optional clearing of per-call counters (spread over all blocks).
   if (zero_ptr != nullptr) {
@@ -59,14 +61,22 @@ __global__ __launch_bounds__(256) void bucket_probs_kernel(
       zero_ptr[i] = 0u;
   }
 
-  // z[j][c] = q_{g*G+j} . R[:, l0*P + c], float64 (bf16/f32 products are exact)
+  // Stage the group's queries and this block's hyperplane columns in LDS
+  // (all loads issued together, coalesced along d and along the columns).
+  const int64_t q0 = ((int64_t)b * Hq + g * G) * d;
+  for (int i = threadIdx.x; i < G * d; i += blockDim.x) qs[i] = T::load(Q, q0 + i);
+  for (int i = threadIdx.x; i < d * ncols; i += blockDim.x) {
+    const int r = i / ncols, c = i % ncols;
+    rs[i] = T::load(R, (int64_t)r * C + l0 * P + c);
+  }
+  __syncthreads();
+
+  // z[j][c] = q_{g*G+j} . R[:, l0*P + c] in float64 (bf16/f32 products are exact)
   for (int pair = threadIdx.x; pair < npairs; pair += blockDim.x) {
     const int j = pair / ncols, c = pair % ncols;
-    const int64_t qrow = ((int64_t)b * Hq + g * G + j) * d;
-    const int col = l0 * P + c;
+    const float* q = qs + j * d;
     double z = 0.0;
-    for (int i = 0; i < d; ++i)
-      z += (double)T::load(Q, qrow + i) * (double)T::load(R, (int64_t)i * C + col);
+    for (int i = 0; i < d; ++i) z += (double)q[i] * (double)rs[i * ncols + c];
     // sigma(+2z/tau) for bit 1 and sigma(-2z/tau) for bit 0, both formed
     // from a = exp(-2|z|/tau) <= 1 so nothing overflows.
     const double a = exp(-fabs(z) * two_over_tau);
@@ -100,12 +110,17 @@ hipError_t launch_bucket_probs(const void* Q, const void* R, bool bf16, int B,
                                int64_t zero_words, hipStream_t stream) {
   const int G = Hq / Hkv;
   const int bhkv = B * Hkv;
-  // enough blocks to cover the chip, and at most ~12 KB of weights per block
+  // enough blocks to cover the chip; LDS per block: float64 weights plus the
+  // staged queries and hyperplane columns
+  auto lds_bytes = [&](int tpb) {
+    return (size_t)tpb * P * G * 2 * sizeof(double) + (size_t)G * d * sizeof(float) +
+           (size_t)d * tpb * P * sizeof(float);
+  };
   int tpb = (int)(((int64_t)L * bhkv + 511) / 512);
-  tpb = max(1, min(tpb, L));
-  while (tpb > 1 && (size_t)tpb * P * G * 2 * sizeof(double) > 12288) --tpb;
+  tpb = std::max(1, std::min(tpb, L));
+  while (tpb > 1 && lds_bytes(tpb) > 48 * 1024) --tpb;
   const int nchunks = (L + tpb - 1) / tpb;
-  const size_t shmem = (size_t)tpb * P * G * 2 * sizeof(double);
+  const size_t shmem = lds_bytes(tpb);
   const double two_over_tau = 2.0 / (double)tau;
   dim3 grid(bhkv, nchunks);
   if (bf16)
@@ -117,6 +132,7 @@ hipError_t launch_bucket_probs(const void* Q, const void* R, bool bf16, int B,
     hipLaunchKernelGGL(bucket_probs_kernel<F32>, grid, dim3(256), shmem,
                        stream, (const float*)Q, (const float*)R, Hq, Hkv, d, L,
                        P, two_over_tau, tpb, table, zero_ptr, zero_words);
+  trace_mark(stream);
   return hipGetLastError();
 }
 

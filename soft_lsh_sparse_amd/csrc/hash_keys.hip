@@ -320,6 +320,7 @@ hipError_t launch_bf16_nw(const uint16_t* K, const uint16_t* V,
   hipLaunchKernelGGL((hash_keys_bf16_kernel<D, NW>), dim3(grid), dim3(NW * 64),
                      0, stream, K, V, R, n_keys, stride, L, P, ids, vnorm,
                      n_tiles, tph, word_store);
+  trace_mark(stream);
   return hipGetLastError();
 }
 
@@ -381,6 +382,7 @@ hipError_t launch_hash_keys_f32(const float* K, const float* V, const float* R,
     hipLaunchKernelGGL(hash_keys_f32_kernel<64>, dim3(grid), dim3(256), 0,
                        stream, K, V, R, n_heads, n_keys, stride, L, P, ids,
                        vnorm);
+  trace_mark(stream);
   return hipGetLastError();
 }
 

@@ -8,6 +8,20 @@
 
 namespace socket_lsh {
 
+// Optional event trace for profiling: when set (by the profiled decode entry
+// point), every launcher records the next event on its stream right after
+// each kernel it enqueues.
+struct LaunchTrace {
+  hipEvent_t* events;
+  int n;
+  int used;
+};
+extern thread_local LaunchTrace* g_trace;
+inline void trace_mark(hipStream_t stream) {
+  if (g_trace != nullptr && g_trace->used < g_trace->n)
+    (void)hipEventRecord(g_trace->events[g_trace->used++], stream);
+}
+
 // ------------------------------------------------------------- prefill hash
 hipError_t launch_hash_keys_bf16(const uint16_t* K, const uint16_t* V,
                                  const uint16_t* R, int64_t n_heads,
@@ -30,6 +44,10 @@ hipError_t launch_bucket_probs(const void* Q, const void* R, bool bf16, int B,
 // ------------------------------------------------------------------ score
 // hist (optional): [B*Hq, 2048] first-digit histograms, accumulated with
 // atomics; must be zero on entry.
+// LDS bytes one score block needs (probability table, plus the packed
+// first-digit histogram when fused).
+size_t score_lds_bytes(int L, int P, int G, bool with_hist);
+constexpr size_t kLdsBytesPerCU = 160 * 1024;
 hipError_t launch_score(const float* table, const uint8_t* ids,
                         const float* vnorm, int B, int Hq, int Hkv,
                         int64_t n_keys, int64_t stride, int L, int P,
@@ -53,6 +71,8 @@ hipError_t launch_topk(const float* scores, const TopkPlan& plan,
                        hipStream_t stream);
 
 // ------------------------------------------------------- sparse attention
+// Largest selection one attention row supports: 1024 chunks of 256 keys.
+constexpr int64_t kMaxSelected = 262144;
 struct AttnPlan {
   int B, Hq, Hkv, d;
   int64_t kk;

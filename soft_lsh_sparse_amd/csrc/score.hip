@@ -21,8 +21,11 @@
 // per key. The L probabilities are summed in float32 in that fixed order and
 // multiplied by the value norm.
 //
-// Optionally the kernel also adds every score to a 2048-bin histogram of the
-// top 11 bits of its order key (the first pass of the top-k radix select).
+// Optionally the kernel also counts every score in a 2048-bin histogram of
+// the top 11 bits of its order key (the first pass of the top-k radix
+// select): per-block counts are kept in LDS as packed 16-bit pairs (a block
+// never scores more than 32768 keys per row) and added to the per-row global
+// histogram with integer atomics, which makes the result order-independent.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -33,6 +36,7 @@ namespace socket_lsh {
 namespace {
 
 constexpr int kScoreThreads = 512;
+constexpr int64_t kMaxSegForHist = 32768;
 
 // Rotate the NB-byte array held in NW 32-bit words left by r bytes
 // (0 <= r < 16): byte i of the result is byte (i + r) mod NB of the input.
@@ -84,6 +88,31 @@ __device__ __forceinline__ bool score_block_coords(int bhkv, int segs, int& bg,
   return true;
 }
 
+// Shared tail of both kernels: store the G scores of key n and count them.
+template <int G>
+__device__ __forceinline__ void emit_scores(const float (&acc)[G], float vn,
+                                            int64_t n, int64_t n_keys,
+                                            float* srow, uint32_t* hloc) {
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const float s = vn * acc[j];
+    srow[(int64_t)j * n_keys + n] = s;
+    if (hloc) {
+      const uint32_t bin = float_order_key(s) >> 21;
+      atomicAdd(hloc + j * (kHistBins / 2) + (bin >> 1), 1u << ((bin & 1) * 16));
+    }
+  }
+}
+
+template <int G>
+__device__ __forceinline__ void flush_hist(const uint32_t* hloc, uint32_t* hrow) {
+  for (int i = threadIdx.x; i < G * kHistBins; i += blockDim.x) {
+    const int j = i / kHistBins, bin = i % kHistBins;
+    const uint32_t v = (hloc[j * (kHistBins / 2) + (bin >> 1)] >> ((bin & 1) * 16)) & 0xffffu;
+    if (v) atomicAdd(hrow + (int64_t)j * kHistBins + bin, v);
+  }
+}
+
 // Fast path: L a multiple of 16 (LW = L/4 words of ids per key).
 template <int G, int LW>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(
@@ -97,11 +126,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(
   if (!score_block_coords(bhkv, segs, bg, seg)) return;
   const int b = bg / Hkv, g = bg % Hkv;
   const int tsize = (1 << P) * L * G;
+  uint32_t* hloc = hist ? reinterpret_cast<uint32_t*>(tab + tsize) : nullptr;
 
   {
     const float4* src = reinterpret_cast<const float4*>(table + (int64_t)bg * tsize);
     float4* dst = reinterpret_cast<float4*>(tab);
     for (int i = threadIdx.x; i < tsize / 4; i += kScoreThreads) dst[i] = src[i];
+    if (hloc)
+      for (int i = threadIdx.x; i < G * kHistBins / 2; i += kScoreThreads) hloc[i] = 0u;
   }
   __syncthreads();
 
@@ -110,7 +142,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(
   const uint8_t* idrow = ids + (int64_t)bg * stride * L;
   const float* vrow = vnorm + (int64_t)bg * stride;
   float* srow = scores + ((int64_t)b * Hq + (int64_t)g * G) * n_keys;
-  uint32_t* hrow = hist ? hist + ((int64_t)b * Hq + (int64_t)g * G) * kHistBins : nullptr;
+  const uint32_t umask = (1u << P) - 1u;  // ids are < 2^P; never index past the table
 
   // ids and norm of the next key are loaded while the current one is scored
   uint4 nxt[LW / 4];
@@ -139,7 +171,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(
     }
     const int r = (int)(n & 15);
     rotate_bytes<LW>(w, r);
-    const uint32_t umask = (1u << P) - 1u;  // ids are < 2^P; never index past the table
     float acc[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) acc[j] = 0.f;
@@ -152,12 +183,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(
 #pragma unroll
       for (int j = 0; j < G; ++j) acc[j] += pr[j];
     }
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float s = vn * acc[j];
-      srow[(int64_t)j * n_keys + n] = s;
-      if (hrow) atomicAdd(hrow + (int64_t)j * kHistBins + (float_order_key(s) >> 21), 1u);
-    }
+    emit_scores<G>(acc, vn, n, n_keys, srow, hloc);
+  }
+  if (hloc) {
+    __syncthreads();
+    flush_hist<G>(hloc, hist + ((int64_t)b * Hq + (int64_t)g * G) * kHistBins);
   }
 }
 
@@ -173,8 +203,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_generic(
   if (!score_block_coords(bhkv, segs, bg, seg)) return;
   const int b = bg / Hkv, g = bg % Hkv;
   const int tsize = (1 << P) * L * G;
+  uint32_t* hloc = hist ? reinterpret_cast<uint32_t*>(tab + tsize) : nullptr;
   for (int i = threadIdx.x; i < tsize; i += kScoreThreads)
     tab[i] = table[(int64_t)bg * tsize + i];
+  if (hloc)
+    for (int i = threadIdx.x; i < G * kHistBins / 2; i += kScoreThreads) hloc[i] = 0u;
   __syncthreads();
 
   const int64_t n0 = seg * seg_len;
@@ -182,7 +215,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_generic(
   const uint8_t* idrow = ids + (int64_t)bg * stride * L;
   const float* vrow = vnorm + (int64_t)bg * stride;
   float* srow = scores + ((int64_t)b * Hq + (int64_t)g * G) * n_keys;
-  uint32_t* hrow = hist ? hist + ((int64_t)b * Hq + (int64_t)g * G) * kHistBins : nullptr;
   for (int64_t n = n0 + threadIdx.x; n < n1; n += kScoreThreads) {
     float acc[G];
 #pragma unroll
@@ -195,13 +227,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_generic(
 #pragma unroll
       for (int j = 0; j < G; ++j) acc[j] += pr[j];
     }
-    const float vn = vrow[n];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float s = vn * acc[j];
-      srow[(int64_t)j * n_keys + n] = s;
-      if (hrow) atomicAdd(hrow + (int64_t)j * kHistBins + (float_order_key(s) >> 21), 1u);
-    }
+    emit_scores<G>(acc, vrow[n], n, n_keys, srow, hloc);
+  }
+  if (hloc) {
+    __syncthreads();
+    flush_hist<G>(hloc, hist + ((int64_t)b * Hq + (int64_t)g * G) * kHistBins);
   }
 }
 
@@ -211,14 +241,16 @@ hipError_t launch_score_g(const float* table, const uint8_t* ids,
                           int64_t n_keys, int64_t stride, int L, int P,
                           float* scores, uint32_t* hist, hipStream_t stream) {
   const int bhkv = B * Hkv;
-  const size_t tbytes = (size_t)(1 << P) * L * G * sizeof(float);
+  const size_t lds = score_lds_bytes(L, P, G, hist != nullptr);
   // blocks resident per CU as limited by the 160 KB of LDS
-  const int per_cu = (int)std::max<size_t>(1, std::min<size_t>(2, (160 * 1024) / tbytes));
+  const int per_cu = (int)std::max<size_t>(1, std::min<size_t>(2, (160 * 1024) / lds));
   const int64_t target = (int64_t)256 * per_cu;
   int64_t segs = (target + bhkv - 1) / bhkv;
   segs = std::max<int64_t>(1, std::min<int64_t>(segs, (n_keys + 2047) / 2048));
+  if (hist) segs = std::max<int64_t>(segs, (n_keys + kMaxSegForHist - 1) / kMaxSegForHist);
   int64_t seg_len = (n_keys + segs - 1) / segs;
   seg_len = (seg_len + 1023) / 1024 * 1024;
+  if (hist && seg_len > kMaxSegForHist) seg_len = kMaxSegForHist;
   segs = (n_keys + seg_len - 1) / seg_len;
   const int total = (int)(bhkv * segs);
   const int grid = ((total + 7) / 8) * 8;
@@ -240,25 +272,34 @@ hipError_t launch_score_g(const float* table, const uint8_t* ids,
                        ((stride * L) % 16 == 0);
   if (aligned && L == 32) {
     hipLaunchKernelGGL((score_kernel_rot<G, 8>), dim3(grid), dim3(kScoreThreads),
-                       tbytes, stream, table, ids, vnorm, Hq, Hkv, bhkv, n_keys,
+                       lds, stream, table, ids, vnorm, Hq, Hkv, bhkv, n_keys,
                        stride, P, (int)segs, seg_len, scores, hist);
+    trace_mark(stream);
   } else if (aligned && L == 64) {
     hipLaunchKernelGGL((score_kernel_rot<G, 16>), dim3(grid), dim3(kScoreThreads),
-                       tbytes, stream, table, ids, vnorm, Hq, Hkv, bhkv, n_keys,
+                       lds, stream, table, ids, vnorm, Hq, Hkv, bhkv, n_keys,
                        stride, P, (int)segs, seg_len, scores, hist);
+    trace_mark(stream);
   } else if (aligned && L == 16) {
     hipLaunchKernelGGL((score_kernel_rot<G, 4>), dim3(grid), dim3(kScoreThreads),
-                       tbytes, stream, table, ids, vnorm, Hq, Hkv, bhkv, n_keys,
+                       lds, stream, table, ids, vnorm, Hq, Hkv, bhkv, n_keys,
                        stride, P, (int)segs, seg_len, scores, hist);
+    trace_mark(stream);
   } else {
     hipLaunchKernelGGL((score_kernel_generic<G>), dim3(grid), dim3(kScoreThreads),
-                       tbytes, stream, table, ids, vnorm, Hq, Hkv, bhkv, n_keys,
+                       lds, stream, table, ids, vnorm, Hq, Hkv, bhkv, n_keys,
                        stride, L, P, (int)segs, seg_len, scores, hist);
+    trace_mark(stream);
   }
   return hipGetLastError();
 }
 
 }  // namespace
+
+size_t score_lds_bytes(int L, int P, int G, bool with_hist) {
+  return (size_t)(1 << P) * L * G * sizeof(float) +
+         (with_hist ? (size_t)G * kHistBins / 2 * sizeof(uint32_t) : 0);
+}
 
 hipError_t launch_score(const float* table, const uint8_t* ids,
                         const float* vnorm, int B, int Hq, int Hkv,

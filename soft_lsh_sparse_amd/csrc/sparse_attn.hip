@@ -173,23 +173,42 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
   }
 }
 
+constexpr int kMergeMaxChunks = 1024;
+
+// Online-softmax merge of the chunk partials of one row, in chunk order.
+// All (m, l) pairs are staged in LDS first; the accumulator loads of the
+// chunks are independent, so they are issued back to back.
 template <typename T, int D>
 __global__ __launch_bounds__(D) void attn_merge_kernel(
     const float* __restrict__ partial, int chunks,
     typename T::storage* __restrict__ out) {
+  __shared__ float sw[kMergeMaxChunks];
+  __shared__ float sl[kMergeMaxChunks];
+  __shared__ float s_tot[2];
   const int64_t row = blockIdx.x;
   const float* p = partial + row * chunks * (D + 2);
   const int t = threadIdx.x;
-  float mt = -INFINITY;
-  for (int c = 0; c < chunks; ++c) mt = fmaxf(mt, p[c * (D + 2) + D]);
-  float lt = 0.f, at = 0.f;
-  for (int c = 0; c < chunks; ++c) {
-    const float mc = p[c * (D + 2) + D];
-    const float w = mc == -INFINITY ? 0.f : expf(mc - mt);
-    lt = fmaf(w, p[c * (D + 2) + D + 1], lt);
-    at = fmaf(w, p[c * (D + 2) + t], at);
+  for (int c = t; c < chunks; c += D) {
+    sw[c] = p[c * (D + 2) + D];
+    sl[c] = p[c * (D + 2) + D + 1];
   }
-  T::store(out, row * D + t, at / lt);
+  __syncthreads();
+  if (t == 0) {
+    float mt = -INFINITY;
+    for (int c = 0; c < chunks; ++c) mt = fmaxf(mt, sw[c]);
+    float lt = 0.f;
+    for (int c = 0; c < chunks; ++c) {
+      const float w = sw[c] == -INFINITY ? 0.f : expf(sw[c] - mt);
+      sw[c] = w;
+      lt = fmaf(w, sl[c], lt);
+    }
+    s_tot[0] = lt;
+  }
+  __syncthreads();
+  float at = 0.f;
+#pragma unroll 8
+  for (int c = 0; c < chunks; ++c) at = fmaf(sw[c], p[c * (D + 2) + t], at);
+  T::store(out, row * D + t, at / s_tot[0]);
 }
 
 template <typename T, int D, int KPW>
@@ -206,10 +225,12 @@ hipError_t launch_attn_t(const void* Q, const void* K, const void* V,
                      dim3(kAttnThreads), 0, stream, (const S*)Q, (const S*)K,
                      (const S*)V, plan.Hq, plan.Hkv, bhkv, stride, idx,
                      plan.kk, plan.chunks, partial);
+  trace_mark(stream);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3(plan.B * plan.Hq),
                      dim3(D), 0, stream, partial, plan.chunks, (S*)out);
+  trace_mark(stream);
   return hipGetLastError();
 }
 

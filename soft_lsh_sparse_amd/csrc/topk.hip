@@ -38,7 +38,7 @@ namespace {
 
 constexpr int kFilterThreads = 256;
 constexpr int kRefineThreads = 1024;
-constexpr int kFilterUnroll = 4;
+constexpr int kFilterUnroll = 4;  // 16-byte loads per thread per iteration
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & 63;
@@ -127,15 +127,27 @@ __global__ __launch_bounds__(kFilterThreads) void topk_hist_kernel(
     if (h[i]) atomicAdd(hr + i, h[i]);
 }
 
+// Wave-inclusive scan of one uint32 per lane.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
 __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(
     const float* __restrict__ scores, int64_t n, int64_t kk, int segs,
     int64_t seg_len, const uint32_t* __restrict__ hist,
-    uint2* __restrict__ lists, uint32_t* __restrict__ seg_cnt) {
+    uint2* __restrict__ lists, uint32_t* __restrict__ seg_cnt, int vec4) {
   constexpr int NWV = kFilterThreads / 64;
+  constexpr int E = kFilterUnroll;
   __shared__ uint32_t scratch[kFilterThreads / 64 + 1];
   __shared__ uint32_t thr[2];
-  __shared__ uint32_t wcnt[kFilterUnroll * NWV];
-  __shared__ uint32_t woff[kFilterUnroll * NWV + 1];
+  __shared__ uint32_t wtot[E * NWV];
+  __shared__ uint32_t woff[E * NWV + 1];
   const int row = blockIdx.y, seg = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
@@ -148,56 +160,86 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(
   const int64_t n1 = min(n, n0 + seg_len);
   uint2* out = lists + (int64_t)row * n + n0;
   uint32_t count = 0;
-  for (int64_t base = n0; base < n1; base += kFilterThreads * kFilterUnroll) {
-    uint32_t u[kFilterUnroll];
-    bool f[kFilterUnroll];
-    uint64_t bal[kFilterUnroll];
+  // Each thread takes 4 consecutive scores per step (one 16-byte load);
+  // element order within an iteration is (step, thread, lane-element), i.e.
+  // ascending index, and the compaction preserves it.
+  for (int64_t base = n0; base < n1; base += (int64_t)kFilterThreads * 4 * E) {
+    uint32_t u[E][4];
+    uint32_t fl[E];
+    uint32_t excl[E];
 #pragma unroll
-    for (int e = 0; e < kFilterUnroll; ++e) {
-      const int64_t i = base + e * kFilterThreads + threadIdx.x;
-      const bool valid = i < n1;
-      u[e] = valid ? float_order_key(s[i]) : 0u;
-      f[e] = valid && (u[e] >> 21) >= b1;
-      bal[e] = __ballot(f[e]);
-      if (lane == 0) wcnt[e * NWV + wave] = (uint32_t)__popcll(bal[e]);
+    for (int e = 0; e < E; ++e) {
+      const int64_t i0 = base + ((int64_t)e * kFilterThreads + threadIdx.x) * 4;
+      float v[4];
+      if (vec4 && i0 + 3 < n1) {
+        const float4 x = *reinterpret_cast<const float4*>(s + i0);
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = i0 + i < n1 ? s[i0 + i] : 0.f;
+      }
+      uint32_t f = 0, c = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u[e][i] = float_order_key(v[i]);
+        if (i0 + i < n1 && (u[e][i] >> 21) >= b1) {
+          f |= 1u << i;
+          ++c;
+        }
+      }
+      fl[e] = f;
+      const uint32_t inc = wave_inclusive_scan(c);
+      excl[e] = inc - c;
+      if (lane == 63) wtot[e * NWV + wave] = inc;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
       uint32_t run = 0;
-      for (int q = 0; q < kFilterUnroll * NWV; ++q) {
+      for (int q = 0; q < E * NWV; ++q) {
         woff[q] = run;
-        run += wcnt[q];
+        run += wtot[q];
       }
-      woff[kFilterUnroll * NWV] = run;
+      woff[E * NWV] = run;
     }
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < kFilterUnroll; ++e) {
-      if (f[e]) {
-        const uint32_t pos = count + woff[e * NWV + wave] +
-                             (uint32_t)__popcll(bal[e] & lanemask_lt());
-        const int64_t i = base + e * kFilterThreads + threadIdx.x;
-        out[pos] = make_uint2(u[e], (uint32_t)i);
+    for (int e = 0; e < E; ++e) {
+      uint32_t pos = count + woff[e * NWV + wave] + excl[e];
+      const int64_t i0 = base + ((int64_t)e * kFilterThreads + threadIdx.x) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (fl[e] & (1u << i)) {
+          out[pos] = make_uint2(u[e][i], (uint32_t)(i0 + i));
+          ++pos;
+        }
       }
     }
-    count += woff[kFilterUnroll * NWV];
+    count += woff[E * NWV];
     __syncthreads();
   }
   if (threadIdx.x == 0) seg_cnt[(int64_t)row * segs + seg] = count;
 }
 
-// Locate list position p (0 <= p < total) in the concatenation of the
-// segment lists: returns the element.
-__device__ __forceinline__ uint2 list_at(const uint2* row_lists,
-                                         const uint32_t* off, int segs,
-                                         int64_t seg_len, uint32_t p) {
-  int lo = 0, hi = segs - 1;  // last segment with off[s] <= p
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (off[mid] <= p) lo = mid; else hi = mid - 1;
+// Element p (0 <= p < total) of the concatenated segment lists of a row:
+// from the LDS copy when the row's candidates fit there, else from HBM.
+struct RowLists {
+  const uint2* glob;      // row's list area (segment s at s * seg_len)
+  const uint2* cache;     // LDS copy in list order, or nullptr
+  const uint32_t* off;    // segment offsets in the concatenation (LDS)
+  int segs;
+  int64_t seg_len;
+  __device__ __forceinline__ uint2 at(uint32_t p) const {
+    if (cache) return cache[p];
+    int lo = 0, hi = segs - 1;  // last segment with off[s] <= p
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    return glob[(int64_t)lo * seg_len + (p - off[lo])];
   }
-  return row_lists[(int64_t)lo * seg_len + (p - off[lo])];
-}
+};
+
+constexpr int kRefineCache = 10240;  // (u, index) pairs kept in LDS (80 KB)
 
 __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
     int64_t n, int64_t kk, int segs, int64_t seg_len,
@@ -207,30 +249,35 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
   __shared__ uint32_t thr[2];
   __shared__ uint32_t h[kHistBins];
   __shared__ uint32_t off[65];
+  __shared__ uint2 cache[kRefineCache];
   const int row = blockIdx.x;
-  const uint2* rl = lists + (int64_t)row * n;
 
   find_threshold_bin<kRefineThreads>(hist + (int64_t)row * kHistBins,
                                      (uint32_t)kk, scratch, thr);
   const uint32_t b1 = thr[0];
   const uint32_t need1 = (uint32_t)kk - thr[1];
 
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int s = 0; s < segs; ++s) {
-      off[s] = run;
-      run += seg_cnt[(int64_t)row * segs + s];
-    }
-    off[segs] = run;
+  if (threadIdx.x < 64) {  // segment offsets: one wave-wide scan (segs <= 64)
+    const uint32_t c = threadIdx.x < segs ? seg_cnt[(int64_t)row * segs + threadIdx.x] : 0u;
+    const uint32_t inc = wave_inclusive_scan(c);
+    if (threadIdx.x < segs) off[threadIdx.x] = inc - c;
+    if (threadIdx.x == 63) off[segs] = inc;
   }
   __syncthreads();
   const uint32_t total = off[segs];
+
+  RowLists rl{lists + (int64_t)row * n, nullptr, off, segs, seg_len};
+  if (total <= (uint32_t)kRefineCache) {
+    for (uint32_t p = threadIdx.x; p < total; p += kRefineThreads) cache[p] = rl.at(p);
+    __syncthreads();
+    rl.cache = cache;
+  }
 
   // pass 2: bits 20..10 of the candidates in bin b1
   for (int i = threadIdx.x; i < kHistBins; i += kRefineThreads) h[i] = 0;
   __syncthreads();
   for (uint32_t p = threadIdx.x; p < total; p += kRefineThreads) {
-    const uint2 e = list_at(rl, off, segs, seg_len, p);
+    const uint2 e = rl.at(p);
     if ((e.x >> 21) == b1) atomicAdd(&h[(e.x >> 10) & 2047u], 1u);
   }
   __syncthreads();
@@ -243,7 +290,7 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
   for (int i = threadIdx.x; i < kHistBins; i += kRefineThreads) h[i] = 0;
   __syncthreads();
   for (uint32_t p = threadIdx.x; p < total; p += kRefineThreads) {
-    const uint2 e = list_at(rl, off, segs, seg_len, p);
+    const uint2 e = rl.at(p);
     if ((e.x >> 10) == pre2) atomicAdd(&h[e.x & 1023u], 1u);
   }
   __syncthreads();
@@ -257,7 +304,7 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
   for (uint32_t base = 0; base < total; base += kRefineThreads) {
     const uint32_t p = base + threadIdx.x;
     uint2 e = make_uint2(0u, 0u);
-    if (p < total) e = list_at(rl, off, segs, seg_len, p);
+    if (p < total) e = rl.at(p);
     const bool valid = p < total;
     const bool is_tie = valid && e.x == T;
     const bool is_gt = valid && e.x > T;
@@ -321,6 +368,7 @@ hipError_t launch_zero_u32(uint32_t* p, int64_t words, hipStream_t stream) {
   const int grid = (int)std::min<int64_t>((words + 255) / 256, 1024);
   hipLaunchKernelGGL(zero_u32_kernel, dim3(grid), dim3(256), 0, stream, p,
                      words);
+  trace_mark(stream);
   return hipGetLastError();
 }
 
@@ -332,6 +380,7 @@ hipError_t launch_topk(const float* scores, const TopkPlan& plan, int32_t* idx,
     const int grid = (int)std::min<int64_t>((total + 255) / 256, 4096);
     hipLaunchKernelGGL(iota_rows_kernel, dim3(grid), dim3(256), 0, stream, idx,
                        plan.rows, plan.n);
+    trace_mark(stream);
     return hipGetLastError();
   }
   unsigned char* base = static_cast<unsigned char*>(ws);
@@ -345,15 +394,19 @@ hipError_t launch_topk(const float* scores, const TopkPlan& plan, int32_t* idx,
     hipLaunchKernelGGL(topk_hist_kernel, dim3(plan.segs, plan.rows),
                        dim3(kFilterThreads), 0, stream, scores, plan.n,
                        plan.seg_len, hist);
+    trace_mark(stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
+  const int vec4 = (plan.n % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0) ? 1 : 0;
   hipLaunchKernelGGL(topk_filter_kernel, dim3(plan.segs, plan.rows),
                      dim3(kFilterThreads), 0, stream, scores, plan.n, plan.kk,
-                     plan.segs, plan.seg_len, hist, lists, cnt);
+                     plan.segs, plan.seg_len, hist, lists, cnt, vec4);
+  trace_mark(stream);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(topk_refine_kernel, dim3(plan.rows), dim3(kRefineThreads),
                      0, stream, plan.n, plan.kk, plan.segs, plan.seg_len, hist,
                      lists, cnt, idx);
+  trace_mark(stream);
   return hipGetLastError();
 }
 
