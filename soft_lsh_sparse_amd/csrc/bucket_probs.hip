@@ -25,6 +25,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "soft_prob.hpp"
 
 #include <algorithm>
 
@@ -75,14 +76,9 @@ __global__ __launch_bounds__(256) void bucket_probs_kernel(
   for (int pair = threadIdx.x; pair < npairs; pair += blockDim.x) {
     const int j = pair / ncols, c = pair % ncols;
     const float* q = qs + j * d;
-    double z = 0.0;
-    for (int i = 0; i < d; ++i) z += (double)q[i] * (double)rs[i * ncols + c];
-    // sigma(+2z/tau) for bit 1 and sigma(-2z/tau) for bit 0, both formed
-    // from a = exp(-2|z|/tau) <= 1 so nothing overflows.
-    const double a = exp(-fabs(z) * two_over_tau);
-    const double big = 1.0 / (1.0 + a), small = a / (1.0 + a);
-    w1[pair] = z > 0.0 ? big : (z < 0.0 ? small : 0.5);
-    w0[pair] = z > 0.0 ? small : (z < 0.0 ? big : 0.5);
+    const double z = proj_dot([&](int i) { return q[i]; },
+                              [&](int i) { return rs[i * ncols + c]; }, d);
+    bit_weights(z, two_over_tau, w1[pair], w0[pair]);
   }
   __syncthreads();
 
@@ -95,10 +91,13 @@ __global__ __launch_bounds__(256) void bucket_probs_kernel(
     const int rem = e % per_bucket;
     const int ll = rem / G, j = rem % G;
     const int base = j * ncols + ll * P;
-    double p = 1.0;
-    for (int jj = 0; jj < P; ++jj)
-      p *= ((u >> jj) & 1) ? w1[base + jj] : w0[base + jj];
-    out[((int64_t)u * L + l0 + ll) * G + j] = (float)p;
+    double a1[kMaxBits], a0[kMaxBits];
+#pragma unroll
+    for (int jj = 0; jj < kMaxBits; ++jj) {
+      a1[jj] = jj < P ? w1[base + jj] : 1.0;
+      a0[jj] = jj < P ? w0[base + jj] : 1.0;
+    }
+    out[((int64_t)u * L + l0 + ll) * G + j] = (float)bucket_prob(u, a1, a0, P);
   }
 }
 

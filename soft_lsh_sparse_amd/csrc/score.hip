@@ -8,10 +8,15 @@
 // bucket, summed over the L tables and weighted by the key's value norm.
 //
 // One block owns one (batch, KV head) and a contiguous range of keys. It
-// stages that head's probability table [2^P][L][G] (float32) in LDS, then
-// streams the bucket-id rows (L bytes per key, coalesced across lanes) and
-// the value norms from HBM. Each id byte is looked up once for the whole GQA
-// group: the G probabilities of the group sit in one 16-byte LDS slot.
+// holds that head's probability table [2^P][L][G] (float32) in LDS: either
+// copied from a table computed by the bucket kernel, or built in place from
+// the queries and hyperplanes (the decode path; identical arithmetic, see
+// soft_prob.hpp), while the first bucket-id rows are already in flight. It
+// then streams the bucket-id rows (L bytes per key, coalesced across lanes)
+// and the value norms from HBM, several iterations ahead in registers so
+// enough bytes are in flight to cover the memory latency. Each id byte is
+// looked up once for the whole GQA group: the G probabilities of the group
+// sit in one 16-byte LDS slot.
 //
 // Bank spread: with the [u][l][G] layout and L a multiple of 16, the LDS bank
 // of slot (u, l) depends only on l mod 16. Lane i walks the tables in the
@@ -29,6 +34,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "soft_prob.hpp"
 
 #include <algorithm>
 
@@ -36,6 +42,7 @@ namespace socket_lsh {
 namespace {
 
 constexpr int kScoreThreads = 512;
+constexpr int kPrefetch = 4;  // iterations of ids kept in flight per thread
 constexpr int64_t kMaxSegForHist = 32768;
 
 // Rotate the NB-byte array held in NW 32-bit words left by r bytes
@@ -74,8 +81,8 @@ __device__ __forceinline__ void lds_load_group(const float* p, float (&o)[G]) {
 }
 
 // Block -> (batch*KV head, key segment), placing all segments of one head
-// on the same XCD (blocks are dealt to the 8 XCDs round-robin) so the head's
-// probability table is fetched into that XCD's L2 once.
+// on the same XCD (blocks are dealt to the 8 XCDs round-robin) so that what
+// they share (the head's table or queries) is fetched into that XCD's L2 once.
 __device__ __forceinline__ bool score_block_coords(int bhkv, int segs, int& bg,
                                                    int& seg) {
   const int total = bhkv * segs;
@@ -88,7 +95,59 @@ __device__ __forceinline__ bool score_block_coords(int bhkv, int segs, int& bg,
   return true;
 }
 
-// Shared tail of both kernels: store the G scores of key n and count them.
+// Table of (batch b, KV head g) into LDS: copied, or built from Q and R.
+// `scratch` holds G*L*P doubles (the projections) while building.
+template <typename T, int G>
+__device__ void stage_table(float* tab, double* scratch, const float* table,
+                            const typename T::storage* Q,
+                            const typename T::storage* R, double two_over_tau,
+                            int b, int g, int bg, int Hq, int d, int L, int P) {
+  const int tsize = (1 << P) * L * G;
+  if (table != nullptr) {
+    if (tsize % 4 == 0) {  // every head's table then starts 16-byte aligned
+      const float4* src = reinterpret_cast<const float4*>(table + (int64_t)bg * tsize);
+      float4* dst = reinterpret_cast<float4*>(tab);
+      for (int i = threadIdx.x; i < tsize / 4; i += blockDim.x) dst[i] = src[i];
+    } else {
+      for (int i = threadIdx.x; i < tsize; i += blockDim.x)
+        tab[i] = table[(int64_t)bg * tsize + i];
+    }
+    return;
+  }
+  // projections z[j][c] of the group's queries on every hyperplane
+  const int C = L * P;
+  for (int pair = threadIdx.x; pair < G * C; pair += blockDim.x) {
+    const int j = pair / C, c = pair % C;
+    const int64_t qrow = ((int64_t)b * Hq + g * G + j) * d;
+    scratch[pair] = proj_dot([&](int i) { return T::load(Q, qrow + i); },
+                             [&](int i) { return T::load(R, (int64_t)i * C + c); }, d);
+  }
+  __syncthreads();
+  // each thread: one (table, head) pair and a power-of-two share of its buckets
+  const int pairs = G * L;
+  const int nb = 1 << P;
+  int groups = 1;
+  while (groups * 2 <= nb && pairs * groups * 2 <= (int)blockDim.x) groups *= 2;
+  const int per = nb / groups;
+  for (int idx = threadIdx.x; idx < pairs * groups; idx += blockDim.x) {
+    const int jl = idx % pairs, q = idx / pairs;
+    const int l = jl / G, j = jl % G;
+    double w1[kMaxBits], w0[kMaxBits];
+#pragma unroll
+    for (int jj = 0; jj < kMaxBits; ++jj) {
+      if (jj < P) {
+        bit_weights(scratch[j * C + l * P + jj], two_over_tau, w1[jj], w0[jj]);
+      } else {
+        w1[jj] = 1.0;
+        w0[jj] = 1.0;
+      }
+    }
+    for (int u = q * per; u < (q + 1) * per; ++u)
+      tab[(u * L + l) * G + j] = (float)bucket_prob(u, w1, w0, P);
+  }
+}
+
+// Shared tail: store the G scores of key n and count them.
 template <int G>
 __device__ __forceinline__ void emit_scores(const float (&acc)[G], float vn,
                                             int64_t n, int64_t n_keys,
@@ -113,108 +172,135 @@ __device__ __forceinline__ void flush_hist(const uint32_t* hloc, uint32_t* hrow)
   }
 }
 
+struct ScoreArgs {
+  const float* table;  // [bhkv][2^P][L][G], or nullptr: build from Q and R
+  const void* Q;
+  const void* R;
+  double two_over_tau;
+  const uint8_t* ids;
+  const float* vnorm;
+  int Hq, Hkv, bhkv, d, P, segs;
+  int64_t n_keys, stride, seg_len;
+  float* scores;
+  uint32_t* hist;
+};
+
 // Fast path: L a multiple of 16 (LW = L/4 words of ids per key).
-template <int G, int LW>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(
-    const float* __restrict__ table, const uint8_t* __restrict__ ids,
-    const float* __restrict__ vnorm, int Hq, int Hkv, int bhkv,
-    int64_t n_keys, int64_t stride, int P, int segs, int64_t seg_len,
-    float* __restrict__ scores, uint32_t* __restrict__ hist) {
+template <typename T, int G, int LW>
+__global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(ScoreArgs a) {
   constexpr int L = LW * 4;
   extern __shared__ __align__(16) float tab[];
   int bg, seg;
-  if (!score_block_coords(bhkv, segs, bg, seg)) return;
-  const int b = bg / Hkv, g = bg % Hkv;
+  if (!score_block_coords(a.bhkv, a.segs, bg, seg)) return;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int P = a.P;
   const int tsize = (1 << P) * L * G;
-  uint32_t* hloc = hist ? reinterpret_cast<uint32_t*>(tab + tsize) : nullptr;
+  float* tail = tab + tsize;  // projections while building, then histogram
 
-  {
-    const float4* src = reinterpret_cast<const float4*>(table + (int64_t)bg * tsize);
-    float4* dst = reinterpret_cast<float4*>(tab);
-    for (int i = threadIdx.x; i < tsize / 4; i += kScoreThreads) dst[i] = src[i];
-    if (hloc)
-      for (int i = threadIdx.x; i < G * kHistBins / 2; i += kScoreThreads) hloc[i] = 0u;
+  const int64_t n0 = seg * a.seg_len;
+  const int64_t n1 = min(a.n_keys, n0 + a.seg_len);
+  const uint8_t* idrow = a.ids + (int64_t)bg * a.stride * L;
+  const float* vrow = a.vnorm + (int64_t)bg * a.stride;
+
+  // first kPrefetch iterations of ids and norms are put in flight before
+  // the table is staged
+  uint4 pf[kPrefetch][LW / 4];
+  float pf_vn[kPrefetch];
+  const int64_t first = n0 + threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < kPrefetch; ++q) {
+    const int64_t n = first + (int64_t)q * kScoreThreads;
+    pf_vn[q] = 0.f;
+    if (n < n1) {
+      const uint4* src = reinterpret_cast<const uint4*>(idrow + n * L);
+#pragma unroll
+      for (int i = 0; i < LW / 4; ++i) pf[q][i] = src[i];
+      pf_vn[q] = vrow[n];
+    }
   }
+
+  stage_table<T, G>(tab, reinterpret_cast<double*>(tail), a.table,
+                    static_cast<const typename T::storage*>(a.Q),
+                    static_cast<const typename T::storage*>(a.R), a.two_over_tau,
+                    b, g, bg, a.Hq, a.d, L, P);
   __syncthreads();
-
-  const int64_t n0 = seg * seg_len;
-  const int64_t n1 = min(n_keys, n0 + seg_len);
-  const uint8_t* idrow = ids + (int64_t)bg * stride * L;
-  const float* vrow = vnorm + (int64_t)bg * stride;
-  float* srow = scores + ((int64_t)b * Hq + (int64_t)g * G) * n_keys;
-  const uint32_t umask = (1u << P) - 1u;  // ids are < 2^P; never index past the table
-
-  // ids and norm of the next key are loaded while the current one is scored
-  uint4 nxt[LW / 4];
-  float nxt_vn = 0.f;
-  int64_t n = n0 + threadIdx.x;
-  if (n < n1) {
-    const uint4* src = reinterpret_cast<const uint4*>(idrow + n * L);
-#pragma unroll
-    for (int i = 0; i < LW / 4; ++i) nxt[i] = src[i];
-    nxt_vn = vrow[n];
+  uint32_t* hloc = a.hist ? reinterpret_cast<uint32_t*>(tail) : nullptr;
+  if (hloc) {
+    for (int i = threadIdx.x; i < G * kHistBins / 2; i += kScoreThreads) hloc[i] = 0u;
+    __syncthreads();
   }
-  for (; n < n1; n += kScoreThreads) {
-    uint32_t w[LW];
+
+  float* srow = a.scores + ((int64_t)b * a.Hq + (int64_t)g * G) * a.n_keys;
+  const uint32_t umask = (1u << P) - 1u;  // ids are < 2^P; never index past the table
+  for (int64_t base = first; base < n1; base += (int64_t)kPrefetch * kScoreThreads) {
 #pragma unroll
-    for (int i = 0; i < LW / 4; ++i) {
-      w[4 * i] = nxt[i].x; w[4 * i + 1] = nxt[i].y;
-      w[4 * i + 2] = nxt[i].z; w[4 * i + 3] = nxt[i].w;
+    for (int q = 0; q < kPrefetch; ++q) {
+      const int64_t n = base + (int64_t)q * kScoreThreads;
+      if (n < n1) {
+        uint32_t w[LW];
+#pragma unroll
+        for (int i = 0; i < LW / 4; ++i) {
+          w[4 * i] = pf[q][i].x; w[4 * i + 1] = pf[q][i].y;
+          w[4 * i + 2] = pf[q][i].z; w[4 * i + 3] = pf[q][i].w;
+        }
+        const float vn = pf_vn[q];
+        const int64_t nn = n + (int64_t)kPrefetch * kScoreThreads;
+        if (nn < n1) {
+          const uint4* src = reinterpret_cast<const uint4*>(idrow + nn * L);
+#pragma unroll
+          for (int i = 0; i < LW / 4; ++i) pf[q][i] = src[i];
+          pf_vn[q] = vrow[nn];
+        }
+        const int r = (int)(n & 15);
+        rotate_bytes<LW>(w, r);
+        float acc[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) acc[j] = 0.f;
+#pragma unroll
+        for (int t = 0; t < L; ++t) {
+          const uint32_t u = (w[t >> 2] >> ((t & 3) * 8)) & umask;
+          const int l = (t + r) & (L - 1);
+          float pr[G];
+          lds_load_group<G>(tab + ((int)u * L + l) * G, pr);
+#pragma unroll
+          for (int j = 0; j < G; ++j) acc[j] += pr[j];
+        }
+        emit_scores<G>(acc, vn, n, a.n_keys, srow, hloc);
+      }
     }
-    const float vn = nxt_vn;
-    const int64_t n2 = n + kScoreThreads;
-    if (n2 < n1) {
-      const uint4* src = reinterpret_cast<const uint4*>(idrow + n2 * L);
-#pragma unroll
-      for (int i = 0; i < LW / 4; ++i) nxt[i] = src[i];
-      nxt_vn = vrow[n2];
-    }
-    const int r = (int)(n & 15);
-    rotate_bytes<LW>(w, r);
-    float acc[G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) acc[j] = 0.f;
-#pragma unroll
-    for (int t = 0; t < L; ++t) {
-      const uint32_t u = (w[t >> 2] >> ((t & 3) * 8)) & umask;
-      const int l = (t + r) & (L - 1);
-      float pr[G];
-      lds_load_group<G>(tab + ((int)u * L + l) * G, pr);
-#pragma unroll
-      for (int j = 0; j < G; ++j) acc[j] += pr[j];
-    }
-    emit_scores<G>(acc, vn, n, n_keys, srow, hloc);
   }
   if (hloc) {
     __syncthreads();
-    flush_hist<G>(hloc, hist + ((int64_t)b * Hq + (int64_t)g * G) * kHistBins);
+    flush_hist<G>(hloc, a.hist + ((int64_t)b * a.Hq + (int64_t)g * G) * kHistBins);
   }
 }
 
 // General path: any L (no bank rotation, byte loads of the ids).
-template <int G>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel_generic(
-    const float* __restrict__ table, const uint8_t* __restrict__ ids,
-    const float* __restrict__ vnorm, int Hq, int Hkv, int bhkv,
-    int64_t n_keys, int64_t stride, int L, int P, int segs, int64_t seg_len,
-    float* __restrict__ scores, uint32_t* __restrict__ hist) {
+template <typename T, int G>
+__global__ __launch_bounds__(kScoreThreads) void score_kernel_generic(ScoreArgs a, int L) {
   extern __shared__ __align__(16) float tab[];
   int bg, seg;
-  if (!score_block_coords(bhkv, segs, bg, seg)) return;
-  const int b = bg / Hkv, g = bg % Hkv;
+  if (!score_block_coords(a.bhkv, a.segs, bg, seg)) return;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int P = a.P;
   const int tsize = (1 << P) * L * G;
-  uint32_t* hloc = hist ? reinterpret_cast<uint32_t*>(tab + tsize) : nullptr;
-  for (int i = threadIdx.x; i < tsize; i += kScoreThreads)
-    tab[i] = table[(int64_t)bg * tsize + i];
-  if (hloc)
-    for (int i = threadIdx.x; i < G * kHistBins / 2; i += kScoreThreads) hloc[i] = 0u;
+  float* tail = tab + tsize;
+  stage_table<T, G>(tab, reinterpret_cast<double*>(tail), a.table,
+                    static_cast<const typename T::storage*>(a.Q),
+                    static_cast<const typename T::storage*>(a.R), a.two_over_tau,
+                    b, g, bg, a.Hq, a.d, L, P);
   __syncthreads();
+  uint32_t* hloc = a.hist ? reinterpret_cast<uint32_t*>(tail) : nullptr;
+  if (hloc) {
+    for (int i = threadIdx.x; i < G * kHistBins / 2; i += kScoreThreads) hloc[i] = 0u;
+    __syncthreads();
+  }
 
-  const int64_t n0 = seg * seg_len;
-  const int64_t n1 = min(n_keys, n0 + seg_len);
-  const uint8_t* idrow = ids + (int64_t)bg * stride * L;
-  const float* vrow = vnorm + (int64_t)bg * stride;
-  float* srow = scores + ((int64_t)b * Hq + (int64_t)g * G) * n_keys;
+  const int64_t n0 = seg * a.seg_len;
+  const int64_t n1 = min(a.n_keys, n0 + a.seg_len);
+  const uint8_t* idrow = a.ids + (int64_t)bg * a.stride * L;
+  const float* vrow = a.vnorm + (int64_t)bg * a.stride;
+  float* srow = a.scores + ((int64_t)b * a.Hq + (int64_t)g * G) * a.n_keys;
   for (int64_t n = n0 + threadIdx.x; n < n1; n += kScoreThreads) {
     float acc[G];
 #pragma unroll
@@ -227,101 +313,112 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_generic(
 #pragma unroll
       for (int j = 0; j < G; ++j) acc[j] += pr[j];
     }
-    emit_scores<G>(acc, vrow[n], n, n_keys, srow, hloc);
+    emit_scores<G>(acc, vrow[n], n, a.n_keys, srow, hloc);
   }
   if (hloc) {
     __syncthreads();
-    flush_hist<G>(hloc, hist + ((int64_t)b * Hq + (int64_t)g * G) * kHistBins);
+    flush_hist<G>(hloc, a.hist + ((int64_t)b * a.Hq + (int64_t)g * G) * kHistBins);
   }
 }
 
-template <int G>
-hipError_t launch_score_g(const float* table, const uint8_t* ids,
-                          const float* vnorm, int B, int Hq, int Hkv,
-                          int64_t n_keys, int64_t stride, int L, int P,
-                          float* scores, uint32_t* hist, hipStream_t stream) {
-  const int bhkv = B * Hkv;
-  const size_t lds = score_lds_bytes(L, P, G, hist != nullptr);
+template <typename T, int G>
+void set_lds_attributes() {
+  static bool done = false;
+  if (done) return;
+  const int max_lds = (int)kLdsBytesPerCU;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_rot<T, G, 8>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_rot<T, G, 16>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_rot<T, G, 4>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_generic<T, G>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+  done = true;
+}
+
+template <typename T, int G>
+hipError_t launch_score_g(ScoreArgs a, int L, int B, hipStream_t stream) {
+  const size_t lds = score_lds_bytes(L, a.P, G, a.hist != nullptr, a.table == nullptr);
   // blocks resident per CU as limited by the 160 KB of LDS
-  const int per_cu = (int)std::max<size_t>(1, std::min<size_t>(2, (160 * 1024) / lds));
+  const int per_cu = (int)std::max<size_t>(1, std::min<size_t>(2, kLdsBytesPerCU / lds));
   const int64_t target = (int64_t)256 * per_cu;
-  int64_t segs = (target + bhkv - 1) / bhkv;
+  const int64_t n_keys = a.n_keys;
+  int64_t segs = (target + a.bhkv - 1) / a.bhkv;
   segs = std::max<int64_t>(1, std::min<int64_t>(segs, (n_keys + 2047) / 2048));
-  if (hist) segs = std::max<int64_t>(segs, (n_keys + kMaxSegForHist - 1) / kMaxSegForHist);
+  if (a.hist) segs = std::max<int64_t>(segs, (n_keys + kMaxSegForHist - 1) / kMaxSegForHist);
   int64_t seg_len = (n_keys + segs - 1) / segs;
   seg_len = (seg_len + 1023) / 1024 * 1024;
-  if (hist && seg_len > kMaxSegForHist) seg_len = kMaxSegForHist;
+  if (a.hist && seg_len > kMaxSegForHist) seg_len = kMaxSegForHist;
   segs = (n_keys + seg_len - 1) / seg_len;
-  const int total = (int)(bhkv * segs);
+  a.segs = (int)segs;
+  a.seg_len = seg_len;
+  const int total = (int)(a.bhkv * segs);
   const int grid = ((total + 7) / 8) * 8;
-  static bool attr_set = false;
-  if (!attr_set) {
-    // allow up to the full 160 KB of LDS for the staged table
-    const int max_lds = 160 * 1024;
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_rot<G, 8>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_rot<G, 16>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_rot<G, 4>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_generic<G>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-    attr_set = true;
-  }
-  const bool aligned = (reinterpret_cast<uintptr_t>(ids) % 16 == 0) &&
-                       ((stride * L) % 16 == 0);
+  set_lds_attributes<T, G>();
+  const bool aligned = (reinterpret_cast<uintptr_t>(a.ids) % 16 == 0) &&
+                       ((a.stride * L) % 16 == 0);
   if (aligned && L == 32) {
-    hipLaunchKernelGGL((score_kernel_rot<G, 8>), dim3(grid), dim3(kScoreThreads),
-                       lds, stream, table, ids, vnorm, Hq, Hkv, bhkv, n_keys,
-                       stride, P, (int)segs, seg_len, scores, hist);
-    trace_mark(stream);
+    hipLaunchKernelGGL((score_kernel_rot<T, G, 8>), dim3(grid), dim3(kScoreThreads),
+                       lds, stream, a);
   } else if (aligned && L == 64) {
-    hipLaunchKernelGGL((score_kernel_rot<G, 16>), dim3(grid), dim3(kScoreThreads),
-                       lds, stream, table, ids, vnorm, Hq, Hkv, bhkv, n_keys,
-                       stride, P, (int)segs, seg_len, scores, hist);
-    trace_mark(stream);
+    hipLaunchKernelGGL((score_kernel_rot<T, G, 16>), dim3(grid), dim3(kScoreThreads),
+                       lds, stream, a);
   } else if (aligned && L == 16) {
-    hipLaunchKernelGGL((score_kernel_rot<G, 4>), dim3(grid), dim3(kScoreThreads),
-                       lds, stream, table, ids, vnorm, Hq, Hkv, bhkv, n_keys,
-                       stride, P, (int)segs, seg_len, scores, hist);
-    trace_mark(stream);
+    hipLaunchKernelGGL((score_kernel_rot<T, G, 4>), dim3(grid), dim3(kScoreThreads),
+                       lds, stream, a);
   } else {
-    hipLaunchKernelGGL((score_kernel_generic<G>), dim3(grid), dim3(kScoreThreads),
-                       lds, stream, table, ids, vnorm, Hq, Hkv, bhkv, n_keys,
-                       stride, L, P, (int)segs, seg_len, scores, hist);
-    trace_mark(stream);
+    hipLaunchKernelGGL((score_kernel_generic<T, G>), dim3(grid), dim3(kScoreThreads),
+                       lds, stream, a, L);
   }
+  trace_mark(stream);
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_score_t(ScoreArgs a, int L, int B, hipStream_t stream) {
+  switch (a.Hq / a.Hkv) {
+    case 1: return launch_score_g<T, 1>(a, L, B, stream);
+    case 2: return launch_score_g<T, 2>(a, L, B, stream);
+    case 4: return launch_score_g<T, 4>(a, L, B, stream);
+    case 8: return launch_score_g<T, 8>(a, L, B, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
-size_t score_lds_bytes(int L, int P, int G, bool with_hist) {
-  return (size_t)(1 << P) * L * G * sizeof(float) +
-         (with_hist ? (size_t)G * kHistBins / 2 * sizeof(uint32_t) : 0);
+size_t score_lds_bytes(int L, int P, int G, bool with_hist, bool build_table) {
+  const size_t table = (size_t)(1 << P) * L * G * sizeof(float);
+  size_t tail = with_hist ? (size_t)G * kHistBins / 2 * sizeof(uint32_t) : 0;
+  if (build_table) tail = std::max(tail, (size_t)G * L * P * sizeof(double));
+  return table + tail;
 }
 
-hipError_t launch_score(const float* table, const uint8_t* ids,
+hipError_t launch_score(const float* table, const void* Q, const void* R,
+                        bool bf16, float tau, int d, const uint8_t* ids,
                         const float* vnorm, int B, int Hq, int Hkv,
                         int64_t n_keys, int64_t stride, int L, int P,
                         float* scores, uint32_t* hist, hipStream_t stream) {
   if (n_keys == 0) return hipSuccess;
-  switch (Hq / Hkv) {
-    case 1:
-      return launch_score_g<1>(table, ids, vnorm, B, Hq, Hkv, n_keys, stride,
-                               L, P, scores, hist, stream);
-    case 2:
-      return launch_score_g<2>(table, ids, vnorm, B, Hq, Hkv, n_keys, stride,
-                               L, P, scores, hist, stream);
-    case 4:
-      return launch_score_g<4>(table, ids, vnorm, B, Hq, Hkv, n_keys, stride,
-                               L, P, scores, hist, stream);
-    case 8:
-      return launch_score_g<8>(table, ids, vnorm, B, Hq, Hkv, n_keys, stride,
-                               L, P, scores, hist, stream);
-    default:
-      return hipErrorInvalidValue;
-  }
+  ScoreArgs a{};
+  a.table = table;
+  a.Q = Q;
+  a.R = R;
+  a.two_over_tau = 2.0 / (double)tau;
+  a.ids = ids;
+  a.vnorm = vnorm;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.bhkv = B * Hkv;
+  a.d = d;
+  a.P = P;
+  a.n_keys = n_keys;
+  a.stride = stride;
+  a.scores = scores;
+  a.hist = hist;
+  if (bf16) return launch_score_t<BF16>(a, L, B, stream);
+  return launch_score_t<F32>(a, L, B, stream);
 }
 
 }  // namespace socket_lsh

@@ -36,7 +36,7 @@
 namespace socket_lsh {
 namespace {
 
-constexpr int kFilterThreads = 256;
+constexpr int kFilterThreads = 1024;
 constexpr int kRefineThreads = 1024;
 constexpr int kFilterUnroll = 4;  // 16-byte loads per thread per iteration
 
@@ -298,24 +298,42 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
   const uint32_t T = (pre2 << 10) | thr[0];
   const uint32_t ties = need2 - thr[1];  // keys equal to T still to take
 
-  // final pass, in index order
+  // final pass, in index order: each thread takes 4 consecutive list entries
   int32_t* o = idx + (int64_t)row * kk;
   uint32_t run_tie = 0, run_out = 0;
-  for (uint32_t base = 0; base < total; base += kRefineThreads) {
-    const uint32_t p = base + threadIdx.x;
-    uint2 e = make_uint2(0u, 0u);
-    if (p < total) e = rl.at(p);
-    const bool valid = p < total;
-    const bool is_tie = valid && e.x == T;
-    const bool is_gt = valid && e.x > T;
+  for (uint32_t base = 0; base < total; base += 4 * kRefineThreads) {
+    uint2 e[4];
+    uint32_t n_tie = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t p = base + threadIdx.x * 4 + i;
+      e[i] = p < total ? rl.at(p) : make_uint2(0u, 0u);
+      if (p < total && e[i].x == T) ++n_tie;
+    }
     uint32_t tie_tot;
-    const uint32_t tie_pre = block_exclusive_scan<kRefineThreads>(
-        is_tie ? 1u : 0u, scratch, &tie_tot);
-    const bool sel = is_gt || (is_tie && run_tie + tie_pre < ties);
+    uint32_t tie_rank = run_tie + block_exclusive_scan<kRefineThreads>(n_tie, scratch, &tie_tot);
+    bool sel[4];
+    uint32_t n_sel = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t p = base + threadIdx.x * 4 + i;
+      const bool valid = p < total;
+      sel[i] = valid && e[i].x > T;
+      if (valid && e[i].x == T) {
+        sel[i] = tie_rank < ties;
+        ++tie_rank;
+      }
+      n_sel += sel[i] ? 1u : 0u;
+    }
     uint32_t sel_tot;
-    const uint32_t pos = block_exclusive_scan<kRefineThreads>(
-        sel ? 1u : 0u, scratch, &sel_tot);
-    if (sel && run_out + pos < (uint32_t)kk) o[run_out + pos] = (int32_t)e.y;
+    uint32_t pos = run_out + block_exclusive_scan<kRefineThreads>(n_sel, scratch, &sel_tot);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (sel[i]) {
+        if (pos < (uint32_t)kk) o[pos] = (int32_t)e[i].y;
+        ++pos;
+      }
+    }
     run_tie += tie_tot;
     run_out += sel_tot;
   }
@@ -343,9 +361,11 @@ TopkPlan plan_topk(int rows, int64_t n, int64_t k) {
   p.rows = rows;
   p.n = n;
   p.kk = k < n ? k : n;
-  int64_t segs = (n + 8191) / 8192;
-  const int64_t want = (1024 + rows - 1) / rows;
-  if (segs < want) segs = std::min<int64_t>(want, (n + 2047) / 2048);
+  // segments of up to 32K scores (16K per filter iteration of 1024 threads);
+  // more, shorter segments when there are too few rows to fill the chip
+  int64_t segs = (n + 32767) / 32768;
+  const int64_t want = (256 + rows - 1) / rows;
+  if (segs < want) segs = std::min<int64_t>(want, (n + 4095) / 4096);
   segs = std::max<int64_t>(1, std::min<int64_t>(segs, 64));
   int64_t seg_len = (n + segs - 1) / segs;
   seg_len = (seg_len + 255) / 256 * 256;

@@ -427,3 +427,22 @@ def test_decode_edge_sizes(N, k):
             assert torch.equal(out[0, h], V[0, h // 2, 0])
     if k >= N:
         assert torch.equal(idx.cpu(), torch.arange(N, dtype=torch.int32).expand(1, 4, N))
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_32k", "tiny_fp32_1k"])
+def test_decode_scores_equal_stage_pipeline_bit_for_bit(name):
+    """The decode path builds each head's probability table inside the score
+    kernel; it must equal the standalone table + score stages exactly."""
+    w = W.WORKLOADS[name]
+    log(f"decode vs stages {w.name}")
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=5)
+    ids, vn = S.hash_keys(K, V, R, w.L, w.P)
+    sc = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=DEV)
+    idx = torch.empty((w.B, w.Hq, w.kk), dtype=torch.int32, device=DEV)
+    S.decode(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, idx_out=idx, scores_out=sc)
+    table = S.bucket_probs(Q, R, w.Hkv, w.L, w.P, w.tau)
+    sc2 = S.score(table, ids, vn, w.Hq)
+    idx2 = S.topk(sc2, w.k)
+    torch.cuda.synchronize()
+    assert torch.equal(sc, sc2)
+    assert torch.equal(idx, idx2)
