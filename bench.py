@@ -61,15 +61,17 @@ def algorithmic_bytes(w):
 
 
 def decode_kernel_names(w):
-    """Kernels socket_decode enqueues for this workload, in order. The score
-    kernel builds the first top-k histogram itself when the table plus the
-    packed histogram fit the 160 KB of LDS (true for every workload here)."""
+    """Kernels socket_decode enqueues for this workload, in order (mirrors the
+    library's choice: the score kernel builds the first top-k histogram
+    itself, cleared by the bucket kernel, when the probability table plus the
+    packed histogram fit the 160 KB of LDS)."""
+    table = (2 ** w.P) * w.L * w.G * 4
+    fused = w.kk < w.N and table + w.G * 1024 * 4 <= 160 * 1024
     names = ["bucket_probs_kernel", "score_kernel"]
     if w.kk >= w.N:
-        names += ["iota_rows_kernel"]
+        names.append("iota_rows_kernel")
     else:
-        lds = (2 ** w.P) * w.L * w.G * 4 + w.G * 1024 * 4
-        if lds > 160 * 1024:
+        if not fused:
             names += ["zero_u32_kernel", "topk_hist_kernel"]
         names += ["topk_filter_kernel", "topk_refine_kernel"]
     return names + ["sparse_attn_kernel", "attn_merge_kernel"]

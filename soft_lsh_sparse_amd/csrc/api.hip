@@ -190,6 +190,8 @@ socket_status socket_bucket_probs(const void* Q, const void* R,
     return fail(SOCKET_ERR_INVALID_ARGUMENT, "tau must be finite and > 0");
   if (!Q || !R || !table)
     return fail(SOCKET_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (!aligned16(R))
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "R must be 16-byte aligned");
   hipError_t err = launch_bucket_probs(Q, R, dtype == SOCKET_DTYPE_BF16, B, Hq,
                                        Hkv, d, L, P, tau, table, nullptr, 0,
                                        static_cast<hipStream_t>(stream));
@@ -211,9 +213,9 @@ socket_status socket_score(const float* table, const uint8_t* ids,
     return fail(SOCKET_ERR_INVALID_ARGUMENT, "null pointer argument");
   if (!aligned16(table))
     return fail(SOCKET_ERR_INVALID_ARGUMENT, "table must be 16-byte aligned");
-  hipError_t err = launch_score(table, nullptr, nullptr, false, 1.0f, 0, ids, vnorm,
-                                B, Hq, Hkv, n_keys, head_stride_rows, L, P, scores,
-                                nullptr, static_cast<hipStream_t>(stream));
+  hipError_t err = launch_score(table, ids, vnorm, B, Hq, Hkv, n_keys,
+                                head_stride_rows, L, P, scores, nullptr,
+                                static_cast<hipStream_t>(stream));
   return from_hip(err, "socket_score launch");
 }
 
@@ -321,8 +323,8 @@ socket_status decode_impl(const void* Q, const void* K, const void* V,
     return fail(SOCKET_ERR_UNSUPPORTED, "head_stride_rows must be < 2^31");
   if (!Q || !K || !V || !R || !ids || !vnorm || !out)
     return fail(SOCKET_ERR_INVALID_ARGUMENT, "null pointer argument");
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V))
-    return fail(SOCKET_ERR_INVALID_ARGUMENT, "Q, K and V must be 16-byte aligned");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(R))
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "Q, K, V and R must be 16-byte aligned");
   const DecodeLayout lay = decode_layout(B, Hq, Hkv, d, n_keys, L, P, k);
   if (!workspace || workspace_bytes < lay.total)
     return fail(SOCKET_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu",
@@ -346,28 +348,18 @@ socket_status decode_impl(const void* Q, const void* K, const void* V,
   float* partial = reinterpret_cast<float*>(ws + lay.attn_off);
   const bool bf16 = dtype == SOCKET_DTYPE_BF16;
 
-  // The score kernel builds each head's probability table in LDS (no
-  // separate table kernel) and the first radix histogram of the top-k, when
-  // its LDS has room for them; the histogram is cleared just before.
-  const int G = Hq / Hkv;
+  // The score kernel builds the first radix histogram of the top-k when its
+  // LDS has room next to the table; the bucket kernel clears it beforehand.
   const int64_t kk = k < n_keys ? k : n_keys;
-  const bool build = score_lds_bytes(L, P, G, false, true) <= kLdsBytesPerCU;
   const bool fused_hist =
-      kk < n_keys && score_lds_bytes(L, P, G, true, build) <= kLdsBytesPerCU;
+      kk < n_keys && score_lds_bytes(L, P, Hq / Hkv, true) <= kLdsBytesPerCU;
   uint32_t* hist = reinterpret_cast<uint32_t*>(tws + lay.topk.hist_off);
-  hipError_t err = hipSuccess;
-  if (!build) {
-    err = launch_bucket_probs(Q, R, bf16, B, Hq, Hkv, d, L, P, tau, table,
-                              nullptr, 0, s);
-    if (err != hipSuccess) return from_hip(err, "socket_decode: bucket_probs");
-  }
-  if (fused_hist) {
-    err = launch_zero_u32(hist, (int64_t)B * Hq * kHistBins, s);
-    if (err != hipSuccess) return from_hip(err, "socket_decode: clear");
-  }
-  err = launch_score(build ? nullptr : table, Q, R, bf16, tau, d, ids, vnorm, B,
-                     Hq, Hkv, n_keys, head_stride_rows, L, P, scores,
-                     fused_hist ? hist : nullptr, s);
+  hipError_t err = launch_bucket_probs(
+      Q, R, bf16, B, Hq, Hkv, d, L, P, tau, table, fused_hist ? hist : nullptr,
+      fused_hist ? (int64_t)B * Hq * kHistBins : 0, s);
+  if (err != hipSuccess) return from_hip(err, "socket_decode: bucket_probs");
+  err = launch_score(table, ids, vnorm, B, Hq, Hkv, n_keys, head_stride_rows, L, P,
+                     scores, fused_hist ? hist : nullptr, s);
   if (err != hipSuccess) return from_hip(err, "socket_decode: score");
   err = launch_topk(scores, lay.topk, idx, tws, fused_hist, s);
   if (err != hipSuccess) return from_hip(err, "socket_decode: topk");

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void bucket_probs_kernel(
     int P, double two_over_tau, int tables_per_block,
     float* __restrict__ table, uint32_t* __restrict__ zero_ptr,
     int64_t zero_words) {
-  extern __shared__ double smem[];
+  extern __shared__ double zs[];  // [G][nl*P] projections, then weights
   const int G = Hq / Hkv;
   const int bg = blockIdx.x;  // b * Hkv + g
   const int b = bg / Hkv, g = bg % Hkv;
@@ -47,11 +47,6 @@ __global__ __launch_bounds__(256) void bucket_probs_kernel(
   const int nl = min(tables_per_block, L - l0);
   const int C = L * P;
   const int ncols = nl * P;
-  const int npairs = G * ncols;
-  double* w1 = smem;                    // weight of bit value 1, [G][ncols]
-  double* w0 = w1 + npairs;             // weight of bit value 0
-  float* qs = reinterpret_cast<float*>(w0 + npairs);  // [G][d]
-  float* rs = qs + G * d;                             // [d][ncols]
 
   // Optional clearing of per-call counters (spread over all blocks).
   if (zero_ptr != nullptr) {
@@ -62,26 +57,16 @@ __global__ __launch_bounds__(256) void bucket_probs_kernel(
       zero_ptr[i] = 0u;
   }
 
-  // Stage the group's queries and this block's hyperplane columns in LDS
-  // (all loads issued together, coalesced along d and along the columns).
-  const int64_t q0 = ((int64_t)b * Hq + g * G) * d;
-  for (int i = threadIdx.x; i < G * d; i += blockDim.x) qs[i] = T::load(Q, q0 + i);
-  for (int i = threadIdx.x; i < d * ncols; i += blockDim.x) {
-    const int r = i / ncols, c = i % ncols;
-    rs[i] = T::load(R, (int64_t)r * C + l0 * P + c);
-  }
+  block_projections<T>(Q, ((int64_t)b * Hq + g * G) * d, R, C, l0 * P, ncols, d, G, zs);
+  __syncthreads();
+  double* w1s = zs + G * ncols;  // bit weights, computed once per column
+  double* w0s = w1s + G * ncols;
+  for (int i = threadIdx.x; i < G * ncols; i += blockDim.x)
+    bit_weights(zs[i], two_over_tau, w1s[i], w0s[i]);
   __syncthreads();
 
-  // z[j][c] = q_{g*G+j} . R[:, l0*P + c] in float64 (bf16/f32 products are exact)
-  for (int pair = threadIdx.x; pair < npairs; pair += blockDim.x) {
-    const int j = pair / ncols, c = pair % ncols;
-    const float* q = qs + j * d;
-    const double z = proj_dot([&](int i) { return q[i]; },
-                              [&](int i) { return rs[i * ncols + c]; }, d);
-    bit_weights(z, two_over_tau, w1[pair], w0[pair]);
-  }
-  __syncthreads();
-
+  // one thread per (bucket, table, head): consecutive threads write
+  // consecutive (table, head) slots of one bucket row
   const int nbuckets = 1 << P;
   const int per_bucket = nl * G;
   const int total = nbuckets * per_bucket;
@@ -90,14 +75,17 @@ __global__ __launch_bounds__(256) void bucket_probs_kernel(
     const int u = e / per_bucket;
     const int rem = e % per_bucket;
     const int ll = rem / G, j = rem % G;
-    const int base = j * ncols + ll * P;
-    double a1[kMaxBits], a0[kMaxBits];
+    double w1[kMaxBits], w0[kMaxBits];
 #pragma unroll
     for (int jj = 0; jj < kMaxBits; ++jj) {
-      a1[jj] = jj < P ? w1[base + jj] : 1.0;
-      a0[jj] = jj < P ? w0[base + jj] : 1.0;
+      w1[jj] = 1.0;
+      w0[jj] = 1.0;
+      if (jj < P) {
+        w1[jj] = w1s[j * ncols + ll * P + jj];
+        w0[jj] = w0s[j * ncols + ll * P + jj];
+      }
     }
-    out[((int64_t)u * L + l0 + ll) * G + j] = (float)bucket_prob(u, a1, a0, P);
+    out[((int64_t)u * L + l0 + ll) * G + j] = (float)bucket_prob(u, w1, w0);
   }
 }
 
@@ -109,17 +97,11 @@ hipError_t launch_bucket_probs(const void* Q, const void* R, bool bf16, int B,
                                int64_t zero_words, hipStream_t stream) {
   const int G = Hq / Hkv;
   const int bhkv = B * Hkv;
-  // enough blocks to cover the chip; LDS per block: float64 weights plus the
-  // staged queries and hyperplane columns
-  auto lds_bytes = [&](int tpb) {
-    return (size_t)tpb * P * G * 2 * sizeof(double) + (size_t)G * d * sizeof(float) +
-           (size_t)d * tpb * P * sizeof(float);
-  };
+  // enough blocks to cover the chip; LDS per block: the float64 projections
   int tpb = (int)(((int64_t)L * bhkv + 511) / 512);
   tpb = std::max(1, std::min(tpb, L));
-  while (tpb > 1 && lds_bytes(tpb) > 48 * 1024) --tpb;
   const int nchunks = (L + tpb - 1) / tpb;
-  const size_t shmem = lds_bytes(tpb);
+  const size_t shmem = (size_t)3 * G * tpb * P * sizeof(double);
   const double two_over_tau = 2.0 / (double)tau;
   dim3 grid(bhkv, nchunks);
   if (bf16)

@@ -42,19 +42,16 @@ hipError_t launch_bucket_probs(const void* Q, const void* R, bool bf16, int B,
                                int64_t zero_words, hipStream_t stream);
 
 // ------------------------------------------------------------------ score
-// table: [B*Hkv, 2^P, L, G] from launch_bucket_probs, or nullptr to build
-// each head's table inside the score kernel from Q, R and tau (same values).
+// table: [B*Hkv, 2^P, L, G] from launch_bucket_probs.
 // hist (optional): [B*Hq, 2048] first-digit histograms, accumulated with
 // atomics; must be zero on entry.
-hipError_t launch_score(const float* table, const void* Q, const void* R,
-                        bool bf16, float tau, int d, const uint8_t* ids,
-                        const float* vnorm, int B, int Hq, int Hkv,
-                        int64_t n_keys, int64_t stride, int L, int P,
-                        float* scores, uint32_t* hist, hipStream_t stream);
+hipError_t launch_score(const float* table, const uint8_t* ids, const float* vnorm,
+                        int B, int Hq, int Hkv, int64_t n_keys, int64_t stride,
+                        int L, int P, float* scores, uint32_t* hist,
+                        hipStream_t stream);
 // LDS bytes one score block needs: the probability table, plus the packed
-// first-digit histogram when fused, or the projection scratch when the
-// table is built in place (the two share the space after the table).
-size_t score_lds_bytes(int L, int P, int G, bool with_hist, bool build_table);
+// first-digit histogram when fused.
+size_t score_lds_bytes(int L, int P, int G, bool with_hist);
 constexpr size_t kLdsBytesPerCU = 160 * 1024;
 
 // ------------------------------------------------------------------ top-k

@@ -8,23 +8,21 @@
 // bucket, summed over the L tables and weighted by the key's value norm.
 //
 // One block owns one (batch, KV head) and a contiguous range of keys. It
-// holds that head's probability table [2^P][L][G] (float32) in LDS: either
-// copied from a table computed by the bucket kernel, or built in place from
-// the queries and hyperplanes (the decode path; identical arithmetic, see
-// soft_prob.hpp), while the first bucket-id rows are already in flight. It
-// then streams the bucket-id rows (L bytes per key, coalesced across lanes)
-// and the value norms from HBM, several iterations ahead in registers so
-// enough bytes are in flight to cover the memory latency. Each id byte is
-// looked up once for the whole GQA group: the G probabilities of the group
-// sit in one 16-byte LDS slot.
+// copies that head's probability table [2^P][L][G] (float32, from the bucket
+// kernel) into LDS, then streams the bucket-id rows (L bytes per key,
+// coalesced across lanes) and the value norms from HBM, several iterations
+// ahead in registers so that enough bytes are in flight to cover the memory
+// latency. Each id byte is looked up once for the whole GQA group: the G
+// probabilities of the group sit in one 16-byte LDS slot.
 //
 // Bank spread: with the [u][l][G] layout and L a multiple of 16, the LDS bank
 // of slot (u, l) depends only on l mod 16. Lane i walks the tables in the
 // rotated order l = (t + n) mod L for its key n (n mod 16 = i mod 16), so the
-// 16 lanes served together hit 16 different bank groups whatever buckets the
-// keys fall in. The rotation is applied to the id bytes in registers once
-// per key. The L probabilities are summed in float32 in that fixed order and
-// multiplied by the value norm.
+// lanes served together hit different bank groups whatever buckets the keys
+// fall in. The rotation is applied to the id bytes in registers once per
+// key; the slot offset of step t is a per-lane base (two candidates, before
+// and after the wrap) plus a compile-time immediate. The L probabilities are
+// summed in float32 in that fixed order and multiplied by the value norm.
 //
 // Optionally the kernel also counts every score in a 2048-bin histogram of
 // the top 11 bits of its order key (the first pass of the top-k radix
@@ -34,7 +32,6 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
-#include "soft_prob.hpp"
 
 #include <algorithm>
 
@@ -81,8 +78,8 @@ __device__ __forceinline__ void lds_load_group(const float* p, float (&o)[G]) {
 }
 
 // Block -> (batch*KV head, key segment), placing all segments of one head
-// on the same XCD (blocks are dealt to the 8 XCDs round-robin) so that what
-// they share (the head's table or queries) is fetched into that XCD's L2 once.
+// on the same XCD (blocks are dealt to the 8 XCDs round-robin) so the head's
+// probability table is fetched into that XCD's L2 once.
 __device__ __forceinline__ bool score_block_coords(int bhkv, int segs, int& bg,
                                                    int& seg) {
   const int total = bhkv * segs;
@@ -95,56 +92,21 @@ __device__ __forceinline__ bool score_block_coords(int bhkv, int segs, int& bg,
   return true;
 }
 
-// Table of (batch b, KV head g) into LDS: copied, or built from Q and R.
-// `scratch` holds G*L*P doubles (the projections) while building.
-template <typename T, int G>
-__device__ void stage_table(float* tab, double* scratch, const float* table,
-                            const typename T::storage* Q,
-                            const typename T::storage* R, double two_over_tau,
-                            int b, int g, int bg, int Hq, int d, int L, int P) {
+// The table of batch*KV head bg into LDS, and the packed histogram cleared.
+template <int G>
+__device__ __forceinline__ void stage_table(float* tab, const float* table, int bg,
+                                            int L, int P, uint32_t* hloc) {
   const int tsize = (1 << P) * L * G;
-  if (table != nullptr) {
-    if (tsize % 4 == 0) {  // every head's table then starts 16-byte aligned
-      const float4* src = reinterpret_cast<const float4*>(table + (int64_t)bg * tsize);
-      float4* dst = reinterpret_cast<float4*>(tab);
-      for (int i = threadIdx.x; i < tsize / 4; i += blockDim.x) dst[i] = src[i];
-    } else {
-      for (int i = threadIdx.x; i < tsize; i += blockDim.x)
-        tab[i] = table[(int64_t)bg * tsize + i];
-    }
-    return;
+  if (tsize % 4 == 0) {  // every head's table then starts 16-byte aligned
+    const float4* src = reinterpret_cast<const float4*>(table + (int64_t)bg * tsize);
+    float4* dst = reinterpret_cast<float4*>(tab);
+    for (int i = threadIdx.x; i < tsize / 4; i += blockDim.x) dst[i] = src[i];
+  } else {
+    for (int i = threadIdx.x; i < tsize; i += blockDim.x)
+      tab[i] = table[(int64_t)bg * tsize + i];
   }
-  // projections z[j][c] of the group's queries on every hyperplane
-  const int C = L * P;
-  for (int pair = threadIdx.x; pair < G * C; pair += blockDim.x) {
-    const int j = pair / C, c = pair % C;
-    const int64_t qrow = ((int64_t)b * Hq + g * G + j) * d;
-    scratch[pair] = proj_dot([&](int i) { return T::load(Q, qrow + i); },
-                             [&](int i) { return T::load(R, (int64_t)i * C + c); }, d);
-  }
-  __syncthreads();
-  // each thread: one (table, head) pair and a power-of-two share of its buckets
-  const int pairs = G * L;
-  const int nb = 1 << P;
-  int groups = 1;
-  while (groups * 2 <= nb && pairs * groups * 2 <= (int)blockDim.x) groups *= 2;
-  const int per = nb / groups;
-  for (int idx = threadIdx.x; idx < pairs * groups; idx += blockDim.x) {
-    const int jl = idx % pairs, q = idx / pairs;
-    const int l = jl / G, j = jl % G;
-    double w1[kMaxBits], w0[kMaxBits];
-#pragma unroll
-    for (int jj = 0; jj < kMaxBits; ++jj) {
-      if (jj < P) {
-        bit_weights(scratch[j * C + l * P + jj], two_over_tau, w1[jj], w0[jj]);
-      } else {
-        w1[jj] = 1.0;
-        w0[jj] = 1.0;
-      }
-    }
-    for (int u = q * per; u < (q + 1) * per; ++u)
-      tab[(u * L + l) * G + j] = (float)bucket_prob(u, w1, w0, P);
-  }
+  if (hloc)
+    for (int i = threadIdx.x; i < G * kHistBins / 2; i += blockDim.x) hloc[i] = 0u;
 }
 
 // Shared tail: store the G scores of key n and count them.
@@ -173,20 +135,17 @@ __device__ __forceinline__ void flush_hist(const uint32_t* hloc, uint32_t* hrow)
 }
 
 struct ScoreArgs {
-  const float* table;  // [bhkv][2^P][L][G], or nullptr: build from Q and R
-  const void* Q;
-  const void* R;
-  double two_over_tau;
+  const float* table;  // [bhkv][2^P][L][G]
   const uint8_t* ids;
   const float* vnorm;
-  int Hq, Hkv, bhkv, d, P, segs;
+  int Hq, Hkv, bhkv, P, segs;
   int64_t n_keys, stride, seg_len;
   float* scores;
   uint32_t* hist;
 };
 
 // Fast path: L a multiple of 16 (LW = L/4 words of ids per key).
-template <typename T, int G, int LW>
+template <int G, int LW>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(ScoreArgs a) {
   constexpr int L = LW * 4;
   extern __shared__ __align__(16) float tab[];
@@ -195,15 +154,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(ScoreArgs a) {
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int P = a.P;
   const int tsize = (1 << P) * L * G;
-  float* tail = tab + tsize;  // projections while building, then histogram
+  uint32_t* hloc = a.hist ? reinterpret_cast<uint32_t*>(tab + tsize) : nullptr;
 
   const int64_t n0 = seg * a.seg_len;
   const int64_t n1 = min(a.n_keys, n0 + a.seg_len);
   const uint8_t* idrow = a.ids + (int64_t)bg * a.stride * L;
   const float* vrow = a.vnorm + (int64_t)bg * a.stride;
 
-  // first kPrefetch iterations of ids and norms are put in flight before
-  // the table is staged
+  // the first kPrefetch iterations of ids and norms go in flight before the
+  // table is staged
   uint4 pf[kPrefetch][LW / 4];
   float pf_vn[kPrefetch];
   const int64_t first = n0 + threadIdx.x;
@@ -218,24 +177,19 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(ScoreArgs a) {
       pf_vn[q] = vrow[n];
     }
   }
-
-  stage_table<T, G>(tab, reinterpret_cast<double*>(tail), a.table,
-                    static_cast<const typename T::storage*>(a.Q),
-                    static_cast<const typename T::storage*>(a.R), a.two_over_tau,
-                    b, g, bg, a.Hq, a.d, L, P);
+  stage_table<G>(tab, a.table, bg, L, P, hloc);
   __syncthreads();
-  uint32_t* hloc = a.hist ? reinterpret_cast<uint32_t*>(tail) : nullptr;
-  if (hloc) {
-    for (int i = threadIdx.x; i < G * kHistBins / 2; i += kScoreThreads) hloc[i] = 0u;
-    __syncthreads();
-  }
 
   float* srow = a.scores + ((int64_t)b * a.Hq + (int64_t)g * G) * a.n_keys;
-  const uint32_t umask = (1u << P) - 1u;  // ids are < 2^P; never index past the table
-  for (int64_t base = first; base < n1; base += (int64_t)kPrefetch * kScoreThreads) {
+  // n0 and the thread stride are multiples of 16, so every key of this
+  // thread has the same rotation r and the same two slot bases
+  const int r = (int)(first & 15);
+  const int base_nowrap = r * G;        // slot offset of step t: t*G + base
+  const int base_wrap = (r - L) * G;    // ... once t + r >= L
+  for (int64_t bn = first; bn < n1; bn += (int64_t)kPrefetch * kScoreThreads) {
 #pragma unroll
     for (int q = 0; q < kPrefetch; ++q) {
-      const int64_t n = base + (int64_t)q * kScoreThreads;
+      const int64_t n = bn + (int64_t)q * kScoreThreads;
       if (n < n1) {
         uint32_t w[LW];
 #pragma unroll
@@ -251,17 +205,18 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(ScoreArgs a) {
           for (int i = 0; i < LW / 4; ++i) pf[q][i] = src[i];
           pf_vn[q] = vrow[nn];
         }
-        const int r = (int)(n & 15);
         rotate_bytes<LW>(w, r);
         float acc[G];
 #pragma unroll
         for (int j = 0; j < G; ++j) acc[j] = 0.f;
 #pragma unroll
         for (int t = 0; t < L; ++t) {
-          const uint32_t u = (w[t >> 2] >> ((t & 3) * 8)) & umask;
-          const int l = (t + r) & (L - 1);
+          // P bits of byte t: ids are < 2^P, so this never leaves the table
+          const uint32_t u = __builtin_amdgcn_ubfe(w[t >> 2], (t & 3) * 8, P);
+          const int base = (t + 15 < L) ? base_nowrap
+                                        : (t + r < L ? base_nowrap : base_wrap);
           float pr[G];
-          lds_load_group<G>(tab + ((int)u * L + l) * G, pr);
+          lds_load_group<G>(tab + (int)u * (L * G) + base + t * G, pr);
 #pragma unroll
           for (int j = 0; j < G; ++j) acc[j] += pr[j];
         }
@@ -276,7 +231,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(ScoreArgs a) {
 }
 
 // General path: any L (no bank rotation, byte loads of the ids).
-template <typename T, int G>
+template <int G>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel_generic(ScoreArgs a, int L) {
   extern __shared__ __align__(16) float tab[];
   int bg, seg;
@@ -284,17 +239,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_generic(ScoreArgs 
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int P = a.P;
   const int tsize = (1 << P) * L * G;
-  float* tail = tab + tsize;
-  stage_table<T, G>(tab, reinterpret_cast<double*>(tail), a.table,
-                    static_cast<const typename T::storage*>(a.Q),
-                    static_cast<const typename T::storage*>(a.R), a.two_over_tau,
-                    b, g, bg, a.Hq, a.d, L, P);
+  uint32_t* hloc = a.hist ? reinterpret_cast<uint32_t*>(tab + tsize) : nullptr;
+  stage_table<G>(tab, a.table, bg, L, P, hloc);
   __syncthreads();
-  uint32_t* hloc = a.hist ? reinterpret_cast<uint32_t*>(tail) : nullptr;
-  if (hloc) {
-    for (int i = threadIdx.x; i < G * kHistBins / 2; i += kScoreThreads) hloc[i] = 0u;
-    __syncthreads();
-  }
 
   const int64_t n0 = seg * a.seg_len;
   const int64_t n1 = min(a.n_keys, n0 + a.seg_len);
@@ -321,25 +268,25 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_generic(ScoreArgs 
   }
 }
 
-template <typename T, int G>
+template <int G>
 void set_lds_attributes() {
   static bool done = false;
   if (done) return;
   const int max_lds = (int)kLdsBytesPerCU;
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_rot<T, G, 8>),
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_rot<G, 8>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_rot<T, G, 16>),
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_rot<G, 16>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_rot<T, G, 4>),
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_rot<G, 4>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_generic<T, G>),
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_generic<G>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
   done = true;
 }
 
-template <typename T, int G>
-hipError_t launch_score_g(ScoreArgs a, int L, int B, hipStream_t stream) {
-  const size_t lds = score_lds_bytes(L, a.P, G, a.hist != nullptr, a.table == nullptr);
+template <int G>
+hipError_t launch_score_g(ScoreArgs a, int L, hipStream_t stream) {
+  const size_t lds = score_lds_bytes(L, a.P, G, a.hist != nullptr);
   // blocks resident per CU as limited by the 160 KB of LDS
   const int per_cu = (int)std::max<size_t>(1, std::min<size_t>(2, kLdsBytesPerCU / lds));
   const int64_t target = (int64_t)256 * per_cu;
@@ -355,70 +302,57 @@ hipError_t launch_score_g(ScoreArgs a, int L, int B, hipStream_t stream) {
   a.seg_len = seg_len;
   const int total = (int)(a.bhkv * segs);
   const int grid = ((total + 7) / 8) * 8;
-  set_lds_attributes<T, G>();
+  set_lds_attributes<G>();
   const bool aligned = (reinterpret_cast<uintptr_t>(a.ids) % 16 == 0) &&
                        ((a.stride * L) % 16 == 0);
   if (aligned && L == 32) {
-    hipLaunchKernelGGL((score_kernel_rot<T, G, 8>), dim3(grid), dim3(kScoreThreads),
-                       lds, stream, a);
+    hipLaunchKernelGGL((score_kernel_rot<G, 8>), dim3(grid), dim3(kScoreThreads), lds,
+                       stream, a);
   } else if (aligned && L == 64) {
-    hipLaunchKernelGGL((score_kernel_rot<T, G, 16>), dim3(grid), dim3(kScoreThreads),
-                       lds, stream, a);
+    hipLaunchKernelGGL((score_kernel_rot<G, 16>), dim3(grid), dim3(kScoreThreads), lds,
+                       stream, a);
   } else if (aligned && L == 16) {
-    hipLaunchKernelGGL((score_kernel_rot<T, G, 4>), dim3(grid), dim3(kScoreThreads),
-                       lds, stream, a);
+    hipLaunchKernelGGL((score_kernel_rot<G, 4>), dim3(grid), dim3(kScoreThreads), lds,
+                       stream, a);
   } else {
-    hipLaunchKernelGGL((score_kernel_generic<T, G>), dim3(grid), dim3(kScoreThreads),
-                       lds, stream, a, L);
+    hipLaunchKernelGGL((score_kernel_generic<G>), dim3(grid), dim3(kScoreThreads), lds,
+                       stream, a, L);
   }
   trace_mark(stream);
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_score_t(ScoreArgs a, int L, int B, hipStream_t stream) {
-  switch (a.Hq / a.Hkv) {
-    case 1: return launch_score_g<T, 1>(a, L, B, stream);
-    case 2: return launch_score_g<T, 2>(a, L, B, stream);
-    case 4: return launch_score_g<T, 4>(a, L, B, stream);
-    case 8: return launch_score_g<T, 8>(a, L, B, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
-
 }  // namespace
 
-size_t score_lds_bytes(int L, int P, int G, bool with_hist, bool build_table) {
-  const size_t table = (size_t)(1 << P) * L * G * sizeof(float);
-  size_t tail = with_hist ? (size_t)G * kHistBins / 2 * sizeof(uint32_t) : 0;
-  if (build_table) tail = std::max(tail, (size_t)G * L * P * sizeof(double));
-  return table + tail;
+size_t score_lds_bytes(int L, int P, int G, bool with_hist) {
+  return (size_t)(1 << P) * L * G * sizeof(float) +
+         (with_hist ? (size_t)G * kHistBins / 2 * sizeof(uint32_t) : 0);
 }
 
-hipError_t launch_score(const float* table, const void* Q, const void* R,
-                        bool bf16, float tau, int d, const uint8_t* ids,
-                        const float* vnorm, int B, int Hq, int Hkv,
-                        int64_t n_keys, int64_t stride, int L, int P,
-                        float* scores, uint32_t* hist, hipStream_t stream) {
+hipError_t launch_score(const float* table, const uint8_t* ids, const float* vnorm,
+                        int B, int Hq, int Hkv, int64_t n_keys, int64_t stride,
+                        int L, int P, float* scores, uint32_t* hist,
+                        hipStream_t stream) {
   if (n_keys == 0) return hipSuccess;
   ScoreArgs a{};
   a.table = table;
-  a.Q = Q;
-  a.R = R;
-  a.two_over_tau = 2.0 / (double)tau;
   a.ids = ids;
   a.vnorm = vnorm;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.bhkv = B * Hkv;
-  a.d = d;
   a.P = P;
   a.n_keys = n_keys;
   a.stride = stride;
   a.scores = scores;
   a.hist = hist;
-  if (bf16) return launch_score_t<BF16>(a, L, B, stream);
-  return launch_score_t<F32>(a, L, B, stream);
+  switch (Hq / Hkv) {
+    case 1: return launch_score_g<1>(a, L, stream);
+    case 2: return launch_score_g<2>(a, L, stream);
+    case 4: return launch_score_g<4>(a, L, stream);
+    case 8: return launch_score_g<8>(a, L, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace socket_lsh

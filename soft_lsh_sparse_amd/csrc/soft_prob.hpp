@@ -1,6 +1,5 @@
-// Soft bucket probabilities, shared by the standalone table kernel and the
-// score kernel that builds its table in LDS (both must produce bit-identical
-// tables).
+// Soft bucket probabilities: projections, per-bit weights and bucket
+// products of the table kernel.
 //
 // Soft assignment of SOCKET (page "Resumen Técnico: SOCKET - Estimador de
 // Núcleo de Colisión Suave para Atención Escasa", section "Mecanismo Central:
@@ -18,16 +17,83 @@ namespace socket_lsh {
 
 constexpr int kMaxBits = 8;
 
-// z = sum_i q_i r_i in float64 (two interleaved partial sums, then added).
-// bf16 and f32 products are exact in float64.
-template <class QF, class RF>
-__device__ __forceinline__ double proj_dot(QF q, RF r, int d) {
-  double z0 = 0.0, z1 = 0.0;
-  for (int i = 0; i < d; i += 2) {
-    z0 = fma((double)q(i), (double)r(i), z0);
-    z1 = fma((double)q(i + 1), (double)r(i + 1), z1);
+template <typename T>
+__device__ __forceinline__ void load8(const typename T::storage* p, bool vec, int valid,
+                                      float (&v)[8]);
+
+template <>
+__device__ __forceinline__ void load8<BF16>(const uint16_t* p, bool vec, int valid,
+                                            float (&v)[8]) {
+  if (vec) {
+    unpack8_bf16(*reinterpret_cast<const uint4*>(p), v);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = e < valid ? bf16_bits_to_f32(p[e]) : 0.f;
   }
-  return z0 + z1;
+}
+
+template <>
+__device__ __forceinline__ void load8<F32>(const float* p, bool vec, int valid,
+                                           float (&v)[8]) {
+  if (vec) {
+    unpack4_f32(*reinterpret_cast<const uint4*>(p), v);
+    unpack4_f32(*reinterpret_cast<const uint4*>(p + 4), v + 4);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = e < valid ? p[e] : 0.f;
+  }
+}
+
+// Projections z[j][c] = q_j . R[:, c0 + c] for the G queries of a GQA group
+// (rows q0 + j*d of Q) and the nc hyperplane columns starting at c0, written
+// to out[j * nc + c] (float64). Block-cooperative: each lane accumulates 8
+// consecutive columns over one sixteenth of the d coordinates (ascending,
+// with fma, from 0); the sixteen parts of a column group sit in sixteen
+// adjacent lanes and are combined by a butterfly of additions (the same
+// pairing on every lane). bf16 and f32 products are exact in float64.
+// blockDim.x must be a multiple of 64.
+template <typename T>
+__device__ void block_projections(const typename T::storage* Q, int64_t q0,
+                                  const typename T::storage* R, int C, int c0,
+                                  int nc, int d, int G, double* out) {
+  constexpr int kParts = 16;
+  const int ncg = (nc + 7) / 8;
+  const int items = G * ncg * kParts;
+  const int dp = d / kParts;
+  const bool aligned = (C % 8 == 0) && (c0 % 8 == 0);
+  for (int base = 0; base < items; base += blockDim.x) {
+    const int item = base + threadIdx.x;
+    const bool active = item < items;  // whole groups of 16 lanes
+    const int part = item % kParts;
+    const int cgj = item / kParts;
+    const int cg = cgj % ncg, j = cgj / ncg;
+    const int valid = min(8, nc - cg * 8);
+    double acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+    if (active) {
+      const typename T::storage* qrow = Q + q0 + (int64_t)j * d;
+      const typename T::storage* rcol = R + c0 + cg * 8;
+      const bool vec = aligned && valid == 8;
+      for (int i = part * dp; i < (part + 1) * dp; ++i) {
+        const double qi = (double)T::load(qrow, i);
+        float r[8];
+        load8<T>(rcol + (int64_t)i * C, vec, valid, r);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fma(qi, (double)r[e], acc[e]);
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < kParts; m <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + __shfl_xor(acc[e], m, kWave);
+    }
+    if (active && part == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e < valid) out[j * nc + cg * 8 + e] = acc[e];
+    }
+  }
 }
 
 // Logistic weight of bit value 1 (sigma(+2z/tau)) and of bit value 0
@@ -40,15 +106,21 @@ __device__ __forceinline__ void bit_weights(double z, double two_over_tau,
   w0 = z > 0.0 ? small : (z < 0.0 ? big : 0.5);
 }
 
-// p(u) = prod_{j < P} (bit j of u ? w1[j] : w0[j]), multiplied in ascending
-// bit order in float64.
+// p(u) = prod_{j < P} (bit j of u ? w1[j] : w0[j]) in float64, in the fixed
+// grouping ((bits 0-2) * (bits 3-5)) * (bits 6-7), each group multiplied in
+// ascending bit order; w1[j] = w0[j] = 1 for j >= P.
 __device__ __forceinline__ double bucket_prob(int u, const double (&w1)[kMaxBits],
-                                              const double (&w0)[kMaxBits], int P) {
-  double p = 1.0;
+                                              const double (&w0)[kMaxBits]) {
+  double g[3];
 #pragma unroll
-  for (int j = 0; j < kMaxBits; ++j)
-    if (j < P) p *= ((u >> j) & 1) ? w1[j] : w0[j];
-  return p;
+  for (int k = 0; k < 3; ++k) {
+    double p = 1.0;
+#pragma unroll
+    for (int j = 3 * k; j < 3 * k + 3 && j < kMaxBits; ++j)
+      p *= ((u >> j) & 1) ? w1[j] : w0[j];
+    g[k] = p;
+  }
+  return (g[0] * g[1]) * g[2];
 }
 
 }  // namespace socket_lsh

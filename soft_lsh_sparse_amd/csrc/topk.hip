@@ -36,7 +36,7 @@
 namespace socket_lsh {
 namespace {
 
-constexpr int kFilterThreads = 1024;
+constexpr int kFilterThreads = 256;
 constexpr int kRefineThreads = 1024;
 constexpr int kFilterUnroll = 4;  // 16-byte loads per thread per iteration
 
@@ -361,11 +361,11 @@ TopkPlan plan_topk(int rows, int64_t n, int64_t k) {
   p.rows = rows;
   p.n = n;
   p.kk = k < n ? k : n;
-  // segments of up to 32K scores (16K per filter iteration of 1024 threads);
+  // segments of up to 8K scores (two filter iterations of 256 threads x 16);
   // more, shorter segments when there are too few rows to fill the chip
-  int64_t segs = (n + 32767) / 32768;
-  const int64_t want = (256 + rows - 1) / rows;
-  if (segs < want) segs = std::min<int64_t>(want, (n + 4095) / 4096);
+  int64_t segs = (n + 8191) / 8192;
+  const int64_t want = (1024 + rows - 1) / rows;
+  if (segs < want) segs = std::min<int64_t>(want, (n + 2047) / 2048);
   segs = std::max<int64_t>(1, std::min<int64_t>(segs, 64));
   int64_t seg_len = (n + segs - 1) / segs;
   seg_len = (seg_len + 255) / 256 * 256;
