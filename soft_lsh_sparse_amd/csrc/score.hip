@@ -16,13 +16,14 @@
 // probabilities of the group sit in one 16-byte LDS slot.
 //
 // Bank spread: with the [u][l][G] layout and L a multiple of 16, the LDS bank
-// of slot (u, l) depends only on l mod 16. Lane i walks the tables in the
-// rotated order l = (t + n) mod L for its key n (n mod 16 = i mod 16), so the
-// lanes served together hit different bank groups whatever buckets the keys
-// fall in. The rotation is applied to the id bytes in registers once per
-// key; the slot offset of step t is a per-lane base (two candidates, before
-// and after the wrap) plus a compile-time immediate. The L probabilities are
-// summed in float32 in that fixed order and multiplied by the value norm.
+// group of slot (u, l) depends only on l mod 8 (32 banks of 4 bytes, 16-byte
+// slots). Lane i walks the tables in the rotated order l = (t + n) mod L for
+// its key n (n mod 8 = i mod 8), so the 8 lanes the LDS serves together hit 8
+// different bank groups whatever buckets the keys fall in. The rotation is
+// applied to the id bytes in registers once per key; the slot offset of step
+// t is a per-lane base (two candidates, before and after the wrap) plus a
+// compile-time immediate. The L probabilities are summed in float32 in that
+// fixed order and multiplied by the value norm.
 //
 // Optionally the kernel also counts every score in a 2048-bin histogram of
 // the top 11 bits of its order key (the first pass of the top-k radix
@@ -39,24 +40,33 @@ namespace socket_lsh {
 namespace {
 
 constexpr int kScoreThreads = 512;
-constexpr int kPrefetch = 4;  // iterations of ids kept in flight per thread
+// iterations of ids kept in flight per thread (fewer for 64-byte id rows,
+// which would not fit the registers otherwise)
+template <int LW>
+constexpr int prefetch_depth() { return LW >= 16 ? 2 : 4; }
 constexpr int64_t kMaxSegForHist = 32768;
 
+// v_cndmask_b32 with an explicit lane mask: b where the lane's mask bit is
+// set, a elsewhere. Written out so the compiler keeps one select per word
+// instead of rewriting the rotation below as a dynamically indexed array.
+__device__ __forceinline__ uint32_t select_lanes(uint32_t a, uint32_t b, uint64_t mask) {
+  uint32_t out;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(out) : "v"(a), "v"(b), "s"(mask));
+  return out;
+}
+
 // Rotate the NB-byte array held in NW 32-bit words left by r bytes
-// (0 <= r < 16): byte i of the result is byte (i + r) mod NB of the input.
+// (0 <= r < 8): byte i of the result is byte (i + r) mod NB of the input.
+// One word-select stage (lanes whose bit is set in by_word: r >= 4) and one
+// byte funnel shift per word.
 template <int NW>
-__device__ __forceinline__ void rotate_bytes(uint32_t (&w)[NW], int r) {
-  const int rw = r >> 2, rb = r & 3;
+__device__ __forceinline__ void rotate_bytes(uint32_t (&w)[NW], uint64_t by_word, int rb) {
   uint32_t t[NW];
 #pragma unroll
-  for (int i = 0; i < NW; ++i) t[i] = (rw & 1) ? w[(i + 1) % NW] : w[i];
-#pragma unroll
-  for (int i = 0; i < NW; ++i) w[i] = (rw & 2) ? t[(i + 2) % NW] : t[i];
+  for (int i = 0; i < NW; ++i) t[i] = select_lanes(w[i], w[(i + 1) % NW], by_word);
 #pragma unroll
   for (int i = 0; i < NW; ++i)
-    t[i] = __builtin_amdgcn_alignbyte(w[(i + 1) % NW], w[i], rb);
-#pragma unroll
-  for (int i = 0; i < NW; ++i) w[i] = t[i];
+    w[i] = __builtin_amdgcn_alignbyte(t[(i + 1) % NW], t[i], rb);
 }
 
 template <int G>
@@ -148,6 +158,7 @@ struct ScoreArgs {
 template <int G, int LW>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(ScoreArgs a) {
   constexpr int L = LW * 4;
+  constexpr int kPrefetch = prefetch_depth<LW>();
   extern __shared__ __align__(16) float tab[];
   int bg, seg;
   if (!score_block_coords(a.bhkv, a.segs, bg, seg)) return;
@@ -181,9 +192,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(ScoreArgs a) {
   __syncthreads();
 
   float* srow = a.scores + ((int64_t)b * a.Hq + (int64_t)g * G) * a.n_keys;
-  // n0 and the thread stride are multiples of 16, so every key of this
+  // n0 and the thread stride are multiples of 8, so every key of this
   // thread has the same rotation r and the same two slot bases
-  const int r = (int)(first & 15);
+  const int r = (int)(first & 7);
+  const uint64_t by_word = __ballot(r >= 4);
+  const int rb = r & 3;
   const int base_nowrap = r * G;        // slot offset of step t: t*G + base
   const int base_wrap = (r - L) * G;    // ... once t + r >= L
   for (int64_t bn = first; bn < n1; bn += (int64_t)kPrefetch * kScoreThreads) {
@@ -205,20 +218,18 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(ScoreArgs a) {
           for (int i = 0; i < LW / 4; ++i) pf[q][i] = src[i];
           pf_vn[q] = vrow[nn];
         }
-        rotate_bytes<LW>(w, r);
+        rotate_bytes<LW>(w, by_word, rb);
         float acc[G];
-#pragma unroll
-        for (int j = 0; j < G; ++j) acc[j] = 0.f;
 #pragma unroll
         for (int t = 0; t < L; ++t) {
           // P bits of byte t: ids are < 2^P, so this never leaves the table
           const uint32_t u = __builtin_amdgcn_ubfe(w[t >> 2], (t & 3) * 8, P);
-          const int base = (t + 15 < L) ? base_nowrap
-                                        : (t + r < L ? base_nowrap : base_wrap);
+          const int base = (t + 7 < L) ? base_nowrap
+                                       : (t + r < L ? base_nowrap : base_wrap);
           float pr[G];
           lds_load_group<G>(tab + (int)u * (L * G) + base + t * G, pr);
 #pragma unroll
-          for (int j = 0; j < G; ++j) acc[j] += pr[j];
+          for (int j = 0; j < G; ++j) acc[j] = t == 0 ? pr[j] : acc[j] + pr[j];
         }
         emit_scores<G>(acc, vn, n, a.n_keys, srow, hloc);
       }
