@@ -57,6 +57,7 @@ __device__ void block_projections(const typename T::storage* Q, int64_t q0,
                                   const typename T::storage* R, int C, int c0,
                                   int nc, int d, int G, double* out) {
   constexpr int kParts = 16;
+  constexpr int kMaxSlice = 8;  // d <= 128
   const int ncg = (nc + 7) / 8;
   const int items = G * ncg * kParts;
   const int dp = d / kParts;
@@ -75,12 +76,23 @@ __device__ void block_projections(const typename T::storage* Q, int64_t q0,
       const typename T::storage* qrow = Q + q0 + (int64_t)j * d;
       const typename T::storage* rcol = R + c0 + cg * 8;
       const bool vec = aligned && valid == 8;
-      for (int i = part * dp; i < (part + 1) * dp; ++i) {
-        const double qi = (double)T::load(qrow, i);
-        float r[8];
-        load8<T>(rcol + (int64_t)i * C, vec, valid, r);
+      // all loads of this lane's slice first (dp <= kMaxSlice), then the fmas
+      float qv[kMaxSlice];
+      float rv[kMaxSlice][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fma(qi, (double)r[e], acc[e]);
+      for (int k = 0; k < kMaxSlice; ++k) {
+        if (k < dp) {
+          const int i = part * dp + k;
+          qv[k] = T::load(qrow, i);
+          load8<T>(rcol + (int64_t)i * C, vec, valid, rv[k]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kMaxSlice; ++k) {
+        if (k < dp) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = fma((double)qv[k], (double)rv[k][e], acc[e]);
+        }
       }
     }
 #pragma unroll
