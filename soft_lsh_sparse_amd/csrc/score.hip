@@ -39,12 +39,14 @@
 namespace socket_lsh {
 namespace {
 
-constexpr int kScoreThreads = 512;
-// iterations of ids kept in flight per thread (fewer for 64-byte id rows,
-// which would not fit the registers otherwise)
-template <int LW>
-constexpr int prefetch_depth() { return LW >= 16 ? 2 : 4; }
+constexpr int kScoreThreads = 512;  // generic path
+// Rotated-path blocks: 16 waves, the most one CU holds at <= 128 VGPRs,
+// with two iterations of ids and norms in flight per thread.
+constexpr int kRotThreads = 1024;
+constexpr int kPrefetch = 2;
 constexpr int64_t kMaxSegForHist = 32768;
+// keeps every per-thread byte offset of a segment (key * L, L <= 1024) in 31 bits
+constexpr int64_t kMaxSeg = 1 << 20;
 
 // v_cndmask_b32 with an explicit lane mask: b where the lane's mask bit is
 // set, a elsewhere. Written out so the compiler keeps one select per word
@@ -67,6 +69,20 @@ __device__ __forceinline__ void rotate_bytes(uint32_t (&w)[NW], uint64_t by_word
 #pragma unroll
   for (int i = 0; i < NW; ++i)
     w[i] = __builtin_amdgcn_alignbyte(t[(i + 1) % NW], t[i], rb);
+}
+
+// Ties the next ids to the running sums (empty asm, no instruction): every
+// sum is complete before this point, and the words w[k0 .. k1) cannot be
+// used, hence no lookup of theirs issued, before it. Keeps the compiler
+// from issuing all lookups of a key at once and from deferring the sums,
+// either of which holds one register per looked-up float.
+template <int G, int LW>
+__device__ __forceinline__ void fence_chunk(float (&acc)[G], uint32_t (&w)[LW], int k0,
+                                            int k1) {
+#pragma unroll
+  for (int j = 0; j < G; ++j) asm volatile("" : "+v"(acc[j]), "+v"(w[k0]));
+#pragma unroll
+  for (int k = k0 + 1; k < k1; ++k) asm volatile("" : "+v"(w[k]) : "v"(w[k0]));
 }
 
 template <int G>
@@ -156,9 +172,10 @@ struct ScoreArgs {
 
 // Fast path: L a multiple of 16 (LW = L/4 words of ids per key).
 template <int G, int LW>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(ScoreArgs a) {
+__global__ __launch_bounds__(kRotThreads) void score_kernel_rot(ScoreArgs a) {
+  constexpr int kThreads = kRotThreads;
   constexpr int L = LW * 4;
-  constexpr int kPrefetch = prefetch_depth<LW>();
+  constexpr int kChunk = 64 / G;  // lookups per dependency step (a multiple of 4)
   extern __shared__ __align__(16) float tab[];
   int bg, seg;
   if (!score_block_coords(a.bhkv, a.segs, bg, seg)) return;
@@ -167,56 +184,57 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(ScoreArgs a) {
   const int tsize = (1 << P) * L * G;
   uint32_t* hloc = a.hist ? reinterpret_cast<uint32_t*>(tab + tsize) : nullptr;
 
+  // block-uniform bases of this segment; per-thread offsets stay 32-bit
   const int64_t n0 = seg * a.seg_len;
-  const int64_t n1 = min(a.n_keys, n0 + a.seg_len);
-  const uint8_t* idrow = a.ids + (int64_t)bg * a.stride * L;
-  const float* vrow = a.vnorm + (int64_t)bg * a.stride;
+  const int cnt = (int)(min(a.n_keys, n0 + a.seg_len) - n0);
+  const uint8_t* idseg = a.ids + ((int64_t)bg * a.stride + n0) * L;
+  const float* vseg = a.vnorm + (int64_t)bg * a.stride + n0;
+  float* sseg = a.scores + ((int64_t)b * a.Hq + (int64_t)g * G) * a.n_keys + n0;
 
   // the first kPrefetch iterations of ids and norms go in flight before the
   // table is staged
   uint4 pf[kPrefetch][LW / 4];
   float pf_vn[kPrefetch];
-  const int64_t first = n0 + threadIdx.x;
+  const int first = threadIdx.x;
 #pragma unroll
   for (int q = 0; q < kPrefetch; ++q) {
-    const int64_t n = first + (int64_t)q * kScoreThreads;
+    const int i = first + q * kThreads;
     pf_vn[q] = 0.f;
-    if (n < n1) {
-      const uint4* src = reinterpret_cast<const uint4*>(idrow + n * L);
+    if (i < cnt) {
+      const uint4* src = reinterpret_cast<const uint4*>(idseg + i * L);
 #pragma unroll
-      for (int i = 0; i < LW / 4; ++i) pf[q][i] = src[i];
-      pf_vn[q] = vrow[n];
+      for (int k = 0; k < LW / 4; ++k) pf[q][k] = src[k];
+      pf_vn[q] = vseg[i];
     }
   }
   stage_table<G>(tab, a.table, bg, L, P, hloc);
   __syncthreads();
 
-  float* srow = a.scores + ((int64_t)b * a.Hq + (int64_t)g * G) * a.n_keys;
   // n0 and the thread stride are multiples of 8, so every key of this
-  // thread has the same rotation r and the same two slot bases
-  const int r = (int)(first & 7);
+  // thread has the same rotation r = key index mod 8 and the same two bases
+  const int r = first & 7;
   const uint64_t by_word = __ballot(r >= 4);
   const int rb = r & 3;
   const int base_nowrap = r * G;        // slot offset of step t: t*G + base
   const int base_wrap = (r - L) * G;    // ... once t + r >= L
-  for (int64_t bn = first; bn < n1; bn += (int64_t)kPrefetch * kScoreThreads) {
+  for (int bi = first; bi < cnt; bi += kPrefetch * kThreads) {
 #pragma unroll
     for (int q = 0; q < kPrefetch; ++q) {
-      const int64_t n = bn + (int64_t)q * kScoreThreads;
-      if (n < n1) {
+      const int i = bi + q * kThreads;
+      if (i < cnt) {
         uint32_t w[LW];
 #pragma unroll
-        for (int i = 0; i < LW / 4; ++i) {
-          w[4 * i] = pf[q][i].x; w[4 * i + 1] = pf[q][i].y;
-          w[4 * i + 2] = pf[q][i].z; w[4 * i + 3] = pf[q][i].w;
+        for (int k = 0; k < LW / 4; ++k) {
+          w[4 * k] = pf[q][k].x; w[4 * k + 1] = pf[q][k].y;
+          w[4 * k + 2] = pf[q][k].z; w[4 * k + 3] = pf[q][k].w;
         }
         const float vn = pf_vn[q];
-        const int64_t nn = n + (int64_t)kPrefetch * kScoreThreads;
-        if (nn < n1) {
-          const uint4* src = reinterpret_cast<const uint4*>(idrow + nn * L);
+        const int ii = i + kPrefetch * kThreads;
+        if (ii < cnt) {
+          const uint4* src = reinterpret_cast<const uint4*>(idseg + ii * L);
 #pragma unroll
-          for (int i = 0; i < LW / 4; ++i) pf[q][i] = src[i];
-          pf_vn[q] = vrow[nn];
+          for (int k = 0; k < LW / 4; ++k) pf[q][k] = src[k];
+          pf_vn[q] = vseg[ii];
         }
         rotate_bytes<LW>(w, by_word, rb);
         float acc[G];
@@ -230,8 +248,20 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(ScoreArgs a) {
           lds_load_group<G>(tab + (int)u * (L * G) + base + t * G, pr);
 #pragma unroll
           for (int j = 0; j < G; ++j) acc[j] = t == 0 ? pr[j] : acc[j] + pr[j];
+          // the next kChunk lookups wait for these sums: at most 64 floats
+          // of lookups in flight per lane, which bounds the registers
+          if ((t + 1) % kChunk == 0 && t + 1 < L)
+            fence_chunk<G, LW>(acc, w, (t + 1) / 4, std::min(LW, (t + 1 + kChunk) / 4));
         }
-        emit_scores<G>(acc, vn, n, a.n_keys, srow, hloc);
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          const float sc = vn * acc[j];
+          sseg[(int64_t)j * a.n_keys + i] = sc;
+          if (hloc) {
+            const uint32_t bin = float_order_key(sc) >> 21;
+            atomicAdd(hloc + j * (kHistBins / 2) + (bin >> 1), 1u << ((bin & 1) * 16));
+          }
+        }
       }
     }
   }
@@ -308,6 +338,7 @@ hipError_t launch_score_g(ScoreArgs a, int L, hipStream_t stream) {
   int64_t seg_len = (n_keys + segs - 1) / segs;
   seg_len = (seg_len + 1023) / 1024 * 1024;
   if (a.hist && seg_len > kMaxSegForHist) seg_len = kMaxSegForHist;
+  if (seg_len > kMaxSeg) seg_len = kMaxSeg;
   segs = (n_keys + seg_len - 1) / seg_len;
   a.segs = (int)segs;
   a.seg_len = seg_len;
@@ -317,13 +348,13 @@ hipError_t launch_score_g(ScoreArgs a, int L, hipStream_t stream) {
   const bool aligned = (reinterpret_cast<uintptr_t>(a.ids) % 16 == 0) &&
                        ((a.stride * L) % 16 == 0);
   if (aligned && L == 32) {
-    hipLaunchKernelGGL((score_kernel_rot<G, 8>), dim3(grid), dim3(kScoreThreads), lds,
+    hipLaunchKernelGGL((score_kernel_rot<G, 8>), dim3(grid), dim3(kRotThreads), lds,
                        stream, a);
   } else if (aligned && L == 64) {
-    hipLaunchKernelGGL((score_kernel_rot<G, 16>), dim3(grid), dim3(kScoreThreads), lds,
+    hipLaunchKernelGGL((score_kernel_rot<G, 16>), dim3(grid), dim3(kRotThreads), lds,
                        stream, a);
   } else if (aligned && L == 16) {
-    hipLaunchKernelGGL((score_kernel_rot<G, 4>), dim3(grid), dim3(kScoreThreads), lds,
+    hipLaunchKernelGGL((score_kernel_rot<G, 4>), dim3(grid), dim3(kRotThreads), lds,
                        stream, a);
   } else {
     hipLaunchKernelGGL((score_kernel_generic<G>), dim3(grid), dim3(kScoreThreads), lds,
