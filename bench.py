@@ -181,7 +181,7 @@ def main():
 
     import soft_lsh_sparse_amd as S
     import synthetic as W
-    from soft_lsh_sparse_amd import _lib
+    from soft_lsh_sparse_amd import _lib, profiling
 
     lib = _lib.load()
     dev = torch.device("cuda:0")
@@ -244,15 +244,16 @@ def main():
     step_bytes = algorithmic_bytes(w)
     hbm_frac = step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9)
 
-    # ---- per-kernel times of the same decode: socket_decode_profiled records
-    # a HIP event on the launch stream before the first kernel and after
-    # every kernel (same kernels, same order, same workspace)
+    # ---- per-kernel times of the same decode: socket_decode_profiled
+    # dispatches every kernel with a start and a stop HIP event, recorded by
+    # the dispatch itself on the launch stream (same kernels, same order,
+    # same workspace)
     kernel_ms = {}
     roofline = None
     if not args.skip_stage_timing:
         names = decode_kernel_names(w)
         hip = _hip_runtime()
-        n_ev = len(names) + 1
+        n_ev = 2 * len(names)
         events = [[_hip_event(hip) for _ in range(n_ev)] for _ in range(args.steps)]
         ev_arrays = [(ctypes.c_void_p * n_ev)(*ev) for ev in events]
         prof = lib.socket_decode_profiled
@@ -266,8 +267,8 @@ def main():
             tot = 0.0
             for ev in events:
                 ms = ctypes.c_float()
-                rc = hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(ev[j]),
-                                             ctypes.c_void_p(ev[j + 1]))
+                rc = hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(ev[2 * j]),
+                                             ctypes.c_void_p(ev[2 * j + 1]))
                 if rc != 0:
                     raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
                 tot += ms.value
@@ -277,6 +278,10 @@ def main():
                 hip.hipEventDestroy(ctypes.c_void_p(e))
         kbytes = kernel_bytes(w)
         dom = max(kernel_ms, key=kernel_ms.get)
+        # HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE
+        # summary of this workload; None once the kernel's sources changed
+        traffic = profiling.load_traffic(
+            os.path.join(ROOT, "profiles", f"decode_{w.name}_hbm_traffic.md"), dom)
         achieved = kbytes[dom] / (kernel_ms[dom] * 1e-3) / 1e9
         roofline = {
             "bound": "hbm",
@@ -285,7 +290,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "algorithmic_bytes_per_launch": kbytes[dom],
             "avg_launch_ms": round(kernel_ms[dom], 5),
         }

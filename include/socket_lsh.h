@@ -209,14 +209,17 @@ socket_status socket_decode(const void* Q, const void* K, const void* V,
                             void* stream);
 
 /*
- * socket_decode with per-kernel timing: identical work and results, and in
- * addition events[0] (a hipEvent_t) is recorded on `stream` before the first
- * kernel and events[i] right after the i-th kernel it enqueues, for at most
- * n_events events. Kernel order: bucket table, scores, then the top-k
- * kernels (clear + histogram, unless the score kernel built the histogram
- * itself, then filter and refine; a single index fill when k >= n_keys),
- * then the attention gather and its merge. Unused events are not touched.
- * For profiling tools; events must not be NULL.
+ * socket_decode with per-kernel timing: identical work and results. In
+ * addition the i-th kernel it enqueues (i = 0, 1, ...) is dispatched with
+ * events[2i] and events[2i+1] (hipEvent_t handles created by the caller) as
+ * its start and stop events, which the dispatch records at the start and
+ * end of that kernel's execution, for the first n_events / 2 kernels.
+ * Kernel order: bucket table, scores, then the top-k kernels (clear +
+ * histogram, unless the score kernel built the histogram itself, then
+ * filter and refine; a single index fill when k >= n_keys), then the
+ * attention gather and its merge. Unused events are not touched. For
+ * profiling tools; events must not be NULL and n_events must be >= 2
+ * (else SOCKET_ERR_INVALID_ARGUMENT).
  */
 socket_status socket_decode_profiled(
     const void* Q, const void* K, const void* V, const void* R,

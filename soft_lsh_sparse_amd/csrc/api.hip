@@ -331,15 +331,14 @@ socket_status decode_impl(const void* Q, const void* K, const void* V,
                 lay.total, workspace ? workspace_bytes : (size_t)0);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (events != nullptr && n_events < 1)
-    return fail(SOCKET_ERR_INVALID_ARGUMENT, "n_events must be >= 1 with events");
+  if (events != nullptr && n_events < 2)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "n_events must be >= 2 with events");
   LaunchTrace trace{reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)),
                     events ? n_events : 0, 0};
   struct TraceScope {
     explicit TraceScope(LaunchTrace* t) { g_trace = t; }
     ~TraceScope() { g_trace = nullptr; }
   } scope(events ? &trace : nullptr);
-  trace_mark(s);  // first event: before the first kernel
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   float* table = reinterpret_cast<float*>(ws + lay.table_off);
   float* scores = scores_out ? scores_out : reinterpret_cast<float*>(ws + lay.scores_off);

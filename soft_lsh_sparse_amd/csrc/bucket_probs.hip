@@ -105,15 +105,14 @@ hipError_t launch_bucket_probs(const void* Q, const void* R, bool bf16, int B,
   const double two_over_tau = 2.0 / (double)tau;
   dim3 grid(bhkv, nchunks);
   if (bf16)
-    hipLaunchKernelGGL(bucket_probs_kernel<BF16>, grid, dim3(256), shmem,
+    launch_kernel(bucket_probs_kernel<BF16>, grid, dim3(256), shmem,
                        stream, (const uint16_t*)Q, (const uint16_t*)R, Hq, Hkv,
                        d, L, P, two_over_tau, tpb, table, zero_ptr,
                        zero_words);
   else
-    hipLaunchKernelGGL(bucket_probs_kernel<F32>, grid, dim3(256), shmem,
+    launch_kernel(bucket_probs_kernel<F32>, grid, dim3(256), shmem,
                        stream, (const float*)Q, (const float*)R, Hq, Hkv, d, L,
                        P, two_over_tau, tpb, table, zero_ptr, zero_words);
-  trace_mark(stream);
   return hipGetLastError();
 }
 

@@ -317,10 +317,9 @@ hipError_t launch_bf16_nw(const uint16_t* K, const uint16_t* V,
   // about 8 waves per CU on 256 CUs; each block loops over tiles
   const int64_t cap = (int64_t)256 * 8 / NW;
   const int grid = (int)std::min<int64_t>(n_tiles, cap);
-  hipLaunchKernelGGL((hash_keys_bf16_kernel<D, NW>), dim3(grid), dim3(NW * 64),
+  launch_kernel((hash_keys_bf16_kernel<D, NW>), dim3(grid), dim3(NW * 64),
                      0, stream, K, V, R, n_keys, stride, L, P, ids, vnorm,
                      n_tiles, tph, word_store);
-  trace_mark(stream);
   return hipGetLastError();
 }
 
@@ -375,14 +374,13 @@ hipError_t launch_hash_keys_f32(const float* K, const float* V, const float* R,
   if (total == 0) return hipSuccess;
   const int grid = (int)((total + 255) / 256);
   if (d == 128)
-    hipLaunchKernelGGL(hash_keys_f32_kernel<128>, dim3(grid), dim3(256), 0,
+    launch_kernel(hash_keys_f32_kernel<128>, dim3(grid), dim3(256), 0,
                        stream, K, V, R, n_heads, n_keys, stride, L, P, ids,
                        vnorm);
   else
-    hipLaunchKernelGGL(hash_keys_f32_kernel<64>, dim3(grid), dim3(256), 0,
+    launch_kernel(hash_keys_f32_kernel<64>, dim3(grid), dim3(256), 0,
                        stream, K, V, R, n_heads, n_keys, stride, L, P, ids,
                        vnorm);
-  trace_mark(stream);
   return hipGetLastError();
 }
 

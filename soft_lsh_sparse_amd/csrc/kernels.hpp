@@ -2,24 +2,35 @@
 // arguments were validated by the C-ABI layer and enqueues on `stream`.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace socket_lsh {
 
-// Optional event trace for profiling: when set (by the profiled decode entry
-// point), every launcher records the next event on its stream right after
-// each kernel it enqueues.
+// Optional kernel timing for profiling: while set (by the profiled decode
+// entry point), every launch takes the next two events of the list, which
+// the dispatch itself records at the start and at the end of the kernel's
+// execution (no extra stream packets, so the time between them is the
+// kernel's own duration).
 struct LaunchTrace {
   hipEvent_t* events;
   int n;
   int used;
 };
 extern thread_local LaunchTrace* g_trace;
-inline void trace_mark(hipStream_t stream) {
-  if (g_trace != nullptr && g_trace->used < g_trace->n)
-    (void)hipEventRecord(g_trace->events[g_trace->used++], stream);
+
+// kernel<<<grid, block, lds, stream>>>(args...), timed under a trace.
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                          Args... args) {
+  hipEvent_t start = nullptr, stop = nullptr;
+  if (g_trace != nullptr && g_trace->used + 2 <= g_trace->n) {
+    start = g_trace->events[g_trace->used++];
+    stop = g_trace->events[g_trace->used++];
+  }
+  hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, stream, start, stop, 0u, args...);
 }
 
 // ------------------------------------------------------------- prefill hash

@@ -348,19 +348,18 @@ hipError_t launch_score_g(ScoreArgs a, int L, hipStream_t stream) {
   const bool aligned = (reinterpret_cast<uintptr_t>(a.ids) % 16 == 0) &&
                        ((a.stride * L) % 16 == 0);
   if (aligned && L == 32) {
-    hipLaunchKernelGGL((score_kernel_rot<G, 8>), dim3(grid), dim3(kRotThreads), lds,
+    launch_kernel((score_kernel_rot<G, 8>), dim3(grid), dim3(kRotThreads), lds,
                        stream, a);
   } else if (aligned && L == 64) {
-    hipLaunchKernelGGL((score_kernel_rot<G, 16>), dim3(grid), dim3(kRotThreads), lds,
+    launch_kernel((score_kernel_rot<G, 16>), dim3(grid), dim3(kRotThreads), lds,
                        stream, a);
   } else if (aligned && L == 16) {
-    hipLaunchKernelGGL((score_kernel_rot<G, 4>), dim3(grid), dim3(kRotThreads), lds,
+    launch_kernel((score_kernel_rot<G, 4>), dim3(grid), dim3(kRotThreads), lds,
                        stream, a);
   } else {
-    hipLaunchKernelGGL((score_kernel_generic<G>), dim3(grid), dim3(kScoreThreads), lds,
+    launch_kernel((score_kernel_generic<G>), dim3(grid), dim3(kScoreThreads), lds,
                        stream, a, L);
   }
-  trace_mark(stream);
   return hipGetLastError();
 }
 

@@ -221,16 +221,14 @@ hipError_t launch_attn_t(const void* Q, const void* K, const void* V,
   const int bhkv = plan.B * plan.Hkv;
   const int per_group = G * plan.chunks;
   const int grid = ((bhkv + 7) / 8) * 8 * per_group;
-  hipLaunchKernelGGL((sparse_attn_kernel<T, D, KPW>), dim3(grid),
+  launch_kernel((sparse_attn_kernel<T, D, KPW>), dim3(grid),
                      dim3(kAttnThreads), 0, stream, (const S*)Q, (const S*)K,
                      (const S*)V, plan.Hq, plan.Hkv, bhkv, stride, idx,
                      plan.kk, plan.chunks, partial);
-  trace_mark(stream);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3(plan.B * plan.Hq),
+  launch_kernel((attn_merge_kernel<T, D>), dim3(plan.B * plan.Hq),
                      dim3(D), 0, stream, partial, plan.chunks, (S*)out);
-  trace_mark(stream);
   return hipGetLastError();
 }
 

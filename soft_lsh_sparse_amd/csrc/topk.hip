@@ -386,9 +386,8 @@ TopkPlan plan_topk(int rows, int64_t n, int64_t k) {
 hipError_t launch_zero_u32(uint32_t* p, int64_t words, hipStream_t stream) {
   if (words <= 0) return hipSuccess;
   const int grid = (int)std::min<int64_t>((words + 255) / 256, 1024);
-  hipLaunchKernelGGL(zero_u32_kernel, dim3(grid), dim3(256), 0, stream, p,
+  launch_kernel(zero_u32_kernel, dim3(grid), dim3(256), 0, stream, p,
                      words);
-  trace_mark(stream);
   return hipGetLastError();
 }
 
@@ -398,9 +397,8 @@ hipError_t launch_topk(const float* scores, const TopkPlan& plan, int32_t* idx,
   if (plan.kk == plan.n) {
     const int64_t total = (int64_t)plan.rows * plan.n;
     const int grid = (int)std::min<int64_t>((total + 255) / 256, 4096);
-    hipLaunchKernelGGL(iota_rows_kernel, dim3(grid), dim3(256), 0, stream, idx,
+    launch_kernel(iota_rows_kernel, dim3(grid), dim3(256), 0, stream, idx,
                        plan.rows, plan.n);
-    trace_mark(stream);
     return hipGetLastError();
   }
   unsigned char* base = static_cast<unsigned char*>(ws);
@@ -411,22 +409,19 @@ hipError_t launch_topk(const float* scores, const TopkPlan& plan, int32_t* idx,
   if (!hist_ready) {
     err = launch_zero_u32(hist, (int64_t)plan.rows * kHistBins, stream);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(topk_hist_kernel, dim3(plan.segs, plan.rows),
+    launch_kernel(topk_hist_kernel, dim3(plan.segs, plan.rows),
                        dim3(kFilterThreads), 0, stream, scores, plan.n,
                        plan.seg_len, hist);
-    trace_mark(stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const int vec4 = (plan.n % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0) ? 1 : 0;
-  hipLaunchKernelGGL(topk_filter_kernel, dim3(plan.segs, plan.rows),
+  launch_kernel(topk_filter_kernel, dim3(plan.segs, plan.rows),
                      dim3(kFilterThreads), 0, stream, scores, plan.n, plan.kk,
                      plan.segs, plan.seg_len, hist, lists, cnt, vec4);
-  trace_mark(stream);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(topk_refine_kernel, dim3(plan.rows), dim3(kRefineThreads),
+  launch_kernel(topk_refine_kernel, dim3(plan.rows), dim3(kRefineThreads),
                      0, stream, plan.n, plan.kk, plan.segs, plan.seg_len, hist,
                      lists, cnt, idx);
-  trace_mark(stream);
   return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@ declared in include/socket_lsh.h, and rejects invalid arguments on the host
 before anything is enqueued (fake non-null pointers are never dereferenced
 because validation fails first)."""
 
+import ctypes
 import os
 import re
 
@@ -81,6 +82,16 @@ def _decode(lib, **over):
 def test_decode_rejects_bad_arguments(lib, over, status):
     assert _decode(lib, **over) == status
     assert lib.socket_last_error()
+
+
+def test_decode_profiled_needs_an_event_pair(lib):
+    ws_bytes = lib.socket_decode_workspace_bytes(1, 32, 8, 128, 1024, 32, 8, 64)
+    events = (ctypes.c_void_p * 1)(FAKE)
+    st = lib.socket_decode_profiled(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 32, 8,
+                                    128, 1024, 1024, 32, 8, 0.3, 64, FAKE, None,
+                                    None, FAKE, ws_bytes, None, events, 1)
+    assert st == _lib.SOCKET_ERR_INVALID_ARGUMENT
+    assert b"n_events" in lib.socket_last_error()
 
 
 def test_hash_keys_validation(lib):
