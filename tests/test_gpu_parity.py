@@ -14,7 +14,6 @@ Gates (tolerances follow from the arithmetic of each step):
     float32, with the oracle attending over the GPU's selection.
 """
 
-import math
 import sys
 
 import numpy as np
@@ -323,11 +322,12 @@ def _check_decode(w, seed=0, step=0, sample_rows=None):
             band = np.abs(s_ref[diff] - kth) <= 1e-5 * kth + 1e-30
             assert band.all(), f"selection differs outside the band in row {(b, h)}"
             swaps += diff.size // 2
-        Kg = f64(K[b, g][torch.from_numpy(idx_np[b, h]).long().to(DEV)])
-        Vg = f64(V[b, g][torch.from_numpy(idx_np[b, h]).long().to(DEV)])
-        a = Kg @ Q64[b, h] / math.sqrt(w.d)
-        a = np.exp(a - a.max())
-        ref_out = (a / a.sum()) @ Vg
+        # the oracle attends over the GPU's selection (the gathered rows only)
+        sel_t = torch.from_numpy(idx_np[b, h]).long().to(DEV)
+        Kg = f64(K[b, g][sel_t])[None, None]
+        Vg = f64(V[b, g][sel_t])[None, None]
+        ref_out = O.subset_attention(Q64[b:b + 1, h:h + 1], Kg, Vg,
+                                     np.arange(kk)[None, None], 1)[0, 0]
         tol = 2e-2 if w.dtype == "bf16" else 1e-4
         assert np.max(np.abs(out64[b, h] - ref_out)) <= tol, f"out row {(b, h)}"
     log(f"{w.name}: {len(rows)} rows checked, {swaps} tolerance-band swaps")
