@@ -97,12 +97,23 @@ const char* socket_last_error(void);
  * Bucket ids are exact: the sign of every projection is that of the exact
  * dot product (projections too close to zero for the fast float32 path are
  * re-evaluated in extended precision). n_keys == 0 is a no-op.
+ *
+ * Workspace: socket_hash_keys_workspace_bytes(dtype, n_heads, n_keys, d, L,
+ * P) bytes of device memory, 256-byte aligned (0 bytes, NULL allowed, for
+ * SOCKET_DTYPE_F32). It holds the transposed hyperplanes and the list of
+ * projections settled in extended precision after the main pass; its
+ * contents on entry do not matter. A smaller or misaligned workspace returns
+ * SOCKET_ERR_WORKSPACE. K, V and R must be 16-byte aligned.
  */
+size_t socket_hash_keys_workspace_bytes(socket_dtype dtype, int64_t n_heads,
+                                        int64_t n_keys, int32_t d, int32_t L,
+                                        int32_t P);
 socket_status socket_hash_keys(const void* K, const void* V, const void* R,
                                socket_dtype dtype, int64_t n_heads,
                                int64_t n_keys, int64_t head_stride_rows,
                                int32_t d, int32_t L, int32_t P, uint8_t* ids,
-                               float* vnorm, void* stream);
+                               float* vnorm, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /*
  * Decode stage 1: soft bucket probabilities of the queries.

@@ -29,9 +29,11 @@ SIGNATURES = {
     "socket_version": (c_int32, []),
     "socket_status_string": (c_char_p, [c_int]),
     "socket_last_error": (c_char_p, []),
+    "socket_hash_keys_workspace_bytes": (c_size_t, [c_int, c_int64, c_int64, c_int32,
+                                                    c_int32, c_int32]),
     "socket_hash_keys": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int64,
                                  c_int64, c_int64, c_int32, c_int32, c_int32,
-                                 c_void_p, c_void_p, c_void_p]),
+                                 c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "socket_bucket_probs": (c_int, [c_void_p, c_void_p, c_int, c_int32, c_int32,
                                     c_int32, c_int32, c_int32, c_int32, c_float,
                                     c_void_p, c_void_p]),

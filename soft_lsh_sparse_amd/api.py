@@ -68,10 +68,13 @@ def hash_keys(K: torch.Tensor, V: torch.Tensor, R: torch.Tensor, L: int,
     if tuple(ids.shape) != (*lead, S, L) or tuple(vnorm.shape) != (*lead, S):
         raise ValueError("ids / vnorm do not match K's layout")
     esz = K.element_size()
+    dt = _dtype_code(K)
+    ws_bytes = lib.socket_hash_keys_workspace_bytes(dt, n_heads, n, d, L, P)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=K.device)
     st = lib.socket_hash_keys(_dev(K, "K") + o * d * esz, _dev(V, "V") + o * d * esz,
-                              _dev(R, "R"), _dtype_code(K), n_heads, n, S, d, L, P,
+                              _dev(R, "R"), dt, n_heads, n, S, d, L, P,
                               _dev(ids, "ids") + o * L, _dev(vnorm, "vnorm") + o * 4,
-                              _stream(K))
+                              ws.data_ptr() if ws_bytes else None, ws_bytes, _stream(K))
     check(st, "socket_hash_keys")
     return ids, vnorm
 

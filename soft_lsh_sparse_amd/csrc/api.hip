@@ -42,8 +42,6 @@ bool aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
 socket_status check_dtype(socket_dtype dt) {
   if (dt != SOCKET_DTYPE_F32 && dt != SOCKET_DTYPE_BF16)
     return fail(SOCKET_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dt);
@@ -141,11 +139,21 @@ const char* socket_status_string(socket_status status) {
 
 const char* socket_last_error(void) { return g_last_error.c_str(); }
 
+size_t socket_hash_keys_workspace_bytes(socket_dtype dtype, int64_t n_heads,
+                                        int64_t n_keys, int32_t d, int32_t L,
+                                        int32_t P) {
+  if (dtype != SOCKET_DTYPE_BF16 || n_heads <= 0 || n_keys <= 0 || d <= 0 || L <= 0 ||
+      P <= 0)
+    return 0;
+  return hash_keys_bf16_workspace_bytes(n_heads * n_keys, d, L * P);
+}
+
 socket_status socket_hash_keys(const void* K, const void* V, const void* R,
                                socket_dtype dtype, int64_t n_heads,
                                int64_t n_keys, int64_t head_stride_rows,
                                int32_t d, int32_t L, int32_t P, uint8_t* ids,
-                               float* vnorm, void* stream) {
+                               float* vnorm, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   SOCKET_TRY(check_dtype(dtype));
   SOCKET_TRY(check_d(d));
   SOCKET_TRY(check_lp(L, P));
@@ -162,14 +170,23 @@ socket_status socket_hash_keys(const void* K, const void* V, const void* R,
   if (n_heads == 0 || n_keys == 0) return ok();
   if (!K || !V || !R || !ids || !vnorm)
     return fail(SOCKET_ERR_INVALID_ARGUMENT, "null pointer argument");
-  if (!aligned16(K) || !aligned16(V))
-    return fail(SOCKET_ERR_INVALID_ARGUMENT, "K and V must be 16-byte aligned");
+  if (!aligned16(K) || !aligned16(V) || !aligned16(R))
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "K, V and R must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
-  if (dtype == SOCKET_DTYPE_BF16)
+  if (dtype == SOCKET_DTYPE_BF16) {
+    if (n_heads * ((n_keys + 31) / 32) >= ((int64_t)1 << 31))
+      return fail(SOCKET_ERR_UNSUPPORTED, "bf16 hashing supports < 2^31 tiles of 32 keys");
+    const size_t need = hash_keys_bf16_workspace_bytes(n_heads * n_keys, d, L * P);
+    if (!workspace || workspace_bytes < need ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+      return fail(SOCKET_ERR_WORKSPACE,
+                  "hashing needs %zu workspace bytes at a 256-byte aligned address, got %zu",
+                  need, workspace ? workspace_bytes : (size_t)0);
     err = launch_hash_keys_bf16((const uint16_t*)K, (const uint16_t*)V,
                                 (const uint16_t*)R, n_heads, n_keys,
-                                head_stride_rows, d, L, P, ids, vnorm, s);
+                                head_stride_rows, d, L, P, ids, vnorm, workspace, s);
+  }
   else
     err = launch_hash_keys_f32((const float*)K, (const float*)V,
                                (const float*)R, n_heads, n_keys,

@@ -81,6 +81,48 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// DPP lane permutations: operand modifiers of a VALU move, no LDS round
+// trip (unlike ds_bpermute-based shuffles).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xf, 0xf, false);
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Sum over each aligned group of 16 lanes, returned in every lane of the
+// group: lane pairs (i, i^1), (i, i^2) within quads, then the two quads of
+// each half-row (mirror) and the two half-rows (mirror). Each step adds the
+// same two values in every lane of a pair, so all 16 results are identical.
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141>(v);  // row_half_mirror
+  v += dpp_f32<0x140>(v);  // row_mirror
+  return v;
+}
+
+__device__ __forceinline__ double sum16_f64(double v) {
+  v += dpp_f64<0xB1>(v);
+  v += dpp_f64<0x4E>(v);
+  v += dpp_f64<0x141>(v);
+  v += dpp_f64<0x140>(v);
+  return v;
+}
+
+// The value of lane i ^ 32 (v_permlane32_swap: the two half-waves trade).
+__device__ __forceinline__ uint32_t xor32_u32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (threadIdx.x & 32) ? r[0] : r[1];
+}
+
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
   for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);

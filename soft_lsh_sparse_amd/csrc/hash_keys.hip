@@ -8,19 +8,39 @@
 // keys are hashed into L independent tables with random projections, one
 // bucket per key and table, and the value norms are cached.
 //
-// bf16 path (the large prefill): the projection y = K R is a GEMM on the
-// gfx950 matrix cores (v_mfma_f32_32x32x16_bf16, float32 accumulation of the
-// exact bf16 products). Each wave keeps 128 hyperplane columns of R^T in
-// registers as the stationary A operand; a 32-key tile of K is staged once
-// in LDS and read by every wave as the B operand, so D = y^T lands with one
-// key per lane column. The sign of a projection is certified when |y| is
-// larger than the worst-case float32 summation error 2*d*2^-24*|k|*|r|;
-// otherwise the wave recomputes that projection cooperatively in
-// double-double arithmetic from the bf16 inputs (exact products), so the
-// bucket ids equal those of the exact dot products. Sign bits are packed
-// with one cross-lane exchange, assembled per key in LDS and written as
-// bytes. The value rows of the same tile stream through registers for the
-// norms.
+// bf16 path (the large prefill), three launches:
+//
+//  1. prep: R [d, C] is transposed to R^T [rows, d] (zero rows past C) in the
+//     workspace, and the fix-up counter is cleared.
+//  2. main: a persistent grid of one 8-wave block per CU. Every block walks
+//     32-key tiles; the K and V rows of the next seven tiles are in flight
+//     into an 8-slot LDS ring (128 KB) through direct-to-LDS loads
+//     (global_load_lds_dwordx4, no registers held), so each CU keeps about
+//     100 KB of loads in flight while it computes. The projection y = K R runs
+//     on the matrix cores (v_mfma_f32_32x32x16_bf16, float32 accumulation of
+//     the exact bf16 products): every wave keeps up to 64 hyperplane
+//     columns of R^T in registers as the stationary A operand and reads the
+//     tile's K rows from LDS as the B operand (XOR-swizzled so the 8 lanes
+//     the LDS serves together hit 8 bank groups), so one lane ends with 16
+//     projections of one key. Their sign bits are packed with one funnel
+//     shift each; the A rows are permuted so that a lane's 16 bits are 16
+//     consecutive hyperplanes and one exchange between the two lane halves
+//     yields a 32-bit word of 32 consecutive sign bits. With P = 8 that word
+//     is four id bytes, stored directly. The value norms of the same tile are
+//     reduced from the V rows in LDS (bf16 dot2).
+//  3. fix-up: a sign is certified when |y| exceeds the worst-case float32
+//     summation error 2*d*2^-24*|k|*max|r| (plus a floor for flushed
+//     denormals). Uncertain projections (about 1.5e-4 of them for random
+//     data) are appended by the main kernel to a list in the workspace with
+//     their float32 sign written; the fix-up kernel recomputes each one from
+//     the bf16 inputs (float64 sum of exact products, certified, with a
+//     double-double fallback) and sets or clears that one bit with an atomic
+//     AND/OR. A block whose list overflows (or any block with an uncertain
+//     sign when id rows are not whole 4-byte words) has all its tiles
+//     re-hashed exactly by a fourth kernel (float64 / double-double, one
+//     thread per key and table), which exits at once when nothing
+//     overflowed. Either way the bucket ids are those of the exact dot
+//     products.
 //
 // f32 path (small inputs): one thread per key, float64 dot products with the
 // same certification and a serial double-double fallback.
@@ -34,230 +54,512 @@ namespace socket_lsh {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+#define SOCKET_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
 constexpr int kTileKeys = 32;
-constexpr int kTilesPerWave = 4;    // 4 x 32 = 128 hyperplane columns per wave
-constexpr int kMaxColWords = 16;    // L*P <= 512 bits per key
+constexpr int kHashWaves = 8;
+constexpr int kHashThreads = kHashWaves * 64;
+constexpr int kRing = 8;              // LDS slots: one tile computed, up to seven in flight
+constexpr int kMaxTilesPerWave = 2;   // 2 x 32 hyperplane columns per wave
+constexpr int kMaxColWords = 16;      // L*P <= 512 bits per key
+constexpr int kRtRows = kHashWaves * kMaxTilesPerWave * 32;
 constexpr float kAbsFloor = 0x1p-100f;  // covers flushed float32 denormals
+constexpr int kColBits = 10;            // fix-up entry: (row << 10) | column
 
 template <int D>
 struct HashGeom {
-  static constexpr int S = D / 16;              // MFMA k-steps of 16
-  static constexpr int chunks = D / 8;          // 16-byte chunks per bf16 row
-  static constexpr int lds_stride = 2 * D + 16; // padded LDS row (bank spread)
+  static constexpr int S = D / 16;                        // MFMA k-steps of 16
+  static constexpr int CH = D / 8;                        // 16-byte chunks per row
+  static constexpr int kTileBytes = kTileKeys * D * 2;    // one matrix of a tile
+  static constexpr int kSlotBytes = 2 * kTileBytes;       // K then V
+  static constexpr int kSegs = kSlotBytes / 1024;         // 1 KB load segments per slot
+  static constexpr int kDmaPerWave = kSegs / kHashWaves;  // loads per wave per tile
+  static_assert(kSegs % kHashWaves == 0, "every wave issues the same number of loads");
 };
 
-__device__ __forceinline__ float sumsq8_bf16(const uint4& w) {
-  float f[8];
-  unpack8_bf16(w, f);
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s = fmaf(f[i], f[i], s);
-  return s;
+struct HashArgs {
+  const uint16_t* K;
+  const uint16_t* V;
+  const uint16_t* R;   // [d, C]
+  const uint16_t* RT;  // [kRtRows, d], zero past C
+  int64_t n_keys, stride;
+  int tph, n_tiles;  // tiles per head, tiles in total (< 2^31)
+  int L, P, C;
+  uint8_t* ids;
+  float* vnorm;
+  unsigned long long* fix_list;  // [grid][fix_cap] entries, one region per block
+  uint32_t* fix_count;           // [grid] entries each block appended
+  uint32_t fix_cap;  // per block; 0: settle every uncertain sign in the main kernel
+};
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Block barrier that orders LDS only: the wave's LDS operations complete,
+// then all waves meet. (__syncthreads would also drain every outstanding
+// global load, which is exactly what the ring keeps in flight.)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 16-byte LDS reads and their completion in one asm block: the ring is
+// filled by direct-to-LDS loads whose progress the compiler cannot see, so
+// the kernel orders these reads itself (wait + barrier before them).
+__device__ __forceinline__ void lds_read4(const uint32_t (&addr)[4], u32x4_t (&o)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3])
+      : "memory");
+}
+
+__device__ __forceinline__ u32x4_t lds_read1(uint32_t addr) {
+  u32x4_t o;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(o) : "v"(addr) : "memory");
+  return o;
+}
+
+// Byte offset of a pointer into LDS, as DS instructions address it.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  typedef __attribute__((address_space(3))) const unsigned char lds_uchar;
+  return (uint32_t)(uintptr_t)(lds_uchar*)p;
+}
+
+__device__ __forceinline__ float sumsq_bf16x2(uint32_t w, float acc) {
+  const bf16x2_t v = __builtin_bit_cast(bf16x2_t, w);
+  return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+}
+
+__device__ __forceinline__ float sumsq_bf16x8(const u32x4_t w, float acc) {
+  const uint32_t w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+  acc = sumsq_bf16x2(w0, acc);
+  acc = sumsq_bf16x2(w1, acc);
+  acc = sumsq_bf16x2(w2, acc);
+  return sumsq_bf16x2(w3, acc);
 }
 
 // P bits starting at bit `off` of a per-key bit vector.
-__device__ __forceinline__ uint32_t extract_bits(const uint32_t* row, int off,
-                                                 int P) {
+__device__ __forceinline__ uint32_t extract_bits(const uint32_t* row, int off, int P) {
   const int w = off >> 5, b = off & 31;
   uint64_t x = row[w];
   if (b + P > 32) x |= (uint64_t)row[w + 1] << 32;
   return (uint32_t)(x >> b) & ((1u << P) - 1u);
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void hash_keys_bf16_kernel(
-    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ R, int64_t n_keys, int64_t stride, int L,
-    int P, uint8_t* __restrict__ ids, float* __restrict__ vnorm,
-    int64_t n_tiles, int64_t tiles_per_head, int word_store) {
-  using Geo = HashGeom<D>;
-  constexpr int NT = NW * 64;
-  constexpr int S = Geo::S;
-  constexpr int CH = Geo::chunks;
-  constexpr int TILE_CHUNKS = kTileKeys * CH;
-  constexpr int PER = (TILE_CHUNKS + NT - 1) / NT;
-  constexpr float kGamma = 2.0f * D * 0x1p-24f;
+// A row m of a 32-column MFMA tile holds hyperplane column jmap(m) of the
+// tile. With the D layout (lane (n, h) holds rows (v/4)*8 + h*4 + v%4,
+// v = 0..15) this gives lane half h the 16 consecutive columns h*16 + v.
+__device__ __forceinline__ int jmap(int m) {
+  return ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3);
+}
 
-  __shared__ __align__(16) unsigned char ktile[kTileKeys * Geo::lds_stride];
-  __shared__ uint32_t bitvec[kTileKeys * kMaxColWords];
+// K and V rows of tile `tile` into one ring slot (K at byte 0, V at
+// kTileBytes). Segment g (1 KB) is loaded by wave g % kHashWaves; lane i
+// fills 16-byte position i of it. K rows are stored XOR-swizzled: position
+// q of row r holds chunk q ^ (r & 7). Rows past the end re-read row 0.
+template <int D>
+__device__ __forceinline__ void dma_tile(const HashArgs& a, int tile, unsigned char* slot,
+                                         int wave, int lane) {
+  using G = HashGeom<D>;
+  const int head = tile / a.tph;
+  const int64_t row0 = (int64_t)(tile - head * a.tph) * kTileKeys;
+  const int rows = (int)min<int64_t>(kTileKeys, a.n_keys - row0);
+  const int64_t base = ((int64_t)head * a.stride + row0) * D;
+#pragma unroll
+  for (int j = 0; j < G::kDmaPerWave; ++j) {
+    const int g = wave + j * kHashWaves;
+    const bool is_v = g >= G::kSegs / 2;
+    const int p = (is_v ? g - G::kSegs / 2 : g) * 64 + lane;
+    const int r = p / G::CH, q = p % G::CH;
+    const int rr = r < rows ? r : 0;
+    const uint16_t* src = is_v ? a.V + base + rr * D + q * 8
+                               : a.K + base + rr * D + (q ^ (r & 7)) * 8;
+    __builtin_amdgcn_global_load_lds((const void*)src, SOCKET_LDS(slot + g * 1024), 16, 0, 0);
+  }
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int kn = lane & 31;  // key (B column) / hyperplane (A row) of this lane
-  const int kh = lane >> 5;  // which half of the reduction dimension
-  const int C = L * P;
-  const int CT = (C + 31) >> 5;
+struct TileRows {
+  int64_t grow0;  // global row (head * stride + row) of key 0 of the tile
+  int rows;       // keys of the tile (32 except at the end of a head)
+};
 
-  // Stationary A operand: R^T columns (wave*4 + t)*32 + kn. The reduction
-  // index of k-step s, lane half kh, element e is d = (kh*S + s)*8 + e; the
-  // B operand below uses the same map, so the product is the plain dot.
-  bf16x8_t ra[kTilesPerWave][S];
-  float rmax[kTilesPerWave];
+__device__ __forceinline__ TileRows tile_rows(const HashArgs& a, int tile) {
+  const int head = tile / a.tph;
+  const int64_t row0 = (int64_t)(tile - head * a.tph) * kTileKeys;
+  return {(int64_t)head * a.stride + row0, (int)min<int64_t>(kTileKeys, a.n_keys - row0)};
+}
+
+// First half of a tile (its slot is valid): the projections on the matrix
+// cores, the squared key norms (into LDS, for the second half) and the
+// value norms (to memory).
+template <int D, int TPW>
+__device__ __forceinline__ void tile_project(const HashArgs& a, int tile,
+                                             const unsigned char* slot,
+                                             const bf16x8_t (&ra)[TPW][HashGeom<D>::S],
+                                             f32x16_t (&acc)[TPW], float* knorm2, int wave,
+                                             int lane) {
+  using G = HashGeom<D>;
+  constexpr int S = G::S;
+  const int kn = lane & 31, kh = lane >> 5;
+  const uint32_t sbase = lds_offset(slot);
+
+  // B operand: chunks kh*S + s of key row kn (the A rows use the same map),
+  // read four k-steps at a time; the second read overlaps the first MFMAs.
+  // (Column tiles past C multiply zero rows of R^T; their bits are dropped.)
 #pragma unroll
-  for (int t = 0; t < kTilesPerWave; ++t) {
-    const int col = (wave * kTilesPerWave + t) * 32 + kn;
-    float sq = 0.f;
+  for (int t = 0; t < TPW; ++t) acc[t] = f32x16_t{};
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      uint32_t w[4];
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    uint32_t addr[4];
+    u32x4_t kw[4];
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const int dd = (kh * S + s) * 8 + e;
-        uint32_t lo = col < C ? R[(int64_t)dd * C + col] : 0u;
-        uint32_t hi = col < C ? R[(int64_t)(dd + 1) * C + col] : 0u;
-        float flo = bf16_bits_to_f32(lo), fhi = bf16_bits_to_f32(hi);
-        sq = fmaf(flo, flo, sq);
-        sq = fmaf(fhi, fhi, sq);
-        w[e >> 1] = lo | (hi << 16);
-      }
-      u32x4_t v = {w[0], w[1], w[2], w[3]};
-      ra[t][s] = __builtin_bit_cast(bf16x8_t, v);
+    for (int s = 0; s < 4; ++s)
+      addr[s] = sbase + kn * (D * 2) + (((kh * S + s0 + s) ^ (kn & 7)) << 4);
+    lds_read4(addr, kw);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            ra[t][s0 + s], __builtin_bit_cast(bf16x8_t, kw[s]), acc[t], 0, 0, 0);
     }
-    sq += __shfl_xor(sq, 32, kWave);
-    rmax[t] = sqrtf(group_max<64>(sq));
   }
 
-  uint4 kreg[PER], vreg[PER];
-  auto load_tile = [&](int64_t tile) {
-    const int64_t head = tile / tiles_per_head;
-    const int64_t row0 = (tile % tiles_per_head) * kTileKeys;
-    const int rows = (int)min<int64_t>(kTileKeys, n_keys - row0);
-    const uint16_t* kb = K + (head * stride + row0) * D;
-    const uint16_t* vb = V + (head * stride + row0) * D;
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int q = tid + p * NT;
-      const int r = q / CH, c = q % CH;
-      const bool ok = q < TILE_CHUNKS && r < rows;
-      kreg[p] = ok ? *reinterpret_cast<const uint4*>(kb + r * D + c * 8)
-                   : make_uint4(0, 0, 0, 0);
-      vreg[p] = ok ? *reinterpret_cast<const uint4*>(vb + r * D + c * 8)
-                   : make_uint4(0, 0, 0, 0);
-    }
-  };
+  // key and value norms: wave w takes keys w*4 .. w*4+3, 16 lanes per key,
+  // one 16-byte chunk per lane (the chunk order of a row does not matter)
+  const TileRows tr = tile_rows(a, tile);
+  const int key = wave * 4 + (lane >> 4);
+  const int c = lane & 15;
+  float ks = 0.f, vs = 0.f;
+  if (c < G::CH) {
+    ks = sumsq_bf16x8(lds_read1(sbase + key * (D * 2) + c * 16), 0.f);
+    vs = sumsq_bf16x8(lds_read1(sbase + G::kTileBytes + key * (D * 2) + c * 16), 0.f);
+  }
+  ks = sum16(ks);
+  vs = sum16(vs);
+  if (c == 0) {
+    knorm2[key] = ks;
+    if (key < tr.rows) a.vnorm[tr.grow0 + key] = sqrtf(vs);
+  }
+  (void)kh;
+}
 
-  int64_t tile = blockIdx.x;
-  if (tile >= n_tiles) return;
-  load_tile(tile);
-
-  for (; tile < n_tiles; tile += gridDim.x) {
-    const int64_t head = tile / tiles_per_head;
-    const int64_t row0 = (tile % tiles_per_head) * kTileKeys;
-    const int rows = (int)min<int64_t>(kTileKeys, n_keys - row0);
-
-    // Stage K in LDS; reduce the value norms of the tile.
+// Second half of a tile, one iteration later (its slot may already be
+// refilled): sign bits, certification, uncertain signs and the ids.
+template <int D, int TPW, bool kWordIds>
+__device__ __forceinline__ void tile_signs(const HashArgs& a, int tile,
+                                           const f32x16_t (&acc)[TPW], const float* knorm2,
+                                           const float (&rmax)[TPW], uint32_t* bitvec,
+                                           uint32_t* fix_n, unsigned long long* fix_list,
+                                           int wave, int lane) {
+  constexpr float kGamma = 2.0f * D * 0x1p-24f;
+  const int kn = lane & 31, kh = lane >> 5;
+  const TileRows tr = tile_rows(a, tile);
+  const int CT = (a.C + 31) >> 5;
+  const float thr_k = kGamma * sqrtf(knorm2[kn]);
+  const bool row_ok = kn < tr.rows;
+  uint32_t half[TPW];
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int q = tid + p * NT;
-      const int r = q / CH, c = q % CH;
-      float s = group_sum<CH>(sumsq8_bf16(vreg[p]));
-      if (q < TILE_CHUNKS) {
-        *reinterpret_cast<uint4*>(ktile + r * Geo::lds_stride + c * 16) = kreg[p];
-        if (c == 0 && r < rows) vnorm[head * stride + row0 + r] = sqrtf(s);
-      }
-    }
-    __syncthreads();
-
-    const int64_t next = tile + gridDim.x;
-    if (next < n_tiles) load_tile(next);
-
-    f32x16_t acc[kTilesPerWave];
+  for (int t = 0; t < TPW; ++t) {
+    const int ct = wave * TPW + t;
+    float mn = fabsf(acc[t][0]);
 #pragma unroll
-    for (int t = 0; t < kTilesPerWave; ++t) acc[t] = f32x16_t{};
-    float ksq = 0.f;
+    for (int v = 1; v < 16; ++v) mn = fminf(mn, fabsf(acc[t][v]));
+    uint32_t h = 0;
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const uint4 kb = *reinterpret_cast<const uint4*>(
-          ktile + kn * Geo::lds_stride + (kh * S + s) * 16);
-      ksq += sumsq8_bf16(kb);
-      u32x4_t kv = {kb.x, kb.y, kb.z, kb.w};
-      const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, kv);
-#pragma unroll
-      for (int t = 0; t < kTilesPerWave; ++t) {
-        if (wave * kTilesPerWave + t < CT)
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[t][s], bop,
-                                                           acc[t], 0, 0, 0);
-      }
-    }
-    ksq += __shfl_xor(ksq, 32, kWave);
-    const float thr_k = kGamma * sqrtf(ksq);
-    const bool row_ok = kn < rows;
-
-#pragma unroll
-    for (int t = 0; t < kTilesPerWave; ++t) {
-      const int ct = wave * kTilesPerWave + t;
-      if (ct >= CT) break;
-      // D layout: lane (kn, kh), register v holds hyperplane row
-      // (v/4)*8 + kh*4 + v%4 of the tile for key kn.
-      const float thr = thr_k * rmax[t] + kAbsFloor;
-      // only real keys and real hyperplane columns (padding columns are zero)
+    for (int v = 15; v >= 0; --v)
+      h = __builtin_amdgcn_alignbit(h, __float_as_uint(acc[t][v]), 31);
+    h = ~h & 0xffffu;  // bit v: projection onto column ct*32 + kh*16 + v is > 0
+    const float thr = thr_k * rmax[t] + kAbsFloor;
+    if (row_ok && ct < CT && mn <= thr) {
+      const int c0 = ct * 32 + kh * 16;
       uint32_t fm = 0;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int colv = ct * 32 + (v >> 2) * 8 + kh * 4 + (v & 3);
-        if (row_ok && colv < C && fabsf(acc[t][v]) <= thr) fm |= 1u << v;
+        // opaque copy: keeps these compares inside the (rare) branch
+        float y = acc[t][v];
+        asm volatile("" : "+v"(y));
+        if (fabsf(y) <= thr) fm |= 1u << v;
       }
-      // Re-evaluate uncertain signs, one projection per wave iteration.
-      while (true) {
-        const uint64_t act = __ballot(fm != 0);
-        if (act == 0) break;
-        const int src = __ffsll((unsigned long long)act) - 1;
-        const uint32_t sfm = __shfl(fm, src, kWave);
-        const int vsel = __ffs(sfm) - 1;
-        const int en = src & 31, eh = src >> 5;
-        const int col = ct * 32 + (vsel >> 2) * 8 + eh * 4 + (vsel & 3);
-        double h = 0.0, l = 0.0;
-        for (int i = lane; i < D; i += kWave) {
-          const uint16_t kb16 = *reinterpret_cast<const uint16_t*>(
-              ktile + en * Geo::lds_stride + i * 2);
-          const double prod = (double)bf16_bits_to_f32(kb16) *
-                              (double)bf16_bits_to_f32(R[(int64_t)i * C + col]);
-          dd_add(h, l, prod, 0.0, h, l);
-        }
-        const double y = wave_sum_dd(h, l);
-        if (lane == src) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (v == vsel) acc[t][v] = y > 0.0 ? 1.0f : -1.0f;
-          fm &= ~(1u << vsel);
+      const int valid = min(max(a.C - c0, 0), 16);  // columns of this lane below C
+      fm &= valid >= 16 ? 0xffffu : (1u << valid) - 1u;
+      // Append each to the block's list (LDS counter). The counter is read
+      // first, so it stops just past the capacity (no wrap-around); a count
+      // above the capacity marks the block for the exact re-hash.
+      while (fm != 0) {
+        const int v = __ffs(fm) - 1;
+        fm &= fm - 1;
+        if (*fix_n <= a.fix_cap) {
+          const uint32_t idx = atomicAdd(fix_n, 1u);
+          if (idx < a.fix_cap)
+            fix_list[idx] = ((unsigned long long)(tr.grow0 + kn) << kColBits) |
+                            (unsigned long long)(c0 + v);
         }
       }
-      uint32_t word = 0;
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        word |= (acc[t][v] > 0.f ? 1u : 0u) << ((v >> 2) * 8 + kh * 4 + (v & 3));
-      word |= __shfl_xor(word, 32, kWave);
-      if (kh == 0) bitvec[kn * kMaxColWords + ct] = word;
     }
-    __syncthreads();
+    half[t] = h;
+  }
 
-    // Bucket ids: bits [l*P, l*P + P) of each key's bit vector.
-    uint8_t* obase = ids + (head * stride + row0) * L;
-    if (word_store) {
-      const int wpk = L >> 2;
-      for (int q = tid; q < kTileKeys * wpk; q += NT) {
-        const int r = q / wpk, w4 = q % wpk;
-        if (r >= rows) continue;
-        uint32_t packed = 0;
+  // 32-bit words of 32 consecutive sign bits, in both lanes of a key
+  uint32_t word[TPW];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          packed |= extract_bits(bitvec + r * kMaxColWords, (w4 * 4 + e) * P, P)
-                    << (8 * e);
-        *reinterpret_cast<uint32_t*>(obase + (int64_t)r * L + w4 * 4) = packed;
-      }
-    } else {
-      for (int q = tid; q < kTileKeys * L; q += NT) {
-        const int r = q / L, l = q % L;
-        if (r >= rows) continue;
-        obase[(int64_t)r * L + l] =
-            (uint8_t)extract_bits(bitvec + r * kMaxColWords, l * P, P);
+  for (int t = 0; t < TPW; ++t) {
+    const uint32_t o = xor32_u32(half[t]);
+    word[t] = kh ? (o | (half[t] << 16)) : (half[t] | (o << 16));
+  }
+  if constexpr (kWordIds) {
+    // P == 8: word ct holds the id bytes of tables 4ct .. 4ct+3
+    if (row_ok) {
+      uint32_t* orow = reinterpret_cast<uint32_t*>(a.ids + (tr.grow0 + kn) * a.L);
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int ct = wave * TPW + t;
+        if ((TPW == 1 ? 0 : (t & 1)) == kh && ct < CT) orow[ct] = word[t];
       }
     }
-    __syncthreads();
+  } else {
+    if (kh == 0) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int ct = wave * TPW + t;
+        if (ct < CT) bitvec[kn * kMaxColWords + ct] = word[t];
+      }
+    }
+    lds_barrier();
+    uint8_t* obase = a.ids + tr.grow0 * a.L;
+    const int tid = wave * 64 + lane;
+    for (int q = tid; q < kTileKeys * a.L; q += kHashThreads) {
+      const int r = q / a.L, l = q - r * a.L;
+      if (r < tr.rows)
+        obase[(int64_t)r * a.L + l] =
+            (uint8_t)extract_bits(bitvec + r * kMaxColWords, l * a.P, a.P);
+    }
+    // the next writer of bitvec is past another barrier
+  }
+}
+
+template <int D, int TPW, bool kWordIds>
+__global__ __launch_bounds__(kHashThreads) void hash_keys_bf16_kernel(HashArgs a) {
+  using G = HashGeom<D>;
+  constexpr int S = G::S;
+  constexpr int kWaitSteady = (kRing - 2) * G::kDmaPerWave;
+  __shared__ __align__(16) unsigned char ring[kRing * G::kSlotBytes];
+  __shared__ uint32_t bitvec[kWordIds ? 1 : kTileKeys * kMaxColWords];
+  __shared__ float knorm2[2][kTileKeys];
+  __shared__ uint32_t fix_n;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kn = lane & 31, kh = lane >> 5;
+  const int nb = gridDim.x;
+  const int b = blockIdx.x;
+  if (b >= a.n_tiles) return;
+  const int iters = (a.n_tiles - b + nb - 1) / nb;  // tiles b, b + nb, ...
+  unsigned long long* const fix_list = a.fix_list + (size_t)b * a.fix_cap;
+  if (threadIdx.x == 0) fix_n = 0u;  // ordered by the first barrier below
+
+  // stationary A operand: R^T rows of this wave's column tiles
+  bf16x8_t ra[TPW][S];
+  float rmax[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int col = (wave * TPW + t) * 32 + jmap(kn);
+    const uint4* src = reinterpret_cast<const uint4*>(a.RT + (int64_t)col * D);
+    float sq = 0.f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const uint4 w = src[kh * S + s];
+      const u32x4_t wv = {w.x, w.y, w.z, w.w};
+      sq = sumsq_bf16x8(wv, sq);
+      ra[t][s] = __builtin_bit_cast(bf16x8_t, wv);
+    }
+    sq += __shfl_xor(sq, 32, kWave);
+    // the bound takes the largest column norm of the tile, rounded up
+    rmax[t] = sqrtf(group_max<64>(sq)) * (1.0f + 0x1p-20f);
+  }
+
+#pragma unroll
+  for (int j = 0; j < kRing - 1; ++j)
+    if (j < iters) dma_tile<D>(a, b + j * nb, ring + j * G::kSlotBytes, wave, lane);
+
+  // Two accumulator sets in turn: tile `it` is projected while the signs of
+  // tile it-1 are packed, so the matrix cores and the vector ALUs overlap.
+  f32x16_t acc0[TPW], acc1[TPW];
+  for (int it = 0; it < iters; ++it) {
+    // this wave's loads into the slot of tile `it` are done once at most the
+    // loads of the later tiles are outstanding; the barrier then makes every
+    // wave's part visible, frees the slot computed last round and publishes
+    // the key norms of tile it-1
+    if (it + kRing - 2 < iters)
+      wait_vmcnt<kWaitSteady>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+    if (it + kRing - 1 < iters)
+      dma_tile<D>(a, b + (it + kRing - 1) * nb,
+                  ring + ((it + kRing - 1) % kRing) * G::kSlotBytes, wave, lane);
+    const unsigned char* slot = ring + (it % kRing) * G::kSlotBytes;
+    if ((it & 1) == 0) {
+      tile_project<D, TPW>(a, b + it * nb, slot, ra, acc0, knorm2[0], wave, lane);
+      if (it > 0)
+        tile_signs<D, TPW, kWordIds>(a, b + (it - 1) * nb, acc1, knorm2[1], rmax, bitvec,
+                                     &fix_n, fix_list, wave, lane);
+    } else {
+      tile_project<D, TPW>(a, b + it * nb, slot, ra, acc1, knorm2[1], wave, lane);
+      tile_signs<D, TPW, kWordIds>(a, b + (it - 1) * nb, acc0, knorm2[0], rmax, bitvec,
+                                   &fix_n, fix_list, wave, lane);
+    }
+  }
+  lds_barrier();
+  const int last = iters - 1;
+  if ((last & 1) == 0)
+    tile_signs<D, TPW, kWordIds>(a, b + last * nb, acc0, knorm2[0], rmax, bitvec, &fix_n,
+                                 fix_list, wave, lane);
+  else
+    tile_signs<D, TPW, kWordIds>(a, b + last * nb, acc1, knorm2[1], rmax, bitvec, &fix_n,
+                                 fix_list, wave, lane);
+  lds_barrier();
+  if (threadIdx.x == 0) a.fix_count[b] = fix_n;
+}
+
+// R [d, C] -> R^T [kRtRows, d] with zero rows past C.
+__global__ __launch_bounds__(256) void hash_prep_kernel(const uint16_t* __restrict__ R, int C,
+                                                        int D, uint16_t* __restrict__ RT) {
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)kRtRows * D;
+  for (int64_t i = i0; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i / D), d = (int)(i % D);
+    RT[i] = c < C ? R[(int64_t)d * C + c] : (uint16_t)0;
+  }
+}
+
+// Settles the listed uncertain projections. Blocks (part, j) take the list
+// region of main-kernel block `part`, kFixBlocksPerPart blocks per region;
+// 16 lanes per entry, each lane D/16 exact products of the key row and the
+// R^T row (one contiguous load each) summed in float64 (the sum of the
+// group's |products| bounds its rounding error); uncertain sums are redone
+// in double-double. The one bit is then set or cleared with an atomic on
+// its 32-bit word.
+constexpr int kFixBlocksPerPart = 8;
+
+template <int D>
+__global__ __launch_bounds__(256) void hash_fixup_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ RT, int C, int L, int P,
+    uint8_t* __restrict__ ids, const unsigned long long* __restrict__ list,
+    const uint32_t* __restrict__ count, uint32_t cap) {
+  constexpr int kPer = D / 16;  // dims per lane: 8 (one 16-byte load) or 4
+  const int part = blockIdx.x / kFixBlocksPerPart;
+  const int j = blockIdx.x % kFixBlocksPerPart;
+  const uint32_t n = min(count[part], cap);
+  const unsigned long long* plist = list + (size_t)part * cap;
+  const int sub = threadIdx.x & 15;
+  const uint32_t groups = blockDim.x / 16;
+  for (uint32_t e = j * groups + threadIdx.x / 16; e < n; e += kFixBlocksPerPart * groups) {
+    const unsigned long long ent = plist[e];
+    const int64_t row = (int64_t)(ent >> kColBits);
+    const int col = (int)(ent & ((1u << kColBits) - 1u));
+    uint16_t kv[kPer], rv[kPer];
+    if constexpr (kPer == 8) {
+      *reinterpret_cast<uint4*>(kv) = *reinterpret_cast<const uint4*>(K + row * D + sub * 8);
+      *reinterpret_cast<uint4*>(rv) = *reinterpret_cast<const uint4*>(RT + col * D + sub * 8);
+    } else {
+      *reinterpret_cast<uint2*>(kv) = *reinterpret_cast<const uint2*>(K + row * D + sub * 4);
+      *reinterpret_cast<uint2*>(rv) = *reinterpret_cast<const uint2*>(RT + col * D + sub * 4);
+    }
+    double p[kPer];
+    double s = 0.0, sa = 0.0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      p[i] = (double)bf16_bits_to_f32(kv[i]) * (double)bf16_bits_to_f32(rv[i]);
+      s += p[i];
+      sa += fabs(p[i]);
+    }
+    // identical sums in all 16 lanes, so the branch below is uniform
+    s = sum16_f64(s);
+    sa = sum16_f64(sa);
+    bool pos;
+    if (fabs(s) > (double)D * 0x1p-52 * sa) {
+      pos = s > 0.0;
+    } else {
+      double h = 0.0, l = 0.0;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) dd_add(h, l, p[i], 0.0, h, l);
+#pragma unroll
+      for (int m = 8; m >= 1; m >>= 1) {
+        const double oh = __shfl_xor(h, m, kWave), ol = __shfl_xor(l, m, kWave);
+        dd_add(h, l, oh, ol, h, l);
+      }
+      pos = h > 0.0;
+    }
+    if (sub == 0) {
+      const uint64_t byte = (uint64_t)row * L + (uint64_t)(col / P);
+      uint32_t* word = reinterpret_cast<uint32_t*>(ids + (byte & ~(uint64_t)3));
+      const uint32_t bit = 1u << ((byte & 3) * 8 + col % P);
+      if (pos)
+        atomicOr(word, bit);
+      else
+        atomicAnd(word, ~bit);
+    }
+  }
+}
+
+// Exact re-hash of the tiles of every main-kernel block whose list
+// overflowed (count above the capacity; with capacity 0, any uncertain
+// sign): one thread per (key, table) recomputes the table's P projections
+// from the bf16 inputs in float64 (exact products; the sum of |products|
+// bounds the rounding) or, when that cannot decide, in double-double, and
+// rewrites the id byte. Blocks of parts without overflow exit at once.
+template <int D>
+__global__ __launch_bounds__(256) void hash_redo_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ R, int64_t n_keys,
+    int64_t stride, int tph, int n_tiles, int nb, int L, int P, uint8_t* __restrict__ ids,
+    const uint32_t* __restrict__ count, uint32_t cap) {
+  const int part = blockIdx.x;
+  if (count[part] <= cap) return;
+  const int C = L * P;
+  for (int tile = part; tile < n_tiles; tile += nb) {
+    const int head = tile / tph;
+    const int64_t row0 = (int64_t)(tile - head * tph) * kTileKeys;
+    const int rows = (int)min<int64_t>(kTileKeys, n_keys - row0);
+    const int64_t grow0 = (int64_t)head * stride + row0;
+    for (int q = threadIdx.x; q < rows * L; q += blockDim.x) {
+      const int r = q / L, l = q - r * L;
+      const uint16_t* krow = K + (grow0 + r) * D;
+      uint32_t id = 0;
+      for (int j = 0; j < P; ++j) {
+        const int col = l * P + j;
+        double y = 0.0, mag = 0.0;
+        for (int i = 0; i < D; ++i) {
+          const double p = (double)bf16_bits_to_f32(krow[i]) *
+                           (double)bf16_bits_to_f32(R[(int64_t)i * C + col]);
+          y += p;
+          mag += fabs(p);
+        }
+        if (fabs(y) <= (double)D * 0x1p-52 * mag) {
+          double h = 0.0, lo = 0.0;
+          for (int i = 0; i < D; ++i)
+            dd_add(h, lo,
+                   (double)bf16_bits_to_f32(krow[i]) *
+                       (double)bf16_bits_to_f32(R[(int64_t)i * C + col]),
+                   0.0, h, lo);
+          y = h;
+        }
+        if (y > 0.0) id |= 1u << j;
+      }
+      ids[(grow0 + r) * L + l] = (uint8_t)id;
+    }
   }
 }
 
@@ -308,61 +610,120 @@ __global__ __launch_bounds__(256) void hash_keys_f32_kernel(
   }
 }
 
-template <int D, int NW>
-hipError_t launch_bf16_nw(const uint16_t* K, const uint16_t* V,
-                          const uint16_t* R, int64_t n_keys, int64_t stride,
-                          int L, int P, uint8_t* ids, float* vnorm,
-                          int64_t n_tiles, int64_t tph, int word_store,
-                          hipStream_t stream) {
-  // about 8 waves per CU on 256 CUs; each block loops over tiles
-  const int64_t cap = (int64_t)256 * 8 / NW;
-  const int grid = (int)std::min<int64_t>(n_tiles, cap);
-  launch_kernel((hash_keys_bf16_kernel<D, NW>), dim3(grid), dim3(NW * 64),
-                     0, stream, K, V, R, n_keys, stride, L, P, ids, vnorm,
-                     n_tiles, tph, word_store);
-  return hipGetLastError();
+// --------------------------------------------------------------- launchers
+
+constexpr int kMaxHashBlocks = 256;  // one block per CU
+
+struct HashWs {
+  uint16_t* rt;
+  uint32_t* count;            // [kMaxHashBlocks]
+  unsigned long long* list;   // [kMaxHashBlocks][cap]
+  uint32_t cap;               // entries per block
+};
+
+HashWs hash_ws_layout(void* ws, int64_t n_total, int d, int C) {
+  HashWs w{};
+  unsigned char* p = static_cast<unsigned char*>(ws);
+  size_t off = 0;
+  w.rt = reinterpret_cast<uint16_t*>(p + off);
+  off = align256(off + (size_t)kRtRows * d * sizeof(uint16_t));
+  w.count = reinterpret_cast<uint32_t*>(p + off);
+  off = align256(off + kMaxHashBlocks * sizeof(uint32_t));
+  w.list = reinterpret_cast<unsigned long long*>(p + off);
+  w.cap = hash_fix_capacity(n_total, C) / kMaxHashBlocks;
+  return w;
+}
+
+template <int D, int TPW, bool kWordIds>
+void launch_main(const HashArgs& a, hipStream_t stream) {
+  // one block per CU (the ring takes most of the 160 KB of LDS)
+  const int grid = std::min(a.n_tiles, kMaxHashBlocks);
+  launch_kernel((hash_keys_bf16_kernel<D, TPW, kWordIds>), dim3(grid), dim3(kHashThreads), 0,
+                stream, a);
 }
 
 template <int D>
-hipError_t launch_bf16_d(const uint16_t* K, const uint16_t* V,
-                         const uint16_t* R, int64_t n_keys, int64_t stride,
-                         int L, int P, uint8_t* ids, float* vnorm,
-                         int64_t n_tiles, int64_t tph, int word_store,
-                         hipStream_t stream) {
-  const int CT = (L * P + 31) / 32;
-  const int NW = (CT + kTilesPerWave - 1) / kTilesPerWave;
-  switch (NW) {
-#define SOCKET_NW_CASE(n)                                                    \
-  case n:                                                                    \
-    return launch_bf16_nw<D, n>(K, V, R, n_keys, stride, L, P, ids, vnorm,   \
-                                n_tiles, tph, word_store, stream);
-    SOCKET_NW_CASE(1)
-    SOCKET_NW_CASE(2)
-    SOCKET_NW_CASE(3)
-    SOCKET_NW_CASE(4)
-#undef SOCKET_NW_CASE
-    default:
-      return hipErrorInvalidValue;
+void launch_main_d(const HashArgs& a, int tpw, bool word_ids, hipStream_t stream) {
+  switch (tpw * 2 + (word_ids ? 1 : 0)) {
+#define SOCKET_HASH_CASE(t)                                            \
+  case 2 * t: launch_main<D, t, false>(a, stream); break;              \
+  case 2 * t + 1: launch_main<D, t, true>(a, stream); break;
+    SOCKET_HASH_CASE(1)
+    SOCKET_HASH_CASE(2)
+#undef SOCKET_HASH_CASE
+    default: break;
   }
 }
 
 }  // namespace
 
+uint32_t hash_fix_capacity(int64_t n_total, int C) {
+  const int64_t want = n_total * C / 512;
+  return (uint32_t)std::max<int64_t>(65536, std::min<int64_t>(want, (int64_t)1 << 26));
+}
+
+size_t hash_keys_bf16_workspace_bytes(int64_t n_total, int d, int C) {
+  size_t off = align256((size_t)kRtRows * d * sizeof(uint16_t));
+  off = align256(off + kMaxHashBlocks * sizeof(uint32_t));
+  return off + (size_t)(hash_fix_capacity(n_total, C) / kMaxHashBlocks) * kMaxHashBlocks *
+                   sizeof(unsigned long long);
+}
+
 hipError_t launch_hash_keys_bf16(const uint16_t* K, const uint16_t* V,
                                  const uint16_t* R, int64_t n_heads,
                                  int64_t n_keys, int64_t stride, int d, int L,
-                                 int P, uint8_t* ids, float* vnorm,
+                                 int P, uint8_t* ids, float* vnorm, void* ws,
                                  hipStream_t stream) {
   if (n_heads == 0 || n_keys == 0) return hipSuccess;
+  const int C = L * P;
   const int64_t tph = (n_keys + kTileKeys - 1) / kTileKeys;
-  const int64_t n_tiles = n_heads * tph;
-  const int word_store =
-      (L % 4 == 0 && (reinterpret_cast<uintptr_t>(ids) & 3) == 0) ? 1 : 0;
+  if (n_heads * tph >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const HashWs w = hash_ws_layout(ws, n_heads * n_keys, d, C);
+  // the fix-up patches bits through 4-byte words inside id rows
+  const bool word_rows = (L % 4 == 0) && (reinterpret_cast<uintptr_t>(ids) & 3) == 0;
+  HashArgs a{};
+  a.K = K;
+  a.V = V;
+  a.R = R;
+  a.RT = w.rt;
+  a.n_keys = n_keys;
+  a.stride = stride;
+  a.tph = (int)tph;
+  a.n_tiles = (int)(n_heads * tph);
+  a.L = L;
+  a.P = P;
+  a.C = C;
+  a.ids = ids;
+  a.vnorm = vnorm;
+  a.fix_list = w.list;
+  a.fix_count = w.count;
+  a.fix_cap = word_rows ? w.cap : 0u;
+
+  launch_kernel(hash_prep_kernel, dim3(64), dim3(256), 0, stream, R, C, d, w.rt);
+  const int CT = (C + 31) / 32;
+  const int tpw = (CT + kHashWaves - 1) / kHashWaves;
+  const bool word_ids = P == 8 && word_rows;
   if (d == 128)
-    return launch_bf16_d<128>(K, V, R, n_keys, stride, L, P, ids, vnorm,
-                              n_tiles, tph, word_store, stream);
-  return launch_bf16_d<64>(K, V, R, n_keys, stride, L, P, ids, vnorm, n_tiles,
-                           tph, word_store, stream);
+    launch_main_d<128>(a, tpw, word_ids, stream);
+  else
+    launch_main_d<64>(a, tpw, word_ids, stream);
+  const int parts = std::min(a.n_tiles, kMaxHashBlocks);
+  if (a.fix_cap != 0) {
+    const dim3 fgrid(parts * kFixBlocksPerPart);
+    if (d == 128)
+      launch_kernel(hash_fixup_kernel<128>, fgrid, dim3(256), 0, stream, K, w.rt, C, L, P,
+                    ids, w.list, w.count, a.fix_cap);
+    else
+      launch_kernel(hash_fixup_kernel<64>, fgrid, dim3(256), 0, stream, K, w.rt, C, L, P,
+                    ids, w.list, w.count, a.fix_cap);
+  }
+  if (d == 128)
+    launch_kernel(hash_redo_kernel<128>, dim3(parts), dim3(256), 0, stream, K, R, n_keys,
+                  stride, a.tph, a.n_tiles, parts, L, P, ids, w.count, a.fix_cap);
+  else
+    launch_kernel(hash_redo_kernel<64>, dim3(parts), dim3(256), 0, stream, K, R, n_keys,
+                  stride, a.tph, a.n_tiles, parts, L, P, ids, w.count, a.fix_cap);
+  return hipGetLastError();
 }
 
 hipError_t launch_hash_keys_f32(const float* K, const float* V, const float* R,
@@ -375,12 +736,10 @@ hipError_t launch_hash_keys_f32(const float* K, const float* V, const float* R,
   const int grid = (int)((total + 255) / 256);
   if (d == 128)
     launch_kernel(hash_keys_f32_kernel<128>, dim3(grid), dim3(256), 0,
-                       stream, K, V, R, n_heads, n_keys, stride, L, P, ids,
-                       vnorm);
+                  stream, K, V, R, n_heads, n_keys, stride, L, P, ids, vnorm);
   else
     launch_kernel(hash_keys_f32_kernel<64>, dim3(grid), dim3(256), 0,
-                       stream, K, V, R, n_heads, n_keys, stride, L, P, ids,
-                       vnorm);
+                  stream, K, V, R, n_heads, n_keys, stride, L, P, ids, vnorm);
   return hipGetLastError();
 }
 

@@ -33,11 +33,19 @@ inline void launch_kernel(F kernel, dim3 grid, dim3 block, size_t lds, hipStream
   hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, stream, start, stop, 0u, args...);
 }
 
+// Workspace sub-buffers start on 256-byte boundaries.
+inline constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 // ------------------------------------------------------------- prefill hash
+// Entries of the deferred sign fix-up list for n_total keys of C hyperplanes.
+uint32_t hash_fix_capacity(int64_t n_total, int C);
+// Workspace of the bf16 path: R^T, the fix-up counter and list.
+size_t hash_keys_bf16_workspace_bytes(int64_t n_total, int d, int C);
+// ws: hash_keys_bf16_workspace_bytes(...) bytes, 256-byte aligned.
 hipError_t launch_hash_keys_bf16(const uint16_t* K, const uint16_t* V,
                                  const uint16_t* R, int64_t n_heads,
                                  int64_t n_keys, int64_t stride, int d, int L,
-                                 int P, uint8_t* ids, float* vnorm,
+                                 int P, uint8_t* ids, float* vnorm, void* ws,
                                  hipStream_t stream);
 hipError_t launch_hash_keys_f32(const float* K, const float* V, const float* R,
                                 int64_t n_heads, int64_t n_keys,

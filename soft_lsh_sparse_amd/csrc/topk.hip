@@ -352,8 +352,6 @@ __global__ void iota_rows_kernel(int32_t* idx, int rows, int64_t n) {
     idx[i] = (int32_t)(i % n);
 }
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
 }  // namespace
 
 TopkPlan plan_topk(int rows, int64_t n, int64_t k) {

@@ -96,7 +96,9 @@ def test_decode_profiled_needs_an_event_pair(lib):
 
 def test_hash_keys_validation(lib):
     f = lib.socket_hash_keys
-    ok_args = [FAKE, FAKE, FAKE, 1, 8, 1024, 1024, 128, 64, 8, FAKE, FAKE, None]
+    ws = lib.socket_hash_keys_workspace_bytes(1, 8, 1024, 128, 64, 8)
+    assert ws > 0 and lib.socket_hash_keys_workspace_bytes(0, 8, 1024, 128, 64, 8) == 0
+    ok_args = [FAKE, FAKE, FAKE, 1, 8, 1024, 1024, 128, 64, 8, FAKE, FAKE, FAKE, ws, None]
     bad = list(ok_args); bad[7] = 80
     assert f(*bad) == _lib.SOCKET_ERR_UNSUPPORTED
     bad = list(ok_args); bad[9] = 9
@@ -109,10 +111,18 @@ def test_hash_keys_validation(lib):
     assert f(*bad) == _lib.SOCKET_ERR_INVALID_ARGUMENT
     bad = list(ok_args); bad[0] = FAKE + 4
     assert f(*bad) == _lib.SOCKET_ERR_INVALID_ARGUMENT
+    bad = list(ok_args); bad[2] = FAKE + 8     # R must be 16-byte aligned
+    assert f(*bad) == _lib.SOCKET_ERR_INVALID_ARGUMENT
+    bad = list(ok_args); bad[13] = ws - 1      # workspace too small
+    assert f(*bad) == _lib.SOCKET_ERR_WORKSPACE
+    bad = list(ok_args); bad[12] = FAKE + 16   # workspace not 256-byte aligned
+    assert f(*bad) == _lib.SOCKET_ERR_WORKSPACE
+    bad = list(ok_args); bad[12] = None
+    assert f(*bad) == _lib.SOCKET_ERR_WORKSPACE
     # nothing to hash: OK without touching any pointer or the GPU
     empty = list(ok_args); empty[5] = 0
     assert f(*empty) == _lib.SOCKET_OK
-    empty = [None, None, None, 1, 0, 5, 5, 128, 64, 8, None, None, None]
+    empty = [None, None, None, 1, 0, 5, 5, 128, 64, 8, None, None, None, 0, None]
     assert f(*empty) == _lib.SOCKET_OK
 
 

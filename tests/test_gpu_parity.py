@@ -94,11 +94,14 @@ def test_hash_keys_bit_exact(case):
     assert_close_rel(vn[:, :N].cpu().numpy(), ref_vn, 1e-5, 0.0, "vnorm")
 
 
-def test_hash_near_zero_projections_are_exact():
+@pytest.mark.parametrize("L,P", [(16, 8), (6, 8), (21, 6)])
+def test_hash_near_zero_projections_are_exact(L, P):
     """Keys built so that some projections are exactly 0 or cancel far below
-    float32 resolution: the certified-sign fix-up must get every bit right."""
-    log("hash near-zero")
-    d, L, P = 128, 16, 8
+    float32 resolution: the certified-sign fix-up must get every bit right
+    (deferred list with whole id words, deferred list with other P, and the
+    in-kernel path when id rows are not whole words)."""
+    log(f"hash near-zero L={L} P={P}")
+    d = 128
     g = torch.Generator().manual_seed(5)
     R = torch.randn(d, L * P, generator=g).to(torch.bfloat16)
     R[0:3, :] = 1.0
@@ -128,6 +131,39 @@ def test_hash_near_zero_projections_are_exact():
     assert np.array_equal(ids.cpu().numpy(), ref)
     bits = O.hash_bits(f64(K), f64(R))
     assert bits[0, L * P].all() and not bits[0, L * P + 1].any()
+
+
+def test_hash_fixup_list_overflow_settles_in_kernel():
+    """More uncertain projections than the fix-up list holds (all-zero and
+    tiny keys): the overflow is settled inside the main kernel."""
+    log("hash fix-up overflow")
+    w = W.custom_workload(B=1, Hq=2, Hkv=2, d=128, N=4096, dtype="bf16", L=64, P=8)
+    K, V = W.make_keys_values(w, DEV, seed=21)
+    R = W.make_hyperplanes(w, DEV, seed=21)
+    K, V = K[0].clone(), V[0]
+    K[:, ::2] = 0                               # 4096 zero keys x 512 projections
+    K[:, 1::4] = K[:, 1::4] * 2.0 ** -120       # tiny keys near the absolute floor
+    ids, _ = S.hash_keys(K, V, R, w.L, w.P)
+    torch.cuda.synchronize()
+    ref = O.hash_keys(f64(K), f64(R), w.L, w.P)
+    got = ids.cpu().numpy()
+    assert np.array_equal(got, ref), f"{int((got != ref).sum())} ids differ"
+
+
+def test_hash_every_id_of_a_64_table_prefill():
+    """Every id of 2 x 16384 Llama-shaped keys (outlier channels, planted
+    keys), 64 tables of 8 bits: about 2.5k projections go through the
+    deferred fix-up list."""
+    w = W.custom_workload("llama3_8b_32k", B=1, Hq=8, Hkv=2, N=16384, L=64, P=8)
+    log(f"hash all ids {w.name}")
+    K, V = W.make_keys_values(w, DEV, seed=4)
+    R = W.make_hyperplanes(w, DEV, seed=4)
+    ids, vn = S.hash_keys(K[0], V[0], R, w.L, w.P)
+    torch.cuda.synchronize()
+    ref = O.hash_keys(f64(K[0]), f64(R), w.L, w.P)
+    got = ids.cpu().numpy()
+    assert np.array_equal(got, ref), f"{int((got != ref).sum())} ids differ"
+    assert_close_rel(vn.cpu().numpy(), O.value_norms(f64(V[0])), 1e-5, 0.0, "vnorm")
 
 
 def test_hash_append_with_row_offset():
