@@ -31,7 +31,8 @@
 //  3. fix-up: a sign is certified when |y| exceeds the worst-case float32
 //     summation error 2*d*2^-24*|k|*max|r| (plus a floor for flushed
 //     denormals). Uncertain projections (about 1.5e-4 of them for random
-//     data) are appended by the main kernel to a list in the workspace with
+//     data) are appended by the main kernel to a per-block list in the
+//     workspace (one entry per key and 16-column group, with a mask) with
 //     their float32 sign written; the fix-up kernel recomputes each one from
 //     the bf16 inputs (float64 sum of exact products, certified, with a
 //     double-double fallback) and sets or clears that one bit with an atomic
@@ -61,14 +62,16 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 #define SOCKET_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 constexpr int kTileKeys = 32;
-constexpr int kHashWaves = 8;
+constexpr int kHashWaves = 4;        // one wave per SIMD; two blocks per CU
 constexpr int kHashThreads = kHashWaves * 64;
-constexpr int kRing = 8;              // LDS slots: one tile computed, up to seven in flight
-constexpr int kMaxTilesPerWave = 2;   // 2 x 32 hyperplane columns per wave
+constexpr int kRing = 4;              // LDS slots per block: one tile computed, three in flight
+constexpr int kBlocksPerCU = 2;
+constexpr int kMaxTilesPerWave = 4;   // 4 x 32 hyperplane columns per wave
 constexpr int kMaxColWords = 16;      // L*P <= 512 bits per key
 constexpr int kRtRows = kHashWaves * kMaxTilesPerWave * 32;
 constexpr float kAbsFloor = 0x1p-100f;  // covers flushed float32 denormals
-constexpr int kColBits = 10;            // fix-up entry: (row << 10) | column
+// fix-up entry: (row << 21) | (16-column group << 16) | mask of its columns
+constexpr int kEntryRowShift = 21;
 
 template <int D>
 struct HashGeom {
@@ -167,27 +170,62 @@ __device__ __forceinline__ int jmap(int m) {
 }
 
 // K and V rows of tile `tile` into one ring slot (K at byte 0, V at
-// kTileBytes). Segment g (1 KB) is loaded by wave g % kHashWaves; lane i
-// fills 16-byte position i of it. K rows are stored XOR-swizzled: position
-// q of row r holds chunk q ^ (r & 7). Rows past the end re-read row 0.
+// kTileBytes). Wave w loads the 1 KB segments w, w + kHashWaves, ... of
+// each matrix; lane i fills 16-byte position i of a segment. K rows are
+// stored XOR-swizzled: position q of row r holds chunk q ^ (r & 7).
+template <int D>
+struct DmaLane {
+  static constexpr int kSegsPerMatrix = HashGeom<D>::kDmaPerWave / 2;
+  // rows between a wave's consecutive segments (a multiple of 8, so the
+  // XOR swizzle of a position is the same in all of them)
+  static constexpr int kRowStep = kHashWaves * 64 / HashGeom<D>::CH;
+  static_assert(kSegsPerMatrix == 1 || kRowStep % 8 == 0, "swizzle period");
+  int r0;    // row of this lane's position in the wave's first segment
+  int koff;  // element offset of that position's K chunk in a full tile
+
+  __device__ __forceinline__ DmaLane(int wave, int lane) {
+    using G = HashGeom<D>;
+    const int p = wave * 64 + lane;
+    const int q = p % G::CH;
+    r0 = p / G::CH;
+    koff = r0 * D + (q ^ (r0 & 7)) * 8;
+  }
+};
+
 template <int D>
 __device__ __forceinline__ void dma_tile(const HashArgs& a, int tile, unsigned char* slot,
-                                         int wave, int lane) {
+                                         const DmaLane<D>& dl, int wave) {
   using G = HashGeom<D>;
   const int head = tile / a.tph;
   const int64_t row0 = (int64_t)(tile - head * a.tph) * kTileKeys;
   const int rows = (int)min<int64_t>(kTileKeys, a.n_keys - row0);
-  const int64_t base = ((int64_t)head * a.stride + row0) * D;
+  const uint16_t* kb = a.K + ((int64_t)head * a.stride + row0) * D;
+  const uint16_t* vb = a.V + ((int64_t)head * a.stride + row0) * D;
+  const int voff = (wave * 64 + (threadIdx.x & 63)) * 8;  // V is stored unswizzled
+  if (rows == kTileKeys) {
 #pragma unroll
-  for (int j = 0; j < G::kDmaPerWave; ++j) {
-    const int g = wave + j * kHashWaves;
-    const bool is_v = g >= G::kSegs / 2;
-    const int p = (is_v ? g - G::kSegs / 2 : g) * 64 + lane;
-    const int r = p / G::CH, q = p % G::CH;
-    const int rr = r < rows ? r : 0;
-    const uint16_t* src = is_v ? a.V + base + rr * D + q * 8
-                               : a.K + base + rr * D + (q ^ (r & 7)) * 8;
-    __builtin_amdgcn_global_load_lds((const void*)src, SOCKET_LDS(slot + g * 1024), 16, 0, 0);
+    for (int j = 0; j < DmaLane<D>::kSegsPerMatrix; ++j) {
+      const int g = wave + j * kHashWaves;
+      const int step = j * DmaLane<D>::kRowStep * D;
+      __builtin_amdgcn_global_load_lds((const void*)(kb + dl.koff + step),
+                                       SOCKET_LDS(slot + g * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vb + voff + step),
+                                       SOCKET_LDS(slot + G::kTileBytes + g * 1024), 16, 0, 0);
+    }
+  } else {
+    // last tile of a head: rows past the end re-read row 0 (same count of
+    // loads, so the wait counts stay exact)
+#pragma unroll
+    for (int j = 0; j < DmaLane<D>::kSegsPerMatrix; ++j) {
+      const int g = wave + j * kHashWaves;
+      const int r = dl.r0 + j * DmaLane<D>::kRowStep;
+      const int step = j * DmaLane<D>::kRowStep * D;
+      const int back = r < rows ? 0 : r * D;  // row r -> row 0
+      __builtin_amdgcn_global_load_lds((const void*)(kb + dl.koff + step - back),
+                                       SOCKET_LDS(slot + g * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vb + voff + step - back),
+                                       SOCKET_LDS(slot + G::kTileBytes + g * 1024), 16, 0, 0);
+    }
   }
 }
 
@@ -202,123 +240,126 @@ __device__ __forceinline__ TileRows tile_rows(const HashArgs& a, int tile) {
   return {(int64_t)head * a.stride + row0, (int)min<int64_t>(kTileKeys, a.n_keys - row0)};
 }
 
-// First half of a tile (its slot is valid): the projections on the matrix
-// cores, the squared key norms (into LDS, for the second half) and the
-// value norms (to memory).
-template <int D, int TPW>
-__device__ __forceinline__ void tile_project(const HashArgs& a, int tile,
-                                             const unsigned char* slot,
-                                             const bf16x8_t (&ra)[TPW][HashGeom<D>::S],
-                                             f32x16_t (&acc)[TPW], float* knorm2, int wave,
-                                             int lane) {
+// One 32-key tile from its ring slot: projections on the matrix cores, the
+// certified sign bits and the ids, the key norms (from the B operand already
+// in registers) and the value norms.
+template <int D, int TPW, bool kWordIds>
+__device__ __forceinline__ void hash_tile(const HashArgs& a, int tile, const unsigned char* slot,
+                                          const bf16x8_t (&ra)[TPW][HashGeom<D>::S],
+                                          const float (&rmax)[TPW], uint32_t* bitvec,
+                                          uint32_t* fix_n, unsigned long long* fix_list,
+                                          int wave, int lane) {
   using G = HashGeom<D>;
   constexpr int S = G::S;
-  const int kn = lane & 31, kh = lane >> 5;
-  const uint32_t sbase = lds_offset(slot);
-
-  // B operand: chunks kh*S + s of key row kn (the A rows use the same map),
-  // read four k-steps at a time; the second read overlaps the first MFMAs.
-  // (Column tiles past C multiply zero rows of R^T; their bits are dropped.)
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) acc[t] = f32x16_t{};
-#pragma unroll
-  for (int s0 = 0; s0 < S; s0 += 4) {
-    uint32_t addr[4];
-    u32x4_t kw[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      addr[s] = sbase + kn * (D * 2) + (((kh * S + s0 + s) ^ (kn & 7)) << 4);
-    lds_read4(addr, kw);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int t = 0; t < TPW; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            ra[t][s0 + s], __builtin_bit_cast(bf16x8_t, kw[s]), acc[t], 0, 0, 0);
-    }
-  }
-
-  // key and value norms: wave w takes keys w*4 .. w*4+3, 16 lanes per key,
-  // one 16-byte chunk per lane (the chunk order of a row does not matter)
-  const TileRows tr = tile_rows(a, tile);
-  const int key = wave * 4 + (lane >> 4);
-  const int c = lane & 15;
-  float ks = 0.f, vs = 0.f;
-  if (c < G::CH) {
-    ks = sumsq_bf16x8(lds_read1(sbase + key * (D * 2) + c * 16), 0.f);
-    vs = sumsq_bf16x8(lds_read1(sbase + G::kTileBytes + key * (D * 2) + c * 16), 0.f);
-  }
-  ks = sum16(ks);
-  vs = sum16(vs);
-  if (c == 0) {
-    knorm2[key] = ks;
-    if (key < tr.rows) a.vnorm[tr.grow0 + key] = sqrtf(vs);
-  }
-  (void)kh;
-}
-
-// Second half of a tile, one iteration later (its slot may already be
-// refilled): sign bits, certification, uncertain signs and the ids.
-template <int D, int TPW, bool kWordIds>
-__device__ __forceinline__ void tile_signs(const HashArgs& a, int tile,
-                                           const f32x16_t (&acc)[TPW], const float* knorm2,
-                                           const float (&rmax)[TPW], uint32_t* bitvec,
-                                           uint32_t* fix_n, unsigned long long* fix_list,
-                                           int wave, int lane) {
   constexpr float kGamma = 2.0f * D * 0x1p-24f;
   const int kn = lane & 31, kh = lane >> 5;
+  const uint32_t sbase = lds_offset(slot);
   const TileRows tr = tile_rows(a, tile);
   const int CT = (a.C + 31) >> 5;
-  const float thr_k = kGamma * sqrtf(knorm2[kn]);
-  const bool row_ok = kn < tr.rows;
-  uint32_t half[TPW];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int ct = wave * TPW + t;
-    float mn = fabsf(acc[t][0]);
-#pragma unroll
-    for (int v = 1; v < 16; ++v) mn = fminf(mn, fabsf(acc[t][v]));
-    uint32_t h = 0;
-#pragma unroll
-    for (int v = 15; v >= 0; --v)
-      h = __builtin_amdgcn_alignbit(h, __float_as_uint(acc[t][v]), 31);
-    h = ~h & 0xffffu;  // bit v: projection onto column ct*32 + kh*16 + v is > 0
-    const float thr = thr_k * rmax[t] + kAbsFloor;
-    if (row_ok && ct < CT && mn <= thr) {
-      const int c0 = ct * 32 + kh * 16;
-      uint32_t fm = 0;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        // opaque copy: keeps these compares inside the (rare) branch
-        float y = acc[t][v];
-        asm volatile("" : "+v"(y));
-        if (fabsf(y) <= thr) fm |= 1u << v;
-      }
-      const int valid = min(max(a.C - c0, 0), 16);  // columns of this lane below C
-      fm &= valid >= 16 ? 0xffffu : (1u << valid) - 1u;
-      // Append each to the block's list (LDS counter). The counter is read
-      // first, so it stops just past the capacity (no wrap-around); a count
-      // above the capacity marks the block for the exact re-hash.
-      while (fm != 0) {
-        const int v = __ffs(fm) - 1;
-        fm &= fm - 1;
-        if (*fix_n <= a.fix_cap) {
-          const uint32_t idx = atomicAdd(fix_n, 1u);
-          if (idx < a.fix_cap)
-            fix_list[idx] = ((unsigned long long)(tr.grow0 + kn) << kColBits) |
-                            (unsigned long long)(c0 + v);
-        }
-      }
+
+  // value norms: wave w takes keys w*8 .. w*8+7, 8 lanes per key
+  {
+    const int vkey = wave * 8 + (lane >> 3);
+    u32x4_t vw[G::CH / 8];
+    if constexpr (G::CH / 8 == 2) {
+      const uint32_t addr[4] = {
+          sbase + G::kTileBytes + vkey * (D * 2) + ((lane & 7) << 4),
+          sbase + G::kTileBytes + vkey * (D * 2) + (((lane & 7) + 8) << 4),
+          sbase + G::kTileBytes + vkey * (D * 2) + ((lane & 7) << 4),
+          sbase + G::kTileBytes + vkey * (D * 2) + (((lane & 7) + 8) << 4)};
+      u32x4_t t4[4];
+      lds_read4(addr, t4);
+      vw[0] = t4[0];
+      vw[1] = t4[1];
+    } else {
+      vw[0] = lds_read1(sbase + G::kTileBytes + vkey * (D * 2) + ((lane & 7) << 4));
     }
-    half[t] = h;
+    float vs = 0.f;
+#pragma unroll
+    for (int j = 0; j < G::CH / 8; ++j) vs = sumsq_bf16x8(vw[j], vs);
+    vs += dpp_f32<0xB1>(vs);   // lanes i ^ 1
+    vs += dpp_f32<0x4E>(vs);   // lanes i ^ 2
+    vs += dpp_f32<0x141>(vs);  // the other quad of the half-row
+    if ((lane & 7) == 0 && vkey < tr.rows)
+      a.vnorm[tr.grow0 + vkey] = __builtin_amdgcn_sqrtf(vs);
   }
 
-  // 32-bit words of 32 consecutive sign bits, in both lanes of a key
-  uint32_t word[TPW];
+  // Column tiles in pairs (two accumulators live at a time): the B operand
+  // (chunks kh*S + s of key row kn; the A rows use the same map) is read
+  // four k-steps at a time, again for every pair. The first pass also sums
+  // the squared key entries. (Column tiles past C multiply zero rows of
+  // R^T; their bits are dropped.)
+  const bool row_ok = kn < tr.rows;
+  uint32_t word[TPW];  // 32 consecutive sign bits, in both lanes of a key
+  float ksq = 0.f, thr_k = 0.f;
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const uint32_t o = xor32_u32(half[t]);
-    word[t] = kh ? (o | (half[t] << 16)) : (half[t] | (o << 16));
+  for (int tp = 0; tp < TPW; tp += 2) {
+    f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      uint32_t addr[4];
+      u32x4_t kw[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        addr[s] = sbase + kn * (D * 2) + (((kh * S + s0 + s) ^ (kn & 7)) << 4);
+      lds_read4(addr, kw);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          if (tp + i < TPW)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                ra[tp + i][s0 + s], __builtin_bit_cast(bf16x8_t, kw[s]), acc[i], 0, 0, 0);
+        if (tp == 0) ksq = sumsq_bf16x8(kw[s], ksq);
+      }
+    }
+    if (tp == 0) {
+      ksq += __builtin_bit_cast(float, xor32_u32(__builtin_bit_cast(uint32_t, ksq)));
+      // an upper bound is enough: the hardware square root (1 ulp) rounded up
+      thr_k = kGamma * 1.000001f * __builtin_amdgcn_sqrtf(ksq);
+    }
+
+    // sign bits, certification, uncertain signs
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = tp + i;
+      if (t >= TPW) break;
+      const int ct = wave * TPW + t;
+      float mn = fabsf(acc[i][0]);
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mn = fminf(mn, fabsf(acc[i][v]));
+      uint32_t h = 0;
+#pragma unroll
+      for (int v = 15; v >= 0; --v)
+        h = __builtin_amdgcn_alignbit(h, __float_as_uint(acc[i][v]), 31);
+      h = ~h & 0xffffu;  // bit v: projection onto column ct*32 + kh*16 + v is > 0
+      const float thr = thr_k * rmax[t] + kAbsFloor;
+      if (row_ok && ct < CT && mn <= thr) {
+        // rare: list this key's uncertain columns of the group (mask), with
+        // their float32 signs left in h. thr goes through an opaque move so
+        // the compares stay inside this branch.
+        float thr_r = thr;
+        asm volatile("" : "+v"(thr_r));
+        const int c0 = ct * 32 + kh * 16;
+        uint32_t fm = 0;
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (fabsf(acc[i][v]) <= thr_r) fm |= 1u << v;
+        const int valid = min(max(a.C - c0, 0), 16);  // columns of this lane below C
+        fm &= valid >= 16 ? 0xffffu : (1u << valid) - 1u;
+        // The block's LDS counter is read first, so it stops just past the
+        // capacity (no wrap-around); a count above the capacity marks the
+        // block for the exact re-hash.
+        if (fm != 0 && *fix_n <= a.fix_cap) {
+          const uint32_t idx = atomicAdd(fix_n, 1u);
+          if (idx < a.fix_cap)
+            fix_list[idx] = ((unsigned long long)(tr.grow0 + kn) << kEntryRowShift) |
+                            ((unsigned long long)(c0 >> 4) << 16) | fm;
+        }
+      }
+      const uint32_t o = xor32_u32(h);
+      word[t] = kh ? (o | (h << 16)) : (h | (o << 16));
+    }
   }
   if constexpr (kWordIds) {
     // P == 8: word ct holds the id bytes of tables 4ct .. 4ct+3
@@ -352,13 +393,12 @@ __device__ __forceinline__ void tile_signs(const HashArgs& a, int tile,
 }
 
 template <int D, int TPW, bool kWordIds>
-__global__ __launch_bounds__(kHashThreads) void hash_keys_bf16_kernel(HashArgs a) {
+__global__ __launch_bounds__(kHashThreads, kBlocksPerCU) void hash_keys_bf16_kernel(HashArgs a) {
   using G = HashGeom<D>;
   constexpr int S = G::S;
   constexpr int kWaitSteady = (kRing - 2) * G::kDmaPerWave;
   __shared__ __align__(16) unsigned char ring[kRing * G::kSlotBytes];
   __shared__ uint32_t bitvec[kWordIds ? 1 : kTileKeys * kMaxColWords];
-  __shared__ float knorm2[2][kTileKeys];
   __shared__ uint32_t fix_n;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -390,18 +430,15 @@ __global__ __launch_bounds__(kHashThreads) void hash_keys_bf16_kernel(HashArgs a
     rmax[t] = sqrtf(group_max<64>(sq)) * (1.0f + 0x1p-20f);
   }
 
+  const DmaLane<D> dl(wave, lane);
 #pragma unroll
   for (int j = 0; j < kRing - 1; ++j)
-    if (j < iters) dma_tile<D>(a, b + j * nb, ring + j * G::kSlotBytes, wave, lane);
+    if (j < iters) dma_tile<D>(a, b + j * nb, ring + j * G::kSlotBytes, dl, wave);
 
-  // Two accumulator sets in turn: tile `it` is projected while the signs of
-  // tile it-1 are packed, so the matrix cores and the vector ALUs overlap.
-  f32x16_t acc0[TPW], acc1[TPW];
   for (int it = 0; it < iters; ++it) {
     // this wave's loads into the slot of tile `it` are done once at most the
     // loads of the later tiles are outstanding; the barrier then makes every
-    // wave's part visible, frees the slot computed last round and publishes
-    // the key norms of tile it-1
+    // wave's part visible and frees the slot computed last round
     if (it + kRing - 2 < iters)
       wait_vmcnt<kWaitSteady>();
     else
@@ -409,27 +446,10 @@ __global__ __launch_bounds__(kHashThreads) void hash_keys_bf16_kernel(HashArgs a
     lds_barrier();
     if (it + kRing - 1 < iters)
       dma_tile<D>(a, b + (it + kRing - 1) * nb,
-                  ring + ((it + kRing - 1) % kRing) * G::kSlotBytes, wave, lane);
-    const unsigned char* slot = ring + (it % kRing) * G::kSlotBytes;
-    if ((it & 1) == 0) {
-      tile_project<D, TPW>(a, b + it * nb, slot, ra, acc0, knorm2[0], wave, lane);
-      if (it > 0)
-        tile_signs<D, TPW, kWordIds>(a, b + (it - 1) * nb, acc1, knorm2[1], rmax, bitvec,
-                                     &fix_n, fix_list, wave, lane);
-    } else {
-      tile_project<D, TPW>(a, b + it * nb, slot, ra, acc1, knorm2[1], wave, lane);
-      tile_signs<D, TPW, kWordIds>(a, b + (it - 1) * nb, acc0, knorm2[0], rmax, bitvec,
-                                   &fix_n, fix_list, wave, lane);
-    }
+                  ring + ((it + kRing - 1) % kRing) * G::kSlotBytes, dl, wave);
+    hash_tile<D, TPW, kWordIds>(a, b + it * nb, ring + (it % kRing) * G::kSlotBytes, ra, rmax,
+                                bitvec, &fix_n, fix_list, wave, lane);
   }
-  lds_barrier();
-  const int last = iters - 1;
-  if ((last & 1) == 0)
-    tile_signs<D, TPW, kWordIds>(a, b + last * nb, acc0, knorm2[0], rmax, bitvec, &fix_n,
-                                 fix_list, wave, lane);
-  else
-    tile_signs<D, TPW, kWordIds>(a, b + last * nb, acc1, knorm2[1], rmax, bitvec, &fix_n,
-                                 fix_list, wave, lane);
   lds_barrier();
   if (threadIdx.x == 0) a.fix_count[b] = fix_n;
 }
@@ -445,13 +465,15 @@ __global__ __launch_bounds__(256) void hash_prep_kernel(const uint16_t* __restri
   }
 }
 
-// Settles the listed uncertain projections. Blocks (part, j) take the list
-// region of main-kernel block `part`, kFixBlocksPerPart blocks per region;
-// 16 lanes per entry, each lane D/16 exact products of the key row and the
-// R^T row (one contiguous load each) summed in float64 (the sum of the
-// group's |products| bounds its rounding error); uncertain sums are redone
-// in double-double. The one bit is then set or cleared with an atomic on
-// its 32-bit word.
+// Settles the listed uncertain projections. An entry names a key row, a
+// group of 16 hyperplane columns and the mask of its uncertain columns.
+// Blocks (part, j) take the list region of main-kernel block `part`,
+// kFixBlocksPerPart blocks per region; 16 lanes per entry, which go
+// through the masked columns one by one: each lane takes D/16 exact
+// products of the key row and the R^T row (one contiguous load each), the
+// float64 sum of the group decides the sign unless it is within the
+// rounding bound of the sum of |products| (then double-double decides).
+// The bit is set or cleared with an atomic on its 32-bit word.
 constexpr int kFixBlocksPerPart = 8;
 
 template <int D>
@@ -468,49 +490,56 @@ __global__ __launch_bounds__(256) void hash_fixup_kernel(
   const uint32_t groups = blockDim.x / 16;
   for (uint32_t e = j * groups + threadIdx.x / 16; e < n; e += kFixBlocksPerPart * groups) {
     const unsigned long long ent = plist[e];
-    const int64_t row = (int64_t)(ent >> kColBits);
-    const int col = (int)(ent & ((1u << kColBits) - 1u));
-    uint16_t kv[kPer], rv[kPer];
-    if constexpr (kPer == 8) {
+    const int64_t row = (int64_t)(ent >> kEntryRowShift);
+    const int c0 = (int)((ent >> 16) & 31u) * 16;
+    uint32_t mask = (uint32_t)(ent & 0xffffu);
+    uint16_t kv[kPer];
+    if constexpr (kPer == 8)
       *reinterpret_cast<uint4*>(kv) = *reinterpret_cast<const uint4*>(K + row * D + sub * 8);
-      *reinterpret_cast<uint4*>(rv) = *reinterpret_cast<const uint4*>(RT + col * D + sub * 8);
-    } else {
+    else
       *reinterpret_cast<uint2*>(kv) = *reinterpret_cast<const uint2*>(K + row * D + sub * 4);
-      *reinterpret_cast<uint2*>(rv) = *reinterpret_cast<const uint2*>(RT + col * D + sub * 4);
-    }
-    double p[kPer];
-    double s = 0.0, sa = 0.0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      p[i] = (double)bf16_bits_to_f32(kv[i]) * (double)bf16_bits_to_f32(rv[i]);
-      s += p[i];
-      sa += fabs(p[i]);
-    }
-    // identical sums in all 16 lanes, so the branch below is uniform
-    s = sum16_f64(s);
-    sa = sum16_f64(sa);
-    bool pos;
-    if (fabs(s) > (double)D * 0x1p-52 * sa) {
-      pos = s > 0.0;
-    } else {
-      double h = 0.0, l = 0.0;
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) dd_add(h, l, p[i], 0.0, h, l);
-#pragma unroll
-      for (int m = 8; m >= 1; m >>= 1) {
-        const double oh = __shfl_xor(h, m, kWave), ol = __shfl_xor(l, m, kWave);
-        dd_add(h, l, oh, ol, h, l);
-      }
-      pos = h > 0.0;
-    }
-    if (sub == 0) {
-      const uint64_t byte = (uint64_t)row * L + (uint64_t)(col / P);
-      uint32_t* word = reinterpret_cast<uint32_t*>(ids + (byte & ~(uint64_t)3));
-      const uint32_t bit = 1u << ((byte & 3) * 8 + col % P);
-      if (pos)
-        atomicOr(word, bit);
+    while (mask != 0) {  // same mask in the 16 lanes: uniform
+      const int col = c0 + __ffs(mask) - 1;
+      mask &= mask - 1;
+      uint16_t rv[kPer];
+      if constexpr (kPer == 8)
+        *reinterpret_cast<uint4*>(rv) = *reinterpret_cast<const uint4*>(RT + col * D + sub * 8);
       else
-        atomicAnd(word, ~bit);
+        *reinterpret_cast<uint2*>(rv) = *reinterpret_cast<const uint2*>(RT + col * D + sub * 4);
+      double p[kPer];
+      double s = 0.0, sa = 0.0;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        p[i] = (double)bf16_bits_to_f32(kv[i]) * (double)bf16_bits_to_f32(rv[i]);
+        s += p[i];
+        sa += fabs(p[i]);
+      }
+      // identical sums in all 16 lanes, so the branch below is uniform
+      s = sum16_f64(s);
+      sa = sum16_f64(sa);
+      bool pos;
+      if (fabs(s) > (double)D * 0x1p-52 * sa) {
+        pos = s > 0.0;
+      } else {
+        double h = 0.0, l = 0.0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) dd_add(h, l, p[i], 0.0, h, l);
+#pragma unroll
+        for (int m = 8; m >= 1; m >>= 1) {
+          const double oh = __shfl_xor(h, m, kWave), ol = __shfl_xor(l, m, kWave);
+          dd_add(h, l, oh, ol, h, l);
+        }
+        pos = h > 0.0;
+      }
+      if (sub == 0) {
+        const uint64_t byte = (uint64_t)row * L + (uint64_t)(col / P);
+        uint32_t* word = reinterpret_cast<uint32_t*>(ids + (byte & ~(uint64_t)3));
+        const uint32_t bit = 1u << ((byte & 3) * 8 + col % P);
+        if (pos)
+          atomicOr(word, bit);
+        else
+          atomicAnd(word, ~bit);
+      }
     }
   }
 }
@@ -612,7 +641,7 @@ __global__ __launch_bounds__(256) void hash_keys_f32_kernel(
 
 // --------------------------------------------------------------- launchers
 
-constexpr int kMaxHashBlocks = 256;  // one block per CU
+constexpr int kMaxHashBlocks = 256 * kBlocksPerCU;
 
 struct HashWs {
   uint16_t* rt;
@@ -636,7 +665,7 @@ HashWs hash_ws_layout(void* ws, int64_t n_total, int d, int C) {
 
 template <int D, int TPW, bool kWordIds>
 void launch_main(const HashArgs& a, hipStream_t stream) {
-  // one block per CU (the ring takes most of the 160 KB of LDS)
+  // two blocks per CU (each ring takes 64 KB of the 160 KB of LDS)
   const int grid = std::min(a.n_tiles, kMaxHashBlocks);
   launch_kernel((hash_keys_bf16_kernel<D, TPW, kWordIds>), dim3(grid), dim3(kHashThreads), 0,
                 stream, a);
@@ -650,6 +679,8 @@ void launch_main_d(const HashArgs& a, int tpw, bool word_ids, hipStream_t stream
   case 2 * t + 1: launch_main<D, t, true>(a, stream); break;
     SOCKET_HASH_CASE(1)
     SOCKET_HASH_CASE(2)
+    SOCKET_HASH_CASE(3)
+    SOCKET_HASH_CASE(4)
 #undef SOCKET_HASH_CASE
     default: break;
   }
