@@ -31,12 +31,13 @@
 //  3. fix-up: a sign is certified when |y| exceeds the worst-case float32
 //     summation error 2*d*2^-24*|k|*max|r| (plus a floor for flushed
 //     denormals). Uncertain projections (about 1.5e-4 of them for random
-//     data) are appended by the main kernel to a per-block list in the
-//     workspace (one entry per key and 16-column group, with a mask) with
-//     their float32 sign written; the fix-up kernel recomputes each one from
+//     data) are appended by the main kernel to a per-wave list in the
+//     workspace (one entry per key and 16-column group, with a mask; slots
+//     from ballot prefix counts) with their float32 sign written; the fix-up
+//     kernel recomputes each one from
 //     the bf16 inputs (float64 sum of exact products, certified, with a
 //     double-double fallback) and sets or clears that one bit with an atomic
-//     AND/OR. A block whose list overflows (or any block with an uncertain
+//     AND/OR. A block with an overflowing list (or any block with an uncertain
 //     sign when id rows are not whole 4-byte words) has all its tiles
 //     re-hashed exactly by a fourth kernel (float64 / double-double, one
 //     thread per key and table), which exits at once when nothing
@@ -94,9 +95,9 @@ struct HashArgs {
   int L, P, C;
   uint8_t* ids;
   float* vnorm;
-  unsigned long long* fix_list;  // [grid][fix_cap] entries, one region per block
-  uint32_t* fix_count;           // [grid] entries each block appended
-  uint32_t fix_cap;  // per block; 0: settle every uncertain sign in the main kernel
+  unsigned long long* fix_list;  // [grid * kHashWaves][fix_cap] entries, one region per wave
+  uint32_t* fix_count;           // [grid * kHashWaves] entries each wave appended
+  uint32_t fix_cap;  // per wave; 0: the block is re-hashed exactly when any sign is uncertain
 };
 
 // s_waitcnt with only the vector-memory counter limited (gfx9 encoding:
@@ -247,7 +248,7 @@ template <int D, int TPW, bool kWordIds>
 __device__ __forceinline__ void hash_tile(const HashArgs& a, int tile, const unsigned char* slot,
                                           const bf16x8_t (&ra)[TPW][HashGeom<D>::S],
                                           const float (&rmax)[TPW], uint32_t* bitvec,
-                                          uint32_t* fix_n, unsigned long long* fix_list,
+                                          uint32_t& fix_n, unsigned long long* fix_list,
                                           int wave, int lane) {
   using G = HashGeom<D>;
   constexpr int S = G::S;
@@ -334,28 +335,29 @@ __device__ __forceinline__ void hash_tile(const HashArgs& a, int tile, const uns
         h = __builtin_amdgcn_alignbit(h, __float_as_uint(acc[i][v]), 31);
       h = ~h & 0xffffu;  // bit v: projection onto column ct*32 + kh*16 + v is > 0
       const float thr = thr_k * rmax[t] + kAbsFloor;
-      if (row_ok && ct < CT && mn <= thr) {
-        // rare: list this key's uncertain columns of the group (mask), with
-        // their float32 signs left in h. thr goes through an opaque move so
-        // the compares stay inside this branch.
-        float thr_r = thr;
-        asm volatile("" : "+v"(thr_r));
+      // Rare: some lanes hold projections too close to zero for their float32
+      // sign. Each such key lists its group of 16 columns with the mask of
+      // uncertain ones (float32 signs stay in h) in the wave's own region:
+      // slots from a ballot prefix count, no atomics. The count runs on past
+      // the capacity, which marks the block for the exact re-hash.
+      const bool cand = row_ok && ct < CT && mn <= thr;
+      if (__ballot(cand) != 0) {
         const int c0 = ct * 32 + kh * 16;
         uint32_t fm = 0;
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          if (fabsf(acc[i][v]) <= thr_r) fm |= 1u << v;
+          if (fabsf(acc[i][v]) <= thr) fm |= 1u << v;
         const int valid = min(max(a.C - c0, 0), 16);  // columns of this lane below C
         fm &= valid >= 16 ? 0xffffu : (1u << valid) - 1u;
-        // The block's LDS counter is read first, so it stops just past the
-        // capacity (no wrap-around); a count above the capacity marks the
-        // block for the exact re-hash.
-        if (fm != 0 && *fix_n <= a.fix_cap) {
-          const uint32_t idx = atomicAdd(fix_n, 1u);
-          if (idx < a.fix_cap)
-            fix_list[idx] = ((unsigned long long)(tr.grow0 + kn) << kEntryRowShift) |
-                            ((unsigned long long)(c0 >> 4) << 16) | fm;
-        }
+        if (!cand) fm = 0;
+        const uint64_t bal = __ballot(fm != 0);
+        const uint32_t pos =
+            fix_n + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        if (fm != 0 && pos < a.fix_cap)
+          fix_list[pos] = ((unsigned long long)(tr.grow0 + kn) << kEntryRowShift) |
+                          ((unsigned long long)(c0 >> 4) << 16) | fm;
+        fix_n += (uint32_t)__popcll(bal);
       }
       const uint32_t o = xor32_u32(h);
       word[t] = kh ? (o | (h << 16)) : (h | (o << 16));
@@ -399,7 +401,6 @@ __global__ __launch_bounds__(kHashThreads, kBlocksPerCU) void hash_keys_bf16_ker
   constexpr int kWaitSteady = (kRing - 2) * G::kDmaPerWave;
   __shared__ __align__(16) unsigned char ring[kRing * G::kSlotBytes];
   __shared__ uint32_t bitvec[kWordIds ? 1 : kTileKeys * kMaxColWords];
-  __shared__ uint32_t fix_n;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kn = lane & 31, kh = lane >> 5;
@@ -407,8 +408,9 @@ __global__ __launch_bounds__(kHashThreads, kBlocksPerCU) void hash_keys_bf16_ker
   const int b = blockIdx.x;
   if (b >= a.n_tiles) return;
   const int iters = (a.n_tiles - b + nb - 1) / nb;  // tiles b, b + nb, ...
-  unsigned long long* const fix_list = a.fix_list + (size_t)b * a.fix_cap;
-  if (threadIdx.x == 0) fix_n = 0u;  // ordered by the first barrier below
+  const int part = b * kHashWaves + wave;  // this wave's list region
+  unsigned long long* const fix_list = a.fix_list + (size_t)part * a.fix_cap;
+  uint32_t fix_n = 0;  // wave-uniform count of listed entries
 
   // stationary A operand: R^T rows of this wave's column tiles
   bf16x8_t ra[TPW][S];
@@ -448,10 +450,9 @@ __global__ __launch_bounds__(kHashThreads, kBlocksPerCU) void hash_keys_bf16_ker
       dma_tile<D>(a, b + (it + kRing - 1) * nb,
                   ring + ((it + kRing - 1) % kRing) * G::kSlotBytes, dl, wave);
     hash_tile<D, TPW, kWordIds>(a, b + it * nb, ring + (it % kRing) * G::kSlotBytes, ra, rmax,
-                                bitvec, &fix_n, fix_list, wave, lane);
+                                bitvec, fix_n, fix_list, wave, lane);
   }
-  lds_barrier();
-  if (threadIdx.x == 0) a.fix_count[b] = fix_n;
+  if (lane == 0) a.fix_count[part] = fix_n;
 }
 
 // R [d, C] -> R^T [kRtRows, d] with zero rows past C.
@@ -467,14 +468,14 @@ __global__ __launch_bounds__(256) void hash_prep_kernel(const uint16_t* __restri
 
 // Settles the listed uncertain projections. An entry names a key row, a
 // group of 16 hyperplane columns and the mask of its uncertain columns.
-// Blocks (part, j) take the list region of main-kernel block `part`,
-// kFixBlocksPerPart blocks per region; 16 lanes per entry, which go
+// Blocks (blk, j) take the list regions of the waves of main-kernel block
+// `blk`, kFixBlocksPerPart blocks per main block; 16 lanes per entry, which go
 // through the masked columns one by one: each lane takes D/16 exact
 // products of the key row and the R^T row (one contiguous load each), the
 // float64 sum of the group decides the sign unless it is within the
 // rounding bound of the sum of |products| (then double-double decides).
 // The bit is set or cleared with an atomic on its 32-bit word.
-constexpr int kFixBlocksPerPart = 8;
+constexpr int kFixBlocksPerPart = 16;
 
 template <int D>
 __global__ __launch_bounds__(256) void hash_fixup_kernel(
@@ -482,14 +483,27 @@ __global__ __launch_bounds__(256) void hash_fixup_kernel(
     uint8_t* __restrict__ ids, const unsigned long long* __restrict__ list,
     const uint32_t* __restrict__ count, uint32_t cap) {
   constexpr int kPer = D / 16;  // dims per lane: 8 (one 16-byte load) or 4
-  const int part = blockIdx.x / kFixBlocksPerPart;
+  const int blk = blockIdx.x / kFixBlocksPerPart;
   const int j = blockIdx.x % kFixBlocksPerPart;
-  const uint32_t n = min(count[part], cap);
-  const unsigned long long* plist = list + (size_t)part * cap;
   const int sub = threadIdx.x & 15;
   const uint32_t groups = blockDim.x / 16;
-  for (uint32_t e = j * groups + threadIdx.x / 16; e < n; e += kFixBlocksPerPart * groups) {
-    const unsigned long long ent = plist[e];
+  // the block's regions back to back as one index range
+  uint32_t n[kHashWaves], total = 0;
+#pragma unroll
+  for (int w = 0; w < kHashWaves; ++w) {
+    n[w] = min(count[blk * kHashWaves + w], cap);
+    total += n[w];
+  }
+  for (uint32_t e = j * groups + threadIdx.x / 16; e < total; e += kFixBlocksPerPart * groups) {
+    uint32_t idx = e;
+    int part = blk * kHashWaves;
+#pragma unroll
+    for (int w = 0; w < kHashWaves - 1; ++w)
+      if (idx >= n[w] && part == blk * kHashWaves + w) {
+        idx -= n[w];
+        ++part;
+      }
+    const unsigned long long ent = list[(size_t)part * cap + idx];
     const int64_t row = (int64_t)(ent >> kEntryRowShift);
     const int c0 = (int)((ent >> 16) & 31u) * 16;
     uint32_t mask = (uint32_t)(ent & 0xffffu);
@@ -555,10 +569,12 @@ __global__ __launch_bounds__(256) void hash_redo_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ R, int64_t n_keys,
     int64_t stride, int tph, int n_tiles, int nb, int L, int P, uint8_t* __restrict__ ids,
     const uint32_t* __restrict__ count, uint32_t cap) {
-  const int part = blockIdx.x;
-  if (count[part] <= cap) return;
+  const int blk = blockIdx.x;
+  bool over = false;
+  for (int w = 0; w < kHashWaves; ++w) over |= count[blk * kHashWaves + w] > cap;
+  if (!over) return;
   const int C = L * P;
-  for (int tile = part; tile < n_tiles; tile += nb) {
+  for (int tile = blk; tile < n_tiles; tile += nb) {
     const int head = tile / tph;
     const int64_t row0 = (int64_t)(tile - head * tph) * kTileKeys;
     const int rows = (int)min<int64_t>(kTileKeys, n_keys - row0);
@@ -645,8 +661,8 @@ constexpr int kMaxHashBlocks = 256 * kBlocksPerCU;
 
 struct HashWs {
   uint16_t* rt;
-  uint32_t* count;            // [kMaxHashBlocks]
-  unsigned long long* list;   // [kMaxHashBlocks][cap]
+  uint32_t* count;            // [kMaxHashBlocks * kHashWaves]
+  unsigned long long* list;   // [kMaxHashBlocks * kHashWaves][cap]
   uint32_t cap;               // entries per block
 };
 
@@ -657,9 +673,9 @@ HashWs hash_ws_layout(void* ws, int64_t n_total, int d, int C) {
   w.rt = reinterpret_cast<uint16_t*>(p + off);
   off = align256(off + (size_t)kRtRows * d * sizeof(uint16_t));
   w.count = reinterpret_cast<uint32_t*>(p + off);
-  off = align256(off + kMaxHashBlocks * sizeof(uint32_t));
+  off = align256(off + kMaxHashBlocks * kHashWaves * sizeof(uint32_t));
   w.list = reinterpret_cast<unsigned long long*>(p + off);
-  w.cap = hash_fix_capacity(n_total, C) / kMaxHashBlocks;
+  w.cap = hash_fix_capacity(n_total, C) / (kMaxHashBlocks * kHashWaves);
   return w;
 }
 
@@ -695,9 +711,9 @@ uint32_t hash_fix_capacity(int64_t n_total, int C) {
 
 size_t hash_keys_bf16_workspace_bytes(int64_t n_total, int d, int C) {
   size_t off = align256((size_t)kRtRows * d * sizeof(uint16_t));
-  off = align256(off + kMaxHashBlocks * sizeof(uint32_t));
-  return off + (size_t)(hash_fix_capacity(n_total, C) / kMaxHashBlocks) * kMaxHashBlocks *
-                   sizeof(unsigned long long);
+  off = align256(off + kMaxHashBlocks * kHashWaves * sizeof(uint32_t));
+  const size_t parts = (size_t)kMaxHashBlocks * kHashWaves;
+  return off + (hash_fix_capacity(n_total, C) / parts) * parts * sizeof(unsigned long long);
 }
 
 hipError_t launch_hash_keys_bf16(const uint16_t* K, const uint16_t* V,
@@ -738,9 +754,9 @@ hipError_t launch_hash_keys_bf16(const uint16_t* K, const uint16_t* V,
     launch_main_d<128>(a, tpw, word_ids, stream);
   else
     launch_main_d<64>(a, tpw, word_ids, stream);
-  const int parts = std::min(a.n_tiles, kMaxHashBlocks);
+  const int blocks = std::min(a.n_tiles, kMaxHashBlocks);
   if (a.fix_cap != 0) {
-    const dim3 fgrid(parts * kFixBlocksPerPart);
+    const dim3 fgrid(blocks * kFixBlocksPerPart);
     if (d == 128)
       launch_kernel(hash_fixup_kernel<128>, fgrid, dim3(256), 0, stream, K, w.rt, C, L, P,
                     ids, w.list, w.count, a.fix_cap);
@@ -749,11 +765,11 @@ hipError_t launch_hash_keys_bf16(const uint16_t* K, const uint16_t* V,
                     ids, w.list, w.count, a.fix_cap);
   }
   if (d == 128)
-    launch_kernel(hash_redo_kernel<128>, dim3(parts), dim3(256), 0, stream, K, R, n_keys,
-                  stride, a.tph, a.n_tiles, parts, L, P, ids, w.count, a.fix_cap);
+    launch_kernel(hash_redo_kernel<128>, dim3(blocks), dim3(256), 0, stream, K, R, n_keys,
+                  stride, a.tph, a.n_tiles, blocks, L, P, ids, w.count, a.fix_cap);
   else
-    launch_kernel(hash_redo_kernel<64>, dim3(parts), dim3(256), 0, stream, K, R, n_keys,
-                  stride, a.tph, a.n_tiles, parts, L, P, ids, w.count, a.fix_cap);
+    launch_kernel(hash_redo_kernel<64>, dim3(blocks), dim3(256), 0, stream, K, R, n_keys,
+                  stride, a.tph, a.n_tiles, blocks, L, P, ids, w.count, a.fix_cap);
   return hipGetLastError();
 }
 
