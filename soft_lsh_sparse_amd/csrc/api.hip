@@ -372,7 +372,7 @@ socket_status decode_impl(const void* Q, const void* K, const void* V,
   uint32_t* hist = reinterpret_cast<uint32_t*>(tws + lay.topk.hist_off);
   hipError_t err = launch_bucket_probs(
       Q, R, bf16, B, Hq, Hkv, d, L, P, tau, table, fused_hist ? hist : nullptr,
-      fused_hist ? (int64_t)B * Hq * kHistBins : 0, s);
+      fused_hist ? lay.topk.zero_words : 0, s);
   if (err != hipSuccess) return from_hip(err, "socket_decode: bucket_probs");
   err = launch_score(table, ids, vnorm, B, Hq, Hkv, n_keys, head_stride_rows, L, P,
                      scores, fused_hist ? hist : nullptr, s);

@@ -117,6 +117,20 @@ __device__ __forceinline__ double sum16_f64(double v) {
   return v;
 }
 
+// Inclusive prefix sum over the wave (lane i gets x_0 + ... + x_i): shifts
+// by 1, 2, 4 and 8 within each row of 16 lanes, then the row totals are
+// carried across rows with two broadcasts. Lanes a shift leaves without a
+// source add 0.
+__device__ __forceinline__ uint32_t wave_inclusive_scan_dpp(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // The value of lane i ^ 32 (v_permlane32_swap: the two half-waves trade).
 __device__ __forceinline__ uint32_t xor32_u32(uint32_t v) {
   const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);

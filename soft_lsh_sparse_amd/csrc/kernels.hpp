@@ -77,9 +77,12 @@ constexpr size_t kLdsBytesPerCU = 160 * 1024;
 struct TopkPlan {
   int rows;
   int64_t n, kk;
-  int segs;
-  int64_t seg_len;
+  int segs;          // blocks per row
+  int64_t seg_len;   // scores per block
+  int subs;          // sub-lists per row (one per wave)
+  int64_t sub_len;   // scores per wave
   size_t hist_off, cnt_off, list_off, total_bytes;
+  int64_t zero_words;  // words from hist_off that must be zero before a call
 };
 TopkPlan plan_topk(int rows, int64_t n, int64_t k);
 constexpr int kHistBins = 2048;

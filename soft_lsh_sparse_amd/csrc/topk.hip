@@ -18,11 +18,13 @@
 //            (order-independent, so the result is deterministic). The score
 //            kernel can produce this histogram itself.
 //  2. filter (rows x segments blocks): every block finds the bin b1 that
-//            holds the kk-th key, then compacts the (u, index) pairs of its
-//            segment with digit >= b1, in index order (wave ballots and a
-//            block scan), into the segment's slice of the row's list.
-//  3. refine (one block per row): two more radix passes over the candidates
-//            of bin b1 give the exact threshold T and the number m of keys
+//            holds the kk-th key; each wave then compacts the (u, index)
+//            pairs of its sub-segment with digit >= b1, in index order (four
+//            ballots and lane prefix counts per step), into its own sub-list
+//            of the row's list.
+//  3. refine (one block per row): the sub-lists are copied back to back
+//            into LDS; two more radix passes over the candidates of bin b1
+//            give the exact threshold T and the number m of keys
 //            equal to T that still have to be taken. A final in-order pass
 //            keeps every key with u > T and the first m keys with u == T,
 //            and writes their indices at positions given by a block scan,
@@ -36,9 +38,10 @@
 namespace socket_lsh {
 namespace {
 
-constexpr int kFilterThreads = 256;
-constexpr int kRefineThreads = 1024;
-constexpr int kFilterUnroll = 4;  // 16-byte loads per thread per iteration
+constexpr int kFilterThreads = 256;   // histogram kernel
+constexpr int kSelectThreads = 256;   // filter kernel (4 waves, one sub-list each)
+constexpr int kRefineThreads = 1024;  // refine kernel (one block per row)
+constexpr int kMaxSubLists = 256;     // per row
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & 63;
@@ -46,29 +49,23 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 }
 
 // Exclusive scan of one uint32 per thread over the block; returns the
-// thread's exclusive prefix and writes the block total to *total.
+// thread's exclusive prefix and writes the block total to *total. Wave scans
+// with DPP; the wave totals are scanned by the first wave the same way.
 // `scratch` needs blockDim/64 + 1 words. Contains __syncthreads().
 template <int NT>
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch,
                                          uint32_t* total) {
   constexpr int NWV = NT / 64;
+  static_assert(NWV <= 64, "one wave scans the wave totals");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off, kWave);
-    if (lane >= off) x += y;
-  }
+  const uint32_t x = wave_inclusive_scan_dpp(v);
   if (lane == 63) scratch[wave] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int w = 0; w < NWV; ++w) {
-      const uint32_t t = scratch[w];
-      scratch[w] = run;
-      run += t;
-    }
-    scratch[NWV] = run;
+  if (wave == 0) {
+    const uint32_t t = lane < NWV ? scratch[lane] : 0u;
+    const uint32_t inc = wave_inclusive_scan_dpp(t);
+    if (lane < NWV) scratch[lane] = inc - t;
+    if (lane == 63) scratch[NWV] = inc;
   }
   __syncthreads();
   const uint32_t res = scratch[wave] + x - v;
@@ -127,181 +124,114 @@ __global__ __launch_bounds__(kFilterThreads) void topk_hist_kernel(
     if (h[i]) atomicAdd(hr + i, h[i]);
 }
 
-// Wave-inclusive scan of one uint32 per lane.
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off, kWave);
-    if (lane >= off) x += y;
-  }
-  return x;
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ uint32_t lane_prefix(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-__global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(
-    const float* __restrict__ scores, int64_t n, int64_t kk, int segs,
-    int64_t seg_len, const uint32_t* __restrict__ hist,
-    uint2* __restrict__ lists, uint32_t* __restrict__ seg_cnt, int vec4) {
-  constexpr int NWV = kFilterThreads / 64;
-  constexpr int E = kFilterUnroll;
-  __shared__ uint32_t scratch[kFilterThreads / 64 + 1];
-  __shared__ uint32_t thr[2];
-  __shared__ uint32_t wtot[E * NWV];
-  __shared__ uint32_t woff[E * NWV + 1];
-  const int row = blockIdx.y, seg = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-
-  find_threshold_bin<kFilterThreads>(hist + (int64_t)row * kHistBins,
-                                     (uint32_t)kk, scratch, thr);
-  const uint32_t b1 = thr[0];
-
-  const float* s = scores + (int64_t)row * n;
-  const int64_t n0 = (int64_t)seg * seg_len;
-  const int64_t n1 = min(n, n0 + seg_len);
-  uint2* out = lists + (int64_t)row * n + n0;
-  uint32_t count = 0;
-  // Each thread takes 4 consecutive scores per step (one 16-byte load);
-  // element order within an iteration is (step, thread, lane-element), i.e.
-  // ascending index, and the compaction preserves it.
-  for (int64_t base = n0; base < n1; base += (int64_t)kFilterThreads * 4 * E) {
-    uint32_t u[E][4];
-    uint32_t fl[E];
-    uint32_t excl[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int64_t i0 = base + ((int64_t)e * kFilterThreads + threadIdx.x) * 4;
-      float v[4];
-      if (vec4 && i0 + 3 < n1) {
-        const float4 x = *reinterpret_cast<const float4*>(s + i0);
-        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = i0 + i < n1 ? s[i0 + i] : 0.f;
-      }
-      uint32_t f = 0, c = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u[e][i] = float_order_key(v[i]);
-        if (i0 + i < n1 && (u[e][i] >> 21) >= b1) {
-          f |= 1u << i;
-          ++c;
-        }
-      }
-      fl[e] = f;
-      const uint32_t inc = wave_inclusive_scan(c);
-      excl[e] = inc - c;
-      if (lane == 63) wtot[e * NWV + wave] = inc;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t run = 0;
-      for (int q = 0; q < E * NWV; ++q) {
-        woff[q] = run;
-        run += wtot[q];
-      }
-      woff[E * NWV] = run;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      uint32_t pos = count + woff[e * NWV + wave] + excl[e];
-      const int64_t i0 = base + ((int64_t)e * kFilterThreads + threadIdx.x) * 4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (fl[e] & (1u << i)) {
-          out[pos] = make_uint2(u[e][i], (uint32_t)(i0 + i));
-          ++pos;
-        }
-      }
-    }
-    count += woff[E * NWV];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) seg_cnt[(int64_t)row * segs + seg] = count;
-}
-
-// Element p (0 <= p < total) of the concatenated segment lists of a row:
-// from the LDS copy when the row's candidates fit there, else from HBM.
+// Element p (0 <= p < total) of the concatenated sub-lists of a row: from
+// the LDS copy when the row's candidates fit there, else from memory.
 struct RowLists {
-  const uint2* glob;      // row's list area (segment s at s * seg_len)
-  const uint2* cache;     // LDS copy in list order, or nullptr
-  const uint32_t* off;    // segment offsets in the concatenation (LDS)
-  int segs;
-  int64_t seg_len;
+  const uint2* glob;      // row's list area (sub-list s at s * sub_len)
+  const uint2* cache;     // LDS copy of the first `cached` entries
+  uint32_t cached;
+  const uint32_t* off;    // sub-list offsets in the concatenation (LDS)
+  int subs;
+  int64_t sub_len;
   __device__ __forceinline__ uint2 at(uint32_t p) const {
-    if (cache) return cache[p];
-    int lo = 0, hi = segs - 1;  // last segment with off[s] <= p
+    if (p < cached) return cache[p];
+    int lo = 0, hi = subs - 1;  // last sub-list with off[s] <= p
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (off[mid] <= p) lo = mid; else hi = mid - 1;
     }
-    return glob[(int64_t)lo * seg_len + (p - off[lo])];
+    return glob[(int64_t)lo * sub_len + (p - off[lo])];
   }
 };
 
 constexpr int kRefineCache = 10240;  // (u, index) pairs kept in LDS (80 KB)
 
+struct RefineShared {
+  uint32_t scratch[kRefineThreads / 64 + 1];
+  uint32_t thr[2];
+  uint32_t h[kHistBins];
+  uint32_t off[kMaxSubLists + 1];
+  uint2 cache[kRefineCache];
+};
+
+// One block per row: passes 2 and 3 of the radix select over the row's
+// candidates (all keys of first-digit bin b1 or above, in index order: the
+// sub-lists back to back) and the in-order emit of the kk selected indices.
+// The candidates are first copied into LDS sub-list by sub-list (one wave
+// per sub-list, contiguous reads); a row with more candidates than fit reads
+// the rest from memory.
 __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
-    int64_t n, int64_t kk, int segs, int64_t seg_len,
-    const uint32_t* __restrict__ hist, const uint2* __restrict__ lists,
-    const uint32_t* __restrict__ seg_cnt, int32_t* __restrict__ idx) {
-  __shared__ uint32_t scratch[kRefineThreads / 64 + 1];
-  __shared__ uint32_t thr[2];
-  __shared__ uint32_t h[kHistBins];
-  __shared__ uint32_t off[65];
-  __shared__ uint2 cache[kRefineCache];
+    int64_t n, int64_t kk, int subs, int64_t sub_len, const uint32_t* __restrict__ hist,
+    const uint2* __restrict__ lists, const uint32_t* __restrict__ sub_cnt,
+    int32_t* __restrict__ idx) {
+  constexpr int NT = kRefineThreads;
+  __shared__ RefineShared sh;
   const int row = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-  find_threshold_bin<kRefineThreads>(hist + (int64_t)row * kHistBins,
-                                     (uint32_t)kk, scratch, thr);
-  const uint32_t b1 = thr[0];
-  const uint32_t need1 = (uint32_t)kk - thr[1];
+  find_threshold_bin<NT>(hist + (int64_t)row * kHistBins, (uint32_t)kk, sh.scratch, sh.thr);
+  const uint32_t b1 = sh.thr[0];
+  const uint32_t need1 = (uint32_t)kk - sh.thr[1];
 
-  if (threadIdx.x < 64) {  // segment offsets: one wave-wide scan (segs <= 64)
-    const uint32_t c = threadIdx.x < segs ? seg_cnt[(int64_t)row * segs + threadIdx.x] : 0u;
-    const uint32_t inc = wave_inclusive_scan(c);
-    if (threadIdx.x < segs) off[threadIdx.x] = inc - c;
-    if (threadIdx.x == 63) off[segs] = inc;
+  // sub-list offsets (subs <= kMaxSubLists <= NT)
+  {
+    const uint32_t c = threadIdx.x < subs ? sub_cnt[(int64_t)row * subs + threadIdx.x] : 0u;
+    uint32_t total;
+    const uint32_t ex = block_exclusive_scan<NT>(c, sh.scratch, &total);
+    if (threadIdx.x < subs) sh.off[threadIdx.x] = ex;
+    if (threadIdx.x == 0) sh.off[subs] = total;
   }
   __syncthreads();
-  const uint32_t total = off[segs];
+  const uint32_t total = sh.off[subs];
 
-  RowLists rl{lists + (int64_t)row * n, nullptr, off, segs, seg_len};
-  if (total <= (uint32_t)kRefineCache) {
-    for (uint32_t p = threadIdx.x; p < total; p += kRefineThreads) cache[p] = rl.at(p);
+  const uint2* rowlists = lists + (int64_t)row * n;
+  RowLists rl{rowlists, sh.cache, 0u, sh.off, subs, sub_len};
+  {
+    const uint32_t cached = min(total, (uint32_t)kRefineCache);
+    for (int sl = wave; sl < subs; sl += NT / 64) {
+      const uint32_t o = sh.off[sl], c = sh.off[sl + 1] - o;
+      const uint2* src = rowlists + (int64_t)sl * sub_len;
+      for (uint32_t i = lane; i < c && o + i < cached; i += 64) sh.cache[o + i] = src[i];
+    }
     __syncthreads();
-    rl.cache = cache;
+    rl.cached = cached;
   }
 
   // pass 2: bits 20..10 of the candidates in bin b1
-  for (int i = threadIdx.x; i < kHistBins; i += kRefineThreads) h[i] = 0;
+  for (int i = threadIdx.x; i < kHistBins; i += NT) sh.h[i] = 0;
   __syncthreads();
-  for (uint32_t p = threadIdx.x; p < total; p += kRefineThreads) {
+  for (uint32_t p = threadIdx.x; p < total; p += NT) {
     const uint2 e = rl.at(p);
-    if ((e.x >> 21) == b1) atomicAdd(&h[(e.x >> 10) & 2047u], 1u);
+    if ((e.x >> 21) == b1) atomicAdd(&sh.h[(e.x >> 10) & 2047u], 1u);
   }
   __syncthreads();
-  find_threshold_bin<kRefineThreads>(h, need1, scratch, thr);
-  const uint32_t b2 = thr[0];
-  const uint32_t need2 = need1 - thr[1];
+  find_threshold_bin<NT>(sh.h, need1, sh.scratch, sh.thr);
+  const uint32_t b2 = sh.thr[0];
+  const uint32_t need2 = need1 - sh.thr[1];
   const uint32_t pre2 = (b1 << 11) | b2;  // u >> 10 of the survivors
 
   // pass 3: bits 9..0
-  for (int i = threadIdx.x; i < kHistBins; i += kRefineThreads) h[i] = 0;
+  for (int i = threadIdx.x; i < kHistBins; i += NT) sh.h[i] = 0;
   __syncthreads();
-  for (uint32_t p = threadIdx.x; p < total; p += kRefineThreads) {
+  for (uint32_t p = threadIdx.x; p < total; p += NT) {
     const uint2 e = rl.at(p);
-    if ((e.x >> 10) == pre2) atomicAdd(&h[e.x & 1023u], 1u);
+    if ((e.x >> 10) == pre2) atomicAdd(&sh.h[e.x & 1023u], 1u);
   }
   __syncthreads();
-  find_threshold_bin<kRefineThreads>(h, need2, scratch, thr);
-  const uint32_t T = (pre2 << 10) | thr[0];
-  const uint32_t ties = need2 - thr[1];  // keys equal to T still to take
+  find_threshold_bin<NT>(sh.h, need2, sh.scratch, sh.thr);
+  const uint32_t T = (pre2 << 10) | sh.thr[0];
+  const uint32_t ties = need2 - sh.thr[1];  // keys equal to T still to take
 
-  // final pass, in index order: each thread takes 4 consecutive list entries
+  // final pass, in index order: each thread takes 4 consecutive entries
   int32_t* o = idx + (int64_t)row * kk;
   uint32_t run_tie = 0, run_out = 0;
-  for (uint32_t base = 0; base < total; base += 4 * kRefineThreads) {
+  for (uint32_t base = 0; base < total; base += 4 * NT) {
     uint2 e[4];
     uint32_t n_tie = 0;
 #pragma unroll
@@ -311,7 +241,7 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
       if (p < total && e[i].x == T) ++n_tie;
     }
     uint32_t tie_tot;
-    uint32_t tie_rank = run_tie + block_exclusive_scan<kRefineThreads>(n_tie, scratch, &tie_tot);
+    uint32_t tie_rank = run_tie + block_exclusive_scan<NT>(n_tie, sh.scratch, &tie_tot);
     bool sel[4];
     uint32_t n_sel = 0;
 #pragma unroll
@@ -326,7 +256,7 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
       n_sel += sel[i] ? 1u : 0u;
     }
     uint32_t sel_tot;
-    uint32_t pos = run_out + block_exclusive_scan<kRefineThreads>(n_sel, scratch, &sel_tot);
+    uint32_t pos = run_out + block_exclusive_scan<NT>(n_sel, sh.scratch, &sel_tot);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (sel[i]) {
@@ -337,6 +267,75 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
     run_tie += tie_tot;
     run_out += sel_tot;
   }
+}
+
+// Filter. Block (seg, row) finds the bin b1 of the kk-th key from the
+// row's first-digit histogram; each wave then streams its sub-segment of
+// sub_len scores (64 lanes x 4 consecutive scores per step, eight steps of
+// loads in flight) and appends the (u, index) pairs with digit >= b1 to its
+// own sub-list in index order, the slots coming from four ballots and lane
+// prefix counts (no block synchronisation after the threshold).
+__global__ __launch_bounds__(kSelectThreads) void topk_filter_kernel(
+    const float* __restrict__ scores, int64_t n, int64_t kk, int segs, int64_t sub_len,
+    const uint32_t* __restrict__ hist, uint2* __restrict__ lists,
+    uint32_t* __restrict__ sub_cnt, int vec4) {
+  constexpr int kWaves = kSelectThreads / 64;
+  __shared__ struct {
+    uint32_t scratch[kSelectThreads / 64 + 1];
+    uint32_t thr[2];
+  } sh;
+  const int row = blockIdx.y, seg = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int subs = segs * kWaves;
+
+  find_threshold_bin<kSelectThreads>(hist + (int64_t)row * kHistBins, (uint32_t)kk,
+                                     sh.scratch, sh.thr);
+  const uint32_t b1 = sh.thr[0];
+
+  const int sub = seg * kWaves + wave;
+  const float* s = scores + (int64_t)row * n;
+  const int64_t w0 = (int64_t)sub * sub_len;
+  const int64_t w1 = min(n, w0 + sub_len);
+  uint2* out = lists + (int64_t)row * n + w0;
+  uint32_t count = 0;  // wave-uniform
+  constexpr int kSteps = 8;  // 16-byte loads in flight per lane
+  for (int64_t base = w0; base < w1; base += 256 * kSteps) {
+    float v[kSteps][4];
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      const int64_t i0 = base + st * 256 + lane * 4;
+      if (vec4 && i0 + 3 < w1) {
+        const float4 x = *reinterpret_cast<const float4*>(s + i0);
+        v[st][0] = x.x; v[st][1] = x.y; v[st][2] = x.z; v[st][3] = x.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[st][i] = i0 + i < w1 ? s[i0 + i] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      const int64_t i0 = base + st * 256 + lane * 4;
+      uint32_t u[4];
+      uint64_t bal[4];
+      uint32_t pos = count, tot = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u[i] = float_order_key(v[st][i]);
+        bal[i] = __ballot(i0 + i < w1 && (u[i] >> 21) >= b1);
+        pos += lane_prefix(bal[i]);  // entries of lower lanes, element i
+        tot += (uint32_t)__popcll(bal[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if ((bal[i] >> lane) & 1ull) {
+          out[pos] = make_uint2(u[i], (uint32_t)(i0 + i));
+          ++pos;
+        }
+      }
+      count += tot;
+    }
+  }
+  if (lane == 0) sub_cnt[(int64_t)row * subs + sub] = count;
 }
 
 __global__ void zero_u32_kernel(uint32_t* p, int64_t words) {
@@ -359,22 +358,25 @@ TopkPlan plan_topk(int rows, int64_t n, int64_t k) {
   p.rows = rows;
   p.n = n;
   p.kk = k < n ? k : n;
-  // segments of up to 8K scores (two filter iterations of 256 threads x 16);
-  // more, shorter segments when there are too few rows to fill the chip
-  int64_t segs = (n + 8191) / 8192;
-  const int64_t want = (1024 + rows - 1) / rows;
-  if (segs < want) segs = std::min<int64_t>(want, (n + 2047) / 2048);
-  segs = std::max<int64_t>(1, std::min<int64_t>(segs, 64));
-  int64_t seg_len = (n + segs - 1) / segs;
-  seg_len = (seg_len + 255) / 256 * 256;
-  p.seg_len = std::max<int64_t>(seg_len, 256);
+  // One sub-list per wave of sub_len scores (a multiple of 2048, one
+  // iteration of a wave): about 4096 waves over the whole call, at most
+  // kMaxSubLists sub-lists per row.
+  constexpr int W = kSelectThreads / 64;
+  int64_t sub_len = ((int64_t)rows * n + 4095) / 4096;
+  sub_len = std::max<int64_t>(sub_len, (n + kMaxSubLists - 1) / kMaxSubLists);
+  sub_len = std::max<int64_t>(2048, (sub_len + 2047) / 2048 * 2048);
+  p.sub_len = sub_len;
+  p.seg_len = sub_len * W;  // scores per block
   p.segs = (int)((n + p.seg_len - 1) / p.seg_len);
   if (p.segs < 1) p.segs = 1;
+  p.subs = p.segs * W;
   size_t off = 0;
   p.hist_off = off;
-  off = align256(off + (size_t)rows * kHistBins * 4);
+  off += (size_t)rows * kHistBins * 4;
+  p.zero_words = (int64_t)rows * kHistBins;
+  off = align256(off);
   p.cnt_off = off;
-  off = align256(off + (size_t)rows * p.segs * 4);
+  off = align256(off + (size_t)rows * p.subs * 4);
   p.list_off = off;
   off = align256(off + (size_t)rows * n * 8);
   p.total_bytes = off;
@@ -395,8 +397,7 @@ hipError_t launch_topk(const float* scores, const TopkPlan& plan, int32_t* idx,
   if (plan.kk == plan.n) {
     const int64_t total = (int64_t)plan.rows * plan.n;
     const int grid = (int)std::min<int64_t>((total + 255) / 256, 4096);
-    launch_kernel(iota_rows_kernel, dim3(grid), dim3(256), 0, stream, idx,
-                       plan.rows, plan.n);
+    launch_kernel(iota_rows_kernel, dim3(grid), dim3(256), 0, stream, idx, plan.rows, plan.n);
     return hipGetLastError();
   }
   unsigned char* base = static_cast<unsigned char*>(ws);
@@ -405,21 +406,19 @@ hipError_t launch_topk(const float* scores, const TopkPlan& plan, int32_t* idx,
   uint2* lists = reinterpret_cast<uint2*>(base + plan.list_off);
   hipError_t err;
   if (!hist_ready) {
-    err = launch_zero_u32(hist, (int64_t)plan.rows * kHistBins, stream);
+    err = launch_zero_u32(hist, plan.zero_words, stream);
     if (err != hipSuccess) return err;
-    launch_kernel(topk_hist_kernel, dim3(plan.segs, plan.rows),
-                       dim3(kFilterThreads), 0, stream, scores, plan.n,
-                       plan.seg_len, hist);
+    launch_kernel(topk_hist_kernel, dim3(plan.segs, plan.rows), dim3(kFilterThreads), 0,
+                  stream, scores, plan.n, plan.seg_len, hist);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const int vec4 = (plan.n % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0) ? 1 : 0;
-  launch_kernel(topk_filter_kernel, dim3(plan.segs, plan.rows),
-                     dim3(kFilterThreads), 0, stream, scores, plan.n, plan.kk,
-                     plan.segs, plan.seg_len, hist, lists, cnt, vec4);
+  launch_kernel(topk_filter_kernel, dim3(plan.segs, plan.rows), dim3(kSelectThreads), 0,
+                stream, scores, plan.n, plan.kk, plan.segs, plan.sub_len, hist, lists, cnt,
+                vec4);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  launch_kernel(topk_refine_kernel, dim3(plan.rows), dim3(kRefineThreads),
-                     0, stream, plan.n, plan.kk, plan.segs, plan.seg_len, hist,
-                     lists, cnt, idx);
+  launch_kernel(topk_refine_kernel, dim3(plan.rows), dim3(kRefineThreads), 0, stream, plan.n,
+                plan.kk, plan.subs, plan.sub_len, hist, lists, cnt, idx);
   return hipGetLastError();
 }
 
