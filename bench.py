@@ -61,20 +61,14 @@ def algorithmic_bytes(w):
 
 
 def decode_kernel_names(w):
-    """Kernels socket_decode enqueues for this workload, in order (mirrors the
-    library's choice: the score kernel builds the first top-k histogram
-    itself, cleared by the bucket kernel, when the probability table plus the
-    packed histogram fit the 160 KB of LDS)."""
-    table = (2 ** w.P) * w.L * w.G * 4
-    fused = w.kk < w.N and table + w.G * 1024 * 4 <= 160 * 1024
-    names = ["bucket_probs_kernel", "score_kernel"]
+    """Kernels socket_decode enqueues for this workload, in order (no score
+    rows are requested: with kk < N the score kernel emits candidates for
+    the select kernel; with kk = N every key is selected and nothing is
+    scored)."""
     if w.kk >= w.N:
-        names.append("iota_rows_kernel")
-    else:
-        if not fused:
-            names += ["zero_u32_kernel", "topk_hist_kernel"]
-        names += ["topk_filter_kernel", "topk_refine_kernel"]
-    return names + ["sparse_attn_kernel", "attn_merge_kernel"]
+        return ["iota_rows_kernel", "sparse_attn_kernel", "attn_merge_kernel"]
+    return ["bucket_probs_kernel", "score_kernel", "topk_select_kernel", "sparse_attn_kernel",
+            "attn_merge_kernel"]
 
 
 def kernel_bytes(w):
@@ -84,15 +78,11 @@ def kernel_bytes(w):
     keys = w.B * w.Hkv * w.N
     kk = w.kk
     table = w.B * w.Hkv * (2 ** w.P) * w.L * w.G * 4
-    scores = rows * w.N * 4
     partial = 0  # intermediates between two kernels are not counted
     return {
         "bucket_probs_kernel": rows * w.d * e + w.d * w.C * e + table,
-        "score_kernel": keys * w.L + keys * 4 + table + scores,
-        "zero_u32_kernel": rows * 2048 * 4,
-        "topk_hist_kernel": scores,
-        "topk_filter_kernel": scores,
-        "topk_refine_kernel": rows * kk * 4,
+        "score_kernel": keys * w.L + keys * 4 + table,
+        "topk_select_kernel": rows * kk * 4,
         "iota_rows_kernel": rows * kk * 4,
         "sparse_attn_kernel": rows * kk * (2 * w.d * e + 4) + rows * w.d * e + partial,
         "attn_merge_kernel": rows * w.d * e,

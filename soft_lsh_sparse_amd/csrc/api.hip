@@ -36,8 +36,6 @@ socket_status from_hip(hipError_t err, const char* what) {
   return fail(SOCKET_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
 }
 
-constexpr size_t kMaxTableBytes = 160 * 1024;  // LDS of one gfx950 CU
-
 bool aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
@@ -78,11 +76,12 @@ socket_status check_heads(int32_t B, int32_t Hq, int32_t Hkv) {
 }
 
 socket_status check_table(int32_t L, int32_t P, int32_t G) {
-  const size_t bytes = ((size_t)1 << P) * L * G * sizeof(float);
-  if (bytes > kMaxTableBytes)
+  const size_t bytes = score_lds_bytes(L, P, G);
+  if (bytes > kLdsBytesPerCU)
     return fail(SOCKET_ERR_UNSUPPORTED,
-                "probability table of one KV head (%zu bytes = 2^P*L*G*4) exceeds the "
-                "%zu bytes of LDS", bytes, kMaxTableBytes);
+                "probability table of one KV head (2^P*L*G*4 bytes) with the score "
+                "kernel's other LDS (%zu bytes in all) exceeds the %zu bytes of LDS",
+                bytes, kLdsBytesPerCU);
   return SOCKET_OK;
 }
 
@@ -93,26 +92,34 @@ socket_status check_table(int32_t L, int32_t P, int32_t G) {
   } while (0)
 
 struct DecodeLayout {
-  size_t table_off, scores_off, idx_off, topk_off, attn_off, total;
-  TopkPlan topk;
+  size_t table_off, scores_off, idx_off, thr_off, cnt_off, list_off, attn_off, total;
+  ScoreGeom score;
   AttnPlan attn;
 };
 
+// Workspace of one decode call: the probability tables, full score rows
+// (written only for rows that need them), selected indices, block
+// thresholds, candidate sub-list lengths and lists, attention partials.
 DecodeLayout decode_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
                            int64_t n_keys, int32_t L, int32_t P, int64_t k) {
   DecodeLayout lay{};
   const int rows = B * Hq;
   const int64_t kk = k < n_keys ? k : n_keys;
+  const bool select = kk < n_keys;
+  lay.score = plan_score(B * Hkv, n_keys, L, P, Hq / Hkv);
   size_t off = 0;
   lay.table_off = off;
   off = align256(off + ((size_t)1 << P) * L * Hq * B * sizeof(float));
   lay.scores_off = off;
-  off = align256(off + (size_t)rows * n_keys * sizeof(float));
+  off = align256(off + (select ? (size_t)rows * n_keys * sizeof(float) : 0));
   lay.idx_off = off;
   off = align256(off + (size_t)rows * kk * sizeof(int32_t));
-  lay.topk = plan_topk(rows, n_keys, k);
-  lay.topk_off = off;
-  off = align256(off + lay.topk.total_bytes);
+  lay.thr_off = off;
+  off = align256(off + (select ? (size_t)rows * lay.score.segs * sizeof(uint32_t) : 0));
+  lay.cnt_off = off;
+  off = align256(off + (select ? (size_t)rows * lay.score.subs * sizeof(uint32_t) : 0));
+  lay.list_off = off;
+  off = align256(off + (select ? (size_t)rows * n_keys * 8 : 0));
   lay.attn = plan_attn(B, Hq, Hkv, d, kk);
   lay.attn_off = off;
   off = align256(off + lay.attn.partial_bytes);
@@ -210,7 +217,7 @@ socket_status socket_bucket_probs(const void* Q, const void* R,
   if (!aligned16(R))
     return fail(SOCKET_ERR_INVALID_ARGUMENT, "R must be 16-byte aligned");
   hipError_t err = launch_bucket_probs(Q, R, dtype == SOCKET_DTYPE_BF16, B, Hq,
-                                       Hkv, d, L, P, tau, table, nullptr, 0,
+                                       Hkv, d, L, P, tau, table,
                                        static_cast<hipStream_t>(stream));
   return from_hip(err, "socket_bucket_probs launch");
 }
@@ -231,7 +238,7 @@ socket_status socket_score(const float* table, const uint8_t* ids,
   if (!aligned16(table))
     return fail(SOCKET_ERR_INVALID_ARGUMENT, "table must be 16-byte aligned");
   hipError_t err = launch_score(table, ids, vnorm, B, Hq, Hkv, n_keys,
-                                head_stride_rows, L, P, scores, nullptr,
+                                head_stride_rows, L, P, scores,
                                 static_cast<hipStream_t>(stream));
   return from_hip(err, "socket_score launch");
 }
@@ -256,7 +263,7 @@ socket_status socket_topk(const float* scores, int32_t rows, int64_t n,
   if (plan.kk < n && (!workspace || workspace_bytes < plan.total_bytes))
     return fail(SOCKET_ERR_WORKSPACE, "top-k needs %zu workspace bytes, got %zu",
                 plan.total_bytes, workspace ? workspace_bytes : (size_t)0);
-  hipError_t err = launch_topk(scores, plan, idx, workspace, false,
+  hipError_t err = launch_topk(scores, plan, idx, workspace,
                                static_cast<hipStream_t>(stream));
   return from_hip(err, "socket_topk launch");
 }
@@ -343,6 +350,9 @@ socket_status decode_impl(const void* Q, const void* K, const void* V,
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(R))
     return fail(SOCKET_ERR_INVALID_ARGUMENT, "Q, K, V and R must be 16-byte aligned");
   const DecodeLayout lay = decode_layout(B, Hq, Hkv, d, n_keys, L, P, k);
+  if (k < n_keys && lay.score.subs > kMaxSelectSubLists)
+    return fail(SOCKET_ERR_UNSUPPORTED, "n_keys=%lld needs %d candidate sub-lists per row "
+                "(at most %d)", (long long)n_keys, lay.score.subs, kMaxSelectSubLists);
   if (!workspace || workspace_bytes < lay.total)
     return fail(SOCKET_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu",
                 lay.total, workspace ? workspace_bytes : (size_t)0);
@@ -358,27 +368,66 @@ socket_status decode_impl(const void* Q, const void* K, const void* V,
   } scope(events ? &trace : nullptr);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   float* table = reinterpret_cast<float*>(ws + lay.table_off);
-  float* scores = scores_out ? scores_out : reinterpret_cast<float*>(ws + lay.scores_off);
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + lay.idx_off);
-  unsigned char* tws = ws + lay.topk_off;
   float* partial = reinterpret_cast<float*>(ws + lay.attn_off);
   const bool bf16 = dtype == SOCKET_DTYPE_BF16;
 
-  // The score kernel builds the first radix histogram of the top-k when its
-  // LDS has room next to the table; the bucket kernel clears it beforehand.
+  // Selection: the score kernel estimates per-block thresholds and emits
+  // the keys that reach them; one block per row then selects the kk best
+  // (from the candidates, or from the full row).
+  const int rows = B * Hq;
   const int64_t kk = k < n_keys ? k : n_keys;
-  const bool fused_hist =
-      kk < n_keys && score_lds_bytes(L, P, Hq / Hkv, true) <= kLdsBytesPerCU;
-  uint32_t* hist = reinterpret_cast<uint32_t*>(tws + lay.topk.hist_off);
-  hipError_t err = launch_bucket_probs(
-      Q, R, bf16, B, Hq, Hkv, d, L, P, tau, table, fused_hist ? hist : nullptr,
-      fused_hist ? lay.topk.zero_words : 0, s);
-  if (err != hipSuccess) return from_hip(err, "socket_decode: bucket_probs");
-  err = launch_score(table, ids, vnorm, B, Hq, Hkv, n_keys, head_stride_rows, L, P,
-                     scores, fused_hist ? hist : nullptr, s);
-  if (err != hipSuccess) return from_hip(err, "socket_decode: score");
-  err = launch_topk(scores, lay.topk, idx, tws, fused_hist, s);
-  if (err != hipSuccess) return from_hip(err, "socket_decode: topk");
+  hipError_t err;
+  if (kk < n_keys) {
+    uint32_t* thr = reinterpret_cast<uint32_t*>(ws + lay.thr_off);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + lay.cnt_off);
+    uint2* lists = reinterpret_cast<uint2*>(ws + lay.list_off);
+    float* rowbuf = scores_out ? scores_out : reinterpret_cast<float*>(ws + lay.scores_off);
+    err = launch_bucket_probs(Q, R, bf16, B, Hq, Hkv, d, L, P, tau, table, s);
+    if (err != hipSuccess) return from_hip(err, "socket_decode: bucket_probs");
+    ScoreSelect sel{};
+    sel.table = table;
+    sel.ids = ids;
+    sel.vnorm = vnorm;
+    sel.kk = kk;
+    sel.thr = thr;
+    sel.lists = lists;
+    sel.sub_cnt = cnt;
+    err = launch_score_select(sel, B, Hq, Hkv, n_keys, head_stride_rows, L, P, scores_out, s);
+    if (err != hipSuccess) return from_hip(err, "socket_decode: score");
+    SelectArgs sa{};
+    sa.n = n_keys;
+    sa.kk = kk;
+    sa.subs = lay.score.subs;
+    sa.sub_len = lay.score.sub_len;
+    sa.segs = lay.score.segs;
+    sa.thr = thr;
+    sa.lists = lists;
+    sa.sub_cnt = cnt;
+    sa.idx = idx;
+    sa.table = table;
+    sa.ids = ids;
+    sa.vnorm = vnorm;
+    sa.Hq = Hq;
+    sa.Hkv = Hkv;
+    sa.L = L;
+    sa.P = P;
+    sa.stride = head_stride_rows;
+    sa.rotated = score_rotated(ids, head_stride_rows, L) ? 1 : 0;
+    sa.scores = rowbuf;
+    err = launch_topk_select(sa, rows, s);
+    if (err != hipSuccess) return from_hip(err, "socket_decode: topk");
+  } else {
+    if (scores_out) {
+      err = launch_bucket_probs(Q, R, bf16, B, Hq, Hkv, d, L, P, tau, table, s);
+      if (err != hipSuccess) return from_hip(err, "socket_decode: bucket_probs");
+      err = launch_score(table, ids, vnorm, B, Hq, Hkv, n_keys, head_stride_rows, L, P,
+                         scores_out, s);
+      if (err != hipSuccess) return from_hip(err, "socket_decode: score");
+    }
+    err = launch_iota_rows(idx, rows, n_keys, s);
+    if (err != hipSuccess) return from_hip(err, "socket_decode: topk");
+  }
   err = launch_sparse_attn(Q, K, V, bf16, lay.attn, head_stride_rows, idx, out,
                            partial, s);
   return from_hip(err, "socket_decode: sparse_attn");

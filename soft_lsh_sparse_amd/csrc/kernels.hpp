@@ -54,24 +54,49 @@ hipError_t launch_hash_keys_f32(const float* K, const float* V, const float* R,
                                 hipStream_t stream);
 
 // ------------------------------------------------------ soft bucket table
-// zero_ptr/zero_words: optional device words cleared by the same launch.
 hipError_t launch_bucket_probs(const void* Q, const void* R, bool bf16, int B,
                                int Hq, int Hkv, int d, int L, int P,
-                               float tau, float* table, uint32_t* zero_ptr,
-                               int64_t zero_words, hipStream_t stream);
+                               float tau, float* table, hipStream_t stream);
 
 // ------------------------------------------------------------------ score
-// table: [B*Hkv, 2^P, L, G] from launch_bucket_probs.
-// hist (optional): [B*Hq, 2048] first-digit histograms, accumulated with
-// atomics; must be zero on entry.
+// Launch geometry of the score kernel: segs blocks per (batch, KV head) of
+// seg_len keys each; every block's 16 waves own sub_len consecutive keys
+// (subs = segs * 16 sub-lists per row when emitting candidates).
+struct ScoreGeom {
+  int segs;
+  int64_t seg_len;
+  int subs;
+  int64_t sub_len;
+};
+ScoreGeom plan_score(int bhkv, int64_t n_keys, int L, int P, int G);
+// true when the kernel sums each key's tables in the rotated order
+// l = (t + key) mod L, t = 0..L-1 (with key taken mod 8); else l = t
+bool score_rotated(const uint8_t* ids, int64_t stride, int L);
+// LDS bytes of one score block.
+size_t score_lds_bytes(int L, int P, int G);
+constexpr size_t kLdsBytesPerCU = 160 * 1024;
+// table: [B*Hkv, 2^P, L, G] from launch_bucket_probs; scores [B*Hq, n_keys].
 hipError_t launch_score(const float* table, const uint8_t* ids, const float* vnorm,
                         int B, int Hq, int Hkv, int64_t n_keys, int64_t stride,
-                        int L, int P, float* scores, uint32_t* hist,
-                        hipStream_t stream);
-// LDS bytes one score block needs: the probability table, plus the packed
-// first-digit histogram when fused.
-size_t score_lds_bytes(int L, int P, int G, bool with_hist);
-constexpr size_t kLdsBytesPerCU = 160 * 1024;
+                        int L, int P, float* scores, hipStream_t stream);
+// Decode path: every block estimates a per-row threshold from its first
+// keys (thr[row * segs + seg], an order key) and appends every key whose
+// score's order key reaches it, as (order key, index), to sub-list (row, s)
+// at lists[row * n_keys + s * sub_len], in index order; sub_cnt[row * subs +
+// s] receives the sub-list's length.
+struct ScoreSelect {
+  const float* table;  // [B*Hkv, 2^P, L, G]
+  const uint8_t* ids;
+  const float* vnorm;
+  int64_t kk;          // < n_keys
+  uint32_t* thr;       // [B*Hq, segs]
+  uint2* lists;        // [B*Hq, n_keys]
+  uint32_t* sub_cnt;   // [B*Hq, subs]
+};
+// scores (optional): full score rows as well.
+hipError_t launch_score_select(const ScoreSelect& s, int B, int Hq, int Hkv, int64_t n_keys,
+                               int64_t stride, int L, int P, float* scores,
+                               hipStream_t stream);
 
 // ------------------------------------------------------------------ top-k
 struct TopkPlan {
@@ -85,13 +110,35 @@ struct TopkPlan {
   int64_t zero_words;  // words from hist_off that must be zero before a call
 };
 TopkPlan plan_topk(int rows, int64_t n, int64_t k);
-constexpr int kHistBins = 2048;
 hipError_t launch_zero_u32(uint32_t* p, int64_t words, hipStream_t stream);
-// hist_ready: the histogram region of ws already holds the first-digit
-// histogram (filled by the score kernel); otherwise it is built here.
 hipError_t launch_topk(const float* scores, const TopkPlan& plan,
-                       int32_t* idx, void* ws, bool hist_ready,
-                       hipStream_t stream);
+                       int32_t* idx, void* ws, hipStream_t stream);
+hipError_t launch_iota_rows(int32_t* idx, int rows, int64_t n, hipStream_t stream);
+
+// Selection from the score kernel's candidates (decode path), one block per
+// row: with T the largest of the row's block thresholds, every key whose
+// order key reaches T is a candidate; when at least kk do, the kk best
+// candidates are the result, otherwise the row is scored in full into
+// scores and selected from there.
+constexpr int kMaxSelectSubLists = 4096;
+struct SelectArgs {
+  int64_t n, kk;              // kk < n
+  int subs;                   // <= kMaxSelectSubLists
+  int64_t sub_len;
+  int segs;
+  const uint32_t* thr;        // [rows][segs]
+  const uint2* lists;
+  const uint32_t* sub_cnt;
+  int32_t* idx;               // [rows][kk]
+  const float* table;         // full-row fallback: the score kernel's inputs
+  const uint8_t* ids;
+  const float* vnorm;
+  int Hq, Hkv, L, P;
+  int64_t stride;
+  int rotated;                // score_rotated(ids, stride, L)
+  float* scores;              // [rows][n] row buffers
+};
+hipError_t launch_topk_select(const SelectArgs& a, int rows, hipStream_t stream);
 
 // ------------------------------------------------------- sparse attention
 // Largest selection one attention row supports: 1024 chunks of 256 keys.

@@ -8,11 +8,11 @@
 // bucket, summed over the L tables and weighted by the key's value norm.
 //
 // One block owns one (batch, KV head) and a contiguous range of keys. It
-// copies that head's probability table [2^P][L][G] (float32, from the bucket
+// copies that head's probability table [2^P][L][G] (float32, from the table
 // kernel) into LDS, then streams the bucket-id rows (L bytes per key,
-// coalesced across lanes) and the value norms from HBM, several iterations
-// ahead in registers so that enough bytes are in flight to cover the memory
-// latency. Each id byte is looked up once for the whole GQA group: the G
+// coalesced across lanes) and the value norms from HBM, two steps ahead in
+// registers (the first steps are requested before the table is staged).
+// Each id byte is looked up once for the whole GQA group: the G
 // probabilities of the group sit in one 16-byte LDS slot.
 //
 // Bank spread: with the [u][l][G] layout and L a multiple of 16, the LDS bank
@@ -25,28 +25,48 @@
 // compile-time immediate. The L probabilities are summed in float32 in that
 // fixed order and multiplied by the value norm.
 //
-// Optionally the kernel also counts every score in a 2048-bin histogram of
-// the top 11 bits of its order key (the first pass of the top-k radix
-// select): per-block counts are kept in LDS as packed 16-bit pairs (a block
-// never scores more than 32768 keys per row) and added to the per-row global
-// histogram with integer atomics, which makes the result order-independent.
+// Candidate emission (the decode path). Every wave owns a contiguous range
+// of the block's keys. The block scores the first step of every wave (up to
+// 2048 keys, spread over its range) and sets, per query row, a threshold
+// that about m of those scores reach, with m = m0 + 6 sqrt(m0) + 8 for the
+// m0 = kk * n_b / n keys of the row's top kk expected among its n_b sampled
+// keys (exactly kk when the block sees the whole row): the sampled order
+// keys are counted in 256 bins of 1/64 octave below the row's largest one,
+// and the threshold is the lower edge of the first bin at which the count
+// from the top reaches m. Thresholds are stored per block and row; every
+// key of the block whose score's order key reaches the threshold is
+// appended as (order key, index) to its wave's sub-list, in index order
+// (slots from one ballot and lane prefix counts per row and step, no
+// atomics), and the sub-list lengths are stored at the end. The selection
+// that follows is exact whatever these thresholds are: it takes the largest
+// threshold of the row, checks that at least kk candidates reach it (every
+// key that does is a candidate) and otherwise scores the whole row.
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "radix.hpp"
 
 #include <algorithm>
 
 namespace socket_lsh {
 namespace {
 
-constexpr int kScoreThreads = 512;  // generic path
-// Rotated-path blocks: 16 waves, the most one CU holds at <= 128 VGPRs,
-// with two iterations of ids and norms in flight per thread.
-constexpr int kRotThreads = 1024;
+// 16 waves per block, the most one CU holds at <= 128 VGPRs; the rotated
+// path keeps two steps of ids and norms in flight per thread.
+constexpr int kScoreThreads = 1024;
+constexpr int kScoreWaves = kScoreThreads / 64;
 constexpr int kPrefetch = 2;
-constexpr int64_t kMaxSegForHist = 32768;
+// keys per wave are a multiple of one rotated-path iteration
+constexpr int kWaveStep = 64 * kPrefetch;
 // keeps every per-thread byte offset of a segment (key * L, L <= 1024) in 31 bits
 constexpr int64_t kMaxSeg = 1 << 20;
+// block thresholds: 256 bins per query row and pass, 1/16 of an octave of
+// the score (2^19 units of the order key) below the row's largest sampled
+// score in the first pass, 2^11 units in the second
+constexpr int kThrBins = 256;
+constexpr int kThrShift1 = 19;
+constexpr int kThrShift2 = 11;
+constexpr int kScratchWords = 160;  // >= 16 * G + G
 
 // v_cndmask_b32 with an explicit lane mask: b where the lane's mask bit is
 // set, a elsewhere. Written out so the compiler keeps one select per word
@@ -118,10 +138,10 @@ __device__ __forceinline__ bool score_block_coords(int bhkv, int segs, int& bg,
   return true;
 }
 
-// The table of batch*KV head bg into LDS, and the packed histogram cleared.
+// The table of batch*KV head bg into LDS.
 template <int G>
 __device__ __forceinline__ void stage_table(float* tab, const float* table, int bg,
-                                            int L, int P, uint32_t* hloc) {
+                                            int L, int P) {
   const int tsize = (1 << P) * L * G;
   if (tsize % 4 == 0) {  // every head's table then starts 16-byte aligned
     const float4* src = reinterpret_cast<const float4*>(table + (int64_t)bg * tsize);
@@ -131,182 +151,388 @@ __device__ __forceinline__ void stage_table(float* tab, const float* table, int 
     for (int i = threadIdx.x; i < tsize; i += blockDim.x)
       tab[i] = table[(int64_t)bg * tsize + i];
   }
-  if (hloc)
-    for (int i = threadIdx.x; i < G * kHistBins / 2; i += blockDim.x) hloc[i] = 0u;
 }
 
-// Shared tail: store the G scores of key n and count them.
-template <int G>
-__device__ __forceinline__ void emit_scores(const float (&acc)[G], float vn,
-                                            int64_t n, int64_t n_keys,
-                                            float* srow, uint32_t* hloc) {
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const float s = vn * acc[j];
-    srow[(int64_t)j * n_keys + n] = s;
-    if (hloc) {
-      const uint32_t bin = float_order_key(s) >> 21;
-      atomicAdd(hloc + j * (kHistBins / 2) + (bin >> 1), 1u << ((bin & 1) * 16));
-    }
-  }
-}
-
-template <int G>
-__device__ __forceinline__ void flush_hist(const uint32_t* hloc, uint32_t* hrow) {
-  for (int i = threadIdx.x; i < G * kHistBins; i += blockDim.x) {
-    const int j = i / kHistBins, bin = i % kHistBins;
-    const uint32_t v = (hloc[j * (kHistBins / 2) + (bin >> 1)] >> ((bin & 1) * 16)) & 0xffffu;
-    if (v) atomicAdd(hrow + (int64_t)j * kHistBins + bin, v);
-  }
-}
 
 struct ScoreArgs {
   const float* table;  // [bhkv][2^P][L][G]
   const uint8_t* ids;
   const float* vnorm;
-  int Hq, Hkv, bhkv, P, segs;
+  int Hq, Hkv, bhkv, L, P, segs;
   int64_t n_keys, stride, seg_len;
-  float* scores;
-  uint32_t* hist;
+  float* scores;       // [rows][n_keys] or null
+  // candidate emission (decode path)
+  int select;
+  int64_t kk;
+  uint32_t* thr;       // [rows][segs] block thresholds (order keys)
+  uint2* lists;        // [rows][n_keys]; sub-list s at s * seg_len / 16
+  uint32_t* sub_cnt;   // [rows][segs * 16]
 };
 
-// Fast path: L a multiple of 16 (LW = L/4 words of ids per key).
-template <int G, int LW>
-__global__ __launch_bounds__(kRotThreads) void score_kernel_rot(ScoreArgs a) {
-  constexpr int kThreads = kRotThreads;
-  constexpr int L = LW * 4;
-  constexpr int kChunk = 64 / G;  // lookups per dependency step (a multiple of 4)
-  extern __shared__ __align__(16) float tab[];
-  int bg, seg;
-  if (!score_block_coords(a.bhkv, a.segs, bg, seg)) return;
-  const int b = bg / a.Hkv, g = bg % a.Hkv;
-  const int P = a.P;
-  const int tsize = (1 << P) * L * G;
-  uint32_t* hloc = a.hist ? reinterpret_cast<uint32_t*>(tab + tsize) : nullptr;
+// LDS layout of a score block: the table, the per-row threshold
+// histograms, scratch words.
+__host__ __device__ inline size_t score_table_region(int L, int P, int G) {
+  return align256(((size_t)1 << P) * L * G * sizeof(float));
+}
 
-  // block-uniform bases of this segment; per-thread offsets stay 32-bit
-  const int64_t n0 = seg * a.seg_len;
-  const int cnt = (int)(min(a.n_keys, n0 + a.seg_len) - n0);
-  const uint8_t* idseg = a.ids + ((int64_t)bg * a.stride + n0) * L;
-  const float* vseg = a.vnorm + (int64_t)bg * a.stride + n0;
-  float* sseg = a.scores + ((int64_t)b * a.Hq + (int64_t)g * G) * a.n_keys + n0;
-
-  // the first kPrefetch iterations of ids and norms go in flight before the
-  // table is staged
-  uint4 pf[kPrefetch][LW / 4];
-  float pf_vn[kPrefetch];
-  const int first = threadIdx.x;
+// Scores of one key for the G heads of a group: written out (sk: the key's
+// slot in the first head's score row, or null) and/or appended to the
+// wave's sub-lists. Called by every lane of the wave (valid marks the lanes
+// that hold a key); cnt is the wave's running count per head.
+template <int G>
+__device__ __forceinline__ void emit_scores(const ScoreArgs& a, const float (&acc)[G], float vn,
+                                            bool valid, uint32_t key, float* sk,
+                                            uint2* const (&lst)[G], const uint32_t (&thr)[G],
+                                            uint32_t (&cnt)[G]) {
 #pragma unroll
-  for (int q = 0; q < kPrefetch; ++q) {
-    const int i = first + q * kThreads;
-    pf_vn[q] = 0.f;
-    if (i < cnt) {
-      const uint4* src = reinterpret_cast<const uint4*>(idseg + i * L);
-#pragma unroll
-      for (int k = 0; k < LW / 4; ++k) pf[q][k] = src[k];
-      pf_vn[q] = vseg[i];
+  for (int j = 0; j < G; ++j) {
+    const float sc = vn * acc[j];
+    if (sk != nullptr && valid) sk[(int64_t)j * a.n_keys] = sc;
+    if (a.select) {
+      const uint32_t u = float_order_key(sc);
+      const bool pass = valid && u >= thr[j];
+      const uint64_t bal = __ballot(pass);
+      if (pass) lst[j][cnt[j] + lane_prefix(bal)] = make_uint2(u, key);
+      cnt[j] += (uint32_t)__popcll(bal);
     }
-  }
-  stage_table<G>(tab, a.table, bg, L, P, hloc);
-  __syncthreads();
-
-  // n0 and the thread stride are multiples of 8, so every key of this
-  // thread has the same rotation r = key index mod 8 and the same two bases
-  const int r = first & 7;
-  const uint64_t by_word = __ballot(r >= 4);
-  const int rb = r & 3;
-  const int base_nowrap = r * G;        // slot offset of step t: t*G + base
-  const int base_wrap = (r - L) * G;    // ... once t + r >= L
-  for (int bi = first; bi < cnt; bi += kPrefetch * kThreads) {
-#pragma unroll
-    for (int q = 0; q < kPrefetch; ++q) {
-      const int i = bi + q * kThreads;
-      if (i < cnt) {
-        uint32_t w[LW];
-#pragma unroll
-        for (int k = 0; k < LW / 4; ++k) {
-          w[4 * k] = pf[q][k].x; w[4 * k + 1] = pf[q][k].y;
-          w[4 * k + 2] = pf[q][k].z; w[4 * k + 3] = pf[q][k].w;
-        }
-        const float vn = pf_vn[q];
-        const int ii = i + kPrefetch * kThreads;
-        if (ii < cnt) {
-          const uint4* src = reinterpret_cast<const uint4*>(idseg + ii * L);
-#pragma unroll
-          for (int k = 0; k < LW / 4; ++k) pf[q][k] = src[k];
-          pf_vn[q] = vseg[ii];
-        }
-        rotate_bytes<LW>(w, by_word, rb);
-        float acc[G];
-#pragma unroll
-        for (int t = 0; t < L; ++t) {
-          // P bits of byte t: ids are < 2^P, so this never leaves the table
-          const uint32_t u = __builtin_amdgcn_ubfe(w[t >> 2], (t & 3) * 8, P);
-          const int base = (t + 7 < L) ? base_nowrap
-                                       : (t + r < L ? base_nowrap : base_wrap);
-          float pr[G];
-          lds_load_group<G>(tab + (int)u * (L * G) + base + t * G, pr);
-#pragma unroll
-          for (int j = 0; j < G; ++j) acc[j] = t == 0 ? pr[j] : acc[j] + pr[j];
-          // the next kChunk lookups wait for these sums: at most 64 floats
-          // of lookups in flight per lane, which bounds the registers
-          if ((t + 1) % kChunk == 0 && t + 1 < L)
-            fence_chunk<G, LW>(acc, w, (t + 1) / 4, std::min(LW, (t + 1 + kChunk) / 4));
-        }
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-          const float sc = vn * acc[j];
-          sseg[(int64_t)j * a.n_keys + i] = sc;
-          if (hloc) {
-            const uint32_t bin = float_order_key(sc) >> 21;
-            atomicAdd(hloc + j * (kHistBins / 2) + (bin >> 1), 1u << ((bin & 1) * 16));
-          }
-        }
-      }
-    }
-  }
-  if (hloc) {
-    __syncthreads();
-    flush_hist<G>(hloc, a.hist + ((int64_t)b * a.Hq + (int64_t)g * G) * kHistBins);
   }
 }
 
-// General path: any L (no bank rotation, byte loads of the ids).
+// Keys [n0 + wb, n0 + we) of this block's segment belong to this wave.
+struct WaveRange {
+  int64_t n0;
+  int cnt, wlen, wb, we;
+  __device__ WaveRange(const ScoreArgs& a, int seg) {
+    n0 = seg * a.seg_len;
+    cnt = (int)(min(a.n_keys, n0 + a.seg_len) - n0);
+    wlen = (int)(a.seg_len / kScoreWaves);
+    wb = (int)(threadIdx.x >> 6) * wlen;
+    we = min(cnt, wb + wlen);
+  }
+  // keys in the first step (kWaveStep keys) of every wave of the block
+  __device__ int first_step_keys() const {
+    int n = 0;
+    for (int w = 0; w < kScoreWaves; ++w) n += max(0, min(kWaveStep, cnt - w * wlen));
+    return n;
+  }
+};
+
+// Rank m (1 = largest) of a block threshold among n_b sampled keys of a row
+// of n keys of which kk are selected; 0: every key passes.
+__device__ inline uint32_t threshold_rank(int64_t kk, int64_t n, int n_b) {
+  if (n_b >= n) return (uint32_t)kk;
+  const double m0 = (double)kk * n_b / (double)n;
+  const double m = ceil(m0 + 6.0 * sqrt(m0) + 8.0);
+  return m >= (double)n_b ? 0u : (uint32_t)m;
+}
+
+// Per query row j of the group: an order key that at least m of the sampled
+// order keys uk[q][j] (valid[q]) reach, and few more. With M the row's
+// largest, D = M - u; the first pass counts D >> 19 in 256 bins (16
+// octaves; farther keys are not counted) and finds the first bin b1 at
+// which the count from bin 0 reaches m; the second counts (D >> 11) & 255
+// of the keys in b1 and finds b2 the same way. The threshold is the lowest
+// key of sub-bin (b1, b2), or 0 when the bins hold fewer than m keys. Each
+// row's bins are searched by 256 threads (four waves, DPP scans).
 template <int G>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel_generic(ScoreArgs a, int L) {
-  extern __shared__ __align__(16) float tab[];
-  int bg, seg;
-  if (!score_block_coords(a.bhkv, a.segs, bg, seg)) return;
+__device__ void block_thresholds(const uint32_t (&uk)[kPrefetch][G],
+                                 const bool (&valid)[kPrefetch], uint32_t m, uint32_t* hist,
+                                 uint32_t* scratch, uint32_t (&thr)[G]) {
+  uint32_t* wmax = scratch;              // [16][G] wave maxima, then [16] wave totals
+  uint32_t* res = scratch + 16 * G;      // [G][2] chosen bin (or kThrBins), count before it
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // row maxima
+  uint32_t mx[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    uint32_t v = 0u;
+#pragma unroll
+    for (int q = 0; q < kPrefetch; ++q) v = max(v, valid[q] ? uk[q][j] : 0u);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    mx[j] = v;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) wmax[wave * G + j] = mx[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    uint32_t v = 0u;
+    for (int w = 0; w < kScoreWaves; ++w) v = max(v, wmax[w * G + j]);
+    mx[j] = v;
+  }
+  uint32_t b1[G];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    __syncthreads();  // wmax / res of the previous step read by every thread
+    for (int i = threadIdx.x; i < G * kThrBins; i += kScoreThreads) hist[i] = 0u;
+    if (threadIdx.x < G) res[2 * threadIdx.x] = kThrBins;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kPrefetch; ++q) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const uint32_t dist = mx[j] - uk[q][j];
+        uint32_t bin;
+        bool in = valid[q];
+        if (pass == 0) {
+          bin = dist >> kThrShift1;
+          in = in && bin < kThrBins;
+        } else {
+          bin = (dist >> kThrShift2) & (kThrBins - 1);
+          in = in && b1[j] < kThrBins && (dist >> kThrShift1) == b1[j];
+        }
+        if (in) atomicAdd(&hist[j * kThrBins + bin], 1u);
+      }
+    }
+    __syncthreads();
+    uint32_t* wtot = scratch;
+    for (int base = 0; base < G * kThrBins; base += kScoreThreads) {
+      const int slot = base + (int)threadIdx.x;
+      const bool act = slot < G * kThrBins;
+      const int r = slot / kThrBins, bin = slot % kThrBins;
+      const uint32_t c = act ? hist[slot] : 0u;
+      const uint32_t inc = wave_inclusive_scan_dpp(c);
+      if (lane == 63) wtot[wave] = inc;
+      __syncthreads();
+      uint32_t before = 0;
+      const int w_in_row = (slot / 64) % (kThrBins / 64);
+      for (int k = 1; k <= w_in_row; ++k) before += wtot[wave - k];
+      const uint32_t base_cnt = pass == 0 ? 0u : res[2 * r + 1];
+      if (act && base_cnt + before + inc >= m && base_cnt + before + inc - c < m) {
+        res[2 * r] = (uint32_t)bin;
+        if (pass == 0) res[2 * r + 1] = before + inc - c;
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      if (pass == 0) {
+        b1[j] = res[2 * j];
+
+      } else if (b1[j] < kThrBins) {
+        const uint32_t b2 = res[2 * j];  // always found: bin b1 holds the m-th key
+        const uint32_t low = (b1[j] << kThrShift1) + ((b2 + 1) << kThrShift2);  // D below
+        thr[j] = mx[j] < low ? 0u : mx[j] - low + 1u;
+      } else {
+        thr[j] = 0u;
+      }
+    }
+  }
+}
+
+// The common body of the score kernels. Scorer: prefetch() requests the
+// first step of ids and norms; score(q, i, acc, vn) scores key i (relative
+// to n0) of slot q of a step and requests the key kWaveStep further on.
+template <int G, class Scorer>
+__device__ void score_block(const ScoreArgs& a, int bg, int seg, float* tab, Scorer& sc,
+                            const WaveRange& wr) {
   const int b = bg / a.Hkv, g = bg % a.Hkv;
-  const int P = a.P;
-  const int tsize = (1 << P) * L * G;
-  uint32_t* hloc = a.hist ? reinterpret_cast<uint32_t*>(tab + tsize) : nullptr;
-  stage_table<G>(tab, a.table, bg, L, P, hloc);
+  const int lane = threadIdx.x & 63;
+  uint32_t* hist = reinterpret_cast<uint32_t*>(reinterpret_cast<unsigned char*>(tab) +
+                                               score_table_region(a.L, a.P, G));
+  uint32_t* scratch = hist + G * kThrBins;
+  float* sseg = a.scores ? a.scores + ((int64_t)b * a.Hq + (int64_t)g * G) * a.n_keys + wr.n0
+                         : nullptr;
+
+  sc.prefetch();
+  stage_table<G>(tab, a.table, bg, a.L, a.P);
   __syncthreads();
 
-  const int64_t n0 = seg * a.seg_len;
-  const int64_t n1 = min(a.n_keys, n0 + a.seg_len);
-  const uint8_t* idrow = a.ids + (int64_t)bg * a.stride * L;
-  const float* vrow = a.vnorm + (int64_t)bg * a.stride;
-  float* srow = a.scores + ((int64_t)b * a.Hq + (int64_t)g * G) * a.n_keys;
-  for (int64_t n = n0 + threadIdx.x; n < n1; n += kScoreThreads) {
-    float acc[G];
+  // first step of every wave: scored, then (decode) the block thresholds
+  float acc[kPrefetch][G], vn[kPrefetch];
+  bool valid[kPrefetch];
+#pragma unroll
+  for (int q = 0; q < kPrefetch; ++q) {
+    const int i = wr.wb + q * 64 + lane;
+    valid[q] = i < wr.we;
+    sc.score(q, i, valid[q], acc[q], vn[q]);
+  }
+  uint32_t thr[G], nsel[G];
+  uint2* lst[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    thr[j] = 0u;
+    nsel[j] = 0u;
+    lst[j] = nullptr;
+  }
+  if (a.select) {
+    const uint32_t m = threshold_rank(a.kk, a.n_keys, wr.first_step_keys());
+    if (m != 0) {
+      uint32_t uk[kPrefetch][G];
+#pragma unroll
+      for (int q = 0; q < kPrefetch; ++q)
+#pragma unroll
+        for (int j = 0; j < G; ++j) uk[q][j] = float_order_key(vn[q] * acc[q][j]);
+      block_thresholds<G>(uk, valid, m, hist, scratch, thr);
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int64_t row = (int64_t)b * a.Hq + (int64_t)g * G + j;
+      if (threadIdx.x == 0) a.thr[row * a.segs + seg] = thr[j];
+      lst[j] = a.lists + row * a.n_keys + wr.n0 + wr.wb;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kPrefetch; ++q) {
+    const int i = wr.wb + q * 64 + lane;
+    emit_scores<G>(a, acc[q], vn[q], valid[q], (uint32_t)(wr.n0 + i), sseg ? sseg + i : nullptr,
+                   lst, thr, nsel);
+  }
+  for (int base = wr.wb + kWaveStep; base < wr.we; base += kWaveStep) {  // wave-uniform
+#pragma unroll
+    for (int q = 0; q < kPrefetch; ++q) {
+      const int i = base + q * 64 + lane;
+      const bool ok = i < wr.we;
+      float a_q[G], v_q;
+      sc.score(q, i, ok, a_q, v_q);
+      emit_scores<G>(a, a_q, v_q, ok, (uint32_t)(wr.n0 + i), sseg ? sseg + i : nullptr, lst,
+                     thr, nsel);
+    }
+  }
+  if (a.select && lane == 0) {
+    const int subs = a.segs * kScoreWaves;
+    const int sub = seg * kScoreWaves + (int)(threadIdx.x >> 6);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int64_t row = (int64_t)b * a.Hq + (int64_t)g * G + j;
+      a.sub_cnt[row * subs + sub] = nsel[j];
+    }
+  }
+}
+
+// Fast path scorer: L a multiple of 16 (LW = L/4 words of ids per key),
+// 16-byte id rows, rotated table order.
+template <int G, int LW>
+struct RotScorer {
+  static constexpr int L = LW * 4;
+  static constexpr int kChunk = 64 / G;  // lookups per dependency step (a multiple of 4)
+  const uint8_t* idseg;
+  const float* vseg;
+  const float* tab;
+  int P, we, wb;
+  uint4 pf[kPrefetch][LW / 4];
+  float pf_vn[kPrefetch];
+  int r, rb, base_nowrap, base_wrap;
+
+  __device__ RotScorer(const ScoreArgs& a, int bg, const WaveRange& wr, const float* tab_)
+      : tab(tab_), P(a.P), we(wr.we), wb(wr.wb) {
+    // block-uniform bases of this segment; per-thread offsets stay 32-bit
+    idseg = a.ids + ((int64_t)bg * a.stride + wr.n0) * L;
+    vseg = a.vnorm + (int64_t)bg * a.stride + wr.n0;
+    // n0 + wb is a multiple of 8, so every key of this lane has the same
+    // rotation r = key index mod 8 and the same two bases
+    const int lane = threadIdx.x & 63;
+    r = lane & 7;
+    rb = r & 3;
+    base_nowrap = r * G;      // slot offset of step t: t*G + base
+    base_wrap = (r - L) * G;  // ... once t + r >= L
+#pragma unroll
+    for (int q = 0; q < kPrefetch; ++q) {
+      pf_vn[q] = 0.f;
+#pragma unroll
+      for (int k = 0; k < LW / 4; ++k) pf[q][k] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  __device__ __forceinline__ void load(int q, int i) {
+    const uint4* src = reinterpret_cast<const uint4*>(idseg + i * L);
+#pragma unroll
+    for (int k = 0; k < LW / 4; ++k) pf[q][k] = src[k];
+    pf_vn[q] = vseg[i];
+  }
+
+  __device__ __forceinline__ void prefetch() {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < kPrefetch; ++q) {
+      const int i = wb + q * 64 + lane;
+      if (i < we) load(q, i);
+    }
+  }
+
+  __device__ __forceinline__ void score(int q, int i, bool valid, float (&acc)[G], float& vn) {
+    uint32_t w[LW];
+#pragma unroll
+    for (int k = 0; k < LW / 4; ++k) {
+      w[4 * k] = pf[q][k].x; w[4 * k + 1] = pf[q][k].y;
+      w[4 * k + 2] = pf[q][k].z; w[4 * k + 3] = pf[q][k].w;
+    }
+    vn = pf_vn[q];
+    if (i + kWaveStep < we) load(q, i + kWaveStep);
 #pragma unroll
     for (int j = 0; j < G; ++j) acc[j] = 0.f;
+    if (!valid) return;
+    rotate_bytes<LW>(w, __ballot(r >= 4), rb);  // lanes with r >= 4 shift by a word
+#pragma unroll
+    for (int t = 0; t < L; ++t) {
+      // P bits of byte t: ids are < 2^P, so this never leaves the table
+      const uint32_t u = __builtin_amdgcn_ubfe(w[t >> 2], (t & 3) * 8, P);
+      const int off = (t + 7 < L) ? base_nowrap : (t + r < L ? base_nowrap : base_wrap);
+      float pr[G];
+      lds_load_group<G>(tab + (int)u * (L * G) + off + t * G, pr);
+#pragma unroll
+      for (int j = 0; j < G; ++j) acc[j] = t == 0 ? pr[j] : acc[j] + pr[j];
+      // the next kChunk lookups wait for these sums: at most 64 floats
+      // of lookups in flight per lane, which bounds the registers
+      if ((t + 1) % kChunk == 0 && t + 1 < L)
+        fence_chunk<G, LW>(acc, w, (t + 1) / 4, std::min(LW, (t + 1 + kChunk) / 4));
+    }
+  }
+};
+
+// General scorer: any L (byte loads of the ids, tables summed in order
+// l = 0..L-1).
+template <int G>
+struct GenericScorer {
+  const uint8_t* idseg;
+  const float* vseg;
+  const float* tab;
+  int L, P;
+  __device__ GenericScorer(const ScoreArgs& a, int bg, const WaveRange& wr, const float* tab_)
+      : tab(tab_), L(a.L), P(a.P) {
+    idseg = a.ids + ((int64_t)bg * a.stride + wr.n0) * a.L;
+    vseg = a.vnorm + (int64_t)bg * a.stride + wr.n0;
+  }
+  __device__ __forceinline__ void prefetch() {}
+  __device__ __forceinline__ void score(int, int i, bool valid, float (&acc)[G], float& vn) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) acc[j] = 0.f;
+    vn = 0.f;
+    if (!valid) return;
+    const uint8_t* id = idseg + (int64_t)i * L;
     for (int l = 0; l < L; ++l) {
-      const int u = idrow[n * L + l] & ((1 << P) - 1);
+      const int u = id[l] & ((1 << P) - 1);
       float pr[G];
 #pragma unroll
       for (int j = 0; j < G; ++j) pr[j] = tab[(u * L + l) * G + j];
 #pragma unroll
       for (int j = 0; j < G; ++j) acc[j] += pr[j];
     }
-    emit_scores<G>(acc, vrow[n], n, a.n_keys, srow, hloc);
+    vn = vseg[i];
   }
-  if (hloc) {
-    __syncthreads();
-    flush_hist<G>(hloc, a.hist + ((int64_t)b * a.Hq + (int64_t)g * G) * kHistBins);
-  }
+};
+
+template <int G, int LW>
+__global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(ScoreArgs a) {
+  extern __shared__ __align__(16) float tab[];
+  int bg, seg;
+  if (!score_block_coords(a.bhkv, a.segs, bg, seg)) return;
+  const WaveRange wr(a, seg);
+  RotScorer<G, LW> sc(a, bg, wr, tab);
+  score_block<G>(a, bg, seg, tab, sc, wr);
+}
+
+template <int G>
+__global__ __launch_bounds__(kScoreThreads) void score_kernel_generic(ScoreArgs a) {
+  extern __shared__ __align__(16) float tab[];
+  int bg, seg;
+  if (!score_block_coords(a.bhkv, a.segs, bg, seg)) return;
+  const WaveRange wr(a, seg);
+  GenericScorer<G> sc(a, bg, wr, tab);
+  score_block<G>(a, bg, seg, tab, sc, wr);
 }
 
 template <int G>
@@ -326,55 +552,37 @@ void set_lds_attributes() {
 }
 
 template <int G>
-hipError_t launch_score_g(ScoreArgs a, int L, hipStream_t stream) {
-  const size_t lds = score_lds_bytes(L, a.P, G, a.hist != nullptr);
-  // blocks resident per CU as limited by the 160 KB of LDS
-  const int per_cu = (int)std::max<size_t>(1, std::min<size_t>(2, kLdsBytesPerCU / lds));
-  const int64_t target = (int64_t)256 * per_cu;
-  const int64_t n_keys = a.n_keys;
-  int64_t segs = (target + a.bhkv - 1) / a.bhkv;
-  segs = std::max<int64_t>(1, std::min<int64_t>(segs, (n_keys + 2047) / 2048));
-  if (a.hist) segs = std::max<int64_t>(segs, (n_keys + kMaxSegForHist - 1) / kMaxSegForHist);
-  int64_t seg_len = (n_keys + segs - 1) / segs;
-  seg_len = (seg_len + 1023) / 1024 * 1024;
-  if (a.hist && seg_len > kMaxSegForHist) seg_len = kMaxSegForHist;
-  if (seg_len > kMaxSeg) seg_len = kMaxSeg;
-  segs = (n_keys + seg_len - 1) / seg_len;
-  a.segs = (int)segs;
-  a.seg_len = seg_len;
-  const int total = (int)(a.bhkv * segs);
+hipError_t launch_score_g(const ScoreArgs& a, hipStream_t stream) {
+  const size_t lds = score_lds_bytes(a.L, a.P, G);
+  const int total = a.bhkv * a.segs;
   const int grid = ((total + 7) / 8) * 8;
   set_lds_attributes<G>();
-  const bool aligned = (reinterpret_cast<uintptr_t>(a.ids) % 16 == 0) &&
-                       ((a.stride * L) % 16 == 0);
-  if (aligned && L == 32) {
-    launch_kernel((score_kernel_rot<G, 8>), dim3(grid), dim3(kRotThreads), lds,
-                       stream, a);
-  } else if (aligned && L == 64) {
-    launch_kernel((score_kernel_rot<G, 16>), dim3(grid), dim3(kRotThreads), lds,
-                       stream, a);
-  } else if (aligned && L == 16) {
-    launch_kernel((score_kernel_rot<G, 4>), dim3(grid), dim3(kRotThreads), lds,
-                       stream, a);
+  if (score_rotated(a.ids, a.stride, a.L)) {
+    if (a.L == 32)
+      launch_kernel((score_kernel_rot<G, 8>), dim3(grid), dim3(kScoreThreads), lds, stream, a);
+    else if (a.L == 64)
+      launch_kernel((score_kernel_rot<G, 16>), dim3(grid), dim3(kScoreThreads), lds, stream, a);
+    else
+      launch_kernel((score_kernel_rot<G, 4>), dim3(grid), dim3(kScoreThreads), lds, stream, a);
   } else {
-    launch_kernel((score_kernel_generic<G>), dim3(grid), dim3(kScoreThreads), lds,
-                       stream, a, L);
+    launch_kernel((score_kernel_generic<G>), dim3(grid), dim3(kScoreThreads), lds, stream, a);
   }
   return hipGetLastError();
 }
 
-}  // namespace
-
-size_t score_lds_bytes(int L, int P, int G, bool with_hist) {
-  return (size_t)(1 << P) * L * G * sizeof(float) +
-         (with_hist ? (size_t)G * kHistBins / 2 * sizeof(uint32_t) : 0);
+hipError_t launch_score_any(const ScoreArgs& a, int G, hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_score_g<1>(a, stream);
+    case 2: return launch_score_g<2>(a, stream);
+    case 4: return launch_score_g<4>(a, stream);
+    case 8: return launch_score_g<8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
-hipError_t launch_score(const float* table, const uint8_t* ids, const float* vnorm,
-                        int B, int Hq, int Hkv, int64_t n_keys, int64_t stride,
-                        int L, int P, float* scores, uint32_t* hist,
-                        hipStream_t stream) {
-  if (n_keys == 0) return hipSuccess;
+ScoreArgs base_args(const float* table, const uint8_t* ids, const float* vnorm, int B, int Hq,
+                    int Hkv, int64_t n_keys, int64_t stride, int L, int P) {
+  const ScoreGeom geo = plan_score(B * Hkv, n_keys, L, P, Hq / Hkv);
   ScoreArgs a{};
   a.table = table;
   a.ids = ids;
@@ -382,18 +590,67 @@ hipError_t launch_score(const float* table, const uint8_t* ids, const float* vno
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.bhkv = B * Hkv;
+  a.L = L;
   a.P = P;
+  a.segs = geo.segs;
+  a.seg_len = geo.seg_len;
   a.n_keys = n_keys;
   a.stride = stride;
+  return a;
+}
+
+}  // namespace
+
+size_t score_lds_bytes(int L, int P, int G) {
+  return score_table_region(L, P, G) +
+         ((size_t)G * kThrBins + kScratchWords) * sizeof(uint32_t);
+}
+
+bool score_rotated(const uint8_t* ids, int64_t stride, int L) {
+  const bool aligned = (reinterpret_cast<uintptr_t>(ids) % 16 == 0) && ((stride * L) % 16 == 0);
+  return aligned && (L == 16 || L == 32 || L == 64);
+}
+
+ScoreGeom plan_score(int bhkv, int64_t n_keys, int L, int P, int G) {
+  ScoreGeom geo{};
+  const size_t lds = score_lds_bytes(L, P, G);
+  // blocks resident per CU as limited by the 160 KB of LDS
+  const int per_cu = (int)std::max<size_t>(1, std::min<size_t>(2, kLdsBytesPerCU / lds));
+  const int64_t target = (int64_t)256 * per_cu;
+  constexpr int64_t kSegUnit = (int64_t)kScoreWaves * kWaveStep;
+  int64_t segs = (target + bhkv - 1) / bhkv;
+  segs = std::max<int64_t>(1, std::min<int64_t>(segs, (n_keys + kSegUnit - 1) / kSegUnit));
+  int64_t seg_len = (n_keys + segs - 1) / segs;
+  seg_len = (seg_len + kSegUnit - 1) / kSegUnit * kSegUnit;
+  if (seg_len > kMaxSeg) seg_len = kMaxSeg;
+  segs = (n_keys + seg_len - 1) / seg_len;
+  geo.segs = (int)segs;
+  geo.seg_len = seg_len;
+  geo.subs = (int)(segs * kScoreWaves);
+  geo.sub_len = seg_len / kScoreWaves;
+  return geo;
+}
+
+hipError_t launch_score(const float* table, const uint8_t* ids, const float* vnorm,
+                        int B, int Hq, int Hkv, int64_t n_keys, int64_t stride,
+                        int L, int P, float* scores, hipStream_t stream) {
+  if (n_keys == 0) return hipSuccess;
+  ScoreArgs a = base_args(table, ids, vnorm, B, Hq, Hkv, n_keys, stride, L, P);
   a.scores = scores;
-  a.hist = hist;
-  switch (Hq / Hkv) {
-    case 1: return launch_score_g<1>(a, L, stream);
-    case 2: return launch_score_g<2>(a, L, stream);
-    case 4: return launch_score_g<4>(a, L, stream);
-    case 8: return launch_score_g<8>(a, L, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_score_any(a, Hq / Hkv, stream);
+}
+
+hipError_t launch_score_select(const ScoreSelect& s, int B, int Hq, int Hkv, int64_t n_keys,
+                               int64_t stride, int L, int P, float* scores,
+                               hipStream_t stream) {
+  ScoreArgs a = base_args(s.table, s.ids, s.vnorm, B, Hq, Hkv, n_keys, stride, L, P);
+  a.scores = scores;
+  a.select = 1;
+  a.kk = s.kk;
+  a.thr = s.thr;
+  a.lists = s.lists;
+  a.sub_cnt = s.sub_cnt;
+  return launch_score_any(a, Hq / Hkv, stream);
 }
 
 }  // namespace socket_lsh

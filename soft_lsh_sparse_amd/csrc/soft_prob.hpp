@@ -1,4 +1,4 @@
-// Soft bucket probabilities: projections, per-bit weights and bucket
+// Soft bucket probabilities: projections, per-bit weights and bit-group
 // products of the table kernel.
 //
 // Soft assignment of SOCKET (page "Resumen Técnico: SOCKET - Estimador de
@@ -9,101 +9,113 @@
 // else -1) the softmax over the 2^P buckets factorises exactly into
 //     p(u) = prod_j sigma(2 s_j(u) z_j / tau),
 // since its normaliser sum_u exp(logit(u) - max) = prod_j (1 + exp(-2|z_j|/tau)).
+//
+// Arithmetic:
+//  * z = q . r in float64: each of d/8 lanes takes 8 consecutive coordinates
+//    (fma from 0, ascending), and the d/8 partial sums of a column are added
+//    by a fixed DPP pattern;
+//  * a bit's weights from a = exp(-2|z|/tau): 1/(1+a) and a/(1+a);
+//  * per table, the products of the bit groups (bits 0-2, 3-5, 6-7; each
+//    multiplied in ascending bit order from 1.0), and
+//    p(u) = (A[u & 7] * B[(u >> 3) & 7]) * C[u >> 6], rounded to float32.
 #pragma once
+
+#include <algorithm>
 
 #include "common.hpp"
 
 namespace socket_lsh {
 
-constexpr int kMaxBits = 8;
-
-template <typename T>
-__device__ __forceinline__ void load8(const typename T::storage* p, bool vec, int valid,
-                                      float (&v)[8]);
-
-template <>
-__device__ __forceinline__ void load8<BF16>(const uint16_t* p, bool vec, int valid,
-                                            float (&v)[8]) {
-  if (vec) {
-    unpack8_bf16(*reinterpret_cast<const uint4*>(p), v);
+// 8 consecutive elements (bf16 when BF, else f32) starting at element
+// `elem` of base, 16-byte aligned, as float.
+template <bool BF>
+__device__ __forceinline__ void load8_vec(const void* base, int64_t elem, float (&v)[8]) {
+  if constexpr (BF) {
+    unpack8_bf16(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem), v);
   } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = e < valid ? bf16_bits_to_f32(p[e]) : 0.f;
-  }
-}
-
-template <>
-__device__ __forceinline__ void load8<F32>(const float* p, bool vec, int valid,
-                                           float (&v)[8]) {
-  if (vec) {
+    const float* p = static_cast<const float*>(base) + elem;
     unpack4_f32(*reinterpret_cast<const uint4*>(p), v);
     unpack4_f32(*reinterpret_cast<const uint4*>(p + 4), v + 4);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = e < valid ? p[e] : 0.f;
   }
 }
 
-// Projections z[j][c] = q_j . R[:, c0 + c] for the G queries of a GQA group
-// (rows q0 + j*d of Q) and the nc hyperplane columns starting at c0, written
-// to out[j * nc + c] (float64). Block-cooperative: each lane accumulates 8
-// consecutive columns over one sixteenth of the d coordinates (ascending,
-// with fma, from 0); the sixteen parts of a column group sit in sixteen
-// adjacent lanes and are combined by a butterfly of additions (the same
-// pairing on every lane). bf16 and f32 products are exact in float64.
-// blockDim.x must be a multiple of 64.
-template <typename T>
-__device__ void block_projections(const typename T::storage* Q, int64_t q0,
-                                  const typename T::storage* R, int C, int c0,
-                                  int nc, int d, int G, double* out) {
-  constexpr int kParts = 16;
-  constexpr int kMaxSlice = 8;  // d <= 128
+template <bool BF>
+__device__ __forceinline__ float load1(const void* base, int64_t elem) {
+  if constexpr (BF) return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[elem]);
+  else return static_cast<const float*>(base)[elem];
+}
+
+// Sum over each aligned group of 8 lanes (the same pairing in every lane).
+__device__ __forceinline__ double sum8_f64(double v) {
+  v += dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f64<0x141>(v);  // row_half_mirror
+  return v;
+}
+
+// Projections z[j * nc + c] = q_j . R[:, c0 + c] (float64) of the `rows`
+// query rows starting at element q0 of Q (d = 64 or 128 coordinates each,
+// bf16 when BF, else f32) on nc of the C hyperplane columns of R [d][C].
+// Block-cooperative: a lane accumulates 8 consecutive columns over 8
+// consecutive coordinates, fma from 0 in ascending coordinate order (loads
+// in two rounds of four coordinates, each issued before its fmas, with no
+// branch between them); the d/8 parts of a column group sit in adjacent
+// lanes. blockDim.x must be a multiple of 64; Q and R 16-byte aligned.
+template <bool BF>
+__device__ __forceinline__ void group_projections(const void* Q, int64_t q0, int rows, int d,
+                                                  const void* R, int C, int c0, int nc,
+                                                  double* out) {
+  const int parts = d / 8;  // 8 or 16
   const int ncg = (nc + 7) / 8;
-  const int items = G * ncg * kParts;
-  const int dp = d / kParts;
-  const bool aligned = (C % 8 == 0) && (c0 % 8 == 0);
+  const int items = rows * ncg * parts;
+  const bool vec = C % 8 == 0 && c0 % 8 == 0;
   for (int base = 0; base < items; base += blockDim.x) {
     const int item = base + threadIdx.x;
-    const bool active = item < items;  // whole groups of 16 lanes
-    const int part = item % kParts;
-    const int cgj = item / kParts;
-    const int cg = cgj % ncg, j = cgj / ncg;
+    const bool active = item < items;  // whole groups of `parts` lanes
+    const int part = item % parts;
+    const int cg = (item / parts) % ncg;
+    const int j = item / (parts * ncg);
     const int valid = min(8, nc - cg * 8);
     double acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-    if (active) {
-      const typename T::storage* qrow = Q + q0 + (int64_t)j * d;
-      const typename T::storage* rcol = R + c0 + cg * 8;
-      const bool vec = aligned && valid == 8;
-      // all loads of this lane's slice first (dp <= kMaxSlice), then the fmas
-      float qv[kMaxSlice];
-      float rv[kMaxSlice][8];
+    if (active && vec) {
+      float qv[8];
+      load8_vec<BF>(Q, q0 + (int64_t)j * d + part * 8, qv);
 #pragma unroll
-      for (int k = 0; k < kMaxSlice; ++k) {
-        if (k < dp) {
-          const int i = part * dp + k;
-          qv[k] = T::load(qrow, i);
-          load8<T>(rcol + (int64_t)i * C, vec, valid, rv[k]);
+      for (int k0 = 0; k0 < 8; k0 += 4) {
+        float rv[4][8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          load8_vec<BF>(R, (int64_t)(part * 8 + k0 + k) * C + c0 + cg * 8, rv[k]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            acc[e] = fma((double)qv[k0 + k], (double)rv[k][e], acc[e]);
         }
       }
+    } else if (active) {
+      for (int k = 0; k < 8; ++k) {
+        const int i = part * 8 + k;
+        const double qi = (double)load1<BF>(Q, q0 + (int64_t)j * d + i);
 #pragma unroll
-      for (int k = 0; k < kMaxSlice; ++k) {
-        if (k < dp) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] = fma((double)qv[k], (double)rv[k][e], acc[e]);
-        }
+        for (int e = 0; e < 8; ++e)
+          if (e < valid)
+            acc[e] = fma(qi, (double)load1<BF>(R, (int64_t)i * C + c0 + cg * 8 + e), acc[e]);
       }
     }
+    if (parts == 16) {
 #pragma unroll
-    for (int m = 1; m < kParts; m <<= 1) {
+      for (int e = 0; e < 8; ++e) acc[e] = sum16_f64(acc[e]);
+    } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + __shfl_xor(acc[e], m, kWave);
+      for (int e = 0; e < 8; ++e) acc[e] = sum8_f64(acc[e]);
     }
     if (active && part == 0) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (e < valid) out[j * nc + cg * 8 + e] = acc[e];
+        if (e < valid) out[(int64_t)j * nc + cg * 8 + e] = acc[e];
     }
   }
 }
@@ -118,21 +130,84 @@ __device__ __forceinline__ void bit_weights(double z, double two_over_tau,
   w0 = z > 0.0 ? small : (z < 0.0 ? big : 0.5);
 }
 
-// p(u) = prod_{j < P} (bit j of u ? w1[j] : w0[j]) in float64, in the fixed
-// grouping ((bits 0-2) * (bits 3-5)) * (bits 6-7), each group multiplied in
-// ascending bit order; w1[j] = w0[j] = 1 for j >= P.
-__device__ __forceinline__ double bucket_prob(int u, const double (&w1)[kMaxBits],
-                                              const double (&w0)[kMaxBits]) {
-  double g[3];
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    double p = 1.0;
-#pragma unroll
-    for (int j = 3 * k; j < 3 * k + 3 && j < kMaxBits; ++j)
-      p *= ((u >> j) & 1) ? w1[j] : w0[j];
-    g[k] = p;
+// Entries of the bit-group products of one table: A (bits 0-2), B (bits
+// 3-5), C (bits 6-7), each 2^(bits of the group below P).
+struct GroupSizes {
+  int a, b, c;
+  __device__ __host__ explicit GroupSizes(int P)
+      : a(1 << std::min(P, 3)), b(1 << std::min(std::max(P - 3, 0), 3)),
+        c(1 << std::min(std::max(P - 6, 0), 2)) {}
+  __device__ __host__ int total() const { return a + b + c; }
+};
+
+__device__ __forceinline__ double group_prob(const double* g, const GroupSizes& gs, int u) {
+  return (g[u & (gs.a - 1)] * g[gs.a + ((u >> 3) & (gs.b - 1))]) * g[gs.a + gs.b + (u >> 6)];
+}
+
+// Strides (doubles) of the group products in LDS: table l of row j at
+// j * row + l * table. The table stride is odd and the row stride is
+// 16/G mod 16 (G: rows whose tables are read side by side, as the entries
+// (u, l, j) with j fastest), so that 16 lanes reading entry k of
+// consecutive (l, j) hit 16 different bank pairs.
+struct GroupStrides {
+  int table, row;
+  __device__ __host__ GroupStrides(int L, int P, int G) {
+    table = GroupSizes(P).total() | 1;
+    const int want = G > 1 ? 16 / G : 0;
+    row = L * table;
+    if (G > 1) row += ((want - row) % 16 + 16) % 16;
   }
-  return (g[0] * g[1]) * g[2];
+};
+
+// LDS (doubles) the set-up of nl tables of `rows` query rows needs:
+// projections, the two weights and the group products.
+__device__ __host__ inline size_t table_setup_doubles(int rows, int nl, int P) {
+  return (size_t)rows * (3 * (size_t)nl * P + (size_t)GroupStrides(nl, P, rows).row);
+}
+
+// Block-cooperative set-up of tables l0 .. l0+nl-1 of `rows` consecutive
+// query rows (from element q0 of Q; bf16 when BF, else f32): projections,
+// weights and group products. tmp holds table_setup_doubles(rows, nl, P)
+// doubles; returns the group products: those of table l0 + ll of row j
+// start at gp + j * GroupStrides(nl, P, rows).row + ll *
+// GroupStrides(nl, P, rows).table. Contains __syncthreads().
+template <bool BF>
+__device__ const double* table_setup(const void* Q, int64_t q0, int rows, int d, const void* R,
+                                     int L, int l0, int nl, int P, double two_over_tau,
+                                     double* tmp) {
+  const int C = L * P, nc = nl * P;
+  const GroupSizes gs(P);
+  const int gsz = gs.total();
+  const GroupStrides st(nl, P, rows);
+  double* z = tmp;                        // [rows][nc]
+  double* w1 = z + (size_t)rows * nc;     // [rows][nc]
+  double* w0 = w1 + (size_t)rows * nc;    // [rows][nc]
+  double* gp = w0 + (size_t)rows * nc;    // [rows][nl][gsz], strided
+  group_projections<BF>(Q, q0, rows, d, R, C, l0 * P, nc, z);
+  __syncthreads();
+  for (int i = threadIdx.x; i < rows * nc; i += blockDim.x)
+    bit_weights(z[i], two_over_tau, w1[i], w0[i]);
+  __syncthreads();
+  for (int e = threadIdx.x; e < rows * nl * gsz; e += blockDim.x) {
+    const int jl = e / gsz, k = e % gsz;  // jl = j * nl + ll
+    int combo, j0, nb;
+    if (k < gs.a) {
+      combo = k; j0 = 0; nb = std::min(P, 3);
+    } else if (k < gs.a + gs.b) {
+      combo = k - gs.a; j0 = 3; nb = std::min(std::max(P - 3, 0), 3);
+    } else {
+      combo = k - gs.a - gs.b; j0 = 6; nb = std::max(P - 6, 0);
+    }
+    double p = 1.0;
+    for (int jj = 0; jj < nb; ++jj) {
+      const int c = jl * P + j0 + jj;  // column ll * P + bit of row j
+      p *= ((combo >> jj) & 1) ? w1[c] : w0[c];
+    }
+    const int j = jl / nl, ll = jl % nl;
+    gp[j * st.row + ll * st.table + k] = p;
+  }
+  __syncthreads();
+  return gp;
 }
 
 }  // namespace socket_lsh

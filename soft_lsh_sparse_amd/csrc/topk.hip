@@ -32,6 +32,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "radix.hpp"
 
 #include <algorithm>
 
@@ -41,70 +42,7 @@ namespace {
 constexpr int kFilterThreads = 256;   // histogram kernel
 constexpr int kSelectThreads = 256;   // filter kernel (4 waves, one sub-list each)
 constexpr int kRefineThreads = 1024;  // refine kernel (one block per row)
-constexpr int kMaxSubLists = 256;     // per row
-
-__device__ __forceinline__ uint64_t lanemask_lt() {
-  const int lane = threadIdx.x & 63;
-  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
-}
-
-// Exclusive scan of one uint32 per thread over the block; returns the
-// thread's exclusive prefix and writes the block total to *total. Wave scans
-// with DPP; the wave totals are scanned by the first wave the same way.
-// `scratch` needs blockDim/64 + 1 words. Contains __syncthreads().
-template <int NT>
-__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch,
-                                         uint32_t* total) {
-  constexpr int NWV = NT / 64;
-  static_assert(NWV <= 64, "one wave scans the wave totals");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t x = wave_inclusive_scan_dpp(v);
-  if (lane == 63) scratch[wave] = x;
-  __syncthreads();
-  if (wave == 0) {
-    const uint32_t t = lane < NWV ? scratch[lane] : 0u;
-    const uint32_t inc = wave_inclusive_scan_dpp(t);
-    if (lane < NWV) scratch[lane] = inc - t;
-    if (lane == 63) scratch[NWV] = inc;
-  }
-  __syncthreads();
-  const uint32_t res = scratch[wave] + x - v;
-  *total = scratch[NWV];
-  __syncthreads();
-  return res;
-}
-
-// Given a 2048-bin histogram (global or LDS), find the bin holding the
-// need-th largest element (need >= 1, need <= sum of bins): the bin b with
-// count(> b) < need <= count(>= b). Writes b and count(> b) to out[0..1].
-template <int NT>
-__device__ void find_threshold_bin(const uint32_t* bins, uint32_t need,
-                                   uint32_t* scratch, uint32_t* out) {
-  constexpr int PER = kHistBins / NT;
-  if (threadIdx.x == 0) {
-    out[0] = 0;
-    out[1] = 0;
-  }
-  // thread t owns bins 2047 - (t*PER + i), i.e. bins in descending order
-  uint32_t cnt[PER];
-  uint32_t sum = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    cnt[i] = bins[kHistBins - 1 - (threadIdx.x * PER + i)];
-    sum += cnt[i];
-  }
-  uint32_t total;
-  uint32_t run = block_exclusive_scan<NT>(sum, scratch, &total);
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if (run < need && run + cnt[i] >= need) {
-      out[0] = kHistBins - 1 - (threadIdx.x * PER + i);
-      out[1] = run;
-    }
-    run += cnt[i];
-  }
-  __syncthreads();
-}
+constexpr int kMaxSubLists = 256;     // per row, filter path
 
 __global__ __launch_bounds__(kFilterThreads) void topk_hist_kernel(
     const float* __restrict__ scores, int64_t n, int64_t seg_len,
@@ -124,12 +62,6 @@ __global__ __launch_bounds__(kFilterThreads) void topk_hist_kernel(
     if (h[i]) atomicAdd(hr + i, h[i]);
 }
 
-// Number of set bits of `mask` below this lane.
-__device__ __forceinline__ uint32_t lane_prefix(uint64_t mask) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
 // Element p (0 <= p < total) of the concatenated sub-lists of a row: from
 // the LDS copy when the row's candidates fit there, else from memory.
 struct RowLists {
@@ -139,8 +71,7 @@ struct RowLists {
   const uint32_t* off;    // sub-list offsets in the concatenation (LDS)
   int subs;
   int64_t sub_len;
-  __device__ __forceinline__ uint2 at(uint32_t p) const {
-    if (p < cached) return cache[p];
+  __device__ __forceinline__ uint2 from_memory(uint32_t p) const {
     int lo = 0, hi = subs - 1;  // last sub-list with off[s] <= p
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -148,88 +79,104 @@ struct RowLists {
     }
     return glob[(int64_t)lo * sub_len + (p - off[lo])];
   }
+  __device__ __forceinline__ uint2 operator()(uint32_t p) const {
+    return p < cached ? cache[p] : from_memory(p);
+  }
 };
 
-constexpr int kRefineCache = 10240;  // (u, index) pairs kept in LDS (80 KB)
+// Entry p of a full score row: (order key, p).
+struct ScoreRowAt {
+  const float* s;
+  __device__ __forceinline__ uint2 operator()(uint32_t p) const {
+    return make_uint2(float_order_key(s[p]), p);
+  }
+};
+
+constexpr int kRefineCache = 16384;  // (u, index) pairs kept in LDS (128 KB)
 
 struct RefineShared {
-  uint32_t scratch[kRefineThreads / 64 + 1];
-  uint32_t thr[2];
+  uint32_t scratch[kRefineThreads / 64 + 3];
   uint32_t h[kHistBins];
-  uint32_t off[kMaxSubLists + 1];
+  uint32_t off[kMaxSelectSubLists + 1];
   uint2 cache[kRefineCache];
 };
 
-// One block per row: passes 2 and 3 of the radix select over the row's
-// candidates (all keys of first-digit bin b1 or above, in index order: the
-// sub-lists back to back) and the in-order emit of the kk selected indices.
-// The candidates are first copied into LDS sub-list by sub-list (one wave
-// per sub-list, contiguous reads); a row with more candidates than fit reads
-// the rest from memory.
-__global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
-    int64_t n, int64_t kk, int subs, int64_t sub_len, const uint32_t* __restrict__ hist,
-    const uint2* __restrict__ lists, const uint32_t* __restrict__ sub_cnt,
-    int32_t* __restrict__ idx) {
-  constexpr int NT = kRefineThreads;
-  __shared__ RefineShared sh;
-  const int row = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Offsets of the row's sub-lists in their concatenation, from their lengths
+// (off[subs] = total). Each thread sums a run of consecutive sub-lists.
+template <int NT>
+__device__ uint32_t sublist_offsets(const uint32_t* cnt, int subs, uint32_t* off,
+                                    uint32_t* scratch) {
+  const int per = (subs + NT - 1) / NT;
+  const int s0 = min(subs, (int)threadIdx.x * per), s1 = min(subs, s0 + per);
+  uint32_t sum = 0;
+  for (int s = s0; s < s1; ++s) sum += cnt[s];
+  uint32_t total;
+  uint32_t run = block_exclusive_scan<NT>(sum, scratch, &total);
+  for (int s = s0; s < s1; ++s) {
+    off[s] = run;
+    run += cnt[s];
+  }
+  if (threadIdx.x == 0) off[subs] = total;
+  __syncthreads();
+  return total;
+}
 
-  find_threshold_bin<NT>(hist + (int64_t)row * kHistBins, (uint32_t)kk, sh.scratch, sh.thr);
-  const uint32_t b1 = sh.thr[0];
-  const uint32_t need1 = (uint32_t)kk - sh.thr[1];
-
-  // sub-list offsets (subs <= kMaxSubLists <= NT)
-  {
-    const uint32_t c = threadIdx.x < subs ? sub_cnt[(int64_t)row * subs + threadIdx.x] : 0u;
-    uint32_t total;
-    const uint32_t ex = block_exclusive_scan<NT>(c, sh.scratch, &total);
-    if (threadIdx.x < subs) sh.off[threadIdx.x] = ex;
-    if (threadIdx.x == 0) sh.off[subs] = total;
+// The first min(total, kRefineCache) candidates into LDS: every thread
+// fetches eight entries (located by binary search over the offsets) before
+// storing any, so the loads overlap.
+template <int NT>
+__device__ void cache_candidates(RowLists& rl, uint2* cache, uint32_t total) {
+  const uint32_t cached = min(total, (uint32_t)kRefineCache);
+  constexpr int kBatch = 8;
+  for (uint32_t base = 0; base < cached; base += kBatch * NT) {
+    uint2 e[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const uint32_t p = base + i * NT + threadIdx.x;
+      if (p < cached) e[i] = rl.from_memory(p);
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const uint32_t p = base + i * NT + threadIdx.x;
+      if (p < cached) cache[p] = e[i];
+    }
   }
   __syncthreads();
-  const uint32_t total = sh.off[subs];
+  rl.cached = cached;
+}
 
-  const uint2* rowlists = lists + (int64_t)row * n;
-  RowLists rl{rowlists, sh.cache, 0u, sh.off, subs, sub_len};
-  {
-    const uint32_t cached = min(total, (uint32_t)kRefineCache);
-    for (int sl = wave; sl < subs; sl += NT / 64) {
-      const uint32_t o = sh.off[sl], c = sh.off[sl + 1] - o;
-      const uint2* src = rowlists + (int64_t)sl * sub_len;
-      for (uint32_t i = lane; i < c && o + i < cached; i += 64) sh.cache[o + i] = src[i];
+// Radix passes start_pass..2 (digits of 11, 11 and 10 bits) over the
+// entries at(0 .. total) of one row with order key >= floor, which hold
+// every key that can be among the kk best: `prefix` is the part of the
+// order key fixed by the passes before start_pass and `need` the number of
+// keys still to take under it. Then a final pass in entry (= index) order keeps every key
+// above the threshold T and the first keys equal to T, and writes their
+// indices at positions given by block scans: o[0 .. kk) ascending.
+template <int NT, typename At>
+__device__ void select_and_emit(const At& at, uint32_t total, uint32_t kk, int start_pass,
+                                uint32_t prefix, uint32_t need, uint32_t floor,
+                                RefineShared& sh, int32_t* o) {
+  uint32_t* res = sh.scratch + NT / 64 + 1;
+  for (int pass = start_pass; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int pshift = pass == 1 ? 21 : 10;
+    const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+    for (int i = threadIdx.x; i < kHistBins; i += NT) sh.h[i] = 0;
+    __syncthreads();
+    for (uint32_t p = threadIdx.x; p < total; p += NT) {
+      const uint32_t u = at(p).x;
+      if (u >= floor && (pass == 0 || (u >> pshift) == prefix))
+        atomicAdd(&sh.h[(u >> shift) & dmask], 1u);
     }
     __syncthreads();
-    rl.cached = cached;
+    find_threshold_bin<NT>(sh.h, need, sh.scratch, res);
+    prefix = pass == 0 ? res[0] : (prefix << (pass == 2 ? 10 : 11)) | res[0];
+    need -= res[1];
   }
-
-  // pass 2: bits 20..10 of the candidates in bin b1
-  for (int i = threadIdx.x; i < kHistBins; i += NT) sh.h[i] = 0;
-  __syncthreads();
-  for (uint32_t p = threadIdx.x; p < total; p += NT) {
-    const uint2 e = rl.at(p);
-    if ((e.x >> 21) == b1) atomicAdd(&sh.h[(e.x >> 10) & 2047u], 1u);
-  }
-  __syncthreads();
-  find_threshold_bin<NT>(sh.h, need1, sh.scratch, sh.thr);
-  const uint32_t b2 = sh.thr[0];
-  const uint32_t need2 = need1 - sh.thr[1];
-  const uint32_t pre2 = (b1 << 11) | b2;  // u >> 10 of the survivors
-
-  // pass 3: bits 9..0
-  for (int i = threadIdx.x; i < kHistBins; i += NT) sh.h[i] = 0;
-  __syncthreads();
-  for (uint32_t p = threadIdx.x; p < total; p += NT) {
-    const uint2 e = rl.at(p);
-    if ((e.x >> 10) == pre2) atomicAdd(&sh.h[e.x & 1023u], 1u);
-  }
-  __syncthreads();
-  find_threshold_bin<NT>(sh.h, need2, sh.scratch, sh.thr);
-  const uint32_t T = (pre2 << 10) | sh.thr[0];
-  const uint32_t ties = need2 - sh.thr[1];  // keys equal to T still to take
+  const uint32_t T = prefix;
+  const uint32_t ties = need;  // keys equal to T still to take
 
   // final pass, in index order: each thread takes 4 consecutive entries
-  int32_t* o = idx + (int64_t)row * kk;
   uint32_t run_tie = 0, run_out = 0;
   for (uint32_t base = 0; base < total; base += 4 * NT) {
     uint2 e[4];
@@ -237,7 +184,7 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t p = base + threadIdx.x * 4 + i;
-      e[i] = p < total ? rl.at(p) : make_uint2(0u, 0u);
+      e[i] = p < total ? at(p) : make_uint2(0u, 0u);
       if (p < total && e[i].x == T) ++n_tie;
     }
     uint32_t tie_tot;
@@ -260,13 +207,103 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (sel[i]) {
-        if (pos < (uint32_t)kk) o[pos] = (int32_t)e[i].y;
+        if (pos < kk) o[pos] = (int32_t)e[i].y;
         ++pos;
       }
     }
     run_tie += tie_tot;
     run_out += sel_tot;
   }
+}
+
+// Refine of the score-row top-k. One block per row: passes 2 and 3 of the
+// radix select over the row's candidates (all keys of first-digit bin b1 or
+// above, in index order: the sub-lists back to back, copied into LDS as far
+// as they fit) and the in-order emit of the kk selected indices.
+__global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
+    int64_t n, int64_t kk, int subs, int64_t sub_len, const uint32_t* __restrict__ hist,
+    const uint2* __restrict__ lists, const uint32_t* __restrict__ sub_cnt,
+    int32_t* __restrict__ idx) {
+  constexpr int NT = kRefineThreads;
+  __shared__ RefineShared sh;
+  const int row = blockIdx.x;
+  uint32_t* res = sh.scratch + NT / 64 + 1;
+  find_threshold_bin<NT>(hist + (int64_t)row * kHistBins, (uint32_t)kk, sh.scratch, res);
+  const uint32_t b1 = res[0];
+  const uint32_t need1 = (uint32_t)kk - res[1];
+  const uint32_t total = sublist_offsets<NT>(sub_cnt + (int64_t)row * subs, subs, sh.off,
+                                             sh.scratch);
+  RowLists rl{lists + (int64_t)row * n, sh.cache, 0u, sh.off, subs, sub_len};
+  cache_candidates<NT>(rl, sh.cache, total);
+  select_and_emit<NT>(rl, total, (uint32_t)kk, 1, b1, need1, 0u, sh, idx + (int64_t)row * kk);
+}
+
+// Selection of the decode path. One block per row. The score kernel's
+// blocks each emitted (in index order) the keys whose score reached their
+// own threshold; with T the largest of those thresholds, every key of the
+// row with order key >= T is a candidate. When at least kk of them are, the
+// kk best keys are among them: the candidates are copied into LDS as far as
+// they fit and go through all three radix passes with floor T. Otherwise
+// the block scores the whole row itself, with the score kernel's order of
+// additions (hence the same float32 values), into the row's score buffer,
+// and selects from that.
+__global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs a) {
+  constexpr int NT = kRefineThreads;
+  __shared__ RefineShared sh;
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t kk = (uint32_t)a.kk;
+  int32_t* o = a.idx + (int64_t)row * a.kk;
+  // T: the largest block threshold of the row
+  uint32_t tmax = 0;
+  for (int s = threadIdx.x; s < a.segs; s += NT) tmax = max(tmax, a.thr[(int64_t)row * a.segs + s]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, m, 64));
+  if (lane == 0) sh.scratch[wave] = tmax;
+  __syncthreads();
+  tmax = 0;
+  for (int w = 0; w < NT / 64; ++w) tmax = max(tmax, sh.scratch[w]);
+  __syncthreads();
+
+  const uint32_t total = sublist_offsets<NT>(a.sub_cnt + (int64_t)row * a.subs, a.subs, sh.off,
+                                             sh.scratch);
+  RowLists rl{a.lists + (int64_t)row * a.n, sh.cache, 0u, sh.off, a.subs, a.sub_len};
+  cache_candidates<NT>(rl, sh.cache, total);
+  uint32_t above = 0;
+  for (uint32_t p = threadIdx.x; p < total; p += NT) above += rl(p).x >= tmax ? 1u : 0u;
+  uint32_t n_above;
+  (void)block_exclusive_scan<NT>(above, sh.scratch, &n_above);
+  if (n_above >= kk) {
+    select_and_emit<NT>(rl, total, kk, 0, 0u, kk, tmax, sh, o);
+    return;
+  }
+
+  const int G = a.Hq / a.Hkv;
+  const int b = row / a.Hq, hq = row % a.Hq;
+  const int bg = b * a.Hkv + hq / G, j = hq % G;
+  const int L = a.L, nb = 1 << a.P;
+  const float* tg = a.table + (int64_t)bg * nb * L * G + j;  // (u, l) at (u * L + l) * G
+  float* tabs = reinterpret_cast<float*>(sh.cache);
+  const bool lds_tab = (size_t)nb * L * sizeof(float) <= sizeof(sh.cache);
+  if (lds_tab)
+    for (int e = threadIdx.x; e < nb * L; e += NT) tabs[e] = tg[(int64_t)e * G];
+  __syncthreads();
+  float* srow = a.scores + (int64_t)row * a.n;
+  const uint8_t* idh = a.ids + (int64_t)bg * a.stride * L;
+  const float* vnh = a.vnorm + (int64_t)bg * a.stride;
+  for (int64_t i = threadIdx.x; i < a.n; i += NT) {
+    const int r = a.rotated ? (int)(i & 7) : 0;
+    float acc = 0.f;
+    for (int t = 0; t < L; ++t) {
+      const int l = t + r < L ? t + r : t + r - L;
+      const int u = idh[i * L + l] & (nb - 1);
+      const float p = lds_tab ? tabs[u * L + l] : tg[(int64_t)(u * L + l) * G];
+      acc = t == 0 ? p : acc + p;
+    }
+    srow[i] = vnh[i] * acc;
+  }
+  __syncthreads();
+  select_and_emit<NT>(ScoreRowAt{srow}, (uint32_t)a.n, kk, 0, 0u, kk, 0u, sh, o);
 }
 
 // Filter. Block (seg, row) finds the bin b1 of the kk-th key from the
@@ -391,27 +428,27 @@ hipError_t launch_zero_u32(uint32_t* p, int64_t words, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t launch_iota_rows(int32_t* idx, int rows, int64_t n, hipStream_t stream) {
+  const int64_t total = (int64_t)rows * n;
+  if (total == 0) return hipSuccess;
+  const int grid = (int)std::min<int64_t>((total + 255) / 256, 4096);
+  launch_kernel(iota_rows_kernel, dim3(grid), dim3(256), 0, stream, idx, rows, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const float* scores, const TopkPlan& plan, int32_t* idx,
-                       void* ws, bool hist_ready, hipStream_t stream) {
+                       void* ws, hipStream_t stream) {
   if (plan.rows == 0 || plan.n == 0) return hipSuccess;
-  if (plan.kk == plan.n) {
-    const int64_t total = (int64_t)plan.rows * plan.n;
-    const int grid = (int)std::min<int64_t>((total + 255) / 256, 4096);
-    launch_kernel(iota_rows_kernel, dim3(grid), dim3(256), 0, stream, idx, plan.rows, plan.n);
-    return hipGetLastError();
-  }
+  if (plan.kk == plan.n) return launch_iota_rows(idx, plan.rows, plan.n, stream);
   unsigned char* base = static_cast<unsigned char*>(ws);
   uint32_t* hist = reinterpret_cast<uint32_t*>(base + plan.hist_off);
   uint32_t* cnt = reinterpret_cast<uint32_t*>(base + plan.cnt_off);
   uint2* lists = reinterpret_cast<uint2*>(base + plan.list_off);
-  hipError_t err;
-  if (!hist_ready) {
-    err = launch_zero_u32(hist, plan.zero_words, stream);
-    if (err != hipSuccess) return err;
-    launch_kernel(topk_hist_kernel, dim3(plan.segs, plan.rows), dim3(kFilterThreads), 0,
-                  stream, scores, plan.n, plan.seg_len, hist);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
+  hipError_t err = launch_zero_u32(hist, plan.zero_words, stream);
+  if (err != hipSuccess) return err;
+  launch_kernel(topk_hist_kernel, dim3(plan.segs, plan.rows), dim3(kFilterThreads), 0,
+                stream, scores, plan.n, plan.seg_len, hist);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   const int vec4 = (plan.n % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0) ? 1 : 0;
   launch_kernel(topk_filter_kernel, dim3(plan.segs, plan.rows), dim3(kSelectThreads), 0,
                 stream, scores, plan.n, plan.kk, plan.segs, plan.sub_len, hist, lists, cnt,
@@ -419,6 +456,12 @@ hipError_t launch_topk(const float* scores, const TopkPlan& plan, int32_t* idx,
   if ((err = hipGetLastError()) != hipSuccess) return err;
   launch_kernel(topk_refine_kernel, dim3(plan.rows), dim3(kRefineThreads), 0, stream, plan.n,
                 plan.kk, plan.subs, plan.sub_len, hist, lists, cnt, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_select(const SelectArgs& a, int rows, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  launch_kernel(topk_select_kernel, dim3(rows), dim3(kRefineThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -40,14 +40,15 @@ CSRC = os.path.join(HERE, "csrc")
 KERNEL_SOURCES = {
     "hash_keys_bf16_kernel": ["hash_keys.hip"],
     "hash_keys_f32_kernel": ["hash_keys.hip"],
-    "bucket_probs_kernel": ["bucket_probs.hip", "soft_prob.hpp"],
-    "score_kernel_rot": ["score.hip"],
-    "score_kernel_generic": ["score.hip"],
-    "zero_u32_kernel": ["topk.hip"],
-    "iota_rows_kernel": ["topk.hip"],
-    "topk_hist_kernel": ["topk.hip"],
-    "topk_filter_kernel": ["topk.hip"],
-    "topk_refine_kernel": ["topk.hip"],
+    "bucket_probs_kernel": ["bucket_probs.hip", "soft_prob.hpp", "radix.hpp"],
+    "score_kernel_rot": ["score.hip", "radix.hpp"],
+    "score_kernel_generic": ["score.hip", "radix.hpp"],
+    "zero_u32_kernel": ["topk.hip", "radix.hpp"],
+    "iota_rows_kernel": ["topk.hip", "radix.hpp"],
+    "topk_hist_kernel": ["topk.hip", "radix.hpp"],
+    "topk_filter_kernel": ["topk.hip", "radix.hpp"],
+    "topk_refine_kernel": ["topk.hip", "radix.hpp"],
+    "topk_select_kernel": ["topk.hip", "radix.hpp"],
     "sparse_attn_kernel": ["sparse_attn.hip"],
     "attn_merge_kernel": ["sparse_attn.hip"],
 }
@@ -77,7 +78,7 @@ def canonical(name: str) -> str:
 def source_digest(kernel: str) -> str:
     files = KERNEL_SOURCES.get(kernel)
     if files is None and kernel == "score_kernel":
-        files = ["score.hip"]
+        files = ["score.hip", "radix.hpp"]
     if files is None:
         raise KeyError(kernel)
     h = hashlib.sha256()

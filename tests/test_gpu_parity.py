@@ -482,3 +482,92 @@ def test_decode_scores_equal_stage_pipeline_bit_for_bit(name):
     torch.cuda.synchronize()
     assert torch.equal(sc, sc2)
     assert torch.equal(idx, idx2)
+
+
+def _sample_positions(n):
+    """Keys the decode's threshold estimate scores: key_i = floor(i * n / n_s),
+    n_s = min(n, 2048)."""
+    n_s = min(n, 2048)
+    return (np.arange(n_s, dtype=np.int64) * n) // n_s
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_128k_b4", "llama3_8b_1m"])
+def test_decode_without_score_rows_selects_the_same(name):
+    """Without score rows the decode keeps only the candidates above the
+    estimated threshold; selection and output must not change."""
+    w = W.WORKLOADS[name]
+    log(f"decode with / without score rows {w.name}")
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=3)
+    ids, vn = S.hash_keys(K, V, R, w.L, w.P)
+    idx = torch.empty((w.B, w.Hq, w.kk), dtype=torch.int32, device=DEV)
+    sc = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=DEV)
+    out, _, _ = S.decode(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, idx_out=idx,
+                         scores_out=sc)
+    idx2 = torch.empty_like(idx)
+    out2, _, _ = S.decode(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, idx_out=idx2)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    assert torch.equal(out, out2)
+    sc_np = sc.cpu().numpy()
+    idx_np = idx.cpu().numpy()
+    for (b, h) in [(0, 0), (w.B - 1, w.Hq - 1)]:
+        assert np.array_equal(idx_np[b, h], O.topk_indices(sc_np[b, h], w.k))
+
+
+@pytest.mark.parametrize("with_rows", [True, False])
+def test_decode_threshold_fallback_selects_from_full_rows(with_rows):
+    """Value norms vanish except on the sampled keys of KV head 0, so that head's
+    rows see fewer than k keys reach the estimated threshold and are selected
+    from fully scored rows; KV head 1 takes the candidate path. Ties among the
+    zero scores go to the lower indices."""
+    w = W.custom_workload(B=1, Hq=4, Hkv=2, d=128, N=65536, dtype="bf16", L=32, P=8,
+                          tau=0.3, k=1024, lognormal_v=True, name="fallback")
+    log(f"decode threshold fallback with_rows={with_rows}")
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=11)
+    ids, vn = S.hash_keys(K, V, R, w.L, w.P)
+    pos = torch.from_numpy(_sample_positions(w.N)).to(DEV)
+    vn_mod = vn.clone()
+    keep = vn[0, 0, pos].clone()
+    vn_mod[0, 0].zero_()
+    vn_mod[0, 0, pos] = keep
+    idx = torch.empty((1, 4, w.kk), dtype=torch.int32, device=DEV)
+    sc = torch.empty((1, 4, w.N), dtype=torch.float32, device=DEV) if with_rows else None
+    out, _, _ = S.decode(Q, K, V, R, ids, vn_mod, w.L, w.P, w.tau, w.k, idx_out=idx,
+                         scores_out=sc)
+    table = S.bucket_probs(Q, R, w.Hkv, w.L, w.P, w.tau)
+    sc_ref = S.score(table, ids, vn_mod, w.Hq)
+    torch.cuda.synchronize()
+    if with_rows:
+        assert torch.equal(sc, sc_ref)
+    s_np = sc_ref.cpu().numpy()
+    idx_np = idx.cpu().numpy()
+    for h in range(4):
+        assert np.array_equal(idx_np[0, h], O.topk_indices(s_np[0, h], w.k)), f"head {h}"
+    # head 0's selection: only sampled keys score above zero
+    assert np.isin(idx_np[0, 0], _sample_positions(w.N)).all()
+    Q64 = f64(Q)
+    for h in (0, 3):
+        g = h // 2
+        sel_t = idx[0, h].long()
+        ref = O.subset_attention(Q64[:, h:h + 1], f64(K[0, g][sel_t])[None, None],
+                                 f64(V[0, g][sel_t])[None, None],
+                                 np.arange(w.kk)[None, None], 1)[0, 0]
+        assert np.max(np.abs(f64(out[0, h]) - ref)) <= 2e-2
+
+
+@pytest.mark.parametrize("N", [9000, 40000])
+def test_decode_all_scores_tied(N):
+    """Every key in the same buckets with the same value norm: all scores of a
+    row are equal, every key reaches the threshold (beyond the LDS copy of
+    the candidates at N = 40000), and the k lowest indices are selected."""
+    w = W.custom_workload(B=1, Hq=4, Hkv=1, d=128, N=N, dtype="bf16", L=32, P=8,
+                          tau=0.3, k=700, lognormal_v=False, name="tied")
+    log(f"decode all tied N={N}")
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=12)
+    ids = torch.full((1, 1, N, w.L), 5, dtype=torch.uint8, device=DEV)
+    vn = torch.ones((1, 1, N), dtype=torch.float32, device=DEV)
+    idx = torch.empty((1, 4, w.kk), dtype=torch.int32, device=DEV)
+    out, _, _ = S.decode(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, idx_out=idx)
+    torch.cuda.synchronize()
+    want = torch.arange(w.kk, dtype=torch.int32).expand(1, 4, w.kk)
+    assert torch.equal(idx.cpu(), want)
