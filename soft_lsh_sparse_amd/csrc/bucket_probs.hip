@@ -48,8 +48,9 @@ __global__ __launch_bounds__(kProbThreads) void bucket_probs_kernel(ProbArgs a) 
   const int nl = min(a.tables_per_block, L - l0);
   const GroupSizes gs(P);
   const GroupStrides st(nl, P, G);
-  const double* gp = table_setup<BF>(a.Q, ((int64_t)b * a.Hq + (int64_t)g * G) * a.d, G, a.d,
-                                     a.R, L, l0, nl, P, a.two_over_tau, smem);
+  double* gp = smem + table_zw_doubles(G, nl, P);
+  table_setup<BF>(a.Q, ((int64_t)b * a.Hq + (int64_t)g * G) * a.d, G, a.d, a.R, L, l0, nl, P,
+                  a.two_over_tau, smem, gp);
   const int nbuckets = 1 << P;
   const int per_u = nl * G;  // entries (ll, j) of one bucket, j fastest
   float* out = a.table + (int64_t)bg * nbuckets * L * G + (int64_t)l0 * G;
@@ -91,7 +92,7 @@ hipError_t launch_bucket_probs(const void* Q, const void* R, bool bf16, int B,
   tpb = std::max(1, std::min(tpb, std::min(L, 8)));
   a.tables_per_block = tpb;
   const int G = Hq / Hkv;
-  const size_t lds = table_setup_doubles(G, tpb, P) * sizeof(double);
+  const size_t lds = (table_zw_doubles(G, tpb, P) + table_gp_doubles(G, tpb, P)) * sizeof(double);
   const dim3 grid(bhkv, (L + tpb - 1) / tpb);
   if (bf16)
     launch_kernel(bucket_probs_kernel<true>, grid, dim3(kProbThreads), lds, stream, a);

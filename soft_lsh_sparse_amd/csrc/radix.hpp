@@ -42,9 +42,48 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch,
   return res;
 }
 
+// Exclusive scans of two uint32 per thread over the block at once (same
+// synchronisations as one); totals to *ta and *tb. `scratch` needs
+// 2 * (blockDim/64 + 1) words. Contains __syncthreads().
+template <int NT>
+__device__ inline void block_exclusive_scan2(uint32_t a, uint32_t b, uint32_t* scratch,
+                                             uint32_t* ea, uint32_t* eb, uint32_t* ta,
+                                             uint32_t* tb) {
+  constexpr int NWV = NT / 64;
+  static_assert(NWV <= 64, "one wave scans the wave totals");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t* sa = scratch;
+  uint32_t* sb = scratch + NWV + 1;
+  const uint32_t xa = wave_inclusive_scan_dpp(a), xb = wave_inclusive_scan_dpp(b);
+  if (lane == 63) {
+    sa[wave] = xa;
+    sb[wave] = xb;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t va = lane < NWV ? sa[lane] : 0u, vb = lane < NWV ? sb[lane] : 0u;
+    const uint32_t ia = wave_inclusive_scan_dpp(va), ib = wave_inclusive_scan_dpp(vb);
+    if (lane < NWV) {
+      sa[lane] = ia - va;
+      sb[lane] = ib - vb;
+    }
+    if (lane == 63) {
+      sa[NWV] = ia;
+      sb[NWV] = ib;
+    }
+  }
+  __syncthreads();
+  *ea = sa[wave] + xa - a;
+  *eb = sb[wave] + xb - b;
+  *ta = sa[NWV];
+  *tb = sb[NWV];
+  __syncthreads();
+}
+
 // Given a 2048-bin histogram (global or LDS), find the bin holding the
-// need-th largest element (need >= 1, need <= sum of bins): the bin b with
-// count(> b) < need <= count(>= b). Writes b and count(> b) to out[0..1].
+// need-th largest element (need >= 1): the bin b with count(> b) < need <=
+// count(>= b). Writes b, count(> b) and the sum of the bins to out[0..2]
+// (out[0..1] stay 0 when the bins hold fewer than need elements).
 template <int NT>
 __device__ inline void find_threshold_bin(const uint32_t* bins, uint32_t need,
                                    uint32_t* scratch, uint32_t* out) {
@@ -63,6 +102,7 @@ __device__ inline void find_threshold_bin(const uint32_t* bins, uint32_t need,
   }
   uint32_t total;
   uint32_t run = block_exclusive_scan<NT>(sum, scratch, &total);
+  if (threadIdx.x == 0) out[2] = total;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     if (run < need && run + cnt[i] >= need) {
@@ -72,36 +112,6 @@ __device__ inline void find_threshold_bin(const uint32_t* bins, uint32_t need,
     run += cnt[i];
   }
   __syncthreads();
-}
-
-// The need-th largest (1 <= need <= number of valid values) of the values
-// u[i] (where valid[i]) that the block's threads hold, PER each: a radix
-// select with digits of 11, 11 and 10 bits over the 2048-bin LDS histogram
-// h. scratch needs NT/64 + 3 words. Every thread gets the result. Contains
-// __syncthreads().
-template <int NT, int PER>
-__device__ inline uint32_t block_select_nth(const uint32_t (&u)[PER], const bool (&valid)[PER],
-                                            uint32_t need, uint32_t* h, uint32_t* scratch) {
-  uint32_t* res = scratch + NT / 64 + 1;
-  uint32_t prefix = 0;  // u >> 21, then u >> 10, of the values still in the running
-#pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int pshift = pass == 1 ? 21 : 10;
-    const uint32_t dmask = pass == 2 ? 1023u : 2047u;
-    for (int i = threadIdx.x; i < kHistBins; i += NT) h[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (valid[i] && (pass == 0 || (u[i] >> pshift) == prefix))
-        atomicAdd(&h[(u[i] >> shift) & dmask], 1u);
-    }
-    __syncthreads();
-    find_threshold_bin<NT>(h, need, scratch, res);
-    prefix = (prefix << (pass == 2 ? 10 : 11)) | res[0];
-    need -= res[1];
-  }
-  return prefix;
 }
 
 }  // namespace socket_lsh

@@ -95,7 +95,8 @@ struct ScoreRowAt {
 constexpr int kRefineCache = 16384;  // (u, index) pairs kept in LDS (128 KB)
 
 struct RefineShared {
-  uint32_t scratch[kRefineThreads / 64 + 3];
+  uint32_t scratch[2 * (kRefineThreads / 64 + 1) + 4];
+  uint32_t tmax[kRefineThreads / 64];
   uint32_t h[kHistBins];
   uint32_t off[kMaxSelectSubLists + 1];
   uint2 cache[kRefineCache];
@@ -176,43 +177,29 @@ __device__ void select_and_emit(const At& at, uint32_t total, uint32_t kk, int s
   const uint32_t T = prefix;
   const uint32_t ties = need;  // keys equal to T still to take
 
-  // final pass, in index order: each thread takes 4 consecutive entries
-  uint32_t run_tie = 0, run_out = 0;
-  for (uint32_t base = 0; base < total; base += 4 * NT) {
-    uint2 e[4];
-    uint32_t n_tie = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t p = base + threadIdx.x * 4 + i;
-      e[i] = p < total ? at(p) : make_uint2(0u, 0u);
-      if (p < total && e[i].x == T) ++n_tie;
+  // final pass, in index order: every thread takes a run of consecutive
+  // entries; one scan gives, per thread, the keys above T and the keys
+  // equal to T before its run
+  const uint32_t per = (total + NT - 1) / NT;
+  const uint32_t p0 = min(total, (uint32_t)threadIdx.x * per), p1 = min(total, p0 + per);
+  uint32_t n_gt = 0, n_eq = 0;
+  for (uint32_t p = p0; p < p1; ++p) {
+    const uint32_t u = at(p).x;
+    n_gt += u > T ? 1u : 0u;
+    n_eq += u == T ? 1u : 0u;
+  }
+  uint32_t ex_gt, ex_eq, tot_gt, tot_eq;
+  block_exclusive_scan2<NT>(n_gt, n_eq, sh.scratch, &ex_gt, &ex_eq, &tot_gt, &tot_eq);
+  uint32_t pos = ex_gt + min(ex_eq, ties);
+  uint32_t tie_rank = ex_eq;
+  for (uint32_t p = p0; p < p1; ++p) {
+    const uint2 e = at(p);
+    bool take = e.x > T;
+    if (e.x == T) take = tie_rank++ < ties;
+    if (take) {
+      if (pos < kk) o[pos] = (int32_t)e.y;
+      ++pos;
     }
-    uint32_t tie_tot;
-    uint32_t tie_rank = run_tie + block_exclusive_scan<NT>(n_tie, sh.scratch, &tie_tot);
-    bool sel[4];
-    uint32_t n_sel = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t p = base + threadIdx.x * 4 + i;
-      const bool valid = p < total;
-      sel[i] = valid && e[i].x > T;
-      if (valid && e[i].x == T) {
-        sel[i] = tie_rank < ties;
-        ++tie_rank;
-      }
-      n_sel += sel[i] ? 1u : 0u;
-    }
-    uint32_t sel_tot;
-    uint32_t pos = run_out + block_exclusive_scan<NT>(n_sel, sh.scratch, &sel_tot);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (sel[i]) {
-        if (pos < kk) o[pos] = (int32_t)e[i].y;
-        ++pos;
-      }
-    }
-    run_tie += tie_tot;
-    run_out += sel_tot;
   }
 }
 
@@ -254,27 +241,50 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t kk = (uint32_t)a.kk;
   int32_t* o = a.idx + (int64_t)row * a.kk;
-  // T: the largest block threshold of the row
+  uint32_t* res = sh.scratch + NT / 64 + 1;
+  // T: the largest block threshold of the row (loads issued with the
+  // sub-list lengths below)
   uint32_t tmax = 0;
   for (int s = threadIdx.x; s < a.segs; s += NT) tmax = max(tmax, a.thr[(int64_t)row * a.segs + s]);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, m, 64));
-  if (lane == 0) sh.scratch[wave] = tmax;
-  __syncthreads();
-  tmax = 0;
-  for (int w = 0; w < NT / 64; ++w) tmax = max(tmax, sh.scratch[w]);
-  __syncthreads();
-
+  for (int i = threadIdx.x; i < kHistBins; i += NT) sh.h[i] = 0u;
   const uint32_t total = sublist_offsets<NT>(a.sub_cnt + (int64_t)row * a.subs, a.subs, sh.off,
                                              sh.scratch);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, m, 64));
+  if (lane == 0) sh.tmax[wave] = tmax;
+  __syncthreads();
+  tmax = 0;
+  for (int w = 0; w < NT / 64; ++w) tmax = max(tmax, sh.tmax[w]);
+
+  // candidates into LDS (as far as they fit), counted into the first-digit
+  // histogram when they reach T
   RowLists rl{a.lists + (int64_t)row * a.n, sh.cache, 0u, sh.off, a.subs, a.sub_len};
-  cache_candidates<NT>(rl, sh.cache, total);
-  uint32_t above = 0;
-  for (uint32_t p = threadIdx.x; p < total; p += NT) above += rl(p).x >= tmax ? 1u : 0u;
-  uint32_t n_above;
-  (void)block_exclusive_scan<NT>(above, sh.scratch, &n_above);
+  {
+    const uint32_t cached = min(total, (uint32_t)kRefineCache);
+    constexpr int kBatch = 8;
+    for (uint32_t base = 0; base < total; base += kBatch * NT) {
+      uint2 e[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const uint32_t p = base + i * NT + threadIdx.x;
+        if (p < total) e[i] = rl.from_memory(p);
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const uint32_t p = base + i * NT + threadIdx.x;
+        if (p < total) {
+          if (p < cached) sh.cache[p] = e[i];
+          if (e[i].x >= tmax) atomicAdd(&sh.h[e[i].x >> 21], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    rl.cached = cached;
+  }
+  find_threshold_bin<NT>(sh.h, kk, sh.scratch, res);
+  const uint32_t b1 = res[0], above1 = res[1], n_above = res[2];
   if (n_above >= kk) {
-    select_and_emit<NT>(rl, total, kk, 0, 0u, kk, tmax, sh, o);
+    select_and_emit<NT>(rl, total, kk, 1, b1, kk - above1, tmax, sh, o);
     return;
   }
 
@@ -319,7 +329,7 @@ __global__ __launch_bounds__(kSelectThreads) void topk_filter_kernel(
   constexpr int kWaves = kSelectThreads / 64;
   __shared__ struct {
     uint32_t scratch[kSelectThreads / 64 + 1];
-    uint32_t thr[2];
+    uint32_t thr[3];
   } sh;
   const int row = blockIdx.y, seg = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
