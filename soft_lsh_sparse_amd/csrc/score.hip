@@ -232,13 +232,13 @@ __device__ inline uint32_t threshold_rank(int64_t kk, int64_t n, int n_b) {
 // octaves; farther keys are not counted) and finds the first bin b1 at
 // which the count from bin 0 reaches m; the second counts (D >> 11) & 255
 // of the keys in b1 and finds b2 the same way. The threshold is the lowest
-// key of sub-bin (b1, b2), or 0 when the bins hold fewer than m keys. Each
-// row's bins are searched by 256 threads (four waves, DPP scans).
+// key of sub-bin (b1, b2), or 0 when the bins hold fewer than m keys. One
+// wave searches each row's bins (DPP scans).
 template <int G>
 __device__ void block_thresholds(const uint32_t (&uk)[kPrefetch][G],
                                  const bool (&valid)[kPrefetch], uint32_t m, uint32_t* hist,
                                  uint32_t* scratch, uint32_t (&thr)[G]) {
-  uint32_t* wmax = scratch;              // [16][G] wave maxima, then [16] wave totals
+  uint32_t* wmax = scratch;              // [16][G] wave maxima
   uint32_t* res = scratch + 16 * G;      // [G][2] chosen bin (or kThrBins), count before it
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // row maxima
@@ -288,25 +288,27 @@ __device__ void block_thresholds(const uint32_t (&uk)[kPrefetch][G],
       }
     }
     __syncthreads();
-    uint32_t* wtot = scratch;
-    for (int base = 0; base < G * kThrBins; base += kScoreThreads) {
-      const int slot = base + (int)threadIdx.x;
-      const bool act = slot < G * kThrBins;
-      const int r = slot / kThrBins, bin = slot % kThrBins;
-      const uint32_t c = act ? hist[slot] : 0u;
-      const uint32_t inc = wave_inclusive_scan_dpp(c);
-      if (lane == 63) wtot[wave] = inc;
-      __syncthreads();
-      uint32_t before = 0;
-      const int w_in_row = (slot / 64) % (kThrBins / 64);
-      for (int k = 1; k <= w_in_row; ++k) before += wtot[wave - k];
-      const uint32_t base_cnt = pass == 0 ? 0u : res[2 * r + 1];
-      if (act && base_cnt + before + inc >= m && base_cnt + before + inc - c < m) {
-        res[2 * r] = (uint32_t)bin;
-        if (pass == 0) res[2 * r + 1] = before + inc - c;
+    // wave j scans row j's bins: 4 consecutive bins per lane, DPP prefix
+    // sums over the lanes
+    static_assert(kThrBins == 4 * 64, "four bins per lane");
+    if (wave < G) {
+      const uint32_t* hr = hist + wave * kThrBins + lane * 4;
+      const uint32_t c0 = hr[0], c1 = hr[1], c2 = hr[2], c3 = hr[3];
+      const uint32_t sum = c0 + c1 + c2 + c3;
+      const uint32_t before = (pass == 0 ? 0u : res[2 * wave + 1]) +
+                              wave_inclusive_scan_dpp(sum) - sum;
+      const uint32_t cs[4] = {c0, c1, c2, c3};
+      uint32_t run = before;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (run < m && run + cs[i] >= m) {
+          res[2 * wave] = (uint32_t)(lane * 4 + i);
+          if (pass == 0) res[2 * wave + 1] = run;
+        }
+        run += cs[i];
       }
-      __syncthreads();
     }
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       if (pass == 0) {

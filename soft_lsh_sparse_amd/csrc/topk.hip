@@ -257,25 +257,31 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
   for (int w = 0; w < NT / 64; ++w) tmax = max(tmax, sh.tmax[w]);
 
   // candidates into LDS (as far as they fit), counted into the first-digit
-  // histogram when they reach T
+  // histogram when they reach T: each wave copies whole sub-lists, the
+  // first 64 entries of eight of them per round with all loads in flight
   RowLists rl{a.lists + (int64_t)row * a.n, sh.cache, 0u, sh.off, a.subs, a.sub_len};
   {
     const uint32_t cached = min(total, (uint32_t)kRefineCache);
-    constexpr int kBatch = 8;
-    for (uint32_t base = 0; base < total; base += kBatch * NT) {
-      uint2 e[kBatch];
+    constexpr int kWaves = NT / 64, kRound = 8;
+    auto take = [&](const uint2& e, uint32_t p) {
+      if (p < cached) sh.cache[p] = e;
+      if (e.x >= tmax) atomicAdd(&sh.h[e.x >> 21], 1u);
+    };
+    for (int s0 = wave; s0 < a.subs; s0 += kWaves * kRound) {
+      uint2 e[kRound];
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const uint32_t p = base + i * NT + threadIdx.x;
-        if (p < total) e[i] = rl.from_memory(p);
+      for (int k = 0; k < kRound; ++k) {
+        const int sl = s0 + k * kWaves;
+        if (sl < a.subs && (uint32_t)lane < sh.off[sl + 1] - sh.off[sl])
+          e[k] = rl.glob[(int64_t)sl * a.sub_len + lane];
       }
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const uint32_t p = base + i * NT + threadIdx.x;
-        if (p < total) {
-          if (p < cached) sh.cache[p] = e[i];
-          if (e[i].x >= tmax) atomicAdd(&sh.h[e[i].x >> 21], 1u);
-        }
+      for (int k = 0; k < kRound; ++k) {
+        const int sl = s0 + k * kWaves;
+        if (sl >= a.subs) continue;
+        const uint32_t o = sh.off[sl], c = sh.off[sl + 1] - o;
+        if ((uint32_t)lane < c) take(e[k], o + lane);
+        for (uint32_t i = lane + 64; i < c; i += 64) take(rl.glob[(int64_t)sl * a.sub_len + i], o + i);
       }
     }
     __syncthreads();
