@@ -44,6 +44,9 @@ def parse():
                     help="approximate budget of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-stage-timing", action="store_true")
+    ap.add_argument("--skip-prefill-hash", action="store_true",
+                    help="leave out the prefill-hash timing (8 KV heads x 131072 keys, "
+                         "L=64, P=8) reported beside the decode figure")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 4 times (reference for HBM "
                          "byte counters) and exit")
@@ -146,6 +149,40 @@ def cpu_baseline(w, budget_s):
                    f"oracle on one host thread, {elapsed:.1f} s timed (prefill "
                    f"hashing not timed)"),
     }
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_hash(S, W, torch, dev, reps=10):
+    """Mean time of socket_hash_keys on the prefill workload (all keys of 8
+    KV heads, inputs resident), as throughput against the dense bf16 MFMA
+    peak (2 * d * L * P flops per key) and HBM (K, V read; ids, norms
+    written)."""
+    w = W.WORKLOADS["prefill_hash_128k"]
+    K, V = W.make_keys_values(w, dev, seed=0)
+    R = W.make_hyperplanes(w, dev, seed=0)
+    K, V = K.reshape(-1, w.N, w.d), V.reshape(-1, w.N, w.d)
+    ids, vn = S.hash_keys(K, V, R, w.L, w.P)
+    S.hash_keys(K, V, R, w.L, w.P, ids=ids, vnorm=vn)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        S.hash_keys(K, V, R, w.L, w.P, ids=ids, vnorm=vn)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nk = K.shape[0] * w.N
+    flops = 2 * w.d * w.L * w.P * nk
+    hbm = 2 * nk * w.d * w.elem_bytes + nk * w.L + nk * 4
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"workload": w.name, "keys": nk, "L": w.L, "P": w.P, "us_per_call": round(ms * 1e3, 2),
+            "tflops": round(tflops, 1), "mfma_bf16_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+            "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "hbm_gbs": round(hbm / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(hbm / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def main():
@@ -285,6 +322,12 @@ def main():
             "avg_launch_ms": round(kernel_ms[dom], 5),
         }
 
+    # ---- prefill hashing (bf16 MFMA projections, fused sign packing and
+    # value norms) on its own workload, reported beside the decode figure
+    prefill = None
+    if not args.skip_prefill_hash:
+        prefill = prefill_hash(S, W, torch, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
@@ -311,6 +354,7 @@ def main():
         "algorithmic_bytes_per_step": step_bytes,
         "kernel_ms": {k: round(v, 5) for k, v in kernel_ms.items()},
         "roofline": roofline,
+        "prefill_hash": prefill,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),
     }

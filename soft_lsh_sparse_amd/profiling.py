@@ -40,7 +40,10 @@ CSRC = os.path.join(HERE, "csrc")
 KERNEL_SOURCES = {
     "hash_keys_bf16_kernel": ["hash_keys.hip"],
     "hash_keys_f32_kernel": ["hash_keys.hip"],
-    "bucket_probs_kernel": ["bucket_probs.hip", "soft_prob.hpp", "radix.hpp"],
+    "hash_prep_kernel": ["hash_keys.hip"],
+    "hash_fixup_kernel": ["hash_keys.hip"],
+    "hash_redo_kernel": ["hash_keys.hip"],
+    "bucket_probs_kernel": ["bucket_probs.hip", "soft_prob.hpp"],
     "score_kernel_rot": ["score.hip", "radix.hpp"],
     "score_kernel_generic": ["score.hip", "radix.hpp"],
     "zero_u32_kernel": ["topk.hip", "radix.hpp"],
@@ -138,7 +141,7 @@ def write_traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
     f_write = copy_bytes / (cw * 1024.0)
     kernels = {}
     for k in sorted(set(fetch) & set(write)):
-        if k == COPY_KERNEL:
+        if k == COPY_KERNEL or (k not in KERNEL_SOURCES and not k.startswith("score_kernel")):
             continue
         fk, nf = fetch[k]
         wk, nw = write[k]
