@@ -12,13 +12,13 @@
 //
 //  1. prep: R [d, C] is transposed to R^T [rows, d] (zero rows past C) in the
 //     workspace, and the fix-up counter is cleared.
-//  2. main: a persistent grid of one 8-wave block per CU. Every block walks
-//     32-key tiles; the K and V rows of the next seven tiles are in flight
-//     into an 8-slot LDS ring (128 KB) through direct-to-LDS loads
+//  2. main: a persistent grid of two 4-wave blocks per CU. Every block walks
+//     32-key tiles; the K and V rows of the next three tiles are in flight
+//     into a 4-slot LDS ring (64 KB per block) through direct-to-LDS loads
 //     (global_load_lds_dwordx4, no registers held), so each CU keeps about
 //     100 KB of loads in flight while it computes. The projection y = K R runs
 //     on the matrix cores (v_mfma_f32_32x32x16_bf16, float32 accumulation of
-//     the exact bf16 products): every wave keeps up to 64 hyperplane
+//     the exact bf16 products): every wave keeps up to 128 hyperplane
 //     columns of R^T in registers as the stationary A operand and reads the
 //     tile's K rows from LDS as the B operand (XOR-swizzled so the 8 lanes
 //     the LDS serves together hit 8 bank groups), so one lane ends with 16
