@@ -33,7 +33,8 @@
  *   - Supported sizes: d in {64, 128}; 1 <= P <= 8; 1 <= L and L*P <= 1024
  *     (L*P <= 512 for bf16 hashing); Hq a multiple of Hkv with
  *     G = Hq/Hkv in {1, 2, 4, 8}; the per-KV-head probability table
- *     2^P * L * G * 4 bytes must fit the 160 KB LDS of a CU; k >= 1;
+ *     2^P * L * G * 4 bytes plus G KB and 640 bytes must fit the 160 KB LDS
+ *     of a CU; k >= 1;
  *     head_stride_rows < 2^31 for decode (int32 key indices).
  *   - Unsupported but valid sizes return SOCKET_ERR_UNSUPPORTED.
  *
@@ -142,8 +143,10 @@ socket_status socket_bucket_probs(const void* Q, const void* R,
  *   ids     [B*Hkv, head_stride_rows, L] uint8
  *   vnorm   [B*Hkv, head_stride_rows] float32
  *   scores  [B, Hq, n_keys] float32 (output)
- * The L probabilities are summed in ascending table order in float32, then
- * multiplied by the value norm.
+ * The L probabilities are summed in float32 in the order l = (t + r) mod L,
+ * t = 0 .. L-1, where r = key index mod 8 when L is 16, 32 or 64 and the id
+ * rows are 16-byte aligned (this spreads LDS banks), else r = 0; the sum is
+ * then multiplied by the value norm.
  */
 socket_status socket_score(const float* table, const uint8_t* ids,
                            const float* vnorm, int32_t B, int32_t Hq,
@@ -202,9 +205,17 @@ socket_status socket_sparse_attn(const void* Q, const void* K, const void* V,
  *   out         [B, Hq, d] dtype (output)
  *   idx_out     [B, Hq, min(k, n_keys)] int32 (output) or NULL
  *   scores_out  [B, Hq, n_keys] float32 (output) or NULL
- * NULL optional outputs are kept in the workspace instead.
+ * A NULL idx_out keeps the indices in the workspace. Score rows are written
+ * only when scores_out is given (the selection itself keeps only the keys
+ * that reach a sampled per-block threshold, verifies that they contain the
+ * top k and otherwise scores the row in full); the indices are those of the
+ * exact top k of the rows socket_score would produce, ties to the lower
+ * index, in ascending order.
  * Workspace: socket_decode_workspace_bytes(...) bytes of device memory.
- * n_keys must be >= 1.
+ * n_keys must be >= 1. With k < n_keys the score kernel needs the table of
+ * one KV head plus 1 KB per query head of the group and 640 bytes within
+ * 160 KB of LDS, and n_keys <= 2^28 (at most 4096 candidate sub-lists per
+ * row); otherwise SOCKET_ERR_UNSUPPORTED.
  */
 size_t socket_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv,
                                      int32_t d, int64_t n_keys, int32_t L,
@@ -225,10 +236,10 @@ socket_status socket_decode(const void* Q, const void* K, const void* V,
  * events[2i] and events[2i+1] (hipEvent_t handles created by the caller) as
  * its start and stop events, which the dispatch records at the start and
  * end of that kernel's execution, for the first n_events / 2 kernels.
- * Kernel order: bucket table, scores, then the top-k kernels (clear +
- * histogram, unless the score kernel built the histogram itself, then
- * filter and refine; a single index fill when k >= n_keys), then the
- * attention gather and its merge. Unused events are not touched. For
+ * Kernel order with k < n_keys: bucket table, scores with candidate
+ * emission, selection, attention gather, attention merge. With k >= n_keys:
+ * (bucket table and scores only when scores_out is given) a single index
+ * fill, attention gather, attention merge. Unused events are not touched. For
  * profiling tools; events must not be NULL and n_events must be >= 2
  * (else SOCKET_ERR_INVALID_ARGUMENT).
  */
