@@ -131,10 +131,43 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan_dpp(uint32_t x) {
   return x;
 }
 
+// The value of lane i ^ 16 (v_permlane16_swap: rows of 16 lanes trade in
+// pairs).
+__device__ __forceinline__ uint32_t xor16_u32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return (threadIdx.x & 16) ? r[0] : r[1];
+}
+
 // The value of lane i ^ 32 (v_permlane32_swap: the two half-waves trade).
 __device__ __forceinline__ uint32_t xor32_u32(uint32_t v) {
   const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
   return (threadIdx.x & 32) ? r[0] : r[1];
+}
+
+// The value of lane i ^ O for O in {8, 16, 32}: permlane swaps for 16 and
+// 32 (VALU), a shuffle otherwise.
+template <int O>
+__device__ __forceinline__ float xor_lanes(float v) {
+  if constexpr (O == 16) return __uint_as_float(xor16_u32(__float_as_uint(v)));
+  else if constexpr (O == 32) return __uint_as_float(xor32_u32(__float_as_uint(v)));
+  else return __shfl_xor(v, O, kWave);
+}
+
+// Sum over each aligned group of W lanes (W in {8, 16, 32, 64}), in every
+// lane of the group, by DPP and permlane swaps.
+template <int W>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  if constexpr (W == 8) {
+    v += dpp_f32<0xB1>(v);
+    v += dpp_f32<0x4E>(v);
+    v += dpp_f32<0x141>(v);
+    return v;
+  } else {
+    v = sum16(v);
+    if constexpr (W >= 32) v += xor_lanes<16>(v);
+    if constexpr (W >= 64) v += xor_lanes<32>(v);
+    return v;
+  }
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {

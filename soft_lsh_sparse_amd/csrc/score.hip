@@ -144,9 +144,17 @@ __device__ __forceinline__ void stage_table(float* tab, const float* table, int 
                                             int L, int P) {
   const int tsize = (1 << P) * L * G;
   if (tsize % 4 == 0) {  // every head's table then starts 16-byte aligned
+    // direct-to-LDS loads: 64 lanes x 16 bytes per instruction into
+    // consecutive LDS, no registers held, all in flight at once
     const float4* src = reinterpret_cast<const float4*>(table + (int64_t)bg * tsize);
-    float4* dst = reinterpret_cast<float4*>(tab);
-    for (int i = threadIdx.x; i < tsize / 4; i += blockDim.x) dst[i] = src[i];
+    const int n4 = tsize / 4;
+    const int lane = threadIdx.x & 63;
+    for (int w0 = (int)(threadIdx.x & ~63); w0 < n4; w0 += (int)blockDim.x) {  // wave-uniform
+      if (w0 + lane < n4)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(src + w0 + lane),
+            (__attribute__((address_space(3))) void*)(tab + (size_t)w0 * 4), 16, 0, 0);
+    }
   } else {
     for (int i = threadIdx.x; i < tsize; i += blockDim.x)
       tab[i] = table[(int64_t)bg * tsize + i];

@@ -117,12 +117,15 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
     float dot = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], f[e], dot);
-    dot = group_sum<LPR>(dot);
+    dot = lane_group_sum<LPR>(dot);
     s[it] = valid[it] ? dot : -INFINITY;
     m = fmaxf(m, s[it]);
   }
-#pragma unroll
-  for (int o = LPR; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+  // the key groups of the wave hold different keys: combine across them
+  // (lane i with lane i ^ o keeps the position within the row)
+  if constexpr (LPR <= 8) m = fmaxf(m, xor_lanes<8>(m));
+  if constexpr (LPR <= 16) m = fmaxf(m, xor_lanes<16>(m));
+  if constexpr (LPR <= 32) m = fmaxf(m, xor_lanes<32>(m));
 
   float l = 0.f;
   float acc[EPL];
@@ -137,11 +140,20 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, f[e], acc[e]);
   }
+  if constexpr (LPR <= 8) {
+    l += xor_lanes<8>(l);
 #pragma unroll
-  for (int o = LPR; o < 64; o <<= 1) {
-    l += __shfl_xor(l, o, kWave);
+    for (int e = 0; e < EPL; ++e) acc[e] += xor_lanes<8>(acc[e]);
+  }
+  if constexpr (LPR <= 16) {
+    l += xor_lanes<16>(l);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
+    for (int e = 0; e < EPL; ++e) acc[e] += xor_lanes<16>(acc[e]);
+  }
+  if constexpr (LPR <= 32) {
+    l += xor_lanes<32>(l);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += xor_lanes<32>(acc[e]);
   }
   if (lane == 0) {
     sm_m[wave] = m;
