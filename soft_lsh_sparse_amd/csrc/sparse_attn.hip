@@ -32,6 +32,7 @@ namespace {
 
 constexpr int kAttnThreads = 256;
 constexpr int kAttnWaves = kAttnThreads / 64;
+constexpr int kAttnLoads = 8;  // 16-byte loads per lane, tensor and batch
 
 template <typename T>
 __device__ __forceinline__ void unpack16(const uint4& w, float* f);
@@ -54,7 +55,11 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
   constexpr int EPL = 16 / T::bytes;  // elements per 16-byte load
   constexpr int LPR = D / EPL;        // lanes per key row
   constexpr int KPI = 64 / LPR;       // key rows per wave-wide load
-  constexpr int IT = KPW / KPI;       // loads per wave per tensor
+  constexpr int IT = kAttnLoads;      // loads per tensor per batch
+  constexpr int KPB = IT * KPI;       // keys per batch
+  constexpr int NB = KPW / KPB;       // batches per wave
+  static_assert(NB * KPB == KPW && KPW % 64 == 0, "keys per wave");
+  constexpr int NREG = KPW / 64;
   constexpr int CHUNK = KPW * kAttnWaves;
   __shared__ float sm_m[kAttnWaves], sm_l[kAttnWaves];
   __shared__ float sm_acc[kAttnWaves][D];
@@ -74,6 +79,18 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
   const int grp = lane / LPR, sub = lane % LPR;
   const float scale = 1.0f / sqrtf((float)D);
 
+  // the wave's key indices, one position per lane and register; positions
+  // past kk repeat the last selected key (loaded, then given weight 0) and
+  // indices outside [0, stride) are clamped, so no load leaves the head
+  const int64_t wbeg = (int64_t)chunk * CHUNK + wave * KPW;
+  const int32_t* irow = idx + row * kk;
+  int ireg[NREG];
+#pragma unroll
+  for (int r = 0; r < NREG; ++r) {
+    const int64_t p = min<int64_t>(wbeg + r * 64 + lane, kk - 1);
+    ireg[r] = (int)min<int64_t>(max(irow[p], 0), stride - 1);
+  }
+
   float qf[EPL];
   {
     const uint4 w = *reinterpret_cast<const uint4*>(Q + row * D + sub * EPL);
@@ -82,63 +99,71 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
     for (int e = 0; e < EPL; ++e) qf[e] *= scale;
   }
 
-  const int64_t kbeg = (int64_t)chunk * CHUNK + wave * KPW;
-  const typename T::storage* Kh = K + (int64_t)gi * stride * D;
-  const typename T::storage* Vh = V + (int64_t)gi * stride * D;
-  const int32_t* irow = idx + row * kk;
+  const typename T::storage* Kh = K + (int64_t)gi * stride * D + sub * EPL;
+  const typename T::storage* Vh = V + (int64_t)gi * stride * D + sub * EPL;
 
-  int key[IT];
-  bool valid[IT];
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int64_t p = kbeg + it * KPI + grp;
-    valid[it] = p < kk;
-    // indices outside [0, stride) are clamped so no load leaves the head
-    key[it] = valid[it] ? (int)min<int64_t>(max(irow[p], 0), stride - 1) : 0;
-  }
-  uint4 kr[IT], vr[IT];
-#pragma unroll
-  for (int it = 0; it < IT; ++it)
-    kr[it] = valid[it] ? *reinterpret_cast<const uint4*>(
-                             Kh + (int64_t)key[it] * D + sub * EPL)
-                       : make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int it = 0; it < IT; ++it)
-    vr[it] = valid[it] ? *reinterpret_cast<const uint4*>(
-                             Vh + (int64_t)key[it] * D + sub * EPL)
-                       : make_uint4(0, 0, 0, 0);
-
-  float s[IT];
-  float m = -INFINITY;
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    float f[EPL];
-    unpack16<T>(kr[it], f);
-    float dot = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], f[e], dot);
-    dot = lane_group_sum<LPR>(dot);
-    s[it] = valid[it] ? dot : -INFINITY;
-    m = fmaxf(m, s[it]);
-  }
-  // the key groups of the wave hold different keys: combine across them
-  // (lane i with lane i ^ o keeps the position within the row)
-  if constexpr (LPR <= 8) m = fmaxf(m, xor_lanes<8>(m));
-  if constexpr (LPR <= 16) m = fmaxf(m, xor_lanes<16>(m));
-  if constexpr (LPR <= 32) m = fmaxf(m, xor_lanes<32>(m));
-
-  float l = 0.f;
+  // Batches of KPB keys, double-buffered: the loads of batch bt + 1 are in
+  // flight while batch bt is consumed. The running softmax (m, l, acc) is
+  // rescaled once per batch; m is the same in every lane of the wave.
+  uint4 kr[2][IT], vr[2][IT];
+  float m = -INFINITY, l = 0.f;
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+
+  auto issue = [&](int bt) {
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const float p = valid[it] ? __expf(s[it] - m) : 0.f;
-    l += p;
-    float f[EPL];
-    unpack16<T>(vr[it], f);
+    for (int it = 0; it < IT; ++it) {
+      const int p = bt * KPB + it * KPI + grp;  // position within the wave
+      const int key = __shfl(ireg[p >> 6], p & 63, kWave);
+      kr[bt & 1][it] = *reinterpret_cast<const uint4*>(Kh + (int64_t)key * D);
+    }
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, f[e], acc[e]);
+    for (int it = 0; it < IT; ++it) {
+      const int p = bt * KPB + it * KPI + grp;
+      const int key = __shfl(ireg[p >> 6], p & 63, kWave);
+      vr[bt & 1][it] = *reinterpret_cast<const uint4*>(Vh + (int64_t)key * D);
+    }
+  };
+
+  issue(0);
+#pragma unroll
+  for (int bt = 0; bt < NB; ++bt) {
+    if (bt + 1 < NB) issue(bt + 1);
+    float s[IT];
+    float mb = -INFINITY;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      float f[EPL];
+      unpack16<T>(kr[bt & 1][it], f);
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], f[e], dot);
+      dot = lane_group_sum<LPR>(dot);
+      const bool valid = wbeg + bt * KPB + it * KPI + grp < kk;
+      s[it] = valid ? dot : -INFINITY;
+      mb = fmaxf(mb, s[it]);
+    }
+    // the key groups of the wave hold different keys: combine across them
+    // (lane i with lane i ^ o keeps the position within the row)
+    if constexpr (LPR <= 8) mb = fmaxf(mb, xor_lanes<8>(mb));
+    if constexpr (LPR <= 16) mb = fmaxf(mb, xor_lanes<16>(mb));
+    if constexpr (LPR <= 32) mb = fmaxf(mb, xor_lanes<32>(mb));
+    const float mn = fmaxf(m, mb);
+    const float c = m == -INFINITY ? 0.f : __expf(m - mn);
+    l *= c;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= c;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const float p = s[it] == -INFINITY ? 0.f : __expf(s[it] - mn);
+      l += p;
+      float f[EPL];
+      unpack16<T>(vr[bt & 1][it], f);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, f[e], acc[e]);
+    }
+    m = mn;
   }
   if constexpr (LPR <= 8) {
     l += xor_lanes<8>(l);
@@ -250,12 +275,12 @@ hipError_t launch_attn_d(const void* Q, const void* K, const void* V,
                          const int32_t* idx, void* out, float* partial,
                          hipStream_t stream) {
   switch (plan.keys_per_wave) {
-    case 64:
-      return launch_attn_t<T, D, 64>(Q, K, V, plan, stride, idx, out, partial, stream);
-    case 32:
-      return launch_attn_t<T, D, 32>(Q, K, V, plan, stride, idx, out, partial, stream);
+    case 256:
+      return launch_attn_t<T, D, 256>(Q, K, V, plan, stride, idx, out, partial, stream);
+    case 128:
+      return launch_attn_t<T, D, 128>(Q, K, V, plan, stride, idx, out, partial, stream);
     default:
-      return launch_attn_t<T, D, 16>(Q, K, V, plan, stride, idx, out, partial, stream);
+      return launch_attn_t<T, D, 64>(Q, K, V, plan, stride, idx, out, partial, stream);
   }
 }
 
@@ -269,10 +294,11 @@ AttnPlan plan_attn(int B, int Hq, int Hkv, int d, int64_t kk) {
   p.d = d;
   p.kk = kk;
   const int64_t rows = (int64_t)B * Hq;
-  int kpw = 16;
-  for (int cand : {64, 32}) {
+  // the most keys per wave that still give 512 blocks (two per CU)
+  int kpw = 64;
+  for (int cand : {256, 128}) {
     const int64_t chunks = (kk + cand * kAttnWaves - 1) / (cand * kAttnWaves);
-    if (rows * chunks >= 1024) {
+    if (rows * chunks >= 512) {
       kpw = cand;
       break;
     }
