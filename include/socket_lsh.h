@@ -33,8 +33,8 @@
  *   - Supported sizes: d in {64, 128}; 1 <= P <= 8; 1 <= L and L*P <= 1024
  *     (L*P <= 512 for bf16 hashing); Hq a multiple of Hkv with
  *     G = Hq/Hkv in {1, 2, 4, 8}; the per-KV-head probability table
- *     2^P * L * G * 4 bytes plus G KB and 640 bytes must fit the 160 KB LDS
- *     of a CU; k >= 1;
+ *     2^P * L * G * 4 bytes plus 2 KB per query head of the group must fit
+ *     the 160 KB LDS of a CU; k >= 1;
  *     head_stride_rows < 2^31 for decode (int32 key indices).
  *   - Unsupported but valid sizes return SOCKET_ERR_UNSUPPORTED.
  *
@@ -213,9 +213,9 @@ socket_status socket_sparse_attn(const void* Q, const void* K, const void* V,
  * index, in ascending order.
  * Workspace: socket_decode_workspace_bytes(...) bytes of device memory.
  * n_keys must be >= 1. With k < n_keys the score kernel needs the table of
- * one KV head plus 1 KB per query head of the group and 640 bytes within
- * 160 KB of LDS, and n_keys <= 2^28 (at most 4096 candidate sub-lists per
- * row); otherwise SOCKET_ERR_UNSUPPORTED.
+ * one KV head plus 2 KB per query head of the group within 160 KB of LDS,
+ * and n_keys <= 2^28 (at most 4096 candidate sub-lists per row); otherwise
+ * SOCKET_ERR_UNSUPPORTED.
  */
 size_t socket_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv,
                                      int32_t d, int64_t n_keys, int32_t L,

@@ -60,13 +60,9 @@ constexpr int kPrefetch = 2;
 constexpr int kWaveStep = 64 * kPrefetch;
 // keeps every per-thread byte offset of a segment (key * L, L <= 1024) in 31 bits
 constexpr int64_t kMaxSeg = 1 << 20;
-// block thresholds: 256 bins per query row and pass, 1/16 of an octave of
-// the score (2^19 units of the order key) below the row's largest sampled
-// score in the first pass, 2^11 units in the second
+// block thresholds: 256 bins per query row and pass (bits 24..31 of the
+// order key, then bits 16..23)
 constexpr int kThrBins = 256;
-constexpr int kThrShift1 = 19;
-constexpr int kThrShift2 = 11;
-constexpr int kScratchWords = 160;  // >= 16 * G + G
 
 // v_cndmask_b32 with an explicit lane mask: b where the lane's mask bit is
 // set, a elsewhere. Written out so the compiler keeps one select per word
@@ -138,10 +134,12 @@ __device__ __forceinline__ bool score_block_coords(int bhkv, int segs, int& bg,
   return true;
 }
 
-// The table of batch*KV head bg into LDS.
+// The table of batch*KV head bg into LDS. The blocks of one head run on
+// one XCD and read the same table: each starts at its own round of 16 KB
+// (start_round) so that they do not all ask the same L2 lines at once.
 template <int G>
 __device__ __forceinline__ void stage_table(float* tab, const float* table, int bg,
-                                            int L, int P) {
+                                            int L, int P, int start_round) {
   const int tsize = (1 << P) * L * G;
   if (tsize % 4 == 0) {  // every head's table then starts 16-byte aligned
     // direct-to-LDS loads: 64 lanes x 16 bytes per instruction into
@@ -149,8 +147,13 @@ __device__ __forceinline__ void stage_table(float* tab, const float* table, int 
     const float4* src = reinterpret_cast<const float4*>(table + (int64_t)bg * tsize);
     const int n4 = tsize / 4;
     const int lane = threadIdx.x & 63;
-    for (int w0 = (int)(threadIdx.x & ~63); w0 < n4; w0 += (int)blockDim.x) {  // wave-uniform
-      if (w0 + lane < n4)
+    const int per_round = (int)blockDim.x;
+    const int rounds = (n4 + per_round - 1) / per_round;
+    const int first = start_round % rounds;
+    for (int k = 0; k < rounds; ++k) {
+      const int rr = k + first < rounds ? k + first : k + first - rounds;
+      const int w0 = rr * per_round + (int)(threadIdx.x & ~63);  // wave-uniform
+      if (w0 < n4 && w0 + lane < n4)
         __builtin_amdgcn_global_load_lds(
             (const void*)(src + w0 + lane),
             (__attribute__((address_space(3))) void*)(tab + (size_t)w0 * 4), 16, 0, 0);
@@ -235,100 +238,71 @@ __device__ inline uint32_t threshold_rank(int64_t kk, int64_t n, int n_b) {
 }
 
 // Per query row j of the group: an order key that at least m of the sampled
-// order keys uk[q][j] (valid[q]) reach, and few more. With M the row's
-// largest, D = M - u; the first pass counts D >> 19 in 256 bins (16
-// octaves; farther keys are not counted) and finds the first bin b1 at
-// which the count from bin 0 reaches m; the second counts (D >> 11) & 255
-// of the keys in b1 and finds b2 the same way. The threshold is the lowest
-// key of sub-bin (b1, b2), or 0 when the bins hold fewer than m keys. One
-// wave searches each row's bins (DPP scans).
+// order keys uk[q][j] (valid[q]) reach, and few more. The first pass counts
+// the keys by their top 8 bits (sign and 7 exponent bits: bins of two
+// octaves) and finds, from the top, the bin b1 at which the count reaches
+// m; the second counts bits 16..23 of the keys in b1 (bins of 1/128 of an
+// octave) and finds b2 the same way. The threshold is the lowest key of
+// (b1, b2), or 0 when fewer than m keys are valid. Every wave scans every
+// row's bins itself (4 bins per lane, DPP prefix sums), so the two passes
+// need two block barriers. hist: 2 * G * kThrBins counters, zero on entry.
 template <int G>
-__device__ void block_thresholds(const uint32_t (&uk)[kPrefetch][G],
-                                 const bool (&valid)[kPrefetch], uint32_t m, uint32_t* hist,
-                                 uint32_t* scratch, uint32_t (&thr)[G]) {
-  uint32_t* wmax = scratch;              // [16][G] wave maxima
-  uint32_t* res = scratch + 16 * G;      // [G][2] chosen bin (or kThrBins), count before it
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // row maxima
-  uint32_t mx[G];
+__device__ __forceinline__ void block_thresholds(const uint32_t (&uk)[kPrefetch][G],
+                                                 const bool (&valid)[kPrefetch], uint32_t m,
+                                                 uint32_t* hist, uint32_t (&thr)[G]) {
+  static_assert(kThrBins == 4 * 64, "four bins per lane");
+  const int lane = threadIdx.x & 63;
+  uint32_t* h1 = hist;                  // [G][256] by bits 24..31
+  uint32_t* h2 = hist + G * kThrBins;   // [G][256] by bits 16..23 within b1
+#pragma unroll
+  for (int q = 0; q < kPrefetch; ++q)
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      if (valid[q]) atomicAdd(&h1[j * kThrBins + (uk[q][j] >> 24)], 1u);
+  __syncthreads();
+  // bin (from the top) at which the running count reaches need; lane 0
+  // holds the 4 highest bins. Returns kThrBins when the bins hold fewer.
+  auto find = [&](const uint32_t* hr, uint32_t need, uint32_t& before) {
+    const uint4 c4 = *reinterpret_cast<const uint4*>(hr + kThrBins - 4 - 4 * lane);
+    const uint32_t cs[4] = {c4.w, c4.z, c4.y, c4.x};  // descending bins
+    const uint32_t sum = c4.x + c4.y + c4.z + c4.w;
+    uint32_t run = wave_inclusive_scan_dpp(sum) - sum;
+    uint32_t bin = kThrBins, bef = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (run < need && run + cs[i] >= need) {
+        bin = (uint32_t)(kThrBins - 1 - 4 * lane - i);
+        bef = run;
+      }
+      run += cs[i];
+    }
+    const uint64_t hit = __ballot(bin != kThrBins);
+    if (hit == 0) return (uint32_t)kThrBins;
+    const int src = __ffsll((unsigned long long)hit) - 1;
+    before = (uint32_t)__shfl((int)bef, src, 64);
+    return (uint32_t)__shfl((int)bin, src, 64);
+  };
+  uint32_t b1[G], need2[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    uint32_t v = 0u;
-#pragma unroll
-    for (int q = 0; q < kPrefetch; ++q) v = max(v, valid[q] ? uk[q][j] : 0u);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-    mx[j] = v;
+    uint32_t before = 0u;
+    b1[j] = find(h1 + j * kThrBins, m, before);
+    need2[j] = m - before;
   }
-  if (lane == 0) {
 #pragma unroll
-    for (int j = 0; j < G; ++j) wmax[wave * G + j] = mx[j];
-  }
+  for (int q = 0; q < kPrefetch; ++q)
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      if (valid[q] && b1[j] < kThrBins && (uk[q][j] >> 24) == b1[j])
+        atomicAdd(&h2[j * kThrBins + ((uk[q][j] >> 16) & 255u)], 1u);
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    uint32_t v = 0u;
-    for (int w = 0; w < kScoreWaves; ++w) v = max(v, wmax[w * G + j]);
-    mx[j] = v;
-  }
-  uint32_t b1[G];
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    __syncthreads();  // wmax / res of the previous step read by every thread
-    for (int i = threadIdx.x; i < G * kThrBins; i += kScoreThreads) hist[i] = 0u;
-    if (threadIdx.x < G) res[2 * threadIdx.x] = kThrBins;
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < kPrefetch; ++q) {
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const uint32_t dist = mx[j] - uk[q][j];
-        uint32_t bin;
-        bool in = valid[q];
-        if (pass == 0) {
-          bin = dist >> kThrShift1;
-          in = in && bin < kThrBins;
-        } else {
-          bin = (dist >> kThrShift2) & (kThrBins - 1);
-          in = in && b1[j] < kThrBins && (dist >> kThrShift1) == b1[j];
-        }
-        if (in) atomicAdd(&hist[j * kThrBins + bin], 1u);
-      }
-    }
-    __syncthreads();
-    // wave j scans row j's bins: 4 consecutive bins per lane, DPP prefix
-    // sums over the lanes
-    static_assert(kThrBins == 4 * 64, "four bins per lane");
-    if (wave < G) {
-      const uint32_t* hr = hist + wave * kThrBins + lane * 4;
-      const uint32_t c0 = hr[0], c1 = hr[1], c2 = hr[2], c3 = hr[3];
-      const uint32_t sum = c0 + c1 + c2 + c3;
-      const uint32_t before = (pass == 0 ? 0u : res[2 * wave + 1]) +
-                              wave_inclusive_scan_dpp(sum) - sum;
-      const uint32_t cs[4] = {c0, c1, c2, c3};
-      uint32_t run = before;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (run < m && run + cs[i] >= m) {
-          res[2 * wave] = (uint32_t)(lane * 4 + i);
-          if (pass == 0) res[2 * wave + 1] = run;
-        }
-        run += cs[i];
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      if (pass == 0) {
-        b1[j] = res[2 * j];
-
-      } else if (b1[j] < kThrBins) {
-        const uint32_t b2 = res[2 * j];  // always found: bin b1 holds the m-th key
-        const uint32_t low = (b1[j] << kThrShift1) + ((b2 + 1) << kThrShift2);  // D below
-        thr[j] = mx[j] < low ? 0u : mx[j] - low + 1u;
-      } else {
-        thr[j] = 0u;
-      }
+    thr[j] = 0u;
+    if (b1[j] < kThrBins) {
+      uint32_t before = 0u;
+      const uint32_t b2 = find(h2 + j * kThrBins, need2[j], before);  // found: b1 holds the m-th
+      thr[j] = (b1[j] << 24) | (b2 << 16);
     }
   }
 }
@@ -343,12 +317,13 @@ __device__ void score_block(const ScoreArgs& a, int bg, int seg, float* tab, Sco
   const int lane = threadIdx.x & 63;
   uint32_t* hist = reinterpret_cast<uint32_t*>(reinterpret_cast<unsigned char*>(tab) +
                                                score_table_region(a.L, a.P, G));
-  uint32_t* scratch = hist + G * kThrBins;
   float* sseg = a.scores ? a.scores + ((int64_t)b * a.Hq + (int64_t)g * G) * a.n_keys + wr.n0
                          : nullptr;
 
   sc.prefetch();
-  stage_table<G>(tab, a.table, bg, a.L, a.P);
+  stage_table<G>(tab, a.table, bg, a.L, a.P, seg);
+  if (a.select)
+    for (int i = threadIdx.x; i < 2 * G * kThrBins; i += kScoreThreads) hist[i] = 0u;
   __syncthreads();
 
   // first step of every wave: scored, then (decode) the block thresholds
@@ -376,7 +351,7 @@ __device__ void score_block(const ScoreArgs& a, int bg, int seg, float* tab, Sco
       for (int q = 0; q < kPrefetch; ++q)
 #pragma unroll
         for (int j = 0; j < G; ++j) uk[q][j] = float_order_key(vn[q] * acc[q][j]);
-      block_thresholds<G>(uk, valid, m, hist, scratch, thr);
+      block_thresholds<G>(uk, valid, m, hist, thr);
     }
 #pragma unroll
     for (int j = 0; j < G; ++j) {
@@ -612,8 +587,7 @@ ScoreArgs base_args(const float* table, const uint8_t* ids, const float* vnorm, 
 }  // namespace
 
 size_t score_lds_bytes(int L, int P, int G) {
-  return score_table_region(L, P, G) +
-         ((size_t)G * kThrBins + kScratchWords) * sizeof(uint32_t);
+  return score_table_region(L, P, G) + (size_t)2 * G * kThrBins * sizeof(uint32_t);
 }
 
 bool score_rotated(const uint8_t* ids, int64_t stride, int L) {
