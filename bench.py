@@ -63,28 +63,31 @@ def algorithmic_bytes(w):
     return keys * w.L + keys * 4 + rows * w.kk * 2 * w.d * e + 2 * rows * w.d * e
 
 
-def decode_kernel_names(w):
-    """Kernels socket_decode enqueues for this workload, in order (no score
-    rows are requested: with kk < N the score kernel emits candidates for
-    the select kernel; with kk = N every key is selected and nothing is
-    scored)."""
-    if w.kk >= w.N:
-        return ["iota_rows_kernel", "sparse_attn_kernel", "attn_merge_kernel"]
-    return ["bucket_probs_kernel", "score_kernel", "topk_select_kernel", "sparse_attn_kernel",
-            "attn_merge_kernel"]
+def decode_kernel_names(lib, w, ids, dt_code):
+    """Kernels socket_decode enqueues for this workload, in order, as the
+    library reports them (no score rows are requested)."""
+    buf = ctypes.create_string_buffer(512)
+    n = lib.socket_decode_kernels(ids.data_ptr(), dt_code, w.B, w.Hq, w.Hkv, w.d, w.N, w.N,
+                                  w.L, w.P, w.k, 0, buf, len(buf))
+    if n < 1:
+        raise RuntimeError(f"socket_decode_kernels failed ({n})")
+    return buf.value.decode().split(",")
 
 
-def kernel_bytes(w):
-    """Compulsory HBM bytes of one launch of each decode kernel."""
+def kernel_bytes(w, names):
+    """Compulsory HBM bytes of one launch of each decode kernel (the score
+    kernel reads the table from the table kernel, or builds it from the
+    queries and hyperplanes when no table kernel runs)."""
     e = w.elem_bytes
     rows = w.B * w.Hq
     keys = w.B * w.Hkv * w.N
     kk = w.kk
     table = w.B * w.Hkv * (2 ** w.P) * w.L * w.G * 4
+    table_in = table if "bucket_probs_kernel" in names else rows * w.d * e + w.d * w.C * e
     partial = 0  # intermediates between two kernels are not counted
     return {
         "bucket_probs_kernel": rows * w.d * e + w.d * w.C * e + table,
-        "score_kernel": keys * w.L + keys * 4 + table,
+        "score_kernel": keys * w.L + keys * 4 + table_in,
         "topk_select_kernel": rows * kk * 4,
         "iota_rows_kernel": rows * kk * 4,
         "sparse_attn_kernel": rows * kk * (2 * w.d * e + 4) + rows * w.d * e + partial,
@@ -278,7 +281,7 @@ def main():
     kernel_ms = {}
     roofline = None
     if not args.skip_stage_timing:
-        names = decode_kernel_names(w)
+        names = decode_kernel_names(lib, w, layers[0][3], dt_code)
         hip = _hip_runtime()
         n_ev = 2 * len(names)
         events = [[_hip_event(hip) for _ in range(n_ev)] for _ in range(args.steps)]
@@ -303,7 +306,7 @@ def main():
         for ev in events:
             for e in ev:
                 hip.hipEventDestroy(ctypes.c_void_p(e))
-        kbytes = kernel_bytes(w)
+        kbytes = kernel_bytes(w, names)
         dom = max(kernel_ms, key=kernel_ms.get)
         # HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE
         # summary of this workload; None once the kernel's sources changed

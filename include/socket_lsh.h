@@ -236,12 +236,9 @@ socket_status socket_decode(const void* Q, const void* K, const void* V,
  * events[2i] and events[2i+1] (hipEvent_t handles created by the caller) as
  * its start and stop events, which the dispatch records at the start and
  * end of that kernel's execution, for the first n_events / 2 kernels.
- * Kernel order with k < n_keys: bucket table, scores with candidate
- * emission, selection, attention gather, attention merge. With k >= n_keys:
- * (bucket table and scores only when scores_out is given) a single index
- * fill, attention gather, attention merge. Unused events are not touched. For
- * profiling tools; events must not be NULL and n_events must be >= 2
- * (else SOCKET_ERR_INVALID_ARGUMENT).
+ * socket_decode_kernels names the kernels in this order. Unused events are
+ * not touched. For profiling tools; events must not be NULL and n_events
+ * must be >= 2 (else SOCKET_ERR_INVALID_ARGUMENT).
  */
 socket_status socket_decode_profiled(
     const void* Q, const void* K, const void* V, const void* R,
@@ -251,6 +248,26 @@ socket_status socket_decode_profiled(
     void* out, int32_t* idx_out, float* scores_out, void* workspace,
     size_t workspace_bytes, void* stream, void* const* events,
     int32_t n_events);
+
+/*
+ * The kernels socket_decode enqueues for these arguments, in launch order.
+ * Host-only (no device work). With k < n_keys: the bucket table kernel
+ * (only when the score kernel cannot build the tables itself, which it does
+ * for bf16, P = 8, d in {64, 128}, L in {16, 32, 64}, 16-byte aligned id
+ * rows and a table plus 16*P*L*G bytes of build state within the LDS), the
+ * score kernel with candidate emission, the selection, the attention gather
+ * and merge. With k >= n_keys: (table and score kernels only when
+ * with_scores is nonzero) an index fill, the attention gather and merge.
+ *   names  NULL, or cap bytes receiving the kernels' base names separated
+ *          by commas, NUL-terminated
+ * Returns the number of kernels; -1 for arguments socket_decode rejects
+ * (socket_last_error() says why); -2 when the names do not fit in cap.
+ */
+int32_t socket_decode_kernels(const uint8_t* ids, socket_dtype dtype, int32_t B,
+                              int32_t Hq, int32_t Hkv, int32_t d,
+                              int64_t n_keys, int64_t head_stride_rows,
+                              int32_t L, int32_t P, int64_t k,
+                              int32_t with_scores, char* names, size_t cap);
 
 #ifdef __cplusplus
 }

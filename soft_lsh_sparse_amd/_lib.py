@@ -60,6 +60,9 @@ SIGNATURES = {
 }
 SIGNATURES["socket_decode_profiled"] = (
     c_int, SIGNATURES["socket_decode"][1] + [c_void_p, c_int32])
+SIGNATURES["socket_decode_kernels"] = (
+    c_int32, [c_void_p, c_int, c_int32, c_int32, c_int32, c_int32, c_int64, c_int64,
+              c_int32, c_int32, c_int64, c_int32, c_char_p, c_size_t])
 
 _lock = threading.Lock()
 _lib = None

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <string>
 
 #include "kernels.hpp"
@@ -76,7 +77,7 @@ socket_status check_heads(int32_t B, int32_t Hq, int32_t Hkv) {
 }
 
 socket_status check_table(int32_t L, int32_t P, int32_t G) {
-  const size_t bytes = score_lds_bytes(L, P, G);
+  const size_t bytes = score_lds_bytes(L, P, G, false);
   if (bytes > kLdsBytesPerCU)
     return fail(SOCKET_ERR_UNSUPPORTED,
                 "probability table of one KV head (2^P*L*G*4 bytes) with the score "
@@ -238,7 +239,7 @@ socket_status socket_score(const float* table, const uint8_t* ids,
   if (!aligned16(table))
     return fail(SOCKET_ERR_INVALID_ARGUMENT, "table must be 16-byte aligned");
   hipError_t err = launch_score(table, ids, vnorm, B, Hq, Hkv, n_keys,
-                                head_stride_rows, L, P, scores,
+                                head_stride_rows, L, P, scores, nullptr,
                                 static_cast<hipStream_t>(stream));
   return from_hip(err, "socket_score launch");
 }
@@ -319,22 +320,15 @@ size_t socket_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv,
 
 namespace {
 
-socket_status decode_impl(const void* Q, const void* K, const void* V,
-                          const void* R, const uint8_t* ids,
-                          const float* vnorm, socket_dtype dtype, int32_t B,
-                          int32_t Hq, int32_t Hkv, int32_t d, int64_t n_keys,
-                          int64_t head_stride_rows, int32_t L, int32_t P,
-                          float tau, int64_t k, void* out, int32_t* idx_out,
-                          float* scores_out, void* workspace,
-                          size_t workspace_bytes, void* stream,
-                          void* const* events, int32_t n_events) {
+// Shapes and sizes socket_decode accepts (pointers and tau aside).
+socket_status check_decode(socket_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                           int64_t n_keys, int64_t head_stride_rows, int32_t L, int32_t P,
+                           int64_t k) {
   SOCKET_TRY(check_dtype(dtype));
   SOCKET_TRY(check_heads(B, Hq, Hkv));
   SOCKET_TRY(check_d(d));
   SOCKET_TRY(check_lp(L, P));
   SOCKET_TRY(check_table(L, P, Hq / Hkv));
-  if (!(std::isfinite(tau) && tau > 0.f))
-    return fail(SOCKET_ERR_INVALID_ARGUMENT, "tau must be finite and > 0");
   if (k < 1) return fail(SOCKET_ERR_INVALID_ARGUMENT, "k must be >= 1");
   if (n_keys < 1) return fail(SOCKET_ERR_INVALID_ARGUMENT, "n_keys must be >= 1");
   if ((k < n_keys ? k : n_keys) > kMaxSelected)
@@ -345,14 +339,30 @@ socket_status decode_impl(const void* Q, const void* K, const void* V,
                 (long long)head_stride_rows, (long long)n_keys);
   if (head_stride_rows >= ((int64_t)1 << 31))
     return fail(SOCKET_ERR_UNSUPPORTED, "head_stride_rows must be < 2^31");
+  const ScoreGeom geo = plan_score(B * Hkv, n_keys, L, P, Hq / Hkv);
+  if (k < n_keys && geo.subs > kMaxSelectSubLists)
+    return fail(SOCKET_ERR_UNSUPPORTED, "n_keys=%lld needs %d candidate sub-lists per row "
+                "(at most %d)", (long long)n_keys, geo.subs, kMaxSelectSubLists);
+  return SOCKET_OK;
+}
+
+socket_status decode_impl(const void* Q, const void* K, const void* V,
+                          const void* R, const uint8_t* ids,
+                          const float* vnorm, socket_dtype dtype, int32_t B,
+                          int32_t Hq, int32_t Hkv, int32_t d, int64_t n_keys,
+                          int64_t head_stride_rows, int32_t L, int32_t P,
+                          float tau, int64_t k, void* out, int32_t* idx_out,
+                          float* scores_out, void* workspace,
+                          size_t workspace_bytes, void* stream,
+                          void* const* events, int32_t n_events) {
+  SOCKET_TRY(check_decode(dtype, B, Hq, Hkv, d, n_keys, head_stride_rows, L, P, k));
+  if (!(std::isfinite(tau) && tau > 0.f))
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "tau must be finite and > 0");
   if (!Q || !K || !V || !R || !ids || !vnorm || !out)
     return fail(SOCKET_ERR_INVALID_ARGUMENT, "null pointer argument");
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(R))
     return fail(SOCKET_ERR_INVALID_ARGUMENT, "Q, K, V and R must be 16-byte aligned");
   const DecodeLayout lay = decode_layout(B, Hq, Hkv, d, n_keys, L, P, k);
-  if (k < n_keys && lay.score.subs > kMaxSelectSubLists)
-    return fail(SOCKET_ERR_UNSUPPORTED, "n_keys=%lld needs %d candidate sub-lists per row "
-                "(at most %d)", (long long)n_keys, lay.score.subs, kMaxSelectSubLists);
   if (!workspace || workspace_bytes < lay.total)
     return fail(SOCKET_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu",
                 lay.total, workspace ? workspace_bytes : (size_t)0);
@@ -377,14 +387,19 @@ socket_status decode_impl(const void* Q, const void* K, const void* V,
   // (from the candidates, or from the full row).
   const int rows = B * Hq;
   const int64_t kk = k < n_keys ? k : n_keys;
+  // the score kernel builds the tables itself where it can (no table kernel)
+  const bool build = score_builds_table(bf16, d, ids, head_stride_rows, L, P, Hq / Hkv);
+  const TableBuild tb{Q, R, d, tau};
   hipError_t err;
   if (kk < n_keys) {
     uint32_t* thr = reinterpret_cast<uint32_t*>(ws + lay.thr_off);
     uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + lay.cnt_off);
     uint2* lists = reinterpret_cast<uint2*>(ws + lay.list_off);
     float* rowbuf = scores_out ? scores_out : reinterpret_cast<float*>(ws + lay.scores_off);
-    err = launch_bucket_probs(Q, R, bf16, B, Hq, Hkv, d, L, P, tau, table, s);
-    if (err != hipSuccess) return from_hip(err, "socket_decode: bucket_probs");
+    if (!build) {
+      err = launch_bucket_probs(Q, R, bf16, B, Hq, Hkv, d, L, P, tau, table, s);
+      if (err != hipSuccess) return from_hip(err, "socket_decode: bucket_probs");
+    }
     ScoreSelect sel{};
     sel.table = table;
     sel.ids = ids;
@@ -393,7 +408,8 @@ socket_status decode_impl(const void* Q, const void* K, const void* V,
     sel.thr = thr;
     sel.lists = lists;
     sel.sub_cnt = cnt;
-    err = launch_score_select(sel, B, Hq, Hkv, n_keys, head_stride_rows, L, P, scores_out, s);
+    err = launch_score_select(sel, B, Hq, Hkv, n_keys, head_stride_rows, L, P, scores_out,
+                              build ? &tb : nullptr, s);
     if (err != hipSuccess) return from_hip(err, "socket_decode: score");
     SelectArgs sa{};
     sa.n = n_keys;
@@ -419,10 +435,12 @@ socket_status decode_impl(const void* Q, const void* K, const void* V,
     if (err != hipSuccess) return from_hip(err, "socket_decode: topk");
   } else {
     if (scores_out) {
-      err = launch_bucket_probs(Q, R, bf16, B, Hq, Hkv, d, L, P, tau, table, s);
-      if (err != hipSuccess) return from_hip(err, "socket_decode: bucket_probs");
+      if (!build) {
+        err = launch_bucket_probs(Q, R, bf16, B, Hq, Hkv, d, L, P, tau, table, s);
+        if (err != hipSuccess) return from_hip(err, "socket_decode: bucket_probs");
+      }
       err = launch_score(table, ids, vnorm, B, Hq, Hkv, n_keys, head_stride_rows, L, P,
-                         scores_out, s);
+                         scores_out, build ? &tb : nullptr, s);
       if (err != hipSuccess) return from_hip(err, "socket_decode: score");
     }
     err = launch_iota_rows(idx, rows, n_keys, s);
@@ -464,6 +482,43 @@ socket_status socket_decode_profiled(
   return decode_impl(Q, K, V, R, ids, vnorm, dtype, B, Hq, Hkv, d, n_keys,
                      head_stride_rows, L, P, tau, k, out, idx_out, scores_out,
                      workspace, workspace_bytes, stream, events, n_events);
+}
+
+int32_t socket_decode_kernels(const uint8_t* ids, socket_dtype dtype, int32_t B,
+                              int32_t Hq, int32_t Hkv, int32_t d,
+                              int64_t n_keys, int64_t head_stride_rows,
+                              int32_t L, int32_t P, int64_t k,
+                              int32_t with_scores, char* names, size_t cap) {
+  if (check_decode(dtype, B, Hq, Hkv, d, n_keys, head_stride_rows, L, P, k) != SOCKET_OK)
+    return -1;
+  const bool build = score_builds_table(dtype == SOCKET_DTYPE_BF16, d, ids, head_stride_rows,
+                                        L, P, Hq / Hkv);
+  // the launch sequence of decode_impl
+  const char* seq[6];
+  int n = 0;
+  if (k < n_keys) {
+    if (!build) seq[n++] = "bucket_probs_kernel";
+    seq[n++] = "score_kernel";
+    seq[n++] = "topk_select_kernel";
+  } else {
+    if (with_scores) {
+      if (!build) seq[n++] = "bucket_probs_kernel";
+      seq[n++] = "score_kernel";
+    }
+    seq[n++] = "iota_rows_kernel";
+  }
+  seq[n++] = "sparse_attn_kernel";
+  seq[n++] = "attn_merge_kernel";
+  if (names) {
+    std::string joined;
+    for (int i = 0; i < n; ++i) {
+      if (i) joined += ',';
+      joined += seq[i];
+    }
+    if (joined.size() + 1 > cap) return -2;
+    std::memcpy(names, joined.c_str(), joined.size() + 1);
+  }
+  return n;
 }
 
 }  // extern "C"

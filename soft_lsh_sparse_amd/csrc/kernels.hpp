@@ -72,20 +72,34 @@ ScoreGeom plan_score(int bhkv, int64_t n_keys, int L, int P, int G);
 // true when the kernel sums each key's tables in the rotated order
 // l = (t + key) mod L, t = 0..L-1 (with key taken mod 8); else l = t
 bool score_rotated(const uint8_t* ids, int64_t stride, int L);
-// LDS bytes of one score block.
-size_t score_lds_bytes(int L, int P, int G);
+// LDS bytes of one score block (build: the block builds its table).
+size_t score_lds_bytes(int L, int P, int G, bool build);
 constexpr size_t kLdsBytesPerCU = 160 * 1024;
-// table: [B*Hkv, 2^P, L, G] from launch_bucket_probs; scores [B*Hq, n_keys].
+// The score kernel builds each head's table itself (no table kernel) for
+// bf16 queries and hyperplanes, P = 8, d in {64, 128}, the rotated path and
+// a table plus build within the LDS of a CU; the table is equal bit for bit
+// to launch_bucket_probs'.
+bool score_builds_table(bool bf16, int d, const uint8_t* ids, int64_t stride, int L, int P,
+                        int G);
+struct TableBuild {
+  const void* Q;  // [B, Hq, d] bf16
+  const void* R;  // [d, L*P] bf16
+  int d;
+  float tau;
+};
+// table: [B*Hkv, 2^P, L, G] from launch_bucket_probs, or unused with build;
+// scores [B*Hq, n_keys].
 hipError_t launch_score(const float* table, const uint8_t* ids, const float* vnorm,
                         int B, int Hq, int Hkv, int64_t n_keys, int64_t stride,
-                        int L, int P, float* scores, hipStream_t stream);
+                        int L, int P, float* scores, const TableBuild* build,
+                        hipStream_t stream);
 // Decode path: every block estimates a per-row threshold from its first
 // keys (thr[row * segs + seg], an order key) and appends every key whose
 // score's order key reaches it, as (order key, index), to sub-list (row, s)
 // at lists[row * n_keys + s * sub_len], in index order; sub_cnt[row * subs +
 // s] receives the sub-list's length.
 struct ScoreSelect {
-  const float* table;  // [B*Hkv, 2^P, L, G]
+  const float* table;  // [B*Hkv, 2^P, L, G] (written by the kernel with build)
   const uint8_t* ids;
   const float* vnorm;
   int64_t kk;          // < n_keys
@@ -96,7 +110,7 @@ struct ScoreSelect {
 // scores (optional): full score rows as well.
 hipError_t launch_score_select(const ScoreSelect& s, int B, int Hq, int Hkv, int64_t n_keys,
                                int64_t stride, int L, int P, float* scores,
-                               hipStream_t stream);
+                               const TableBuild* build, hipStream_t stream);
 
 // ------------------------------------------------------------------ top-k
 struct TopkPlan {

@@ -8,12 +8,15 @@
 // bucket, summed over the L tables and weighted by the key's value norm.
 //
 // One block owns one (batch, KV head) and a contiguous range of keys. It
-// copies that head's probability table [2^P][L][G] (float32, from the table
-// kernel) into LDS, then streams the bucket-id rows (L bytes per key,
-// coalesced across lanes) and the value norms from HBM, two steps ahead in
-// registers (the first steps are requested before the table is staged).
-// Each id byte is looked up once for the whole GQA group: the G
-// probabilities of the group sit in one 16-byte LDS slot.
+// gets that head's probability table [2^P][L][G] (float32) into LDS, either
+// copied from the table kernel's output or, in the decode path for bf16
+// queries with P = 8, built in place with the table kernel's arithmetic
+// (bit for bit the same table; no table kernel runs), then streams the
+// bucket-id rows (L bytes per key, coalesced across lanes) and the value
+// norms from HBM, two steps ahead in registers (the first steps are
+// requested while the table is being set up). Each id byte is looked up
+// once for the whole GQA group: the G probabilities of the group sit in one
+// 16-byte LDS slot.
 //
 // Bank spread: with the [u][l][G] layout and L a multiple of 16, the LDS bank
 // group of slot (u, l) depends only on l mod 8 (32 banks of 4 bytes, 16-byte
@@ -31,20 +34,22 @@
 // that about m of those scores reach, with m = m0 + 6 sqrt(m0) + 8 for the
 // m0 = kk * n_b / n keys of the row's top kk expected among its n_b sampled
 // keys (exactly kk when the block sees the whole row): the sampled order
-// keys are counted in 256 bins of 1/64 octave below the row's largest one,
-// and the threshold is the lower edge of the first bin at which the count
-// from the top reaches m. Thresholds are stored per block and row; every
-// key of the block whose score's order key reaches the threshold is
-// appended as (order key, index) to its wave's sub-list, in index order
-// (slots from one ballot and lane prefix counts per row and step, no
-// atomics), and the sub-list lengths are stored at the end. The selection
-// that follows is exact whatever these thresholds are: it takes the largest
+// keys are counted in 256 bins by their top 8 bits, then those of the bin
+// holding the m-th largest in 256 bins by the next 8 bits, and the
+// threshold is the lower edge of the sub-bin at which the count from the
+// top reaches m. Thresholds are stored per block and row; every key of the
+// block whose score's order key reaches the threshold is appended as
+// (order key, index) to its wave's sub-list, in index order (slots from one
+// ballot and lane prefix counts per row and step, no atomics), and the
+// sub-list lengths are stored at the end. The selection that follows is
+// exact whatever these thresholds are: it takes the largest
 // threshold of the row, checks that at least kk candidates reach it (every
 // key that does is a candidate) and otherwise scores the whole row.
 
 #include "common.hpp"
 #include "kernels.hpp"
 #include "radix.hpp"
+#include "soft_prob.hpp"
 
 #include <algorithm>
 
@@ -178,12 +183,22 @@ struct ScoreArgs {
   uint32_t* thr;       // [rows][segs] block thresholds (order keys)
   uint2* lists;        // [rows][n_keys]; sub-list s at s * seg_len / 16
   uint32_t* sub_cnt;   // [rows][segs * 16]
+  // table built in the kernel: bf16 query rows [B][Hq][d] and hyperplanes
+  // [d][L*P]; the built table is also stored to table_out when given
+  const uint16_t* Qb;
+  const uint16_t* Rb;
+  int d;
+  double two_over_tau;
+  float* table_out;
 };
 
-// LDS layout of a score block: the table, the per-row threshold
-// histograms, scratch words.
+// LDS layout of a score block: the table, (when the block builds the
+// table) the bit weights of the build, the per-row threshold histograms.
 __host__ __device__ inline size_t score_table_region(int L, int P, int G) {
   return align256(((size_t)1 << P) * L * G * sizeof(float));
+}
+__host__ __device__ inline size_t build_weights_region(int L, int P, int G) {
+  return align256((size_t)2 * P * L * G * sizeof(double));
 }
 
 // Scores of one key for the G heads of a group: written out (sk: the key's
@@ -235,6 +250,225 @@ __device__ inline uint32_t threshold_rank(int64_t kk, int64_t n, int n_b) {
   const double m0 = (double)kk * n_b / (double)n;
   const double m = ceil(m0 + 6.0 * sqrt(m0) + 8.0);
   return m >= (double)n_b ? 0u : (uint32_t)m;
+}
+
+// Lane i ^ 8, i ^ 16, i ^ 32 of a double (DPP row rotation by 8, lane swaps).
+__device__ __forceinline__ double xor8_f64(double v) { return dpp_f64<0x128>(v); }
+__device__ __forceinline__ double xor16_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint64_t lo = xor16_u32((uint32_t)u), hi = xor16_u32((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, (hi << 32) | lo);
+}
+__device__ __forceinline__ double xor32_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint64_t lo = xor32_u32((uint32_t)u), hi = xor32_u32((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, (hi << 32) | lo);
+}
+
+// Builds the probability table of KV head bg in LDS (layout [u][l][j], as
+// the table kernel writes it) from the G query rows of the group and the
+// hyperplanes (bf16, P = 8, d = 64 or 128), with the table kernel's
+// arithmetic, so both tables are equal bit for bit:
+//  * z = q . r in float64: with P = 8 the 8 columns of table l are its 8
+//    bits; the lane of (rows, table l, part) takes 16 consecutive
+//    coordinates (fma from 0 ascending) for R_ROWS query rows at once, so
+//    each hyperplane value is converted to float64 once per R_ROWS rows; the
+//    d/16 parts sit 8 lanes apart (lane = part * 8 + table within a block of
+//    8 tables: the 8 lanes of a part read 128 consecutive bytes of a
+//    hyperplane row) and are added pairwise in the table kernel's order
+//    ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7)) by a reduce-scatter
+//    that leaves bit `part` (and part + 4 when d = 64) in each lane;
+//  * the bit weights (bit_weights), then per (table, row) the bit-group
+//    products (bits 0-2, 3-5, 6-7; each multiplied in ascending bit order
+//    from 1.0) and p(u) = (A[u & 7] * B[(u >> 3) & 7]) * C[u >> 6] rounded
+//    to float32.
+// The hyperplanes and the query rows are staged in the table's LDS
+// (direct-to-LDS loads, in flight with the caller's first id loads, issued
+// by before()); the weights go to w as [bit][l][j] (2 * 8 * L * G doubles).
+// The entries are written by 8 threads per (table, row) pair p = l * G + j:
+// thread c takes buckets 32c .. 32c + 31, for which it needs the 8 products
+// of group A, 4 of group B and 1 of group C. Contains __syncthreads().
+template <int G, class Before>
+__device__ __forceinline__ void build_table(float* tab, double* w, const ScoreArgs& a, int bg,
+                                            Before before) {
+  constexpr int P = 8;
+  constexpr int R_ROWS = G >= 2 ? 2 : 1;  // query rows per lane
+  const int L = a.L, d = a.d;
+  const int C = L * P;
+  const int parts = d / 16;  // 4 or 8
+  const int pairs = L * G;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double* w1 = w;
+  double* w0 = w + (size_t)P * pairs;
+  const size_t r_bytes = (size_t)16 * d * L;
+  unsigned char* stage = reinterpret_cast<unsigned char*>(tab);
+
+  // hyperplanes, then the group's query rows, into LDS: 1 KB per wave and
+  // instruction
+  {
+    const uint4* rsrc = reinterpret_cast<const uint4*>(a.Rb);
+    const uint4* qsrc =
+        reinterpret_cast<const uint4*>(a.Qb + ((int64_t)b * a.Hq + (int64_t)g * G) * d);
+    const int nr = (int)(r_bytes / 16), nq = G * d / 8;
+    for (int i0 = wave * 64; i0 < nr + nq; i0 += kScoreThreads) {  // wave-uniform
+      const int i = i0 + lane;
+      if (i < nr + nq)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(i < nr ? rsrc + i : qsrc + (i - nr)),
+            (__attribute__((address_space(3))) void*)(stage + (size_t)i0 * 16), 16, 0, 0);
+    }
+  }
+  before();
+  __syncthreads();
+
+  // units of (R_ROWS rows, 8 tables), 8 * parts lanes each
+  const int lanes_per_unit = 8 * parts;
+  const int per_wave = 64 / lanes_per_unit;  // 1 or 2
+  const int row_groups = G / R_ROWS;
+  const int units = row_groups * (L / 8);
+  const int part = (lane / 8) % parts, li = lane % 8;
+  const uint16_t* qs = reinterpret_cast<const uint16_t*>(stage + r_bytes);
+  for (int u0 = wave * per_wave; u0 < units; u0 += kScoreWaves * per_wave) {  // wave-uniform
+    const int unit = u0 + lane / lanes_per_unit;
+    const bool active = unit < units;
+    const int uc = min(unit, units - 1);
+    const int jr = uc % row_groups, l = (uc / row_groups) * 8 + li;
+    const unsigned char* rcol = stage + (size_t)l * 16;
+    double acc[R_ROWS][8];
+#pragma unroll
+    for (int jj = 0; jj < R_ROWS; ++jj)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[jj][e] = 0.0;
+    const unsigned char* rp = rcol + (size_t)part * 16 * C * 2;
+    uint4 rnext = *reinterpret_cast<const uint4*>(rp);
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      uint4 qh[R_ROWS];  // 8 coordinates of each row
+#pragma unroll
+      for (int jj = 0; jj < R_ROWS; ++jj)
+        qh[jj] = *reinterpret_cast<const uint4*>(qs + (jr * R_ROWS + jj) * d + part * 16 + kh * 8);
+#pragma unroll
+      for (int k8 = 0; k8 < 8; ++k8) {
+        const int k = kh * 8 + k8;
+        // one hyperplane row ahead in flight, no more (registers)
+        const uint4 rw = rnext;
+        if (k + 1 < 16) rnext = *reinterpret_cast<const uint4*>(rp + (size_t)(k + 1) * C * 2);
+        float rv[8];
+        unpack8_bf16(rw, rv);
+        double rd[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rd[e] = (double)rv[e];
+#pragma unroll
+        for (int jj = 0; jj < R_ROWS; ++jj) {
+          const uint32_t wq = k8 < 2 ? qh[jj].x : k8 < 4 ? qh[jj].y : k8 < 6 ? qh[jj].z : qh[jj].w;
+          const double qk = (double)__uint_as_float((k8 & 1) ? (wq & 0xffff0000u) : (wq << 16));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[jj][e] = fma(qk, rd[e], acc[jj][e]);
+        }
+        // every row's sums of this coordinate are complete here (keeps the
+        // compiler from splitting the rows into passes that park rd)
+#pragma unroll
+        for (int jj = 0; jj < R_ROWS; ++jj)
+          asm volatile("" : "+v"(acc[jj][0]), "+v"(acc[jj][1]), "+v"(acc[jj][2]), "+v"(acc[jj][3]),
+                       "+v"(acc[jj][4]), "+v"(acc[jj][5]), "+v"(acc[jj][6]), "+v"(acc[jj][7]));
+      }
+    }
+    // reduce-scatter over the parts (lane bits 3, 4, 5 = part bits 0, 1, 2)
+    const bool b0 = (part & 1) != 0, b1 = (part & 2) != 0, b2 = (part & 4) != 0;
+#pragma unroll
+    for (int jj = 0; jj < R_ROWS; ++jj) {
+      double s1[4], s2[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double keep = b0 ? acc[jj][2 * i + 1] : acc[jj][2 * i];
+        const double send = b0 ? acc[jj][2 * i] : acc[jj][2 * i + 1];
+        s1[i] = keep + xor8_f64(send);
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const double keep = b1 ? s1[2 * m + 1] : s1[2 * m];
+        const double send = b1 ? s1[2 * m] : s1[2 * m + 1];
+        s2[m] = keep + xor16_f64(send);
+      }
+      const int j = jr * R_ROWS + jj;
+      if (parts == 8) {
+        const double z = (b2 ? s2[1] : s2[0]) + xor32_f64(b2 ? s2[0] : s2[1]);
+        double x1, x0;
+        bit_weights(z, a.two_over_tau, x1, x0);
+        if (active) {
+          w1[part * pairs + l * G + j] = x1;
+          w0[part * pairs + l * G + j] = x0;
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          double x1, x0;
+          bit_weights(s2[m], a.two_over_tau, x1, x0);
+          if (active) {
+            w1[(part + 4 * m) * pairs + l * G + j] = x1;
+            w0[(part + 4 * m) * pairs + l * G + j] = x0;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // table entries
+  constexpr int kPairsPerPass = kScoreThreads / 8;
+  for (int p0 = 0; p0 < pairs; p0 += kPairsPerPass) {  // block-uniform
+    const int np = min(kPairsPerPass, pairs - p0);
+    const int t = threadIdx.x;
+    if (t < np * 8) {
+      const int p = p0 + t % np, c = t / np;
+      double v1[8], v0[8];
+#pragma unroll
+      for (int bit = 0; bit < 8; ++bit) {
+        v1[bit] = w1[bit * pairs + p];
+        v0[bit] = w0[bit * pairs + p];
+      }
+      double A[8], Bq[4];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        double v = 1.0;
+        v *= (x & 1) ? v1[0] : v0[0];
+        v *= (x & 2) ? v1[1] : v0[1];
+        v *= (x & 4) ? v1[2] : v0[2];
+        A[x] = v;
+      }
+      const bool hb = (c & 1) != 0;  // bit 5 of these buckets
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        double v = 1.0;
+        v *= (x & 1) ? v1[3] : v0[3];
+        v *= (x & 2) ? v1[4] : v0[4];
+        v *= hb ? v1[5] : v0[5];
+        Bq[x] = v;
+      }
+      const int cc = c >> 1;  // bits 6-7 of these buckets
+      double Cv = 1.0;
+      Cv *= (cc & 1) ? v1[6] : v0[6];
+      Cv *= (cc & 2) ? v1[7] : v0[7];
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        tab[(c * 32 + i) * pairs + p] = (float)((A[i & 7] * Bq[i >> 3]) * Cv);
+    }
+  }
+}
+
+// The block's share (segment seg of segs) of its head's table, from LDS to
+// table_out.
+template <int G>
+__device__ __forceinline__ void store_table_share(const float* tab, const ScoreArgs& a, int bg,
+                                                  int seg) {
+  const int tsize = (1 << a.P) * a.L * G;
+  const int n4 = tsize / 4;
+  const int per = (n4 + a.segs - 1) / a.segs;
+  const int s1 = min(n4, (seg + 1) * per);
+  float4* dst = reinterpret_cast<float4*>(a.table_out + (int64_t)bg * tsize);
+  const float4* src = reinterpret_cast<const float4*>(tab);
+  for (int i = seg * per + (int)threadIdx.x; i < s1; i += kScoreThreads) dst[i] = src[i];
 }
 
 // Per query row j of the group: an order key that at least m of the sampled
@@ -310,21 +544,29 @@ __device__ __forceinline__ void block_thresholds(const uint32_t (&uk)[kPrefetch]
 // The common body of the score kernels. Scorer: prefetch() requests the
 // first step of ids and norms; score(q, i, acc, vn) scores key i (relative
 // to n0) of slot q of a step and requests the key kWaveStep further on.
-template <int G, class Scorer>
+template <int G, bool BUILD, class Scorer>
 __device__ void score_block(const ScoreArgs& a, int bg, int seg, float* tab, Scorer& sc,
                             const WaveRange& wr) {
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int lane = threadIdx.x & 63;
-  uint32_t* hist = reinterpret_cast<uint32_t*>(reinterpret_cast<unsigned char*>(tab) +
-                                               score_table_region(a.L, a.P, G));
+  unsigned char* lds = reinterpret_cast<unsigned char*>(tab);
+  const size_t treg = score_table_region(a.L, a.P, G);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(
+      lds + treg + (BUILD ? build_weights_region(a.L, a.P, G) : 0));
   float* sseg = a.scores ? a.scores + ((int64_t)b * a.Hq + (int64_t)g * G) * a.n_keys + wr.n0
                          : nullptr;
 
-  sc.prefetch();
-  stage_table<G>(tab, a.table, bg, a.L, a.P, seg);
   if (a.select)
     for (int i = threadIdx.x; i < 2 * G * kThrBins; i += kScoreThreads) hist[i] = 0u;
+  if constexpr (BUILD) {
+    build_table<G>(tab, reinterpret_cast<double*>(lds + treg), a, bg, [&] { sc.prefetch(); });
+  } else {
+    sc.prefetch();
+    stage_table<G>(tab, a.table, bg, a.L, a.P, seg);
+  }
   __syncthreads();
+  if constexpr (BUILD)
+    if (a.table_out) store_table_share<G>(tab, a, bg, seg);
 
   // first step of every wave: scored, then (decode) the block thresholds
   float acc[kPrefetch][G], vn[kPrefetch];
@@ -500,14 +742,14 @@ struct GenericScorer {
   }
 };
 
-template <int G, int LW>
+template <int G, int LW, bool BUILD>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(ScoreArgs a) {
   extern __shared__ __align__(16) float tab[];
   int bg, seg;
   if (!score_block_coords(a.bhkv, a.segs, bg, seg)) return;
   const WaveRange wr(a, seg);
   RotScorer<G, LW> sc(a, bg, wr, tab);
-  score_block<G>(a, bg, seg, tab, sc, wr);
+  score_block<G, BUILD>(a, bg, seg, tab, sc, wr);
 }
 
 template <int G>
@@ -517,7 +759,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_generic(ScoreArgs 
   if (!score_block_coords(a.bhkv, a.segs, bg, seg)) return;
   const WaveRange wr(a, seg);
   GenericScorer<G> sc(a, bg, wr, tab);
-  score_block<G>(a, bg, seg, tab, sc, wr);
+  score_block<G, false>(a, bg, seg, tab, sc, wr);
 }
 
 template <int G>
@@ -525,33 +767,42 @@ void set_lds_attributes() {
   static bool done = false;
   if (done) return;
   const int max_lds = (int)kLdsBytesPerCU;
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_rot<G, 8>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_rot<G, 16>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_rot<G, 4>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel_generic<G>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+  const void* fns[] = {
+      reinterpret_cast<const void*>(&score_kernel_rot<G, 4, false>),
+      reinterpret_cast<const void*>(&score_kernel_rot<G, 8, false>),
+      reinterpret_cast<const void*>(&score_kernel_rot<G, 16, false>),
+      reinterpret_cast<const void*>(&score_kernel_rot<G, 4, true>),
+      reinterpret_cast<const void*>(&score_kernel_rot<G, 8, true>),
+      reinterpret_cast<const void*>(&score_kernel_rot<G, 16, true>),
+      reinterpret_cast<const void*>(&score_kernel_generic<G>)};
+  for (const void* f : fns)
+    (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
   done = true;
+}
+
+template <int G, bool BUILD>
+void launch_score_rot(const ScoreArgs& a, int grid, size_t lds, hipStream_t stream) {
+  if (a.L == 32)
+    launch_kernel((score_kernel_rot<G, 8, BUILD>), dim3(grid), dim3(kScoreThreads), lds, stream, a);
+  else if (a.L == 64)
+    launch_kernel((score_kernel_rot<G, 16, BUILD>), dim3(grid), dim3(kScoreThreads), lds, stream, a);
+  else
+    launch_kernel((score_kernel_rot<G, 4, BUILD>), dim3(grid), dim3(kScoreThreads), lds, stream, a);
 }
 
 template <int G>
 hipError_t launch_score_g(const ScoreArgs& a, hipStream_t stream) {
-  const size_t lds = score_lds_bytes(a.L, a.P, G);
+  const bool build = a.Qb != nullptr;
+  const size_t lds = score_lds_bytes(a.L, a.P, G, build);
   const int total = a.bhkv * a.segs;
   const int grid = ((total + 7) / 8) * 8;
   set_lds_attributes<G>();
-  if (score_rotated(a.ids, a.stride, a.L)) {
-    if (a.L == 32)
-      launch_kernel((score_kernel_rot<G, 8>), dim3(grid), dim3(kScoreThreads), lds, stream, a);
-    else if (a.L == 64)
-      launch_kernel((score_kernel_rot<G, 16>), dim3(grid), dim3(kScoreThreads), lds, stream, a);
-    else
-      launch_kernel((score_kernel_rot<G, 4>), dim3(grid), dim3(kScoreThreads), lds, stream, a);
-  } else {
+  if (build)
+    launch_score_rot<G, true>(a, grid, lds, stream);
+  else if (score_rotated(a.ids, a.stride, a.L))
+    launch_score_rot<G, false>(a, grid, lds, stream);
+  else
     launch_kernel((score_kernel_generic<G>), dim3(grid), dim3(kScoreThreads), lds, stream, a);
-  }
   return hipGetLastError();
 }
 
@@ -586,8 +837,18 @@ ScoreArgs base_args(const float* table, const uint8_t* ids, const float* vnorm, 
 
 }  // namespace
 
-size_t score_lds_bytes(int L, int P, int G) {
-  return score_table_region(L, P, G) + (size_t)2 * G * kThrBins * sizeof(uint32_t);
+size_t score_lds_bytes(int L, int P, int G, bool build) {
+  return score_table_region(L, P, G) + (build ? build_weights_region(L, P, G) : 0) +
+         (size_t)2 * G * kThrBins * sizeof(uint32_t);
+}
+
+bool score_builds_table(bool bf16, int d, const uint8_t* ids, int64_t stride, int L, int P,
+                        int G) {
+  // hyperplanes (16 * d * L bytes) and query rows (2 * G * d) staged in
+  // the table's LDS
+  return bf16 && P == 8 && (d == 64 || d == 128) && score_rotated(ids, stride, L) &&
+         score_lds_bytes(L, P, G, true) <= kLdsBytesPerCU &&
+         (size_t)16 * d * L + (size_t)2 * G * d <= score_table_region(L, P, G);
 }
 
 bool score_rotated(const uint8_t* ids, int64_t stride, int L) {
@@ -597,7 +858,9 @@ bool score_rotated(const uint8_t* ids, int64_t stride, int L) {
 
 ScoreGeom plan_score(int bhkv, int64_t n_keys, int L, int P, int G) {
   ScoreGeom geo{};
-  const size_t lds = score_lds_bytes(L, P, G);
+  // the same geometry whether or not the block builds its table
+  const bool could_build = P == 8 && (L == 16 || L == 32 || L == 64);
+  const size_t lds = score_lds_bytes(L, P, G, could_build);
   // blocks resident per CU as limited by the 160 KB of LDS
   const int per_cu = (int)std::max<size_t>(1, std::min<size_t>(2, kLdsBytesPerCU / lds));
   const int64_t target = (int64_t)256 * per_cu;
@@ -615,18 +878,29 @@ ScoreGeom plan_score(int bhkv, int64_t n_keys, int L, int P, int G) {
   return geo;
 }
 
+void set_build(ScoreArgs& a, const TableBuild* build, float* table_out) {
+  if (!build) return;
+  a.Qb = static_cast<const uint16_t*>(build->Q);
+  a.Rb = static_cast<const uint16_t*>(build->R);
+  a.d = build->d;
+  a.two_over_tau = 2.0 / (double)build->tau;
+  a.table_out = table_out;
+}
+
 hipError_t launch_score(const float* table, const uint8_t* ids, const float* vnorm,
                         int B, int Hq, int Hkv, int64_t n_keys, int64_t stride,
-                        int L, int P, float* scores, hipStream_t stream) {
+                        int L, int P, float* scores, const TableBuild* build,
+                        hipStream_t stream) {
   if (n_keys == 0) return hipSuccess;
   ScoreArgs a = base_args(table, ids, vnorm, B, Hq, Hkv, n_keys, stride, L, P);
   a.scores = scores;
+  set_build(a, build, nullptr);
   return launch_score_any(a, Hq / Hkv, stream);
 }
 
 hipError_t launch_score_select(const ScoreSelect& s, int B, int Hq, int Hkv, int64_t n_keys,
                                int64_t stride, int L, int P, float* scores,
-                               hipStream_t stream) {
+                               const TableBuild* build, hipStream_t stream) {
   ScoreArgs a = base_args(s.table, s.ids, s.vnorm, B, Hq, Hkv, n_keys, stride, L, P);
   a.scores = scores;
   a.select = 1;
@@ -634,6 +908,7 @@ hipError_t launch_score_select(const ScoreSelect& s, int B, int Hq, int Hkv, int
   a.thr = s.thr;
   a.lists = s.lists;
   a.sub_cnt = s.sub_cnt;
+  set_build(a, build, const_cast<float*>(s.table));
   return launch_score_any(a, Hq / Hkv, stream);
 }
 

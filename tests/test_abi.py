@@ -153,3 +153,31 @@ def test_workspace_sizes_are_sane(lib):
     assert lib.socket_decode_workspace_bytes(0, 32, 8, 128, 1, 32, 8, 1) == 0
     assert lib.socket_topk_workspace_bytes(128, 131072, 4096) >= 128 * 2048 * 4
     assert lib.socket_sparse_attn_workspace_bytes(4, 32, 128, 4096) >= 4 * 32 * 130 * 4
+
+
+def _kernels(lib, ids=FAKE, dtype=_lib.DTYPE_BF16, B=4, Hq=32, Hkv=8, d=128, N=131072,
+             L=32, P=8, k=4096, with_scores=0, cap=512):
+    buf = ctypes.create_string_buffer(cap)
+    n = lib.socket_decode_kernels(ids, dtype, B, Hq, Hkv, d, N, N, L, P, k, with_scores,
+                                  buf, cap)
+    return n, buf.value.decode().split(",") if n > 0 else []
+
+
+def test_decode_kernel_sequence(lib):
+    """The launch sequence socket_decode reports (host-only query): the score
+    kernel builds the tables itself for bf16, P = 8, aligned id rows; the
+    table kernel runs otherwise; k >= n_keys skips selection."""
+    tail = ["sparse_attn_kernel", "attn_merge_kernel"]
+    assert _kernels(lib) == (4, ["score_kernel", "topk_select_kernel"] + tail)
+    n, names = _kernels(lib, dtype=_lib.DTYPE_F32)
+    assert names == ["bucket_probs_kernel", "score_kernel", "topk_select_kernel"] + tail
+    assert n == 5
+    assert _kernels(lib, P=6)[1][0] == "bucket_probs_kernel"
+    assert _kernels(lib, ids=FAKE + 8)[1][0] == "bucket_probs_kernel"  # unaligned id rows
+    assert _kernels(lib, L=24, P=8)[1][0] == "bucket_probs_kernel"     # not the rotated path
+    assert _kernels(lib, k=131072) == (3, ["iota_rows_kernel"] + tail)
+    assert _kernels(lib, k=131072, with_scores=1)[1] == ["score_kernel", "iota_rows_kernel"] + tail
+    assert _kernels(lib, Hq=30)[0] == -1      # G not an integer
+    assert _kernels(lib, cap=8)[0] == -2      # names do not fit
+    assert lib.socket_decode_kernels(FAKE, _lib.DTYPE_BF16, 4, 32, 8, 128, 131072, 131072,
+                                     32, 8, 4096, 0, None, 0) == 4
