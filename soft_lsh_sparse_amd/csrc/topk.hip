@@ -84,6 +84,12 @@ struct RowLists {
   }
 };
 
+// Entry p of a row whose candidates are all in LDS.
+struct CacheAt {
+  const uint2* cache;
+  __device__ __forceinline__ uint2 operator()(uint32_t p) const { return cache[p]; }
+};
+
 // Entry p of a full score row: (order key, p).
 struct ScoreRowAt {
   const float* s;
@@ -157,6 +163,9 @@ template <int NT, typename At>
 __device__ void select_and_emit(const At& at, uint32_t total, uint32_t kk, int start_pass,
                                 uint32_t prefix, uint32_t need, uint32_t floor,
                                 RefineShared& sh, int32_t* o) {
+  // the in-order loops below keep kB entries per lane in flight
+  // (addresses clamped to the entries, results of the surplus ones unused)
+  constexpr int kB = 8;
   uint32_t* res = sh.scratch + NT / 64 + 1;
   for (int pass = start_pass; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
@@ -177,28 +186,56 @@ __device__ void select_and_emit(const At& at, uint32_t total, uint32_t kk, int s
   const uint32_t T = prefix;
   const uint32_t ties = need;  // keys equal to T still to take
 
-  // final pass, in index order: every thread takes a run of consecutive
-  // entries; one scan gives, per thread, the keys above T and the keys
-  // equal to T before its run
-  const uint32_t per = (total + NT - 1) / NT;
-  const uint32_t p0 = min(total, (uint32_t)threadIdx.x * per), p1 = min(total, p0 + per);
-  uint32_t n_gt = 0, n_eq = 0;
-  for (uint32_t p = p0; p < p1; ++p) {
-    const uint32_t u = at(p).x;
-    n_gt += u > T ? 1u : 0u;
-    n_eq += u == T ? 1u : 0u;
+  // final pass, in entry (= index) order: wave w takes a contiguous chunk
+  // of entries, 64 per step. First every wave counts the keys above T and
+  // equal to T in its chunk (ballots); then, from the counts of the waves
+  // before it, it knows how many keys precede its chunk in the output and
+  // how many of the ties are taken before it, and writes the indices it
+  // keeps at consecutive positions (ballot, lane prefix).
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t chunk = (total + NW * 64 - 1) / (NW * 64) * 64;
+  const uint32_t c0 = min(total, (uint32_t)wave * chunk), c1 = min(total, c0 + chunk);
+  uint32_t n_gt = 0, n_eq = 0;  // wave-uniform
+  for (uint32_t base = c0; base < c1; base += kB * 64) {  // wave-uniform
+    uint32_t u[kB];
+#pragma unroll
+    for (int i = 0; i < kB; ++i) u[i] = at(min(base + i * 64 + lane, total - 1)).x;
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      const bool valid = base + i * 64 + lane < c1;
+      n_gt += (uint32_t)__popcll(__ballot(valid && u[i] > T));
+      n_eq += (uint32_t)__popcll(__ballot(valid && u[i] == T));
+    }
   }
-  uint32_t ex_gt, ex_eq, tot_gt, tot_eq;
-  block_exclusive_scan2<NT>(n_gt, n_eq, sh.scratch, &ex_gt, &ex_eq, &tot_gt, &tot_eq);
-  uint32_t pos = ex_gt + min(ex_eq, ties);
-  uint32_t tie_rank = ex_eq;
-  for (uint32_t p = p0; p < p1; ++p) {
-    const uint2 e = at(p);
-    bool take = e.x > T;
-    if (e.x == T) take = tie_rank++ < ties;
-    if (take) {
-      if (pos < kk) o[pos] = (int32_t)e.y;
-      ++pos;
+  uint32_t* wc = sh.h;  // [NW][2]; the histogram is no longer read
+  if (lane == 0) {
+    wc[2 * wave] = n_gt;
+    wc[2 * wave + 1] = n_eq;
+  }
+  __syncthreads();
+  uint32_t before_gt = 0, before_eq = 0;
+  for (int w = 0; w < wave; ++w) {
+    before_gt += wc[2 * w];
+    before_eq += wc[2 * w + 1];
+  }
+  uint32_t pos = before_gt + min(before_eq, ties);
+  uint32_t eq_seen = before_eq;
+  for (uint32_t base = c0; base < c1; base += kB * 64) {  // wave-uniform
+    uint2 e[kB];
+#pragma unroll
+    for (int i = 0; i < kB; ++i) e[i] = at(min(base + i * 64 + lane, total - 1));
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      const bool valid = base + i * 64 + lane < c1;
+      const bool gt = valid && e[i].x > T, eq = valid && e[i].x == T;
+      const uint64_t beq = __ballot(eq);
+      const bool take = gt || (eq && eq_seen + lane_prefix(beq) < ties);
+      const uint64_t bt = __ballot(take);
+      const uint32_t slot = pos + lane_prefix(bt);
+      if (take && slot < kk) o[slot] = (int32_t)e[i].y;
+      pos += (uint32_t)__popcll(bt);
+      eq_seen += (uint32_t)__popcll(beq);
     }
   }
 }
@@ -222,7 +259,11 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
                                              sh.scratch);
   RowLists rl{lists + (int64_t)row * n, sh.cache, 0u, sh.off, subs, sub_len};
   cache_candidates<NT>(rl, sh.cache, total);
-  select_and_emit<NT>(rl, total, (uint32_t)kk, 1, b1, need1, 0u, sh, idx + (int64_t)row * kk);
+  if (total <= rl.cached)
+    select_and_emit<NT>(CacheAt{sh.cache}, total, (uint32_t)kk, 1, b1, need1, 0u, sh,
+                        idx + (int64_t)row * kk);
+  else
+    select_and_emit<NT>(rl, total, (uint32_t)kk, 1, b1, need1, 0u, sh, idx + (int64_t)row * kk);
 }
 
 // Selection of the decode path. One block per row. The score kernel's
@@ -242,13 +283,46 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
   const uint32_t kk = (uint32_t)a.kk;
   int32_t* o = a.idx + (int64_t)row * a.kk;
   uint32_t* res = sh.scratch + NT / 64 + 1;
-  // T: the largest block threshold of the row (loads issued with the
-  // sub-list lengths below)
-  uint32_t tmax = 0;
-  for (int s = threadIdx.x; s < a.segs; s += NT) tmax = max(tmax, a.thr[(int64_t)row * a.segs + s]);
+  // The first round of candidate copies (below) is requested before the
+  // sub-list lengths are known: each wave loads the first kSpec * 64
+  // entries of its kRound sub-lists (clamped to the row, unused beyond a
+  // sub-list's length), in flight with the length and threshold loads.
+  constexpr int kWaves = NT / 64, kRound = 8, kSpec = 1;
+  const uint2* glob = a.lists + (int64_t)row * a.n;
+  uint2 spec[kRound][kSpec];
+#pragma unroll
+  for (int k = 0; k < kRound; ++k) {
+    const int sl = min(wave + k * kWaves, a.subs - 1);
+#pragma unroll
+    for (int t = 0; t < kSpec; ++t)
+      spec[k][t] = glob[min((int64_t)sl * a.sub_len + t * 64 + lane, a.n - 1)];
+  }
+  // T (the largest block threshold of the row) and the sub-list lengths:
+  // straight-line loads (segs <= subs / 16 <= NT, at most kMaxSelectSubLists
+  // / NT lengths per thread, a run of consecutive sub-lists), all in flight
+  // with the copies above
+  constexpr int kPerMax = kMaxSelectSubLists / NT;
+  const int per = (a.subs + NT - 1) / NT;
+  const int s0 = min(a.subs, (int)threadIdx.x * per);
+  const uint32_t* cnt = a.sub_cnt + (int64_t)row * a.subs;
+  uint32_t cn[kPerMax];
+#pragma unroll
+  for (int q = 0; q < kPerMax; ++q) cn[q] = (q < per && s0 + q < a.subs) ? cnt[s0 + q] : 0u;
+  uint32_t tmax = (int)threadIdx.x < a.segs ? a.thr[(int64_t)row * a.segs + threadIdx.x] : 0u;
   for (int i = threadIdx.x; i < kHistBins; i += NT) sh.h[i] = 0u;
-  const uint32_t total = sublist_offsets<NT>(a.sub_cnt + (int64_t)row * a.subs, a.subs, sh.off,
-                                             sh.scratch);
+  uint32_t total;
+  {
+    uint32_t sum = 0;
+#pragma unroll
+    for (int q = 0; q < kPerMax; ++q) sum += cn[q];
+    uint32_t run = block_exclusive_scan<NT>(sum, sh.scratch, &total);
+#pragma unroll
+    for (int q = 0; q < kPerMax; ++q) {
+      if (q < per && s0 + q < a.subs) sh.off[s0 + q] = run;
+      run += cn[q];
+    }
+    if (threadIdx.x == 0) sh.off[a.subs] = total;
+  }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, m, 64));
   if (lane == 0) sh.tmax[wave] = tmax;
@@ -257,31 +331,50 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
   for (int w = 0; w < NT / 64; ++w) tmax = max(tmax, sh.tmax[w]);
 
   // candidates into LDS (as far as they fit), counted into the first-digit
-  // histogram when they reach T: each wave copies whole sub-lists, the
-  // first 64 entries of eight of them per round with all loads in flight
-  RowLists rl{a.lists + (int64_t)row * a.n, sh.cache, 0u, sh.off, a.subs, a.sub_len};
+  // histogram when they reach T: each wave copies whole sub-lists, eight of
+  // them per round, 64 entries of each per batch of loads
+  RowLists rl{glob, sh.cache, 0u, sh.off, a.subs, a.sub_len};
   {
     const uint32_t cached = min(total, (uint32_t)kRefineCache);
-    constexpr int kWaves = NT / 64, kRound = 8;
     auto take = [&](const uint2& e, uint32_t p) {
       if (p < cached) sh.cache[p] = e;
       if (e.x >= tmax) atomicAdd(&sh.h[e.x >> 21], 1u);
     };
-    for (int s0 = wave; s0 < a.subs; s0 += kWaves * kRound) {
-      uint2 e[kRound];
+    for (int s0 = wave; s0 < a.subs; s0 += kWaves * kRound) {  // wave-uniform
+      const bool first = s0 == wave;
+      uint2 e[kRound][kSpec];
 #pragma unroll
       for (int k = 0; k < kRound; ++k) {
         const int sl = s0 + k * kWaves;
-        if (sl < a.subs && (uint32_t)lane < sh.off[sl + 1] - sh.off[sl])
-          e[k] = rl.glob[(int64_t)sl * a.sub_len + lane];
+#pragma unroll
+        for (int t = 0; t < kSpec; ++t) {
+          if (first) {
+            e[k][t] = spec[k][t];
+          } else if (sl < a.subs && (uint32_t)(t * 64 + lane) < sh.off[sl + 1] - sh.off[sl]) {
+            e[k][t] = glob[(int64_t)sl * a.sub_len + t * 64 + lane];
+          }
+        }
+      }
+      // the next 64 entries of every sub-list that has them, all requested
+      // before any is used
+      uint2 x[kRound];
+#pragma unroll
+      for (int k = 0; k < kRound; ++k) {
+        const int sl = s0 + k * kWaves;
+        if (sl < a.subs && (uint32_t)(kSpec * 64 + lane) < sh.off[sl + 1] - sh.off[sl])
+          x[k] = glob[(int64_t)sl * a.sub_len + kSpec * 64 + lane];
       }
 #pragma unroll
       for (int k = 0; k < kRound; ++k) {
         const int sl = s0 + k * kWaves;
         if (sl >= a.subs) continue;
         const uint32_t o = sh.off[sl], c = sh.off[sl + 1] - o;
-        if ((uint32_t)lane < c) take(e[k], o + lane);
-        for (uint32_t i = lane + 64; i < c; i += 64) take(rl.glob[(int64_t)sl * a.sub_len + i], o + i);
+#pragma unroll
+        for (int t = 0; t < kSpec; ++t)
+          if ((uint32_t)(t * 64 + lane) < c) take(e[k][t], o + t * 64 + lane);
+        if ((uint32_t)(kSpec * 64 + lane) < c) take(x[k], o + kSpec * 64 + lane);
+        for (uint32_t i = (kSpec + 1) * 64 + lane; i < c; i += 64)
+          take(glob[(int64_t)sl * a.sub_len + i], o + i);
       }
     }
     __syncthreads();
@@ -290,7 +383,10 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
   find_threshold_bin<NT>(sh.h, kk, sh.scratch, res);
   const uint32_t b1 = res[0], above1 = res[1], n_above = res[2];
   if (n_above >= kk) {
-    select_and_emit<NT>(rl, total, kk, 1, b1, kk - above1, tmax, sh, o);
+    if (total <= rl.cached)
+      select_and_emit<NT>(CacheAt{sh.cache}, total, kk, 1, b1, kk - above1, tmax, sh, o);
+    else
+      select_and_emit<NT>(rl, total, kk, 1, b1, kk - above1, tmax, sh, o);
     return;
   }
 
