@@ -477,9 +477,9 @@ __device__ __forceinline__ void store_table_share(const float* tab, const ScoreA
 // octaves) and finds, from the top, the bin b1 at which the count reaches
 // m; the second counts bits 16..23 of the keys in b1 (bins of 1/128 of an
 // octave) and finds b2 the same way. The threshold is the lowest key of
-// (b1, b2), or 0 when fewer than m keys are valid. Every wave scans every
-// row's bins itself (4 bins per lane, DPP prefix sums), so the two passes
-// need two block barriers. hist: 2 * G * kThrBins counters, zero on entry.
+// (b1, b2), or 0 when fewer than m keys are valid. Wave j searches row j's
+// bins (4 bins per lane, DPP prefix sums). hist: 2 * G * kThrBins
+// counters, zero on entry. Contains __syncthreads().
 template <int G>
 __device__ __forceinline__ void block_thresholds(const uint32_t (&uk)[kPrefetch][G],
                                                  const bool (&valid)[kPrefetch], uint32_t m,
@@ -496,32 +496,45 @@ __device__ __forceinline__ void block_thresholds(const uint32_t (&uk)[kPrefetch]
   __syncthreads();
   // bin (from the top) at which the running count reaches need; lane 0
   // holds the 4 highest bins. Returns kThrBins when the bins hold fewer.
+  // the bin (from the top) at which the running count of a row's bins hr
+  // reaches need, and the count before it (kThrBins, 0 when the bins hold
+  // fewer); lane 0 holds the 4 highest bins. One wave per row.
   auto find = [&](const uint32_t* hr, uint32_t need, uint32_t& before) {
     const uint4 c4 = *reinterpret_cast<const uint4*>(hr + kThrBins - 4 - 4 * lane);
     const uint32_t cs[4] = {c4.w, c4.z, c4.y, c4.x};  // descending bins
     const uint32_t sum = c4.x + c4.y + c4.z + c4.w;
     uint32_t run = wave_inclusive_scan_dpp(sum) - sum;
-    uint32_t bin = kThrBins, bef = 0u;
+    uint32_t b = kThrBins, bef = 0u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (run < need && run + cs[i] >= need) {
-        bin = (uint32_t)(kThrBins - 1 - 4 * lane - i);
+        b = (uint32_t)(kThrBins - 1 - 4 * lane - i);
         bef = run;
       }
       run += cs[i];
     }
-    const uint64_t hit = __ballot(bin != kThrBins);
-    if (hit == 0) return (uint32_t)kThrBins;
-    const int src = __ffsll((unsigned long long)hit) - 1;
-    before = (uint32_t)__shfl((int)bef, src, 64);
-    return (uint32_t)__shfl((int)bin, src, 64);
+    const uint64_t hit = __ballot(b != kThrBins);
+    const int src = hit ? __ffsll((unsigned long long)hit) - 1 : 0;
+    before = hit ? (uint32_t)__builtin_amdgcn_readlane((int)bef, src) : 0u;
+    return hit ? (uint32_t)__builtin_amdgcn_readlane((int)b, src) : (uint32_t)kThrBins;
   };
+  // wave j < G searches row j and leaves its result in the row's first
+  // bins, which no other wave reads
+  const int wave = threadIdx.x >> 6;
+  if (wave < G) {
+    uint32_t before;
+    const uint32_t b = find(h1 + wave * kThrBins, m, before);
+    if (lane == 0) {
+      h1[wave * kThrBins] = b;
+      h1[wave * kThrBins + 1] = m - before;
+    }
+  }
+  __syncthreads();
   uint32_t b1[G], need2[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    uint32_t before = 0u;
-    b1[j] = find(h1 + j * kThrBins, m, before);
-    need2[j] = m - before;
+    b1[j] = h1[j * kThrBins];
+    need2[j] = h1[j * kThrBins + 1];
   }
 #pragma unroll
   for (int q = 0; q < kPrefetch; ++q)
@@ -530,15 +543,16 @@ __device__ __forceinline__ void block_thresholds(const uint32_t (&uk)[kPrefetch]
       if (valid[q] && b1[j] < kThrBins && (uk[q][j] >> 24) == b1[j])
         atomicAdd(&h2[j * kThrBins + ((uk[q][j] >> 16) & 255u)], 1u);
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    thr[j] = 0u;
-    if (b1[j] < kThrBins) {
-      uint32_t before = 0u;
-      const uint32_t b2 = find(h2 + j * kThrBins, need2[j], before);  // found: b1 holds the m-th
-      thr[j] = (b1[j] << 24) | (b2 << 16);
-    }
+  if (wave < G) {
+    uint32_t before;
+    const uint32_t b1w = h1[wave * kThrBins];
+    // b2 is found whenever b1 is: bin b1 holds the m-th key
+    const uint32_t b2 = find(h2 + wave * kThrBins, h1[wave * kThrBins + 1], before);
+    if (lane == 0) h2[wave * kThrBins] = b1w < kThrBins ? (b1w << 24) | (b2 << 16) : 0u;
   }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < G; ++j) thr[j] = h2[j * kThrBins];
 }
 
 // The common body of the score kernels. Scorer: prefetch() requests the
