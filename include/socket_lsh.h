@@ -144,7 +144,7 @@ socket_status socket_bucket_probs(const void* Q, const void* R,
  *   vnorm   [B*Hkv, head_stride_rows] float32
  *   scores  [B, Hq, n_keys] float32 (output)
  * The L probabilities are summed in float32 in the order l = (t + r) mod L,
- * t = 0 .. L-1, where r = key index mod 8 when L is 16, 32 or 64 and the id
+ * t = 0 .. L-1, where r = key index mod 16 when L is 16, 32 or 64 and the id
  * rows are 16-byte aligned (this spreads LDS banks), else r = 0; the sum is
  * then multiplied by the value norm.
  */

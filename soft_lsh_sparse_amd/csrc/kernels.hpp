@@ -70,7 +70,7 @@ struct ScoreGeom {
 };
 ScoreGeom plan_score(int bhkv, int64_t n_keys, int L, int P, int G);
 // true when the kernel sums each key's tables in the rotated order
-// l = (t + key) mod L, t = 0..L-1 (with key taken mod 8); else l = t
+// l = (t + key) mod L, t = 0..L-1 (with key taken mod 16); else l = t
 bool score_rotated(const uint8_t* ids, int64_t stride, int L);
 // LDS bytes of one score block (build: the block builds its table).
 size_t score_lds_bytes(int L, int P, int G, bool build);

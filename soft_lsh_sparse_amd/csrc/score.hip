@@ -19,14 +19,14 @@
 // 16-byte LDS slot.
 //
 // Bank spread: with the [u][l][G] layout and L a multiple of 16, the LDS bank
-// group of slot (u, l) depends only on l mod 8 (32 banks of 4 bytes, 16-byte
-// slots). Lane i walks the tables in the rotated order l = (t + n) mod L for
-// its key n (n mod 8 = i mod 8), so the 8 lanes the LDS serves together hit 8
-// different bank groups whatever buckets the keys fall in. The rotation is
-// applied to the id bytes in registers once per key; the slot offset of step
-// t is a per-lane base (two candidates, before and after the wrap) plus a
-// compile-time immediate. The L probabilities are summed in float32 in that
-// fixed order and multiplied by the value norm.
+// group of slot (u, l) depends only on l mod 16 (64 banks of 4 bytes,
+// 16-byte slots). Lane i walks the tables in the rotated order l = (t + n)
+// mod L for its key n (n mod 16 = i mod 16), so the 16 lanes the LDS serves
+// together hit 16 different bank groups whatever buckets the keys fall in.
+// The rotation is applied to the id bytes in registers once per key; the
+// slot offset of step t is a per-lane base (two candidates, before and
+// after the wrap) plus a compile-time immediate. The L probabilities are
+// summed in float32 in that fixed order and multiplied by the value norm.
 //
 // Candidate emission (the decode path). Every wave owns a contiguous range
 // of the block's keys. The block scores the first step of every wave (up to
@@ -79,17 +79,21 @@ __device__ __forceinline__ uint32_t select_lanes(uint32_t a, uint32_t b, uint64_
 }
 
 // Rotate the NB-byte array held in NW 32-bit words left by r bytes
-// (0 <= r < 8): byte i of the result is byte (i + r) mod NB of the input.
-// One word-select stage (lanes whose bit is set in by_word: r >= 4) and one
-// byte funnel shift per word.
+// (0 <= r < 16): byte i of the result is byte (i + r) mod NB of the input.
+// Two word-select stages (by one word in the lanes set in by1: bit 2 of r,
+// by two words in those set in by2: bit 3 of r) and one byte funnel shift
+// per word.
 template <int NW>
-__device__ __forceinline__ void rotate_bytes(uint32_t (&w)[NW], uint64_t by_word, int rb) {
-  uint32_t t[NW];
+__device__ __forceinline__ void rotate_bytes(uint32_t (&w)[NW], uint64_t by1, uint64_t by2,
+                                             int rb) {
+  uint32_t t[NW], v[NW];
 #pragma unroll
-  for (int i = 0; i < NW; ++i) t[i] = select_lanes(w[i], w[(i + 1) % NW], by_word);
+  for (int i = 0; i < NW; ++i) t[i] = select_lanes(w[i], w[(i + 1) % NW], by1);
+#pragma unroll
+  for (int i = 0; i < NW; ++i) v[i] = select_lanes(t[i], t[(i + 2) % NW], by2);
 #pragma unroll
   for (int i = 0; i < NW; ++i)
-    w[i] = __builtin_amdgcn_alignbyte(t[(i + 1) % NW], t[i], rb);
+    w[i] = __builtin_amdgcn_alignbyte(v[(i + 1) % NW], v[i], rb);
 }
 
 // Ties the next ids to the running sums (empty asm, no instruction): every
@@ -663,10 +667,10 @@ struct RotScorer {
     // block-uniform bases of this segment; per-thread offsets stay 32-bit
     idseg = a.ids + ((int64_t)bg * a.stride + wr.n0) * L;
     vseg = a.vnorm + (int64_t)bg * a.stride + wr.n0;
-    // n0 + wb is a multiple of 8, so every key of this lane has the same
-    // rotation r = key index mod 8 and the same two bases
+    // n0 + wb is a multiple of 16, so every key of this lane has the same
+    // rotation r = key index mod 16 and the same two bases
     const int lane = threadIdx.x & 63;
-    r = lane & 7;
+    r = lane & 15;
     rb = r & 3;
     base_nowrap = r * G;      // slot offset of step t: t*G + base
     base_wrap = (r - L) * G;  // ... once t + r >= L
@@ -706,12 +710,12 @@ struct RotScorer {
 #pragma unroll
     for (int j = 0; j < G; ++j) acc[j] = 0.f;
     if (!valid) return;
-    rotate_bytes<LW>(w, __ballot(r >= 4), rb);  // lanes with r >= 4 shift by a word
+    rotate_bytes<LW>(w, __ballot(r & 4), __ballot(r & 8), rb);
 #pragma unroll
     for (int t = 0; t < L; ++t) {
       // P bits of byte t: ids are < 2^P, so this never leaves the table
       const uint32_t u = __builtin_amdgcn_ubfe(w[t >> 2], (t & 3) * 8, P);
-      const int off = (t + 7 < L) ? base_nowrap : (t + r < L ? base_nowrap : base_wrap);
+      const int off = (t + 15 < L) ? base_nowrap : (t + r < L ? base_nowrap : base_wrap);
       float pr[G];
       lds_load_group<G>(tab + (int)u * (L * G) + off + t * G, pr);
 #pragma unroll

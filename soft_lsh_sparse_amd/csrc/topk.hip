@@ -404,7 +404,7 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
   const uint8_t* idh = a.ids + (int64_t)bg * a.stride * L;
   const float* vnh = a.vnorm + (int64_t)bg * a.stride;
   for (int64_t i = threadIdx.x; i < a.n; i += NT) {
-    const int r = a.rotated ? (int)(i & 7) : 0;
+    const int r = a.rotated ? (int)(i & 15) : 0;
     float acc = 0.f;
     for (int t = 0; t < L; ++t) {
       const int l = t + r < L ? t + r : t + r - L;
