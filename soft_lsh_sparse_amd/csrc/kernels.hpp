@@ -95,7 +95,7 @@ hipError_t launch_score(const float* table, const uint8_t* ids, const float* vno
                         hipStream_t stream);
 // Decode path: every block estimates a per-row threshold from its first
 // keys (thr[row * segs + seg], an order key) and appends every key whose
-// score's order key reaches it, as (order key, index), to sub-list (row, s)
+// score's order key reaches it, as (float32 score bits, index), to sub-list (row, s)
 // at lists[row * n_keys + s * sub_len], in index order; sub_cnt[row * subs +
 // s] receives the sub-list's length.
 struct ScoreSelect {

@@ -39,7 +39,8 @@
 // threshold is the lower edge of the sub-bin at which the count from the
 // top reaches m. Thresholds are stored per block and row; every key of the
 // block whose score's order key reaches the threshold is appended as
-// (order key, index) to its wave's sub-list, in index order (slots from one
+// (score bits, index) to its wave's sub-list, in index order (the test is
+// one float compare against the smallest float with that key; slots from one
 // ballot and lane prefix counts per row and step, no atomics), and the
 // sub-list lengths are stored at the end. The selection that follows is
 // exact whatever these thresholds are: it takes the largest
@@ -212,20 +213,27 @@ __host__ __device__ inline size_t build_weights_region(int L, int P, int G) {
 template <int G>
 __device__ __forceinline__ void emit_scores(const ScoreArgs& a, const float (&acc)[G], float vn,
                                             bool valid, uint32_t key, float* sk,
-                                            uint2* const (&lst)[G], const uint32_t (&thr)[G],
+                                            uint2* const (&lst)[G], const float (&thrf)[G],
                                             uint32_t (&cnt)[G]) {
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     const float sc = vn * acc[j];
     if (sk != nullptr && valid) sk[(int64_t)j * a.n_keys] = sc;
     if (a.select) {
-      const uint32_t u = float_order_key(sc);
-      const bool pass = valid && u >= thr[j];
+      const bool pass = valid && sc >= thrf[j];
       const uint64_t bal = __ballot(pass);
-      if (pass) lst[j][cnt[j] + lane_prefix(bal)] = make_uint2(u, key);
+      if (pass) lst[j][cnt[j] + lane_prefix(bal)] = make_uint2(__float_as_uint(sc), key);
       cnt[j] += (uint32_t)__popcll(bal);
     }
   }
+}
+
+// The smallest float whose order key (float_order_key) is at least thr, so
+// that for finite s, s >= threshold_float(thr) exactly when
+// float_order_key(s) >= thr (-0 and +0 share one key); -inf for thr = 0.
+__device__ __forceinline__ float threshold_float(uint32_t thr) {
+  if (thr == 0u) return -INFINITY;
+  return __uint_as_float(thr >= 0x80000000u ? (thr & 0x7fffffffu) : ~thr);
 }
 
 // Keys [n0 + wb, n0 + we) of this block's segment belong to this wave.
@@ -596,6 +604,7 @@ __device__ void score_block(const ScoreArgs& a, int bg, int seg, float* tab, Sco
     sc.score(q, i, valid[q], acc[q], vn[q]);
   }
   uint32_t thr[G], nsel[G];
+  float thrf[G];
   uint2* lst[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
@@ -617,14 +626,21 @@ __device__ void score_block(const ScoreArgs& a, int bg, int seg, float* tab, Sco
     for (int j = 0; j < G; ++j) {
       const int64_t row = (int64_t)b * a.Hq + (int64_t)g * G + j;
       if (threadIdx.x == 0) a.thr[row * a.segs + seg] = thr[j];
-      lst[j] = a.lists + row * a.n_keys + wr.n0 + wr.wb;
+      // the wave's sub-list base, held in scalar registers (the stores then
+      // take a 32-bit lane offset)
+      const uint64_t base = reinterpret_cast<uint64_t>(a.lists + row * a.n_keys + wr.n0 + wr.wb);
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
+      lst[j] = reinterpret_cast<uint2*>(((uint64_t)hi << 32) | lo);
     }
   }
+#pragma unroll
+  for (int j = 0; j < G; ++j) thrf[j] = threshold_float(thr[j]);
 #pragma unroll
   for (int q = 0; q < kPrefetch; ++q) {
     const int i = wr.wb + q * 64 + lane;
     emit_scores<G>(a, acc[q], vn[q], valid[q], (uint32_t)(wr.n0 + i), sseg ? sseg + i : nullptr,
-                   lst, thr, nsel);
+                   lst, thrf, nsel);
   }
   for (int base = wr.wb + kWaveStep; base < wr.we; base += kWaveStep) {  // wave-uniform
 #pragma unroll
@@ -634,7 +650,7 @@ __device__ void score_block(const ScoreArgs& a, int bg, int seg, float* tab, Sco
       float a_q[G], v_q;
       sc.score(q, i, ok, a_q, v_q);
       emit_scores<G>(a, a_q, v_q, ok, (uint32_t)(wr.n0 + i), sseg ? sseg + i : nullptr, lst,
-                     thr, nsel);
+                     thrf, nsel);
     }
   }
   if (a.select && lane == 0) {

@@ -66,18 +66,21 @@ __global__ __launch_bounds__(kFilterThreads) void topk_hist_kernel(
 // the LDS copy when the row's candidates fit there, else from memory.
 struct RowLists {
   const uint2* glob;      // row's list area (sub-list s at s * sub_len)
-  const uint2* cache;     // LDS copy of the first `cached` entries
+  const uint2* cache;     // LDS copy of the first `cached` entries (order keys)
   uint32_t cached;
   const uint32_t* off;    // sub-list offsets in the concatenation (LDS)
   int subs;
   int64_t sub_len;
+  bool score_bits;        // glob holds (score bits, index): map to order keys
   __device__ __forceinline__ uint2 from_memory(uint32_t p) const {
     int lo = 0, hi = subs - 1;  // last sub-list with off[s] <= p
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (off[mid] <= p) lo = mid; else hi = mid - 1;
     }
-    return glob[(int64_t)lo * sub_len + (p - off[lo])];
+    uint2 e = glob[(int64_t)lo * sub_len + (p - off[lo])];
+    if (score_bits) e.x = float_order_key(__uint_as_float(e.x));
+    return e;
   }
   __device__ __forceinline__ uint2 operator()(uint32_t p) const {
     return p < cached ? cache[p] : from_memory(p);
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
   const uint32_t need1 = (uint32_t)kk - res[1];
   const uint32_t total = sublist_offsets<NT>(sub_cnt + (int64_t)row * subs, subs, sh.off,
                                              sh.scratch);
-  RowLists rl{lists + (int64_t)row * n, sh.cache, 0u, sh.off, subs, sub_len};
+  RowLists rl{lists + (int64_t)row * n, sh.cache, 0u, sh.off, subs, sub_len, false};
   cache_candidates<NT>(rl, sh.cache, total);
   if (total <= rl.cached)
     select_and_emit<NT>(CacheAt{sh.cache}, total, (uint32_t)kk, 1, b1, need1, 0u, sh,
@@ -333,10 +336,12 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
   // candidates into LDS (as far as they fit), counted into the first-digit
   // histogram when they reach T: each wave copies whole sub-lists, eight of
   // them per round, 64 entries of each per batch of loads
-  RowLists rl{glob, sh.cache, 0u, sh.off, a.subs, a.sub_len};
+  RowLists rl{glob, sh.cache, 0u, sh.off, a.subs, a.sub_len, true};
   {
     const uint32_t cached = min(total, (uint32_t)kRefineCache);
-    auto take = [&](const uint2& e, uint32_t p) {
+    // the score kernel stores (score bits, index): cached as (order key, index)
+    auto take = [&](const uint2& s, uint32_t p) {
+      const uint2 e = make_uint2(float_order_key(__uint_as_float(s.x)), s.y);
       if (p < cached) sh.cache[p] = e;
       if (e.x >= tmax) atomicAdd(&sh.h[e.x >> 21], 1u);
     };
