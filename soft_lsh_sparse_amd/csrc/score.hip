@@ -721,12 +721,14 @@ struct RotScorer {
       w[4 * k] = pf[q][k].x; w[4 * k + 1] = pf[q][k].y;
       w[4 * k + 2] = pf[q][k].z; w[4 * k + 3] = pf[q][k].w;
     }
+    // rotated before the next ids are requested into the same registers
+    // (the rotation's results are fresh registers: no copies of the buffer)
+    rotate_bytes<LW>(w, __ballot(r & 4), __ballot(r & 8), rb);
     vn = pf_vn[q];
     if (i + kWaveStep < we) load(q, i + kWaveStep);
 #pragma unroll
     for (int j = 0; j < G; ++j) acc[j] = 0.f;
     if (!valid) return;
-    rotate_bytes<LW>(w, __ballot(r & 4), __ballot(r & 8), rb);
 #pragma unroll
     for (int t = 0; t < L; ++t) {
       // P bits of byte t: ids are < 2^P, so this never leaves the table
