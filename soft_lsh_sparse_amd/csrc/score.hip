@@ -111,6 +111,16 @@ __device__ __forceinline__ void fence_chunk(float (&acc)[G], uint32_t (&w)[LW], 
   for (int k = k0 + 1; k < k1; ++k) asm volatile("" : "+v"(w[k]) : "v"(w[k0]));
 }
 
+// Buffer resource over `bytes` bytes from base (raw, untyped accesses):
+// loads and stores through it take a 32-bit lane offset and no 64-bit
+// address arithmetic. base must be the same in every lane.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
+
 template <int G>
 __device__ __forceinline__ void lds_load_group(const float* p, float (&o)[G]) {
   if constexpr (G == 4) {
@@ -213,8 +223,8 @@ __host__ __device__ inline size_t build_weights_region(int L, int P, int G) {
 template <int G>
 __device__ __forceinline__ void emit_scores(const ScoreArgs& a, const float (&acc)[G], float vn,
                                             bool valid, uint32_t key, float* sk,
-                                            uint2* const (&lst)[G], const float (&thrf)[G],
-                                            uint32_t (&cnt)[G]) {
+                                            const __amdgpu_buffer_rsrc_t (&lst)[G],
+                                            const float (&thrf)[G], uint32_t (&cnt)[G]) {
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     const float sc = vn * acc[j];
@@ -222,7 +232,10 @@ __device__ __forceinline__ void emit_scores(const ScoreArgs& a, const float (&ac
     if (a.select) {
       const bool pass = valid && sc >= thrf[j];
       const uint64_t bal = __ballot(pass);
-      if (pass) lst[j][cnt[j] + lane_prefix(bal)] = make_uint2(__float_as_uint(sc), key);
+      if (pass) {
+        const u32x2_t e = {__float_as_uint(sc), key};
+        __builtin_amdgcn_raw_buffer_store_b64(e, lst[j], (cnt[j] + lane_prefix(bal)) * 8u, 0, 0);
+      }
       cnt[j] += (uint32_t)__popcll(bal);
     }
   }
@@ -605,12 +618,12 @@ __device__ void score_block(const ScoreArgs& a, int bg, int seg, float* tab, Sco
   }
   uint32_t thr[G], nsel[G];
   float thrf[G];
-  uint2* lst[G];
+  __amdgpu_buffer_rsrc_t lst[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     thr[j] = 0u;
     nsel[j] = 0u;
-    lst[j] = nullptr;
+    lst[j] = raw_rsrc(nullptr, 0u);
   }
   if (a.select) {
     const uint32_t m = threshold_rank(a.kk, a.n_keys, wr.first_step_keys());
@@ -626,12 +639,13 @@ __device__ void score_block(const ScoreArgs& a, int bg, int seg, float* tab, Sco
     for (int j = 0; j < G; ++j) {
       const int64_t row = (int64_t)b * a.Hq + (int64_t)g * G + j;
       if (threadIdx.x == 0) a.thr[row * a.segs + seg] = thr[j];
-      // the wave's sub-list base, held in scalar registers (the stores then
-      // take a 32-bit lane offset)
+      // the wave's sub-list as a buffer in scalar registers (the stores then
+      // take a 32-bit lane offset); at most wlen entries
       const uint64_t base = reinterpret_cast<uint64_t>(a.lists + row * a.n_keys + wr.n0 + wr.wb);
       const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
       const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
-      lst[j] = reinterpret_cast<uint2*>(((uint64_t)hi << 32) | lo);
+      lst[j] = raw_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo),
+                        (uint32_t)wr.wlen * 8u);
     }
   }
 #pragma unroll
@@ -670,8 +684,7 @@ template <int G, int LW>
 struct RotScorer {
   static constexpr int L = LW * 4;
   static constexpr int kChunk = 64 / G;  // lookups per dependency step (a multiple of 4)
-  const uint8_t* idseg;
-  const float* vseg;
+  __amdgpu_buffer_rsrc_t idseg, vseg;  // the segment's id rows and norms
   const float* tab;
   int P, we, wb;
   uint4 pf[kPrefetch][LW / 4];
@@ -680,9 +693,10 @@ struct RotScorer {
 
   __device__ RotScorer(const ScoreArgs& a, int bg, const WaveRange& wr, const float* tab_)
       : tab(tab_), P(a.P), we(wr.we), wb(wr.wb) {
-    // block-uniform bases of this segment; per-thread offsets stay 32-bit
-    idseg = a.ids + ((int64_t)bg * a.stride + wr.n0) * L;
-    vseg = a.vnorm + (int64_t)bg * a.stride + wr.n0;
+    // block-uniform bases of this segment (buffers: per-thread offsets stay
+    // 32-bit, seg_len * L < 2^31 bytes)
+    idseg = raw_rsrc(a.ids + ((int64_t)bg * a.stride + wr.n0) * L, (uint32_t)wr.cnt * L);
+    vseg = raw_rsrc(a.vnorm + (int64_t)bg * a.stride + wr.n0, (uint32_t)wr.cnt * 4u);
     // n0 + wb is a multiple of 16, so every key of this lane has the same
     // rotation r = key index mod 16 and the same two bases
     const int lane = threadIdx.x & 63;
@@ -699,10 +713,12 @@ struct RotScorer {
   }
 
   __device__ __forceinline__ void load(int q, int i) {
-    const uint4* src = reinterpret_cast<const uint4*>(idseg + i * L);
 #pragma unroll
-    for (int k = 0; k < LW / 4; ++k) pf[q][k] = src[k];
-    pf_vn[q] = vseg[i];
+    for (int k = 0; k < LW / 4; ++k) {
+      const u32x4v_t x = __builtin_amdgcn_raw_buffer_load_b128(idseg, (uint32_t)i * L + k * 16, 0, 0);
+      pf[q][k] = make_uint4(x.x, x.y, x.z, x.w);
+    }
+    pf_vn[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vseg, (uint32_t)i * 4u, 0, 0));
   }
 
   __device__ __forceinline__ void prefetch() {
