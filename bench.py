@@ -193,8 +193,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE={world}); the SOCKET decode path has no multi-GPU "
-              f"implementation in this build", file=sys.stderr)
+              f"WORLD_SIZE={world}); the SOCKET decode path here has no multi-GPU "
+              f"implementation", file=sys.stderr)
         sys.exit(2)
 
     import torch

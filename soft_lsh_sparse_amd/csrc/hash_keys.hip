@@ -12,22 +12,21 @@
 //
 //  1. prep: R [d, C] is transposed to R^T [rows, d] (zero rows past C) in the
 //     workspace, and the fix-up counter is cleared.
-//  2. main: a persistent grid of two 4-wave blocks per CU. Every block walks
-//     32-key tiles; the K and V rows of the next three tiles are in flight
-//     into a 4-slot LDS ring (64 KB per block) through direct-to-LDS loads
-//     (global_load_lds_dwordx4, no registers held), so each CU keeps about
-//     100 KB of loads in flight while it computes. The projection y = K R runs
-//     on the matrix cores (v_mfma_f32_32x32x16_bf16, float32 accumulation of
-//     the exact bf16 products): every wave keeps up to 128 hyperplane
-//     columns of R^T in registers as the stationary A operand and reads the
-//     tile's K rows from LDS as the B operand (XOR-swizzled so the 8 lanes
-//     the LDS serves together hit 8 bank groups), so one lane ends with 16
-//     projections of one key. Their sign bits are packed with one funnel
-//     shift each; the A rows are permuted so that a lane's 16 bits are 16
-//     consecutive hyperplanes and one exchange between the two lane halves
-//     yields a 32-bit word of 32 consecutive sign bits. With P = 8 that word
-//     is four id bytes, stored directly. The value norms of the same tile are
-//     reduced from the V rows in LDS (bf16 dot2).
+//  2. main: one block of 8 waves per CU (two per SIMD). R^T of all the
+//     hyperplane columns sits in LDS in the order the MFMA A operand reads
+//     it (fragment (column tile, k-step) = 1 KB, conflict-free 16-byte
+//     reads); every wave owns its own 32-key tiles and loads their K and V
+//     half-rows straight into registers (the next tile's K while the
+//     current one is computed, the current tile's V for its value norms at
+//     the end), so no wave waits for another after the set-up. The
+//     projection y = K R runs on the matrix cores (v_mfma_f32_32x32x16_bf16,
+//     float32 accumulation of the exact bf16 products), one 32-column tile
+//     at a time, and the sign work of the previous column tile sits between
+//     its k-steps. One lane ends with 16 projections of one key; their sign
+//     bits are packed with one funnel shift each; the A rows are permuted so
+//     that a lane's 16 bits are 16 consecutive hyperplanes and one exchange
+//     between the two lane halves yields a 32-bit word of 32 consecutive
+//     sign bits. With P = 8 that word is four id bytes, stored directly.
 //  3. fix-up: a sign is certified when |y| exceeds the worst-case float32
 //     summation error 2*d*2^-24*|k|*max|r| (plus a floor for flushed
 //     denormals). Uncertain projections (about 1.5e-4 of them for random
@@ -37,7 +36,7 @@
 //     kernel recomputes each one from
 //     the bf16 inputs (float64 sum of exact products, certified, with a
 //     double-double fallback) and sets or clears that one bit with an atomic
-//     AND/OR. A block with an overflowing list (or any block with an uncertain
+//     AND/OR. A wave with an overflowing list (or any wave with an uncertain
 //     sign when id rows are not whole 4-byte words) has all its tiles
 //     re-hashed exactly by a fourth kernel (float64 / double-double, one
 //     thread per key and table), which exits at once when nothing
@@ -63,27 +62,13 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 #define SOCKET_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 constexpr int kTileKeys = 32;
-constexpr int kHashWaves = 4;        // one wave per SIMD; two blocks per CU
+constexpr int kHashWaves = 8;         // two waves per SIMD, one block per CU
 constexpr int kHashThreads = kHashWaves * 64;
-constexpr int kRing = 4;              // LDS slots per block: one tile computed, three in flight
-constexpr int kBlocksPerCU = 2;
-constexpr int kMaxTilesPerWave = 4;   // 4 x 32 hyperplane columns per wave
 constexpr int kMaxColWords = 16;      // L*P <= 512 bits per key
-constexpr int kRtRows = kHashWaves * kMaxTilesPerWave * 32;
+constexpr int kRtRows = kMaxColWords * 32;
 constexpr float kAbsFloor = 0x1p-100f;  // covers flushed float32 denormals
 // fix-up entry: (row << 21) | (16-column group << 16) | mask of its columns
 constexpr int kEntryRowShift = 21;
-
-template <int D>
-struct HashGeom {
-  static constexpr int S = D / 16;                        // MFMA k-steps of 16
-  static constexpr int CH = D / 8;                        // 16-byte chunks per row
-  static constexpr int kTileBytes = kTileKeys * D * 2;    // one matrix of a tile
-  static constexpr int kSlotBytes = 2 * kTileBytes;       // K then V
-  static constexpr int kSegs = kSlotBytes / 1024;         // 1 KB load segments per slot
-  static constexpr int kDmaPerWave = kSegs / kHashWaves;  // loads per wave per tile
-  static_assert(kSegs % kHashWaves == 0, "every wave issues the same number of loads");
-};
 
 struct HashArgs {
   const uint16_t* K;
@@ -91,56 +76,14 @@ struct HashArgs {
   const uint16_t* R;   // [d, C]
   const uint16_t* RT;  // [kRtRows, d], zero past C
   int64_t n_keys, stride;
-  int tph, n_tiles;  // tiles per head, tiles in total (< 2^31)
+  int tph, n_tiles;  // 32-key tiles per head, tiles in total (< 2^31)
   int L, P, C;
   uint8_t* ids;
   float* vnorm;
   unsigned long long* fix_list;  // [grid * kHashWaves][fix_cap] entries, one region per wave
   uint32_t* fix_count;           // [grid * kHashWaves] entries each wave appended
-  uint32_t fix_cap;  // per wave; 0: the block is re-hashed exactly when any sign is uncertain
+  uint32_t fix_cap;  // per wave; 0: the wave's tiles are re-hashed exactly when any sign is uncertain
 };
-
-// s_waitcnt with only the vector-memory counter limited (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Block barrier that orders LDS only: the wave's LDS operations complete,
-// then all waves meet. (__syncthreads would also drain every outstanding
-// global load, which is exactly what the ring keeps in flight.)
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// 16-byte LDS reads and their completion in one asm block: the ring is
-// filled by direct-to-LDS loads whose progress the compiler cannot see, so
-// the kernel orders these reads itself (wait + barrier before them).
-__device__ __forceinline__ void lds_read4(const uint32_t (&addr)[4], u32x4_t (&o)[4]) {
-  asm volatile(
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %5\n\t"
-      "ds_read_b128 %2, %6\n\t"
-      "ds_read_b128 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
-      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3])
-      : "memory");
-}
-
-__device__ __forceinline__ u32x4_t lds_read1(uint32_t addr) {
-  u32x4_t o;
-  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(o) : "v"(addr) : "memory");
-  return o;
-}
-
-// Byte offset of a pointer into LDS, as DS instructions address it.
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  typedef __attribute__((address_space(3))) const unsigned char lds_uchar;
-  return (uint32_t)(uintptr_t)(lds_uchar*)p;
-}
 
 __device__ __forceinline__ float sumsq_bf16x2(uint32_t w, float acc) {
   const bf16x2_t v = __builtin_bit_cast(bf16x2_t, w);
@@ -163,71 +106,21 @@ __device__ __forceinline__ uint32_t extract_bits(const uint32_t* row, int off, i
   return (uint32_t)(x >> b) & ((1u << P) - 1u);
 }
 
-// A row m of a 32-column MFMA tile holds hyperplane column jmap(m) of the
-// tile. With the D layout (lane (n, h) holds rows (v/4)*8 + h*4 + v%4,
-// v = 0..15) this gives lane half h the 16 consecutive columns h*16 + v.
-__device__ __forceinline__ int jmap(int m) {
-  return ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3);
+// Row m of a 32-column MFMA tile holds hyperplane column
+// ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3) of the tile. With the D
+// layout (lane (n, h) holds rows (v/4)*8 + h*4 + v%4, v = 0..15) this gives
+// lane half h the 16 consecutive columns h*16 + v. jmap_inv: the row of
+// column j.
+__device__ __forceinline__ int jmap_inv(int j) {
+  return (((j >> 2) & 3) << 3) | (((j >> 4) & 1) << 2) | (j & 3);
 }
 
-// K and V rows of tile `tile` into one ring slot (K at byte 0, V at
-// kTileBytes). Wave w loads the 1 KB segments w, w + kHashWaves, ... of
-// each matrix; lane i fills 16-byte position i of a segment. K rows are
-// stored XOR-swizzled: position q of row r holds chunk q ^ (r & 7).
-template <int D>
-struct DmaLane {
-  static constexpr int kSegsPerMatrix = HashGeom<D>::kDmaPerWave / 2;
-  // rows between a wave's consecutive segments (a multiple of 8, so the
-  // XOR swizzle of a position is the same in all of them)
-  static constexpr int kRowStep = kHashWaves * 64 / HashGeom<D>::CH;
-  static_assert(kSegsPerMatrix == 1 || kRowStep % 8 == 0, "swizzle period");
-  int r0;    // row of this lane's position in the wave's first segment
-  int koff;  // element offset of that position's K chunk in a full tile
+typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
 
-  __device__ __forceinline__ DmaLane(int wave, int lane) {
-    using G = HashGeom<D>;
-    const int p = wave * 64 + lane;
-    const int q = p % G::CH;
-    r0 = p / G::CH;
-    koff = r0 * D + (q ^ (r0 & 7)) * 8;
-  }
-};
-
-template <int D>
-__device__ __forceinline__ void dma_tile(const HashArgs& a, int tile, unsigned char* slot,
-                                         const DmaLane<D>& dl, int wave) {
-  using G = HashGeom<D>;
-  const int head = tile / a.tph;
-  const int64_t row0 = (int64_t)(tile - head * a.tph) * kTileKeys;
-  const int rows = (int)min<int64_t>(kTileKeys, a.n_keys - row0);
-  const uint16_t* kb = a.K + ((int64_t)head * a.stride + row0) * D;
-  const uint16_t* vb = a.V + ((int64_t)head * a.stride + row0) * D;
-  const int voff = (wave * 64 + (threadIdx.x & 63)) * 8;  // V is stored unswizzled
-  if (rows == kTileKeys) {
-#pragma unroll
-    for (int j = 0; j < DmaLane<D>::kSegsPerMatrix; ++j) {
-      const int g = wave + j * kHashWaves;
-      const int step = j * DmaLane<D>::kRowStep * D;
-      __builtin_amdgcn_global_load_lds((const void*)(kb + dl.koff + step),
-                                       SOCKET_LDS(slot + g * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vb + voff + step),
-                                       SOCKET_LDS(slot + G::kTileBytes + g * 1024), 16, 0, 0);
-    }
-  } else {
-    // last tile of a head: rows past the end re-read row 0 (same count of
-    // loads, so the wait counts stay exact)
-#pragma unroll
-    for (int j = 0; j < DmaLane<D>::kSegsPerMatrix; ++j) {
-      const int g = wave + j * kHashWaves;
-      const int r = dl.r0 + j * DmaLane<D>::kRowStep;
-      const int step = j * DmaLane<D>::kRowStep * D;
-      const int back = r < rows ? 0 : r * D;  // row r -> row 0
-      __builtin_amdgcn_global_load_lds((const void*)(kb + dl.koff + step - back),
-                                       SOCKET_LDS(slot + g * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vb + voff + step - back),
-                                       SOCKET_LDS(slot + G::kTileBytes + g * 1024), 16, 0, 0);
-    }
-  }
+// Byte offset of a pointer into LDS, as DS instructions address it.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  typedef __attribute__((address_space(3))) const unsigned char lds_uchar;
+  return (uint32_t)(uintptr_t)(lds_uchar*)p;
 }
 
 struct TileRows {
@@ -241,217 +134,234 @@ __device__ __forceinline__ TileRows tile_rows(const HashArgs& a, int tile) {
   return {(int64_t)head * a.stride + row0, (int)min<int64_t>(kTileKeys, a.n_keys - row0)};
 }
 
-// One 32-key tile from its ring slot: projections on the matrix cores, the
-// certified sign bits and the ids, the key norms (from the B operand already
-// in registers) and the value norms.
-template <int D, int TPW, bool kWordIds>
-__device__ __forceinline__ void hash_tile(const HashArgs& a, int tile, const unsigned char* slot,
-                                          const bf16x8_t (&ra)[TPW][HashGeom<D>::S],
-                                          const float (&rmax)[TPW], uint32_t* bitvec,
-                                          uint32_t& fix_n, unsigned long long* fix_list,
-                                          int wave, int lane) {
-  using G = HashGeom<D>;
-  constexpr int S = G::S;
-  constexpr float kGamma = 2.0f * D * 0x1p-24f;
+// Half-rows of one lane for a 32-key tile: lane (kn, kh) holds elements
+// kh*d/2 .. kh*d/2 + d/2 - 1 of row kn of K (the B operand of k-steps
+// 0..S-1) or of V (rows past the end of the head repeat its last row).
+template <int D>
+struct HalfRows {
+  u32x4_t q[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ void load_half_rows(const HashArgs& a, const uint16_t* base, int tile,
+                                               HalfRows<D>& r, int lane) {
   const int kn = lane & 31, kh = lane >> 5;
-  const uint32_t sbase = lds_offset(slot);
   const TileRows tr = tile_rows(a, tile);
-  const int CT = (a.C + 31) >> 5;
-
-  // value norms: wave w takes keys w*8 .. w*8+7, 8 lanes per key
-  {
-    const int vkey = wave * 8 + (lane >> 3);
-    u32x4_t vw[G::CH / 8];
-    if constexpr (G::CH / 8 == 2) {
-      const uint32_t addr[4] = {
-          sbase + G::kTileBytes + vkey * (D * 2) + ((lane & 7) << 4),
-          sbase + G::kTileBytes + vkey * (D * 2) + (((lane & 7) + 8) << 4),
-          sbase + G::kTileBytes + vkey * (D * 2) + ((lane & 7) << 4),
-          sbase + G::kTileBytes + vkey * (D * 2) + (((lane & 7) + 8) << 4)};
-      u32x4_t t4[4];
-      lds_read4(addr, t4);
-      vw[0] = t4[0];
-      vw[1] = t4[1];
-    } else {
-      vw[0] = lds_read1(sbase + G::kTileBytes + vkey * (D * 2) + ((lane & 7) << 4));
-    }
-    float vs = 0.f;
+  const int64_t row = tr.grow0 + min(kn, tr.rows - 1);
+  const uint4* p = reinterpret_cast<const uint4*>(base + row * D + kh * (D / 2));
 #pragma unroll
-    for (int j = 0; j < G::CH / 8; ++j) vs = sumsq_bf16x8(vw[j], vs);
-    vs += dpp_f32<0xB1>(vs);   // lanes i ^ 1
-    vs += dpp_f32<0x4E>(vs);   // lanes i ^ 2
-    vs += dpp_f32<0x141>(vs);  // the other quad of the half-row
-    if ((lane & 7) == 0 && vkey < tr.rows)
-      a.vnorm[tr.grow0 + vkey] = __builtin_amdgcn_sqrtf(vs);
-  }
-
-  // Column tiles in pairs (two accumulators live at a time): the B operand
-  // (chunks kh*S + s of key row kn; the A rows use the same map) is read
-  // four k-steps at a time, again for every pair. The first pass also sums
-  // the squared key entries. (Column tiles past C multiply zero rows of
-  // R^T; their bits are dropped.)
-  const bool row_ok = kn < tr.rows;
-  uint32_t word[TPW];  // 32 consecutive sign bits, in both lanes of a key
-  float ksq = 0.f, thr_k = 0.f;
-#pragma unroll
-  for (int tp = 0; tp < TPW; tp += 2) {
-    f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
-#pragma unroll
-    for (int s0 = 0; s0 < S; s0 += 4) {
-      uint32_t addr[4];
-      u32x4_t kw[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        addr[s] = sbase + kn * (D * 2) + (((kh * S + s0 + s) ^ (kn & 7)) << 4);
-      lds_read4(addr, kw);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          if (tp + i < TPW)
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                ra[tp + i][s0 + s], __builtin_bit_cast(bf16x8_t, kw[s]), acc[i], 0, 0, 0);
-        if (tp == 0) ksq = sumsq_bf16x8(kw[s], ksq);
-      }
-    }
-    if (tp == 0) {
-      ksq += __builtin_bit_cast(float, xor32_u32(__builtin_bit_cast(uint32_t, ksq)));
-      // an upper bound is enough: the hardware square root (1 ulp) rounded up
-      thr_k = kGamma * 1.000001f * __builtin_amdgcn_sqrtf(ksq);
-    }
-
-    // sign bits, certification, uncertain signs
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int t = tp + i;
-      if (t >= TPW) break;
-      const int ct = wave * TPW + t;
-      float mn = fabsf(acc[i][0]);
-#pragma unroll
-      for (int v = 1; v < 16; ++v) mn = fminf(mn, fabsf(acc[i][v]));
-      uint32_t h = 0;
-#pragma unroll
-      for (int v = 15; v >= 0; --v)
-        h = __builtin_amdgcn_alignbit(h, __float_as_uint(acc[i][v]), 31);
-      h = ~h & 0xffffu;  // bit v: projection onto column ct*32 + kh*16 + v is > 0
-      const float thr = thr_k * rmax[t] + kAbsFloor;
-      // Rare: some lanes hold projections too close to zero for their float32
-      // sign. Each such key lists its group of 16 columns with the mask of
-      // uncertain ones (float32 signs stay in h) in the wave's own region:
-      // slots from a ballot prefix count, no atomics. The count runs on past
-      // the capacity, which marks the block for the exact re-hash.
-      const bool cand = row_ok && ct < CT && mn <= thr;
-      if (__ballot(cand) != 0) {
-        const int c0 = ct * 32 + kh * 16;
-        uint32_t fm = 0;
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (fabsf(acc[i][v]) <= thr) fm |= 1u << v;
-        const int valid = min(max(a.C - c0, 0), 16);  // columns of this lane below C
-        fm &= valid >= 16 ? 0xffffu : (1u << valid) - 1u;
-        if (!cand) fm = 0;
-        const uint64_t bal = __ballot(fm != 0);
-        const uint32_t pos =
-            fix_n + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-        if (fm != 0 && pos < a.fix_cap)
-          fix_list[pos] = ((unsigned long long)(tr.grow0 + kn) << kEntryRowShift) |
-                          ((unsigned long long)(c0 >> 4) << 16) | fm;
-        fix_n += (uint32_t)__popcll(bal);
-      }
-      const uint32_t o = xor32_u32(h);
-      word[t] = kh ? (o | (h << 16)) : (h | (o << 16));
-    }
-  }
-  if constexpr (kWordIds) {
-    // P == 8: word ct holds the id bytes of tables 4ct .. 4ct+3
-    if (row_ok) {
-      uint32_t* orow = reinterpret_cast<uint32_t*>(a.ids + (tr.grow0 + kn) * a.L);
-#pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        const int ct = wave * TPW + t;
-        if ((TPW == 1 ? 0 : (t & 1)) == kh && ct < CT) orow[ct] = word[t];
-      }
-    }
-  } else {
-    if (kh == 0) {
-#pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        const int ct = wave * TPW + t;
-        if (ct < CT) bitvec[kn * kMaxColWords + ct] = word[t];
-      }
-    }
-    lds_barrier();
-    uint8_t* obase = a.ids + tr.grow0 * a.L;
-    const int tid = wave * 64 + lane;
-    for (int q = tid; q < kTileKeys * a.L; q += kHashThreads) {
-      const int r = q / a.L, l = q - r * a.L;
-      if (r < tr.rows)
-        obase[(int64_t)r * a.L + l] =
-            (uint8_t)extract_bits(bitvec + r * kMaxColWords, l * a.P, a.P);
-    }
-    // the next writer of bitvec is past another barrier
+  for (int s = 0; s < D / 16; ++s) {
+    const uint4 x = p[s];
+    r.q[s] = u32x4_t{x.x, x.y, x.z, x.w};
   }
 }
 
-template <int D, int TPW, bool kWordIds>
-__global__ __launch_bounds__(kHashThreads, kBlocksPerCU) void hash_keys_bf16_kernel(HashArgs a) {
-  using G = HashGeom<D>;
-  constexpr int S = G::S;
-  constexpr int kWaitSteady = (kRing - 2) * G::kDmaPerWave;
-  __shared__ __align__(16) unsigned char ring[kRing * G::kSlotBytes];
-  __shared__ uint32_t bitvec[kWordIds ? 1 : kTileKeys * kMaxColWords];
+// Sign bits and the certification test of a column tile's projections
+// (acc, lane (kn, kh): the 16 columns ct*32 + kh*16 + v of key kn), in S
+// steps of 16 / S projections each, so that every step fits beside one
+// k-step of the next column tile's MFMAs: word collects the sign bits
+// (complemented at the end) and mn the smallest magnitude.
+struct ColSigns {
+  uint32_t word;
+  float mn;
+};
+
+template <int S>
+__device__ __forceinline__ void col_signs_step(const f32x16_t& acc, int s, ColSigns& cs) {
+  constexpr int kPer = 16 / S;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int v = 15 - (s * kPer + i);
+    const float m = fabsf(acc[v]);
+    cs.mn = (s == 0 && i == 0) ? m : fminf(cs.mn, m);
+    cs.word = __builtin_amdgcn_alignbit((s == 0 && i == 0) ? 0u : cs.word, __float_as_uint(acc[v]), 31);
+  }
+}
+
+// The signs of column tile ct of a tile: its 32-bit word of sign bits (the
+// same in both lanes of a key) and, rarely, list entries for uncertain ones
+// (see the file comment). Returns the word.
+__device__ __forceinline__ uint32_t col_finish(const HashArgs& a, const f32x16_t& acc,
+                                               const ColSigns& cs, int ct, float thr,
+                                               bool row_ok, int64_t grow, int CT,
+                                               uint32_t& fix_n, unsigned long long* fix_list,
+                                               int lane) {
+  const int kh = lane >> 5;
+  const uint32_t h = ~cs.word & 0xffffu;  // bit v: projection onto column ct*32 + kh*16 + v is > 0
+  const bool cand = row_ok && ct < CT && cs.mn <= thr;
+  // Rare: some lanes hold projections too close to zero for their float32
+  // sign. Each such key lists its group of 16 columns with the mask of
+  // uncertain ones (float32 signs stay in the ids) in the wave's own
+  // region: slots from a ballot prefix count, no atomics. The count runs on
+  // past the capacity, which marks the wave for the exact re-hash.
+  if (__ballot(cand) != 0) {
+    const int c0 = ct * 32 + kh * 16;
+    uint32_t fm = 0;
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if (fabsf(acc[v]) <= thr) fm |= 1u << v;
+    const int valid = min(max(a.C - c0, 0), 16);  // columns of this lane below C
+    fm &= valid >= 16 ? 0xffffu : (1u << valid) - 1u;
+    if (!cand) fm = 0;
+    const uint64_t bal = __ballot(fm != 0);
+    const uint32_t pos =
+        fix_n + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    if (fm != 0 && pos < a.fix_cap)
+      fix_list[pos] = ((unsigned long long)grow << kEntryRowShift) |
+                      ((unsigned long long)(c0 >> 4) << 16) | fm;
+    fix_n += (uint32_t)__popcll(bal);
+  }
+  const uint32_t o = xor32_u32(h);
+  return kh ? (o | (h << 16)) : (h | (o << 16));
+}
+
+// Main kernel: one block of 8 waves per CU. R^T of all NCT column tiles
+// sits in LDS in the order the A operand is read (fragment (ct, s) = 1 KB,
+// lane l at 16*l: conflict-free 16-byte reads). Every wave owns the 32-key
+// tiles part, part + parts, ... (part = block * 8 + wave) and needs no
+// other wave after the set-up: the next tile's K and V half-rows are in
+// flight into registers while the current one is computed; the two waves
+// of a SIMD take turns on its matrix core. Per tile: the key and value
+// norms, then for every column tile the S k-steps on the matrix cores
+// interleaved with the sign work of the previous column tile.
+template <int D, int NCT, bool kWordIds>
+__global__ __launch_bounds__(kHashThreads, 1) void hash_keys_bf16_kernel(HashArgs a) {
+  constexpr int S = D / 16;
+  constexpr int CH = D / 8;          // 16-byte chunks per row
+  constexpr float kGamma = 2.0f * D * 0x1p-24f;
+  __shared__ u32x4_t frag[NCT * S * 64];
+  __shared__ float rmax_s[NCT];
+  __shared__ uint32_t bitvec[kWordIds ? 1 : kHashWaves * kTileKeys * kMaxColWords];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kn = lane & 31, kh = lane >> 5;
-  const int nb = gridDim.x;
-  const int b = blockIdx.x;
-  if (b >= a.n_tiles) return;
-  const int iters = (a.n_tiles - b + nb - 1) / nb;  // tiles b, b + nb, ...
-  const int part = b * kHashWaves + wave;  // this wave's list region
+  const int CT = (a.C + 31) >> 5;
+  const int parts = gridDim.x * kHashWaves;
+  const int part = blockIdx.x * kHashWaves + wave;  // this wave's tiles and list region
   unsigned long long* const fix_list = a.fix_list + (size_t)part * a.fix_cap;
   uint32_t fix_n = 0;  // wave-uniform count of listed entries
 
-  // stationary A operand: R^T rows of this wave's column tiles
-  bf16x8_t ra[TPW][S];
-  float rmax[TPW];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int col = (wave * TPW + t) * 32 + jmap(kn);
-    const uint4* src = reinterpret_cast<const uint4*>(a.RT + (int64_t)col * D);
+  // the first tile's key rows are in flight during the set-up
+  HalfRows<D> ka, kb;
+  load_half_rows<D>(a, a.K, min(part, a.n_tiles - 1), ka, lane);
+
+  // set-up: thread t moves R^T row t (hyperplane column t) into its
+  // fragment places and takes its squared norm; the largest of each column
+  // tile (rounded up) bounds the projection errors
+  for (int r = threadIdx.x; r < NCT * 32; r += kHashThreads) {
+    const uint4* src = reinterpret_cast<const uint4*>(a.RT + (int64_t)r * D);
+    const int ct = r >> 5, m = jmap_inv(r & 31);
     float sq = 0.f;
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const uint4 w = src[kh * S + s];
-      const u32x4_t wv = {w.x, w.y, w.z, w.w};
-      sq = sumsq_bf16x8(wv, sq);
-      ra[t][s] = __builtin_bit_cast(bf16x8_t, wv);
+    for (int c = 0; c < CH; ++c) {
+      const uint4 x = src[c];
+      const u32x4_t w = {x.x, x.y, x.z, x.w};
+      sq = sumsq_bf16x8(w, sq);
+      const int h = c / S, st = c % S;
+      frag[(ct * S + st) * 64 + h * 32 + m] = w;
     }
-    sq += __shfl_xor(sq, 32, kWave);
-    // the bound takes the largest column norm of the tile, rounded up
-    rmax[t] = sqrtf(group_max<64>(sq)) * (1.0f + 0x1p-20f);
+    const float mx = group_max<32>(sq);  // the 32 columns of the tile are 32 aligned lanes
+    if ((r & 31) == 0) rmax_s[ct] = sqrtf(mx) * (1.0f + 0x1p-20f);
   }
-
-  const DmaLane<D> dl(wave, lane);
+  __syncthreads();
+  float rmax[NCT];
 #pragma unroll
-  for (int j = 0; j < kRing - 1; ++j)
-    if (j < iters) dma_tile<D>(a, b + j * nb, ring + j * G::kSlotBytes, dl, wave);
+  for (int ct = 0; ct < NCT; ++ct)
+    rmax[ct] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                             __builtin_bit_cast(int, rmax_s[ct])));
+  const u32x4_t* const fl0 = frag + lane;
 
-  for (int it = 0; it < iters; ++it) {
-    // this wave's loads into the slot of tile `it` are done once at most the
-    // loads of the later tiles are outstanding; the barrier then makes every
-    // wave's part visible and frees the slot computed last round
-    if (it + kRing - 2 < iters)
-      wait_vmcnt<kWaitSteady>();
-    else
-      wait_vmcnt<0>();
-    lds_barrier();
-    if (it + kRing - 1 < iters)
-      dma_tile<D>(a, b + (it + kRing - 1) * nb,
-                  ring + ((it + kRing - 1) % kRing) * G::kSlotBytes, dl, wave);
-    hash_tile<D, TPW, kWordIds>(a, b + it * nb, ring + (it % kRing) * G::kSlotBytes, ra, rmax,
-                                bitvec, fix_n, fix_list, wave, lane);
+  // One tile with its key rows in cur, while the next tile's key rows load
+  // into nxt (after the last tile the last tile's rows again, unused) and
+  // the tile's value rows arrive for its value norms at the end.
+  auto step = [&](const HalfRows<D>& cur, HalfRows<D>& nxt, int tile) {
+    HalfRows<D> vr;
+    load_half_rows<D>(a, a.V, tile, vr, lane);
+    load_half_rows<D>(a, a.K, min(tile + parts, a.n_tiles - 1), nxt, lane);
+    const TileRows tr = tile_rows(a, tile);
+    const bool row_ok = kn < tr.rows;
+    const int64_t grow = tr.grow0 + kn;
+    // the fragments are read again for every tile (not hoisted out of the
+    // loop into registers)
+    uint32_t flo = lds_offset(fl0);
+    asm volatile("" : "+v"(flo));
+    const lds_u32x4_t* fl = reinterpret_cast<const lds_u32x4_t*>((uintptr_t)flo);
+
+    // key norm (each lane half holds half of the row); an upper bound is
+    // enough: the hardware square root (1 ulp) rounded up
+    float ks = 0.f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) ks = sumsq_bf16x8(cur.q[s], ks);
+    ks += __builtin_bit_cast(float, xor32_u32(__builtin_bit_cast(uint32_t, ks)));
+    const float thr_k = kGamma * 1.000001f * __builtin_amdgcn_sqrtf(ks);
+
+    // column tiles: the k-steps of ct on the matrix cores while the signs
+    // of ct - 1 are packed
+    uint32_t words[NCT / 2];  // lane half kh: the words of column tiles kh*NCT/2 + i
+    f32x16_t prev = {};
+#pragma unroll
+    for (int ct = 0; ct <= NCT; ++ct) {
+      f32x16_t acc = {};
+      ColSigns cs;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        if (ct < NCT)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, fl[(ct * S + s) * 64]),
+              __builtin_bit_cast(bf16x8_t, cur.q[s]), acc, 0, 0, 0);
+        if (ct > 0) col_signs_step<S>(prev, s, cs);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (ct > 0) {
+        const int pc = ct - 1;
+        const uint32_t w = col_finish(a, prev, cs, pc, thr_k * rmax[pc] + kAbsFloor, row_ok,
+                                      grow, CT, fix_n, fix_list, lane);
+        if (pc / (NCT / 2) == kh) words[pc % (NCT / 2)] = w;  // both halves hold the word
+      }
+      prev = acc;
+    }
+
+    float vs = 0.f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) vs = sumsq_bf16x8(vr.q[s], vs);
+    vs += __builtin_bit_cast(float, xor32_u32(__builtin_bit_cast(uint32_t, vs)));
+    if (kh == 0 && row_ok) a.vnorm[grow] = __builtin_amdgcn_sqrtf(vs);
+
+    if constexpr (kWordIds) {
+      // P == 8: word ct holds the id bytes of tables 4ct .. 4ct+3
+      if (row_ok) {
+        uint32_t* orow = reinterpret_cast<uint32_t*>(a.ids + grow * a.L);
+#pragma unroll
+        for (int i = 0; i < NCT / 2; ++i) {
+          const int ct = kh * (NCT / 2) + i;
+          if (ct < CT) orow[ct] = words[i];
+        }
+      }
+    } else {
+      // any P: the words through this wave's LDS rows, then id bytes
+      uint32_t* bv = bitvec + wave * kTileKeys * kMaxColWords;
+#pragma unroll
+      for (int i = 0; i < NCT / 2; ++i) bv[kn * kMaxColWords + kh * (NCT / 2) + i] = words[i];
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes are done
+      __builtin_amdgcn_wave_barrier();
+      uint8_t* obase = a.ids + tr.grow0 * a.L;
+      for (int q = lane; q < kTileKeys * a.L; q += 64) {
+        const int r = q / a.L, l = q - r * a.L;
+        if (r < tr.rows)
+          obase[(int64_t)r * a.L + l] = (uint8_t)extract_bits(bv + r * kMaxColWords, l * a.P, a.P);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+    }
+  };
+  // tiles in pairs, so that the two row buffers swap roles without copies
+  int tile = part;
+  for (; tile + parts < a.n_tiles; tile += 2 * parts) {
+    step(ka, kb, tile);
+    step(kb, ka, tile + parts);
   }
+  if (tile < a.n_tiles) step(ka, kb, tile);
   if (lane == 0) a.fix_count[part] = fix_n;
 }
 
@@ -558,23 +468,22 @@ __global__ __launch_bounds__(256) void hash_fixup_kernel(
   }
 }
 
-// Exact re-hash of the tiles of every main-kernel block whose list
+// Exact re-hash of the tiles of every main-kernel wave whose list
 // overflowed (count above the capacity; with capacity 0, any uncertain
 // sign): one thread per (key, table) recomputes the table's P projections
 // from the bf16 inputs in float64 (exact products; the sum of |products|
 // bounds the rounding) or, when that cannot decide, in double-double, and
-// rewrites the id byte. Blocks of parts without overflow exit at once.
+// rewrites the id byte. Block blk takes the waves of main-kernel block blk
+// and exits at once when none overflowed.
 template <int D>
 __global__ __launch_bounds__(256) void hash_redo_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ R, int64_t n_keys,
-    int64_t stride, int tph, int n_tiles, int nb, int L, int P, uint8_t* __restrict__ ids,
+    int64_t stride, int tph, int n_tiles, int parts, int L, int P, uint8_t* __restrict__ ids,
     const uint32_t* __restrict__ count, uint32_t cap) {
-  const int blk = blockIdx.x;
-  bool over = false;
-  for (int w = 0; w < kHashWaves; ++w) over |= count[blk * kHashWaves + w] > cap;
-  if (!over) return;
   const int C = L * P;
-  for (int tile = blk; tile < n_tiles; tile += nb) {
+  for (int part = blockIdx.x * kHashWaves; part < (int)(blockIdx.x + 1) * kHashWaves; ++part) {
+    if (count[part] <= cap) continue;  // uniform
+  for (int tile = part; tile < n_tiles; tile += parts) {
     const int head = tile / tph;
     const int64_t row0 = (int64_t)(tile - head * tph) * kTileKeys;
     const int rows = (int)min<int64_t>(kTileKeys, n_keys - row0);
@@ -605,6 +514,7 @@ __global__ __launch_bounds__(256) void hash_redo_kernel(
       }
       ids[(grow0 + r) * L + l] = (uint8_t)id;
     }
+  }
   }
 }
 
@@ -657,13 +567,13 @@ __global__ __launch_bounds__(256) void hash_keys_f32_kernel(
 
 // --------------------------------------------------------------- launchers
 
-constexpr int kMaxHashBlocks = 256 * kBlocksPerCU;
+constexpr int kMaxHashBlocks = 256;  // one per CU
 
 struct HashWs {
   uint16_t* rt;
   uint32_t* count;            // [kMaxHashBlocks * kHashWaves]
   unsigned long long* list;   // [kMaxHashBlocks * kHashWaves][cap]
-  uint32_t cap;               // entries per block
+  uint32_t cap;               // entries per wave
 };
 
 HashWs hash_ws_layout(void* ws, int64_t n_total, int d, int C) {
@@ -679,26 +589,21 @@ HashWs hash_ws_layout(void* ws, int64_t n_total, int d, int C) {
   return w;
 }
 
-template <int D, int TPW, bool kWordIds>
-void launch_main(const HashArgs& a, hipStream_t stream) {
-  // two blocks per CU (each ring takes 64 KB of the 160 KB of LDS)
-  const int grid = std::min(a.n_tiles, kMaxHashBlocks);
-  launch_kernel((hash_keys_bf16_kernel<D, TPW, kWordIds>), dim3(grid), dim3(kHashThreads), 0,
+template <int D, int NCT, bool kWordIds>
+void launch_main(const HashArgs& a, int grid, hipStream_t stream) {
+  launch_kernel((hash_keys_bf16_kernel<D, NCT, kWordIds>), dim3(grid), dim3(kHashThreads), 0,
                 stream, a);
 }
 
 template <int D>
-void launch_main_d(const HashArgs& a, int tpw, bool word_ids, hipStream_t stream) {
-  switch (tpw * 2 + (word_ids ? 1 : 0)) {
-#define SOCKET_HASH_CASE(t)                                            \
-  case 2 * t: launch_main<D, t, false>(a, stream); break;              \
-  case 2 * t + 1: launch_main<D, t, true>(a, stream); break;
-    SOCKET_HASH_CASE(1)
-    SOCKET_HASH_CASE(2)
-    SOCKET_HASH_CASE(3)
-    SOCKET_HASH_CASE(4)
-#undef SOCKET_HASH_CASE
-    default: break;
+void launch_main_d(const HashArgs& a, int grid, bool word_ids, hipStream_t stream) {
+  const int CT = (a.C + 31) / 32;
+  if (CT <= 8) {
+    if (word_ids) launch_main<D, 8, true>(a, grid, stream);
+    else launch_main<D, 8, false>(a, grid, stream);
+  } else {
+    if (word_ids) launch_main<D, 16, true>(a, grid, stream);
+    else launch_main<D, 16, false>(a, grid, stream);
   }
 }
 
@@ -747,14 +652,14 @@ hipError_t launch_hash_keys_bf16(const uint16_t* K, const uint16_t* V,
   a.fix_cap = word_rows ? w.cap : 0u;
 
   launch_kernel(hash_prep_kernel, dim3(64), dim3(256), 0, stream, R, C, d, w.rt);
-  const int CT = (C + 31) / 32;
-  const int tpw = (CT + kHashWaves - 1) / kHashWaves;
   const bool word_ids = P == 8 && word_rows;
+  // enough 8-wave blocks that every wave has a tile, at most one per CU
+  const int blocks = (int)std::min<int64_t>((a.n_tiles + kHashWaves - 1) / kHashWaves,
+                                            kMaxHashBlocks);
   if (d == 128)
-    launch_main_d<128>(a, tpw, word_ids, stream);
+    launch_main_d<128>(a, blocks, word_ids, stream);
   else
-    launch_main_d<64>(a, tpw, word_ids, stream);
-  const int blocks = std::min(a.n_tiles, kMaxHashBlocks);
+    launch_main_d<64>(a, blocks, word_ids, stream);
   if (a.fix_cap != 0) {
     const dim3 fgrid(blocks * kFixBlocksPerPart);
     if (d == 128)
@@ -766,10 +671,10 @@ hipError_t launch_hash_keys_bf16(const uint16_t* K, const uint16_t* V,
   }
   if (d == 128)
     launch_kernel(hash_redo_kernel<128>, dim3(blocks), dim3(256), 0, stream, K, R, n_keys,
-                  stride, a.tph, a.n_tiles, blocks, L, P, ids, w.count, a.fix_cap);
+                  stride, a.tph, a.n_tiles, blocks * kHashWaves, L, P, ids, w.count, a.fix_cap);
   else
     launch_kernel(hash_redo_kernel<64>, dim3(blocks), dim3(256), 0, stream, K, R, n_keys,
-                  stride, a.tph, a.n_tiles, blocks, L, P, ids, w.count, a.fix_cap);
+                  stride, a.tph, a.n_tiles, blocks * kHashWaves, L, P, ids, w.count, a.fix_cap);
   return hipGetLastError();
 }
 
