@@ -37,6 +37,14 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source additions. hash_keys.hip: the tile counter's answer is read a
+# tile after the request; the atomic optimizer would combine the request
+# across lanes and wait for the answer at once.
+FILE_FLAGS = {
+    "hash_keys.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+}
+
+
 def _hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -45,7 +53,7 @@ def _hipcc() -> str:
 
 
 def _compile(src: str, obj: str) -> None:
-    cmd = [_hipcc(), *COMMON_FLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

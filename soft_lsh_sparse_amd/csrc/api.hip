@@ -153,7 +153,7 @@ size_t socket_hash_keys_workspace_bytes(socket_dtype dtype, int64_t n_heads,
   if (dtype != SOCKET_DTYPE_BF16 || n_heads <= 0 || n_keys <= 0 || d <= 0 || L <= 0 ||
       P <= 0)
     return 0;
-  return hash_keys_bf16_workspace_bytes(n_heads * n_keys, d, L * P);
+  return hash_keys_bf16_workspace_bytes(n_heads, n_keys, d, L * P);
 }
 
 socket_status socket_hash_keys(const void* K, const void* V, const void* R,
@@ -185,7 +185,7 @@ socket_status socket_hash_keys(const void* K, const void* V, const void* R,
   if (dtype == SOCKET_DTYPE_BF16) {
     if (n_heads * ((n_keys + 31) / 32) >= ((int64_t)1 << 31))
       return fail(SOCKET_ERR_UNSUPPORTED, "bf16 hashing supports < 2^31 tiles of 32 keys");
-    const size_t need = hash_keys_bf16_workspace_bytes(n_heads * n_keys, d, L * P);
+    const size_t need = hash_keys_bf16_workspace_bytes(n_heads, n_keys, d, L * P);
     if (!workspace || workspace_bytes < need ||
         (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
       return fail(SOCKET_ERR_WORKSPACE,

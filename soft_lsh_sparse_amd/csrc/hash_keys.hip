@@ -83,6 +83,7 @@ struct HashArgs {
   unsigned long long* fix_list;  // [grid * kHashWaves][fix_cap] entries, one region per wave
   uint32_t* fix_count;           // [grid * kHashWaves] entries each wave appended
   uint32_t fix_cap;  // per wave; 0: the wave's tiles are re-hashed exactly when any sign is uncertain
+  int* owner;           // [n_tiles] the wave (list region) that hashed the tile
 };
 
 __device__ __forceinline__ float sumsq_bf16x2(uint32_t w, float acc) {
@@ -195,12 +196,15 @@ __device__ __forceinline__ uint32_t col_finish(const HashArgs& a, const f32x16_t
   // region: slots from a ballot prefix count, no atomics. The count runs on
   // past the capacity, which marks the wave for the exact re-hash.
   if (__ballot(cand) != 0) {
-    const int c0 = ct * 32 + kh * 16;
-    uint32_t fm = 0;
+    // (values the compiler would otherwise compute once for every column
+    // tile ahead of the loop and keep in registers)
+    int C = a.C, khl = kh;
+    asm volatile("" : "+s"(C), "+v"(khl));
+    const int c0 = ct * 32 + khl * 16;
+    uint32_t fm = 0;  // (built by shifts: no mask constants held in registers)
 #pragma unroll
-    for (int v = 0; v < 16; ++v)
-      if (fabsf(acc[v]) <= thr) fm |= 1u << v;
-    const int valid = min(max(a.C - c0, 0), 16);  // columns of this lane below C
+    for (int v = 15; v >= 0; --v) fm = (fm << 1) | (fabsf(acc[v]) <= thr ? 1u : 0u);
+    const int valid = min(max(C - c0, 0), 16);  // columns of this lane below C
     fm &= valid >= 16 ? 0xffffu : (1u << valid) - 1u;
     if (!cand) fm = 0;
     const uint64_t bal = __ballot(fm != 0);
@@ -218,13 +222,16 @@ __device__ __forceinline__ uint32_t col_finish(const HashArgs& a, const f32x16_t
 
 // Main kernel: one block of 8 waves per CU. R^T of all NCT column tiles
 // sits in LDS in the order the A operand is read (fragment (ct, s) = 1 KB,
-// lane l at 16*l: conflict-free 16-byte reads). Every wave owns the 32-key
-// tiles part, part + parts, ... (part = block * 8 + wave) and needs no
-// other wave after the set-up: the next tile's K and V half-rows are in
-// flight into registers while the current one is computed; the two waves
-// of a SIMD take turns on its matrix core. Per tile: the key and value
-// norms, then for every column tile the S k-steps on the matrix cores
-// interleaved with the sign work of the previous column tile.
+// lane l at 16*l: conflict-free 16-byte reads). Block b hashes the 32-key
+// tiles b, b + grid, ...; its waves take them one at a time (the first two
+// each fixed, then from a counter in LDS) and need no other wave after the
+// set-up: the next tile's K half-rows are in flight into registers while
+// the current one is computed; the two waves of a SIMD take turns on its
+// matrix core. Per tile: the key norms, then for every column tile the S
+// k-steps on the matrix cores interleaved with the sign work of the
+// previous column tile, then the value norms. A wave's uncertain signs go
+// to its own list region (part = block * 8 + wave); owner records the part
+// of every tile for the exact re-hash.
 template <int D, int NCT, bool kWordIds>
 __global__ __launch_bounds__(kHashThreads, 1) void hash_keys_bf16_kernel(HashArgs a) {
   constexpr int S = D / 16;
@@ -233,18 +240,22 @@ __global__ __launch_bounds__(kHashThreads, 1) void hash_keys_bf16_kernel(HashArg
   __shared__ u32x4_t frag[NCT * S * 64];
   __shared__ float rmax_s[NCT];
   __shared__ uint32_t bitvec[kWordIds ? 1 : kHashWaves * kTileKeys * kMaxColWords];
+  __shared__ uint32_t tiles_taken;  // the block's tiles handed out past the first two per wave
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kn = lane & 31, kh = lane >> 5;
   const int CT = (a.C + 31) >> 5;
-  const int parts = gridDim.x * kHashWaves;
-  const int part = blockIdx.x * kHashWaves + wave;  // this wave's tiles and list region
+  const int part = blockIdx.x * kHashWaves + wave;  // this wave's list region
+  // the block's tiles: blockIdx.x + j * gridDim.x, j < nblk
+  const int nblk = (a.n_tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  auto block_tile = [&](int j) { return j < nblk ? (int)blockIdx.x + j * (int)gridDim.x : a.n_tiles; };
   unsigned long long* const fix_list = a.fix_list + (size_t)part * a.fix_cap;
   uint32_t fix_n = 0;  // wave-uniform count of listed entries
 
   // the first tile's key rows are in flight during the set-up
   HalfRows<D> ka, kb;
-  load_half_rows<D>(a, a.K, min(part, a.n_tiles - 1), ka, lane);
+  load_half_rows<D>(a, a.K, min(block_tile(wave), a.n_tiles - 1), ka, lane);
+  if (threadIdx.x == 0) tiles_taken = 0;
 
   // set-up: thread t moves R^T row t (hyperplane column t) into its
   // fragment places and takes its squared norm; the largest of each column
@@ -265,20 +276,56 @@ __global__ __launch_bounds__(kHashThreads, 1) void hash_keys_bf16_kernel(HashArg
     if ((r & 31) == 0) rmax_s[ct] = sqrtf(mx) * (1.0f + 0x1p-20f);
   }
   __syncthreads();
-  float rmax[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
-    rmax[ct] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
-                                             __builtin_bit_cast(int, rmax_s[ct])));
   const u32x4_t* const fl0 = frag + lane;
 
-  // One tile with its key rows in cur, while the next tile's key rows load
-  // into nxt (after the last tile the last tile's rows again, unused) and
-  // the tile's value rows arrive for its value norms at the end.
-  auto step = [&](const HalfRows<D>& cur, HalfRows<D>& nxt, int tile) {
+  // The ids and the value norm of a finished tile, stored in the middle of
+  // the next one: a store still in flight at a wave's next wait for its
+  // loads would be waited for too.
+  struct Pending {
+    uint32_t words[NCT / 2];
+    float vn;
+    int64_t grow;
+    bool ok;
+  } pend;
+  pend.ok = false;
+  auto flush = [&]() {
+    if (pend.ok) {
+      if (kh == 0) a.vnorm[pend.grow] = pend.vn;
+      if constexpr (kWordIds) {
+        // P == 8: word ct holds the id bytes of tables 4ct .. 4ct+3
+        uint32_t* orow = reinterpret_cast<uint32_t*>(a.ids + pend.grow * a.L);
+#pragma unroll
+        for (int i = 0; i < NCT / 2; ++i) {
+          const int ct = kh * (NCT / 2) + i;
+          if (ct < CT) orow[ct] = pend.words[i];
+        }
+      }
+    }
+    pend.ok = false;
+  };
+
+  // Tiles: the wave's first two are the block's tiles wave and wave + 8,
+  // later ones are handed out by the block's counter in LDS, which balances
+  // the two waves of a SIMD (the hardware serves the older one first). A
+  // request is sent a tile ahead of the one whose rows it names.
+  auto grab = [&]() {
+    uint32_t t = 0;
+    if (lane == 0) t = atomicAdd(&tiles_taken, 1u);
+    return t;  // in lane 0
+  };
+  auto tile_of = [&](uint32_t t) {
+    t = (uint32_t)__builtin_amdgcn_readfirstlane((int)t);
+    return block_tile((int)min<uint32_t>(2u * kHashWaves + t, (uint32_t)nblk));
+  };
+
+  // One tile with its key rows in cur, while the key rows of tile `next`
+  // load into nxt (the last tile's rows again when there is none) and the
+  // tile's value rows arrive for its value norms at the end.
+  auto step = [&](const HalfRows<D>& cur, HalfRows<D>& nxt, int tile, int next) {
     HalfRows<D> vr;
     load_half_rows<D>(a, a.V, tile, vr, lane);
-    load_half_rows<D>(a, a.K, min(tile + parts, a.n_tiles - 1), nxt, lane);
+    load_half_rows<D>(a, a.K, min(next, a.n_tiles - 1), nxt, lane);
+    if (lane == 0) a.owner[tile] = part;
     const TileRows tr = tile_rows(a, tile);
     const bool row_ok = kn < tr.rows;
     const int64_t grow = tr.grow0 + kn;
@@ -300,22 +347,32 @@ __global__ __launch_bounds__(kHashThreads, 1) void hash_keys_bf16_kernel(HashArg
     // of ct - 1 are packed
     uint32_t words[NCT / 2];  // lane half kh: the words of column tiles kh*NCT/2 + i
     f32x16_t prev = {};
+    // A fragments kAhead k-steps ahead of their MFMA (LDS latency)
+    constexpr int kAhead = 3, kSteps = NCT * S;
+    u32x4_t fr[kAhead + 1];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) fr[i] = fl[i * 64];
 #pragma unroll
     for (int ct = 0; ct <= NCT; ++ct) {
       f32x16_t acc = {};
       ColSigns cs;
+      const float rm = ct > 0 ? rmax_s[ct - 1] : 0.f;  // read early, used at the end
+      if (ct == NCT / 2) flush();
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        if (ct < NCT)
+        const int i = ct * S + s;
+        if (ct < NCT) {
+          if (i + kAhead < kSteps) fr[(i + kAhead) % (kAhead + 1)] = fl[(i + kAhead) * 64];
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, fl[(ct * S + s) * 64]),
+              __builtin_bit_cast(bf16x8_t, fr[i % (kAhead + 1)]),
               __builtin_bit_cast(bf16x8_t, cur.q[s]), acc, 0, 0, 0);
+        }
         if (ct > 0) col_signs_step<S>(prev, s, cs);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (ct > 0) {
         const int pc = ct - 1;
-        const uint32_t w = col_finish(a, prev, cs, pc, thr_k * rmax[pc] + kAbsFloor, row_ok,
+        const uint32_t w = col_finish(a, prev, cs, pc, thr_k * rm + kAbsFloor, row_ok,
                                       grow, CT, fix_n, fix_list, lane);
         if (pc / (NCT / 2) == kh) words[pc % (NCT / 2)] = w;  // both halves hold the word
       }
@@ -326,19 +383,13 @@ __global__ __launch_bounds__(kHashThreads, 1) void hash_keys_bf16_kernel(HashArg
 #pragma unroll
     for (int s = 0; s < S; ++s) vs = sumsq_bf16x8(vr.q[s], vs);
     vs += __builtin_bit_cast(float, xor32_u32(__builtin_bit_cast(uint32_t, vs)));
-    if (kh == 0 && row_ok) a.vnorm[grow] = __builtin_amdgcn_sqrtf(vs);
-
-    if constexpr (kWordIds) {
-      // P == 8: word ct holds the id bytes of tables 4ct .. 4ct+3
-      if (row_ok) {
-        uint32_t* orow = reinterpret_cast<uint32_t*>(a.ids + grow * a.L);
+    pend.vn = __builtin_amdgcn_sqrtf(vs);
+    pend.grow = grow;
+    pend.ok = row_ok;
 #pragma unroll
-        for (int i = 0; i < NCT / 2; ++i) {
-          const int ct = kh * (NCT / 2) + i;
-          if (ct < CT) orow[ct] = words[i];
-        }
-      }
-    } else {
+    for (int i = 0; i < NCT / 2; ++i) pend.words[i] = words[i];
+
+    if constexpr (!kWordIds) {
       // any P: the words through this wave's LDS rows, then id bytes
       uint32_t* bv = bitvec + wave * kTileKeys * kMaxColWords;
 #pragma unroll
@@ -355,13 +406,18 @@ __global__ __launch_bounds__(kHashThreads, 1) void hash_keys_bf16_kernel(HashArg
       __builtin_amdgcn_wave_barrier();
     }
   };
+
   // tiles in pairs, so that the two row buffers swap roles without copies
-  int tile = part;
-  for (; tile + parts < a.n_tiles; tile += 2 * parts) {
-    step(ka, kb, tile);
-    step(kb, ka, tile + parts);
+  int t0 = block_tile(wave), t1 = block_tile(wave + kHashWaves);
+  uint32_t r2 = grab();  // the tile after t1
+  while (t0 < a.n_tiles) {
+    step(ka, kb, t0, t1);
+    t0 = t1; t1 = tile_of(r2); r2 = grab();
+    if (t0 >= a.n_tiles) break;
+    step(kb, ka, t0, t1);
+    t0 = t1; t1 = tile_of(r2); r2 = grab();
   }
-  if (tile < a.n_tiles) step(ka, kb, tile);
+  flush();
   if (lane == 0) a.fix_count[part] = fix_n;
 }
 
@@ -473,17 +529,29 @@ __global__ __launch_bounds__(256) void hash_fixup_kernel(
 // sign): one thread per (key, table) recomputes the table's P projections
 // from the bf16 inputs in float64 (exact products; the sum of |products|
 // bounds the rounding) or, when that cannot decide, in double-double, and
-// rewrites the id byte. Block blk takes the waves of main-kernel block blk
-// and exits at once when none overflowed.
+// rewrites the id byte. Each block checks 256 tiles at a time (owner: the
+// wave that hashed the tile) and goes on at once when none needs it.
 template <int D>
 __global__ __launch_bounds__(256) void hash_redo_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ R, int64_t n_keys,
     int64_t stride, int tph, int n_tiles, int parts, int L, int P, uint8_t* __restrict__ ids,
-    const uint32_t* __restrict__ count, uint32_t cap) {
+    const uint32_t* __restrict__ count, const int* __restrict__ owner, uint32_t cap) {
+  __shared__ int list[256];
+  __shared__ int nlist;
   const int C = L * P;
-  for (int part = blockIdx.x * kHashWaves; part < (int)(blockIdx.x + 1) * kHashWaves; ++part) {
-    if (count[part] <= cap) continue;  // uniform
-  for (int tile = part; tile < n_tiles; tile += parts) {
+  for (int64_t base = (int64_t)blockIdx.x * 256; base < n_tiles; base += (int64_t)gridDim.x * 256) {
+    const int64_t t = base + threadIdx.x;
+    // (an owner outside the waves of the main kernel cannot occur; it is
+    // not used as an index then)
+    const int o = t < n_tiles ? owner[t] : -1;
+    const bool need = (unsigned)o < (unsigned)parts && count[o] > cap;
+    if (!__syncthreads_or(need)) continue;
+    if (threadIdx.x == 0) nlist = 0;
+    __syncthreads();
+    if (need) list[atomicAdd(&nlist, 1)] = (int)t;
+    __syncthreads();
+    for (int e = 0; e < nlist; ++e) {
+    const int tile = list[e];
     const int head = tile / tph;
     const int64_t row0 = (int64_t)(tile - head * tph) * kTileKeys;
     const int rows = (int)min<int64_t>(kTileKeys, n_keys - row0);
@@ -514,7 +582,8 @@ __global__ __launch_bounds__(256) void hash_redo_kernel(
       }
       ids[(grow0 + r) * L + l] = (uint8_t)id;
     }
-  }
+    }
+    __syncthreads();
   }
 }
 
@@ -572,11 +641,16 @@ constexpr int kMaxHashBlocks = 256;  // one per CU
 struct HashWs {
   uint16_t* rt;
   uint32_t* count;            // [kMaxHashBlocks * kHashWaves]
+  int* owner;                 // [n_tiles]
   unsigned long long* list;   // [kMaxHashBlocks * kHashWaves][cap]
   uint32_t cap;               // entries per wave
 };
 
-HashWs hash_ws_layout(void* ws, int64_t n_total, int d, int C) {
+int64_t hash_tiles(int64_t n_heads, int64_t n_keys) {
+  return n_heads * ((n_keys + kTileKeys - 1) / kTileKeys);
+}
+
+HashWs hash_ws_layout(void* ws, int64_t n_heads, int64_t n_keys, int d, int C) {
   HashWs w{};
   unsigned char* p = static_cast<unsigned char*>(ws);
   size_t off = 0;
@@ -584,8 +658,10 @@ HashWs hash_ws_layout(void* ws, int64_t n_total, int d, int C) {
   off = align256(off + (size_t)kRtRows * d * sizeof(uint16_t));
   w.count = reinterpret_cast<uint32_t*>(p + off);
   off = align256(off + kMaxHashBlocks * kHashWaves * sizeof(uint32_t));
+  w.owner = reinterpret_cast<int*>(p + off);
+  off = align256(off + (size_t)hash_tiles(n_heads, n_keys) * sizeof(int));
   w.list = reinterpret_cast<unsigned long long*>(p + off);
-  w.cap = hash_fix_capacity(n_total, C) / (kMaxHashBlocks * kHashWaves);
+  w.cap = hash_fix_capacity(n_heads * n_keys, C) / (kMaxHashBlocks * kHashWaves);
   return w;
 }
 
@@ -614,11 +690,12 @@ uint32_t hash_fix_capacity(int64_t n_total, int C) {
   return (uint32_t)std::max<int64_t>(65536, std::min<int64_t>(want, (int64_t)1 << 26));
 }
 
-size_t hash_keys_bf16_workspace_bytes(int64_t n_total, int d, int C) {
+size_t hash_keys_bf16_workspace_bytes(int64_t n_heads, int64_t n_keys, int d, int C) {
   size_t off = align256((size_t)kRtRows * d * sizeof(uint16_t));
   off = align256(off + kMaxHashBlocks * kHashWaves * sizeof(uint32_t));
+  off = align256(off + (size_t)hash_tiles(n_heads, n_keys) * sizeof(int));
   const size_t parts = (size_t)kMaxHashBlocks * kHashWaves;
-  return off + (hash_fix_capacity(n_total, C) / parts) * parts * sizeof(unsigned long long);
+  return off + (hash_fix_capacity(n_heads * n_keys, C) / parts) * parts * sizeof(unsigned long long);
 }
 
 hipError_t launch_hash_keys_bf16(const uint16_t* K, const uint16_t* V,
@@ -630,7 +707,7 @@ hipError_t launch_hash_keys_bf16(const uint16_t* K, const uint16_t* V,
   const int C = L * P;
   const int64_t tph = (n_keys + kTileKeys - 1) / kTileKeys;
   if (n_heads * tph >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  const HashWs w = hash_ws_layout(ws, n_heads * n_keys, d, C);
+  const HashWs w = hash_ws_layout(ws, n_heads, n_keys, d, C);
   // the fix-up patches bits through 4-byte words inside id rows
   const bool word_rows = (L % 4 == 0) && (reinterpret_cast<uintptr_t>(ids) & 3) == 0;
   HashArgs a{};
@@ -650,6 +727,7 @@ hipError_t launch_hash_keys_bf16(const uint16_t* K, const uint16_t* V,
   a.fix_list = w.list;
   a.fix_count = w.count;
   a.fix_cap = word_rows ? w.cap : 0u;
+  a.owner = w.owner;
 
   launch_kernel(hash_prep_kernel, dim3(64), dim3(256), 0, stream, R, C, d, w.rt);
   const bool word_ids = P == 8 && word_rows;
@@ -670,11 +748,13 @@ hipError_t launch_hash_keys_bf16(const uint16_t* K, const uint16_t* V,
                     ids, w.list, w.count, a.fix_cap);
   }
   if (d == 128)
-    launch_kernel(hash_redo_kernel<128>, dim3(blocks), dim3(256), 0, stream, K, R, n_keys,
-                  stride, a.tph, a.n_tiles, blocks * kHashWaves, L, P, ids, w.count, a.fix_cap);
+    launch_kernel(hash_redo_kernel<128>, dim3(kMaxHashBlocks), dim3(256), 0, stream, K, R,
+                  n_keys, stride, a.tph, a.n_tiles, blocks * kHashWaves, L, P, ids, w.count,
+                  w.owner, a.fix_cap);
   else
-    launch_kernel(hash_redo_kernel<64>, dim3(blocks), dim3(256), 0, stream, K, R, n_keys,
-                  stride, a.tph, a.n_tiles, blocks * kHashWaves, L, P, ids, w.count, a.fix_cap);
+    launch_kernel(hash_redo_kernel<64>, dim3(kMaxHashBlocks), dim3(256), 0, stream, K, R,
+                  n_keys, stride, a.tph, a.n_tiles, blocks * kHashWaves, L, P, ids, w.count,
+                  w.owner, a.fix_cap);
   return hipGetLastError();
 }
 

@@ -39,8 +39,9 @@ inline constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // ------------------------------------------------------------- prefill hash
 // Entries of the deferred sign fix-up list for n_total keys of C hyperplanes.
 uint32_t hash_fix_capacity(int64_t n_total, int C);
-// Workspace of the bf16 path: R^T, the fix-up counter and list.
-size_t hash_keys_bf16_workspace_bytes(int64_t n_total, int d, int C);
+// Workspace of the bf16 path: R^T, the fix-up counts and lists, the tile
+// counter and the tile owners.
+size_t hash_keys_bf16_workspace_bytes(int64_t n_heads, int64_t n_keys, int d, int C);
 // ws: hash_keys_bf16_workspace_bytes(...) bytes, 256-byte aligned.
 hipError_t launch_hash_keys_bf16(const uint16_t* K, const uint16_t* V,
                                  const uint16_t* R, int64_t n_heads,
