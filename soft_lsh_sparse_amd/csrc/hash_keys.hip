@@ -75,6 +75,7 @@ struct HashArgs {
   const uint16_t* V;
   const uint16_t* R;   // [d, C]
   const uint16_t* RT;  // [kRtRows, d], zero past C
+  const uint4* RTF;    // R^T in the order of the MFMA A fragments (see the main kernel)
   int64_t n_keys, stride;
   int tph, n_tiles;  // 32-key tiles per head, tiles in total (< 2^31)
   int L, P, C;
@@ -110,8 +111,11 @@ __device__ __forceinline__ uint32_t extract_bits(const uint32_t* row, int off, i
 // Row m of a 32-column MFMA tile holds hyperplane column
 // ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3) of the tile. With the D
 // layout (lane (n, h) holds rows (v/4)*8 + h*4 + v%4, v = 0..15) this gives
-// lane half h the 16 consecutive columns h*16 + v. jmap_inv: the row of
-// column j.
+// lane half h the 16 consecutive columns h*16 + v. jmap: the column of row
+// m; jmap_inv: the row of column j.
+__device__ __forceinline__ int jmap(int m) {
+  return ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3);
+}
 __device__ __forceinline__ int jmap_inv(int j) {
   return (((j >> 2) & 3) << 3) | (((j >> 4) & 1) << 2) | (j & 3);
 }
@@ -177,18 +181,19 @@ __device__ __forceinline__ void col_signs_step(const f32x16_t& acc, int s, ColSi
     cs.mn = (s == 0 && i == 0) ? m : fminf(cs.mn, m);
     cs.word = __builtin_amdgcn_alignbit((s == 0 && i == 0) ? 0u : cs.word, __float_as_uint(acc[v]), 31);
   }
+  // done here, beside this k-step (not gathered after the loop)
+  asm volatile("" : "+v"(cs.word), "+v"(cs.mn));
 }
 
-// The signs of column tile ct of a tile: its 32-bit word of sign bits (the
-// same in both lanes of a key) and, rarely, list entries for uncertain ones
-// (see the file comment). Returns the word.
+// The certification of column tile ct of a tile: rarely, list entries for
+// uncertain signs (see the file comment). Returns h, the tile's 16 sign
+// bits of the lane (bit v: projection onto column ct*32 + kh*16 + v > 0).
 __device__ __forceinline__ uint32_t col_finish(const HashArgs& a, const f32x16_t& acc,
                                                const ColSigns& cs, int ct, float thr,
                                                bool row_ok, int64_t grow, int CT,
                                                uint32_t& fix_n, unsigned long long* fix_list,
                                                int lane) {
   const int kh = lane >> 5;
-  const uint32_t h = ~cs.word & 0xffffu;  // bit v: projection onto column ct*32 + kh*16 + v is > 0
   const bool cand = row_ok && ct < CT && cs.mn <= thr;
   // Rare: some lanes hold projections too close to zero for their float32
   // sign. Each such key lists its group of 16 columns with the mask of
@@ -216,8 +221,18 @@ __device__ __forceinline__ uint32_t col_finish(const HashArgs& a, const f32x16_t
                       ((unsigned long long)(c0 >> 4) << 16) | fm;
     fix_n += (uint32_t)__popcll(bal);
   }
-  const uint32_t o = xor32_u32(h);
-  return kh ? (o | (h << 16)) : (h | (o << 16));
+  return ~cs.word & 0xffffu;
+}
+
+// The 32-bit sign words of column tiles ct (h0) and ct + 1 (h1), ct even,
+// from the lane halves' 16 bits: one swap of the halves (lanes 32-63 of the
+// first operand trade places with lanes 0-31 of the second) leaves the word
+// of ct in lanes 0-31 and the word of ct + 1 in lanes 32-63.
+__device__ __forceinline__ uint32_t pair_words(uint32_t h0, uint32_t h1) {
+  const auto r = __builtin_amdgcn_permlane32_swap(h0, h1, false, false);
+  // lanes 0-31: r[0] = own bits of ct, r[1] = the partner's bits of ct;
+  // lanes 32-63: r[0] = the partner's bits of ct + 1, r[1] = own bits of ct + 1
+  return r[0] | (r[1] << 16);
 }
 
 // Main kernel: one block of 8 waves per CU. R^T of all NCT column tiles
@@ -257,21 +272,19 @@ __global__ __launch_bounds__(kHashThreads, 1) void hash_keys_bf16_kernel(HashArg
   load_half_rows<D>(a, a.K, min(block_tile(wave), a.n_tiles - 1), ka, lane);
   if (threadIdx.x == 0) tiles_taken = 0;
 
-  // set-up: thread t moves R^T row t (hyperplane column t) into its
-  // fragment places and takes its squared norm; the largest of each column
-  // tile (rounded up) bounds the projection errors
+  // set-up: the fragments into LDS (a plain copy), then thread t takes the
+  // squared norm of hyperplane column t; the largest of each column tile
+  // (rounded up) bounds the projection errors
+  for (int q = threadIdx.x; q < NCT * S * 64; q += kHashThreads) {
+    const uint4 x = a.RTF[q];
+    frag[q] = u32x4_t{x.x, x.y, x.z, x.w};
+  }
+  __syncthreads();
   for (int r = threadIdx.x; r < NCT * 32; r += kHashThreads) {
-    const uint4* src = reinterpret_cast<const uint4*>(a.RT + (int64_t)r * D);
     const int ct = r >> 5, m = jmap_inv(r & 31);
     float sq = 0.f;
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const uint4 x = src[c];
-      const u32x4_t w = {x.x, x.y, x.z, x.w};
-      sq = sumsq_bf16x8(w, sq);
-      const int h = c / S, st = c % S;
-      frag[(ct * S + st) * 64 + h * 32 + m] = w;
-    }
+    for (int c = 0; c < CH; ++c) sq = sumsq_bf16x8(frag[(ct * S + c % S) * 64 + (c / S) * 32 + m], sq);
     const float mx = group_max<32>(sq);  // the 32 columns of the tile are 32 aligned lanes
     if ((r & 31) == 0) rmax_s[ct] = sqrtf(mx) * (1.0f + 0x1p-20f);
   }
@@ -296,7 +309,7 @@ __global__ __launch_bounds__(kHashThreads, 1) void hash_keys_bf16_kernel(HashArg
         uint32_t* orow = reinterpret_cast<uint32_t*>(a.ids + pend.grow * a.L);
 #pragma unroll
         for (int i = 0; i < NCT / 2; ++i) {
-          const int ct = kh * (NCT / 2) + i;
+          const int ct = 2 * i + kh;
           if (ct < CT) orow[ct] = pend.words[i];
         }
       }
@@ -345,7 +358,8 @@ __global__ __launch_bounds__(kHashThreads, 1) void hash_keys_bf16_kernel(HashArg
 
     // column tiles: the k-steps of ct on the matrix cores while the signs
     // of ct - 1 are packed
-    uint32_t words[NCT / 2];  // lane half kh: the words of column tiles kh*NCT/2 + i
+    uint32_t words[NCT / 2];  // lane half kh: the words of column tiles 2i + kh
+    uint32_t h_even = 0;      // sign bits of the last even column tile
     f32x16_t prev = {};
     // A fragments kAhead k-steps ahead of their MFMA (LDS latency)
     constexpr int kAhead = 3, kSteps = NCT * S;
@@ -372,9 +386,12 @@ __global__ __launch_bounds__(kHashThreads, 1) void hash_keys_bf16_kernel(HashArg
       }
       if (ct > 0) {
         const int pc = ct - 1;
-        const uint32_t w = col_finish(a, prev, cs, pc, thr_k * rm + kAbsFloor, row_ok,
-                                      grow, CT, fix_n, fix_list, lane);
-        if (pc / (NCT / 2) == kh) words[pc % (NCT / 2)] = w;  // both halves hold the word
+        const uint32_t h = col_finish(a, prev, cs, pc, thr_k * rm + kAbsFloor, row_ok, grow,
+                                      CT, fix_n, fix_list, lane);
+        if (pc % 2 == 0)
+          h_even = h;
+        else
+          words[pc / 2] = pair_words(h_even, h);
       }
       prev = acc;
     }
@@ -393,7 +410,7 @@ __global__ __launch_bounds__(kHashThreads, 1) void hash_keys_bf16_kernel(HashArg
       // any P: the words through this wave's LDS rows, then id bytes
       uint32_t* bv = bitvec + wave * kTileKeys * kMaxColWords;
 #pragma unroll
-      for (int i = 0; i < NCT / 2; ++i) bv[kn * kMaxColWords + kh * (NCT / 2) + i] = words[i];
+      for (int i = 0; i < NCT / 2; ++i) bv[kn * kMaxColWords + 2 * i + kh] = words[i];
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes are done
       __builtin_amdgcn_wave_barrier();
       uint8_t* obase = a.ids + tr.grow0 * a.L;
@@ -421,14 +438,28 @@ __global__ __launch_bounds__(kHashThreads, 1) void hash_keys_bf16_kernel(HashArg
   if (lane == 0) a.fix_count[part] = fix_n;
 }
 
-// R [d, C] -> R^T [kRtRows, d] with zero rows past C.
+// R [d, C] -> R^T [kRtRows, d] with zero rows past C, and the same in the
+// order of the main kernel's A fragments: 16-byte chunk q holds, for
+// f = q / 64 = ct * S + st and l = q % 64 = h * 32 + m, elements
+// (h * S + st) * 8 .. + 7 of R^T row ct * 32 + jmap(m) (S = D / 16).
 __global__ __launch_bounds__(256) void hash_prep_kernel(const uint16_t* __restrict__ R, int C,
-                                                        int D, uint16_t* __restrict__ RT) {
+                                                        int D, uint16_t* __restrict__ RT,
+                                                        uint16_t* __restrict__ RTF) {
   const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t total = (int64_t)kRtRows * D;
-  for (int64_t i = i0; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t i = i0; i < total; i += stride) {
     const int c = (int)(i / D), d = (int)(i % D);
     RT[i] = c < C ? R[(int64_t)d * C + c] : (uint16_t)0;
+  }
+  const int S = D / 16;
+  for (int64_t i = i0; i < total; i += stride) {
+    const int64_t q = i / 8;
+    const int e = (int)(i % 8);
+    const int f = (int)(q / 64), l = (int)(q % 64);
+    const int ct = f / S, st = f % S, h = l / 32, m = l % 32;
+    const int r = ct * 32 + jmap(m), d = (h * S + st) * 8 + e;
+    RTF[i] = r < C ? R[(int64_t)d * C + r] : (uint16_t)0;
   }
 }
 
@@ -640,6 +671,7 @@ constexpr int kMaxHashBlocks = 256;  // one per CU
 
 struct HashWs {
   uint16_t* rt;
+  uint16_t* rtf;              // R^T in fragment order
   uint32_t* count;            // [kMaxHashBlocks * kHashWaves]
   int* owner;                 // [n_tiles]
   unsigned long long* list;   // [kMaxHashBlocks * kHashWaves][cap]
@@ -655,6 +687,8 @@ HashWs hash_ws_layout(void* ws, int64_t n_heads, int64_t n_keys, int d, int C) {
   unsigned char* p = static_cast<unsigned char*>(ws);
   size_t off = 0;
   w.rt = reinterpret_cast<uint16_t*>(p + off);
+  off = align256(off + (size_t)kRtRows * d * sizeof(uint16_t));
+  w.rtf = reinterpret_cast<uint16_t*>(p + off);
   off = align256(off + (size_t)kRtRows * d * sizeof(uint16_t));
   w.count = reinterpret_cast<uint32_t*>(p + off);
   off = align256(off + kMaxHashBlocks * kHashWaves * sizeof(uint32_t));
@@ -692,6 +726,7 @@ uint32_t hash_fix_capacity(int64_t n_total, int C) {
 
 size_t hash_keys_bf16_workspace_bytes(int64_t n_heads, int64_t n_keys, int d, int C) {
   size_t off = align256((size_t)kRtRows * d * sizeof(uint16_t));
+  off = align256(off + (size_t)kRtRows * d * sizeof(uint16_t));
   off = align256(off + kMaxHashBlocks * kHashWaves * sizeof(uint32_t));
   off = align256(off + (size_t)hash_tiles(n_heads, n_keys) * sizeof(int));
   const size_t parts = (size_t)kMaxHashBlocks * kHashWaves;
@@ -715,6 +750,7 @@ hipError_t launch_hash_keys_bf16(const uint16_t* K, const uint16_t* V,
   a.V = V;
   a.R = R;
   a.RT = w.rt;
+  a.RTF = reinterpret_cast<const uint4*>(w.rtf);
   a.n_keys = n_keys;
   a.stride = stride;
   a.tph = (int)tph;
@@ -729,7 +765,7 @@ hipError_t launch_hash_keys_bf16(const uint16_t* K, const uint16_t* V,
   a.fix_cap = word_rows ? w.cap : 0u;
   a.owner = w.owner;
 
-  launch_kernel(hash_prep_kernel, dim3(64), dim3(256), 0, stream, R, C, d, w.rt);
+  launch_kernel(hash_prep_kernel, dim3(256), dim3(256), 0, stream, R, C, d, w.rt, w.rtf);
   const bool word_ids = P == 8 && word_rows;
   // enough 8-wave blocks that every wave has a tile, at most one per CU
   const int blocks = (int)std::min<int64_t>((a.n_tiles + kHashWaves - 1) / kHashWaves,
