@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--skip-prefill-hash", action="store_true",
                     help="leave out the prefill-hash timing (8 KV heads x 131072 keys, "
                          "L=64, P=8) reported beside the decode figure")
+    ap.add_argument("--skip-dense", action="store_true",
+                    help="leave out the dense flash-decode baseline (every key, same "
+                         "caches and queries) reported beside the decode figure")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 4 times (reference for HBM "
                          "byte counters) and exit")
@@ -325,6 +328,47 @@ def main():
             "avg_launch_ms": round(kernel_ms[dom], 5),
         }
 
+    # ---- dense baseline: exact attention over every key of the same
+    # rotated caches and queries (the comparison SOCKET's speed-up is stated
+    # against), timed the same way; its bytes are all K and V rows once per
+    # KV head plus q and out
+    dense = None
+    if not args.skip_dense:
+        dws_bytes = lib.socket_dense_attn_workspace_bytes(w.B, w.Hq, w.d, w.N)
+        dws = torch.empty(dws_bytes, dtype=torch.uint8, device=dev)
+        dfn = lib.socket_dense_attn
+
+        def dense_args(step):
+            layer = step % args.layers
+            K, V = layers[layer][0], layers[layer][1]
+            Q = queries[layer][step % n_q]
+            return (Q.data_ptr(), K.data_ptr(), V.data_ptr(), dt_code, w.B, w.Hq, w.Hkv,
+                    w.d, w.N, w.N, out.data_ptr(), dws.data_ptr(), dws_bytes, stream)
+
+        dlist = [dense_args(s) for s in range(total)]
+        for s in range(args.warmup):
+            st = dfn(*dlist[s])
+            if st:
+                _lib.check(st, "socket_dense_attn")
+        torch.cuda.synchronize()
+        ev0.record()
+        for s in range(args.warmup, total):
+            dfn(*dlist[s])
+        ev1.record()
+        torch.cuda.synchronize()
+        dense_ms = ev0.elapsed_time(ev1) / args.steps
+        dense_bytes = (2 * w.B * w.Hkv * w.N * w.d + 2 * w.B * w.Hq * w.d) * w.elem_bytes
+        dense_gbs = dense_bytes / (dense_ms * 1e-3) / 1e9
+        dense = {
+            "kernel": "dense_attn_kernel + attn_merge_kernel",
+            "ms_per_step": round(dense_ms, 5),
+            "tokens_per_s": round(w.B / (dense_ms * 1e-3), 1),
+            "algorithmic_bytes_per_step": dense_bytes,
+            "hbm_gbs": round(dense_gbs, 1),
+            "hbm_frac": round(dense_gbs / HBM_PEAK_GBS, 4),
+            "socket_speedup": round(dense_ms / ms_per_step, 3),
+        }
+
     # ---- prefill hashing (bf16 MFMA projections, fused sign packing and
     # value norms) on its own workload, reported beside the decode figure
     prefill = None
@@ -357,6 +401,7 @@ def main():
         "algorithmic_bytes_per_step": step_bytes,
         "kernel_ms": {k: round(v, 5) for k, v in kernel_ms.items()},
         "roofline": roofline,
+        "dense_baseline": dense,
         "prefill_hash": prefill,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),

@@ -194,6 +194,28 @@ socket_status socket_sparse_attn(const void* Q, const void* K, const void* V,
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * Baseline: dense attention decoding (every key), the comparison SOCKET's
+ * speed-up is stated against.
+ * Defines: the dense FlashAttention decoding of the pages' efficiency
+ * results (page "Resumen Técnico: SOCKET - Estimador de Núcleo de Colisión
+ * Suave para Atención Escasa", section "Resultados Experimentales").
+ *
+ *   Q    [B, Hq, d] dtype
+ *   K, V [B, Hkv, head_stride_rows, d] dtype; rows 0..n-1 are attended
+ *   out  [B, Hq, d] dtype (output)
+ * out[b,h] = sum_{i<n} softmax_i(q . k_i / sqrt(d)) v_i with query head h
+ * reading KV head h / (Hq / Hkv); float32 accumulation in a fixed order.
+ * 1 <= n <= 2^20 and Hq / Hkv <= 8, else SOCKET_ERR_UNSUPPORTED.
+ * Workspace: socket_dense_attn_workspace_bytes(B, Hq, d, n) bytes of device
+ * memory (chunk partials); all pointers are device pointers the caller owns.
+ */
+size_t socket_dense_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t d, int64_t n);
+socket_status socket_dense_attn(const void* Q, const void* K, const void* V,
+                                socket_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                int32_t d, int64_t n, int64_t head_stride_rows, void* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One whole decode step: stages 1-4 back to back on one stream, no host
  * synchronisation.
  * Defines: steps 2-4 of the soft-LSH mechanism (the decode side).

@@ -10,6 +10,7 @@ from .api import (  # noqa: F401
     bucket_probs,
     decode,
     decode_workspace_bytes,
+    dense_attn,
     hash_keys,
     score,
     sparse_attn,

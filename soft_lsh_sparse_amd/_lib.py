@@ -49,6 +49,10 @@ SIGNATURES = {
                                    c_int32, c_int32, c_int32, c_int64, c_void_p,
                                    c_int64, c_void_p, c_void_p, c_size_t,
                                    c_void_p]),
+    "socket_dense_attn_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int64]),
+    "socket_dense_attn": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int32, c_int32,
+                                  c_int32, c_int32, c_int64, c_int64, c_void_p, c_void_p,
+                                  c_size_t, c_void_p]),
     "socket_decode_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32,
                                                  c_int32, c_int64, c_int32,
                                                  c_int32, c_int64]),

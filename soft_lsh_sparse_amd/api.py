@@ -145,6 +145,22 @@ def sparse_attn(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
     return out
 
 
+def dense_attn(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+               n: int | None = None) -> torch.Tensor:
+    """Dense attention of Q [B, Hq, d] over the first n keys of K, V [B, Hkv, S, d]."""
+    lib = _lib.load()
+    B, Hq, d = Q.shape
+    _, Hkv, S, _ = K.shape
+    n = S if n is None else int(n)
+    out = torch.empty_like(Q)
+    ws = _workspace(lib.socket_dense_attn_workspace_bytes(B, Hq, d, n), Q.device)
+    st = lib.socket_dense_attn(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dtype_code(Q),
+                               B, Hq, Hkv, d, n, S, _dev(out, "out"), ws.data_ptr(),
+                               ws.numel(), _stream(Q))
+    check(st, "socket_dense_attn")
+    return out
+
+
 def decode_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, n_keys: int,
                            L: int, P: int, k: int) -> int:
     return int(_lib.load().socket_decode_workspace_bytes(B, Hq, Hkv, d, n_keys, L, P, k))

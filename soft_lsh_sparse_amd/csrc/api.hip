@@ -307,6 +307,41 @@ socket_status socket_sparse_attn(const void* Q, const void* K, const void* V,
   return from_hip(err, "socket_sparse_attn launch");
 }
 
+size_t socket_dense_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t d, int64_t n) {
+  if (B < 1 || Hq < 1 || d < 1 || n < 1) return 0;
+  return plan_dense(B, Hq, Hq, d, n).partial_bytes;
+}
+
+socket_status socket_dense_attn(const void* Q, const void* K, const void* V,
+                                socket_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                int32_t d, int64_t n, int64_t head_stride_rows, void* out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  SOCKET_TRY(check_dtype(dtype));
+  SOCKET_TRY(check_heads(B, Hq, Hkv));
+  SOCKET_TRY(check_d(d));
+  if (Hq / Hkv > 8)
+    return fail(SOCKET_ERR_UNSUPPORTED, "dense attention takes at most 8 query heads per KV head");
+  if (n < 1) return fail(SOCKET_ERR_INVALID_ARGUMENT, "n must be >= 1");
+  if (n > kMaxDenseKeys)
+    return fail(SOCKET_ERR_UNSUPPORTED, "dense attention takes at most %lld keys",
+                (long long)kMaxDenseKeys);
+  if (head_stride_rows < n)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "head_stride_rows (%lld) < n (%lld)",
+                (long long)head_stride_rows, (long long)n);
+  if (!Q || !K || !V || !out)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V))
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "Q, K and V must be 16-byte aligned");
+  const DensePlan plan = plan_dense(B, Hq, Hkv, d, n);
+  if (!workspace || workspace_bytes < plan.partial_bytes)
+    return fail(SOCKET_ERR_WORKSPACE, "dense attention needs %zu workspace bytes, got %zu",
+                plan.partial_bytes, workspace ? workspace_bytes : (size_t)0);
+  hipError_t err = launch_dense_attn(Q, K, V, dtype == SOCKET_DTYPE_BF16, plan, head_stride_rows,
+                                     out, static_cast<float*>(workspace),
+                                     static_cast<hipStream_t>(stream));
+  return from_hip(err, "socket_dense_attn launch");
+}
+
 size_t socket_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv,
                                      int32_t d, int64_t n_keys, int32_t L,
                                      int32_t P, int64_t k) {

@@ -1,0 +1,258 @@
+// Dense flash-decode attention: the baseline SOCKET is compared against.
+//
+// SOCKET's speed-up is stated against dense FlashAttention decoding (page
+// "Resumen Técnico: SOCKET - Estimador de Núcleo de Colisión Suave para
+// Atención Escasa", section "Resultados Experimentales", item Eficiencia;
+// German page "SOCKET: SOft Collision Kernel EsTimator for Sparse
+// Attention", section "Experimentelle Ergebnisse"): every query attends to
+// all n cached keys with the exact softmax. This kernel computes that on
+// the same GPU and data layout as the sparse path, so both are timed on one
+// harness.
+//
+// Split-k decoding with the GQA group shared: each block takes one KV head
+// (b, g) and a chunk of consecutive keys for all G query heads of the group,
+// so every K and V row is read from memory once per group (the sparse path
+// reads the rows each query head selected). Each of the 4 waves streams
+// its share of the chunk with 16-byte loads (one row per LPR lanes, whole
+// 1 KB runs of consecutive rows per load instruction, the next batch in
+// flight while one is used), keeps a running softmax per head, and the
+// block merges its waves in LDS. The chunk partials (m, l, acc[d]) of each
+// query row are merged by the sparse path's merge kernel, in chunk order.
+// Everything accumulates in float32 in a fixed order.
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+#include <algorithm>
+
+namespace socket_lsh {
+namespace {
+
+constexpr int kDenseThreads = 256;
+constexpr int kDenseWaves = kDenseThreads / 64;
+constexpr int kDenseKeysPerWave = 256;
+constexpr int kDenseChunk = kDenseKeysPerWave * kDenseWaves;
+
+template <typename T>
+__device__ __forceinline__ void unpack16d(const uint4& w, float* f);
+template <>
+__device__ __forceinline__ void unpack16d<BF16>(const uint4& w, float* f) {
+  unpack8_bf16(w, f);
+}
+template <>
+__device__ __forceinline__ void unpack16d<F32>(const uint4& w, float* f) {
+  unpack4_f32(w, f);
+}
+
+// G query heads per KV head; IT loads per tensor and batch.
+template <typename T, int D, int G, int IT>
+__global__ __launch_bounds__(kDenseThreads) void dense_attn_kernel(
+    const typename T::storage* __restrict__ Q, const typename T::storage* __restrict__ K,
+    const typename T::storage* __restrict__ V, int Hq, int Hkv, int64_t stride, int64_t n,
+    int chunks, float* __restrict__ partial) {
+  constexpr int EPL = 16 / T::bytes;  // elements per 16-byte load
+  constexpr int LPR = D / EPL;        // lanes per key row
+  constexpr int KPI = 64 / LPR;       // key rows per wave-wide load
+  constexpr int KPB = IT * KPI;       // keys per batch
+  constexpr int NB = kDenseKeysPerWave / KPB;
+  static_assert(NB * KPB == kDenseKeysPerWave, "keys per wave");
+  __shared__ float sm_m[G][kDenseWaves], sm_l[G][kDenseWaves];
+  __shared__ float sm_acc[G][kDenseWaves][D];
+
+  const int gi = blockIdx.x / chunks, chunk = blockIdx.x % chunks;  // gi = b * Hkv + g
+  const int b = gi / Hkv, g = gi % Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = lane / LPR, sub = lane % LPR;
+  const float scale = 1.0f / sqrtf((float)D);
+
+  float qf[G][EPL];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const int64_t row = (int64_t)b * Hq + g * G + j;
+    const uint4 w = *reinterpret_cast<const uint4*>(Q + row * D + sub * EPL);
+    unpack16d<T>(w, qf[j]);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[j][e] *= scale;
+  }
+
+  const typename T::storage* Kh = K + (int64_t)gi * stride * D + sub * EPL;
+  const typename T::storage* Vh = V + (int64_t)gi * stride * D + sub * EPL;
+  const int64_t wbeg = (int64_t)chunk * kDenseChunk + wave * kDenseKeysPerWave;
+
+  // Batches of KPB consecutive keys, double-buffered. Keys past n are
+  // loaded as row n - 1 (inside the head) and get weight 0.
+  uint4 kr[2][IT], vr[2][IT];
+  float m[G], l[G], acc[G][EPL];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
+  }
+  auto issue = [&](int bt) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int64_t key = min<int64_t>(wbeg + bt * KPB + it * KPI + grp, n - 1);
+      kr[bt & 1][it] = *reinterpret_cast<const uint4*>(Kh + key * D);
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int64_t key = min<int64_t>(wbeg + bt * KPB + it * KPI + grp, n - 1);
+      vr[bt & 1][it] = *reinterpret_cast<const uint4*>(Vh + key * D);
+    }
+  };
+
+  if (wbeg < n) {
+    issue(0);
+#pragma unroll
+    for (int bt = 0; bt < NB; ++bt) {
+      if (bt + 1 < NB) issue(bt + 1);
+      if (wbeg + bt * KPB >= n) continue;  // wave-uniform: past the last key
+      float s[G][IT];
+      float mb[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) mb[j] = -INFINITY;
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        float f[EPL];
+        unpack16d<T>(kr[bt & 1][it], f);
+        const bool valid = wbeg + bt * KPB + it * KPI + grp < n;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          float dot = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) dot = fmaf(qf[j][e], f[e], dot);
+          dot = lane_group_sum<LPR>(dot);
+          s[j][it] = valid ? dot : -INFINITY;
+          mb[j] = fmaxf(mb[j], s[j][it]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        // the key groups of the wave hold different keys: combine across them
+        if constexpr (LPR <= 8) mb[j] = fmaxf(mb[j], xor_lanes<8>(mb[j]));
+        if constexpr (LPR <= 16) mb[j] = fmaxf(mb[j], xor_lanes<16>(mb[j]));
+        if constexpr (LPR <= 32) mb[j] = fmaxf(mb[j], xor_lanes<32>(mb[j]));
+        const float mn = fmaxf(m[j], mb[j]);
+        const float c = m[j] == -INFINITY ? 0.f : __expf(m[j] - mn);
+        l[j] *= c;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j][e] *= c;
+        m[j] = mn;
+      }
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        float f[EPL];
+        unpack16d<T>(vr[bt & 1][it], f);
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          const float p = s[j][it] == -INFINITY ? 0.f : __expf(s[j][it] - m[j]);
+          l[j] += p;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[j][e] = fmaf(p, f[e], acc[j][e]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    if constexpr (LPR <= 8) {
+      l[j] += xor_lanes<8>(l[j]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[j][e] += xor_lanes<8>(acc[j][e]);
+    }
+    if constexpr (LPR <= 16) {
+      l[j] += xor_lanes<16>(l[j]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[j][e] += xor_lanes<16>(acc[j][e]);
+    }
+    if constexpr (LPR <= 32) {
+      l[j] += xor_lanes<32>(l[j]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[j][e] += xor_lanes<32>(acc[j][e]);
+    }
+    if (lane == 0) {
+      sm_m[j][wave] = m[j];
+      sm_l[j][wave] = l[j];
+    }
+    if (grp == 0) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sm_acc[j][wave][sub * EPL + e] = acc[j][e];
+    }
+  }
+  __syncthreads();
+
+  for (int q = threadIdx.x; q < G * D; q += kDenseThreads) {
+    const int j = q / D, t = q % D;
+    const int64_t row = (int64_t)b * Hq + g * G + j;
+    float* out = partial + (row * chunks + chunk) * (D + 2);
+    float mt = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDenseWaves; ++w) mt = fmaxf(mt, sm_m[j][w]);
+    float lt = 0.f, at = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDenseWaves; ++w) {
+      const float c = sm_m[j][w] == -INFINITY ? 0.f : expf(sm_m[j][w] - mt);
+      lt = fmaf(c, sm_l[j][w], lt);
+      at = fmaf(c, sm_acc[j][w][t], at);
+    }
+    out[t] = at;
+    if (t == 0) {
+      out[D] = mt;
+      out[D + 1] = lt;
+    }
+  }
+}
+
+template <typename T, int D, int G>
+hipError_t launch_dense_g(const void* Q, const void* K, const void* V, const DensePlan& p,
+                          int64_t stride, void* out, float* partial, hipStream_t stream) {
+  using S = typename T::storage;
+  constexpr int IT = G >= 4 ? 4 : 8;
+  launch_kernel((dense_attn_kernel<T, D, G, IT>), dim3(p.B * p.Hkv * p.chunks),
+                dim3(kDenseThreads), 0, stream, (const S*)Q, (const S*)K, (const S*)V, p.Hq,
+                p.Hkv, stride, p.n, p.chunks, partial);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_attn_merge(partial, p.B * p.Hq, p.chunks, p.d, T::bytes == 2, out, stream);
+}
+
+template <typename T, int D>
+hipError_t launch_dense_d(const void* Q, const void* K, const void* V, const DensePlan& p,
+                          int64_t stride, void* out, float* partial, hipStream_t stream) {
+  switch (p.Hq / p.Hkv) {
+    case 1: return launch_dense_g<T, D, 1>(Q, K, V, p, stride, out, partial, stream);
+    case 2: return launch_dense_g<T, D, 2>(Q, K, V, p, stride, out, partial, stream);
+    case 4: return launch_dense_g<T, D, 4>(Q, K, V, p, stride, out, partial, stream);
+    default: return launch_dense_g<T, D, 8>(Q, K, V, p, stride, out, partial, stream);
+  }
+}
+
+}  // namespace
+
+DensePlan plan_dense(int B, int Hq, int Hkv, int d, int64_t n) {
+  DensePlan p{};
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.d = d;
+  p.n = n;
+  p.chunks = (int)std::max<int64_t>(1, (n + kDenseChunk - 1) / kDenseChunk);
+  p.partial_bytes = (size_t)B * Hq * p.chunks * (d + 2) * sizeof(float);
+  return p;
+}
+
+hipError_t launch_dense_attn(const void* Q, const void* K, const void* V, bool bf16,
+                             const DensePlan& p, int64_t stride, void* out, float* partial,
+                             hipStream_t stream) {
+  if (p.B == 0 || p.Hq == 0) return hipSuccess;
+  if (bf16) {
+    if (p.d == 128) return launch_dense_d<BF16, 128>(Q, K, V, p, stride, out, partial, stream);
+    return launch_dense_d<BF16, 64>(Q, K, V, p, stride, out, partial, stream);
+  }
+  if (p.d == 128) return launch_dense_d<F32, 128>(Q, K, V, p, stride, out, partial, stream);
+  return launch_dense_d<F32, 64>(Q, K, V, p, stride, out, partial, stream);
+}
+
+}  // namespace socket_lsh

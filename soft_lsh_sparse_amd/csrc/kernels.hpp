@@ -170,4 +170,23 @@ hipError_t launch_sparse_attn(const void* Q, const void* K, const void* V,
                               const int32_t* idx, void* out, float* partial,
                               hipStream_t stream);
 
+// Online-softmax merge of chunk partials [rows][chunks][d + 2] (acc[d], m,
+// l) into out [rows, d] in the input dtype.
+hipError_t launch_attn_merge(const float* partial, int rows, int chunks, int d, bool bf16,
+                             void* out, hipStream_t stream);
+
+// ------------------------------------------------- dense attention baseline
+struct DensePlan {
+  int B, Hq, Hkv, d;
+  int64_t n;
+  int chunks;            // of 1024 keys per (b, KV head)
+  size_t partial_bytes;
+};
+// Largest context the dense baseline takes: 1024 chunks (the merge's limit).
+constexpr int64_t kMaxDenseKeys = 1024 * 1024;
+DensePlan plan_dense(int B, int Hq, int Hkv, int d, int64_t n);
+hipError_t launch_dense_attn(const void* Q, const void* K, const void* V, bool bf16,
+                             const DensePlan& plan, int64_t stride, void* out,
+                             float* partial, hipStream_t stream);
+
 }  // namespace socket_lsh

@@ -286,6 +286,27 @@ hipError_t launch_attn_d(const void* Q, const void* K, const void* V,
 
 }  // namespace
 
+hipError_t launch_attn_merge(const float* partial, int rows, int chunks, int d, bool bf16,
+                             void* out, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  if (bf16) {
+    if (d == 128)
+      launch_kernel((attn_merge_kernel<BF16, 128>), dim3(rows), dim3(128), 0, stream, partial,
+                    chunks, (BF16::storage*)out);
+    else
+      launch_kernel((attn_merge_kernel<BF16, 64>), dim3(rows), dim3(64), 0, stream, partial,
+                    chunks, (BF16::storage*)out);
+  } else {
+    if (d == 128)
+      launch_kernel((attn_merge_kernel<F32, 128>), dim3(rows), dim3(128), 0, stream, partial,
+                    chunks, (F32::storage*)out);
+    else
+      launch_kernel((attn_merge_kernel<F32, 64>), dim3(rows), dim3(64), 0, stream, partial,
+                    chunks, (F32::storage*)out);
+  }
+  return hipGetLastError();
+}
+
 AttnPlan plan_attn(int B, int Hq, int Hkv, int d, int64_t kk) {
   AttnPlan p{};
   p.B = B;

@@ -181,3 +181,36 @@ def test_decode_kernel_sequence(lib):
     assert _kernels(lib, cap=8)[0] == -2      # names do not fit
     assert lib.socket_decode_kernels(FAKE, _lib.DTYPE_BF16, 4, 32, 8, 128, 131072, 131072,
                                      32, 8, 4096, 0, None, 0) == 4
+
+
+def _dense(lib, **over):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, dt=1, B=1, Hq=32, Hkv=8, d=128, n=1024,
+             stride=1024, out=FAKE, ws=FAKE, ws_bytes=0)
+    a.update(over)
+    return lib.socket_dense_attn(a["Q"], a["K"], a["V"], a["dt"], a["B"], a["Hq"],
+                                 a["Hkv"], a["d"], a["n"], a["stride"], a["out"],
+                                 a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dt=7), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(Hq=30), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(d=96), _lib.SOCKET_ERR_UNSUPPORTED),
+    (dict(n=0), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(n=(1 << 20) + 1, stride=(1 << 20) + 1), _lib.SOCKET_ERR_UNSUPPORTED),
+    (dict(stride=100), _lib.SOCKET_ERR_INVALID_ARGUMENT),    # stride < n
+    (dict(Q=None), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(out=None), _lib.SOCKET_ERR_INVALID_ARGUMENT),
+    (dict(V=FAKE + 4), _lib.SOCKET_ERR_INVALID_ARGUMENT),    # misaligned
+    (dict(ws=None), _lib.SOCKET_ERR_WORKSPACE),
+    (dict(ws_bytes=1000), _lib.SOCKET_ERR_WORKSPACE),
+])
+def test_dense_attn_rejects_invalid_arguments(lib, over, status):
+    assert _dense(lib, **over) == status
+
+
+def test_dense_attn_workspace_covers_every_chunk(lib):
+    # partials of (m, l, acc[d]) per query row and 1024-key chunk
+    assert lib.socket_dense_attn_workspace_bytes(4, 32, 128, 131072) == 4 * 32 * 128 * 130 * 4
+    assert lib.socket_dense_attn_workspace_bytes(1, 1, 64, 1) == 66 * 4
+    assert lib.socket_dense_attn_workspace_bytes(1, 1, 64, 0) == 0

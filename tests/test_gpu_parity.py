@@ -317,6 +317,67 @@ def test_sparse_attn_stage(B, Hq, Hkv, d, N, kk, dt):
     assert np.max(np.abs(f64(out) - ref)) <= tol
 
 
+# ------------------------------------------------ dense attention baseline
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,N,dt", [
+    (1, 4, 1, 128, 1, "bf16"),          # one key
+    (1, 4, 1, 128, 37, "bf16"),         # part of one batch
+    (2, 8, 2, 128, 2500, "bf16"),       # several chunks and a ragged tail
+    (1, 8, 1, 64, 1500, "bf16"),        # 8 heads per KV head
+    (1, 2, 1, 64, 777, "f32"),
+    (1, 3, 3, 128, 4096, "f32"),        # one head per KV head, whole chunks
+])
+def test_dense_attn_matches_the_oracle(B, Hq, Hkv, d, N, dt):
+    log(f"dense {(B, Hq, Hkv, d, N, dt)}")
+    w = W.custom_workload(B=B, Hq=Hq, Hkv=Hkv, d=d, N=N, dtype=dt, lognormal_v=True)
+    Q, K, V, _ = W.make_decode_inputs(w, DEV, seed=12)
+    out = S.dense_attn(Q, K, V)
+    torch.cuda.synchronize()
+    idx = np.broadcast_to(np.arange(N), (B, Hq, N))
+    ref = O.subset_attention(f64(Q), f64(K), f64(V), idx, Hq // Hkv)
+    tol = 2e-2 if dt == "bf16" else 1e-4
+    assert np.max(np.abs(f64(out) - ref)) <= tol
+
+
+def test_dense_attn_reads_only_the_first_n_rows():
+    w = W.custom_workload(B=1, Hq=4, Hkv=1, d=128, N=3000, dtype="bf16", lognormal_v=True)
+    Q, K, V, _ = W.make_decode_inputs(w, DEV, seed=13)
+    out = S.dense_attn(Q, K, V, n=2049)
+    torch.cuda.synchronize()
+    idx = np.broadcast_to(np.arange(2049), (1, 4, 2049))
+    ref = O.subset_attention(f64(Q), f64(K), f64(V), idx, 4)
+    assert np.max(np.abs(f64(out) - ref)) <= 2e-2
+
+
+def test_dense_attn_at_128k_sampled_rows():
+    """The bench's dense baseline: B=4, 32/8 heads, d=128, 131072 keys;
+    four query rows checked against the oracle over every key."""
+    w = W.WORKLOADS["llama3_8b_128k_b4"]
+    log(f"dense 128k {w}")
+    Q, K, V, _ = W.make_decode_inputs(w, DEV, seed=0)
+    out = S.dense_attn(Q, K, V)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    for b, h in [(0, 0), (1, 13), (2, 22), (3, 31)]:
+        g = h // G
+        ref = O.subset_attention(f64(Q[b:b + 1, h:h + 1]), f64(K[b:b + 1, g:g + 1]),
+                                 f64(V[b:b + 1, g:g + 1]),
+                                 np.arange(w.N).reshape(1, 1, -1), 1)
+        assert np.max(np.abs(f64(out[b, h]) - ref[0, 0])) <= 2e-2, (b, h)
+
+
+def test_dense_attn_equals_sparse_attn_over_every_key():
+    """k = N: the sparse path over all indices and the dense baseline agree
+    (both float32 accumulation; different orders, so within rounding)."""
+    w = W.custom_workload(B=1, Hq=8, Hkv=2, d=128, N=3000, dtype="bf16", lognormal_v=True)
+    Q, K, V, _ = W.make_decode_inputs(w, DEV, seed=14)
+    idx = torch.arange(w.N, dtype=torch.int32, device=DEV).expand(1, 8, w.N).contiguous()
+    a = S.sparse_attn(Q, K, V, idx)
+    d = S.dense_attn(Q, K, V)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(f64(a) - f64(d))) <= 1e-2
+
+
 # ----------------------------------------------------------- decode end to end
 
 def _check_decode(w, seed=0, step=0, sample_rows=None):
