@@ -50,6 +50,10 @@ def parse():
     ap.add_argument("--skip-dense", action="store_true",
                     help="leave out the dense flash-decode baseline (every key, same "
                          "caches and queries) reported beside the decode figure")
+    ap.add_argument("--skip-decode-loop", action="store_true",
+                    help="leave out the decode loop with one appended key per KV head "
+                         "and step (eager, and the same steps as one HIP graph)")
+    ap.add_argument("--loop-steps", type=int, default=64)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 4 times (reference for HBM "
                          "byte counters) and exit")
@@ -369,6 +373,74 @@ def main():
             "socket_speedup": round(dense_ms / ms_per_step, 3),
         }
 
+    # ---- decode loop: every step appends one key per KV head (hashed alone,
+    # n = 1 at its row) and decodes over the grown cache; the last T keys of
+    # layer 0 are appended in turn (their values are the prefilled ones).
+    # Timed eager, then the same T steps captured in one HIP graph.
+    loop = None
+    if not args.skip_decode_loop:
+        T = max(1, min(args.loop_steps, w.N - 1))
+        K0, V0, R0, ids0, vn0 = layers[0]
+        n0 = w.N - T
+        esz = w.elem_bytes
+        hws_bytes = lib.socket_hash_keys_workspace_bytes(dt_code, w.B * w.Hkv, 1, w.d, w.L, w.P)
+        hws = torch.empty(max(hws_bytes, 1), dtype=torch.uint8, device=dev)
+        hfn = lib.socket_hash_keys
+
+        def loop_calls(t, strm):
+            o = n0 + t  # the appended row
+            q = queries[0][t % n_q]
+            h = (K0.data_ptr() + o * w.d * esz, V0.data_ptr() + o * w.d * esz, R0.data_ptr(),
+                 dt_code, w.B * w.Hkv, 1, w.N, w.d, w.L, w.P, ids0.data_ptr() + o * w.L,
+                 vn0.data_ptr() + o * 4, hws.data_ptr(), hws_bytes, strm)
+            dd = (q.data_ptr(), K0.data_ptr(), V0.data_ptr(), R0.data_ptr(), ids0.data_ptr(),
+                  vn0.data_ptr(), dt_code, w.B, w.Hq, w.Hkv, w.d, o + 1, w.N, w.L, w.P, w.tau,
+                  w.k, out.data_ptr(), idx.data_ptr(), None, ws.data_ptr(), ws_bytes, strm)
+            return h, dd
+
+        def run_loop(strm):
+            for t in range(T):
+                h, dd = loop_calls(t, strm)
+                st = hfn(*h)
+                if st:
+                    _lib.check(st, "socket_hash_keys")
+                st = fn(*dd)
+                if st:
+                    _lib.check(st, "socket_decode")
+
+        run_loop(stream)  # warm-up
+        torch.cuda.synchronize()
+        ev0.record()
+        run_loop(stream)
+        ev1.record()
+        torch.cuda.synchronize()
+        eager_ms = ev0.elapsed_time(ev1) / T
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run_loop(side.cuda_stream)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run_loop(torch.cuda.current_stream().cuda_stream)
+        graph.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        graph.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        graph_ms = ev0.elapsed_time(ev1) / T
+        del graph
+        loop = {
+            "steps": T,
+            "keys_appended_per_step": w.B * w.Hkv,
+            "context": [n0 + 1, w.N],
+            "eager_ms_per_step": round(eager_ms, 5),
+            "graph_ms_per_step": round(graph_ms, 5),
+            "graph_tokens_per_s": round(w.B / (graph_ms * 1e-3), 1),
+        }
+
     # ---- prefill hashing (bf16 MFMA projections, fused sign packing and
     # value norms) on its own workload, reported beside the decode figure
     prefill = None
@@ -402,6 +474,7 @@ def main():
         "kernel_ms": {k: round(v, 5) for k, v in kernel_ms.items()},
         "roofline": roofline,
         "dense_baseline": dense,
+        "decode_loop": loop,
         "prefill_hash": prefill,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),

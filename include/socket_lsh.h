@@ -94,16 +94,20 @@ const char* socket_last_error(void);
  *   vnorm  [n_heads, head_stride_rows]   float32 (output, Euclidean norm)
  *
  * n_heads is B*Hkv. Appending keys at row offset o of every head works by
- * passing K, V, ids and vnorm advanced by o rows with the same stride.
+ * passing K, V, ids and vnorm advanced by o rows with the same stride. A
+ * decode loop appends one key per head and step: bf16 calls of at most 32
+ * keys in all run as one launch (one block per key), and their ids and
+ * norms equal those a prefill of the same rows gives, bit for bit.
  * Bucket ids are exact: the sign of every projection is that of the exact
  * dot product (projections too close to zero for the fast float32 path are
  * re-evaluated in extended precision). n_keys == 0 is a no-op.
  *
  * Workspace: socket_hash_keys_workspace_bytes(dtype, n_heads, n_keys, d, L,
  * P) bytes of device memory, 256-byte aligned (0 bytes, NULL allowed, for
- * SOCKET_DTYPE_F32). It holds the transposed hyperplanes and the list of
- * projections settled in extended precision after the main pass; its
- * contents on entry do not matter. A smaller or misaligned workspace returns
+ * SOCKET_DTYPE_F32). It holds the transposed hyperplanes, the list of
+ * projections settled in extended precision after the main pass and a
+ * record of which wave hashed each 32-key tile; its contents on entry do not
+ * matter. A smaller or misaligned workspace returns
  * SOCKET_ERR_WORKSPACE. K, V and R must be 16-byte aligned.
  */
 size_t socket_hash_keys_workspace_bytes(socket_dtype dtype, int64_t n_heads,

@@ -43,8 +43,10 @@
 //     overflowed. Either way the bucket ids are those of the exact dot
 //     products.
 //
-// f32 path (small inputs): one thread per key, float64 dot products with the
-// same certification and a serial double-double fallback.
+// f32 path: one thread per key, float64 dot products with the same
+// certification and a serial double-double fallback. bf16 inputs of at most
+// 32 keys (the keys a decode step appends) take one launch of one block per
+// key and one thread per hyperplane column, with the same arithmetic.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -618,10 +620,13 @@ __global__ __launch_bounds__(256) void hash_redo_kernel(
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void hash_keys_f32_kernel(
-    const float* __restrict__ K, const float* __restrict__ V,
-    const float* __restrict__ R, int64_t n_heads, int64_t n_keys,
+__device__ __forceinline__ float load_elem(const float* p, int64_t i) { return p[i]; }
+
+// The f32 path: one thread per key.
+template <int D, typename T>
+__global__ __launch_bounds__(256) void hash_keys_direct_kernel(
+    const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ R, int64_t n_heads, int64_t n_keys,
     int64_t stride, int L, int P, uint8_t* __restrict__ ids,
     float* __restrict__ vnorm) {
   const int64_t gidx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -632,11 +637,12 @@ __global__ __launch_bounds__(256) void hash_keys_f32_kernel(
   constexpr double kBound = 2.0 * D * 0x1p-53;
 
   float kr[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) kr[i] = load_elem(K, off * D + i);
   double vs = 0.0;
 #pragma unroll
   for (int i = 0; i < D; ++i) {
-    kr[i] = K[off * D + i];
-    const double v = V[off * D + i];
+    const double v = load_elem(V, off * D + i);
     vs += v * v;
   }
   vnorm[off] = (float)sqrt(vs);
@@ -648,14 +654,14 @@ __global__ __launch_bounds__(256) void hash_keys_f32_kernel(
       double y = 0.0, mag = 0.0;
 #pragma unroll
       for (int i = 0; i < D; ++i) {
-        const double p = (double)kr[i] * (double)R[(int64_t)i * C + c];
+        const double p = (double)kr[i] * (double)load_elem(R, (int64_t)i * C + c);
         y += p;
         mag += fabs(p);
       }
       if (fabs(y) <= kBound * mag) {
         double h = 0.0, lo = 0.0;
         for (int i = 0; i < D; ++i)
-          dd_add(h, lo, (double)kr[i] * (double)R[(int64_t)i * C + c], 0.0, h,
+          dd_add(h, lo, (double)kr[i] * (double)load_elem(R, (int64_t)i * C + c), 0.0, h,
                  lo);
         y = h;
       }
@@ -665,9 +671,68 @@ __global__ __launch_bounds__(256) void hash_keys_f32_kernel(
   }
 }
 
+// A few bf16 keys (a decode step's appended ones): one block per key, one
+// thread per hyperplane column (a second pass for C > 256). Each projection
+// is the float64 sum of the exact products over the key row (staged in
+// LDS) and column c of R (consecutive threads read consecutive columns),
+// certified against the rounding bound of the sum of |products|, else
+// recomputed in double-double; the sign bits meet in LDS and threads
+// l < L write the id bytes. The value norm follows the main kernel's
+// arithmetic exactly (bf16 dot2 steps per half-row, then the halves).
+template <int D>
+__global__ __launch_bounds__(256) void hash_keys_small_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ R, int64_t n_keys, int64_t stride, int L, int P,
+    uint8_t* __restrict__ ids, float* __restrict__ vnorm) {
+  __shared__ float kr[D];
+  __shared__ uint32_t bits[kMaxColWords];
+  const int64_t key = blockIdx.x;
+  const int64_t off = (key / n_keys) * stride + key % n_keys;
+  const int C = L * P;
+  constexpr double kBound = 2.0 * D * 0x1p-53;
+  const int t = threadIdx.x;
+  if (t < D) kr[t] = bf16_bits_to_f32(K[off * D + t]);
+  if (t < kMaxColWords) bits[t] = 0u;
+  if (t == 0) {
+    const u32x4_t* vrow = reinterpret_cast<const u32x4_t*>(V + off * D);
+    float half[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      half[h] = 0.f;
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) half[h] = sumsq_bf16x8(vrow[h * (D / 16) + c], half[h]);
+    }
+    vnorm[off] = __builtin_amdgcn_sqrtf(half[0] + half[1]);
+  }
+  __syncthreads();
+  for (int c = t; c < C; c += blockDim.x) {
+    double y = 0.0, mag = 0.0;
+#pragma unroll 8
+    for (int i = 0; i < D; ++i) {
+      const double p = (double)kr[i] * (double)bf16_bits_to_f32(R[(int64_t)i * C + c]);
+      y += p;
+      mag += fabs(p);
+    }
+    if (fabs(y) <= kBound * mag) {
+      double h = 0.0, lo = 0.0;
+      for (int i = 0; i < D; ++i)
+        dd_add(h, lo, (double)kr[i] * (double)bf16_bits_to_f32(R[(int64_t)i * C + c]), 0.0, h,
+               lo);
+      y = h;
+    }
+    if (y > 0.0) atomicOr(&bits[c >> 5], 1u << (c & 31));
+  }
+  __syncthreads();
+  for (int l = t; l < L; l += blockDim.x)
+    ids[off * L + l] = (uint8_t)extract_bits(bits, l * P, P);
+}
+
 // --------------------------------------------------------------- launchers
 
 constexpr int kMaxHashBlocks = 256;  // one per CU
+// bf16 inputs of at most this many keys (the keys a decode step appends,
+// one per KV head) go to the one-launch direct kernel
+constexpr int64_t kDirectMaxKeys = 32;
 
 struct HashWs {
   uint16_t* rt;
@@ -739,6 +804,16 @@ hipError_t launch_hash_keys_bf16(const uint16_t* K, const uint16_t* V,
                                  int P, uint8_t* ids, float* vnorm, void* ws,
                                  hipStream_t stream) {
   if (n_heads == 0 || n_keys == 0) return hipSuccess;
+  if (n_heads * n_keys <= kDirectMaxKeys) {
+    const dim3 grid((unsigned)(n_heads * n_keys));
+    if (d == 128)
+      launch_kernel(hash_keys_small_kernel<128>, grid, dim3(256), 0, stream, K, V, R, n_keys,
+                    stride, L, P, ids, vnorm);
+    else
+      launch_kernel(hash_keys_small_kernel<64>, grid, dim3(256), 0, stream, K, V, R, n_keys,
+                    stride, L, P, ids, vnorm);
+    return hipGetLastError();
+  }
   const int C = L * P;
   const int64_t tph = (n_keys + kTileKeys - 1) / kTileKeys;
   if (n_heads * tph >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
@@ -803,10 +878,10 @@ hipError_t launch_hash_keys_f32(const float* K, const float* V, const float* R,
   if (total == 0) return hipSuccess;
   const int grid = (int)((total + 255) / 256);
   if (d == 128)
-    launch_kernel(hash_keys_f32_kernel<128>, dim3(grid), dim3(256), 0,
+    launch_kernel(hash_keys_direct_kernel<128, float>, dim3(grid), dim3(256), 0,
                   stream, K, V, R, n_heads, n_keys, stride, L, P, ids, vnorm);
   else
-    launch_kernel(hash_keys_f32_kernel<64>, dim3(grid), dim3(256), 0,
+    launch_kernel(hash_keys_direct_kernel<64, float>, dim3(grid), dim3(256), 0,
                   stream, K, V, R, n_heads, n_keys, stride, L, P, ids, vnorm);
   return hipGetLastError();
 }

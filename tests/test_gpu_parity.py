@@ -541,6 +541,102 @@ def test_decode_replays_from_a_hip_graph():
     del g
 
 
+def _append_and_decode(Q, K, V, R, ids, vn, w, n, ws, out, idx, sc=None):
+    """One decode-loop step: hash the key appended at row n - 1 of every head
+    (n = 1 at that offset), then decode over the first n keys."""
+    S.hash_keys(K, V, R, w.L, w.P, n_keys=1, ids=ids, vnorm=vn, row_offset=n - 1)
+    S.decode(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, n_keys=n, out=out, idx_out=idx,
+             scores_out=sc, workspace=ws)
+
+
+def test_decode_loop_appends_one_key_per_step():
+    """Decode loop: every step appends one key per KV head (hashed alone,
+    through the one-launch path) and decodes over the grown cache. After each
+    step the ids and norms equal a prefill of the same rows bit for bit, and
+    the step matches the oracle (scores, exact selection on those scores,
+    output over the selection)."""
+    w = W.custom_workload(B=1, Hq=8, Hkv=2, d=128, N=1030, dtype="bf16", L=32, P=8,
+                          tau=0.3, k=64, lognormal_v=True)
+    log("decode loop with appends")
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=8)
+    n0 = 1024
+    ids = torch.zeros((w.B, w.Hkv, w.N, w.L), dtype=torch.uint8, device=DEV)
+    vn = torch.zeros((w.B, w.Hkv, w.N), dtype=torch.float32, device=DEV)
+    S.hash_keys(K, V, R, w.L, w.P, n_keys=n0, ids=ids, vnorm=vn)
+    full_ids, full_vn = S.hash_keys(K, V, R, w.L, w.P)
+    ws = torch.empty(S.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, w.N, w.L, w.P, w.k),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(Q)
+    kk = min(w.k, n0)
+    for t in range(w.N - n0):
+        n = n0 + t + 1
+        Qt = W.make_query(w, DEV, seed=8, step=t)
+        idx = torch.empty((w.B, w.Hq, kk), dtype=torch.int32, device=DEV)
+        sc = torch.empty((w.B, w.Hq, n), dtype=torch.float32, device=DEV)
+        _append_and_decode(Qt, K, V, R, ids, vn, w, n, ws, out, idx, sc)
+        torch.cuda.synchronize()
+        assert torch.equal(ids[:, :, :n], full_ids[:, :, :n]), f"ids after step {t}"
+        assert torch.equal(vn[:, :, :n], full_vn[:, :, :n]), f"norms after step {t}"
+        p_ref = O.soft_bucket_probs(f64(Qt), f64(R), w.L, w.P, tau32(w.tau))
+        sc_np, idx_np = sc.cpu().numpy(), idx.cpu().numpy()
+        ref_sc = O.soft_scores(p_ref, ids[:, :, :n].cpu().numpy(), f64(vn[:, :, :n]), w.G)
+        assert_close_rel(sc_np, ref_sc, 1e-5, 1e-30, f"scores step {t}")
+        for h in range(w.Hq):
+            assert np.array_equal(idx_np[0, h], O.topk_indices(sc_np[0, h], w.k)), (t, h)
+        ref_out = O.subset_attention(f64(Qt), f64(K[:, :, :n]), f64(V[:, :, :n]), idx_np, w.G)
+        assert np.max(np.abs(f64(out) - ref_out)) <= 2e-2, f"output step {t}"
+
+
+def test_decode_loop_replays_from_one_hip_graph():
+    """Four steps of the decode loop (append, then decode over the grown
+    cache) captured in one HIP graph: two replays, with eager work between
+    them, reproduce the eager loop's outputs and selections bit for bit."""
+    w = W.custom_workload(B=2, Hq=8, Hkv=2, d=128, N=4100, dtype="bf16", L=32, P=8,
+                          tau=0.3, k=256, lognormal_v=True)
+    log("decode loop graph")
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=9)
+    n0, steps = 4096, 4
+    qs = [W.make_query(w, DEV, seed=9, step=t) for t in range(steps)]
+    ws = torch.empty(S.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, w.N, w.L, w.P, w.k),
+                     dtype=torch.uint8, device=DEV)
+    outs = [torch.empty_like(Q) for _ in range(steps)]
+    idxs = [torch.empty((w.B, w.Hq, w.kk), dtype=torch.int32, device=DEV) for _ in range(steps)]
+
+    def fresh_cache():
+        ids = torch.zeros((w.B, w.Hkv, w.N, w.L), dtype=torch.uint8, device=DEV)
+        vn = torch.zeros((w.B, w.Hkv, w.N), dtype=torch.float32, device=DEV)
+        S.hash_keys(K, V, R, w.L, w.P, n_keys=n0, ids=ids, vnorm=vn)
+        return ids, vn
+
+    ids, vn = fresh_cache()
+    for t in range(steps):
+        _append_and_decode(qs[t], K, V, R, ids, vn, w, n0 + t + 1, ws, outs[t], idxs[t])
+    torch.cuda.synchronize()
+    ref = [(o.clone(), i.clone()) for o, i in zip(outs, idxs)]
+    ids, vn = fresh_cache()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on a side stream before capture
+        _append_and_decode(qs[0], K, V, R, ids, vn, w, n0 + 1, ws, outs[0], idxs[0])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t in range(steps):
+            _append_and_decode(qs[t], K, V, R, ids, vn, w, n0 + t + 1, ws, outs[t], idxs[t])
+    for rep in range(2):
+        for o in outs:
+            o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for t in range(steps):
+            assert torch.equal(outs[t], ref[t][0]), (rep, t)
+            assert torch.equal(idxs[t], ref[t][1]), (rep, t)
+        busy = (K[0, 0, :4096].float() * 2.0).sum()  # eager work between replays
+        assert torch.isfinite(busy)
+    del g
+
+
 def test_decode_identical_group_queries_give_identical_outputs():
     w = W.custom_workload(B=1, Hq=8, Hkv=2, d=128, N=4000, dtype="bf16", L=32, P=8,
                           tau=0.3, k=256, lognormal_v=True)
