@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import json
+import math
 import os
 import sys
 import time
@@ -54,6 +55,8 @@ def parse():
                     help="leave out the decode loop with one appended key per KV head "
                          "and step (eager, and the same steps as one HIP graph)")
     ap.add_argument("--loop-steps", type=int, default=64)
+    ap.add_argument("--skip-ranking-study", action="store_true",
+                    help="leave out the soft-versus-hard LSH ranking comparison")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 4 times (reference for HBM "
                          "byte counters) and exit")
@@ -441,6 +444,51 @@ def main():
             "graph_tokens_per_s": round(w.B / (graph_ms * 1e-3), 1),
         }
 
+    # ---- soft versus hard LSH scores (the tau -> 0 one-hot table) on layer
+    # 0's cache and step 0's queries: per query row, the Pearson correlation
+    # of the collision sum (score / value norm) with the true q . k / sqrt(d),
+    # and the recall of the top-k keys by attention mass (q . k / sqrt(d) +
+    # log |v|); means over the B * Hq rows. Analysis only, not the path.
+    study = None
+    if not args.skip_ranking_study:
+        K0, V0, R0, ids0, vn0 = layers[0]
+        q0 = queries[0][0]
+        soft = S.score(S.bucket_probs(q0, R0, w.Hkv, w.L, w.P, w.tau), ids0, vn0, w.Hq)
+        hard = S.score(S.hard_bucket_table(q0, R0, w.Hkv, w.L, w.P), ids0, vn0, w.Hq)
+        G = w.Hq // w.Hkv
+        kk = min(w.k, w.N)
+        acc = {"pearson_soft": 0.0, "pearson_hard": 0.0, "recall_soft": 0.0, "recall_hard": 0.0}
+        for b in range(w.B):
+            kf = K0[b].float()                                   # [Hkv, N, d]
+            qf = q0[b].float().view(w.Hkv, G, w.d).transpose(1, 2).contiguous()  # [Hkv, d, G]
+            logit = torch.matmul(kf, qf).permute(0, 2, 1).reshape(w.Hq, w.N) / math.sqrt(w.d)
+            vnr = vn0[b].repeat_interleave(G, dim=0)             # [Hq, N]
+            mass = logit + torch.log(vnr.clamp_min(1e-30))
+            top_true = torch.zeros_like(mass, dtype=torch.bool).scatter_(
+                1, torch.topk(mass, kk, dim=1).indices, True)
+            for name, sc in (("soft", soft[b]), ("hard", hard[b])):
+                coll = sc / vnr.clamp_min(1e-30)
+                x = coll - coll.mean(1, keepdim=True)
+                y = logit - logit.mean(1, keepdim=True)
+                r = (x * y).sum(1) / (x.norm(dim=1) * y.norm(dim=1)).clamp_min(1e-30)
+                acc["pearson_" + name] += r.sum().item()
+                sel = torch.topk(sc, kk, dim=1).indices
+                acc["recall_" + name] += top_true.gather(1, sel).float().mean(1).sum().item()
+        rows = w.B * w.Hq
+        study = {k: round(v / rows, 4) for k, v in acc.items()}
+        study.update({"rows": rows, "k": kk, "tau": w.tau})
+        if w.planted > 0:
+            # the planted keys (cos 0.9 with the step-0 query of the group's
+            # first head): the share of them inside that head's top-k
+            pos = W.planted_positions(w, seed=0, layer=0).to(dev)   # [B, Hkv, planted]
+            for name, sc in (("soft", soft), ("hard", hard)):
+                hit = 0.0
+                for b in range(w.B):
+                    for g in range(w.Hkv):
+                        sel = torch.topk(sc[b, g * G], kk).indices
+                        hit += torch.isin(pos[b, g], sel).float().mean().item()
+                study["planted_recall_" + name] = round(hit / (w.B * w.Hkv), 4)
+
     # ---- prefill hashing (bf16 MFMA projections, fused sign packing and
     # value norms) on its own workload, reported beside the decode figure
     prefill = None
@@ -475,6 +523,7 @@ def main():
         "roofline": roofline,
         "dense_baseline": dense,
         "decode_loop": loop,
+        "ranking_study": study,
         "prefill_hash": prefill,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),

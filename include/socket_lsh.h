@@ -139,6 +139,23 @@ socket_status socket_bucket_probs(const void* Q, const void* R,
                                   void* stream);
 
 /*
+ * Hard-LSH comparison: the tau -> 0 limit of socket_bucket_probs, a one-hot
+ * table with 1 at the query's own bucket of every table (the bucket of its
+ * projection signs; a projection of exactly 0 splits its bit 1/2 : 1/2, as
+ * every soft table does). socket_score on this table gives each key its
+ * value norm times the number of tables in which it collides with the
+ * query: the hard collision count the soft score replaces.
+ * Defines: the tau -> 0 limit and the soft-versus-hard comparison of the
+ * German page "SOCKET: SOft Collision Kernel EsTimator for Sparse
+ * Attention", section "Theoretische Grundlage" (Stabilität, Korrelation).
+ *
+ *   Q, R, table: as for socket_bucket_probs.
+ */
+socket_status socket_hard_bucket_table(const void* Q, const void* R, socket_dtype dtype,
+                                      int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t L,
+                                      int32_t P, float* table, void* stream);
+
+/*
  * Decode stage 2: soft collision scores.
  * Defines: step 3 of the soft-LSH mechanism (per key, the probability mass
  * on its own bucket summed over the L tables, weighted by its value norm).

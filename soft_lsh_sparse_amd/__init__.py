@@ -11,6 +11,7 @@ from .api import (  # noqa: F401
     decode,
     decode_workspace_bytes,
     dense_attn,
+    hard_bucket_table,
     hash_keys,
     score,
     sparse_attn,

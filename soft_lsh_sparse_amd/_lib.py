@@ -37,6 +37,8 @@ SIGNATURES = {
     "socket_bucket_probs": (c_int, [c_void_p, c_void_p, c_int, c_int32, c_int32,
                                     c_int32, c_int32, c_int32, c_int32, c_float,
                                     c_void_p, c_void_p]),
+    "socket_hard_bucket_table": (c_int, [c_void_p, c_void_p, c_int, c_int32, c_int32, c_int32,
+                                         c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     "socket_score": (c_int, [c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                              c_int32, c_int64, c_int64, c_int32, c_int32,
                              c_void_p, c_void_p]),

@@ -93,6 +93,20 @@ def bucket_probs(Q: torch.Tensor, R: torch.Tensor, Hkv: int, L: int, P: int,
     return table
 
 
+def hard_bucket_table(Q: torch.Tensor, R: torch.Tensor, Hkv: int, L: int,
+                      P: int) -> torch.Tensor:
+    """One-hot table [B, Hkv, 2^P, L, G] (float32) at the queries' own buckets:
+    the tau -> 0 limit of bucket_probs (hard LSH)."""
+    lib = _lib.load()
+    B, Hq, d = Q.shape
+    G = Hq // Hkv
+    table = torch.empty((B, Hkv, 2 ** P, L, G), dtype=torch.float32, device=Q.device)
+    st = lib.socket_hard_bucket_table(_dev(Q, "Q"), _dev(R, "R"), _dtype_code(Q), B, Hq, Hkv,
+                                      d, L, P, _dev(table, "table"), _stream(Q))
+    check(st, "socket_hard_bucket_table")
+    return table
+
+
 def score(table: torch.Tensor, ids: torch.Tensor, vnorm: torch.Tensor,
           Hq: int, n_keys: int | None = None) -> torch.Tensor:
     """Soft collision scores [B, Hq, n_keys] from a table and the hash cache.

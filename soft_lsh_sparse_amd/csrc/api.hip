@@ -223,6 +223,24 @@ socket_status socket_bucket_probs(const void* Q, const void* R,
   return from_hip(err, "socket_bucket_probs launch");
 }
 
+socket_status socket_hard_bucket_table(const void* Q, const void* R, socket_dtype dtype,
+                                      int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t L,
+                                      int32_t P, float* table, void* stream) {
+  SOCKET_TRY(check_dtype(dtype));
+  SOCKET_TRY(check_heads(B, Hq, Hkv));
+  SOCKET_TRY(check_d(d));
+  SOCKET_TRY(check_lp(L, P));
+  if (!Q || !R || !table)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (!aligned16(R))
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "R must be 16-byte aligned");
+  // tau = 0: 2 / tau = +inf makes every bit weight 1 or 0 (1/2 each for a
+  // projection of exactly 0), the limit of the soft weights
+  hipError_t err = launch_bucket_probs(Q, R, dtype == SOCKET_DTYPE_BF16, B, Hq, Hkv, d, L, P,
+                                       0.0f, table, static_cast<hipStream_t>(stream));
+  return from_hip(err, "socket_hard_bucket_table launch");
+}
+
 socket_status socket_score(const float* table, const uint8_t* ids,
                            const float* vnorm, int32_t B, int32_t Hq,
                            int32_t Hkv, int64_t n_keys,

@@ -214,3 +214,20 @@ def test_dense_attn_workspace_covers_every_chunk(lib):
     assert lib.socket_dense_attn_workspace_bytes(4, 32, 128, 131072) == 4 * 32 * 128 * 130 * 4
     assert lib.socket_dense_attn_workspace_bytes(1, 1, 64, 1) == 66 * 4
     assert lib.socket_dense_attn_workspace_bytes(1, 1, 64, 0) == 0
+
+
+def test_hard_bucket_table_rejects_invalid_arguments(lib):
+    args = dict(Q=FAKE, R=FAKE, dt=1, B=1, Hq=8, Hkv=2, d=128, L=8, P=4, table=FAKE)
+
+    def call(**over):
+        a = dict(args)
+        a.update(over)
+        return lib.socket_hard_bucket_table(a["Q"], a["R"], a["dt"], a["B"], a["Hq"], a["Hkv"],
+                                            a["d"], a["L"], a["P"], a["table"], None)
+
+    assert call(dt=7) == _lib.SOCKET_ERR_INVALID_ARGUMENT
+    assert call(Hq=7) == _lib.SOCKET_ERR_INVALID_ARGUMENT
+    assert call(P=0) == _lib.SOCKET_ERR_INVALID_ARGUMENT
+    assert call(Q=None) == _lib.SOCKET_ERR_INVALID_ARGUMENT
+    assert call(table=None) == _lib.SOCKET_ERR_INVALID_ARGUMENT
+    assert call(R=FAKE + 8) == _lib.SOCKET_ERR_INVALID_ARGUMENT

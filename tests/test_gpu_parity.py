@@ -317,6 +317,41 @@ def test_sparse_attn_stage(B, Hq, Hkv, d, N, kk, dt):
     assert np.max(np.abs(f64(out) - ref)) <= tol
 
 
+# ------------------------------------------------ hard-LSH comparison
+
+@pytest.mark.parametrize("dt,L,P", [("bf16", 32, 8), ("f32", 8, 4), ("bf16", 11, 6)])
+def test_hard_bucket_table_is_one_hot_at_the_query_buckets(dt, L, P):
+    w = W.custom_workload(B=2, Hq=8, Hkv=2, d=128, N=64, dtype=dt, L=L, P=P)
+    Q, _, _, R = W.make_decode_inputs(w, DEV, seed=15)
+    table = S.hard_bucket_table(Q, R, w.Hkv, L, P)
+    torch.cuda.synchronize()
+    t = table.cpu().numpy()                       # [B, Hkv, 2^P, L, G]
+    hb = O.hard_query_buckets(f64(Q), f64(R), L, P)  # [B, Hq, L]
+    onehot = np.zeros_like(t)
+    G = w.Hq // w.Hkv
+    for b in range(w.B):
+        for h in range(w.Hq):
+            for l in range(L):
+                onehot[b, h // G, hb[b, h, l], l, h % G] = 1.0
+    assert np.array_equal(t, onehot)
+
+
+def test_hard_scores_are_value_norm_weighted_collision_counts():
+    w = W.custom_workload(B=1, Hq=8, Hkv=2, d=128, N=5000, dtype="bf16", L=32, P=8,
+                          lognormal_v=True)
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=16)
+    ids, vn = S.hash_keys(K, V, R, w.L, w.P)
+    sc = S.score(S.hard_bucket_table(Q, R, w.Hkv, w.L, w.P), ids, vn, w.Hq)
+    torch.cuda.synchronize()
+    hb = O.hard_query_buckets(f64(Q), f64(R), w.L, w.P)       # [B, Hq, L]
+    ids_np = ids.cpu().numpy().astype(np.int64)              # [B, Hkv, N, L]
+    G = w.Hq // w.Hkv
+    counts = np.stack([(ids_np[0, h // G] == hb[0, h][None, :]).sum(-1)
+                       for h in range(w.Hq)])[None]          # [B, Hq, N]
+    ref = counts * f64(vn)[:, np.arange(w.Hq) // G]
+    assert_close_rel(sc.cpu().numpy(), ref, 1e-6, 0.0, "hard scores")
+
+
 # ------------------------------------------------ dense attention baseline
 
 @pytest.mark.parametrize("B,Hq,Hkv,d,N,dt", [
