@@ -63,6 +63,7 @@ __all__ = [
     "query_projections",
     "soft_bucket_probs",
     "soft_scores",
+    "group_scores",
     "topk_indices",
     "subset_attention",
     "decode",
@@ -203,6 +204,19 @@ def soft_scores(p, ids, vnorm, G: int) -> np.ndarray:
             mass = p[b, h][tables, ids[b, g].astype(np.intp)]  # [N, L]
             out[b, h] = vnorm[b, g] * mass.sum(axis=-1)
     return out
+
+
+def group_scores(p, ids, vnorm, G: int) -> np.ndarray:
+    """GQA group-shared score (a reading: the pages leave GQA open): for KV
+    head g, the sum of the soft scores of the G query heads of its group,
+    s[b, g, n] = sum_j soft_scores[b, g*G + j, n]; one top-k of these gives
+    the group one shared index set.
+
+    p [B, Hq, L, 2^P]; ids [B, Hkv, N, L]; vnorm [B, Hkv, N] -> [B, Hkv, N].
+    """
+    s = soft_scores(p, ids, vnorm, G)
+    B, Hq, N = s.shape
+    return s.reshape(B, Hq // G, G, N).sum(axis=2)
 
 
 # ---------------------------------------------------------------------------

@@ -254,6 +254,45 @@ def test_scores_gqa_uses_floor_h_over_g():
     assert big[3] > 50 * max(big[0], big[1], big[4], big[5])
 
 
+def test_group_scores_reduce_to_soft_scores_and_sum_the_group():
+    # G = 1: the group score is the head's own soft score
+    Q, K, V, R, L, P, tau = _small_problem(33, B=1, Hq=3, Hkv=3)
+    ids = O.hash_keys(K, R, L, P)
+    vn = O.value_norms(V)
+    p = O.soft_bucket_probs(Q, R, L, P, tau)
+    assert np.array_equal(O.group_scores(p, ids, vn, 1), O.soft_scores(p, ids, vn, 1))
+    # every head of a group asks the same query: G times one head's score,
+    # and the shared top-k is that head's top-k
+    Q, K, V, R, L, P, tau = _small_problem(34, B=1, Hq=4, Hkv=2)
+    Q[:, 1] = Q[:, 0]
+    Q[:, 3] = Q[:, 2]
+    ids = O.hash_keys(K, R, L, P)
+    vn = O.value_norms(V)
+    p = O.soft_bucket_probs(Q, R, L, P, tau)
+    gs = O.group_scores(p, ids, vn, 2)
+    one = O.soft_scores(p, ids, vn, 2)
+    assert np.allclose(gs[:, 0], 2 * one[:, 0], rtol=1e-14, atol=0)
+    assert np.allclose(gs[:, 1], 2 * one[:, 2], rtol=1e-14, atol=0)
+    k = 5
+    assert np.array_equal(O.topk_indices(gs[0, 0], k), O.topk_indices(one[0, 0], k))
+
+
+def test_group_scores_brute_force():
+    Q, K, V, R, L, P, tau = _small_problem(35, B=1, Hq=4, Hkv=2)
+    ids = O.hash_keys(K, R, L, P)
+    vn = O.value_norms(V)
+    p = O.soft_bucket_probs(Q, R, L, P, tau)
+    gs = O.group_scores(p, ids, vn, 2)
+    N = ids.shape[2]
+    for g in range(2):
+        for n in range(N):
+            tot = 0.0
+            for j in range(2):
+                for l in range(L):
+                    tot += float(p[0, 2 * g + j, l, int(ids[0, g, n, l])])
+            assert abs(gs[0, g, n] - float(vn[0, g, n]) * tot) <= 1e-12 * max(1.0, abs(gs[0, g, n]))
+
+
 # --------------------------------------------------------------------- top-k
 
 def test_topk_golden(golden_dir):
