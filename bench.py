@@ -55,6 +55,8 @@ def parse():
                     help="leave out the decode loop with one appended key per KV head "
                          "and step (eager, and the same steps as one HIP graph)")
     ap.add_argument("--loop-steps", type=int, default=64)
+    ap.add_argument("--skip-group-shared", action="store_true",
+                    help="leave out the GQA group-shared selection variant")
     ap.add_argument("--skip-ranking-study", action="store_true",
                     help="leave out the soft-versus-hard LSH ranking comparison")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -444,6 +446,38 @@ def main():
             "graph_tokens_per_s": round(w.B / (graph_ms * 1e-3), 1),
         }
 
+    # ---- GQA group-shared variant (one index set per KV head from the
+    # group's summed scores; one gather serves the G heads), timed like the
+    # decode on the same rotated caches and queries
+    group = None
+    if not args.skip_group_shared:
+        gws_bytes = lib.socket_decode_group_shared_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, w.N,
+                                                                   w.L, w.P, w.k)
+        gws = torch.empty(gws_bytes, dtype=torch.uint8, device=dev)
+        gfn = lib.socket_decode_group_shared
+
+        def group_args(step):
+            a = list(decode_args(step))
+            a[18] = None                 # idx_out: the variant's is [B, Hkv, kk]
+            a[20], a[21] = gws.data_ptr(), gws_bytes
+            return tuple(a)
+
+        glist = [group_args(s_) for s_ in range(total)]
+        for s_ in range(args.warmup):
+            st = gfn(*glist[s_])
+            if st:
+                _lib.check(st, "socket_decode_group_shared")
+        torch.cuda.synchronize()
+        ev0.record()
+        for s_ in range(args.warmup, total):
+            gfn(*glist[s_])
+        ev1.record()
+        torch.cuda.synchronize()
+        gms = ev0.elapsed_time(ev1) / args.steps
+        group = {"ms_per_step": round(gms, 5), "tokens_per_s": round(w.B / (gms * 1e-3), 1),
+                 "speedup_vs_per_head": round(ms_per_step / gms, 3),
+                 "selection": "one shared top-k per KV head by the group's summed scores"}
+
     # ---- soft versus hard LSH scores (the tau -> 0 one-hot table) on layer
     # 0's cache and step 0's queries: per query row, the Pearson correlation
     # of the collision sum (score / value norm) with the true q . k / sqrt(d),
@@ -524,6 +558,7 @@ def main():
         "dense_baseline": dense,
         "decode_loop": loop,
         "ranking_study": study,
+        "group_shared_variant": group,
         "prefill_hash": prefill,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),

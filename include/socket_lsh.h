@@ -215,6 +215,33 @@ socket_status socket_sparse_attn(const void* Q, const void* K, const void* V,
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * Variant: GQA group-shared selection. One index set per KV head: the keys
+ * are ranked by the sum of the soft scores of the G query heads of the group
+ * (equivalently, by the group table sum_j p[u, l, j] in place of each head's
+ * own), the kk best are kept (ties to the lower index), and every head of
+ * the group attends over that same set, so one gather of K and V rows serves
+ * the G heads. The pages leave GQA open (page "Resumen Técnico: SOCKET -
+ * Estimador de Núcleo de Colisión Suave para Atención Escasa", section
+ * "Mecanismo Central: LSH Suave"); socket_decode keeps per-head selection.
+ *
+ * Arguments as for socket_decode, except:
+ *   idx_out     optional, [B, Hkv, min(k, n_keys)] int32, ascending
+ *   scores_out  optional, [B, Hkv, n_keys] float32 group scores
+ * Hq / Hkv <= 8 and min(k, n_keys) <= 2^20, else SOCKET_ERR_UNSUPPORTED.
+ * Workspace: socket_decode_group_shared_workspace_bytes(...) bytes.
+ */
+size_t socket_decode_group_shared_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                                                  int64_t n_keys, int32_t L, int32_t P,
+                                                  int64_t k);
+socket_status socket_decode_group_shared(const void* Q, const void* K, const void* V,
+                                         const void* R, const uint8_t* ids, const float* vnorm,
+                                         socket_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                         int32_t d, int64_t n_keys, int64_t head_stride_rows,
+                                         int32_t L, int32_t P, float tau, int64_t k, void* out,
+                                         int32_t* idx_out, float* scores_out, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+/*
  * Baseline: dense attention decoding (every key), the comparison SOCKET's
  * speed-up is stated against.
  * Defines: the dense FlashAttention decoding of the pages' efficiency

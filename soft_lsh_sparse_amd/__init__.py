@@ -9,6 +9,7 @@ from ._lib import SocketError, load  # noqa: F401
 from .api import (  # noqa: F401
     bucket_probs,
     decode,
+    decode_group_shared,
     decode_workspace_bytes,
     dense_attn,
     hard_bucket_table,

@@ -55,6 +55,14 @@ SIGNATURES = {
     "socket_dense_attn": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int32, c_int32,
                                   c_int32, c_int32, c_int64, c_int64, c_void_p, c_void_p,
                                   c_size_t, c_void_p]),
+    "socket_decode_group_shared_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32,
+                                                             c_int32, c_int64, c_int32,
+                                                             c_int32, c_int64]),
+    "socket_decode_group_shared": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                           c_void_p, c_int, c_int32, c_int32, c_int32,
+                                           c_int32, c_int64, c_int64, c_int32, c_int32,
+                                           c_float, c_int64, c_void_p, c_void_p, c_void_p,
+                                           c_void_p, c_size_t, c_void_p]),
     "socket_decode_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32,
                                                  c_int32, c_int64, c_int32,
                                                  c_int32, c_int64]),

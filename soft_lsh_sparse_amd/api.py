@@ -211,3 +211,28 @@ def decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, R: torch.Tensor,
         _dev(workspace, "workspace"), workspace.numel(), _stream(Q))
     check(st, "socket_decode")
     return out, idx_out, scores_out
+
+
+def decode_group_shared(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, R: torch.Tensor,
+                        ids: torch.Tensor, vnorm: torch.Tensor, L: int, P: int, tau: float,
+                        k: int, n_keys: int | None = None, out: torch.Tensor | None = None,
+                        idx_out: torch.Tensor | None = None,
+                        scores_out: torch.Tensor | None = None):
+    """GQA group-shared variant of decode: one index set [B, Hkv, kk] per KV
+    head from the group's summed scores; returns (out, idx_out, scores_out)."""
+    lib = _lib.load()
+    B, Hq, d = Q.shape
+    _, Hkv, S, _ = K.shape
+    n = S if n_keys is None else int(n_keys)
+    if out is None:
+        out = torch.empty_like(Q)
+    need = lib.socket_decode_group_shared_workspace_bytes(B, Hq, Hkv, d, n, L, P, int(k))
+    ws = _workspace(need, Q.device)
+    st = lib.socket_decode_group_shared(
+        _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(R, "R"), _dev(ids, "ids"),
+        _dev(vnorm, "vnorm"), _dtype_code(Q), B, Hq, Hkv, d, n, S, L, P, float(tau), int(k),
+        _dev(out, "out"), _dev(idx_out, "idx_out") if idx_out is not None else None,
+        _dev(scores_out, "scores_out") if scores_out is not None else None,
+        _dev(ws, "workspace"), ws.numel(), _stream(Q))
+    check(st, "socket_decode_group_shared")
+    return out, idx_out, scores_out

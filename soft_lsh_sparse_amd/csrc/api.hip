@@ -355,7 +355,7 @@ socket_status socket_dense_attn(const void* Q, const void* K, const void* V,
     return fail(SOCKET_ERR_WORKSPACE, "dense attention needs %zu workspace bytes, got %zu",
                 plan.partial_bytes, workspace ? workspace_bytes : (size_t)0);
   hipError_t err = launch_dense_attn(Q, K, V, dtype == SOCKET_DTYPE_BF16, plan, head_stride_rows,
-                                     out, static_cast<float*>(workspace),
+                                     nullptr, out, static_cast<float*>(workspace),
                                      static_cast<hipStream_t>(stream));
   return from_hip(err, "socket_dense_attn launch");
 }
@@ -504,9 +504,140 @@ socket_status decode_impl(const void* Q, const void* K, const void* V,
   return from_hip(err, "socket_decode: sparse_attn");
 }
 
+// GQA group-shared variant: the per-KV-head decode layout (one score row
+// per KV head, G = 1 over the group table) plus the heads' full table and
+// the attention partials of the Hq query rows over the kk shared keys.
+struct GroupLayout {
+  DecodeLayout head;   // B rows of Hkv, "G = 1"
+  size_t full_table_off, attn_off, total;
+  DensePlan attn;
+};
+
+GroupLayout group_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t n_keys,
+                         int32_t L, int32_t P, int64_t k) {
+  GroupLayout g{};
+  g.head = decode_layout(B, Hkv, Hkv, d, n_keys, L, P, k);
+  size_t off = g.head.total;
+  g.full_table_off = off;
+  off = align256(off + ((size_t)1 << P) * L * Hq * B * sizeof(float));
+  const int64_t kk = k < n_keys ? k : n_keys;
+  g.attn = plan_dense(B, Hq, Hkv, d, kk);
+  g.attn_off = off;
+  off = align256(off + g.attn.partial_bytes);
+  g.total = off;
+  return g;
+}
+
+socket_status decode_group_impl(const void* Q, const void* K, const void* V, const void* R,
+                                const uint8_t* ids, const float* vnorm, socket_dtype dtype,
+                                int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t n_keys,
+                                int64_t head_stride_rows, int32_t L, int32_t P, float tau,
+                                int64_t k, void* out, int32_t* idx_out, float* scores_out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  SOCKET_TRY(check_decode(dtype, B, Hq, Hkv, d, n_keys, head_stride_rows, L, P, k));
+  if (!(std::isfinite(tau) && tau > 0.f))
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "tau must be finite and > 0");
+  if (!Q || !K || !V || !R || !ids || !vnorm || !out)
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(R))
+    return fail(SOCKET_ERR_INVALID_ARGUMENT, "Q, K, V and R must be 16-byte aligned");
+  if (Hq / Hkv > 8)
+    return fail(SOCKET_ERR_UNSUPPORTED, "at most 8 query heads per KV head");
+  const int64_t kk = k < n_keys ? k : n_keys;
+  if (kk > kMaxDenseKeys)
+    return fail(SOCKET_ERR_UNSUPPORTED, "at most %lld selected keys", (long long)kMaxDenseKeys);
+  const GroupLayout lay = group_layout(B, Hq, Hkv, d, n_keys, L, P, k);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(SOCKET_ERR_WORKSPACE, "group-shared decode needs %zu workspace bytes, got %zu",
+                lay.total, workspace ? workspace_bytes : (size_t)0);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  float* full = reinterpret_cast<float*>(ws + lay.full_table_off);
+  float* gtable = reinterpret_cast<float*>(ws + lay.head.table_off);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + lay.head.idx_off);
+  const bool bf16 = dtype == SOCKET_DTYPE_BF16;
+  const int G = Hq / Hkv;
+  const int rows = B * Hkv;
+  hipError_t err = launch_bucket_probs(Q, R, bf16, B, Hq, Hkv, d, L, P, tau, full, s);
+  if (err != hipSuccess) return from_hip(err, "group-shared decode: bucket_probs");
+  err = launch_group_table_sum(full, B * Hkv, L, P, G, gtable, s);
+  if (err != hipSuccess) return from_hip(err, "group-shared decode: group table");
+  if (kk < n_keys) {
+    // the per-head pipeline at G = 1 over the group tables
+    uint32_t* thr = reinterpret_cast<uint32_t*>(ws + lay.head.thr_off);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + lay.head.cnt_off);
+    uint2* lists = reinterpret_cast<uint2*>(ws + lay.head.list_off);
+    float* rowbuf = scores_out ? scores_out : reinterpret_cast<float*>(ws + lay.head.scores_off);
+    ScoreSelect sel{};
+    sel.table = gtable;
+    sel.ids = ids;
+    sel.vnorm = vnorm;
+    sel.kk = kk;
+    sel.thr = thr;
+    sel.lists = lists;
+    sel.sub_cnt = cnt;
+    err = launch_score_select(sel, B, Hkv, Hkv, n_keys, head_stride_rows, L, P, scores_out,
+                              nullptr, s);
+    if (err != hipSuccess) return from_hip(err, "group-shared decode: score");
+    SelectArgs sa{};
+    sa.n = n_keys;
+    sa.kk = kk;
+    sa.subs = lay.head.score.subs;
+    sa.sub_len = lay.head.score.sub_len;
+    sa.segs = lay.head.score.segs;
+    sa.thr = thr;
+    sa.lists = lists;
+    sa.sub_cnt = cnt;
+    sa.idx = idx;
+    sa.table = gtable;
+    sa.ids = ids;
+    sa.vnorm = vnorm;
+    sa.Hq = Hkv;
+    sa.Hkv = Hkv;
+    sa.L = L;
+    sa.P = P;
+    sa.stride = head_stride_rows;
+    sa.rotated = score_rotated(ids, head_stride_rows, L) ? 1 : 0;
+    sa.scores = rowbuf;
+    err = launch_topk_select(sa, rows, s);
+    if (err != hipSuccess) return from_hip(err, "group-shared decode: topk");
+  } else {
+    if (scores_out) {
+      err = launch_score(gtable, ids, vnorm, B, Hkv, Hkv, n_keys, head_stride_rows, L, P,
+                         scores_out, nullptr, s);
+      if (err != hipSuccess) return from_hip(err, "group-shared decode: score");
+    }
+    err = launch_iota_rows(idx, rows, n_keys, s);
+    if (err != hipSuccess) return from_hip(err, "group-shared decode: topk");
+  }
+  err = launch_dense_attn(Q, K, V, bf16, lay.attn, head_stride_rows, idx, out,
+                          reinterpret_cast<float*>(ws + lay.attn_off), s);
+  return from_hip(err, "group-shared decode: attention");
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t socket_decode_group_shared_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                                                  int64_t n_keys, int32_t L, int32_t P,
+                                                  int64_t k) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || d < 1 || n_keys < 1 || L < 1 || P < 1 || P > 8 || k < 1)
+    return 0;
+  return group_layout(B, Hq, Hkv, d, n_keys, L, P, k).total;
+}
+
+socket_status socket_decode_group_shared(const void* Q, const void* K, const void* V,
+                                         const void* R, const uint8_t* ids, const float* vnorm,
+                                         socket_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                         int32_t d, int64_t n_keys, int64_t head_stride_rows,
+                                         int32_t L, int32_t P, float tau, int64_t k, void* out,
+                                         int32_t* idx_out, float* scores_out, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  return decode_group_impl(Q, K, V, R, ids, vnorm, dtype, B, Hq, Hkv, d, n_keys,
+                           head_stride_rows, L, P, tau, k, out, idx_out, scores_out, workspace,
+                           workspace_bytes, stream);
+}
 
 socket_status socket_decode(const void* Q, const void* K, const void* V,
                             const void* R, const uint8_t* ids,

@@ -61,7 +61,28 @@ __global__ __launch_bounds__(kProbThreads) void bucket_probs_kernel(ProbArgs a) 
   }
 }
 
+// Group table of the GQA group-shared variant: out[bg, u, l] = the sum over
+// the G heads j (in order) of table[bg, u, l, j].
+__global__ __launch_bounds__(256) void group_table_sum_kernel(const float* __restrict__ table,
+                                                              int64_t entries, int G,
+                                                              float* __restrict__ out) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < entries;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    float s = 0.f;
+    for (int j = 0; j < G; ++j) s += table[e * G + j];
+    out[e] = s;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_group_table_sum(const float* table, int bhkv, int L, int P, int G, float* out,
+                                  hipStream_t stream) {
+  const int64_t entries = (int64_t)bhkv * ((int64_t)1 << P) * L;
+  const int grid = (int)std::min<int64_t>((entries + 255) / 256, 1024);
+  launch_kernel(group_table_sum_kernel, dim3(grid), dim3(256), 0, stream, table, entries, G, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_bucket_probs(const void* Q, const void* R, bool bf16, int B,
                                int Hq, int Hkv, int d, int L, int P,

@@ -44,12 +44,14 @@ __device__ __forceinline__ void unpack16d<F32>(const uint4& w, float* f) {
   unpack4_f32(w, f);
 }
 
-// G query heads per KV head; IT loads per tensor and batch.
-template <typename T, int D, int G, int IT>
+// G query heads per KV head; IT loads per tensor and batch. INDEXED: the n
+// keys of KV head gi are the rows idx[gi * n + i] (a shared index set of the
+// group, each in [0, stride)) instead of rows 0..n-1.
+template <typename T, int D, int G, int IT, bool INDEXED>
 __global__ __launch_bounds__(kDenseThreads) void dense_attn_kernel(
     const typename T::storage* __restrict__ Q, const typename T::storage* __restrict__ K,
     const typename T::storage* __restrict__ V, int Hq, int Hkv, int64_t stride, int64_t n,
-    int chunks, float* __restrict__ partial) {
+    int chunks, const int32_t* __restrict__ idx, float* __restrict__ partial) {
   constexpr int EPL = 16 / T::bytes;  // elements per 16-byte load
   constexpr int LPR = D / EPL;        // lanes per key row
   constexpr int KPI = 64 / LPR;       // key rows per wave-wide load
@@ -78,6 +80,26 @@ __global__ __launch_bounds__(kDenseThreads) void dense_attn_kernel(
   const typename T::storage* Kh = K + (int64_t)gi * stride * D + sub * EPL;
   const typename T::storage* Vh = V + (int64_t)gi * stride * D + sub * EPL;
   const int64_t wbeg = (int64_t)chunk * kDenseChunk + wave * kDenseKeysPerWave;
+  // INDEXED: the wave's key rows, one position per lane and register
+  // (positions past n repeat the last one; rows are clamped into the head)
+  constexpr int NREG = kDenseKeysPerWave / 64;
+  int ireg[NREG];
+  if constexpr (INDEXED) {
+    const int32_t* irow = idx + (int64_t)gi * n;
+#pragma unroll
+    for (int r = 0; r < NREG; ++r) {
+      const int64_t p = min<int64_t>(wbeg + r * 64 + lane, n - 1);
+      ireg[r] = (int)min<int64_t>(max(irow[p], 0), stride - 1);
+    }
+  }
+  auto row_of = [&](int bt, int it) -> int64_t {
+    if constexpr (INDEXED) {
+      const int p = bt * KPB + it * KPI + grp;  // position within the wave
+      return __shfl(ireg[p >> 6], p & 63, kWave);
+    } else {
+      return min<int64_t>(wbeg + bt * KPB + it * KPI + grp, n - 1);
+    }
+  };
 
   // Batches of KPB consecutive keys, double-buffered. Keys past n are
   // loaded as row n - 1 (inside the head) and get weight 0.
@@ -93,12 +115,12 @@ __global__ __launch_bounds__(kDenseThreads) void dense_attn_kernel(
   auto issue = [&](int bt) {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int64_t key = min<int64_t>(wbeg + bt * KPB + it * KPI + grp, n - 1);
+      const int64_t key = row_of(bt, it);
       kr[bt & 1][it] = *reinterpret_cast<const uint4*>(Kh + key * D);
     }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int64_t key = min<int64_t>(wbeg + bt * KPB + it * KPI + grp, n - 1);
+      const int64_t key = row_of(bt, it);
       vr[bt & 1][it] = *reinterpret_cast<const uint4*>(Vh + key * D);
     }
   };
@@ -207,12 +229,18 @@ __global__ __launch_bounds__(kDenseThreads) void dense_attn_kernel(
 
 template <typename T, int D, int G>
 hipError_t launch_dense_g(const void* Q, const void* K, const void* V, const DensePlan& p,
-                          int64_t stride, void* out, float* partial, hipStream_t stream) {
+                          int64_t stride, const int32_t* idx, void* out, float* partial,
+                          hipStream_t stream) {
   using S = typename T::storage;
   constexpr int IT = G >= 4 ? 4 : 8;
-  launch_kernel((dense_attn_kernel<T, D, G, IT>), dim3(p.B * p.Hkv * p.chunks),
-                dim3(kDenseThreads), 0, stream, (const S*)Q, (const S*)K, (const S*)V, p.Hq,
-                p.Hkv, stride, p.n, p.chunks, partial);
+  if (idx != nullptr)
+    launch_kernel((dense_attn_kernel<T, D, G, IT, true>), dim3(p.B * p.Hkv * p.chunks),
+                  dim3(kDenseThreads), 0, stream, (const S*)Q, (const S*)K, (const S*)V, p.Hq,
+                  p.Hkv, stride, p.n, p.chunks, idx, partial);
+  else
+    launch_kernel((dense_attn_kernel<T, D, G, IT, false>), dim3(p.B * p.Hkv * p.chunks),
+                  dim3(kDenseThreads), 0, stream, (const S*)Q, (const S*)K, (const S*)V, p.Hq,
+                  p.Hkv, stride, p.n, p.chunks, idx, partial);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_attn_merge(partial, p.B * p.Hq, p.chunks, p.d, T::bytes == 2, out, stream);
@@ -220,12 +248,13 @@ hipError_t launch_dense_g(const void* Q, const void* K, const void* V, const Den
 
 template <typename T, int D>
 hipError_t launch_dense_d(const void* Q, const void* K, const void* V, const DensePlan& p,
-                          int64_t stride, void* out, float* partial, hipStream_t stream) {
+                          int64_t stride, const int32_t* idx, void* out, float* partial,
+                          hipStream_t stream) {
   switch (p.Hq / p.Hkv) {
-    case 1: return launch_dense_g<T, D, 1>(Q, K, V, p, stride, out, partial, stream);
-    case 2: return launch_dense_g<T, D, 2>(Q, K, V, p, stride, out, partial, stream);
-    case 4: return launch_dense_g<T, D, 4>(Q, K, V, p, stride, out, partial, stream);
-    default: return launch_dense_g<T, D, 8>(Q, K, V, p, stride, out, partial, stream);
+    case 1: return launch_dense_g<T, D, 1>(Q, K, V, p, stride, idx, out, partial, stream);
+    case 2: return launch_dense_g<T, D, 2>(Q, K, V, p, stride, idx, out, partial, stream);
+    case 4: return launch_dense_g<T, D, 4>(Q, K, V, p, stride, idx, out, partial, stream);
+    default: return launch_dense_g<T, D, 8>(Q, K, V, p, stride, idx, out, partial, stream);
   }
 }
 
@@ -244,15 +273,16 @@ DensePlan plan_dense(int B, int Hq, int Hkv, int d, int64_t n) {
 }
 
 hipError_t launch_dense_attn(const void* Q, const void* K, const void* V, bool bf16,
-                             const DensePlan& p, int64_t stride, void* out, float* partial,
-                             hipStream_t stream) {
+                             const DensePlan& p, int64_t stride, const int32_t* idx, void* out,
+                             float* partial, hipStream_t stream) {
   if (p.B == 0 || p.Hq == 0) return hipSuccess;
   if (bf16) {
-    if (p.d == 128) return launch_dense_d<BF16, 128>(Q, K, V, p, stride, out, partial, stream);
-    return launch_dense_d<BF16, 64>(Q, K, V, p, stride, out, partial, stream);
+    if (p.d == 128)
+      return launch_dense_d<BF16, 128>(Q, K, V, p, stride, idx, out, partial, stream);
+    return launch_dense_d<BF16, 64>(Q, K, V, p, stride, idx, out, partial, stream);
   }
-  if (p.d == 128) return launch_dense_d<F32, 128>(Q, K, V, p, stride, out, partial, stream);
-  return launch_dense_d<F32, 64>(Q, K, V, p, stride, out, partial, stream);
+  if (p.d == 128) return launch_dense_d<F32, 128>(Q, K, V, p, stride, idx, out, partial, stream);
+  return launch_dense_d<F32, 64>(Q, K, V, p, stride, idx, out, partial, stream);
 }
 
 }  // namespace socket_lsh

@@ -185,8 +185,14 @@ struct DensePlan {
 // Largest context the dense baseline takes: 1024 chunks (the merge's limit).
 constexpr int64_t kMaxDenseKeys = 1024 * 1024;
 DensePlan plan_dense(int B, int Hq, int Hkv, int d, int64_t n);
+// idx: nullptr for rows 0..n-1 of every KV head, else a shared index set per
+// KV head [B*Hkv, n] (the GQA group-shared variant).
 hipError_t launch_dense_attn(const void* Q, const void* K, const void* V, bool bf16,
-                             const DensePlan& plan, int64_t stride, void* out,
-                             float* partial, hipStream_t stream);
+                             const DensePlan& plan, int64_t stride, const int32_t* idx,
+                             void* out, float* partial, hipStream_t stream);
+// Group table [B*Hkv, 2^P, L] = the sum over the G heads of a table
+// [B*Hkv, 2^P, L, G] (the GQA group-shared variant).
+hipError_t launch_group_table_sum(const float* table, int bhkv, int L, int P, int G, float* out,
+                                  hipStream_t stream);
 
 }  // namespace socket_lsh

@@ -317,6 +317,44 @@ def test_sparse_attn_stage(B, Hq, Hkv, d, N, kk, dt):
     assert np.max(np.abs(f64(out) - ref)) <= tol
 
 
+# ------------------------------------------------ GQA group-shared variant
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,k", [
+    (1, 8, 2, 3000, 256),       # selection from candidates, ragged tail
+    (2, 4, 1, 1500, 2000),      # k >= N: every key, one set per KV head
+    (1, 8, 8, 2048, 64),        # G = 1: the per-head decode
+])
+def test_decode_group_shared_matches_the_oracle(B, Hq, Hkv, N, k):
+    w = W.custom_workload(B=B, Hq=Hq, Hkv=Hkv, d=128, N=N, dtype="bf16", L=32, P=8,
+                          tau=0.3, k=k, lognormal_v=True)
+    log(f"group-shared {(B, Hq, Hkv, N, k)}")
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=17)
+    ids, vn = S.hash_keys(K, V, R, w.L, w.P)
+    kk = min(k, N)
+    idx = torch.empty((B, Hkv, kk), dtype=torch.int32, device=DEV)
+    sc = torch.empty((B, Hkv, N), dtype=torch.float32, device=DEV)
+    out, _, _ = S.decode_group_shared(Q, K, V, R, ids, vn, w.L, w.P, w.tau, k, idx_out=idx,
+                                      scores_out=sc)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    p = O.soft_bucket_probs(f64(Q), f64(R), w.L, w.P, tau32(w.tau))
+    ref_sc = O.group_scores(p, ids.cpu().numpy(), f64(vn), G)
+    sc_np, idx_np = sc.cpu().numpy(), idx.cpu().numpy()
+    assert_close_rel(sc_np, ref_sc, 1e-5, 1e-30, "group scores")
+    for b in range(B):
+        for g in range(Hkv):
+            assert np.array_equal(idx_np[b, g], O.topk_indices(sc_np[b, g], kk)), (b, g)
+    # every head of a group attends over its group's set
+    idx_h = np.repeat(idx_np, G, axis=1)
+    ref = O.subset_attention(f64(Q), f64(K), f64(V), idx_h, G)
+    assert np.max(np.abs(f64(out) - ref)) <= 2e-2
+    if G == 1:  # one head per group: the per-head decode, bit for bit
+        out1, idx1, _ = S.decode(Q, K, V, R, ids, vn, w.L, w.P, w.tau, k,
+                                 idx_out=torch.empty_like(idx))
+        torch.cuda.synchronize()
+        assert torch.equal(idx1, idx)
+
+
 # ------------------------------------------------ hard-LSH comparison
 
 @pytest.mark.parametrize("dt,L,P", [("bf16", 32, 8), ("f32", 8, 4), ("bf16", 11, 6)])
