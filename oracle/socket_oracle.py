@@ -42,9 +42,13 @@ Readings where the pages are silent (each one is also used by the GPU path):
     returned, in ascending index order.
   * Attention over the subset uses the scale 1/sqrt(d), is renormalised over
     the subset only, and has no sink, window or causal mask.
-Parity status: every function below is pinned by the CPU tests (closed forms,
-limits, hand-worked examples, brute force with exact rationals); none is
-"parity unpinned".
+  * Hard LSH (the tau -> 0 limit of the soft table): the limit puts equal
+    mass on every bucket that maximises the logit, so a projection of exactly
+    0 leaves its bit free and splits the mass 1/2 : 1/2 (sigma(0) = 1/2 at any
+    tau); the hash itself still sends such a key projection to bit 0.
+Parity status: every function below is pinned by the CPU tests in
+tests/test_oracle.py (closed forms, limits, hand-worked examples, brute force
+with exact rationals); none is "parity unpinned".
 """
 
 from __future__ import annotations
@@ -54,7 +58,6 @@ import math
 import numpy as np
 
 __all__ = [
-    "projections",
     "hash_bits",
     "pack_bucket_ids",
     "hash_keys",
@@ -68,6 +71,7 @@ __all__ = [
     "subset_attention",
     "decode",
     "hard_query_buckets",
+    "hard_bucket_table",
 ]
 
 _U64 = 2.0 ** -53  # unit roundoff of float64
@@ -81,15 +85,6 @@ def _f64(x) -> np.ndarray:
 # Step 1: prefill hashing  [SOCKET-es, Mecanismo Central: LSH Suave, item 1]
 #                          [SOCKET-de, Kernmechanismus, Vorverarbeitung]
 # ---------------------------------------------------------------------------
-
-def projections(K, R) -> np.ndarray:
-    """y[..., n, c] = sum_i K[..., n, i] * R[i, c] in float64.
-
-    Inputs are float32 or bfloat16 values, so every product is exact in
-    float64; only the summation rounds.
-    """
-    return _f64(K) @ _f64(R)
-
 
 def hash_bits(K, R, chunk: int = 1 << 16) -> np.ndarray:
     """Sign bit of every exact projection: True where K[n] . R[:, c] > 0.
@@ -175,10 +170,35 @@ def soft_bucket_probs(Q, R, L: int, P: int, tau: float) -> np.ndarray:
 
 
 def hard_query_buckets(Q, R, L: int, P: int) -> np.ndarray:
-    """The query's own hard bucket per table (sign of its projections)."""
+    """The query's own hard bucket per table, with the hash's convention:
+    bit j is 1 when z[l, j] > 0 (a projection of exactly 0 gives bit 0)."""
     z = query_projections(Q, R, L, P)
     weights = np.left_shift(1, np.arange(P, dtype=np.int64))
     return ((z > 0).astype(np.int64) * weights).sum(-1)
+
+
+def hard_bucket_table(Q, R, L: int, P: int) -> np.ndarray:
+    """p0[..., l, u]: the tau -> 0 limit of soft_bucket_probs (hard LSH).
+
+    [SOCKET-es, Fundamento Teórico, Teorema 3: as tau -> 0 the soft score
+    becomes the hard collision count] [SOCKET-de, Theoretische Grundlage]
+
+    The logit of bucket u, (1/tau) * sum_j s_j(u) z[l, j], is largest exactly
+    for the buckets whose bit j equals [z[l, j] > 0] wherever z[l, j] != 0
+    (bits with z[l, j] == 0 contribute 0 either way). As tau -> 0 the softmax
+    puts equal mass on those maximisers and none elsewhere: with m exactly-zero
+    projections in table l, each of the 2^m maximising buckets gets 2^-m. The
+    maximisers are found from the signs, not by comparing rounded sums.
+    """
+    z = query_projections(Q, R, L, P)                     # [..., L, P]
+    u = np.arange(2 ** P)
+    bits = ((u[:, None] >> np.arange(P)[None, :]) & 1).astype(bool)  # [2^P, P]
+    pos = (z > 0)[..., None, :]                           # [..., L, 1, P]
+    zero = (z == 0)[..., None, :]
+    agree = zero | (bits[None, :, :] == pos)              # [..., L, 2^P, P]
+    maximiser = agree.all(axis=-1)                        # [..., L, 2^P]
+    m = zero.sum(axis=-1)                                 # [..., L, 1]
+    return np.where(maximiser, np.ldexp(1.0, -m), 0.0)
 
 
 # ---------------------------------------------------------------------------

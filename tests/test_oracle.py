@@ -200,6 +200,64 @@ def test_soft_probs_query_negation_maps_to_complement_bucket():
     assert np.allclose(pn, p[..., comp], rtol=1e-13, atol=1e-300)
 
 
+def test_hard_table_golden(golden_dir):
+    """Hand-worked tau -> 0 tables, including projections of exactly 0."""
+    g = _load(golden_dir, "hard_table_hand.json")
+    for case in g["cases"]:
+        Q = np.array(case["Q"], float)[None, None, :]
+        R = np.eye(Q.shape[-1])
+        t = O.hard_bucket_table(Q, R, case["L"], case["P"])[0, 0]
+        assert t.tolist() == case["table"]
+        if "key" in case:
+            K = np.array(case["key"], float)[None, None, None, :]
+            V = np.array(case["value"], float)[None, None, None, :]
+            ids = O.hash_keys(K, R, case["L"], case["P"])
+            s = O.soft_scores(t[None, None], ids, O.value_norms(V), 1)
+            assert s[0, 0, 0] == case["score"]
+
+
+def _with_zero_projections(seed, d=16, L=6, P=4):
+    """Queries with some projections exactly 0 (pairs of coordinates that
+    cancel exactly: q_2m = r_2m+1, q_2m+1 = -r_2m for the chosen column),
+    the other projections at least 1e-3 away from 0."""
+    r = _rng(seed)
+    R = np.round(r.standard_normal((d, L * P)) * 64) / 64      # exact products
+    while True:
+        Q = np.round(r.standard_normal((2, 3, d)) * 64) / 64
+        for (b, h, c) in [(0, 0, 1), (0, 2, 5), (1, 1, 9), (1, 2, 9 + P)]:
+            Q[b, h, 0::2] = R[1::2, c]
+            Q[b, h, 1::2] = -R[0::2, c]
+        z = Q @ R
+        nz = np.abs(z[z != 0])
+        if nz.min() > 1e-3:
+            return Q, R, L, P, z
+
+
+def test_hard_table_is_the_tau0_limit_of_the_soft_table():
+    """A different route: the literal softmax of soft_bucket_probs at a tiny
+    tau, with exact-zero projections present (their bit splits 1/2 : 1/2)."""
+    Q, R, L, P, z = _with_zero_projections(50)
+    assert (z == 0).sum() == 4
+    hard = O.hard_bucket_table(Q, R, L, P)
+    soft = O.soft_bucket_probs(Q, R, L, P, 1e-9)
+    assert np.allclose(hard, soft, atol=1e-12, rtol=0)
+    assert np.array_equal(hard.sum(-1), np.ones(hard.shape[:-1]))
+    # the tables holding a zero projection split their mass over 2 buckets
+    zt = (z.reshape(2, 3, L, P) == 0).any(-1)
+    assert np.array_equal((hard > 0).sum(-1), np.where(zt, 2, 1))
+
+
+def test_hard_table_without_zeros_is_one_hot_at_the_hard_bucket():
+    r = _rng(51)
+    L, P, d = 9, 6, 32
+    Q = r.standard_normal((2, 4, d))
+    R = r.standard_normal((d, L * P))
+    hard = O.hard_bucket_table(Q, R, L, P)
+    onehot = np.zeros_like(hard)
+    np.put_along_axis(onehot, O.hard_query_buckets(Q, R, L, P)[..., None], 1.0, axis=-1)
+    assert np.array_equal(hard, onehot)
+
+
 # -------------------------------------------------------------------- scores
 
 def _small_problem(seed, B=2, Hq=4, Hkv=2, d=16, N=50, L=6, P=3, tau=0.5):
