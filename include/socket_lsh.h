@@ -18,6 +18,7 @@
  *   - All tensor pointers are DEVICE pointers, caller-allocated, contiguous,
  *     row-major in the layouts written next to each argument. The library
  *     allocates nothing, frees nothing and keeps no state between calls.
+
  *   - dtype selects the element type of Q, K, V, R and the attention output:
  *     SOCKET_DTYPE_F32 (float) or SOCKET_DTYPE_BF16 (bfloat16 bits, round to
  *     nearest even on output). Bucket ids are uint8, norms, probabilities
@@ -32,9 +33,12 @@
  *   - Inputs must be finite. This is not checked on the device.
  *   - Supported sizes: d in {64, 128}; 1 <= P <= 8; 1 <= L and L*P <= 1024
  *     (L*P <= 512 for bf16 hashing); Hq a multiple of Hkv with
- *     G = Hq/Hkv in {1, 2, 4, 8}; the per-KV-head probability table
- *     2^P * L * G * 4 bytes plus 2 KB per query head of the group must fit
- *     the 160 KB LDS of a CU; k >= 1;
+ *     G = Hq/Hkv in {1, 2, 4, 8}; k >= 1. The score kernel keeps the
+ *     probability tables of Gp query heads of a KV head in the 160 KB LDS of
+ *     a CU (2^P * L * Gp * 4 bytes plus 2 KB per head): Gp is the largest
+ *     power of two dividing G that fits, and with Gp < G the ids of a KV head
+ *     are streamed once per pack of Gp heads (every L*P <= 1024 fits at
+ *     Gp = 1);
  *     head_stride_rows < 2^31 for decode (int32 key indices).
  *   - Unsupported but valid sizes return SOCKET_ERR_UNSUPPORTED.
  *
@@ -282,10 +286,9 @@ socket_status socket_dense_attn(const void* Q, const void* K, const void* V,
  * exact top k of the rows socket_score would produce, ties to the lower
  * index, in ascending order.
  * Workspace: socket_decode_workspace_bytes(...) bytes of device memory.
- * n_keys must be >= 1. With k < n_keys the score kernel needs the table of
- * one KV head plus 2 KB per query head of the group within 160 KB of LDS,
- * and n_keys <= 2^28 (at most 4096 candidate sub-lists per row); otherwise
- * SOCKET_ERR_UNSUPPORTED.
+ * n_keys must be >= 1. With k < n_keys the selection reads at most 4096
+ * candidate sub-lists per row (n_keys up to about 2^28 at one pack per CU,
+ * fewer where two score blocks fit a CU); otherwise SOCKET_ERR_UNSUPPORTED.
  */
 size_t socket_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv,
                                      int32_t d, int64_t n_keys, int32_t L,

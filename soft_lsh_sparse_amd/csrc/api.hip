@@ -76,14 +76,32 @@ socket_status check_heads(int32_t B, int32_t Hq, int32_t Hkv) {
   return SOCKET_OK;
 }
 
+// The score kernel holds the tables of Gp query heads of one KV head (the
+// largest Gp dividing G that fits, see score_pack); fails only when not even
+// one head's table fits.
 socket_status check_table(int32_t L, int32_t P, int32_t G) {
-  const size_t bytes = score_lds_bytes(L, P, G, false);
-  if (bytes > kLdsBytesPerCU)
+  if (score_pack(L, P, G) == 0)
     return fail(SOCKET_ERR_UNSUPPORTED,
-                "probability table of one KV head (2^P*L*G*4 bytes) with the score "
+                "probability table of one query head (2^P*L*4 bytes) with the score "
                 "kernel's other LDS (%zu bytes in all) exceeds the %zu bytes of LDS",
-                bytes, kLdsBytesPerCU);
+                score_lds_bytes(L, P, 1, false), kLdsBytesPerCU);
   return SOCKET_OK;
+}
+
+// Virtual KV heads of the score pipeline: Hkv * (G / Gp), see score_pack.
+struct HeadPack {
+  int gp;      // query heads per score block
+  int np;      // packs per KV head (id divisor)
+  int hkv_v;   // virtual KV heads
+};
+HeadPack head_pack(int32_t Hq, int32_t Hkv, int32_t L, int32_t P) {
+  HeadPack hp{};
+  const int G = Hq / Hkv;
+  hp.gp = score_pack(L, P, G);
+  if (hp.gp < 1) hp.gp = 1;
+  hp.np = G / hp.gp;
+  hp.hkv_v = Hkv * hp.np;
+  return hp;
 }
 
 #define SOCKET_TRY(expr)                 \
@@ -94,6 +112,7 @@ socket_status check_table(int32_t L, int32_t P, int32_t G) {
 
 struct DecodeLayout {
   size_t table_off, scores_off, idx_off, thr_off, cnt_off, list_off, attn_off, total;
+  HeadPack pack;
   ScoreGeom score;
   AttnPlan attn;
 };
@@ -107,7 +126,8 @@ DecodeLayout decode_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
   const int rows = B * Hq;
   const int64_t kk = k < n_keys ? k : n_keys;
   const bool select = kk < n_keys;
-  lay.score = plan_score(B * Hkv, n_keys, L, P, Hq / Hkv);
+  lay.pack = head_pack(Hq, Hkv, L, P);
+  lay.score = plan_score(B * lay.pack.hkv_v, n_keys, L, P, lay.pack.gp);
   size_t off = 0;
   lay.table_off = off;
   off = align256(off + ((size_t)1 << P) * L * Hq * B * sizeof(float));
@@ -256,7 +276,8 @@ socket_status socket_score(const float* table, const uint8_t* ids,
     return fail(SOCKET_ERR_INVALID_ARGUMENT, "null pointer argument");
   if (!aligned16(table))
     return fail(SOCKET_ERR_INVALID_ARGUMENT, "table must be 16-byte aligned");
-  hipError_t err = launch_score(table, ids, vnorm, B, Hq, Hkv, n_keys,
+  const HeadPack hp = head_pack(Hq, Hkv, L, P);
+  hipError_t err = launch_score(table, Hq / Hkv, ids, vnorm, B, Hq, hp.hkv_v, hp.np, n_keys,
                                 head_stride_rows, L, P, scores, nullptr,
                                 static_cast<hipStream_t>(stream));
   return from_hip(err, "socket_score launch");
@@ -373,15 +394,24 @@ size_t socket_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv,
 
 namespace {
 
-// Shapes and sizes socket_decode accepts (pointers and tau aside).
-socket_status check_decode(socket_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
-                           int64_t n_keys, int64_t head_stride_rows, int32_t L, int32_t P,
-                           int64_t k) {
+// The candidate sub-lists the selection of one row reads must fit its
+// offsets: checked on the geometry the score kernel is launched with.
+socket_status check_sublists(const ScoreGeom& geo, int64_t n_keys, int64_t k) {
+  if (k < n_keys && geo.subs > kMaxSelectSubLists)
+    return fail(SOCKET_ERR_UNSUPPORTED, "n_keys=%lld needs %d candidate sub-lists per row "
+                "(at most %d)", (long long)n_keys, geo.subs, kMaxSelectSubLists);
+  return SOCKET_OK;
+}
+
+// Shapes and sizes both decode entry points accept (pointers, tau and the
+// score geometry aside).
+socket_status check_decode_common(socket_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                  int32_t d, int64_t n_keys, int64_t head_stride_rows, int32_t L,
+                                  int32_t P, int64_t k) {
   SOCKET_TRY(check_dtype(dtype));
   SOCKET_TRY(check_heads(B, Hq, Hkv));
   SOCKET_TRY(check_d(d));
   SOCKET_TRY(check_lp(L, P));
-  SOCKET_TRY(check_table(L, P, Hq / Hkv));
   if (k < 1) return fail(SOCKET_ERR_INVALID_ARGUMENT, "k must be >= 1");
   if (n_keys < 1) return fail(SOCKET_ERR_INVALID_ARGUMENT, "n_keys must be >= 1");
   if ((k < n_keys ? k : n_keys) > kMaxSelected)
@@ -392,11 +422,17 @@ socket_status check_decode(socket_dtype dtype, int32_t B, int32_t Hq, int32_t Hk
                 (long long)head_stride_rows, (long long)n_keys);
   if (head_stride_rows >= ((int64_t)1 << 31))
     return fail(SOCKET_ERR_UNSUPPORTED, "head_stride_rows must be < 2^31");
-  const ScoreGeom geo = plan_score(B * Hkv, n_keys, L, P, Hq / Hkv);
-  if (k < n_keys && geo.subs > kMaxSelectSubLists)
-    return fail(SOCKET_ERR_UNSUPPORTED, "n_keys=%lld needs %d candidate sub-lists per row "
-                "(at most %d)", (long long)n_keys, geo.subs, kMaxSelectSubLists);
   return SOCKET_OK;
+}
+
+// Shapes and sizes socket_decode accepts (pointers and tau aside).
+socket_status check_decode(socket_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                           int64_t n_keys, int64_t head_stride_rows, int32_t L, int32_t P,
+                           int64_t k) {
+  SOCKET_TRY(check_decode_common(dtype, B, Hq, Hkv, d, n_keys, head_stride_rows, L, P, k));
+  SOCKET_TRY(check_table(L, P, Hq / Hkv));
+  const HeadPack hp = head_pack(Hq, Hkv, L, P);
+  return check_sublists(plan_score(B * hp.hkv_v, n_keys, L, P, hp.gp), n_keys, k);
 }
 
 socket_status decode_impl(const void* Q, const void* K, const void* V,
@@ -440,8 +476,11 @@ socket_status decode_impl(const void* Q, const void* K, const void* V,
   // (from the candidates, or from the full row).
   const int rows = B * Hq;
   const int64_t kk = k < n_keys ? k : n_keys;
-  // the score kernel builds the tables itself where it can (no table kernel)
-  const bool build = score_builds_table(bf16, d, ids, head_stride_rows, L, P, Hq / Hkv);
+  // the score kernel builds the tables itself where it can (no table kernel);
+  // the score pipeline runs over Hv virtual KV heads of Gp query heads each
+  const HeadPack hp = lay.pack;
+  const int Hv = hp.hkv_v;
+  const bool build = score_builds_table(bf16, d, ids, head_stride_rows, L, P, hp.gp);
   const TableBuild tb{Q, R, d, tau};
   hipError_t err;
   if (kk < n_keys) {
@@ -450,18 +489,19 @@ socket_status decode_impl(const void* Q, const void* K, const void* V,
     uint2* lists = reinterpret_cast<uint2*>(ws + lay.list_off);
     float* rowbuf = scores_out ? scores_out : reinterpret_cast<float*>(ws + lay.scores_off);
     if (!build) {
-      err = launch_bucket_probs(Q, R, bf16, B, Hq, Hkv, d, L, P, tau, table, s);
+      err = launch_bucket_probs(Q, R, bf16, B, Hq, Hv, d, L, P, tau, table, s);
       if (err != hipSuccess) return from_hip(err, "socket_decode: bucket_probs");
     }
     ScoreSelect sel{};
     sel.table = table;
+    sel.id_div = hp.np;
     sel.ids = ids;
     sel.vnorm = vnorm;
     sel.kk = kk;
     sel.thr = thr;
     sel.lists = lists;
     sel.sub_cnt = cnt;
-    err = launch_score_select(sel, B, Hq, Hkv, n_keys, head_stride_rows, L, P, scores_out,
+    err = launch_score_select(sel, B, Hq, Hv, n_keys, head_stride_rows, L, P, scores_out,
                               build ? &tb : nullptr, s);
     if (err != hipSuccess) return from_hip(err, "socket_decode: score");
     SelectArgs sa{};
@@ -478,7 +518,8 @@ socket_status decode_impl(const void* Q, const void* K, const void* V,
     sa.ids = ids;
     sa.vnorm = vnorm;
     sa.Hq = Hq;
-    sa.Hkv = Hkv;
+    sa.Hkv = Hv;
+    sa.id_div = hp.np;
     sa.L = L;
     sa.P = P;
     sa.stride = head_stride_rows;
@@ -489,11 +530,11 @@ socket_status decode_impl(const void* Q, const void* K, const void* V,
   } else {
     if (scores_out) {
       if (!build) {
-        err = launch_bucket_probs(Q, R, bf16, B, Hq, Hkv, d, L, P, tau, table, s);
+        err = launch_bucket_probs(Q, R, bf16, B, Hq, Hv, d, L, P, tau, table, s);
         if (err != hipSuccess) return from_hip(err, "socket_decode: bucket_probs");
       }
-      err = launch_score(table, ids, vnorm, B, Hq, Hkv, n_keys, head_stride_rows, L, P,
-                         scores_out, build ? &tb : nullptr, s);
+      err = launch_score(table, hp.gp, ids, vnorm, B, Hq, Hv, hp.np, n_keys, head_stride_rows,
+                         L, P, scores_out, build ? &tb : nullptr, s);
       if (err != hipSuccess) return from_hip(err, "socket_decode: score");
     }
     err = launch_iota_rows(idx, rows, n_keys, s);
@@ -528,13 +569,24 @@ GroupLayout group_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t 
   return g;
 }
 
+// Shapes the group-shared variant accepts: its score and selection run at
+// one (summed) table per KV head, so both the LDS and the sub-list checks
+// use that geometry.
+socket_status check_group_decode(socket_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                 int32_t d, int64_t n_keys, int64_t head_stride_rows, int32_t L,
+                                 int32_t P, int64_t k) {
+  SOCKET_TRY(check_decode_common(dtype, B, Hq, Hkv, d, n_keys, head_stride_rows, L, P, k));
+  SOCKET_TRY(check_table(L, P, 1));
+  return check_sublists(plan_score(B * Hkv, n_keys, L, P, 1), n_keys, k);
+}
+
 socket_status decode_group_impl(const void* Q, const void* K, const void* V, const void* R,
                                 const uint8_t* ids, const float* vnorm, socket_dtype dtype,
                                 int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t n_keys,
                                 int64_t head_stride_rows, int32_t L, int32_t P, float tau,
                                 int64_t k, void* out, int32_t* idx_out, float* scores_out,
                                 void* workspace, size_t workspace_bytes, void* stream) {
-  SOCKET_TRY(check_decode(dtype, B, Hq, Hkv, d, n_keys, head_stride_rows, L, P, k));
+  SOCKET_TRY(check_group_decode(dtype, B, Hq, Hkv, d, n_keys, head_stride_rows, L, P, k));
   if (!(std::isfinite(tau) && tau > 0.f))
     return fail(SOCKET_ERR_INVALID_ARGUMENT, "tau must be finite and > 0");
   if (!Q || !K || !V || !R || !ids || !vnorm || !out)
@@ -570,6 +622,7 @@ socket_status decode_group_impl(const void* Q, const void* K, const void* V, con
     float* rowbuf = scores_out ? scores_out : reinterpret_cast<float*>(ws + lay.head.scores_off);
     ScoreSelect sel{};
     sel.table = gtable;
+    sel.id_div = 1;
     sel.ids = ids;
     sel.vnorm = vnorm;
     sel.kk = kk;
@@ -594,6 +647,7 @@ socket_status decode_group_impl(const void* Q, const void* K, const void* V, con
     sa.vnorm = vnorm;
     sa.Hq = Hkv;
     sa.Hkv = Hkv;
+    sa.id_div = 1;
     sa.L = L;
     sa.P = P;
     sa.stride = head_stride_rows;
@@ -603,7 +657,7 @@ socket_status decode_group_impl(const void* Q, const void* K, const void* V, con
     if (err != hipSuccess) return from_hip(err, "group-shared decode: topk");
   } else {
     if (scores_out) {
-      err = launch_score(gtable, ids, vnorm, B, Hkv, Hkv, n_keys, head_stride_rows, L, P,
+      err = launch_score(gtable, 1, ids, vnorm, B, Hkv, Hkv, 1, n_keys, head_stride_rows, L, P,
                          scores_out, nullptr, s);
       if (err != hipSuccess) return from_hip(err, "group-shared decode: score");
     }
@@ -676,7 +730,7 @@ int32_t socket_decode_kernels(const uint8_t* ids, socket_dtype dtype, int32_t B,
   if (check_decode(dtype, B, Hq, Hkv, d, n_keys, head_stride_rows, L, P, k) != SOCKET_OK)
     return -1;
   const bool build = score_builds_table(dtype == SOCKET_DTYPE_BF16, d, ids, head_stride_rows,
-                                        L, P, Hq / Hkv);
+                                        L, P, head_pack(Hq, Hkv, L, P).gp);
   // the launch sequence of decode_impl
   const char* seq[6];
   int n = 0;

@@ -70,6 +70,14 @@ struct ScoreGeom {
   int64_t sub_len;
 };
 ScoreGeom plan_score(int bhkv, int64_t n_keys, int L, int P, int G);
+// GQA packing. When the probability table of a whole group (2^P * L * G
+// floats) does not fit a score block's LDS, each block scores Gp of the G
+// query heads of its KV head: the score pipeline then runs over B * Hkv * np
+// "virtual" KV heads of Gp query heads each (np = G / Gp; query head h
+// belongs to virtual head h / Gp, which reads the ids and norms of KV head
+// (virtual head) / np). Returns the largest such Gp (a power of two dividing
+// G) whose table fits, or 0 when not even Gp = 1 does.
+int score_pack(int L, int P, int G);
 // true when the kernel sums each key's tables in the rotated order
 // l = (t + key) mod L, t = 0..L-1 (with key taken mod 16); else l = t
 bool score_rotated(const uint8_t* ids, int64_t stride, int L);
@@ -88,10 +96,13 @@ struct TableBuild {
   int d;
   float tau;
 };
-// table: [B*Hkv, 2^P, L, G] from launch_bucket_probs, or unused with build;
+// Hkv: virtual KV heads (Hq / Hkv query heads each, see score_pack); the
+// ids and norms of virtual head v are those of head v / id_div. table:
+// [B*Hkv/id_div, 2^P, L, table_G] from launch_bucket_probs (virtual head v
+// takes heads (v % id_div) * Hq/Hkv ... of its slots), or unused with build;
 // scores [B*Hq, n_keys].
-hipError_t launch_score(const float* table, const uint8_t* ids, const float* vnorm,
-                        int B, int Hq, int Hkv, int64_t n_keys, int64_t stride,
+hipError_t launch_score(const float* table, int table_G, const uint8_t* ids, const float* vnorm,
+                        int B, int Hq, int Hkv, int id_div, int64_t n_keys, int64_t stride,
                         int L, int P, float* scores, const TableBuild* build,
                         hipStream_t stream);
 // Decode path: every block estimates a per-row threshold from its first
@@ -100,7 +111,8 @@ hipError_t launch_score(const float* table, const uint8_t* ids, const float* vno
 // at lists[row * n_keys + s * sub_len], in index order; sub_cnt[row * subs +
 // s] receives the sub-list's length.
 struct ScoreSelect {
-  const float* table;  // [B*Hkv, 2^P, L, G] (written by the kernel with build)
+  const float* table;  // [B*Hkv, 2^P, L, G] over virtual heads (written by the kernel with build)
+  int id_div;          // virtual head v reads the ids and norms of head v / id_div
   const uint8_t* ids;
   const float* vnorm;
   int64_t kk;          // < n_keys
@@ -148,7 +160,8 @@ struct SelectArgs {
   const float* table;         // full-row fallback: the score kernel's inputs
   const uint8_t* ids;
   const float* vnorm;
-  int Hq, Hkv, L, P;
+  int Hq, Hkv, L, P;          // Hkv: virtual KV heads (score_pack)
+  int id_div;                 // virtual head v reads the ids of head v / id_div
   int64_t stride;
   int rotated;                // score_rotated(ids, stride, L)
   float* scores;              // [rows][n] row buffers

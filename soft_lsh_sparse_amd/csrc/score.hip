@@ -159,9 +159,17 @@ __device__ __forceinline__ bool score_block_coords(int bhkv, int segs, int& bg,
 // (start_round) so that they do not all ask the same L2 lines at once.
 template <int G>
 __device__ __forceinline__ void stage_table(float* tab, const float* table, int bg,
-                                            int L, int P, int start_round) {
+                                            int L, int P, int start_round, int id_div,
+                                            int table_G) {
   const int tsize = (1 << P) * L * G;
-  if (tsize % 4 == 0) {  // every head's table then starts 16-byte aligned
+  if (table_G != G) {
+    // a pack of G of the table_G heads of each slot (socket_score on a
+    // group table too large for one block): element by element
+    const float* src = table + (int64_t)(bg / id_div) * ((int64_t)tsize / G * table_G) +
+                       (bg % id_div) * G;
+    for (int i = threadIdx.x; i < tsize; i += blockDim.x)
+      tab[i] = src[(int64_t)(i / G) * table_G + i % G];
+  } else if (tsize % 4 == 0) {  // every head's table then starts 16-byte aligned
     // direct-to-LDS loads: 64 lanes x 16 bytes per instruction into
     // consecutive LDS, no registers held, all in flight at once
     const float4* src = reinterpret_cast<const float4*>(table + (int64_t)bg * tsize);
@@ -186,10 +194,12 @@ __device__ __forceinline__ void stage_table(float* tab, const float* table, int 
 
 
 struct ScoreArgs {
-  const float* table;  // [bhkv][2^P][L][G]
+  const float* table;  // [bhkv / id_div][2^P][L][table_G]
   const uint8_t* ids;
   const float* vnorm;
-  int Hq, Hkv, bhkv, L, P, segs;
+  int Hq, Hkv, bhkv, L, P, segs;  // Hkv, bhkv: virtual KV heads (score_pack)
+  int id_div;          // virtual head bg reads the ids and norms of head bg / id_div
+  int table_G;         // heads per table slot (G, or the whole group when packing a stage call)
   int64_t n_keys, stride, seg_len;
   float* scores;       // [rows][n_keys] or null
   // candidate emission (decode path)
@@ -601,7 +611,7 @@ __device__ void score_block(const ScoreArgs& a, int bg, int seg, float* tab, Sco
     build_table<G>(tab, reinterpret_cast<double*>(lds + treg), a, bg, [&] { sc.prefetch(); });
   } else {
     sc.prefetch();
-    stage_table<G>(tab, a.table, bg, a.L, a.P, seg);
+    stage_table<G>(tab, a.table, bg, a.L, a.P, seg, a.id_div, a.table_G);
   }
   __syncthreads();
   if constexpr (BUILD)
@@ -695,8 +705,9 @@ struct RotScorer {
       : tab(tab_), P(a.P), we(wr.we), wb(wr.wb) {
     // block-uniform bases of this segment (buffers: per-thread offsets stay
     // 32-bit, seg_len * L < 2^31 bytes)
-    idseg = raw_rsrc(a.ids + ((int64_t)bg * a.stride + wr.n0) * L, (uint32_t)wr.cnt * L);
-    vseg = raw_rsrc(a.vnorm + (int64_t)bg * a.stride + wr.n0, (uint32_t)wr.cnt * 4u);
+    const int64_t hg = bg / a.id_div;  // the KV head whose ids this block reads
+    idseg = raw_rsrc(a.ids + (hg * a.stride + wr.n0) * L, (uint32_t)wr.cnt * L);
+    vseg = raw_rsrc(a.vnorm + hg * a.stride + wr.n0, (uint32_t)wr.cnt * 4u);
     // n0 + wb is a multiple of 16, so every key of this lane has the same
     // rotation r = key index mod 16 and the same two bases
     const int lane = threadIdx.x & 63;
@@ -772,8 +783,9 @@ struct GenericScorer {
   int L, P;
   __device__ GenericScorer(const ScoreArgs& a, int bg, const WaveRange& wr, const float* tab_)
       : tab(tab_), L(a.L), P(a.P) {
-    idseg = a.ids + ((int64_t)bg * a.stride + wr.n0) * a.L;
-    vseg = a.vnorm + (int64_t)bg * a.stride + wr.n0;
+    const int64_t hg = bg / a.id_div;
+    idseg = a.ids + (hg * a.stride + wr.n0) * a.L;
+    vseg = a.vnorm + hg * a.stride + wr.n0;
   }
   __device__ __forceinline__ void prefetch() {}
   __device__ __forceinline__ void score(int, int i, bool valid, float (&acc)[G], float& vn) {
@@ -868,11 +880,14 @@ hipError_t launch_score_any(const ScoreArgs& a, int G, hipStream_t stream) {
   }
 }
 
-ScoreArgs base_args(const float* table, const uint8_t* ids, const float* vnorm, int B, int Hq,
-                    int Hkv, int64_t n_keys, int64_t stride, int L, int P) {
+ScoreArgs base_args(const float* table, int table_G, const uint8_t* ids, const float* vnorm,
+                    int B, int Hq, int Hkv, int id_div, int64_t n_keys, int64_t stride, int L,
+                    int P) {
   const ScoreGeom geo = plan_score(B * Hkv, n_keys, L, P, Hq / Hkv);
   ScoreArgs a{};
   a.table = table;
+  a.table_G = table_G;
+  a.id_div = id_div;
   a.ids = ids;
   a.vnorm = vnorm;
   a.Hq = Hq;
@@ -901,6 +916,12 @@ bool score_builds_table(bool bf16, int d, const uint8_t* ids, int64_t stride, in
   return bf16 && P == 8 && (d == 64 || d == 128) && score_rotated(ids, stride, L) &&
          score_lds_bytes(L, P, G, true) <= kLdsBytesPerCU &&
          (size_t)16 * d * L + (size_t)2 * G * d <= score_table_region(L, P, G);
+}
+
+int score_pack(int L, int P, int G) {
+  for (int gp = G; gp >= 1; gp >>= 1)
+    if (G % gp == 0 && score_lds_bytes(L, P, gp, false) <= kLdsBytesPerCU) return gp;
+  return 0;
 }
 
 bool score_rotated(const uint8_t* ids, int64_t stride, int L) {
@@ -939,12 +960,12 @@ void set_build(ScoreArgs& a, const TableBuild* build, float* table_out) {
   a.table_out = table_out;
 }
 
-hipError_t launch_score(const float* table, const uint8_t* ids, const float* vnorm,
-                        int B, int Hq, int Hkv, int64_t n_keys, int64_t stride,
+hipError_t launch_score(const float* table, int table_G, const uint8_t* ids, const float* vnorm,
+                        int B, int Hq, int Hkv, int id_div, int64_t n_keys, int64_t stride,
                         int L, int P, float* scores, const TableBuild* build,
                         hipStream_t stream) {
   if (n_keys == 0) return hipSuccess;
-  ScoreArgs a = base_args(table, ids, vnorm, B, Hq, Hkv, n_keys, stride, L, P);
+  ScoreArgs a = base_args(table, table_G, ids, vnorm, B, Hq, Hkv, id_div, n_keys, stride, L, P);
   a.scores = scores;
   set_build(a, build, nullptr);
   return launch_score_any(a, Hq / Hkv, stream);
@@ -953,7 +974,8 @@ hipError_t launch_score(const float* table, const uint8_t* ids, const float* vno
 hipError_t launch_score_select(const ScoreSelect& s, int B, int Hq, int Hkv, int64_t n_keys,
                                int64_t stride, int L, int P, float* scores,
                                const TableBuild* build, hipStream_t stream) {
-  ScoreArgs a = base_args(s.table, s.ids, s.vnorm, B, Hq, Hkv, n_keys, stride, L, P);
+  ScoreArgs a = base_args(s.table, Hq / Hkv, s.ids, s.vnorm, B, Hq, Hkv, s.id_div, n_keys, stride,
+                          L, P);
   a.scores = scores;
   a.select = 1;
   a.kk = s.kk;

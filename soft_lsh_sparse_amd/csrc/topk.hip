@@ -281,6 +281,9 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
 __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs a) {
   constexpr int NT = kRefineThreads;
   __shared__ RefineShared sh;
+  // the host never launches more sub-lists than the offsets hold; a row
+  // that would have more is left alone rather than read out of bounds
+  if (a.subs > kMaxSelectSubLists) return;
   const int row = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t kk = (uint32_t)a.kk;
@@ -398,6 +401,7 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
   const int G = a.Hq / a.Hkv;
   const int b = row / a.Hq, hq = row % a.Hq;
   const int bg = b * a.Hkv + hq / G, j = hq % G;
+  const int64_t hg = bg / a.id_div;  // the KV head whose ids the row reads
   const int L = a.L, nb = 1 << a.P;
   const float* tg = a.table + (int64_t)bg * nb * L * G + j;  // (u, l) at (u * L + l) * G
   float* tabs = reinterpret_cast<float*>(sh.cache);
@@ -406,8 +410,8 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
     for (int e = threadIdx.x; e < nb * L; e += NT) tabs[e] = tg[(int64_t)e * G];
   __syncthreads();
   float* srow = a.scores + (int64_t)row * a.n;
-  const uint8_t* idh = a.ids + (int64_t)bg * a.stride * L;
-  const float* vnh = a.vnorm + (int64_t)bg * a.stride;
+  const uint8_t* idh = a.ids + hg * a.stride * L;
+  const float* vnh = a.vnorm + hg * a.stride;
   for (int64_t i = threadIdx.x; i < a.n; i += NT) {
     const int r = a.rotated ? (int)(i & 15) : 0;
     float acc = 0.f;

@@ -64,7 +64,6 @@ def _decode(lib, **over):
     (dict(P=9), _lib.SOCKET_ERR_INVALID_ARGUMENT),
     (dict(L=0), _lib.SOCKET_ERR_INVALID_ARGUMENT),
     (dict(L=200, P=8), _lib.SOCKET_ERR_UNSUPPORTED),         # L*P > 1024
-    (dict(L=64, P=8), _lib.SOCKET_ERR_UNSUPPORTED),          # 256 KB table
     (dict(tau=0.0), _lib.SOCKET_ERR_INVALID_ARGUMENT),
     (dict(tau=-1.0), _lib.SOCKET_ERR_INVALID_ARGUMENT),
     (dict(tau=float("inf")), _lib.SOCKET_ERR_INVALID_ARGUMENT),
@@ -82,6 +81,46 @@ def _decode(lib, **over):
 def test_decode_rejects_bad_arguments(lib, over, status):
     assert _decode(lib, **over) == status
     assert lib.socket_last_error()
+
+
+def test_decode_packs_query_heads_when_the_group_table_overflows_lds(lib):
+    """L=64, P=8, G=4 needs 256 KB for a group's tables: the score blocks then
+    take 2 query heads each (G-pack) instead of the call being rejected. The
+    host-only launch query and the workspace check show the call accepted
+    (the fake pointers are never used)."""
+    n, names = _kernels(lib, L=64, P=8)
+    assert n == 5 and names[:3] == ["bucket_probs_kernel", "score_kernel",
+                                    "topk_select_kernel"]
+    assert _kernels(lib, L=128, P=8, Hq=64, Hkv=8)[0] == 5     # G = 8 -> one head per block
+    assert _decode(lib, L=64, P=8) == _lib.SOCKET_ERR_WORKSPACE   # accepted up to the workspace
+    ws = lib.socket_decode_workspace_bytes(1, 32, 8, 128, 1024, 64, 8, 64)
+    assert ws >= 256 * 64 * 32 * 4                                   # tables of all 32 heads
+
+
+def _group(lib, **over):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, R=FAKE, ids=FAKE, vnorm=FAKE, dt=1, B=1,
+             Hq=4, Hkv=1, d=128, n=1024, stride=1024, L=32, P=8, tau=0.3,
+             k=64, out=FAKE, idx=None, scores=None, ws=FAKE, ws_bytes=0)
+    a.update(over)
+    return lib.socket_decode_group_shared(
+        a["Q"], a["K"], a["V"], a["R"], a["ids"], a["vnorm"], a["dt"], a["B"], a["Hq"],
+        a["Hkv"], a["d"], a["n"], a["stride"], a["L"], a["P"], a["tau"], a["k"], a["out"],
+        a["idx"], a["scores"], a["ws"], a["ws_bytes"], None)
+
+
+def test_group_shared_checks_the_geometry_it_launches(lib):
+    """The group-shared variant scores one summed table per KV head, so its
+    score kernel fits twice the blocks per CU of the per-head kernel: with
+    one KV head and 600,000 keys that geometry needs more candidate sub-lists
+    per row than the selection holds (the per-head geometry would not). The
+    call must be rejected on the host, before any launch."""
+    n = 600_000
+    assert _group(lib, n=n, stride=n) == _lib.SOCKET_ERR_UNSUPPORTED
+    assert b"sub-lists" in lib.socket_last_error()
+    # the per-head decode of the same shape is within its own geometry
+    assert _decode(lib, Hq=4, Hkv=1, n=n, stride=n) == _lib.SOCKET_ERR_WORKSPACE
+    # a shape within both geometries reaches the workspace check
+    assert _group(lib, n=400_000, stride=400_000) == _lib.SOCKET_ERR_WORKSPACE
 
 
 def test_decode_profiled_needs_an_event_pair(lib):
