@@ -33,6 +33,24 @@ def _dev(t: torch.Tensor, name: str) -> int:
     return t.data_ptr()
 
 
+def _expect(t, name: str, shape, dtype=None) -> None:
+    """Shape and dtype check of an argument before its pointer reaches the C
+    ABI, which cannot see either (a wrong one would be read or written out of
+    bounds on the device)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
+def _heads(Hq: int, Hkv: int) -> int:
+    if Hkv < 1 or Hq % Hkv != 0:
+        raise ValueError(f"Hq={Hq} is not a multiple of Hkv={Hkv}")
+    return Hq // Hkv
+
+
 def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
@@ -51,9 +69,12 @@ def hash_keys(K: torch.Tensor, V: torch.Tensor, R: torch.Tensor, L: int,
     S rows); pass the existing ids / vnorm to append to a cache.
     """
     lib = _lib.load()
-    if K.shape != V.shape or K.dtype != V.dtype or R.dtype != K.dtype:
-        raise ValueError("K and V must have the same shape and dtype as R")
+    _dtype_code(K)
+    if K.dim() < 2:
+        raise ValueError("K must be [..., S, d]")
+    _expect(V, "V", K.shape, K.dtype)
     *lead, S, d = K.shape
+    _expect(R, "R", (d, L * P), K.dtype)
     n_heads = 1
     for x in lead:
         n_heads *= x
@@ -65,8 +86,8 @@ def hash_keys(K: torch.Tensor, V: torch.Tensor, R: torch.Tensor, L: int,
         ids = torch.empty((*lead, S, L), dtype=torch.uint8, device=K.device)
     if vnorm is None:
         vnorm = torch.empty((*lead, S), dtype=torch.float32, device=K.device)
-    if tuple(ids.shape) != (*lead, S, L) or tuple(vnorm.shape) != (*lead, S):
-        raise ValueError("ids / vnorm do not match K's layout")
+    _expect(ids, "ids", (*lead, S, L), torch.uint8)
+    _expect(vnorm, "vnorm", (*lead, S), torch.float32)
     esz = K.element_size()
     dt = _dtype_code(K)
     ws_bytes = lib.socket_hash_keys_workspace_bytes(dt, n_heads, n, d, L, P)
@@ -84,7 +105,8 @@ def bucket_probs(Q: torch.Tensor, R: torch.Tensor, Hkv: int, L: int, P: int,
     """Soft bucket table [B, Hkv, 2^P, L, G] (float32) for queries Q [B, Hq, d]."""
     lib = _lib.load()
     B, Hq, d = Q.shape
-    G = Hq // Hkv
+    G = _heads(Hq, Hkv)
+    _expect(R, "R", (d, L * P), Q.dtype)
     table = torch.empty((B, Hkv, 2 ** P, L, G), dtype=torch.float32, device=Q.device)
     st = lib.socket_bucket_probs(_dev(Q, "Q"), _dev(R, "R"), _dtype_code(Q), B,
                                  Hq, Hkv, d, L, P, float(tau),
@@ -99,7 +121,8 @@ def hard_bucket_table(Q: torch.Tensor, R: torch.Tensor, Hkv: int, L: int,
     the tau -> 0 limit of bucket_probs (hard LSH)."""
     lib = _lib.load()
     B, Hq, d = Q.shape
-    G = Hq // Hkv
+    G = _heads(Hq, Hkv)
+    _expect(R, "R", (d, L * P), Q.dtype)
     table = torch.empty((B, Hkv, 2 ** P, L, G), dtype=torch.float32, device=Q.device)
     st = lib.socket_hard_bucket_table(_dev(Q, "Q"), _dev(R, "R"), _dtype_code(Q), B, Hq, Hkv,
                                       d, L, P, _dev(table, "table"), _stream(Q))
@@ -114,10 +137,22 @@ def score(table: torch.Tensor, ids: torch.Tensor, vnorm: torch.Tensor,
     table [B, Hkv, 2^P, L, G]; ids [B, Hkv, S, L]; vnorm [B, Hkv, S].
     """
     lib = _lib.load()
+    _expect(table, "table", None, torch.float32)
+    if table.dim() != 5:
+        raise ValueError("table must be [B, Hkv, 2^P, L, G]")
     B, Hkv, nb, L, G = table.shape
     P = nb.bit_length() - 1
+    if nb != 1 << P or Hq != Hkv * G:
+        raise ValueError(f"table {tuple(table.shape)} does not fit Hq={Hq} (2^P buckets, "
+                         "G = Hq / Hkv heads per slot)")
+    if ids.dim() != 4:
+        raise ValueError("ids must be [B, Hkv, S, L]")
     S = ids.shape[-2]
+    _expect(ids, "ids", (B, Hkv, S, L), torch.uint8)
+    _expect(vnorm, "vnorm", (B, Hkv, S), torch.float32)
     n = S if n_keys is None else int(n_keys)
+    if not 0 <= n <= S:
+        raise ValueError(f"n_keys={n} outside [0, {S}]")
     scores = torch.empty((B, Hq, n), dtype=torch.float32, device=table.device)
     st = lib.socket_score(_dev(table, "table"), _dev(ids, "ids"),
                           _dev(vnorm, "vnorm"), B, Hq, Hkv, n, S, L, P,
@@ -129,6 +164,7 @@ def score(table: torch.Tensor, ids: torch.Tensor, vnorm: torch.Tensor,
 def topk(scores: torch.Tensor, k: int) -> torch.Tensor:
     """Deterministic top-k of each row of scores [..., n] -> int32 [..., min(k, n)]."""
     lib = _lib.load()
+    _expect(scores, "scores", None, torch.float32)
     *lead, n = scores.shape
     rows = 1
     for x in lead:
@@ -146,9 +182,16 @@ def sparse_attn(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
                 idx: torch.Tensor) -> torch.Tensor:
     """Attention of Q [B, Hq, d] over the keys idx [B, Hq, kk] of K, V [B, Hkv, S, d]."""
     lib = _lib.load()
+    _dtype_code(Q)
     B, Hq, d = Q.shape
+    if K.dim() != 4:
+        raise ValueError("K must be [B, Hkv, S, d]")
     _, Hkv, S, _ = K.shape
+    _heads(Hq, Hkv)
+    _expect(K, "K", (B, Hkv, S, d), Q.dtype)
+    _expect(V, "V", (B, Hkv, S, d), Q.dtype)
     kk = idx.shape[-1]
+    _expect(idx, "idx", (B, Hq, kk), torch.int32)
     out = torch.empty_like(Q)
     ws = _workspace(lib.socket_sparse_attn_workspace_bytes(B, Hq, d, kk), Q.device)
     st = lib.socket_sparse_attn(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"),
@@ -163,8 +206,14 @@ def dense_attn(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
                n: int | None = None) -> torch.Tensor:
     """Dense attention of Q [B, Hq, d] over the first n keys of K, V [B, Hkv, S, d]."""
     lib = _lib.load()
+    _dtype_code(Q)
     B, Hq, d = Q.shape
+    if K.dim() != 4:
+        raise ValueError("K must be [B, Hkv, S, d]")
     _, Hkv, S, _ = K.shape
+    _heads(Hq, Hkv)
+    _expect(K, "K", (B, Hkv, S, d), Q.dtype)
+    _expect(V, "V", (B, Hkv, S, d), Q.dtype)
     n = S if n is None else int(n)
     out = torch.empty_like(Q)
     ws = _workspace(lib.socket_dense_attn_workspace_bytes(B, Hq, d, n), Q.device)
@@ -173,6 +222,33 @@ def dense_attn(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
                                ws.numel(), _stream(Q))
     check(st, "socket_dense_attn")
     return out
+
+
+def _check_decode_args(Q, K, V, R, ids, vnorm, L, P, k, n_keys, out, idx_out, scores_out,
+                       group_shared):
+    """Shapes and dtypes of a decode call; returns (B, Hq, Hkv, d, S, n)."""
+    _dtype_code(Q)
+    if Q.dim() != 3 or K.dim() != 4:
+        raise ValueError("Q must be [B, Hq, d] and K [B, Hkv, S, d]")
+    B, Hq, d = Q.shape
+    _, Hkv, S, _ = K.shape
+    _heads(Hq, Hkv)
+    _expect(K, "K", (B, Hkv, S, d), Q.dtype)
+    _expect(V, "V", (B, Hkv, S, d), Q.dtype)
+    _expect(R, "R", (d, L * P), Q.dtype)
+    _expect(ids, "ids", (B, Hkv, S, L), torch.uint8)
+    _expect(vnorm, "vnorm", (B, Hkv, S), torch.float32)
+    n = S if n_keys is None else int(n_keys)
+    if not 1 <= n <= S:
+        raise ValueError(f"n_keys={n} outside [1, {S}]")
+    rows = Hkv if group_shared else Hq
+    if out is not None:
+        _expect(out, "out", (B, Hq, d), Q.dtype)
+    if idx_out is not None:
+        _expect(idx_out, "idx_out", (B, rows, min(int(k), n)), torch.int32)
+    if scores_out is not None:
+        _expect(scores_out, "scores_out", (B, rows, n), torch.float32)
+    return B, Hq, Hkv, d, S, n
 
 
 def decode_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, n_keys: int,
@@ -194,14 +270,14 @@ def decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, R: torch.Tensor,
     an allocation per call.
     """
     lib = _lib.load()
-    B, Hq, d = Q.shape
-    _, Hkv, S, _ = K.shape
-    n = S if n_keys is None else int(n_keys)
+    B, Hq, Hkv, d, S, n = _check_decode_args(Q, K, V, R, ids, vnorm, L, P, k, n_keys, out,
+                                             idx_out, scores_out, False)
     if out is None:
         out = torch.empty_like(Q)
     need = lib.socket_decode_workspace_bytes(B, Hq, Hkv, d, n, L, P, int(k))
     if workspace is None:
         workspace = _workspace(need, Q.device)
+    _expect(workspace, "workspace", None, torch.uint8)
     st = lib.socket_decode(
         _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(R, "R"), _dev(ids, "ids"),
         _dev(vnorm, "vnorm"), _dtype_code(Q), B, Hq, Hkv, d, n, S, L, P,
@@ -221,9 +297,8 @@ def decode_group_shared(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, R: to
     """GQA group-shared variant of decode: one index set [B, Hkv, kk] per KV
     head from the group's summed scores; returns (out, idx_out, scores_out)."""
     lib = _lib.load()
-    B, Hq, d = Q.shape
-    _, Hkv, S, _ = K.shape
-    n = S if n_keys is None else int(n_keys)
+    B, Hq, Hkv, d, S, n = _check_decode_args(Q, K, V, R, ids, vnorm, L, P, k, n_keys, out,
+                                             idx_out, scores_out, True)
     if out is None:
         out = torch.empty_like(Q)
     need = lib.socket_decode_group_shared_workspace_bytes(B, Hq, Hkv, d, n, L, P, int(k))
