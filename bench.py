@@ -41,8 +41,6 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b_128k_b4")
     ap.add_argument("--layers", type=int, default=4,
                     help="independent KV caches the steps rotate over")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="approximate budget of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-stage-timing", action="store_true")
     ap.add_argument("--skip-prefill-hash", action="store_true",
@@ -59,6 +57,10 @@ def parse():
                     help="leave out the GQA group-shared selection variant")
     ap.add_argument("--skip-ranking-study", action="store_true",
                     help="leave out the soft-versus-hard LSH ranking comparison")
+    ap.add_argument("--skip-other-configs", action="store_true",
+                    help="leave out the 32K (eager and graphed) and 1M-key decode legs")
+    ap.add_argument("--skip-fallback", action="store_true",
+                    help="leave out the timing of the selection's full-row fallback")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 4 times (reference for HBM "
                          "byte counters) and exit")
@@ -124,45 +126,98 @@ def _hip_event(hip):
     return ev.value
 
 
-def cpu_baseline(w, budget_s):
-    """Oracle decode on the host for a bounded sample of the workload."""
-    import numpy as np
-    import torch
+# Inputs of the CPU baseline, set before the worker pool is forked so the
+# workers share them copy-on-write (the GPU is not touched before the fork).
+_CPU = {}
+
+
+def _cpu_prefill_task(b):
+    """Oracle prefill of sequence b (bucket ids and value norms); not timed."""
     from threadpoolctl import threadpool_limits
 
     import oracle as O
+
+    c = _CPU
+    with threadpool_limits(limits=1):
+        return O.hash_keys(c["K"][b], c["R"], c["L"], c["P"]), O.value_norms(c["V"][b])
+
+
+def _cpu_decode_task(t):
+    """One oracle decode step of one sequence on one worker (one thread)."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+
+    step, b = t
+    c = _CPU
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.decode(c["Q"][step][b:b + 1], c["K"][b], c["V"][b], c["R"], c["ids"][b], c["vn"][b],
+                 c["L"], c["P"], c["tau"], c["k"])
+        return time.perf_counter() - t0
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, steps=(0, 1, 127, 255)):
+    """The float64 oracle's decode on the host's cores: every sequence of the
+    batch at the given steps, one (step, sequence) per worker process with one
+    thread each (the oracle as it stands, untuned). Inputs are the workload's
+    seeded tensors drawn on the CPU (same shapes and distributions as the
+    GPU's); the oracle's own prefill hashing is not timed. Runs before the
+    GPU is touched, so the workers are forked from a process without a GPU
+    context."""
+    import multiprocessing as mp
+
+    import numpy as np
+
     import synthetic as W
 
+    steps = [s for s in steps if s < max(1, w.steps)]
     K, V = W.make_keys_values(w, "cpu", seed=0, layer=0)
-    R64 = W.make_hyperplanes(w, "cpu", seed=0, layer=0).double().numpy()
-    tau = float(np.float32(w.tau))
-    done = 0
-    steps = 0
-    elapsed = 0.0
-    with threadpool_limits(limits=1):
-        cache = []
-        for b in range(w.B):                         # prefill, not timed
-            K64 = K[b:b + 1].double().numpy()
-            V64 = V[b:b + 1].double().numpy()
-            cache.append((K64, V64, O.hash_keys(K64, R64, w.L, w.P), O.value_norms(V64)))
-        while elapsed < budget_s and steps < w.steps:
-            Q64 = W.make_query(w, "cpu", seed=0, step=steps, layer=0).double().numpy()
-            t0 = time.perf_counter()
-            for b in range(w.B):
-                K64, V64, ids, vn = cache[b]
-                O.decode(Q64[b:b + 1], K64, V64, R64, ids, vn, w.L, w.P, tau, w.k)
-            elapsed += time.perf_counter() - t0
-            done += w.B
-            steps += 1
+    _CPU.update(
+        K=[K[b:b + 1].double().numpy() for b in range(w.B)],
+        V=[V[b:b + 1].double().numpy() for b in range(w.B)],
+        R=W.make_hyperplanes(w, "cpu", seed=0, layer=0).double().numpy(),
+        Q={s: W.make_query(w, "cpu", seed=0, step=s, layer=0).double().numpy() for s in steps},
+        L=w.L, P=w.P, tau=float(np.float32(w.tau)), k=w.k)
+    del K, V
+    tasks = [(s, b) for s in steps for b in range(w.B)]
+    workers = max(1, min(len(os.sched_getaffinity(0)), 16, len(tasks)))
+    ctx = mp.get_context("fork")
+    with ctx.Pool(min(workers, w.B)) as pool:           # prefill, not timed
+        pre = pool.map(_cpu_prefill_task, range(w.B), chunksize=1)
+    _CPU["ids"] = [p[0] for p in pre]
+    _CPU["vn"] = [p[1] for p in pre]
+    with ctx.Pool(workers) as pool:
+        pool.map(abs, range(workers))                   # workers up before the clock
+        t0 = time.perf_counter()
+        busy = pool.map(_cpu_decode_task, tasks, chunksize=1)
+        wall = time.perf_counter() - t0
+    _CPU.clear()
+    tokens = len(tasks)
     return {
-        "value": done / elapsed,
+        "value": tokens / wall,
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
-        "sample": (f"{w.name}: decode steps 0..{steps - 1} of the whole batch "
-                   f"({done} tokens, {w.Hq} heads x {w.N} keys each), numpy float64 "
-                   f"oracle on one host thread, {elapsed:.1f} s timed (prefill "
-                   f"hashing not timed)"),
+        "cpu_model": _cpu_model(),
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "per_token_s_one_thread": round(sum(busy) / tokens, 3),
+        "sample": (f"{w.name}: decode steps {steps} of all {w.B} sequences ({tokens} tokens, "
+                   f"{w.Hq} heads x {w.N} keys each), numpy float64 oracle, one (step, "
+                   f"sequence) per worker process, {workers} processes of one thread, "
+                   f"{wall:.1f} s wall ({sum(busy):.1f} s of CPU work); inputs drawn on the "
+                   f"CPU from the same seeded distributions, oracle prefill not timed"),
     }
 
 
@@ -200,6 +255,165 @@ def prefill_hash(S, W, torch, dev, reps=10):
             "hbm_frac": round(hbm / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def make_layers(S, W, torch, w, dev, n_layers, n_q):
+    """Independent caches (K, V, R, ids, vnorm) for n_layers rotated layers and
+    n_q queries per layer, all resident on the device."""
+    layers = []
+    for layer in range(n_layers):
+        K, V = W.make_keys_values(w, dev, seed=0, layer=layer)
+        R = W.make_hyperplanes(w, dev, seed=0, layer=layer)
+        ids, vn = S.hash_keys(K, V, R, w.L, w.P)
+        layers.append((K, V, R, ids, vn))
+        torch.cuda.synchronize()
+    queries = [[W.make_query(w, dev, seed=0, step=s, layer=layer) for s in range(n_q)]
+               for layer in range(n_layers)]
+    return layers, queries
+
+
+def decode_call_args(w, layers, queries, step, dt_code, out, idx, ws, ws_bytes, stream,
+                     vnorm=None):
+    """socket_decode's arguments for one step (rotating over the layers)."""
+    layer = step % len(layers)
+    K, V, R, ids, vn = layers[layer]
+    if vnorm is not None:
+        vn = vnorm[layer]
+    Q = queries[layer][step % len(queries[layer])]
+    return (Q.data_ptr(), K.data_ptr(), V.data_ptr(), R.data_ptr(), ids.data_ptr(),
+            vn.data_ptr(), dt_code, w.B, w.Hq, w.Hkv, w.d, w.N, w.N, w.L, w.P, w.tau, w.k,
+            out.data_ptr(), idx.data_ptr(), None, ws.data_ptr(), ws_bytes, stream)
+
+
+def decode_leg(lib, S, W, torch, w, dev, layers, queries, steps, warmup, stage_timing=True,
+               profiling=None, graph=False, vnorm=None):
+    """Times `steps` socket_decode calls (after `warmup` untimed ones) with HIP
+    events on the launch stream, then the same steps through
+    socket_decode_profiled for per-kernel times (events recorded by each
+    dispatch), and optionally the same steps replayed from one HIP graph.
+    Returns the figures of the leg, including the roofline of its longest
+    kernel (algorithmic bytes per launch / mean launch time)."""
+    from soft_lsh_sparse_amd import _lib
+
+    dt_code = _lib.DTYPE_BF16 if w.dtype == "bf16" else _lib.DTYPE_F32
+    out = torch.empty((w.B, w.Hq, w.d), dtype=w.torch_dtype, device=dev)
+    idx = torch.empty((w.B, w.Hq, w.kk), dtype=torch.int32, device=dev)
+    ws_bytes = lib.socket_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, w.N, w.L, w.P, w.k)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    total = warmup + steps
+    arglist = [decode_call_args(w, layers, queries, s, dt_code, out, idx, ws, ws_bytes, stream,
+                                vnorm) for s in range(total)]
+    fn = lib.socket_decode
+    for s in range(warmup):
+        st = fn(*arglist[s])
+        if st:
+            _lib.check(st, "socket_decode")
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for s in range(warmup, total):
+        fn(*arglist[s])
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / steps
+    step_bytes = algorithmic_bytes(w)
+    leg = {
+        "workload": w.name,
+        "ms_per_step": round(ms_per_step, 5),
+        "tokens_per_s": round(w.B / (ms_per_step * 1e-3), 1),
+        "hbm_peak_frac": round(step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+        "algorithmic_bytes_per_step": step_bytes,
+        "steps": steps,
+        "layers_rotated": len(layers),
+        "wall_s_timed": round(wall, 4),
+        "kernel_ms": {},
+        "roofline": None,
+    }
+    if graph:
+        # the same steps captured in one HIP graph (launch overheads removed)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for s in range(warmup, total):
+                a = list(arglist[s])
+                a[-1] = side.cuda_stream
+                fn(*a)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cap = torch.cuda.current_stream().cuda_stream
+            for s in range(warmup, total):
+                a = list(arglist[s])
+                a[-1] = cap
+                st = fn(*a)
+                if st:
+                    _lib.check(st, "socket_decode (capture)")
+        g.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        gms = ev0.elapsed_time(ev1) / steps
+        del g
+        leg["graph_ms_per_step"] = round(gms, 5)
+        leg["graph_tokens_per_s"] = round(w.B / (gms * 1e-3), 1)
+    if not stage_timing:
+        return leg
+    names = decode_kernel_names(lib, w, layers[0][3], dt_code)
+    hip = _hip_runtime()
+    n_ev = 2 * len(names)
+    events = [[_hip_event(hip) for _ in range(n_ev)] for _ in range(steps)]
+    ev_arrays = [(ctypes.c_void_p * n_ev)(*ev) for ev in events]
+    prof = lib.socket_decode_profiled
+    torch.cuda.synchronize()
+    for i, s in enumerate(range(warmup, total)):
+        st = prof(*arglist[s], ev_arrays[i], n_ev)
+        if st:
+            _lib.check(st, "socket_decode_profiled")
+    torch.cuda.synchronize()
+    kernel_ms = {}
+    for j, name in enumerate(names):
+        tot = 0.0
+        for ev in events:
+            ms = ctypes.c_float()
+            rc = hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(ev[2 * j]),
+                                         ctypes.c_void_p(ev[2 * j + 1]))
+            if rc != 0:
+                raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+            tot += ms.value
+        kernel_ms[name] = tot / steps
+    for ev in events:
+        for e in ev:
+            hip.hipEventDestroy(ctypes.c_void_p(e))
+    kbytes = kernel_bytes(w, names)
+    dom = max(kernel_ms, key=kernel_ms.get)
+    # HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary
+    # of this workload; None once the kernel's sources changed
+    traffic = None
+    if profiling is not None:
+        traffic = profiling.load_traffic(
+            os.path.join(ROOT, "profiles", f"decode_{w.name}_hbm_traffic.md"), dom)
+    achieved = kbytes[dom] / (kernel_ms[dom] * 1e-3) / 1e9
+    leg["kernel_ms"] = {k: round(v, 5) for k, v in kernel_ms.items()}
+    leg["roofline"] = {
+        "bound": "hbm",
+        "kernel": dom,
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "algorithmic_bytes_per_launch": kbytes[dom],
+        "avg_launch_ms": round(kernel_ms[dom], 5),
+    }
+    return leg
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -225,6 +439,12 @@ def main():
     import synthetic as W
     from soft_lsh_sparse_amd import _lib, profiling
 
+    # the CPU baseline first: its worker processes are forked before this
+    # process touches the GPU
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(W.WORKLOADS[args.workload])
+
     lib = _lib.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -232,110 +452,31 @@ def main():
     assert w.decode, f"{w.name} is not a decode workload"
     dt_code = _lib.DTYPE_BF16 if w.dtype == "bf16" else _lib.DTYPE_F32
 
-    # ---- setup: caches for every rotated layer, queries for every step
-    layers = []
-    for layer in range(args.layers):
-        K, V = W.make_keys_values(w, dev, seed=0, layer=layer)
-        R = W.make_hyperplanes(w, dev, seed=0, layer=layer)
-        ids, vn = S.hash_keys(K, V, R, w.L, w.P)
-        layers.append((K, V, R, ids, vn))
-        torch.cuda.synchronize()
+    # ---- the headline workload: caches for every rotated layer, queries for
+    # every step, timed decode steps and per-kernel times
     n_q = max(1, min(w.steps, args.steps + args.warmup))
-    queries = [[W.make_query(w, dev, seed=0, step=s, layer=layer)
-                for s in range(n_q)] for layer in range(args.layers)]
+    layers, queries = make_layers(S, W, torch, w, dev, args.layers, n_q)
+    leg = decode_leg(lib, S, W, torch, w, dev, layers, queries, args.steps, args.warmup,
+                     stage_timing=not args.skip_stage_timing, profiling=profiling)
+    ms_per_step = leg["ms_per_step"]
+    tokens_per_s = leg["tokens_per_s"]
+    step_bytes = leg["algorithmic_bytes_per_step"]
+    hbm_frac = leg["hbm_peak_frac"]
+    kernel_ms = leg["kernel_ms"]
+    roofline = leg["roofline"]
+    wall = leg["wall_s_timed"]
     out = torch.empty((w.B, w.Hq, w.d), dtype=w.torch_dtype, device=dev)
     idx = torch.empty((w.B, w.Hq, w.kk), dtype=torch.int32, device=dev)
-    ws_bytes = lib.socket_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, w.N, w.L,
-                                                 w.P, w.k)
+    ws_bytes = lib.socket_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, w.N, w.L, w.P, w.k)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-
-    def decode_args(step):
-        layer = step % args.layers
-        K, V, R, ids, vn = layers[layer]
-        Q = queries[layer][step % n_q]
-        return (Q.data_ptr(), K.data_ptr(), V.data_ptr(), R.data_ptr(),
-                ids.data_ptr(), vn.data_ptr(), dt_code, w.B, w.Hq, w.Hkv, w.d,
-                w.N, w.N, w.L, w.P, w.tau, w.k, out.data_ptr(), idx.data_ptr(),
-                None, ws.data_ptr(), ws_bytes, stream)
-
-    total = args.warmup + args.steps
-    arglist = [decode_args(s) for s in range(total)]
     fn = lib.socket_decode
-
-    for s in range(args.warmup):
-        st = fn(*arglist[s])
-        if st:
-            _lib.check(st, "socket_decode")
-    torch.cuda.synchronize()
-
-    # ---- timed region: exactly `steps` decode steps
+    total = args.warmup + args.steps
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for s in range(args.warmup, total):
-        fn(*arglist[s])
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    tokens_per_s = w.B / (ms_per_step * 1e-3)
 
-    step_bytes = algorithmic_bytes(w)
-    hbm_frac = step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9)
-
-    # ---- per-kernel times of the same decode: socket_decode_profiled
-    # dispatches every kernel with a start and a stop HIP event, recorded by
-    # the dispatch itself on the launch stream (same kernels, same order,
-    # same workspace)
-    kernel_ms = {}
-    roofline = None
-    if not args.skip_stage_timing:
-        names = decode_kernel_names(lib, w, layers[0][3], dt_code)
-        hip = _hip_runtime()
-        n_ev = 2 * len(names)
-        events = [[_hip_event(hip) for _ in range(n_ev)] for _ in range(args.steps)]
-        ev_arrays = [(ctypes.c_void_p * n_ev)(*ev) for ev in events]
-        prof = lib.socket_decode_profiled
-        torch.cuda.synchronize()
-        for i, s in enumerate(range(args.warmup, total)):
-            st = prof(*arglist[s], ev_arrays[i], n_ev)
-            if st:
-                _lib.check(st, "socket_decode_profiled")
-        torch.cuda.synchronize()
-        for j, name in enumerate(names):
-            tot = 0.0
-            for ev in events:
-                ms = ctypes.c_float()
-                rc = hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(ev[2 * j]),
-                                             ctypes.c_void_p(ev[2 * j + 1]))
-                if rc != 0:
-                    raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
-                tot += ms.value
-            kernel_ms[name] = tot / args.steps
-        for ev in events:
-            for e in ev:
-                hip.hipEventDestroy(ctypes.c_void_p(e))
-        kbytes = kernel_bytes(w, names)
-        dom = max(kernel_ms, key=kernel_ms.get)
-        # HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE
-        # summary of this workload; None once the kernel's sources changed
-        traffic = profiling.load_traffic(
-            os.path.join(ROOT, "profiles", f"decode_{w.name}_hbm_traffic.md"), dom)
-        achieved = kbytes[dom] / (kernel_ms[dom] * 1e-3) / 1e9
-        roofline = {
-            "bound": "hbm",
-            "kernel": dom,
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": kbytes[dom],
-            "avg_launch_ms": round(kernel_ms[dom], 5),
-        }
+    def decode_args(step):
+        return decode_call_args(w, layers, queries, step, dt_code, out, idx, ws, ws_bytes, stream)
 
     # ---- dense baseline: exact attention over every key of the same
     # rotated caches and queries (the comparison SOCKET's speed-up is stated
@@ -523,15 +664,46 @@ def main():
                         hit += torch.isin(pos[b, g], sel).float().mean().item()
                 study["planted_recall_" + name] = round(hit / (w.B * w.Hkv), 4)
 
+    # ---- the selection's full-row fallback, forced on every row: value norms
+    # vanish except on the keys the score kernel samples for its thresholds
+    # (the first 128 keys of every 1024 at this shape: 16 waves of 1024 keys
+    # per block), so fewer than k keys reach the largest block threshold and
+    # every row is scored again in full by the select kernel
+    fallback = None
+    if not args.skip_fallback and w.name == "llama3_8b_128k_b4":
+        keep = (torch.arange(w.N, device=dev) % 1024) < 128
+        vmask = [lay[4] * keep for lay in layers]
+        fb = decode_leg(lib, S, W, torch, w, dev, layers, queries, min(args.steps, 20),
+                        min(args.warmup, 3), stage_timing=not args.skip_stage_timing,
+                        vnorm=vmask)
+        fallback = {"ms_per_step": fb["ms_per_step"], "kernel_ms": fb["kernel_ms"],
+                    "slowdown_vs_decode": round(fb["ms_per_step"] / ms_per_step, 2),
+                    "rows_forced": w.B * w.Hq}
+        del vmask
+
+    # ---- the other decode configurations, one leg each: 32K keys (B=1,
+    # 20 rotated layers so the 256 MB Infinity Cache cannot hold a step's
+    # working set; eager and replayed from one HIP graph, since launches
+    # weigh most there) and 1M keys (B=1, L=64, P=6, k=16384)
+    others = None
+    if not args.skip_other_configs and w.name == "llama3_8b_128k_b4":
+        others = {}
+        for name, n_layers, steps, warm, graph in (("llama3_8b_32k", 20, 64, 5, True),
+                                                   ("llama3_8b_1m", 2, 8, 2, False)):
+            ow = W.WORKLOADS[name]
+            olayers, oq = make_layers(S, W, torch, ow, dev, n_layers, 1)
+            others[name] = decode_leg(lib, S, W, torch, ow, dev, olayers, oq, steps, warm,
+                                      stage_timing=not args.skip_stage_timing,
+                                      profiling=profiling, graph=graph)
+            del olayers, oq
+            torch.cuda.empty_cache()
+
     # ---- prefill hashing (bf16 MFMA projections, fused sign packing and
     # value norms) on its own workload, reported beside the decode figure
     prefill = None
     if not args.skip_prefill_hash:
         prefill = prefill_hash(S, W, torch, dev)
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_seconds)
 
     rec = {
         "metric": METRIC,
@@ -560,6 +732,8 @@ def main():
         "ranking_study": study,
         "group_shared_variant": group,
         "prefill_hash": prefill,
+        "select_fallback": fallback,
+        "other_configs": others,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),
     }
