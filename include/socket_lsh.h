@@ -17,8 +17,9 @@
  * Conventions shared by every call
  *   - All tensor pointers are DEVICE pointers, caller-allocated, contiguous,
  *     row-major in the layouts written next to each argument. The library
- *     allocates nothing, frees nothing and keeps no state between calls.
-
+ *     allocates nothing, frees nothing and keeps no state between calls
+ *     (socket_decode_noalloc aside: it works in a device array the library
+ *     holds on each GPU, see there).
  *   - dtype selects the element type of Q, K, V, R and the attention output:
  *     SOCKET_DTYPE_F32 (float) or SOCKET_DTYPE_BF16 (bfloat16 bits, round to
  *     nearest even on output). Bucket ids are uint8, norms, probabilities
@@ -302,6 +303,36 @@ socket_status socket_decode(const void* Q, const void* K, const void* V,
                             void* out, int32_t* idx_out, float* scores_out,
                             void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * Allocation-free decode, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It is socket_decode with the workspace in a device array the
+ * library owns instead of caller memory: SOCKET_DECODE_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) per GPU, held by every GPU the library runs on until the process
+ * ends. Arguments, validation and results are those of socket_decode (the
+ * same kernels, bit for bit), without workspace and workspace_bytes.
+ *   - A call whose socket_decode_workspace_bytes(...) exceeds the array
+ *     returns SOCKET_ERR_UNSUPPORTED (e.g. B = 1 at 131072 keys fits,
+ *     B = 4 at 131072 keys does not).
+ *   - It calls no hipMalloc, hipFree or other allocating routine. The first
+ *     call on each device resolves the array's address there
+ *     (hipGetSymbolAddress, with that device current); make that first call
+ *     outside graph capture.
+ *   - All calls on one GPU share its array, which keeps the last call's
+ *     contents (nothing in it needs clearing between calls). Calls that
+ *     overlap on one GPU (several streams or threads at once) race on it:
+ *     the caller must serialise them.
+ */
+#define SOCKET_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+socket_status socket_decode_noalloc(const void* Q, const void* K, const void* V,
+                                    const void* R, const uint8_t* ids,
+                                    const float* vnorm, socket_dtype dtype,
+                                    int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                                    int64_t n_keys, int64_t head_stride_rows,
+                                    int32_t L, int32_t P, float tau, int64_t k,
+                                    void* out, int32_t* idx_out,
+                                    float* scores_out, void* stream);
 
 /*
  * socket_decode with per-kernel timing: identical work and results. In

@@ -24,6 +24,9 @@ SOCKET_ERR_HIP = 4
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 
+# size of the library's device array behind socket_decode_noalloc
+DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
 # name -> (restype, argtypes); mirrors include/socket_lsh.h
 SIGNATURES = {
     "socket_version": (c_int32, []),
@@ -72,6 +75,8 @@ SIGNATURES = {
                               c_float, c_int64, c_void_p, c_void_p, c_void_p,
                               c_void_p, c_size_t, c_void_p]),
 }
+SIGNATURES["socket_decode_noalloc"] = (
+    c_int, SIGNATURES["socket_decode"][1][:20] + [c_void_p])
 SIGNATURES["socket_decode_profiled"] = (
     c_int, SIGNATURES["socket_decode"][1] + [c_void_p, c_int32])
 SIGNATURES["socket_decode_kernels"] = (

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "kernels.hpp"
@@ -720,6 +721,68 @@ socket_status socket_decode_profiled(
   return decode_impl(Q, K, V, R, ids, vnorm, dtype, B, Hq, Hkv, d, n_keys,
                      head_stride_rows, L, P, tau, k, out, idx_out, scores_out,
                      workspace, workspace_bytes, stream, events, n_events);
+}
+
+}  // extern "C"
+
+// ----------------------------------------------------- allocation-free decode
+// The decode workspace in a device array of the library instead of caller
+// memory. Every GPU the library runs on holds its own copy of the array (at
+// its own address) until the process ends. In host code the array's name is
+// only a stand-in: the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is used.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[SOCKET_DECODE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of the array (resolved on the first call there).
+socket_status current_scratch(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return from_hip(err, "socket_decode_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SOCKET_ERR_UNSUPPORTED, "socket_decode_noalloc: device %d beyond the %d the "
+                "library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || p == nullptr)
+      return from_hip(err != hipSuccess ? err : hipErrorInvalidSymbol,
+                      "socket_decode_noalloc: hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SOCKET_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+socket_status socket_decode_noalloc(const void* Q, const void* K, const void* V, const void* R,
+                                    const uint8_t* ids, const float* vnorm, socket_dtype dtype,
+                                    int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                                    int64_t n_keys, int64_t head_stride_rows, int32_t L,
+                                    int32_t P, float tau, int64_t k, void* out,
+                                    int32_t* idx_out, float* scores_out, void* stream) {
+  // shapes first (the workspace size below is only meaningful for them)
+  SOCKET_TRY(check_decode(dtype, B, Hq, Hkv, d, n_keys, head_stride_rows, L, P, k));
+  const size_t need = decode_layout(B, Hq, Hkv, d, n_keys, L, P, k).total;
+  if (need > (size_t)SOCKET_DECODE_NOALLOC_SCRATCH_BYTES)
+    return fail(SOCKET_ERR_UNSUPPORTED,
+                "socket_decode_noalloc: this call needs %zu bytes of workspace, more than "
+                "the library's %zu-byte device array (use socket_decode with a workspace)",
+                need, (size_t)SOCKET_DECODE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  SOCKET_TRY(current_scratch(&ws));
+  return decode_impl(Q, K, V, R, ids, vnorm, dtype, B, Hq, Hkv, d, n_keys, head_stride_rows, L,
+                     P, tau, k, out, idx_out, scores_out, ws,
+                     (size_t)SOCKET_DECODE_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0);
 }
 
 int32_t socket_decode_kernels(const uint8_t* ids, socket_dtype dtype, int32_t B,
