@@ -169,10 +169,13 @@ socket_status socket_hard_bucket_table(const void* Q, const void* R, socket_dtyp
  *   ids     [B*Hkv, head_stride_rows, L] uint8
  *   vnorm   [B*Hkv, head_stride_rows] float32
  *   scores  [B, Hq, n_keys] float32 (output)
- * The L probabilities are summed in float32 in the order l = (t + r) mod L,
- * t = 0 .. L-1, where r = key index mod 16 when L is 16, 32 or 64 and the id
- * rows are 16-byte aligned (this spreads LDS banks), else r = 0; the sum is
- * then multiplied by the value norm.
+ * The L probabilities are summed in float32 in a fixed order, then
+ * multiplied by the value norm. With r = key index mod 16, when L is 16, 32
+ * or 64 and the id rows are 16-byte aligned (this spreads LDS banks): for
+ * P = 8, 32 or 16 tables and 4 query heads per block, table
+ * 16c + (t + r) mod 16 at step 16c + t (t < 16: each run of 16 tables
+ * rotated on its own); otherwise l = (t + r) mod L at step t. In all other
+ * cases l = t.
  */
 socket_status socket_score(const float* table, const uint8_t* ids,
                            const float* vnorm, int32_t B, int32_t Hq,

@@ -525,6 +525,7 @@ socket_status decode_impl(const void* Q, const void* K, const void* V,
     sa.P = P;
     sa.stride = head_stride_rows;
     sa.rotated = score_rotated(ids, head_stride_rows, L) ? 1 : 0;
+    sa.region = sa.rotated && score_region(sa.Hq / sa.Hkv, P, L) ? 1 : 0;
     sa.scores = rowbuf;
     err = launch_topk_select(sa, rows, s);
     if (err != hipSuccess) return from_hip(err, "socket_decode: topk");
@@ -653,6 +654,7 @@ socket_status decode_group_impl(const void* Q, const void* K, const void* V, con
     sa.P = P;
     sa.stride = head_stride_rows;
     sa.rotated = score_rotated(ids, head_stride_rows, L) ? 1 : 0;
+    sa.region = sa.rotated && score_region(sa.Hq / sa.Hkv, P, L) ? 1 : 0;
     sa.scores = rowbuf;
     err = launch_topk_select(sa, rows, s);
     if (err != hipSuccess) return from_hip(err, "group-shared decode: topk");

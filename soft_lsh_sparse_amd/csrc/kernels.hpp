@@ -78,9 +78,14 @@ ScoreGeom plan_score(int bhkv, int64_t n_keys, int L, int P, int G);
 // (virtual head) / np). Returns the largest such Gp (a power of two dividing
 // G) whose table fits, or 0 when not even Gp = 1 does.
 int score_pack(int L, int P, int G);
-// true when the kernel sums each key's tables in the rotated order
-// l = (t + key) mod L, t = 0..L-1 (with key taken mod 16); else l = t
+// true when the kernel sums each key's tables in a rotated order (r = key
+// mod 16): l = (t + r) mod L, t = 0..L-1, or, when score_region(G, P, L),
+// l = 16 c + (t' + r) mod 16 for t = 16 c + t' (each 16-table region
+// rotated on its own); else l = t
 bool score_rotated(const uint8_t* ids, int64_t stride, int L);
+// The rotated path keeps the table in 16-table regions (G = 4, P = 8,
+// L = 16 or 32).
+bool score_region(int G, int P, int L);
 // LDS bytes of one score block (build: the block builds its table).
 size_t score_lds_bytes(int L, int P, int G, bool build);
 constexpr size_t kLdsBytesPerCU = 160 * 1024;
@@ -164,6 +169,7 @@ struct SelectArgs {
   int id_div;                 // virtual head v reads the ids of head v / id_div
   int64_t stride;
   int rotated;                // score_rotated(ids, stride, L)
+  int region;                 // rotated and score_region(Hq / Hkv, P, L)
   float* scores;              // [rows][n] row buffers
 };
 hipError_t launch_topk_select(const SelectArgs& a, int rows, hipStream_t stream);

@@ -154,10 +154,19 @@ __device__ __forceinline__ bool score_block_coords(int bhkv, int segs, int& bg,
   return true;
 }
 
-// The table of batch*KV head bg into LDS. The blocks of one head run on
-// one XCD and read the same table: each starts at its own round of 16 KB
-// (start_round) so that they do not all ask the same L2 lines at once.
-template <int G>
+// Region layout of the LDS table (G = 4 query heads, P = 8, L = 16 or 32,
+// the rotated scorer): tables 16c .. 16c + 15 form region c at byte 65536 c;
+// in it, bucket u takes 256 bytes, 16 table slots of 16 bytes (the 4 heads'
+// probabilities). Float index of entry (u, l, j):
+__host__ __device__ __forceinline__ int region_index(int u, int l, int j) {
+  return (l >> 4) * 16384 + u * 64 + (l & 15) * 4 + j;
+}
+
+// The table of batch*KV head bg into LDS ([u][l][j], or the region layout
+// when REGION). The blocks of one head run on one XCD and read the same
+// table: each starts at its own round of 16 KB (start_round) so that they do
+// not all ask the same L2 lines at once.
+template <int G, bool REGION>
 __device__ __forceinline__ void stage_table(float* tab, const float* table, int bg,
                                             int L, int P, int start_round, int id_div,
                                             int table_G) {
@@ -167,8 +176,30 @@ __device__ __forceinline__ void stage_table(float* tab, const float* table, int 
     // group table too large for one block): element by element
     const float* src = table + (int64_t)(bg / id_div) * ((int64_t)tsize / G * table_G) +
                        (bg % id_div) * G;
-    for (int i = threadIdx.x; i < tsize; i += blockDim.x)
-      tab[i] = src[(int64_t)(i / G) * table_G + i % G];
+    for (int i = threadIdx.x; i < tsize; i += blockDim.x) {
+      const int u = i / (L * G), l = (i / G) % L, j = i % G;
+      tab[REGION ? region_index(u, l, j) : i] = src[(int64_t)(i / G) * table_G + j];
+    }
+  } else if (REGION) {
+    // direct-to-LDS loads into the region layout: LDS slot f (16 bytes) of
+    // region c, bucket u, table 16c + s holds table slot u * L + 16c + s
+    const float4* src = reinterpret_cast<const float4*>(table + (int64_t)bg * tsize);
+    const int n4 = tsize / 4;
+    const int lane = threadIdx.x & 63;
+    const int per_round = (int)blockDim.x;
+    const int rounds = (n4 + per_round - 1) / per_round;
+    const int first = start_round % rounds;
+    for (int k = 0; k < rounds; ++k) {
+      const int rr = k + first < rounds ? k + first : k + first - rounds;
+      const int f0 = rr * per_round + (int)(threadIdx.x & ~63);  // wave-uniform
+      const int f = f0 + lane;
+      if (f0 < n4 && f < n4) {
+        const int c = f >> 12, u = (f >> 4) & 255, sl = f & 15;
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(src + u * L + c * 16 + sl),
+            (__attribute__((address_space(3))) void*)(tab + (size_t)f0 * 4), 16, 0, 0);
+      }
+    }
   } else if (tsize % 4 == 0) {  // every head's table then starts 16-byte aligned
     // direct-to-LDS loads: 64 lanes x 16 bytes per instruction into
     // consecutive LDS, no registers held, all in flight at once
@@ -323,7 +354,7 @@ __device__ __forceinline__ double xor32_f64(double v) {
 // The entries are written by 8 threads per (table, row) pair p = l * G + j:
 // thread c takes buckets 32c .. 32c + 31, for which it needs the 8 products
 // of group A, 4 of group B and 1 of group C. Contains __syncthreads().
-template <int G, class Before>
+template <int G, bool REGION, class Before>
 __device__ __forceinline__ void build_table(float* tab, double* w, const ScoreArgs& a, int bg,
                                             Before before) {
   constexpr int P = 8;
@@ -486,15 +517,20 @@ __device__ __forceinline__ void build_table(float* tab, double* w, const ScoreAr
       Cv *= (cc & 1) ? v1[6] : v0[6];
       Cv *= (cc & 2) ? v1[7] : v0[7];
 #pragma unroll
-      for (int i = 0; i < 32; ++i)
-        tab[(c * 32 + i) * pairs + p] = (float)((A[i & 7] * Bq[i >> 3]) * Cv);
+      for (int i = 0; i < 32; ++i) {
+        const float e = (float)((A[i & 7] * Bq[i >> 3]) * Cv);
+        if constexpr (REGION)  // p = l * 4 + j: region p / 64, slot p % 64
+          tab[(p >> 6) * 16384 + (c * 32 + i) * 64 + (p & 63)] = e;
+        else
+          tab[(c * 32 + i) * pairs + p] = e;
+      }
     }
   }
 }
 
 // The block's share (segment seg of segs) of its head's table, from LDS to
 // table_out.
-template <int G>
+template <int G, bool REGION>
 __device__ __forceinline__ void store_table_share(const float* tab, const ScoreArgs& a, int bg,
                                                   int seg) {
   const int tsize = (1 << a.P) * a.L * G;
@@ -503,7 +539,10 @@ __device__ __forceinline__ void store_table_share(const float* tab, const ScoreA
   const int s1 = min(n4, (seg + 1) * per);
   float4* dst = reinterpret_cast<float4*>(a.table_out + (int64_t)bg * tsize);
   const float4* src = reinterpret_cast<const float4*>(tab);
-  for (int i = seg * per + (int)threadIdx.x; i < s1; i += kScoreThreads) dst[i] = src[i];
+  for (int i = seg * per + (int)threadIdx.x; i < s1; i += kScoreThreads) {
+    // slot i = u * L + l of the [u][l][j] layout the select kernel reads
+    dst[i] = REGION ? src[region_index(i / a.L, i % a.L, 0) / 4] : src[i];
+  }
 }
 
 // Per query row j of the group: an order key that at least m of the sampled
@@ -593,7 +632,7 @@ __device__ __forceinline__ void block_thresholds(const uint32_t (&uk)[kPrefetch]
 // The common body of the score kernels. Scorer: prefetch() requests the
 // first step of ids and norms; score(q, i, acc, vn) scores key i (relative
 // to n0) of slot q of a step and requests the key kWaveStep further on.
-template <int G, bool BUILD, class Scorer>
+template <int G, bool BUILD, bool REGION, class Scorer>
 __device__ void score_block(const ScoreArgs& a, int bg, int seg, float* tab, Scorer& sc,
                             const WaveRange& wr) {
   const int b = bg / a.Hkv, g = bg % a.Hkv;
@@ -608,14 +647,15 @@ __device__ void score_block(const ScoreArgs& a, int bg, int seg, float* tab, Sco
   if (a.select)
     for (int i = threadIdx.x; i < 2 * G * kThrBins; i += kScoreThreads) hist[i] = 0u;
   if constexpr (BUILD) {
-    build_table<G>(tab, reinterpret_cast<double*>(lds + treg), a, bg, [&] { sc.prefetch(); });
+    build_table<G, REGION>(tab, reinterpret_cast<double*>(lds + treg), a, bg,
+                           [&] { sc.prefetch(); });
   } else {
     sc.prefetch();
-    stage_table<G>(tab, a.table, bg, a.L, a.P, seg, a.id_div, a.table_G);
+    stage_table<G, REGION>(tab, a.table, bg, a.L, a.P, seg, a.id_div, a.table_G);
   }
   __syncthreads();
   if constexpr (BUILD)
-    if (a.table_out) store_table_share<G>(tab, a, bg, seg);
+    if (a.table_out) store_table_share<G, REGION>(tab, a, bg, seg);
 
   // first step of every wave: scored, then (decode) the block thresholds
   float acc[kPrefetch][G], vn[kPrefetch];
@@ -773,6 +813,109 @@ struct RotScorer {
   }
 };
 
+// Rotated scorer over the region layout (G = 4 query heads, P = 8, L = 16
+// or 32): lane key n walks the 16 tables of each region c in the order
+// 16c + (t + r) mod 16, r = n mod 16 (the key's id row is rotated by r
+// bytes within each 16-byte half), so the 16 lanes the LDS serves together
+// hit 16 bank groups. One v_perm_b32 forms a lookup's LDS byte address
+// 65536 c + 256 u + 16 s: byte 1 the (rotated) id byte u, byte 0 the lane's
+// slot s = (t + r) mod 16 times 16 from a per-lane constant, byte 2 the
+// region bit from another constant (0 for region 0).
+template <int LW>
+struct RegionScorer {
+  static constexpr int G = 4;
+  static constexpr int L = LW * 4;
+  static constexpr int kChunk = 64 / G;  // lookups per dependency step
+  static_assert(LW == 4 || LW == 8, "16 or 32 tables");
+  __amdgpu_buffer_rsrc_t idseg, vseg;
+  const float* tab;
+  int we, wb;
+  uint4 pf[kPrefetch][LW / 4];
+  float pf_vn[kPrefetch];
+  int r, rb;
+  uint32_t slot0[4];  // region 0: byte q of word k = slot of step 4k + q
+  uint32_t slot1[8];  // region 1: bytes 0, 1 of word k = slots of steps 16 + 2k, + 1; bytes 2, 3 = 1
+
+  __device__ RegionScorer(const ScoreArgs& a, int bg, const WaveRange& wr, const float* tab_)
+      : tab(tab_), we(wr.we), wb(wr.wb) {
+    const int64_t hg = bg / a.id_div;  // the KV head whose ids this block reads
+    idseg = raw_rsrc(a.ids + (hg * a.stride + wr.n0) * L, (uint32_t)wr.cnt * L);
+    vseg = raw_rsrc(a.vnorm + hg * a.stride + wr.n0, (uint32_t)wr.cnt * 4u);
+    // n0 + wb is a multiple of 16: every key of this lane has r = lane mod 16
+    const int lane = threadIdx.x & 63;
+    r = lane & 15;
+    rb = r & 3;
+    auto slot = [&](int t) { return (uint32_t)(((t + r) & 15) << 4); };
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      slot0[k] = slot(4 * k) | slot(4 * k + 1) << 8 | slot(4 * k + 2) << 16 | slot(4 * k + 3) << 24;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) slot1[k] = slot(2 * k) | slot(2 * k + 1) << 8 | 0x01010000u;
+#pragma unroll
+    for (int q = 0; q < kPrefetch; ++q) {
+      pf_vn[q] = 0.f;
+#pragma unroll
+      for (int k = 0; k < LW / 4; ++k) pf[q][k] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  __device__ __forceinline__ void load(int q, int i) {
+#pragma unroll
+    for (int k = 0; k < LW / 4; ++k) {
+      const u32x4v_t x = __builtin_amdgcn_raw_buffer_load_b128(idseg, (uint32_t)i * L + k * 16, 0, 0);
+      pf[q][k] = make_uint4(x.x, x.y, x.z, x.w);
+    }
+    pf_vn[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vseg, (uint32_t)i * 4u, 0, 0));
+  }
+
+  __device__ __forceinline__ void prefetch() {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < kPrefetch; ++q) {
+      const int i = wb + q * 64 + lane;
+      if (i < we) load(q, i);
+    }
+  }
+
+  __device__ __forceinline__ void score(int q, int i, bool valid, float (&acc)[G], float& vn) {
+    uint32_t w[LW];
+    const uint64_t by1 = __ballot(r & 4), by2 = __ballot(r & 8);
+#pragma unroll
+    for (int k = 0; k < LW / 4; ++k) {  // each 16-byte half rotated by r
+      uint32_t h[4] = {pf[q][k].x, pf[q][k].y, pf[q][k].z, pf[q][k].w};
+      rotate_bytes<4>(h, by1, by2, rb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[4 * k + e] = h[e];
+    }
+    vn = pf_vn[q];
+    if (i + kWaveStep < we) load(q, i + kWaveStep);
+#pragma unroll
+    for (int j = 0; j < G; ++j) acc[j] = 0.f;
+    if (!valid) return;
+#pragma unroll
+    for (int t = 0; t < L; ++t) {
+      // byte selectors: 0-3 pick bytes of the slot word, 4-7 bytes of the
+      // id word, 0x0c gives 0
+      const uint32_t addr =
+          t < 16 ? __builtin_amdgcn_perm(w[t >> 2], slot0[(t & 15) >> 2],
+                                         0x0c0c0000u | ((4u + (t & 3)) << 8) | (uint32_t)(t & 3))
+                 : __builtin_amdgcn_perm(w[t >> 2], slot1[(t & 15) >> 1],
+                                         0x0c020000u | ((4u + (t & 3)) << 8) | (uint32_t)(t & 1));
+      // the table is the block's dynamic LDS, which starts at LDS address 0
+      // (the kernel has no static LDS; the host checks it before launching
+      // this scorer): addr is the slot's absolute LDS address
+      typedef float f32x4_t __attribute__((ext_vector_type(4)));
+      const f32x4_t x = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(
+          (uintptr_t)addr);
+      const float pr[G] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int j = 0; j < G; ++j) acc[j] = t == 0 ? pr[j] : acc[j] + pr[j];
+      if ((t + 1) % kChunk == 0 && t + 1 < L)
+        fence_chunk<G, LW>(acc, w, (t + 1) / 4, std::min(LW, (t + 1 + kChunk) / 4));
+    }
+  }
+};
+
 // General scorer: any L (byte loads of the ids, tables summed in order
 // l = 0..L-1).
 template <int G>
@@ -806,14 +949,19 @@ struct GenericScorer {
   }
 };
 
-template <int G, int LW, bool BUILD>
+template <int G, int LW, bool BUILD, bool REGION>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(ScoreArgs a) {
   extern __shared__ __align__(16) float tab[];
   int bg, seg;
   if (!score_block_coords(a.bhkv, a.segs, bg, seg)) return;
   const WaveRange wr(a, seg);
-  RotScorer<G, LW> sc(a, bg, wr, tab);
-  score_block<G, BUILD>(a, bg, seg, tab, sc, wr);
+  if constexpr (REGION) {
+    RegionScorer<LW> sc(a, bg, wr, tab);
+    score_block<G, BUILD, true>(a, bg, seg, tab, sc, wr);
+  } else {
+    RotScorer<G, LW> sc(a, bg, wr, tab);
+    score_block<G, BUILD, false>(a, bg, seg, tab, sc, wr);
+  }
 }
 
 template <int G>
@@ -823,7 +971,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_generic(ScoreArgs 
   if (!score_block_coords(a.bhkv, a.segs, bg, seg)) return;
   const WaveRange wr(a, seg);
   GenericScorer<G> sc(a, bg, wr, tab);
-  score_block<G, false>(a, bg, seg, tab, sc, wr);
+  score_block<G, false, false>(a, bg, seg, tab, sc, wr);
 }
 
 template <int G>
@@ -832,26 +980,48 @@ void set_lds_attributes() {
   if (done) return;
   const int max_lds = (int)kLdsBytesPerCU;
   const void* fns[] = {
-      reinterpret_cast<const void*>(&score_kernel_rot<G, 4, false>),
-      reinterpret_cast<const void*>(&score_kernel_rot<G, 8, false>),
-      reinterpret_cast<const void*>(&score_kernel_rot<G, 16, false>),
-      reinterpret_cast<const void*>(&score_kernel_rot<G, 4, true>),
-      reinterpret_cast<const void*>(&score_kernel_rot<G, 8, true>),
-      reinterpret_cast<const void*>(&score_kernel_rot<G, 16, true>),
+      reinterpret_cast<const void*>(&score_kernel_rot<G, 4, false, false>),
+      reinterpret_cast<const void*>(&score_kernel_rot<G, 8, false, false>),
+      reinterpret_cast<const void*>(&score_kernel_rot<G, 16, false, false>),
+      reinterpret_cast<const void*>(&score_kernel_rot<G, 4, true, false>),
+      reinterpret_cast<const void*>(&score_kernel_rot<G, 8, true, false>),
+      reinterpret_cast<const void*>(&score_kernel_rot<G, 16, true, false>),
       reinterpret_cast<const void*>(&score_kernel_generic<G>)};
   for (const void* f : fns)
     (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+  if constexpr (G == 4) {
+    const void* rf[] = {reinterpret_cast<const void*>(&score_kernel_rot<4, 4, false, true>),
+                        reinterpret_cast<const void*>(&score_kernel_rot<4, 8, false, true>),
+                        reinterpret_cast<const void*>(&score_kernel_rot<4, 4, true, true>),
+                        reinterpret_cast<const void*>(&score_kernel_rot<4, 8, true, true>)};
+    for (const void* f : rf)
+      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+  }
   done = true;
 }
 
 template <int G, bool BUILD>
 void launch_score_rot(const ScoreArgs& a, int grid, size_t lds, hipStream_t stream) {
+  if constexpr (G == 4) {
+    if (score_region(G, a.P, a.L)) {
+      if (a.L == 32)
+        launch_kernel((score_kernel_rot<4, 8, BUILD, true>), dim3(grid), dim3(kScoreThreads), lds,
+                      stream, a);
+      else
+        launch_kernel((score_kernel_rot<4, 4, BUILD, true>), dim3(grid), dim3(kScoreThreads), lds,
+                      stream, a);
+      return;
+    }
+  }
   if (a.L == 32)
-    launch_kernel((score_kernel_rot<G, 8, BUILD>), dim3(grid), dim3(kScoreThreads), lds, stream, a);
+    launch_kernel((score_kernel_rot<G, 8, BUILD, false>), dim3(grid), dim3(kScoreThreads), lds,
+                  stream, a);
   else if (a.L == 64)
-    launch_kernel((score_kernel_rot<G, 16, BUILD>), dim3(grid), dim3(kScoreThreads), lds, stream, a);
+    launch_kernel((score_kernel_rot<G, 16, BUILD, false>), dim3(grid), dim3(kScoreThreads), lds,
+                  stream, a);
   else
-    launch_kernel((score_kernel_rot<G, 4, BUILD>), dim3(grid), dim3(kScoreThreads), lds, stream, a);
+    launch_kernel((score_kernel_rot<G, 4, BUILD, false>), dim3(grid), dim3(kScoreThreads), lds,
+                  stream, a);
 }
 
 template <int G>
@@ -922,6 +1092,29 @@ int score_pack(int L, int P, int G) {
   for (int gp = G; gp >= 1; gp >>= 1)
     if (G % gp == 0 && score_lds_bytes(L, P, gp, false) <= kLdsBytesPerCU) return gp;
   return 0;
+}
+
+namespace {
+// The region scorer addresses its LDS table absolutely: it needs the
+// kernels' dynamic LDS to start at address 0, i.e. no static LDS.
+bool region_kernels_have_no_static_lds() {
+  static const bool ok = [] {
+    const void* fns[] = {reinterpret_cast<const void*>(&score_kernel_rot<4, 4, false, true>),
+                         reinterpret_cast<const void*>(&score_kernel_rot<4, 8, false, true>),
+                         reinterpret_cast<const void*>(&score_kernel_rot<4, 4, true, true>),
+                         reinterpret_cast<const void*>(&score_kernel_rot<4, 8, true, true>)};
+    for (const void* f : fns) {
+      hipFuncAttributes attr{};
+      if (hipFuncGetAttributes(&attr, f) != hipSuccess || attr.sharedSizeBytes != 0) return false;
+    }
+    return true;
+  }();
+  return ok;
+}
+}  // namespace
+
+bool score_region(int G, int P, int L) {
+  return G == 4 && P == 8 && (L == 16 || L == 32) && region_kernels_have_no_static_lds();
 }
 
 bool score_rotated(const uint8_t* ids, int64_t stride, int L) {

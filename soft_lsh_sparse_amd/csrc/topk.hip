@@ -106,6 +106,7 @@ constexpr int kRefineCache = 16384;  // (u, index) pairs kept in LDS (128 KB)
 struct RefineShared {
   uint32_t scratch[2 * (kRefineThreads / 64 + 1) + 4];
   uint32_t tmax[kRefineThreads / 64];
+  uint32_t wmax[kRefineThreads / 64];  // per-wave maxima of the candidates
   uint32_t h[kHistBins];
   uint32_t off[kMaxSelectSubLists + 1];
   uint2 cache[kRefineCache];
@@ -163,12 +164,13 @@ __device__ void cache_candidates(RowLists& rl, uint2* cache, uint32_t total) {
 // above the threshold T and the first keys equal to T, and writes their
 // indices at positions given by block scans: o[0 .. kk) ascending.
 template <int NT, typename At>
+__device__ void emit_in_order(const At& at, uint32_t total, uint32_t kk, uint32_t T,
+                              uint32_t ties, RefineShared& sh, int32_t* o);
+
+template <int NT, typename At>
 __device__ void select_and_emit(const At& at, uint32_t total, uint32_t kk, int start_pass,
                                 uint32_t prefix, uint32_t need, uint32_t floor,
                                 RefineShared& sh, int32_t* o) {
-  // the in-order loops below keep kB entries per lane in flight
-  // (addresses clamped to the entries, results of the surplus ones unused)
-  constexpr int kB = 8;
   uint32_t* res = sh.scratch + NT / 64 + 1;
   for (int pass = start_pass; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
@@ -186,9 +188,63 @@ __device__ void select_and_emit(const At& at, uint32_t total, uint32_t kk, int s
     prefix = pass == 0 ? res[0] : (prefix << (pass == 2 ? 10 : 11)) | res[0];
     need -= res[1];
   }
-  const uint32_t T = prefix;
-  const uint32_t ties = need;  // keys equal to T still to take
+  // keys above T = prefix, and the first `need` keys equal to it
+  emit_in_order<NT>(at, total, kk, prefix, need, sh, o);
+}
 
+// The kk best entries among at(0 .. total) whose order keys lie in
+// [lo, hi] (entries below lo are never among them; at least kk reach lo),
+// emitted in entry order. Radix passes of up to 11 bits on x = u - lo,
+// from the top bit of hi - lo down: the digits spread over the range the
+// candidates actually span, so few keys share a histogram bin. A pass
+// stops the search early when the bin holding the kk-th key is taken whole.
+template <int NT, typename At>
+__device__ void select_range_and_emit(const At& at, uint32_t total, uint32_t kk, uint32_t lo,
+                                      uint32_t hi, RefineShared& sh, int32_t* o) {
+  uint32_t* res = sh.scratch + NT / 64 + 1;
+  int top = hi > lo ? 32 - __clz(hi - lo) : 0;  // bits of x still undecided
+  const int nbits = top;
+  uint32_t prefix = 0, need = kk;  // x >> top == prefix for the keys still in play
+  bool whole = false;
+  while (top > 0) {  // block-uniform
+    const int db = min(11, top), shift = top - db;
+    const uint32_t dmask = (1u << db) - 1u;
+    for (int i = threadIdx.x; i < kHistBins; i += NT) sh.h[i] = 0;
+    __syncthreads();
+    for (uint32_t p = threadIdx.x; p < total; p += NT) {
+      const uint32_t u = at(p).x;
+      if (u < lo) continue;
+      const uint32_t x = u - lo;
+      if (top < nbits && (x >> top) != prefix) continue;
+      atomicAdd(&sh.h[(x >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    find_threshold_bin<NT>(sh.h, need, sh.scratch, res);
+    const uint32_t bin = res[0], in_bin = sh.h[bin];
+    prefix = (prefix << db) | bin;
+    need -= res[1];
+    top = shift;
+    __syncthreads();  // every thread has read the bin before the next pass clears it
+    if (in_bin == need) {
+      whole = true;
+      break;
+    }
+  }
+  if (whole)  // every key from the bin's lowest up
+    emit_in_order<NT>(at, total, kk, lo + (prefix << top), 0xffffffffu, sh, o);
+  else        // top == 0: prefix is the kk-th key's x
+    emit_in_order<NT>(at, total, kk, lo + prefix, need, sh, o);
+}
+
+// Writes, in entry (= index) order, every key above T and the first `ties`
+// keys equal to T (all of them when ties is larger than their count):
+// o[0 .. kk) ascending.
+template <int NT, typename At>
+__device__ void emit_in_order(const At& at, uint32_t total, uint32_t kk, uint32_t T,
+                              uint32_t ties, RefineShared& sh, int32_t* o) {
+  // the in-order loops below keep kB entries per lane in flight
+  // (addresses clamped to the entries, results of the surplus ones unused)
+  constexpr int kB = 8;
   // final pass, in entry (= index) order: wave w takes a contiguous chunk
   // of entries, 64 per step. First every wave counts the keys above T and
   // equal to T in its chunk (ballots); then, from the counts of the waves
@@ -281,14 +337,13 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
 __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs a) {
   constexpr int NT = kRefineThreads;
   __shared__ RefineShared sh;
+  const int row = blockIdx.x;
   // the host never launches more sub-lists than the offsets hold; a row
   // that would have more is left alone rather than read out of bounds
   if (a.subs > kMaxSelectSubLists) return;
-  const int row = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t kk = (uint32_t)a.kk;
   int32_t* o = a.idx + (int64_t)row * a.kk;
-  uint32_t* res = sh.scratch + NT / 64 + 1;
   // The first round of candidate copies (below) is requested before the
   // sub-list lengths are known: each wave loads the first kSpec * 64
   // entries of its kRound sub-lists (clamped to the row, unused beyond a
@@ -315,7 +370,6 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
 #pragma unroll
   for (int q = 0; q < kPerMax; ++q) cn[q] = (q < per && s0 + q < a.subs) ? cnt[s0 + q] : 0u;
   uint32_t tmax = (int)threadIdx.x < a.segs ? a.thr[(int64_t)row * a.segs + threadIdx.x] : 0u;
-  for (int i = threadIdx.x; i < kHistBins; i += NT) sh.h[i] = 0u;
   uint32_t total;
   {
     uint32_t sum = 0;
@@ -336,17 +390,21 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
   tmax = 0;
   for (int w = 0; w < NT / 64; ++w) tmax = max(tmax, sh.tmax[w]);
 
-  // candidates into LDS (as far as they fit), counted into the first-digit
-  // histogram when they reach T: each wave copies whole sub-lists, eight of
+  // candidates into LDS (as far as they fit), counting those that reach T
+  // and the largest of them: each wave copies whole sub-lists, eight of
   // them per round, 64 entries of each per batch of loads
   RowLists rl{glob, sh.cache, 0u, sh.off, a.subs, a.sub_len, true};
+  uint32_t n_above_t = 0, umax_t = 0;  // this thread's
   {
     const uint32_t cached = min(total, (uint32_t)kRefineCache);
     // the score kernel stores (score bits, index): cached as (order key, index)
     auto take = [&](const uint2& s, uint32_t p) {
       const uint2 e = make_uint2(float_order_key(__uint_as_float(s.x)), s.y);
       if (p < cached) sh.cache[p] = e;
-      if (e.x >= tmax) atomicAdd(&sh.h[e.x >> 21], 1u);
+      if (e.x >= tmax) {
+        ++n_above_t;
+        umax_t = max(umax_t, e.x);
+      }
     };
     for (int s0 = wave; s0 < a.subs; s0 += kWaves * kRound) {  // wave-uniform
       const bool first = s0 == wave;
@@ -385,16 +443,32 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
           take(glob[(int64_t)sl * a.sub_len + i], o + i);
       }
     }
-    __syncthreads();
     rl.cached = cached;
   }
-  find_threshold_bin<NT>(sh.h, kk, sh.scratch, res);
-  const uint32_t b1 = res[0], above1 = res[1], n_above = res[2];
+  // the count and the largest key at or above T, over the block
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    n_above_t += (uint32_t)__shfl_xor((int)n_above_t, m, 64);
+    umax_t = max(umax_t, (uint32_t)__shfl_xor((int)umax_t, m, 64));
+  }
+  // (scratch is free since the offsets' scan; sh.tmax may still be read by
+  // a wave that has not left the threshold's maximum yet, hence wmax)
+  if (lane == 0) {
+    sh.scratch[wave] = n_above_t;
+    sh.wmax[wave] = umax_t;
+  }
+  __syncthreads();  // also completes the candidate copy
+  uint32_t n_above = 0, umax = 0;
+  for (int w = 0; w < NT / 64; ++w) {
+    n_above += sh.scratch[w];
+    umax = max(umax, sh.wmax[w]);
+  }
+  __syncthreads();  // scratch is reused below
   if (n_above >= kk) {
     if (total <= rl.cached)
-      select_and_emit<NT>(CacheAt{sh.cache}, total, kk, 1, b1, kk - above1, tmax, sh, o);
+      select_range_and_emit<NT>(CacheAt{sh.cache}, total, kk, tmax, umax, sh, o);
     else
-      select_and_emit<NT>(rl, total, kk, 1, b1, kk - above1, tmax, sh, o);
+      select_range_and_emit<NT>(rl, total, kk, tmax, umax, sh, o);
     return;
   }
 
@@ -416,7 +490,8 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
     const int r = a.rotated ? (int)(i & 15) : 0;
     float acc = 0.f;
     for (int t = 0; t < L; ++t) {
-      const int l = t + r < L ? t + r : t + r - L;
+      // the score kernel's order of additions
+      const int l = a.region ? (t & ~15) | ((t + r) & 15) : (t + r < L ? t + r : t + r - L);
       const int u = idh[i * L + l] & (nb - 1);
       const float p = lds_tab ? tabs[u * L + l] : tg[(int64_t)(u * L + l) * G];
       acc = t == 0 ? p : acc + p;

@@ -799,15 +799,15 @@ def test_decode_without_score_rows_selects_the_same(name):
         assert np.array_equal(idx_np[b, h], O.topk_indices(sc_np[b, h], w.k))
 
 
-@pytest.mark.parametrize("with_rows", [True, False])
-def test_decode_threshold_fallback_selects_from_full_rows(with_rows):
+@pytest.mark.parametrize("with_rows,Hq", [(True, 4), (False, 4), (False, 8)])
+def test_decode_threshold_fallback_selects_from_full_rows(with_rows, Hq):
     """Value norms vanish except on the sampled keys of KV head 0, so that head's
     rows see fewer than k keys reach the estimated threshold and are selected
     from fully scored rows; KV head 1 takes the candidate path. Ties among the
     zero scores go to the lower indices."""
-    w = W.custom_workload(B=1, Hq=4, Hkv=2, d=128, N=65536, dtype="bf16", L=32, P=8,
+    w = W.custom_workload(B=1, Hq=Hq, Hkv=2, d=128, N=65536, dtype="bf16", L=32, P=8,
                           tau=0.3, k=1024, lognormal_v=True, name="fallback")
-    log(f"decode threshold fallback with_rows={with_rows}")
+    log(f"decode threshold fallback with_rows={with_rows} Hq={Hq}")
     Q, K, V, R = W.make_decode_inputs(w, DEV, seed=11)
     ids, vn = S.hash_keys(K, V, R, w.L, w.P)
     pos = torch.from_numpy(_sample_positions(w.N)).to(DEV)
@@ -815,8 +815,8 @@ def test_decode_threshold_fallback_selects_from_full_rows(with_rows):
     keep = vn[0, 0, pos].clone()
     vn_mod[0, 0].zero_()
     vn_mod[0, 0, pos] = keep
-    idx = torch.empty((1, 4, w.kk), dtype=torch.int32, device=DEV)
-    sc = torch.empty((1, 4, w.N), dtype=torch.float32, device=DEV) if with_rows else None
+    idx = torch.empty((1, Hq, w.kk), dtype=torch.int32, device=DEV)
+    sc = torch.empty((1, Hq, w.N), dtype=torch.float32, device=DEV) if with_rows else None
     out, _, _ = S.decode(Q, K, V, R, ids, vn_mod, w.L, w.P, w.tau, w.k, idx_out=idx,
                          scores_out=sc)
     table = S.bucket_probs(Q, R, w.Hkv, w.L, w.P, w.tau)
@@ -826,13 +826,13 @@ def test_decode_threshold_fallback_selects_from_full_rows(with_rows):
         assert torch.equal(sc, sc_ref)
     s_np = sc_ref.cpu().numpy()
     idx_np = idx.cpu().numpy()
-    for h in range(4):
+    for h in range(Hq):
         assert np.array_equal(idx_np[0, h], O.topk_indices(s_np[0, h], w.k)), f"head {h}"
     # head 0's selection: only sampled keys score above zero
     assert np.isin(idx_np[0, 0], _sample_positions(w.N)).all()
     Q64 = f64(Q)
-    for h in (0, 3):
-        g = h // 2
+    for h in (0, Hq - 1):
+        g = h // w.G
         sel_t = idx[0, h].long()
         ref = O.subset_attention(Q64[:, h:h + 1], f64(K[0, g][sel_t])[None, None],
                                  f64(V[0, g][sel_t])[None, None],
