@@ -5,6 +5,10 @@ command that produced its input):
 
 * a kernel-trace summary (``rocprofv3 --kernel-trace --stats``): calls and
   average / min / max duration of every kernel of this library;
+* a counter summary: the mean per dispatch of several ``--pmc`` counters
+  (one run) for every kernel of this library, e.g. the LDS and VALU
+  instruction counts and LDS bank-conflict cycles of the score kernel, or
+  the MFMA counters of the hash kernel;
 * an HBM-traffic summary: the ``FETCH_SIZE`` and ``WRITE_SIZE`` counters
   (KiB per dispatch, one ``--pmc`` run each) of every kernel, each scaled by
   the factor that turns the same counter into the known byte count of a
@@ -18,6 +22,7 @@ changed since, so a stale counter reading is never reported as current.
 Usage::
 
     python -m soft_lsh_sparse_amd.profiling trace <stats.csv> <out.md> --command "..."
+    python -m soft_lsh_sparse_amd.profiling counters <pmc.csv> <out.md> --command "..."
     python -m soft_lsh_sparse_amd.profiling traffic --fetch <csv> --write <csv> \\
         --copy-fetch <csv> --copy-write <csv> --copy-bytes N --out <md> \\
         --command "..." --copy-command "..."
@@ -72,6 +77,15 @@ def short_name(full: str) -> str | None:
     return None
 
 
+def instance_name(full: str) -> str | None:
+    """short_name plus the template arguments of the instance, if any."""
+    n = short_name(full)
+    if n is None:
+        return None
+    m = re.search(r"::\w+(<[^()]*?>)?\(", full)
+    return n + (m.group(1) if m and m.group(1) else "")
+
+
 def canonical(name: str) -> str:
     """Decode-stage name used by the benchmark (score_kernel_rot and
     score_kernel_generic are both the score kernel)."""
@@ -96,12 +110,10 @@ def kernel_stats(stats_csv: str):
     out = []
     with open(stats_csv) as fh:
         for r in csv.DictReader(fh):
-            n = short_name(r["Name"])
+            n = instance_name(r["Name"])
             if n is None or n == COPY_KERNEL:
                 continue
-            m = re.search(r"::\w+(<[^()]*?>)?\(", r["Name"])
-            targs = m.group(1) if m and m.group(1) else ""
-            out.append((n + targs, int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+            out.append((n, int(r["Calls"]), float(r["AverageNs"]) / 1e3,
                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
     return out
 
@@ -117,6 +129,44 @@ def counter_means(pmc_csv: str, counter: str):
             if n is not None:
                 vals[n].append(float(r["Counter_Value"]))
     return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+
+
+def counter_table(pmc_csv: str):
+    """kernel instance (with its template arguments) -> {counter: mean value
+    per dispatch}, and dispatches per instance (the smallest count over its
+    counters)."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    with open(pmc_csv) as fh:
+        for r in csv.DictReader(fh):
+            n = instance_name(r["Kernel_Name"])
+            if n is None or n == COPY_KERNEL:
+                continue
+            vals[n][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    means = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in vals.items()}
+    counts = {k: min(len(v) for v in cs.values()) for k, cs in vals.items()}
+    return means, counts
+
+
+def write_counter_summary(pmc_csv: str, out_md: str, command: str, title: str,
+                          notes: str = "") -> dict:
+    means, counts = counter_table(pmc_csv)
+    counters = sorted({c for cs in means.values() for c in cs})
+    lines = [f"# {title}", "", "Command (from the repository root on the GPU host):", "",
+             "```", command, "```", "",
+             "Mean value per dispatch of each counter (summed over the whole device).", ""]
+    if notes:
+        lines += [notes, ""]
+    lines += ["| kernel | dispatches | " + " | ".join(counters) + " |",
+              "|---|---|" + "---|" * len(counters)]
+    for k in sorted(means):
+        row = [f"{means[k].get(c, float('nan')):.4g}" for c in counters]
+        lines.append(f"| `{k}` | {counts[k]} | " + " | ".join(row) + " |")
+    data = {"kernels": {k: {"dispatches": counts[k], **{c: round(v, 1) for c, v in means[k].items()}}
+                        for k in sorted(means)}}
+    lines += ["", "```json", json.dumps(data, indent=1), "```", ""]
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines))
+    return data
 
 
 def write_trace_summary(stats_csv: str, out_md: str, command: str, title: str) -> None:
@@ -203,6 +253,12 @@ def main():
     t.add_argument("out")
     t.add_argument("--command", required=True)
     t.add_argument("--title", default="Kernel trace")
+    n = sub.add_parser("counters")
+    n.add_argument("pmc_csv")
+    n.add_argument("out")
+    n.add_argument("--command", required=True)
+    n.add_argument("--title", default="Counters")
+    n.add_argument("--notes", default="")
     c = sub.add_parser("traffic")
     for a in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--out",
               "--command", "--copy-command"):
@@ -212,6 +268,8 @@ def main():
     args = ap.parse_args()
     if args.cmd == "trace":
         write_trace_summary(args.stats_csv, args.out, args.command, args.title)
+    elif args.cmd == "counters":
+        write_counter_summary(args.pmc_csv, args.out, args.command, args.title, args.notes)
     else:
         write_traffic_summary(args.fetch, args.write, args.copy_fetch, args.copy_write,
                               args.copy_bytes, args.out, args.command,

@@ -62,3 +62,35 @@ def test_short_names():
     assert profiling.canonical(profiling.short_name(SCORE)) == "score_kernel"
     assert profiling.short_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
     assert profiling.short_name("at::native::foo") is None
+
+
+def test_counter_summary_means_per_kernel(tmp_path):
+    path = tmp_path / "c.csv"
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=FIELDS)
+        w.writeheader()
+        for name, counter, value in [(SCORE, "SQ_INSTS_LDS", 10), (SCORE, "SQ_INSTS_LDS", 30),
+                                     (SCORE, "SQ_INSTS_VALU", 7), (SCORE, "SQ_INSTS_VALU", 9),
+                                     (ATTN, "SQ_INSTS_LDS", 4), ("other", "SQ_INSTS_LDS", 1)]:
+            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+    out = tmp_path / "c.md"
+    data = profiling.write_counter_summary(str(path), str(out), "cmd", "t")
+    assert data["kernels"]["score_kernel_rot<4, 8>"] == {"dispatches": 2, "SQ_INSTS_LDS": 20.0,
+                                                         "SQ_INSTS_VALU": 8.0}
+    assert data["kernels"]["sparse_attn_kernel<socket_lsh::BF16, 128, 64>"]["dispatches"] == 1
+    assert len(data["kernels"]) == 2
+    text = out.read_text()
+    assert "| `score_kernel_rot<4, 8>` | 2 |" in text
+
+
+def test_counter_summary_keeps_template_instances_apart(tmp_path):
+    path = tmp_path / "c.csv"
+    other = SCORE.replace("<4, 8>", "<4, 16>")
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=FIELDS)
+        w.writeheader()
+        for name, value in [(SCORE, 10), (SCORE, 30), (other, 100)]:
+            w.writerow({"Kernel_Name": name, "Counter_Name": "SQ_WAVES", "Counter_Value": value})
+    data = profiling.write_counter_summary(str(path), str(tmp_path / "c.md"), "cmd", "t")
+    assert data["kernels"]["score_kernel_rot<4, 8>"]["SQ_WAVES"] == 20.0
+    assert data["kernels"]["score_kernel_rot<4, 16>"]["SQ_WAVES"] == 100.0
