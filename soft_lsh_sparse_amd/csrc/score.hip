@@ -349,8 +349,11 @@ __device__ __forceinline__ double xor32_f64(double v) {
 //    from 1.0) and p(u) = (A[u & 7] * B[(u >> 3) & 7]) * C[u >> 6] rounded
 //    to float32.
 // The hyperplanes and the query rows are staged in the table's LDS
-// (direct-to-LDS loads, in flight with the caller's first id loads, issued
-// by before()); the weights go to w as [bit][l][j] (2 * 8 * L * G doubles).
+// (direct-to-LDS loads); before() is called once they have landed (the
+// barrier that waits for them waits for every load the wave has issued)
+// and requests the caller's first ids and norms, which then arrive while
+// the table is being built. The weights go to w as [bit][l][j]
+// (2 * 8 * L * G doubles).
 // The entries are written by 8 threads per (table, row) pair p = l * G + j:
 // thread c takes buckets 32c .. 32c + 31, for which it needs the 8 products
 // of group A, 4 of group B and 1 of group C. Contains __syncthreads().
@@ -385,8 +388,8 @@ __device__ __forceinline__ void build_table(float* tab, double* w, const ScoreAr
             (__attribute__((address_space(3))) void*)(stage + (size_t)i0 * 16), 16, 0, 0);
     }
   }
-  before();
   __syncthreads();
+  before();
 
   // units of (R_ROWS rows, 8 tables), 8 * parts lanes each
   const int lanes_per_unit = 8 * parts;
