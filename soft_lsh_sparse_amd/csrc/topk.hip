@@ -72,6 +72,7 @@ struct RowLists {
   int subs;
   int64_t sub_len;
   bool score_bits;        // glob holds (score bits, index): map to order keys
+  bool raw_cache;         // so does the LDS copy
   __device__ __forceinline__ uint2 from_memory(uint32_t p) const {
     int lo = 0, hi = subs - 1;  // last sub-list with off[s] <= p
     while (lo < hi) {
@@ -83,7 +84,10 @@ struct RowLists {
     return e;
   }
   __device__ __forceinline__ uint2 operator()(uint32_t p) const {
-    return p < cached ? cache[p] : from_memory(p);
+    if (p >= cached) return from_memory(p);
+    uint2 e = cache[p];
+    if (raw_cache) e.x = float_order_key(__uint_as_float(e.x));
+    return e;
   }
 };
 
@@ -106,7 +110,7 @@ constexpr int kRefineCache = 16384;  // (u, index) pairs kept in LDS (128 KB)
 struct RefineShared {
   uint32_t scratch[2 * (kRefineThreads / 64 + 1) + 4];
   uint32_t tmax[kRefineThreads / 64];
-  uint32_t wmax[kRefineThreads / 64];  // per-wave maxima of the candidates
+  uint32_t wmax[kRefineThreads / 64];  // per-wave largest order keys of the candidates
   uint32_t h[kHistBins];
   uint32_t off[kMaxSelectSubLists + 1];
   uint2 cache[kRefineCache];
@@ -156,6 +160,11 @@ __device__ void cache_candidates(RowLists& rl, uint2* cache, uint32_t total) {
   rl.cached = cached;
 }
 
+// Entries each thread requests before it uses any, in the histogram passes
+// below (entries read from memory then overlap instead of each waiting for
+// the one before it).
+constexpr int kPassBatch = 8;
+
 // Radix passes start_pass..2 (digits of 11, 11 and 10 bits) over the
 // entries at(0 .. total) of one row with order key >= floor, which hold
 // every key that can be among the kk best: `prefix` is the part of the
@@ -178,10 +187,16 @@ __device__ void select_and_emit(const At& at, uint32_t total, uint32_t kk, int s
     const uint32_t dmask = pass == 2 ? 1023u : 2047u;
     for (int i = threadIdx.x; i < kHistBins; i += NT) sh.h[i] = 0;
     __syncthreads();
-    for (uint32_t p = threadIdx.x; p < total; p += NT) {
-      const uint32_t u = at(p).x;
-      if (u >= floor && (pass == 0 || (u >> pshift) == prefix))
-        atomicAdd(&sh.h[(u >> shift) & dmask], 1u);
+    for (uint32_t base = threadIdx.x; base < total; base += kPassBatch * NT) {
+      uint32_t uu[kPassBatch];
+#pragma unroll
+      for (int i = 0; i < kPassBatch; ++i) uu[i] = at(min(base + i * NT, total - 1)).x;
+#pragma unroll
+      for (int i = 0; i < kPassBatch; ++i) {
+        const uint32_t u = uu[i];
+        if (base + i * NT < total && u >= floor && (pass == 0 || (u >> pshift) == prefix))
+          atomicAdd(&sh.h[(u >> shift) & dmask], 1u);
+      }
     }
     __syncthreads();
     find_threshold_bin<NT>(sh.h, need, sh.scratch, res);
@@ -193,33 +208,42 @@ __device__ void select_and_emit(const At& at, uint32_t total, uint32_t kk, int s
 }
 
 // The kk best entries among at(0 .. total) whose order keys lie in
-// [lo, hi] (entries below lo are never among them; at least kk reach lo),
-// emitted in entry order. Radix passes of up to 11 bits on x = u - lo,
-// from the top bit of hi - lo down: the digits spread over the range the
+// [lo, hi] (entries below lo are never among them; none is above hi),
+// emitted in entry order; false (nothing written) when fewer than kk
+// entries reach lo. Radix passes of up to 11 bits on x = u - lo, from the
+// top bit of hi - lo down: the digits spread over the range the
 // candidates actually span, so few keys share a histogram bin. A pass
 // stops the search early when the bin holding the kk-th key is taken whole.
 template <int NT, typename At>
-__device__ void select_range_and_emit(const At& at, uint32_t total, uint32_t kk, uint32_t lo,
+__device__ bool select_range_and_emit(const At& at, uint32_t total, uint32_t kk, uint32_t lo,
                                       uint32_t hi, RefineShared& sh, int32_t* o) {
   uint32_t* res = sh.scratch + NT / 64 + 1;
   int top = hi > lo ? 32 - __clz(hi - lo) : 0;  // bits of x still undecided
   const int nbits = top;
   uint32_t prefix = 0, need = kk;  // x >> top == prefix for the keys still in play
-  bool whole = false;
-  while (top > 0) {  // block-uniform
+  bool whole = false, first = true;
+  do {  // block-uniform; at least one pass, which counts the entries reaching lo
     const int db = min(11, top), shift = top - db;
     const uint32_t dmask = (1u << db) - 1u;
     for (int i = threadIdx.x; i < kHistBins; i += NT) sh.h[i] = 0;
     __syncthreads();
-    for (uint32_t p = threadIdx.x; p < total; p += NT) {
-      const uint32_t u = at(p).x;
-      if (u < lo) continue;
-      const uint32_t x = u - lo;
-      if (top < nbits && (x >> top) != prefix) continue;
-      atomicAdd(&sh.h[(x >> shift) & dmask], 1u);
+    for (uint32_t base = threadIdx.x; base < total; base += kPassBatch * NT) {
+      uint32_t uu[kPassBatch];
+#pragma unroll
+      for (int i = 0; i < kPassBatch; ++i) uu[i] = at(min(base + i * NT, total - 1)).x;
+#pragma unroll
+      for (int i = 0; i < kPassBatch; ++i) {
+        const uint32_t u = uu[i];
+        if (base + i * NT >= total || u < lo) continue;
+        const uint32_t x = u - lo;
+        if (top < nbits && (x >> top) != prefix) continue;
+        atomicAdd(&sh.h[(x >> shift) & dmask], 1u);
+      }
     }
     __syncthreads();
     find_threshold_bin<NT>(sh.h, need, sh.scratch, res);
+    if (first && res[2] < kk) return false;
+    first = false;
     const uint32_t bin = res[0], in_bin = sh.h[bin];
     prefix = (prefix << db) | bin;
     need -= res[1];
@@ -229,11 +253,12 @@ __device__ void select_range_and_emit(const At& at, uint32_t total, uint32_t kk,
       whole = true;
       break;
     }
-  }
+  } while (top > 0);
   if (whole)  // every key from the bin's lowest up
     emit_in_order<NT>(at, total, kk, lo + (prefix << top), 0xffffffffu, sh, o);
   else        // top == 0: prefix is the kk-th key's x
     emit_in_order<NT>(at, total, kk, lo + prefix, need, sh, o);
+  return true;
 }
 
 // Writes, in entry (= index) order, every key above T and the first `ties`
@@ -330,10 +355,15 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
 // own threshold; with T the largest of those thresholds, every key of the
 // row with order key >= T is a candidate. When at least kk of them are, the
 // kk best keys are among them: the candidates are copied into LDS as far as
-// they fit and go through all three radix passes with floor T. Otherwise
-// the block scores the whole row itself, with the score kernel's order of
+// they fit and go through the radix passes with floor T. Otherwise the
+// block scores the whole row itself, with the score kernel's order of
 // additions (hence the same float32 values), into the row's score buffer,
 // and selects from that.
+//
+// Two dependent rounds of memory requests: the sub-list lengths and the
+// block thresholds, then the candidates themselves, copied by
+// direct-to-LDS loads (one dword per lane, so any entry offset will do)
+// straight to their place in the concatenation.
 __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs a) {
   constexpr int NT = kRefineThreads;
   __shared__ RefineShared sh;
@@ -342,26 +372,14 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
   // that would have more is left alone rather than read out of bounds
   if (a.subs > kMaxSelectSubLists) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kWaves = NT / 64;
   const uint32_t kk = (uint32_t)a.kk;
   int32_t* o = a.idx + (int64_t)row * a.kk;
-  // The first round of candidate copies (below) is requested before the
-  // sub-list lengths are known: each wave loads the first kSpec * 64
-  // entries of its kRound sub-lists (clamped to the row, unused beyond a
-  // sub-list's length), in flight with the length and threshold loads.
-  constexpr int kWaves = NT / 64, kRound = 8, kSpec = 1;
   const uint2* glob = a.lists + (int64_t)row * a.n;
-  uint2 spec[kRound][kSpec];
-#pragma unroll
-  for (int k = 0; k < kRound; ++k) {
-    const int sl = min(wave + k * kWaves, a.subs - 1);
-#pragma unroll
-    for (int t = 0; t < kSpec; ++t)
-      spec[k][t] = glob[min((int64_t)sl * a.sub_len + t * 64 + lane, a.n - 1)];
-  }
   // T (the largest block threshold of the row) and the sub-list lengths:
-  // straight-line loads (segs <= subs / 16 <= NT, at most kMaxSelectSubLists
-  // / NT lengths per thread, a run of consecutive sub-lists), all in flight
-  // with the copies above
+  // straight-line loads (segs <= subs / 16 <= NT, at most
+  // kMaxSelectSubLists / NT lengths per thread, a run of consecutive
+  // sub-lists)
   constexpr int kPerMax = kMaxSelectSubLists / NT;
   const int per = (a.subs + NT - 1) / NT;
   const int s0 = min(a.subs, (int)threadIdx.x * per);
@@ -388,88 +406,78 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
   if (lane == 0) sh.tmax[wave] = tmax;
   __syncthreads();
   tmax = 0;
-  for (int w = 0; w < NT / 64; ++w) tmax = max(tmax, sh.tmax[w]);
+  for (int w = 0; w < kWaves; ++w) tmax = max(tmax, sh.tmax[w]);
+  // (no key of a finite score has an order key below 1)
+  const uint32_t floor = max(tmax, 1u);
 
-  // candidates into LDS (as far as they fit), counting those that reach T
-  // and the largest of them: each wave copies whole sub-lists, eight of
-  // them per round, 64 entries of each per batch of loads
-  RowLists rl{glob, sh.cache, 0u, sh.off, a.subs, a.sub_len, true};
-  uint32_t n_above_t = 0, umax_t = 0;  // this thread's
+  // The first `cached` entries of the concatenation into LDS: wave w
+  // copies the run of sub-lists [w * spw, (w + 1) * spw), 32 entries (64
+  // dwords) per load, lane i taking dword i. The run's offsets are read
+  // once (one per lane) and handed to the issuing loop through lane reads.
+  const uint32_t cached = min(total, (uint32_t)kRefineCache);
+  unsigned char* cache_bytes = reinterpret_cast<unsigned char*>(sh.cache);
   {
-    const uint32_t cached = min(total, (uint32_t)kRefineCache);
-    // the score kernel stores (score bits, index): cached as (order key, index)
-    auto take = [&](const uint2& s, uint32_t p) {
-      const uint2 e = make_uint2(float_order_key(__uint_as_float(s.x)), s.y);
-      if (p < cached) sh.cache[p] = e;
-      if (e.x >= tmax) {
-        ++n_above_t;
-        umax_t = max(umax_t, e.x);
-      }
-    };
-    for (int s0 = wave; s0 < a.subs; s0 += kWaves * kRound) {  // wave-uniform
-      const bool first = s0 == wave;
-      uint2 e[kRound][kSpec];
-#pragma unroll
-      for (int k = 0; k < kRound; ++k) {
-        const int sl = s0 + k * kWaves;
-#pragma unroll
-        for (int t = 0; t < kSpec; ++t) {
-          if (first) {
-            e[k][t] = spec[k][t];
-          } else if (sl < a.subs && (uint32_t)(t * 64 + lane) < sh.off[sl + 1] - sh.off[sl]) {
-            e[k][t] = glob[(int64_t)sl * a.sub_len + t * 64 + lane];
-          }
+    const int spw = (a.subs + kWaves - 1) / kWaves;
+    const int sb = min(a.subs, wave * spw), se = min(a.subs, sb + spw);
+    for (int k0 = sb; k0 < se; k0 += 63) {  // wave-uniform
+      // lane i: the offset of sub-list k0 + i (i <= 63: its end too)
+      const uint32_t offv = sh.off[min(k0 + lane, a.subs)];
+      const int nk = min(63, se - k0);
+      for (int k = 0; k < nk; ++k) {  // wave-uniform
+        const uint32_t o0 = (uint32_t)__builtin_amdgcn_readlane((int)offv, k);
+        if (o0 >= cached) break;  // offsets ascend
+        const uint32_t o1 = min((uint32_t)__builtin_amdgcn_readlane((int)offv, k + 1), cached);
+        const uint32_t dws = 2u * (o1 - o0);
+        const uint32_t* src =
+            reinterpret_cast<const uint32_t*>(glob + (int64_t)(k0 + k) * a.sub_len);
+        for (uint32_t d0 = 0; d0 < dws; d0 += 64) {  // wave-uniform
+          if (d0 + lane < dws)
+            __builtin_amdgcn_global_load_lds(
+                src + d0 + lane,
+                (__attribute__((address_space(3))) void*)(cache_bytes +
+                                                          ((size_t)o0 * 2 + d0) * 4),
+                4, 0, 0);
         }
       }
-      // the next 64 entries of every sub-list that has them, all requested
-      // before any is used
-      uint2 x[kRound];
-#pragma unroll
-      for (int k = 0; k < kRound; ++k) {
-        const int sl = s0 + k * kWaves;
-        if (sl < a.subs && (uint32_t)(kSpec * 64 + lane) < sh.off[sl + 1] - sh.off[sl])
-          x[k] = glob[(int64_t)sl * a.sub_len + kSpec * 64 + lane];
-      }
-#pragma unroll
-      for (int k = 0; k < kRound; ++k) {
-        const int sl = s0 + k * kWaves;
-        if (sl >= a.subs) continue;
-        const uint32_t o = sh.off[sl], c = sh.off[sl + 1] - o;
-#pragma unroll
-        for (int t = 0; t < kSpec; ++t)
-          if ((uint32_t)(t * 64 + lane) < c) take(e[k][t], o + t * 64 + lane);
-        if ((uint32_t)(kSpec * 64 + lane) < c) take(x[k], o + kSpec * 64 + lane);
-        for (uint32_t i = (kSpec + 1) * 64 + lane; i < c; i += 64)
-          take(glob[(int64_t)sl * a.sub_len + i], o + i);
-      }
     }
-    rl.cached = cached;
   }
-  // the count and the largest key at or above T, over the block
+  __syncthreads();  // the copies have landed
+  // score bits to order keys in place, and the largest order key of the
+  // row (the entries beyond the LDS copy read from memory)
+  const RowLists rl{glob, sh.cache, cached, sh.off, a.subs, a.sub_len, true, false};
+  uint32_t umax = 0;  // this thread's
+  for (uint32_t base = threadIdx.x; base < cached; base += kPassBatch * NT) {
+    uint32_t uu[kPassBatch];
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    n_above_t += (uint32_t)__shfl_xor((int)n_above_t, m, 64);
-    umax_t = max(umax_t, (uint32_t)__shfl_xor((int)umax_t, m, 64));
+    for (int i = 0; i < kPassBatch; ++i)
+      uu[i] = base + i * NT < cached ? sh.cache[base + i * NT].x : 0u;
+#pragma unroll
+    for (int i = 0; i < kPassBatch; ++i) {
+      if (base + i * NT >= cached) break;
+      const uint32_t u = float_order_key(__uint_as_float(uu[i]));
+      sh.cache[base + i * NT].x = u;
+      umax = max(umax, u);
+    }
   }
-  // (scratch is free since the offsets' scan; sh.tmax may still be read by
-  // a wave that has not left the threshold's maximum yet, hence wmax)
-  if (lane == 0) {
-    sh.scratch[wave] = n_above_t;
-    sh.wmax[wave] = umax_t;
+  for (uint32_t base = cached + threadIdx.x; base < total; base += kPassBatch * NT) {
+    uint32_t uu[kPassBatch];
+#pragma unroll
+    for (int i = 0; i < kPassBatch; ++i) uu[i] = rl.from_memory(min(base + i * NT, total - 1)).x;
+#pragma unroll
+    for (int i = 0; i < kPassBatch; ++i) umax = max(umax, uu[i]);
   }
-  __syncthreads();  // also completes the candidate copy
-  uint32_t n_above = 0, umax = 0;
-  for (int w = 0; w < NT / 64; ++w) {
-    n_above += sh.scratch[w];
-    umax = max(umax, sh.wmax[w]);
-  }
-  __syncthreads();  // scratch is reused below
-  if (n_above >= kk) {
-    if (total <= rl.cached)
-      select_range_and_emit<NT>(CacheAt{sh.cache}, total, kk, tmax, umax, sh, o);
-    else
-      select_range_and_emit<NT>(rl, total, kk, tmax, umax, sh, o);
-    return;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) umax = max(umax, (uint32_t)__shfl_xor((int)umax, m, 64));
+  if (lane == 0) sh.wmax[wave] = umax;
+  __syncthreads();  // also completes the conversion
+  umax = 0;
+  for (int w = 0; w < kWaves; ++w) umax = max(umax, sh.wmax[w]);
+  if (umax >= floor) {
+    const bool done =
+        total <= cached
+            ? select_range_and_emit<NT>(CacheAt{sh.cache}, total, kk, floor, umax, sh, o)
+            : select_range_and_emit<NT>(rl, total, kk, floor, umax, sh, o);
+    if (done) return;
   }
 
   const int G = a.Hq / a.Hkv;
@@ -486,17 +494,44 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
   float* srow = a.scores + (int64_t)row * a.n;
   const uint8_t* idh = a.ids + hg * a.stride * L;
   const float* vnh = a.vnorm + hg * a.stride;
-  for (int64_t i = threadIdx.x; i < a.n; i += NT) {
-    const int r = a.rotated ? (int)(i & 15) : 0;
-    float acc = 0.f;
-    for (int t = 0; t < L; ++t) {
-      // the score kernel's order of additions
-      const int l = a.region ? (t & ~15) | ((t + r) & 15) : (t + r < L ? t + r : t + r - L);
-      const int u = idh[i * L + l] & (nb - 1);
-      const float p = lds_tab ? tabs[u * L + l] : tg[(int64_t)(u * L + l) * G];
-      acc = t == 0 ? p : acc + p;
+  // kKeys keys per thread at a time, their ids kTabs tables at a time: all
+  // kKeys * kTabs id bytes are requested before any is looked up
+  constexpr int kKeys = 4, kTabs = 8;
+  for (int64_t i0 = threadIdx.x; i0 < a.n; i0 += (int64_t)NT * kKeys) {
+    int64_t ik[kKeys];
+    int rk[kKeys];
+    float acc[kKeys], vk[kKeys];
+#pragma unroll
+    for (int k = 0; k < kKeys; ++k) {
+      ik[k] = min(i0 + (int64_t)k * NT, a.n - 1);
+      rk[k] = a.rotated ? (int)(ik[k] & 15) : 0;
+      acc[k] = 0.f;
+      vk[k] = vnh[ik[k]];
     }
-    srow[i] = vnh[i] * acc;
+    for (int t0 = 0; t0 < L; t0 += kTabs) {
+      int lk[kKeys][kTabs], uk[kKeys][kTabs];
+#pragma unroll
+      for (int k = 0; k < kKeys; ++k)
+#pragma unroll
+        for (int q = 0; q < kTabs; ++q) {
+          // the score kernel's order of additions
+          const int t = min(t0 + q, L - 1), r = rk[k];
+          lk[k][q] = a.region ? (t & ~15) | ((t + r) & 15) : (t + r < L ? t + r : t + r - L);
+          uk[k][q] = idh[ik[k] * L + lk[k][q]];
+        }
+#pragma unroll
+      for (int k = 0; k < kKeys; ++k)
+#pragma unroll
+        for (int q = 0; q < kTabs; ++q) {
+          if (t0 + q >= L) break;
+          const int u = uk[k][q] & (nb - 1), l = lk[k][q];
+          const float p = lds_tab ? tabs[u * L + l] : tg[(int64_t)(u * L + l) * G];
+          acc[k] = t0 + q == 0 ? p : acc[k] + p;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kKeys; ++k)
+      if (i0 + (int64_t)k * NT < a.n) srow[ik[k]] = vk[k] * acc[k];
   }
   __syncthreads();
   select_and_emit<NT>(ScoreRowAt{srow}, (uint32_t)a.n, kk, 0, 0u, kk, 0u, sh, o);
