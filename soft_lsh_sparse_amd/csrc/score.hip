@@ -1130,8 +1130,16 @@ ScoreGeom plan_score(int bhkv, int64_t n_keys, int L, int P, int G) {
   // the same geometry whether or not the block builds its table
   const bool could_build = P == 8 && (L == 16 || L == 32 || L == 64);
   const size_t lds = score_lds_bytes(L, P, G, could_build);
-  // blocks resident per CU as limited by the 160 KB of LDS
-  const int per_cu = (int)std::max<size_t>(1, std::min<size_t>(2, kLdsBytesPerCU / lds));
+  // blocks resident per CU as limited by the 160 KB of LDS and by the
+  // registers: two 1024-thread blocks need <= 64 VGPRs per lane, which
+  // only the kernels for one query head per block with L <= 32 and the
+  // table-copying kernels with L = 16 and G <= 4 use (the others take
+  // 72-128); a second block that cannot be resident would run in a
+  // second round
+  const bool regs_fit_two = (G == 1 && L <= 32) || (L <= 16 && G <= 4 && P != 8);
+  const int per_cu = regs_fit_two
+                         ? (int)std::max<size_t>(1, std::min<size_t>(2, kLdsBytesPerCU / lds))
+                         : 1;
   const int64_t target = (int64_t)256 * per_cu;
   constexpr int64_t kSegUnit = (int64_t)kScoreWaves * kWaveStep;
   int64_t segs = (target + bhkv - 1) / bhkv;
