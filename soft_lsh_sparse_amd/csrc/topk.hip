@@ -63,7 +63,11 @@ __global__ __launch_bounds__(kFilterThreads) void topk_hist_kernel(
 }
 
 // Element p (0 <= p < total) of the concatenated sub-lists of a row: from
-// the LDS copy when the row's candidates fit there, else from memory.
+// the LDS copy when the row's candidates fit there, else from memory. Each
+// thread holds its own copy, whose cursor remembers the sub-list of the
+// last position read from memory: the loops below read ascending positions
+// per lane, so finding the next one's sub-list takes a step or two forward
+// (a binary search only when a loop starts over).
 struct RowLists {
   const uint2* glob;      // row's list area (sub-list s at s * sub_len)
   const uint2* cache;     // LDS copy of the first `cached` entries (order keys)
@@ -73,13 +77,22 @@ struct RowLists {
   int64_t sub_len;
   bool score_bits;        // glob holds (score bits, index): map to order keys
   bool raw_cache;         // so does the LDS copy
-  __device__ __forceinline__ uint2 from_memory(uint32_t p) const {
-    int lo = 0, hi = subs - 1;  // last sub-list with off[s] <= p
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (off[mid] <= p) lo = mid; else hi = mid - 1;
+  mutable int cur = -1;   // sub-list of the last position read from memory
+  // element index in glob of position p (moves the cursor)
+  __device__ __forceinline__ int64_t locate(uint32_t p) const {
+    if (cur < 0 || p < off[cur]) {
+      int lo = 0, hi = subs - 1;  // last sub-list with off[s] <= p
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= p) lo = mid; else hi = mid - 1;
+      }
+      cur = lo;
     }
-    uint2 e = glob[(int64_t)lo * sub_len + (p - off[lo])];
+    while (cur + 1 < subs && off[cur + 1] <= p) ++cur;
+    return (int64_t)cur * sub_len + (p - off[cur]);
+  }
+  __device__ __forceinline__ uint2 from_memory(uint32_t p) const {
+    uint2 e = glob[locate(p)];
     if (score_bits) e.x = float_order_key(__uint_as_float(e.x));
     return e;
   }
@@ -165,6 +178,64 @@ __device__ void cache_candidates(RowLists& rl, uint2* cache, uint32_t total) {
 // the one before it).
 constexpr int kPassBatch = 8;
 
+// Wave w's share [c0, c1) of positions 0 .. total: contiguous runs of a
+// multiple of 64 positions, in wave order (lane i reads positions c0 + i,
+// c0 + 64 + i, ...: ascending per lane, consecutive across lanes).
+struct WaveRun {
+  uint32_t c0, c1;
+  __device__ __forceinline__ WaveRun(uint32_t total, int nt) {
+    const uint32_t nw = (uint32_t)nt / 64;
+    const uint32_t chunk = (total + nw * 64 - 1) / (nw * 64) * 64;
+    c0 = min(total, (threadIdx.x >> 6) * chunk);
+    c1 = min(total, c0 + chunk);
+  }
+};
+
+// Entries base + 64 i + lane (clamped to last), i < K, of any accessor.
+template <int K, typename At>
+__device__ __forceinline__ void read_run(const At& at, uint32_t base, uint32_t last,
+                                         uint2 (&e)[K]) {
+  const uint32_t lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < K; ++i) e[i] = at(min(base + i * 64 + lane, last));
+}
+
+// at[I ..] = element indices of positions base + 64 i + lane (clamped to
+// last), written out one by one (constant indices: registers, although
+// each step holds loops)
+template <int I, int K>
+__device__ __forceinline__ void locate_run(const RowLists& rl, uint32_t base, uint32_t last,
+                                           int64_t (&at)[K]) {
+  if constexpr (I < K) {
+    at[I] = rl.locate(min(base + I * 64 + (threadIdx.x & 63), last));
+    locate_run<I + 1, K>(rl, base, last, at);
+  }
+}
+
+// The same for a row read partly from memory: when the whole run lies past
+// the LDS copy (wave-uniform), every lane first finds the K addresses
+// (cursor steps, LDS reads and branches) and only then issues the K loads,
+// back to back, so that no branch separates them (at a branch the compiler
+// would wait for every load in flight).
+template <int K>
+__device__ __forceinline__ void read_run(const RowLists& rl, uint32_t base, uint32_t last,
+                                         uint2 (&e)[K]) {
+  const uint32_t lane = threadIdx.x & 63;
+  if (base < rl.cached) {  // wave-uniform: the run starts in the LDS copy
+#pragma unroll
+    for (int i = 0; i < K; ++i) e[i] = rl(min(base + i * 64 + lane, last));
+    return;
+  }
+  int64_t at[K];
+  locate_run<0, K>(rl, base, last, at);
+#pragma unroll
+  for (int i = 0; i < K; ++i) e[i] = rl.glob[at[i]];
+  if (rl.score_bits) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) e[i].x = float_order_key(__uint_as_float(e[i].x));
+  }
+}
+
 // Radix passes start_pass..2 (digits of 11, 11 and 10 bits) over the
 // entries at(0 .. total) of one row with order key >= floor, which hold
 // every key that can be among the kk best: `prefix` is the part of the
@@ -173,28 +244,34 @@ constexpr int kPassBatch = 8;
 // above the threshold T and the first keys equal to T, and writes their
 // indices at positions given by block scans: o[0 .. kk) ascending.
 template <int NT, typename At>
-__device__ void emit_in_order(const At& at, uint32_t total, uint32_t kk, uint32_t T,
+__device__ void emit_in_order(At at, uint32_t total, uint32_t kk, uint32_t T,
                               uint32_t ties, RefineShared& sh, int32_t* o);
 
 template <int NT, typename At>
-__device__ void select_and_emit(const At& at, uint32_t total, uint32_t kk, int start_pass,
+__device__ void select_and_emit(At at, uint32_t total, uint32_t kk, int start_pass,
                                 uint32_t prefix, uint32_t need, uint32_t floor,
                                 RefineShared& sh, int32_t* o) {
   uint32_t* res = sh.scratch + NT / 64 + 1;
+  const int lane = threadIdx.x & 63;
+  const WaveRun wr(total, NT);
   for (int pass = start_pass; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const int pshift = pass == 1 ? 21 : 10;
     const uint32_t dmask = pass == 2 ? 1023u : 2047u;
     for (int i = threadIdx.x; i < kHistBins; i += NT) sh.h[i] = 0;
     __syncthreads();
-    for (uint32_t base = threadIdx.x; base < total; base += kPassBatch * NT) {
+    for (uint32_t base = wr.c0; base < wr.c1; base += kPassBatch * 64) {  // wave-uniform
       uint32_t uu[kPassBatch];
+      {
+        uint2 ee[kPassBatch];
+        read_run(at, base, wr.c1 - 1, ee);
 #pragma unroll
-      for (int i = 0; i < kPassBatch; ++i) uu[i] = at(min(base + i * NT, total - 1)).x;
+        for (int i = 0; i < kPassBatch; ++i) uu[i] = ee[i].x;
+      }
 #pragma unroll
       for (int i = 0; i < kPassBatch; ++i) {
         const uint32_t u = uu[i];
-        if (base + i * NT < total && u >= floor && (pass == 0 || (u >> pshift) == prefix))
+        if (base + i * 64 + lane < wr.c1 && u >= floor && (pass == 0 || (u >> pshift) == prefix))
           atomicAdd(&sh.h[(u >> shift) & dmask], 1u);
       }
     }
@@ -215,9 +292,11 @@ __device__ void select_and_emit(const At& at, uint32_t total, uint32_t kk, int s
 // candidates actually span, so few keys share a histogram bin. A pass
 // stops the search early when the bin holding the kk-th key is taken whole.
 template <int NT, typename At>
-__device__ bool select_range_and_emit(const At& at, uint32_t total, uint32_t kk, uint32_t lo,
+__device__ bool select_range_and_emit(At at, uint32_t total, uint32_t kk, uint32_t lo,
                                       uint32_t hi, RefineShared& sh, int32_t* o) {
   uint32_t* res = sh.scratch + NT / 64 + 1;
+  const int lane = threadIdx.x & 63;
+  const WaveRun wr(total, NT);
   int top = hi > lo ? 32 - __clz(hi - lo) : 0;  // bits of x still undecided
   const int nbits = top;
   uint32_t prefix = 0, need = kk;  // x >> top == prefix for the keys still in play
@@ -227,14 +306,18 @@ __device__ bool select_range_and_emit(const At& at, uint32_t total, uint32_t kk,
     const uint32_t dmask = (1u << db) - 1u;
     for (int i = threadIdx.x; i < kHistBins; i += NT) sh.h[i] = 0;
     __syncthreads();
-    for (uint32_t base = threadIdx.x; base < total; base += kPassBatch * NT) {
+    for (uint32_t base = wr.c0; base < wr.c1; base += kPassBatch * 64) {  // wave-uniform
       uint32_t uu[kPassBatch];
+      {
+        uint2 ee[kPassBatch];
+        read_run(at, base, wr.c1 - 1, ee);
 #pragma unroll
-      for (int i = 0; i < kPassBatch; ++i) uu[i] = at(min(base + i * NT, total - 1)).x;
+        for (int i = 0; i < kPassBatch; ++i) uu[i] = ee[i].x;
+      }
 #pragma unroll
       for (int i = 0; i < kPassBatch; ++i) {
         const uint32_t u = uu[i];
-        if (base + i * NT >= total || u < lo) continue;
+        if (base + i * 64 + lane >= wr.c1 || u < lo) continue;
         const uint32_t x = u - lo;
         if (top < nbits && (x >> top) != prefix) continue;
         atomicAdd(&sh.h[(x >> shift) & dmask], 1u);
@@ -265,7 +348,7 @@ __device__ bool select_range_and_emit(const At& at, uint32_t total, uint32_t kk,
 // keys equal to T (all of them when ties is larger than their count):
 // o[0 .. kk) ascending.
 template <int NT, typename At>
-__device__ void emit_in_order(const At& at, uint32_t total, uint32_t kk, uint32_t T,
+__device__ void emit_in_order(At at, uint32_t total, uint32_t kk, uint32_t T,
                               uint32_t ties, RefineShared& sh, int32_t* o) {
   // the in-order loops below keep kB entries per lane in flight
   // (addresses clamped to the entries, results of the surplus ones unused)
@@ -283,8 +366,12 @@ __device__ void emit_in_order(const At& at, uint32_t total, uint32_t kk, uint32_
   uint32_t n_gt = 0, n_eq = 0;  // wave-uniform
   for (uint32_t base = c0; base < c1; base += kB * 64) {  // wave-uniform
     uint32_t u[kB];
+    {
+      uint2 ee[kB];
+      read_run(at, base, total - 1, ee);
 #pragma unroll
-    for (int i = 0; i < kB; ++i) u[i] = at(min(base + i * 64 + lane, total - 1)).x;
+      for (int i = 0; i < kB; ++i) u[i] = ee[i].x;
+    }
 #pragma unroll
     for (int i = 0; i < kB; ++i) {
       const bool valid = base + i * 64 + lane < c1;
@@ -307,8 +394,7 @@ __device__ void emit_in_order(const At& at, uint32_t total, uint32_t kk, uint32_
   uint32_t eq_seen = before_eq;
   for (uint32_t base = c0; base < c1; base += kB * 64) {  // wave-uniform
     uint2 e[kB];
-#pragma unroll
-    for (int i = 0; i < kB; ++i) e[i] = at(min(base + i * 64 + lane, total - 1));
+    read_run(at, base, total - 1, e);
 #pragma unroll
     for (int i = 0; i < kB; ++i) {
       const bool valid = base + i * 64 + lane < c1;
@@ -459,12 +545,15 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
       umax = max(umax, u);
     }
   }
-  for (uint32_t base = cached + threadIdx.x; base < total; base += kPassBatch * NT) {
-    uint32_t uu[kPassBatch];
+  {
+    // the entries past the LDS copy, wave-contiguous runs of positions
+    const WaveRun mr(total - cached, NT);
+    for (uint32_t base = cached + mr.c0; base < cached + mr.c1; base += kPassBatch * 64) {
+      uint2 ee[kPassBatch];
+      read_run(rl, base, cached + mr.c1 - 1, ee);
 #pragma unroll
-    for (int i = 0; i < kPassBatch; ++i) uu[i] = rl.from_memory(min(base + i * NT, total - 1)).x;
-#pragma unroll
-    for (int i = 0; i < kPassBatch; ++i) umax = max(umax, uu[i]);
+      for (int i = 0; i < kPassBatch; ++i) umax = max(umax, ee[i].x);
+    }
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) umax = max(umax, (uint32_t)__shfl_xor((int)umax, m, 64));
