@@ -23,6 +23,7 @@
 #include "soft_prob.hpp"
 
 #include <algorithm>
+#include <numeric>
 
 namespace socket_lsh {
 namespace {
@@ -107,10 +108,15 @@ hipError_t launch_bucket_probs(const void* Q, const void* R, bool bf16, int B,
   a.P = P;
   a.two_over_tau = 2.0 / (double)tau;
   a.table = table;
-  // about 512 blocks over the chip, at most 8 tables per block (bounds LDS)
+  // about 512 blocks over the chip, at most 8 tables per block (bounds LDS);
+  // a block's first column and column count are multiples of 8 where the
+  // tables allow (whole 16-byte loads of the hyperplane rows: the
+  // projections then take all their loads at once)
   const int bhkv = B * Hkv;
   int tpb = (int)(((int64_t)L * bhkv + 511) / 512);
   tpb = std::max(1, std::min(tpb, std::min(L, 8)));
+  const int m = 8 / std::gcd(P, 8);  // tables per 8 columns
+  if (m <= std::min(L, 8)) tpb = std::min((tpb + m - 1) / m * m, std::min(L, 8) / m * m);
   a.tables_per_block = tpb;
   const int G = Hq / Hkv;
   const size_t lds = (table_zw_doubles(G, tpb, P) + table_gp_doubles(G, tpb, P)) * sizeof(double);
