@@ -11,7 +11,7 @@
 // bf16 path (the large prefill), three launches:
 //
 //  1. prep: R [d, C] is transposed to R^T [rows, d] (zero rows past C) in the
-//     workspace, and the fix-up counter is cleared.
+//     workspace, and written again in the main kernel's fragment order.
 //  2. main: one block of 8 waves per CU (two per SIMD). R^T of all the
 //     hyperplane columns sits in LDS in the order the MFMA A operand reads
 //     it (fragment (column tile, k-step) = 1 KB, conflict-free 16-byte
@@ -27,21 +27,21 @@
 //     that a lane's 16 bits are 16 consecutive hyperplanes and one exchange
 //     between the two lane halves yields a 32-bit word of 32 consecutive
 //     sign bits. With P = 8 that word is four id bytes, stored directly.
-//  3. fix-up: a sign is certified when |y| exceeds the worst-case float32
+//  3. settle: a sign is certified when |y| exceeds the worst-case float32
 //     summation error 2*d*2^-24*|k|*max|r| (plus a floor for flushed
 //     denormals). Uncertain projections (about 1.5e-4 of them for random
 //     data) are appended by the main kernel to a per-wave list in the
 //     workspace (one entry per key and 16-column group, with a mask; slots
-//     from ballot prefix counts) with their float32 sign written; the fix-up
-//     kernel recomputes each one from
-//     the bf16 inputs (float64 sum of exact products, certified, with a
-//     double-double fallback) and sets or clears that one bit with an atomic
-//     AND/OR. A wave with an overflowing list (or any wave with an uncertain
-//     sign when id rows are not whole 4-byte words) has all its tiles
-//     re-hashed exactly by a fourth kernel (float64 / double-double, one
-//     thread per key and table), which exits at once when nothing
-//     overflowed. Either way the bucket ids are those of the exact dot
-//     products.
+//     from ballot prefix counts) with their float32 sign written; the
+//     blocks of a settling kernel recompute each one from the bf16 inputs
+//     (float64 sum of exact products, certified, with a double-double
+//     fallback) and set or clear that one bit with an atomic AND/OR. A
+//     wave with an overflowing list (or any wave with an uncertain sign
+//     when id rows are not whole 4-byte words) has all its tiles re-hashed
+//     exactly by the other blocks of the same launch (float64 /
+//     double-double, one thread per key and table; its list is left
+//     alone), which go on at once when nothing overflowed. Either way the
+//     bucket ids are those of the exact dot products.
 //
 // f32 path: one thread per key, float64 dot products with the same
 // certification and a serial double-double fallback. bf16 inputs of at most
@@ -477,20 +477,23 @@ __global__ __launch_bounds__(256) void hash_prep_kernel(const uint16_t* __restri
 constexpr int kFixBlocksPerPart = 16;
 
 template <int D>
-__global__ __launch_bounds__(256) void hash_fixup_kernel(
-    const uint16_t* __restrict__ K, const uint16_t* __restrict__ RT, int C, int L, int P,
-    uint8_t* __restrict__ ids, const unsigned long long* __restrict__ list,
+__device__ __forceinline__ void hash_fixup_block(
+    int bid, const uint16_t* __restrict__ K, const uint16_t* __restrict__ RT, int C, int L,
+    int P, uint8_t* __restrict__ ids, const unsigned long long* __restrict__ list,
     const uint32_t* __restrict__ count, uint32_t cap) {
   constexpr int kPer = D / 16;  // dims per lane: 8 (one 16-byte load) or 4
-  const int blk = blockIdx.x / kFixBlocksPerPart;
-  const int j = blockIdx.x % kFixBlocksPerPart;
+  const int blk = bid / kFixBlocksPerPart;
+  const int j = bid % kFixBlocksPerPart;
   const int sub = threadIdx.x & 15;
   const uint32_t groups = blockDim.x / 16;
   // the block's regions back to back as one index range
   uint32_t n[kHashWaves], total = 0;
 #pragma unroll
   for (int w = 0; w < kHashWaves; ++w) {
-    n[w] = min(count[blk * kHashWaves + w], cap);
+    // a wave whose list overflowed has all its tiles hashed again exactly
+    // (below), so its entries are left alone
+    const uint32_t c = count[blk * kHashWaves + w];
+    n[w] = c > cap ? 0u : c;
     total += n[w];
   }
   for (uint32_t e = j * groups + threadIdx.x / 16; e < total; e += kFixBlocksPerPart * groups) {
@@ -565,14 +568,15 @@ __global__ __launch_bounds__(256) void hash_fixup_kernel(
 // rewrites the id byte. Each block checks 256 tiles at a time (owner: the
 // wave that hashed the tile) and goes on at once when none needs it.
 template <int D>
-__global__ __launch_bounds__(256) void hash_redo_kernel(
-    const uint16_t* __restrict__ K, const uint16_t* __restrict__ R, int64_t n_keys,
-    int64_t stride, int tph, int n_tiles, int parts, int L, int P, uint8_t* __restrict__ ids,
-    const uint32_t* __restrict__ count, const int* __restrict__ owner, uint32_t cap) {
+__device__ __forceinline__ void hash_redo_block(
+    int bid, int nblocks, const uint16_t* __restrict__ K, const uint16_t* __restrict__ R,
+    int64_t n_keys, int64_t stride, int tph, int n_tiles, int parts, int L, int P,
+    uint8_t* __restrict__ ids, const uint32_t* __restrict__ count, const int* __restrict__ owner,
+    uint32_t cap) {
   __shared__ int list[256];
   __shared__ int nlist;
   const int C = L * P;
-  for (int64_t base = (int64_t)blockIdx.x * 256; base < n_tiles; base += (int64_t)gridDim.x * 256) {
+  for (int64_t base = (int64_t)bid * 256; base < n_tiles; base += (int64_t)nblocks * 256) {
     const int64_t t = base + threadIdx.x;
     // (an owner outside the waves of the main kernel cannot occur; it is
     // not used as an index then)
@@ -618,6 +622,24 @@ __global__ __launch_bounds__(256) void hash_redo_kernel(
     }
     __syncthreads();
   }
+}
+
+// The fix-up and the exact re-hash in one launch: blocks 0 .. fix_blocks-1
+// settle the listed signs, the next redo_blocks check the tiles for waves
+// whose list overflowed (disjoint rows: a tile belongs to one wave).
+template <int D>
+__global__ __launch_bounds__(256) void hash_settle_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ R,
+    const uint16_t* __restrict__ RT, int64_t n_keys, int64_t stride, int tph, int n_tiles,
+    int parts, int L, int P, uint8_t* __restrict__ ids,
+    const unsigned long long* __restrict__ list, const uint32_t* __restrict__ count,
+    const int* __restrict__ owner, uint32_t cap, int fix_blocks, int redo_blocks) {
+  const int bid = (int)blockIdx.x;  // block-uniform roles
+  if (bid < fix_blocks)
+    hash_fixup_block<D>(bid, K, RT, L * P, L, P, ids, list, count, cap);
+  else
+    hash_redo_block<D>(bid - fix_blocks, redo_blocks, K, R, n_keys, stride, tph, n_tiles, parts,
+                       L, P, ids, count, owner, cap);
 }
 
 __device__ __forceinline__ float load_elem(const float* p, int64_t i) { return p[i]; }
@@ -849,23 +871,17 @@ hipError_t launch_hash_keys_bf16(const uint16_t* K, const uint16_t* V,
     launch_main_d<128>(a, blocks, word_ids, stream);
   else
     launch_main_d<64>(a, blocks, word_ids, stream);
-  if (a.fix_cap != 0) {
-    const dim3 fgrid(blocks * kFixBlocksPerPart);
-    if (d == 128)
-      launch_kernel(hash_fixup_kernel<128>, fgrid, dim3(256), 0, stream, K, w.rt, C, L, P,
-                    ids, w.list, w.count, a.fix_cap);
-    else
-      launch_kernel(hash_fixup_kernel<64>, fgrid, dim3(256), 0, stream, K, w.rt, C, L, P,
-                    ids, w.list, w.count, a.fix_cap);
-  }
+  // listed signs (none with a capacity of 0) and overflowed waves, one launch
+  const int fix_blocks = a.fix_cap != 0 ? blocks * kFixBlocksPerPart : 0;
+  const dim3 sgrid(fix_blocks + kMaxHashBlocks);
   if (d == 128)
-    launch_kernel(hash_redo_kernel<128>, dim3(kMaxHashBlocks), dim3(256), 0, stream, K, R,
-                  n_keys, stride, a.tph, a.n_tiles, blocks * kHashWaves, L, P, ids, w.count,
-                  w.owner, a.fix_cap);
+    launch_kernel(hash_settle_kernel<128>, sgrid, dim3(256), 0, stream, K, R, w.rt, n_keys, stride,
+                  a.tph, a.n_tiles, blocks * kHashWaves, L, P, ids, w.list, w.count, w.owner,
+                  a.fix_cap, fix_blocks, kMaxHashBlocks);
   else
-    launch_kernel(hash_redo_kernel<64>, dim3(kMaxHashBlocks), dim3(256), 0, stream, K, R,
-                  n_keys, stride, a.tph, a.n_tiles, blocks * kHashWaves, L, P, ids, w.count,
-                  w.owner, a.fix_cap);
+    launch_kernel(hash_settle_kernel<64>, sgrid, dim3(256), 0, stream, K, R, w.rt, n_keys, stride,
+                  a.tph, a.n_tiles, blocks * kHashWaves, L, P, ids, w.list, w.count, w.owner,
+                  a.fix_cap, fix_blocks, kMaxHashBlocks);
   return hipGetLastError();
 }
 

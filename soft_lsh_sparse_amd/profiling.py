@@ -46,8 +46,7 @@ KERNEL_SOURCES = {
     "hash_keys_bf16_kernel": ["hash_keys.hip"],
     "hash_keys_f32_kernel": ["hash_keys.hip"],
     "hash_prep_kernel": ["hash_keys.hip"],
-    "hash_fixup_kernel": ["hash_keys.hip"],
-    "hash_redo_kernel": ["hash_keys.hip"],
+    "hash_settle_kernel": ["hash_keys.hip"],
     "bucket_probs_kernel": ["bucket_probs.hip", "soft_prob.hpp"],
     "score_kernel_rot": ["score.hip", "radix.hpp"],
     "score_kernel_generic": ["score.hip", "radix.hpp"],

@@ -402,6 +402,8 @@ def test_hard_scores_are_value_norm_weighted_collision_counts():
     (1, 4, 1, 128, 37, "bf16"),         # part of one batch
     (2, 8, 2, 128, 2500, "bf16"),       # several chunks and a ragged tail
     (1, 8, 1, 64, 1500, "bf16"),        # 8 heads per KV head
+    (1, 2, 1, 128, 3333, "bf16"),       # 2 heads per KV head, four chunks, ragged
+    (1, 4, 4, 64, 2049, "bf16"),        # one head per KV head, one key past two chunks
     (1, 2, 1, 64, 777, "f32"),
     (1, 3, 3, 128, 4096, "f32"),        # one head per KV head, whole chunks
 ])
