@@ -102,6 +102,7 @@ def kernel_bytes(w, names):
     return {
         "bucket_probs_kernel": rows * w.d * e + w.d * w.C * e + table,
         "score_kernel": keys * w.L + keys * 4 + table_in,
+        "topk_gather_kernel": 0,  # moves candidates between two kernels only
         "topk_select_kernel": rows * kk * 4,
         "iota_rows_kernel": rows * kk * 4,
         "sparse_attn_kernel": rows * kk * (2 * w.d * e + 4) + rows * w.d * e + partial,

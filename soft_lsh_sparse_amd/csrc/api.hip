@@ -112,15 +112,16 @@ HeadPack head_pack(int32_t Hq, int32_t Hkv, int32_t L, int32_t P) {
   } while (0)
 
 struct DecodeLayout {
-  size_t table_off, scores_off, idx_off, thr_off, cnt_off, list_off, attn_off, total;
+  size_t table_off, scores_off, idx_off, thr_off, cnt_off, list_off, bmax_off, attn_off, total;
   HeadPack pack;
   ScoreGeom score;
   AttnPlan attn;
 };
 
 // Workspace of one decode call: the probability tables, full score rows
-// (written only for rows that need them), selected indices, block
-// thresholds, candidate sub-list lengths and lists, attention partials.
+// (written only for rows that need them; with large kk the rows' gathered
+// candidates first), selected indices, block thresholds, candidate sub-list
+// lengths and lists, the gather blocks' largest keys, attention partials.
 DecodeLayout decode_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
                            int64_t n_keys, int32_t L, int32_t P, int64_t k) {
   DecodeLayout lay{};
@@ -142,6 +143,8 @@ DecodeLayout decode_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
   off = align256(off + (select ? (size_t)rows * lay.score.subs * sizeof(uint32_t) : 0));
   lay.list_off = off;
   off = align256(off + (select ? (size_t)rows * n_keys * 8 : 0));
+  lay.bmax_off = off;
+  off = align256(off + (select ? (size_t)rows * select_gather_blocks(lay.score.subs, kk) * 4 : 0));
   lay.attn = plan_attn(B, Hq, Hkv, d, kk);
   lay.attn_off = off;
   off = align256(off + lay.attn.partial_bytes);
@@ -527,6 +530,8 @@ socket_status decode_impl(const void* Q, const void* K, const void* V,
     sa.rotated = score_rotated(ids, head_stride_rows, L) ? 1 : 0;
     sa.region = sa.rotated && score_region(sa.Hq / sa.Hkv, P, L) ? 1 : 0;
     sa.scores = rowbuf;
+    sa.spill = reinterpret_cast<uint2*>(ws + lay.scores_off);
+    sa.bmax = reinterpret_cast<uint32_t*>(ws + lay.bmax_off);
     err = launch_topk_select(sa, rows, s);
     if (err != hipSuccess) return from_hip(err, "socket_decode: topk");
   } else {
@@ -656,6 +661,8 @@ socket_status decode_group_impl(const void* Q, const void* K, const void* V, con
     sa.rotated = score_rotated(ids, head_stride_rows, L) ? 1 : 0;
     sa.region = sa.rotated && score_region(sa.Hq / sa.Hkv, P, L) ? 1 : 0;
     sa.scores = rowbuf;
+    sa.spill = reinterpret_cast<uint2*>(ws + lay.head.scores_off);
+    sa.bmax = reinterpret_cast<uint32_t*>(ws + lay.head.bmax_off);
     err = launch_topk_select(sa, rows, s);
     if (err != hipSuccess) return from_hip(err, "group-shared decode: topk");
   } else {
@@ -797,11 +804,13 @@ int32_t socket_decode_kernels(const uint8_t* ids, socket_dtype dtype, int32_t B,
   const bool build = score_builds_table(dtype == SOCKET_DTYPE_BF16, d, ids, head_stride_rows,
                                         L, P, head_pack(Hq, Hkv, L, P).gp);
   // the launch sequence of decode_impl
-  const char* seq[6];
+  const char* seq[7];
   int n = 0;
   if (k < n_keys) {
     if (!build) seq[n++] = "bucket_probs_kernel";
     seq[n++] = "score_kernel";
+    if (select_gather_blocks(decode_layout(B, Hq, Hkv, d, n_keys, L, P, k).score.subs, k) > 0)
+      seq[n++] = "topk_gather_kernel";
     seq[n++] = "topk_select_kernel";
   } else {
     if (with_scores) {

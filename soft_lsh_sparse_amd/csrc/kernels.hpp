@@ -171,7 +171,17 @@ struct SelectArgs {
   int rotated;                // score_rotated(ids, stride, L)
   int region;                 // rotated and score_region(Hq / Hkv, P, L)
   float* scores;              // [rows][n] row buffers
+  // Rows with many candidates (large kk): a gather kernel first copies each
+  // row's candidates, as order keys in index order, into one contiguous run
+  // inside the row's region of `spill` ([rows][n] float32 words, 16-byte
+  // aligned; never the caller's score rows), with the largest order key of
+  // each gather block in `bmax` [rows][select_gather_blocks(subs, kk)].
+  // Null spill: no gather.
+  uint2* spill;
+  uint32_t* bmax;
 };
+// Gather blocks per row the selection launches for these sizes (0: none).
+int select_gather_blocks(int subs, int64_t kk);
 hipError_t launch_topk_select(const SelectArgs& a, int rows, hipStream_t stream);
 
 // ------------------------------------------------------- sparse attention

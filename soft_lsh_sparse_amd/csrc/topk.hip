@@ -102,12 +102,18 @@ struct RowLists {
     if (raw_cache) e.x = float_order_key(__uint_as_float(e.x));
     return e;
   }
+  // positions below split() are in LDS; keys / entries requested per lane
+  // at a time past it
+  __device__ __forceinline__ uint32_t split() const { return cached; }
+  static constexpr int kMemKeys = 8, kMemEntries = 8;
 };
 
 // Entry p of a row whose candidates are all in LDS.
 struct CacheAt {
   const uint2* cache;
   __device__ __forceinline__ uint2 operator()(uint32_t p) const { return cache[p]; }
+  __device__ __forceinline__ uint32_t split() const { return 0xffffffffu; }
+  static constexpr int kMemKeys = 8, kMemEntries = 8;
 };
 
 // Entry p of a full score row: (order key, p).
@@ -116,6 +122,8 @@ struct ScoreRowAt {
   __device__ __forceinline__ uint2 operator()(uint32_t p) const {
     return make_uint2(float_order_key(s[p]), p);
   }
+  __device__ __forceinline__ uint32_t split() const { return 0u; }
+  static constexpr int kMemKeys = 8, kMemEntries = 8;
 };
 
 constexpr int kRefineCache = 16384;  // (u, index) pairs kept in LDS (128 KB)
@@ -126,7 +134,7 @@ struct RefineShared {
   uint32_t wmax[kRefineThreads / 64];  // per-wave largest order keys of the candidates
   uint32_t h[kHistBins];
   uint32_t off[kMaxSelectSubLists + 1];
-  uint2 cache[kRefineCache];
+  alignas(16) uint2 cache[kRefineCache];  // 16-byte direct-to-LDS copies
 };
 
 // Offsets of the row's sub-lists in their concatenation, from their lengths
@@ -221,6 +229,15 @@ template <int K>
 __device__ __forceinline__ void read_run(const RowLists& rl, uint32_t base, uint32_t last,
                                          uint2 (&e)[K]) {
   const uint32_t lane = threadIdx.x & 63;
+  if (last < rl.cached) {  // wave-uniform: the whole run is in the LDS copy
+#pragma unroll
+    for (int i = 0; i < K; ++i) e[i] = rl.cache[min(base + i * 64 + lane, last)];
+    if (rl.raw_cache) {
+#pragma unroll
+      for (int i = 0; i < K; ++i) e[i].x = float_order_key(__uint_as_float(e[i].x));
+    }
+    return;
+  }
   if (base < rl.cached) {  // wave-uniform: the run starts in the LDS copy
 #pragma unroll
     for (int i = 0; i < K; ++i) e[i] = rl(min(base + i * 64 + lane, last));
@@ -236,6 +253,110 @@ __device__ __forceinline__ void read_run(const RowLists& rl, uint32_t base, uint
   }
 }
 
+// Entry p of a row whose candidates were gathered into one contiguous run
+// of (order key, index) pairs: from the LDS copy of its first `cached`
+// entries, else from the run in memory.
+struct SpillAt {
+  const uint2* cache;
+  uint32_t cached;
+  const uint2* glob;
+  __device__ __forceinline__ uint2 operator()(uint32_t p) const {
+    return p < cached ? cache[p] : glob[p];
+  }
+  __device__ __forceinline__ uint32_t split() const { return cached; }
+  // plain addresses: deep batches (one round of requests per pass at 22
+  // memory entries per lane)
+  static constexpr int kMemKeys = 24, kMemEntries = 16;
+};
+
+// Runs that lie wholly past the LDS copy load straight from the gathered
+// run (consecutive addresses across the lanes, no branch between loads).
+template <int K>
+__device__ __forceinline__ void read_run(const SpillAt& at, uint32_t base, uint32_t last,
+                                         uint2 (&e)[K]) {
+  const uint32_t lane = threadIdx.x & 63;
+  if (base >= at.cached) {  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < K; ++i) e[i] = at.glob[min(base + i * 64 + lane, last)];
+    return;
+  }
+  if (last < at.cached) {  // wave-uniform: the whole run is in LDS
+#pragma unroll
+    for (int i = 0; i < K; ++i) e[i] = at.cache[min(base + i * 64 + lane, last)];
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < K; ++i) e[i] = at(min(base + i * 64 + lane, last));
+}
+
+// Order keys only (the histogram passes and the emit's counts).
+template <int K, typename At>
+__device__ __forceinline__ void read_keys(const At& at, uint32_t base, uint32_t last,
+                                          uint32_t (&u)[K]) {
+  uint2 e[K];
+  read_run(at, base, last, e);
+#pragma unroll
+  for (int i = 0; i < K; ++i) u[i] = e[i].x;
+}
+
+template <int K>
+__device__ __forceinline__ void read_keys(const SpillAt& at, uint32_t base, uint32_t last,
+                                          uint32_t (&u)[K]) {
+  const uint32_t lane = threadIdx.x & 63;
+  if (base >= at.cached) {  // wave-uniform: one dword of each entry
+    const uint32_t* kw = reinterpret_cast<const uint32_t*>(at.glob);
+#pragma unroll
+    for (int i = 0; i < K; ++i) u[i] = kw[2 * (size_t)min(base + i * 64 + lane, last)];
+    return;
+  }
+  if (last < at.cached) {  // wave-uniform: the whole run is in LDS
+#pragma unroll
+    for (int i = 0; i < K; ++i) u[i] = at.cache[min(base + i * 64 + lane, last)].x;
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < K; ++i) u[i] = at(min(base + i * 64 + lane, last)).x;
+}
+
+// f(u, valid) for the order keys of positions [c0, c1), K per lane at a
+// time (lane i: c0 + i, c0 + 64 + i, ...; valid is false for the padding
+// of the last step).
+template <int K, typename At, typename F>
+__device__ __forceinline__ void for_keys(At at, uint32_t c0, uint32_t c1, F& f) {
+  const uint32_t lane = threadIdx.x & 63;
+  for (uint32_t base = c0; base < c1; base += K * 64) {  // wave-uniform
+    uint32_t u[K];
+    read_keys(at, base, c1 - 1, u);
+#pragma unroll
+    for (int i = 0; i < K; ++i) f(u[i], base + i * 64 + lane < c1);
+  }
+}
+
+// f(u, valid) for the order key of every position in [0, total), in no
+// particular order: each wave takes an equal contiguous share of the
+// positions in LDS (below at.split()) and of those read from memory, so
+// that every wave has memory requests in flight.
+template <int NT, typename At, typename F>
+__device__ __forceinline__ void for_all_keys(At at, uint32_t total, F&& f) {
+  const uint32_t mid = min(at.split(), total);
+  const WaveRun r0(mid, NT), r1(total - mid, NT);
+  for_keys<kPassBatch>(at, r0.c0, r0.c1, f);
+  for_keys<At::kMemKeys>(at, mid + r1.c0, mid + r1.c1, f);
+}
+
+// Row r's gather region: uint2 entries [start, start + cap) inside the
+// bytes of float32 row r of an [rows][n] buffer, the start rounded up to 16
+// bytes (so that each row's region lies within its own score row).
+struct SpillRow {
+  int64_t start;
+  uint32_t cap;
+};
+__device__ __forceinline__ SpillRow spill_row(int64_t n, int row) {
+  const int64_t w0 = (int64_t)row * n;  // float32 words
+  const int64_t start = (w0 + 3) / 4 * 2, end = (w0 + n) / 2;
+  return SpillRow{start, (uint32_t)(end > start ? end - start : 0)};
+}
+
 // Radix passes start_pass..2 (digits of 11, 11 and 10 bits) over the
 // entries at(0 .. total) of one row with order key >= floor, which hold
 // every key that can be among the kk best: `prefix` is the part of the
@@ -244,37 +365,24 @@ __device__ __forceinline__ void read_run(const RowLists& rl, uint32_t base, uint
 // above the threshold T and the first keys equal to T, and writes their
 // indices at positions given by block scans: o[0 .. kk) ascending.
 template <int NT, typename At>
-__device__ void emit_in_order(At at, uint32_t total, uint32_t kk, uint32_t T,
-                              uint32_t ties, RefineShared& sh, int32_t* o);
+__device__ __forceinline__ void emit_in_order(At at, uint32_t total, uint32_t kk, uint32_t T,
+                                              uint32_t ties, RefineShared& sh, int32_t* o);
 
 template <int NT, typename At>
-__device__ void select_and_emit(At at, uint32_t total, uint32_t kk, int start_pass,
+__device__ __forceinline__ void select_and_emit(At at, uint32_t total, uint32_t kk, int start_pass,
                                 uint32_t prefix, uint32_t need, uint32_t floor,
                                 RefineShared& sh, int32_t* o) {
   uint32_t* res = sh.scratch + NT / 64 + 1;
-  const int lane = threadIdx.x & 63;
-  const WaveRun wr(total, NT);
   for (int pass = start_pass; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const int pshift = pass == 1 ? 21 : 10;
     const uint32_t dmask = pass == 2 ? 1023u : 2047u;
     for (int i = threadIdx.x; i < kHistBins; i += NT) sh.h[i] = 0;
     __syncthreads();
-    for (uint32_t base = wr.c0; base < wr.c1; base += kPassBatch * 64) {  // wave-uniform
-      uint32_t uu[kPassBatch];
-      {
-        uint2 ee[kPassBatch];
-        read_run(at, base, wr.c1 - 1, ee);
-#pragma unroll
-        for (int i = 0; i < kPassBatch; ++i) uu[i] = ee[i].x;
-      }
-#pragma unroll
-      for (int i = 0; i < kPassBatch; ++i) {
-        const uint32_t u = uu[i];
-        if (base + i * 64 + lane < wr.c1 && u >= floor && (pass == 0 || (u >> pshift) == prefix))
-          atomicAdd(&sh.h[(u >> shift) & dmask], 1u);
-      }
-    }
+    for_all_keys<NT>(at, total, [&](uint32_t u, bool valid) {
+      if (valid && u >= floor && (pass == 0 || (u >> pshift) == prefix))
+        atomicAdd(&sh.h[(u >> shift) & dmask], 1u);
+    });
     __syncthreads();
     find_threshold_bin<NT>(sh.h, need, sh.scratch, res);
     prefix = pass == 0 ? res[0] : (prefix << (pass == 2 ? 10 : 11)) | res[0];
@@ -292,11 +400,9 @@ __device__ void select_and_emit(At at, uint32_t total, uint32_t kk, int start_pa
 // candidates actually span, so few keys share a histogram bin. A pass
 // stops the search early when the bin holding the kk-th key is taken whole.
 template <int NT, typename At>
-__device__ bool select_range_and_emit(At at, uint32_t total, uint32_t kk, uint32_t lo,
+__device__ __forceinline__ bool select_range_and_emit(At at, uint32_t total, uint32_t kk, uint32_t lo,
                                       uint32_t hi, RefineShared& sh, int32_t* o) {
   uint32_t* res = sh.scratch + NT / 64 + 1;
-  const int lane = threadIdx.x & 63;
-  const WaveRun wr(total, NT);
   int top = hi > lo ? 32 - __clz(hi - lo) : 0;  // bits of x still undecided
   const int nbits = top;
   uint32_t prefix = 0, need = kk;  // x >> top == prefix for the keys still in play
@@ -306,23 +412,12 @@ __device__ bool select_range_and_emit(At at, uint32_t total, uint32_t kk, uint32
     const uint32_t dmask = (1u << db) - 1u;
     for (int i = threadIdx.x; i < kHistBins; i += NT) sh.h[i] = 0;
     __syncthreads();
-    for (uint32_t base = wr.c0; base < wr.c1; base += kPassBatch * 64) {  // wave-uniform
-      uint32_t uu[kPassBatch];
-      {
-        uint2 ee[kPassBatch];
-        read_run(at, base, wr.c1 - 1, ee);
-#pragma unroll
-        for (int i = 0; i < kPassBatch; ++i) uu[i] = ee[i].x;
-      }
-#pragma unroll
-      for (int i = 0; i < kPassBatch; ++i) {
-        const uint32_t u = uu[i];
-        if (base + i * 64 + lane >= wr.c1 || u < lo) continue;
-        const uint32_t x = u - lo;
-        if (top < nbits && (x >> top) != prefix) continue;
-        atomicAdd(&sh.h[(x >> shift) & dmask], 1u);
-      }
-    }
+    for_all_keys<NT>(at, total, [&](uint32_t u, bool valid) {
+      if (!valid || u < lo) return;
+      const uint32_t x = u - lo;
+      if (top < nbits && (x >> top) != prefix) return;
+      atomicAdd(&sh.h[(x >> shift) & dmask], 1u);
+    });
     __syncthreads();
     find_threshold_bin<NT>(sh.h, need, sh.scratch, res);
     if (first && res[2] < kk) return false;
@@ -337,66 +432,26 @@ __device__ bool select_range_and_emit(At at, uint32_t total, uint32_t kk, uint32
       break;
     }
   } while (top > 0);
-  if (whole)  // every key from the bin's lowest up
-    emit_in_order<NT>(at, total, kk, lo + (prefix << top), 0xffffffffu, sh, o);
-  else        // top == 0: prefix is the kk-th key's x
-    emit_in_order<NT>(at, total, kk, lo + prefix, need, sh, o);
+  // whole: every key from the bin's lowest up; else top == 0 and prefix is
+  // the kk-th key's x
+  emit_in_order<NT>(at, total, kk, lo + (prefix << top), whole ? 0xffffffffu : need, sh, o);
   return true;
 }
 
-// Writes, in entry (= index) order, every key above T and the first `ties`
-// keys equal to T (all of them when ties is larger than their count):
-// o[0 .. kk) ascending.
-template <int NT, typename At>
-__device__ void emit_in_order(At at, uint32_t total, uint32_t kk, uint32_t T,
-                              uint32_t ties, RefineShared& sh, int32_t* o) {
-  // the in-order loops below keep kB entries per lane in flight
-  // (addresses clamped to the entries, results of the surplus ones unused)
-  constexpr int kB = 8;
-  // final pass, in entry (= index) order: wave w takes a contiguous chunk
-  // of entries, 64 per step. First every wave counts the keys above T and
-  // equal to T in its chunk (ballots); then, from the counts of the waves
-  // before it, it knows how many keys precede its chunk in the output and
-  // how many of the ties are taken before it, and writes the indices it
-  // keeps at consecutive positions (ballot, lane prefix).
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t chunk = (total + NW * 64 - 1) / (NW * 64) * 64;
-  const uint32_t c0 = min(total, (uint32_t)wave * chunk), c1 = min(total, c0 + chunk);
-  uint32_t n_gt = 0, n_eq = 0;  // wave-uniform
-  for (uint32_t base = c0; base < c1; base += kB * 64) {  // wave-uniform
-    uint32_t u[kB];
-    {
-      uint2 ee[kB];
-      read_run(at, base, total - 1, ee);
+// Writes the kept entries of positions [c0, c1), in order, at output
+// positions from pos on: every key above T, and keys equal to T while
+// fewer than `ties` of them come before (eq_seen counts those before c0).
+// One ballot and a lane prefix count per 64 entries.
+template <int K, typename At>
+__device__ __forceinline__ void emit_run(At at, uint32_t c0, uint32_t c1, uint32_t kk,
+                                         uint32_t T, uint32_t ties, uint32_t pos,
+                                         uint32_t eq_seen, int32_t* o) {
+  const uint32_t lane = threadIdx.x & 63;
+  for (uint32_t base = c0; base < c1; base += K * 64) {  // wave-uniform
+    uint2 e[K];
+    read_run(at, base, c1 - 1, e);
 #pragma unroll
-      for (int i = 0; i < kB; ++i) u[i] = ee[i].x;
-    }
-#pragma unroll
-    for (int i = 0; i < kB; ++i) {
-      const bool valid = base + i * 64 + lane < c1;
-      n_gt += (uint32_t)__popcll(__ballot(valid && u[i] > T));
-      n_eq += (uint32_t)__popcll(__ballot(valid && u[i] == T));
-    }
-  }
-  uint32_t* wc = sh.h;  // [NW][2]; the histogram is no longer read
-  if (lane == 0) {
-    wc[2 * wave] = n_gt;
-    wc[2 * wave + 1] = n_eq;
-  }
-  __syncthreads();
-  uint32_t before_gt = 0, before_eq = 0;
-  for (int w = 0; w < wave; ++w) {
-    before_gt += wc[2 * w];
-    before_eq += wc[2 * w + 1];
-  }
-  uint32_t pos = before_gt + min(before_eq, ties);
-  uint32_t eq_seen = before_eq;
-  for (uint32_t base = c0; base < c1; base += kB * 64) {  // wave-uniform
-    uint2 e[kB];
-    read_run(at, base, total - 1, e);
-#pragma unroll
-    for (int i = 0; i < kB; ++i) {
+    for (int i = 0; i < K; ++i) {
       const bool valid = base + i * 64 + lane < c1;
       const bool gt = valid && e[i].x > T, eq = valid && e[i].x == T;
       const uint64_t beq = __ballot(eq);
@@ -408,6 +463,59 @@ __device__ void emit_in_order(At at, uint32_t total, uint32_t kk, uint32_t T,
       eq_seen += (uint32_t)__popcll(beq);
     }
   }
+}
+
+// Writes, in entry (= index) order, every key above T and the first `ties`
+// keys equal to T (all of them when ties is larger than their count):
+// o[0 .. kk) ascending. The positions fall into two parts, those in LDS
+// and those read from memory (either may be empty), and each wave takes a
+// contiguous chunk of each part. First every wave counts the keys above T
+// and equal to T in its chunks (ballots); then, from the counts of the
+// chunks before each of its own (all of the LDS part's chunks come before
+// the memory part's), it knows how many keys precede the chunk in the
+// output and how many of the ties are taken before it, and writes the
+// indices it keeps at consecutive positions.
+template <int NT, typename At>
+__device__ __forceinline__ void emit_in_order(At at, uint32_t total, uint32_t kk, uint32_t T,
+                                              uint32_t ties, RefineShared& sh, int32_t* o) {
+  constexpr int NW = NT / 64;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t mid = min(at.split(), total);
+  const WaveRun r0(mid, NT), r1(total - mid, NT);
+  const uint32_t b0 = mid + r1.c0, b1 = mid + r1.c1;
+  uint32_t n_gt0 = 0, n_eq0 = 0, n_gt1 = 0, n_eq1 = 0;  // wave-uniform
+  auto count0 = [&](uint32_t u, bool valid) {
+    n_gt0 += (uint32_t)__popcll(__ballot(valid && u > T));
+    n_eq0 += (uint32_t)__popcll(__ballot(valid && u == T));
+  };
+  auto count1 = [&](uint32_t u, bool valid) {
+    n_gt1 += (uint32_t)__popcll(__ballot(valid && u > T));
+    n_eq1 += (uint32_t)__popcll(__ballot(valid && u == T));
+  };
+  for_keys<kPassBatch>(at, r0.c0, r0.c1, count0);
+  for_keys<At::kMemKeys>(at, b0, b1, count1);
+  uint32_t* wc = sh.h;  // [NW][4]; the histogram is no longer read
+  if ((threadIdx.x & 63) == 0) {
+    wc[4 * wave] = n_gt0;
+    wc[4 * wave + 1] = n_eq0;
+    wc[4 * wave + 2] = n_gt1;
+    wc[4 * wave + 3] = n_eq1;
+  }
+  __syncthreads();
+  uint32_t gt0 = 0, eq0 = 0, gt0_all = 0, eq0_all = 0, gt1 = 0, eq1 = 0;
+  for (int w = 0; w < NW; ++w) {
+    if (w < wave) {
+      gt0 += wc[4 * w];
+      eq0 += wc[4 * w + 1];
+      gt1 += wc[4 * w + 2];
+      eq1 += wc[4 * w + 3];
+    }
+    gt0_all += wc[4 * w];
+    eq0_all += wc[4 * w + 1];
+  }
+  emit_run<kPassBatch>(at, r0.c0, r0.c1, kk, T, ties, gt0 + min(eq0, ties), eq0, o);
+  eq1 += eq0_all;
+  emit_run<At::kMemEntries>(at, b0, b1, kk, T, ties, gt0_all + gt1 + min(eq1, ties), eq1, o);
 }
 
 // Refine of the score-row top-k. One block per row: passes 2 and 3 of the
@@ -436,6 +544,118 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
     select_and_emit<NT>(rl, total, (uint32_t)kk, 1, b1, need1, 0u, sh, idx + (int64_t)row * kk);
 }
 
+constexpr int kGatherThreads = 1024;
+constexpr int kGatherPerWave = 4;  // sub-lists per wave
+constexpr int kGatherSubs = kGatherThreads / 64 * kGatherPerWave;  // per block
+
+// Gather (rows with many candidates). Block (g, row) takes sub-lists
+// [64 g, 64 g + 64) of the row, four per wave: the lengths of the sub-lists
+// before them give their place in the row's concatenation, and each wave
+// copies its sub-lists there, in the row's gather region, as (order key,
+// index) pairs. The first 128 entries of all four are requested before any
+// is stored (eight loads per lane in flight); longer sub-lists continue in
+// a second loop. The block's largest order key goes to bmax. A row whose
+// candidates would not fit its region is left alone (the select kernel
+// then reads the sub-lists themselves).
+__global__ __launch_bounds__(kGatherThreads) void topk_gather_kernel(SelectArgs a) {
+  constexpr int NT = kGatherThreads, NW = NT / 64, Q = kGatherPerWave;
+  __shared__ uint32_t red[3 * NW];
+  __shared__ uint32_t bc[kGatherSubs];
+  if (a.subs > kMaxSelectSubLists) return;  // as in the select kernel
+  const int row = blockIdx.y, g = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int s0 = g * kGatherSubs;
+  const uint32_t* cnt = a.sub_cnt + (int64_t)row * a.subs;
+  // lengths before the block's sub-lists, and of the whole row
+  if (threadIdx.x < kGatherSubs) bc[threadIdx.x] = 0u;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+  for (int s = threadIdx.x; s < a.subs; s += NT) {
+    const uint32_t c = cnt[s];
+    all += c;
+    if (s < s0) before += c;
+    else if (s < s0 + kGatherSubs) bc[s - s0] = c;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    before += (uint32_t)__shfl_xor((int)before, m, 64);
+    all += (uint32_t)__shfl_xor((int)all, m, 64);
+  }
+  if (lane == 0) {
+    red[wave] = before;
+    red[NW + wave] = all;
+  }
+  __syncthreads();
+  before = 0;
+  all = 0;
+  for (int w = 0; w < NW; ++w) {
+    before += red[w];
+    all += red[NW + w];
+  }
+  const SpillRow sr = spill_row(a.n, row);
+  if (all > sr.cap) return;  // block-uniform
+  // the wave's sub-lists: lengths, sources, destinations (wave-uniform)
+  uint32_t off = before;
+  for (int i = 0; i < Q * wave; ++i) off += bc[i];
+  uint32_t len[Q];
+  const uint2* src[Q];
+  uint2* dst[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int sl = Q * wave + q;
+    len[q] = bc[sl];  // 0 past the row's last sub-list
+    src[q] = a.lists + (int64_t)row * a.n + (int64_t)min(s0 + sl, a.subs - 1) * a.sub_len;
+    dst[q] = a.spill + sr.start + off;
+    off += len[q];
+  }
+  uint32_t umax = 0;
+  {
+    uint2 e[Q][2];
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        e[q][i] = src[q][min((uint32_t)(i * 64 + lane), max(len[q], 1u) - 1)];
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t j = i * 64 + lane;
+        const uint32_t u = float_order_key(__uint_as_float(e[q][i].x));
+        if (j < len[q]) {
+          dst[q][j] = make_uint2(u, e[q][i].y);
+          umax = max(umax, u);
+        }
+      }
+  }
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    constexpr int kB = 4;
+    for (uint32_t j0 = 128; j0 < len[q]; j0 += kB * 64) {  // wave-uniform
+      uint2 e[kB];
+#pragma unroll
+      for (int i = 0; i < kB; ++i) e[i] = src[q][min(j0 + i * 64 + lane, len[q] - 1)];
+#pragma unroll
+      for (int i = 0; i < kB; ++i) {
+        const uint32_t j = j0 + i * 64 + lane;
+        const uint32_t u = float_order_key(__uint_as_float(e[i].x));
+        if (j < len[q]) {
+          dst[q][j] = make_uint2(u, e[i].y);
+          umax = max(umax, u);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) umax = max(umax, (uint32_t)__shfl_xor((int)umax, m, 64));
+  if (lane == 0) red[2 * NW + wave] = umax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 0; w < NW; ++w) umax = max(umax, red[2 * NW + w]);
+    a.bmax[(int64_t)row * gridDim.x + g] = umax;
+  }
+}
+
 // Selection of the decode path. One block per row. The score kernel's
 // blocks each emitted (in index order) the keys whose score reached their
 // own threshold; with T the largest of those thresholds, every key of the
@@ -449,7 +669,10 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
 // Two dependent rounds of memory requests: the sub-list lengths and the
 // block thresholds, then the candidates themselves, copied by
 // direct-to-LDS loads (one dword per lane, so any entry offset will do)
-// straight to their place in the concatenation.
+// straight to their place in the concatenation. A row the gather kernel
+// copied into one contiguous run (already order keys, its largest key
+// known) is copied from there instead, 16 bytes per lane, and the entries
+// past the LDS copy are read from that run.
 __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs a) {
   constexpr int NT = kRefineThreads;
   __shared__ RefineShared sh;
@@ -474,6 +697,9 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
 #pragma unroll
   for (int q = 0; q < kPerMax; ++q) cn[q] = (q < per && s0 + q < a.subs) ? cnt[s0 + q] : 0u;
   uint32_t tmax = (int)threadIdx.x < a.segs ? a.thr[(int64_t)row * a.segs + threadIdx.x] : 0u;
+  // gathered rows: the largest order key of each gather block
+  const int gw = (a.subs + kGatherSubs - 1) / kGatherSubs;
+  uint32_t gmax = a.spill && (int)threadIdx.x < gw ? a.bmax[(int64_t)row * gw + threadIdx.x] : 0u;
   uint32_t total;
   {
     uint32_t sum = 0;
@@ -488,21 +714,49 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
     if (threadIdx.x == 0) sh.off[a.subs] = total;
   }
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, m, 64));
-  if (lane == 0) sh.tmax[wave] = tmax;
+  for (int m = 32; m >= 1; m >>= 1) {
+    tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, m, 64));
+    gmax = max(gmax, (uint32_t)__shfl_xor((int)gmax, m, 64));
+  }
+  if (lane == 0) {
+    sh.tmax[wave] = tmax;
+    sh.wmax[wave] = gmax;
+  }
   __syncthreads();
   tmax = 0;
-  for (int w = 0; w < kWaves; ++w) tmax = max(tmax, sh.tmax[w]);
+  gmax = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    tmax = max(tmax, sh.tmax[w]);
+    gmax = max(gmax, sh.wmax[w]);
+  }
   // (no key of a finite score has an order key below 1)
   const uint32_t floor = max(tmax, 1u);
-
-  // The first `cached` entries of the concatenation into LDS: wave w
-  // copies the run of sub-lists [w * spw, (w + 1) * spw), 32 entries (64
-  // dwords) per load, lane i taking dword i. The run's offsets are read
-  // once (one per lane) and handed to the issuing loop through lane reads.
+  // the gather kernel copied the row's candidates when they fit its region
+  const SpillRow sr = spill_row(a.n, row);
+  const bool gathered = a.spill != nullptr && total <= sr.cap;  // block-uniform
   const uint32_t cached = min(total, (uint32_t)kRefineCache);
   unsigned char* cache_bytes = reinterpret_cast<unsigned char*>(sh.cache);
-  {
+  const RowLists rl{glob, sh.cache, cached, sh.off, a.subs, a.sub_len, true, false};
+  uint32_t umax = 0;
+  if (gathered) {
+    // the first `cached` entries of the contiguous run into LDS, 16 bytes
+    // (two entries) per lane and load; an odd last entry by one thread
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.spill + sr.start);
+    const uint32_t pairs = cached / 2;
+    for (uint32_t c0 = (uint32_t)wave * 64; c0 < pairs; c0 += NT) {  // wave-uniform
+      if (c0 + lane < pairs)
+        __builtin_amdgcn_global_load_lds(
+            src + 4 * (size_t)(c0 + lane),
+            (__attribute__((address_space(3))) void*)(cache_bytes + (size_t)c0 * 16), 16, 0, 0);
+    }
+    if ((cached & 1u) && threadIdx.x == 0) sh.cache[cached - 1] = a.spill[sr.start + cached - 1];
+    __syncthreads();  // the copies have landed
+    umax = gmax;
+  } else {
+    // The first `cached` entries of the concatenation into LDS: wave w
+    // copies the run of sub-lists [w * spw, (w + 1) * spw), 32 entries (64
+    // dwords) per load, lane i taking dword i. The run's offsets are read
+    // once (one per lane) and handed to the issuing loop through lane reads.
     const int spw = (a.subs + kWaves - 1) / kWaves;
     const int sb = min(a.subs, wave * spw), se = min(a.subs, sb + spw);
     for (int k0 = sb; k0 < se; k0 += 63) {  // wave-uniform
@@ -526,46 +780,48 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
         }
       }
     }
-  }
-  __syncthreads();  // the copies have landed
-  // score bits to order keys in place, and the largest order key of the
-  // row (the entries beyond the LDS copy read from memory)
-  const RowLists rl{glob, sh.cache, cached, sh.off, a.subs, a.sub_len, true, false};
-  uint32_t umax = 0;  // this thread's
-  for (uint32_t base = threadIdx.x; base < cached; base += kPassBatch * NT) {
-    uint32_t uu[kPassBatch];
+    __syncthreads();  // the copies have landed
+    // score bits to order keys in place, and the largest order key of the
+    // row (the entries beyond the LDS copy read from memory)
+    for (uint32_t base = threadIdx.x; base < cached; base += kPassBatch * NT) {
+      uint32_t uu[kPassBatch];
 #pragma unroll
-    for (int i = 0; i < kPassBatch; ++i)
-      uu[i] = base + i * NT < cached ? sh.cache[base + i * NT].x : 0u;
+      for (int i = 0; i < kPassBatch; ++i)
+        uu[i] = base + i * NT < cached ? sh.cache[base + i * NT].x : 0u;
 #pragma unroll
-    for (int i = 0; i < kPassBatch; ++i) {
-      if (base + i * NT >= cached) break;
-      const uint32_t u = float_order_key(__uint_as_float(uu[i]));
-      sh.cache[base + i * NT].x = u;
-      umax = max(umax, u);
+      for (int i = 0; i < kPassBatch; ++i) {
+        if (base + i * NT >= cached) break;
+        const uint32_t u = float_order_key(__uint_as_float(uu[i]));
+        sh.cache[base + i * NT].x = u;
+        umax = max(umax, u);
+      }
     }
-  }
-  {
-    // the entries past the LDS copy, wave-contiguous runs of positions
-    const WaveRun mr(total - cached, NT);
-    for (uint32_t base = cached + mr.c0; base < cached + mr.c1; base += kPassBatch * 64) {
-      uint2 ee[kPassBatch];
-      read_run(rl, base, cached + mr.c1 - 1, ee);
+    {
+      // the entries past the LDS copy, wave-contiguous runs of positions
+      const WaveRun mr(total - cached, NT);
+      for (uint32_t base = cached + mr.c0; base < cached + mr.c1; base += kPassBatch * 64) {
+        uint2 ee[kPassBatch];
+        read_run(rl, base, cached + mr.c1 - 1, ee);
 #pragma unroll
-      for (int i = 0; i < kPassBatch; ++i) umax = max(umax, ee[i].x);
+        for (int i = 0; i < kPassBatch; ++i) umax = max(umax, ee[i].x);
+      }
     }
-  }
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) umax = max(umax, (uint32_t)__shfl_xor((int)umax, m, 64));
-  if (lane == 0) sh.wmax[wave] = umax;
-  __syncthreads();  // also completes the conversion
-  umax = 0;
-  for (int w = 0; w < kWaves; ++w) umax = max(umax, sh.wmax[w]);
+    for (int m = 32; m >= 1; m >>= 1) umax = max(umax, (uint32_t)__shfl_xor((int)umax, m, 64));
+    if (lane == 0) sh.wmax[wave] = umax;
+    __syncthreads();  // also completes the conversion
+    umax = 0;
+    for (int w = 0; w < kWaves; ++w) umax = max(umax, sh.wmax[w]);
+  }
   if (umax >= floor) {
-    const bool done =
-        total <= cached
-            ? select_range_and_emit<NT>(CacheAt{sh.cache}, total, kk, floor, umax, sh, o)
-            : select_range_and_emit<NT>(rl, total, kk, floor, umax, sh, o);
+    bool done;
+    if (total <= cached)
+      done = select_range_and_emit<NT>(CacheAt{sh.cache}, total, kk, floor, umax, sh, o);
+    else if (gathered)
+      done = select_range_and_emit<NT>(SpillAt{sh.cache, cached, a.spill + sr.start}, total, kk,
+                                       floor, umax, sh, o);
+    else
+      done = select_range_and_emit<NT>(rl, total, kk, floor, umax, sh, o);
     if (done) return;
   }
 
@@ -779,9 +1035,24 @@ hipError_t launch_topk(const float* scores, const TopkPlan& plan, int32_t* idx,
   return hipGetLastError();
 }
 
+int select_gather_blocks(int subs, int64_t kk) {
+  // a row's candidates number about 2 to 4 kk: gather them when they would
+  // overflow the select kernel's LDS copy
+  return 3 * kk > kRefineCache ? (subs + kGatherSubs - 1) / kGatherSubs : 0;
+}
+
 hipError_t launch_topk_select(const SelectArgs& a, int rows, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  launch_kernel(topk_select_kernel, dim3(rows), dim3(kRefineThreads), 0, stream, a);
+  SelectArgs b = a;
+  const int gw = b.spill && b.bmax ? select_gather_blocks(b.subs, b.kk) : 0;
+  if (gw == 0) {
+    b.spill = nullptr;
+  } else {
+    launch_kernel(topk_gather_kernel, dim3(gw, rows), dim3(kGatherThreads), 0, stream, b);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  launch_kernel(topk_select_kernel, dim3(rows), dim3(kRefineThreads), 0, stream, b);
   return hipGetLastError();
 }
 

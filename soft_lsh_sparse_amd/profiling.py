@@ -55,6 +55,7 @@ KERNEL_SOURCES = {
     "topk_hist_kernel": ["topk.hip", "radix.hpp"],
     "topk_filter_kernel": ["topk.hip", "radix.hpp"],
     "topk_refine_kernel": ["topk.hip", "radix.hpp"],
+    "topk_gather_kernel": ["topk.hip", "radix.hpp"],
     "topk_select_kernel": ["topk.hip", "radix.hpp"],
     "sparse_attn_kernel": ["sparse_attn.hip"],
     "attn_merge_kernel": ["sparse_attn.hip"],

@@ -214,6 +214,11 @@ def test_decode_kernel_sequence(lib):
     assert _kernels(lib, P=6)[1][0] == "bucket_probs_kernel"
     assert _kernels(lib, ids=FAKE + 8)[1][0] == "bucket_probs_kernel"  # unaligned id rows
     assert _kernels(lib, L=24, P=8)[1][0] == "bucket_probs_kernel"     # not the rotated path
+    # large k: the candidates are gathered before the select
+    gathered = ["score_kernel", "topk_gather_kernel", "topk_select_kernel"] + tail
+    assert _kernels(lib, k=16384) == (5, gathered)
+    assert _kernels(lib, k=5462)[1] == gathered
+    assert _kernels(lib, k=5461)[1] == ["score_kernel", "topk_select_kernel"] + tail
     assert _kernels(lib, k=131072) == (3, ["iota_rows_kernel"] + tail)
     assert _kernels(lib, k=131072, with_scores=1)[1] == ["score_kernel", "iota_rows_kernel"] + tail
     assert _kernels(lib, Hq=30)[0] == -1      # G not an integer

@@ -801,15 +801,17 @@ def test_decode_without_score_rows_selects_the_same(name):
         assert np.array_equal(idx_np[b, h], O.topk_indices(sc_np[b, h], w.k))
 
 
-@pytest.mark.parametrize("with_rows,Hq", [(True, 4), (False, 4), (False, 8)])
-def test_decode_threshold_fallback_selects_from_full_rows(with_rows, Hq):
+@pytest.mark.parametrize("with_rows,Hq,k", [(True, 4, 1024), (False, 4, 1024), (False, 8, 1024),
+                                             (False, 4, 6000), (True, 4, 6000)])
+def test_decode_threshold_fallback_selects_from_full_rows(with_rows, Hq, k):
     """Value norms vanish except on the sampled keys of KV head 0, so that head's
     rows see fewer than k keys reach the estimated threshold and are selected
     from fully scored rows; KV head 1 takes the candidate path. Ties among the
-    zero scores go to the lower indices."""
+    zero scores go to the lower indices. k = 6000: the candidates are gathered
+    first (and head 0's rows have fewer of them than k)."""
     w = W.custom_workload(B=1, Hq=Hq, Hkv=2, d=128, N=65536, dtype="bf16", L=32, P=8,
-                          tau=0.3, k=1024, lognormal_v=True, name="fallback")
-    log(f"decode threshold fallback with_rows={with_rows} Hq={Hq}")
+                          tau=0.3, k=k, lognormal_v=True, name="fallback")
+    log(f"decode threshold fallback with_rows={with_rows} Hq={Hq} k={k}")
     Q, K, V, R = W.make_decode_inputs(w, DEV, seed=11)
     ids, vn = S.hash_keys(K, V, R, w.L, w.P)
     pos = torch.from_numpy(_sample_positions(w.N)).to(DEV)
@@ -831,7 +833,11 @@ def test_decode_threshold_fallback_selects_from_full_rows(with_rows, Hq):
     for h in range(Hq):
         assert np.array_equal(idx_np[0, h], O.topk_indices(s_np[0, h], w.k)), f"head {h}"
     # head 0's selection: only sampled keys score above zero
-    assert np.isin(idx_np[0, 0], _sample_positions(w.N)).all()
+    samples = _sample_positions(w.N)
+    if w.kk <= samples.size:
+        assert np.isin(idx_np[0, 0], samples).all()
+    else:  # every sampled key that scores above zero, the rest zeros
+        assert np.isin(samples[s_np[0, 0, samples] > 0], idx_np[0, 0]).all()
     Q64 = f64(Q)
     for h in (0, Hq - 1):
         g = h // w.G
@@ -858,3 +864,45 @@ def test_decode_all_scores_tied(N):
     torch.cuda.synchronize()
     want = torch.arange(w.kk, dtype=torch.int32).expand(1, 4, w.kk)
     assert torch.equal(idx.cpu(), want)
+
+
+@pytest.mark.parametrize("N,k", [(30000, 6000), (100000, 8000)])
+def test_decode_gathered_candidates(N, k):
+    """With k large enough the selection first gathers each row's candidates
+    into one contiguous run (16K of them in LDS, the rest read from the run):
+    full oracle check of every row, and the call without score rows (whose
+    row buffers hold the gathered runs) selects the same."""
+    w = W.custom_workload(B=1, Hq=4, Hkv=2, d=128, N=N, dtype="bf16", L=32, P=8,
+                          tau=0.3, k=k, outlier_channels=4, outlier_scale=8.0,
+                          lognormal_v=True, planted=16, name="gathered")
+    log(f"decode gathered candidates N={N} k={k}")
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=5)
+    ids, vn, out, idx, sc = _check_decode(w, seed=5)
+    idx2 = torch.empty_like(idx)
+    out2, _, _ = S.decode(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, idx_out=idx2)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    assert torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("N,top", [(40000, 19000), (40000, 40000), (24000, 9000)])
+def test_decode_gathered_ties(N, top):
+    """All keys below `top` share one score, the others score 0: k = 6000 of
+    the tied keys are taken, the lowest indices first. top = 19000: the
+    19000 candidates are gathered (past the LDS copy); top = 40000: they
+    overflow the row's gather region and are read from the sub-lists;
+    N = 24000: gathered, all in LDS."""
+    w = W.custom_workload(B=1, Hq=4, Hkv=1, d=128, N=N, dtype="bf16", L=32, P=8,
+                          tau=0.3, k=6000, lognormal_v=False, name="tied_gathered")
+    log(f"decode gathered ties N={N} top={top}")
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=13)
+    ids = torch.full((1, 1, N, w.L), 5, dtype=torch.uint8, device=DEV)
+    vn = torch.zeros((1, 1, N), dtype=torch.float32, device=DEV)
+    vn[..., :top] = 1.0
+    for with_rows in (False, True):
+        idx = torch.empty((1, 4, w.kk), dtype=torch.int32, device=DEV)
+        sc = torch.empty((1, 4, N), dtype=torch.float32, device=DEV) if with_rows else None
+        S.decode(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, idx_out=idx, scores_out=sc)
+        torch.cuda.synchronize()
+        want = torch.arange(w.kk, dtype=torch.int32).expand(1, 4, w.kk)
+        assert torch.equal(idx.cpu(), want), f"with_rows={with_rows}"
