@@ -16,13 +16,13 @@
 //     hyperplane columns sits in LDS in the order the MFMA A operand reads
 //     it (fragment (column tile, k-step) = 1 KB, conflict-free 16-byte
 //     reads); every wave owns its own 32-key tiles and loads their K and V
-//     half-rows straight into registers (the next tile's K while the
-//     current one is computed, the current tile's V for its value norms at
-//     the end), so no wave waits for another after the set-up. The
-//     projection y = K R runs on the matrix cores (v_mfma_f32_32x32x16_bf16,
-//     float32 accumulation of the exact bf16 products), one 32-column tile
-//     at a time, and the sign work of the previous column tile sits between
-//     its k-steps. One lane ends with 16 projections of one key; their sign
+//     rows straight into registers, each lane every other 16-byte chunk of
+//     one row (the next tile's K while the current one is computed, the
+//     current tile's V for its value norms at the end), so no wave waits
+//     for another after the set-up. The projection y = K R runs on the
+//     matrix cores (v_mfma_f32_32x32x16_bf16, float32 accumulation of the
+//     exact bf16 products), one 32-column tile at a time, and the sign work
+//     of the previous column tile sits between its k-steps. One lane ends with 16 projections of one key; their sign
 //     bits are packed with one funnel shift each; the A rows are permuted so
 //     that a lane's 16 bits are 16 consecutive hyperplanes and one exchange
 //     between the two lane halves yields a 32-bit word of 32 consecutive
@@ -141,9 +141,11 @@ __device__ __forceinline__ TileRows tile_rows(const HashArgs& a, int tile) {
   return {(int64_t)head * a.stride + row0, (int)min<int64_t>(kTileKeys, a.n_keys - row0)};
 }
 
-// Half-rows of one lane for a 32-key tile: lane (kn, kh) holds elements
-// kh*d/2 .. kh*d/2 + d/2 - 1 of row kn of K (the B operand of k-steps
-// 0..S-1) or of V (rows past the end of the head repeat its last row).
+// Half-rows of one lane for a 32-key tile: lane (kn, kh) holds the 16-byte
+// chunks 2s + kh (s = 0..S-1: the B operand of k-step s) of row kn of K, or
+// of V (rows past the end of the head repeat its last row). The two lanes
+// of a key read neighbouring chunks, so each load instruction touches 32
+// rows in 32-byte runs.
 template <int D>
 struct HalfRows {
   u32x4_t q[D / 16];
@@ -155,10 +157,10 @@ __device__ __forceinline__ void load_half_rows(const HashArgs& a, const uint16_t
   const int kn = lane & 31, kh = lane >> 5;
   const TileRows tr = tile_rows(a, tile);
   const int64_t row = tr.grow0 + min(kn, tr.rows - 1);
-  const uint4* p = reinterpret_cast<const uint4*>(base + row * D + kh * (D / 2));
+  const uint4* p = reinterpret_cast<const uint4*>(base + row * D) + kh;
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    const uint4 x = p[s];
+    const uint4 x = p[2 * s];
     r.q[s] = u32x4_t{x.x, x.y, x.z, x.w};
   }
 }
@@ -443,7 +445,8 @@ __global__ __launch_bounds__(kHashThreads, 1) void hash_keys_bf16_kernel(HashArg
 // R [d, C] -> R^T [kRtRows, d] with zero rows past C, and the same in the
 // order of the main kernel's A fragments: 16-byte chunk q holds, for
 // f = q / 64 = ct * S + st and l = q % 64 = h * 32 + m, elements
-// (h * S + st) * 8 .. + 7 of R^T row ct * 32 + jmap(m) (S = D / 16).
+// (2 * st + h) * 8 .. + 7 of R^T row ct * 32 + jmap(m) (S = D / 16), the
+// chunk the B operand of k-step st holds in lane half h.
 __global__ __launch_bounds__(256) void hash_prep_kernel(const uint16_t* __restrict__ R, int C,
                                                         int D, uint16_t* __restrict__ RT,
                                                         uint16_t* __restrict__ RTF) {
@@ -460,7 +463,7 @@ __global__ __launch_bounds__(256) void hash_prep_kernel(const uint16_t* __restri
     const int e = (int)(i % 8);
     const int f = (int)(q / 64), l = (int)(q % 64);
     const int ct = f / S, st = f % S, h = l / 32, m = l % 32;
-    const int r = ct * 32 + jmap(m), d = (h * S + st) * 8 + e;
+    const int r = ct * 32 + jmap(m), d = (2 * st + h) * 8 + e;
     RTF[i] = r < C ? R[(int64_t)d * C + r] : (uint16_t)0;
   }
 }
@@ -700,7 +703,8 @@ __global__ __launch_bounds__(256) void hash_keys_direct_kernel(
 // certified against the rounding bound of the sum of |products|, else
 // recomputed in double-double; the sign bits meet in LDS and threads
 // l < L write the id bytes. The value norm follows the main kernel's
-// arithmetic exactly (bf16 dot2 steps per half-row, then the halves).
+// arithmetic exactly (bf16 dot2 steps over the even and over the odd
+// 16-byte chunks of the row, then the two sums).
 template <int D>
 __global__ __launch_bounds__(256) void hash_keys_small_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -722,7 +726,7 @@ __global__ __launch_bounds__(256) void hash_keys_small_kernel(
     for (int h = 0; h < 2; ++h) {
       half[h] = 0.f;
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) half[h] = sumsq_bf16x8(vrow[h * (D / 16) + c], half[h]);
+      for (int c = 0; c < D / 16; ++c) half[h] = sumsq_bf16x8(vrow[2 * c + h], half[h]);
     }
     vnorm[off] = __builtin_amdgcn_sqrtf(half[0] + half[1]);
   }
