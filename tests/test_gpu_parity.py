@@ -298,6 +298,7 @@ def test_sparse_attn_stage(B, Hq, Hkv, d, N, kk, dt):
     (1, 8, 2, 3000, 256),       # selection from candidates, ragged tail
     (2, 4, 1, 1500, 2000),      # k >= N: every key, one set per KV head
     (1, 8, 8, 2048, 64),        # G = 1: the per-head decode
+    (1, 8, 2, 30000, 6000),     # large k: candidates gathered before the select
 ])
 def test_decode_group_shared_matches_the_oracle(B, Hq, Hkv, N, k):
     w = W.custom_workload(B=B, Hq=Hq, Hkv=Hkv, d=128, N=N, dtype="bf16", L=32, P=8,
@@ -848,7 +849,7 @@ def test_decode_threshold_fallback_selects_from_full_rows(with_rows, Hq, k):
         assert np.max(np.abs(f64(out[0, h]) - ref)) <= 2e-2
 
 
-@pytest.mark.parametrize("N", [9000, 40000])
+@pytest.mark.parametrize("N", [9000, 9001, 40000])
 def test_decode_all_scores_tied(N):
     """Every key in the same buckets with the same value norm: all scores of a
     row are equal, every key reaches the threshold (beyond the LDS copy of
@@ -885,13 +886,14 @@ def test_decode_gathered_candidates(N, k):
     assert torch.equal(out, out2)
 
 
-@pytest.mark.parametrize("N,top", [(40000, 19000), (40000, 40000), (24000, 9000)])
+@pytest.mark.parametrize("N,top", [(40000, 19000), (40000, 19001), (40000, 40000),
+                                   (24000, 9000), (24000, 9001)])
 def test_decode_gathered_ties(N, top):
     """All keys below `top` share one score, the others score 0: k = 6000 of
-    the tied keys are taken, the lowest indices first. top = 19000: the
-    19000 candidates are gathered (past the LDS copy); top = 40000: they
+    the tied keys are taken, the lowest indices first. top = 19000 or 19001:
+    the candidates are gathered (past the LDS copy); top = 40000: they
     overflow the row's gather region and are read from the sub-lists;
-    N = 24000: gathered, all in LDS."""
+    N = 24000: gathered, all in LDS. Odd counts end in half a pair."""
     w = W.custom_workload(B=1, Hq=4, Hkv=1, d=128, N=N, dtype="bf16", L=32, P=8,
                           tau=0.3, k=6000, lognormal_v=False, name="tied_gathered")
     log(f"decode gathered ties N={N} top={top}")

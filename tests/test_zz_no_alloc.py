@@ -89,6 +89,26 @@ def test_noalloc_decode_equals_decode_on_two_calls_in_a_row():
         assert np.array_equal(i.cpu().numpy(), O.topk_indices(sc_np, w.k))
 
 
+def test_noalloc_decode_gathers_large_k():
+    """k large enough that the selection gathers each row's candidates into
+    the workspace first (inside the device array here): same results as
+    socket_decode, then a smaller call."""
+    lib = _lib.load()
+    big = W.custom_workload(B=1, Hq=8, Hkv=2, d=128, N=30000, dtype="bf16", L=32, P=8,
+                            tau=0.3, k=6000, lognormal_v=True, name="noalloc_gathered")
+    small = W.custom_workload(B=1, Hq=4, Hkv=1, d=128, N=20000, dtype="bf16", L=32, P=8,
+                              tau=0.3, k=5500, lognormal_v=True, name="noalloc_gathered_small")
+    for w, seed in ((big, 23), (small, 24)):
+        assert lib.socket_decode_kernels(0x1000, _lib.DTYPE_BF16, w.B, w.Hq, w.Hkv, w.d, w.N,
+                                         w.N, w.L, w.P, w.k, 0, None, 0) == 5  # + gather
+        _log(f"noalloc decode {w.name}")
+        Q, K, V, outs = _run_both(lib, w, seed)
+        (o_ref, i_ref, s_ref, o2_ref, i2_ref), (o, i, s, o2, i2) = outs
+        assert torch.equal(i, i_ref) and torch.equal(s, s_ref) and torch.equal(o, o_ref)
+        assert torch.equal(i2, i_ref) and torch.equal(o2, o_ref), f"{w.name}: benched form"
+        assert np.array_equal(i.cpu().numpy(), O.topk_indices(s.cpu().numpy(), w.k))
+
+
 def test_noalloc_decode_rejects_a_call_larger_than_its_array():
     lib = _lib.load()
     w = W.WORKLOADS["llama3_8b_128k_b4"]
