@@ -132,6 +132,7 @@ struct RefineShared {
   uint32_t scratch[2 * (kRefineThreads / 64 + 1) + 4];
   uint32_t tmax[kRefineThreads / 64];
   uint32_t wmax[kRefineThreads / 64];  // per-wave largest order keys of the candidates
+  uint32_t cmax[kRefineThreads / 64];  // per-wave longest sub-lists
   uint32_t h[kHistBins];
   uint32_t off[kMaxSelectSubLists + 1];
   alignas(16) uint2 cache[kRefineCache];  // 16-byte direct-to-LDS copies
@@ -544,6 +545,10 @@ __global__ __launch_bounds__(kRefineThreads) void topk_refine_kernel(
     select_and_emit<NT>(rl, total, (uint32_t)kk, 1, b1, need1, 0u, sh, idx + (int64_t)row * kk);
 }
 
+// The select kernel's copy of short sub-lists: entries each thread
+// requests at a time.
+constexpr int kShortBatch = 8;
+
 constexpr int kGatherThreads = 1024;
 constexpr int kGatherPerWave = 4;  // sub-lists per wave
 constexpr int kGatherSubs = kGatherThreads / 64 * kGatherPerWave;  // per block
@@ -672,7 +677,8 @@ __global__ __launch_bounds__(kGatherThreads) void topk_gather_kernel(SelectArgs 
 // straight to their place in the concatenation. A row the gather kernel
 // copied into one contiguous run (already order keys, its largest key
 // known) is copied from there instead, 16 bytes per lane, and the entries
-// past the LDS copy are read from that run.
+// past the LDS copy are read from that run. A row of short sub-lists that
+// fits LDS is copied by plain loads, a few threads per sub-list.
 __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs a) {
   constexpr int NT = kRefineThreads;
   __shared__ RefineShared sh;
@@ -700,11 +706,14 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
   // gathered rows: the largest order key of each gather block
   const int gw = (a.subs + kGatherSubs - 1) / kGatherSubs;
   uint32_t gmax = a.spill && (int)threadIdx.x < gw ? a.bmax[(int64_t)row * gw + threadIdx.x] : 0u;
-  uint32_t total;
+  uint32_t total, cmax = 0;  // cmax: the longest sub-list
   {
     uint32_t sum = 0;
 #pragma unroll
-    for (int q = 0; q < kPerMax; ++q) sum += cn[q];
+    for (int q = 0; q < kPerMax; ++q) {
+      sum += cn[q];
+      cmax = max(cmax, cn[q]);
+    }
     uint32_t run = block_exclusive_scan<NT>(sum, sh.scratch, &total);
 #pragma unroll
     for (int q = 0; q < kPerMax; ++q) {
@@ -717,17 +726,21 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
   for (int m = 32; m >= 1; m >>= 1) {
     tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, m, 64));
     gmax = max(gmax, (uint32_t)__shfl_xor((int)gmax, m, 64));
+    cmax = max(cmax, (uint32_t)__shfl_xor((int)cmax, m, 64));
   }
   if (lane == 0) {
     sh.tmax[wave] = tmax;
     sh.wmax[wave] = gmax;
+    sh.cmax[wave] = cmax;
   }
   __syncthreads();
   tmax = 0;
   gmax = 0;
+  cmax = 0;
   for (int w = 0; w < kWaves; ++w) {
     tmax = max(tmax, sh.tmax[w]);
     gmax = max(gmax, sh.wmax[w]);
+    cmax = max(cmax, sh.cmax[w]);
   }
   // (no key of a finite score has an order key below 1)
   const uint32_t floor = max(tmax, 1u);
@@ -737,6 +750,7 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
   const uint32_t cached = min(total, (uint32_t)kRefineCache);
   unsigned char* cache_bytes = reinterpret_cast<unsigned char*>(sh.cache);
   const RowLists rl{glob, sh.cache, cached, sh.off, a.subs, a.sub_len, true, false};
+  const int tps = a.subs <= NT ? NT / a.subs : 1;  // threads per sub-list (short lists)
   uint32_t umax = 0;
   if (gathered) {
     // the first `cached` entries of the contiguous run into LDS, 16 bytes
@@ -752,6 +766,37 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
     if ((cached & 1u) && threadIdx.x == 0) sh.cache[cached - 1] = a.spill[sr.start + cached - 1];
     __syncthreads();  // the copies have landed
     umax = gmax;
+  } else if (total <= cached && cmax <= (uint32_t)tps * kShortBatch * 2) {
+    // Short sub-lists (at most two requests per thread): tps threads per
+    // sub-list copy it with plain loads, thread r of a sub-list taking
+    // entries r, r + tps, ..., kShortBatch requested at a time, converted
+    // to order keys on the way (no direct-to-LDS load per sub-list, no
+    // conversion sweep).
+    for (int t = threadIdx.x; t < a.subs * tps; t += NT) {
+      const int sl = t / tps, r = t - sl * tps;
+      const uint32_t o0 = sh.off[sl], n = sh.off[sl + 1] - o0;
+      const uint2* src = glob + (int64_t)sl * a.sub_len;
+      for (uint32_t j0 = r; j0 < n; j0 += tps * kShortBatch) {
+        uint2 e[kShortBatch];
+#pragma unroll
+        for (int i = 0; i < kShortBatch; ++i) e[i] = src[min(j0 + i * tps, n - 1)];
+#pragma unroll
+        for (int i = 0; i < kShortBatch; ++i) {
+          const uint32_t j = j0 + i * tps;
+          const uint32_t u = float_order_key(__uint_as_float(e[i].x));
+          if (j < n) {
+            sh.cache[o0 + j] = make_uint2(u, e[i].y);
+            umax = max(umax, u);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) umax = max(umax, (uint32_t)__shfl_xor((int)umax, m, 64));
+    if (lane == 0) sh.wmax[wave] = umax;
+    __syncthreads();  // also completes the copy
+    umax = 0;
+    for (int w = 0; w < kWaves; ++w) umax = max(umax, sh.wmax[w]);
   } else {
     // The first `cached` entries of the concatenation into LDS: wave w
     // copies the run of sub-lists [w * spw, (w + 1) * spw), 32 entries (64

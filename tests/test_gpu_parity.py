@@ -908,3 +908,37 @@ def test_decode_gathered_ties(N, top):
         torch.cuda.synchronize()
         want = torch.arange(w.kk, dtype=torch.int32).expand(1, 4, w.kk)
         assert torch.equal(idx.cpu(), want), f"with_rows={with_rows}"
+
+
+@pytest.mark.parametrize("with_rows", [False, True])
+def test_decode_clustered_candidates(with_rows):
+    """The first 4096 keys sit, in every table, in query head 0's most likely
+    bucket, with a value norm of 1; the others keep their own buckets with a
+    norm of 1e-3. L = 24 (tables summed in the same order for every key), so
+    head 0's candidates are exactly those 4096 tied keys (every other score
+    is below 24e-3, theirs at least 24/256), in full sub-lists too long for
+    the select's per-thread copy (its direct-to-LDS path runs), and its k
+    lowest indices are selected. Every head's selection equals the oracle's
+    top-k of the GPU's own scores."""
+    w = W.custom_workload(B=1, Hq=4, Hkv=1, d=128, N=65536, dtype="bf16", L=24, P=8,
+                          tau=0.3, k=2000, lognormal_v=False, name="clustered")
+    log(f"decode clustered candidates with_rows={with_rows}")
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=14)
+    ids, vn = S.hash_keys(K, V, R, w.L, w.P)
+    table = S.bucket_probs(Q, R, w.Hkv, w.L, w.P, w.tau)  # [B, Hkv, 2^P, L, G]
+    best = table[0, 0, :, :, 0].argmax(dim=0).to(torch.uint8)  # per table
+    ids[..., :4096, :] = best
+    vn = torch.full_like(vn, 1e-3)
+    vn[..., :4096] = 1.0
+    idx = torch.empty((1, 4, w.kk), dtype=torch.int32, device=DEV)
+    sc = torch.empty((1, 4, w.N), dtype=torch.float32, device=DEV) if with_rows else None
+    S.decode(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, idx_out=idx, scores_out=sc)
+    sc_ref = S.score(table, ids, vn, w.Hq)
+    torch.cuda.synchronize()
+    if with_rows:
+        assert torch.equal(sc, sc_ref)
+    s_np, idx_np = sc_ref.cpu().numpy(), idx.cpu().numpy()
+    for h in range(4):
+        assert np.array_equal(idx_np[0, h], O.topk_indices(s_np[0, h], w.k)), f"head {h}"
+    assert s_np[0, 0, 4096:].max() < s_np[0, 0, 0]
+    assert np.array_equal(idx_np[0, 0], np.arange(w.kk))
