@@ -942,3 +942,27 @@ def test_decode_clustered_candidates(with_rows):
         assert np.array_equal(idx_np[0, h], O.topk_indices(s_np[0, h], w.k)), f"head {h}"
     assert s_np[0, 0, 4096:].max() < s_np[0, 0, 0]
     assert np.array_equal(idx_np[0, 0], np.arange(w.kk))
+
+
+@pytest.mark.parametrize("with_rows", [False, True])
+def test_decode_many_sub_lists(with_rows):
+    """One KV head of 600000 keys: 147 score blocks of 16 waves give 2352
+    candidate sub-lists per row, more than the select's 1024 threads, each
+    of which then copies several short sub-lists.
+    Selection equals the oracle's top-k of the GPU's own scores."""
+    w = W.custom_workload(B=1, Hq=4, Hkv=1, d=128, N=600000, dtype="bf16", L=32, P=8,
+                          tau=0.3, k=500, lognormal_v=True, name="many_sub_lists")
+    log(f"decode many sub-lists with_rows={with_rows}")
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=15)
+    ids, vn = S.hash_keys(K, V, R, w.L, w.P)
+    idx = torch.empty((1, 4, w.kk), dtype=torch.int32, device=DEV)
+    sc = torch.empty((1, 4, w.N), dtype=torch.float32, device=DEV) if with_rows else None
+    S.decode(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, idx_out=idx, scores_out=sc)
+    table = S.bucket_probs(Q, R, w.Hkv, w.L, w.P, w.tau)
+    sc_ref = S.score(table, ids, vn, w.Hq)
+    torch.cuda.synchronize()
+    if with_rows:
+        assert torch.equal(sc, sc_ref)
+    s_np, idx_np = sc_ref.cpu().numpy(), idx.cpu().numpy()
+    for h in range(4):
+        assert np.array_equal(idx_np[0, h], O.topk_indices(s_np[0, h], w.k)), f"head {h}"
