@@ -737,6 +737,9 @@ template <int G, int LW>
 struct RotScorer {
   static constexpr int L = LW * 4;
   static constexpr int kChunk = 64 / G;  // lookups per dependency step (a multiple of 4)
+  // the kernels planned with two resident 1024-thread blocks per CU, which
+  // must stay within 64 VGPRs (see plan_score)
+  static constexpr bool kTwoPerCU = (G == 1 && LW <= 8) || (G <= 4 && LW <= 4);
   __amdgpu_buffer_rsrc_t idseg, vseg;  // the segment's id rows and norms
   const float* tab;
   int P, we, wb;
@@ -799,19 +802,58 @@ struct RotScorer {
 #pragma unroll
     for (int j = 0; j < G; ++j) acc[j] = 0.f;
     if (!valid) return;
+    if constexpr (kTwoPerCU) {
+      // one lookup at a time (the registers of two resident blocks per CU;
+      // their 32 waves keep the LDS busy)
 #pragma unroll
-    for (int t = 0; t < L; ++t) {
-      // P bits of byte t: ids are < 2^P, so this never leaves the table
-      const uint32_t u = __builtin_amdgcn_ubfe(w[t >> 2], (t & 3) * 8, P);
-      const int off = (t + 15 < L) ? base_nowrap : (t + r < L ? base_nowrap : base_wrap);
-      float pr[G];
-      lds_load_group<G>(tab + (int)u * (L * G) + off + t * G, pr);
+      for (int t = 0; t < L; ++t) {
+        // P bits of byte t: ids are < 2^P, so this never leaves the table
+        const uint32_t u = __builtin_amdgcn_ubfe(w[t >> 2], (t & 3) * 8, P);
+        const int off = (t + 15 < L) ? base_nowrap : (t + r < L ? base_nowrap : base_wrap);
+        float pr[G];
+        lds_load_group<G>(tab + (int)u * (L * G) + off + t * G, pr);
 #pragma unroll
-      for (int j = 0; j < G; ++j) acc[j] = t == 0 ? pr[j] : acc[j] + pr[j];
+        for (int j = 0; j < G; ++j) acc[j] = t == 0 ? pr[j] : acc[j] + pr[j];
+        // the next kChunk lookups wait for these sums: at most 64 floats
+        // of lookups in flight per lane, which bounds the registers
+        if ((t + 1) % kChunk == 0 && t + 1 < L)
+          fence_chunk<G, LW>(acc, w, (t + 1) / 4, std::min(LW, (t + 1 + kChunk) / 4));
+      }
+      return;
+    }
+    // Lookups in batches of kBatch (16 floats): batch b + 1 is requested
+    // before batch b is added (left to itself the compiler issues each read
+    // right before its add, one read in flight per wave); the sums stay in
+    // table order.
+    constexpr int kBatch = 16 / G, NB = L / kBatch;
+    float pr[2][kBatch * G];
+    auto request = [&](int b) {
+#pragma unroll
+      for (int s = 0; s < kBatch; ++s) {
+        const int t = b * kBatch + s;
+        // P bits of byte t: ids are < 2^P, so this never leaves the table
+        const uint32_t u = __builtin_amdgcn_ubfe(w[t >> 2], (t & 3) * 8, P);
+        const int off = (t + 15 < L) ? base_nowrap : (t + r < L ? base_nowrap : base_wrap);
+        lds_load_group<G>(tab + (int)u * (L * G) + off + t * G,
+                          *reinterpret_cast<float(*)[G]>(&pr[b & 1][s * G]));
+      }
+    };
+    request(0);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b + 1 < NB) request(b + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < kBatch; ++s)
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+          acc[j] = b + s == 0 ? pr[b & 1][s * G + j] : acc[j] + pr[b & 1][s * G + j];
       // the next kChunk lookups wait for these sums: at most 64 floats
       // of lookups in flight per lane, which bounds the registers
+      const int t = b * kBatch + kBatch - 1;
       if ((t + 1) % kChunk == 0 && t + 1 < L)
         fence_chunk<G, LW>(acc, w, (t + 1) / 4, std::min(LW, (t + 1 + kChunk) / 4));
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 };
