@@ -937,26 +937,45 @@ struct RegionScorer {
 #pragma unroll
     for (int j = 0; j < G; ++j) acc[j] = 0.f;
     if (!valid) return;
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    // lookups in batches of kBatch, batch b + 1 requested before batch b is
+    // added (as in RotScorer); the sums stay in table order
+    constexpr int kBatch = 4, NB = L / kBatch;
+    f32x4_t pr[2][kBatch];
+    auto request = [&](int b) {
 #pragma unroll
-    for (int t = 0; t < L; ++t) {
-      // byte selectors: 0-3 pick bytes of the slot word, 4-7 bytes of the
-      // id word, 0x0c gives 0
-      const uint32_t addr =
-          t < 16 ? __builtin_amdgcn_perm(w[t >> 2], slot0[(t & 15) >> 2],
-                                         0x0c0c0000u | ((4u + (t & 3)) << 8) | (uint32_t)(t & 3))
-                 : __builtin_amdgcn_perm(w[t >> 2], slot1[(t & 15) >> 1],
-                                         0x0c020000u | ((4u + (t & 3)) << 8) | (uint32_t)(t & 1));
-      // the table is the block's dynamic LDS, which starts at LDS address 0
-      // (the kernel has no static LDS; the host checks it before launching
-      // this scorer): addr is the slot's absolute LDS address
-      typedef float f32x4_t __attribute__((ext_vector_type(4)));
-      const f32x4_t x = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(
-          (uintptr_t)addr);
-      const float pr[G] = {x.x, x.y, x.z, x.w};
+      for (int s = 0; s < kBatch; ++s) {
+        const int t = b * kBatch + s;
+        // byte selectors: 0-3 pick bytes of the slot word, 4-7 bytes of the
+        // id word, 0x0c gives 0
+        const uint32_t addr =
+            t < 16 ? __builtin_amdgcn_perm(w[t >> 2], slot0[(t & 15) >> 2],
+                                           0x0c0c0000u | ((4u + (t & 3)) << 8) | (uint32_t)(t & 3))
+                   : __builtin_amdgcn_perm(w[t >> 2], slot1[(t & 15) >> 1],
+                                           0x0c020000u | ((4u + (t & 3)) << 8) | (uint32_t)(t & 1));
+        // the table is the block's dynamic LDS, which starts at LDS address 0
+        // (the kernel has no static LDS; the host checks it before launching
+        // this scorer): addr is the slot's absolute LDS address
+        pr[b & 1][s] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(
+            (uintptr_t)addr);
+      }
+    };
+    request(0);
 #pragma unroll
-      for (int j = 0; j < G; ++j) acc[j] = t == 0 ? pr[j] : acc[j] + pr[j];
+    for (int b = 0; b < NB; ++b) {
+      if (b + 1 < NB) request(b + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < kBatch; ++s) {
+        const f32x4_t x = pr[b & 1][s];
+        const float p4[G] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int j = 0; j < G; ++j) acc[j] = b + s == 0 ? p4[j] : acc[j] + p4[j];
+      }
+      const int t = b * kBatch + kBatch - 1;
       if ((t + 1) % kChunk == 0 && t + 1 < L)
         fence_chunk<G, LW>(acc, w, (t + 1) / 4, std::min(LW, (t + 1 + kChunk) / 4));
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 };
