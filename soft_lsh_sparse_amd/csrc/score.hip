@@ -803,21 +803,32 @@ struct RotScorer {
     for (int j = 0; j < G; ++j) acc[j] = 0.f;
     if (!valid) return;
     if constexpr (kTwoPerCU) {
-      // one lookup at a time (the registers of two resident blocks per CU;
-      // their 32 waves keep the LDS busy)
+      // batches of 4 floats, each requested whole before it is added (the
+      // registers of two resident blocks per CU; their 32 waves keep the
+      // LDS busy)
+      constexpr int kB = G >= 4 ? 1 : 4 / G;
 #pragma unroll
-      for (int t = 0; t < L; ++t) {
-        // P bits of byte t: ids are < 2^P, so this never leaves the table
-        const uint32_t u = __builtin_amdgcn_ubfe(w[t >> 2], (t & 3) * 8, P);
-        const int off = (t + 15 < L) ? base_nowrap : (t + r < L ? base_nowrap : base_wrap);
-        float pr[G];
-        lds_load_group<G>(tab + (int)u * (L * G) + off + t * G, pr);
+      for (int t0 = 0; t0 < L; t0 += kB) {
+        float pr[kB][G];
 #pragma unroll
-        for (int j = 0; j < G; ++j) acc[j] = t == 0 ? pr[j] : acc[j] + pr[j];
+        for (int s = 0; s < kB; ++s) {
+          const int t = t0 + s;
+          // P bits of byte t: ids are < 2^P, so this never leaves the table
+          const uint32_t u = __builtin_amdgcn_ubfe(w[t >> 2], (t & 3) * 8, P);
+          const int off = (t + 15 < L) ? base_nowrap : (t + r < L ? base_nowrap : base_wrap);
+          lds_load_group<G>(tab + (int)u * (L * G) + off + t * G, pr[s]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < kB; ++s)
+#pragma unroll
+          for (int j = 0; j < G; ++j) acc[j] = t0 + s == 0 ? pr[s][j] : acc[j] + pr[s][j];
         // the next kChunk lookups wait for these sums: at most 64 floats
         // of lookups in flight per lane, which bounds the registers
+        const int t = t0 + kB - 1;
         if ((t + 1) % kChunk == 0 && t + 1 < L)
           fence_chunk<G, LW>(acc, w, (t + 1) / 4, std::min(LW, (t + 1 + kChunk) / 4));
+        __builtin_amdgcn_sched_barrier(0);
       }
       return;
     }
