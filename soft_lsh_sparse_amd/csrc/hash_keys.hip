@@ -477,7 +477,7 @@ __global__ __launch_bounds__(256) void hash_prep_kernel(const uint16_t* __restri
 // float64 sum of the group decides the sign unless it is within the
 // rounding bound of the sum of |products| (then double-double decides).
 // The bit is set or cleared with an atomic on its 32-bit word.
-constexpr int kFixBlocksPerPart = 16;
+constexpr int kFixBlocksPerPart = 8;
 
 template <int D>
 __device__ __forceinline__ void hash_fixup_block(
