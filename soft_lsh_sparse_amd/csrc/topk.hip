@@ -609,7 +609,9 @@ __global__ __launch_bounds__(kGatherThreads) void topk_gather_kernel(SelectArgs 
   for (int q = 0; q < Q; ++q) {
     const int sl = Q * wave + q;
     len[q] = bc[sl];  // 0 past the row's last sub-list
-    src[q] = a.lists + (int64_t)row * a.n + (int64_t)min(s0 + sl, a.subs - 1) * a.sub_len;
+    // (an empty sub-list may start past the row's end, e.g. in the last,
+    // partial segment: its slot stands in for it, read but not used)
+    src[q] = a.lists + (int64_t)row * a.n + (len[q] > 0 ? (int64_t)(s0 + sl) * a.sub_len : 0);
     dst[q] = a.spill + sr.start + off;
     off += len[q];
   }

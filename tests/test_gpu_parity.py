@@ -966,3 +966,25 @@ def test_decode_many_sub_lists(with_rows):
     s_np, idx_np = sc_ref.cpu().numpy(), idx.cpu().numpy()
     for h in range(4):
         assert np.array_equal(idx_np[0, h], O.topk_indices(s_np[0, h], w.k)), f"head {h}"
+
+
+@pytest.mark.parametrize("N", [6145, 8191])
+def test_decode_gathered_ragged_last_segment(N):
+    """One query head, k = 6000 (the candidates are gathered): the last score
+    block holds a few keys only, so most of its waves' sub-lists are empty
+    and start past the row's end; nothing may be read there. Selection
+    equals the oracle's top-k of the GPU's own scores, with and without
+    score rows."""
+    w = W.custom_workload(B=1, Hq=1, Hkv=1, d=128, N=N, dtype="bf16", L=32, P=8,
+                          tau=0.3, k=6000, lognormal_v=True, name="gathered_tail")
+    log(f"decode gathered ragged last segment N={N}")
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=16)
+    ids, vn = S.hash_keys(K, V, R, w.L, w.P)
+    idx = torch.empty((1, 1, w.kk), dtype=torch.int32, device=DEV)
+    sc = torch.empty((1, 1, N), dtype=torch.float32, device=DEV)
+    S.decode(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, idx_out=idx, scores_out=sc)
+    idx2 = torch.empty_like(idx)
+    S.decode(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, idx_out=idx2)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    assert np.array_equal(idx.cpu().numpy()[0, 0], O.topk_indices(sc.cpu().numpy()[0, 0], w.k))
