@@ -513,6 +513,8 @@ socket_status decode_impl(const void* Q, const void* K, const void* V,
     sa.kk = kk;
     sa.subs = lay.score.subs;
     sa.sub_len = lay.score.sub_len;
+    sa.skew0 = lay.score.skew0;
+    sa.skew1 = lay.score.skew1;
     sa.segs = lay.score.segs;
     sa.thr = thr;
     sa.lists = lists;
@@ -644,6 +646,8 @@ socket_status decode_group_impl(const void* Q, const void* K, const void* V, con
     sa.kk = kk;
     sa.subs = lay.head.score.subs;
     sa.sub_len = lay.head.score.sub_len;
+    sa.skew0 = lay.head.score.skew0;
+    sa.skew1 = lay.head.score.skew1;
     sa.segs = lay.head.score.segs;
     sa.thr = thr;
     sa.lists = lists;

@@ -61,14 +61,35 @@ hipError_t launch_bucket_probs(const void* Q, const void* R, bool bf16, int B,
 
 // ------------------------------------------------------------------ score
 // Launch geometry of the score kernel: segs blocks per (batch, KV head) of
-// seg_len keys each; every block's 16 waves own sub_len consecutive keys
-// (subs = segs * 16 sub-lists per row when emitting candidates).
+// seg_len keys each; every block's 16 waves own consecutive keys, sub_len
+// of them on average (subs = segs * 16 sub-lists per row when emitting
+// candidates). The shares are unequal: each SIMD serves its oldest wave
+// first, so with equal shares waves 0-3 finish first and waves 12-15 last,
+// each group of four a few percent of the block's time after the one
+// before. Waves 4g..4g+3 therefore take sub_len + {skew0, skew1, -skew1,
+// -skew0}[g] keys (multiples of 128), which evens out their finish times.
 struct ScoreGeom {
   int segs;
   int64_t seg_len;
   int subs;
   int64_t sub_len;
+  int skew0, skew1;
 };
+// Sub-list s (= 16 * segment + wave) of a row: its keys start at
+// sub_begin(s, ...) and number sub_size(s, ...) (fewer in a last, partial
+// segment), and its candidates are stored from the same position.
+__host__ __device__ inline int64_t sub_begin(int s, int64_t sub_len, int skew0, int skew1) {
+  // wave w = 4g + i starts A(w) * skew0 + B(w) * skew1 past w * sub_len:
+  // A = i, 4, 4, 4 - i and B = 0, i, 4 - i, 0 for g = 0..3 (4-bit fields)
+  const int w = s & 15;
+  const int a = (int)((0x1234444444443210ull >> (4 * w)) & 15u);
+  const int b = (int)((0x0000123432100000ull >> (4 * w)) & 15u);
+  return (int64_t)s * sub_len + a * skew0 + b * skew1;
+}
+__host__ __device__ inline int64_t sub_size(int s, int64_t sub_len, int skew0, int skew1) {
+  const int g = (s & 15) >> 2;
+  return sub_len + (g == 0 ? skew0 : g == 1 ? skew1 : g == 2 ? -skew1 : -skew0);
+}
 ScoreGeom plan_score(int bhkv, int64_t n_keys, int L, int P, int G);
 // GQA packing. When the probability table of a whole group (2^P * L * G
 // floats) does not fit a score block's LDS, each block scores Gp of the G
@@ -113,8 +134,8 @@ hipError_t launch_score(const float* table, int table_G, const uint8_t* ids, con
 // Decode path: every block estimates a per-row threshold from its first
 // keys (thr[row * segs + seg], an order key) and appends every key whose
 // score's order key reaches it, as (float32 score bits, index), to sub-list (row, s)
-// at lists[row * n_keys + s * sub_len], in index order; sub_cnt[row * subs +
-// s] receives the sub-list's length.
+// at lists[row * n_keys + sub_begin(s, ...)], in index order; sub_cnt[row *
+// subs + s] receives the sub-list's length.
 struct ScoreSelect {
   const float* table;  // [B*Hkv, 2^P, L, G] over virtual heads (written by the kernel with build)
   int id_div;          // virtual head v reads the ids and norms of head v / id_div
@@ -157,6 +178,7 @@ struct SelectArgs {
   int64_t n, kk;              // kk < n
   int subs;                   // <= kMaxSelectSubLists
   int64_t sub_len;
+  int skew0, skew1;           // sub-list s at sub_begin(s, sub_len, skew0, skew1)
   int segs;
   const uint32_t* thr;        // [rows][segs]
   const uint2* lists;

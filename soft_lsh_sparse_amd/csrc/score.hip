@@ -232,12 +232,13 @@ struct ScoreArgs {
   int id_div;          // virtual head bg reads the ids and norms of head bg / id_div
   int table_G;         // heads per table slot (G, or the whole group when packing a stage call)
   int64_t n_keys, stride, seg_len;
+  int skew0, skew1;    // unequal wave shares (sub_begin)
   float* scores;       // [rows][n_keys] or null
   // candidate emission (decode path)
   int select;
   int64_t kk;
   uint32_t* thr;       // [rows][segs] block thresholds (order keys)
-  uint2* lists;        // [rows][n_keys]; sub-list s at s * seg_len / 16
+  uint2* lists;        // [rows][n_keys]; sub-list s at sub_begin(s, seg_len / 16, ...)
   uint32_t* sub_cnt;   // [rows][segs * 16]
   // table built in the kernel: bf16 query rows [B][Hq][d] and hyperplanes
   // [d][L*P]; the built table is also stored to table_out when given
@@ -290,21 +291,31 @@ __device__ __forceinline__ float threshold_float(uint32_t thr) {
   return __uint_as_float(thr >= 0x80000000u ? (thr & 0x7fffffffu) : ~thr);
 }
 
-// Keys [n0 + wb, n0 + we) of this block's segment belong to this wave.
+// Keys [n0 + wb, n0 + we) of this block's segment belong to this wave:
+// its share (wlen keys, unequal across the waves) of the segment, cut at
+// the row's end.
 struct WaveRange {
   int64_t n0;
   int cnt, wlen, wb, we;
-  __device__ WaveRange(const ScoreArgs& a, int seg) {
+  int sub_len, skew0, skew1;
+  __device__ WaveRange(const ScoreArgs& a, int seg)
+      : sub_len((int)(a.seg_len / kScoreWaves)), skew0(a.skew0), skew1(a.skew1) {
     n0 = seg * a.seg_len;
     cnt = (int)(min(a.n_keys, n0 + a.seg_len) - n0);
-    wlen = (int)(a.seg_len / kScoreWaves);
-    wb = (int)(threadIdx.x >> 6) * wlen;
+    // (wave-uniform: in scalar registers, as the sub-list buffers need)
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    wb = (int)sub_begin(w, sub_len, skew0, skew1);
+    wlen = (int)sub_size(w, sub_len, skew0, skew1);
     we = min(cnt, wb + wlen);
   }
   // keys in the first step (kWaveStep keys) of every wave of the block
   __device__ int first_step_keys() const {
     int n = 0;
-    for (int w = 0; w < kScoreWaves; ++w) n += max(0, min(kWaveStep, cnt - w * wlen));
+    for (int w = 0; w < kScoreWaves; ++w) {
+      const int b = (int)sub_begin(w, sub_len, skew0, skew1);
+      const int e = min(cnt, b + (int)sub_size(w, sub_len, skew0, skew1));
+      n += max(0, min(kWaveStep, e - b));
+    }
     return n;
   }
 };
@@ -1142,6 +1153,8 @@ ScoreArgs base_args(const float* table, int table_G, const uint8_t* ids, const f
   a.P = P;
   a.segs = geo.segs;
   a.seg_len = geo.seg_len;
+  a.skew0 = geo.skew0;
+  a.skew1 = geo.skew1;
   a.n_keys = n_keys;
   a.stride = stride;
   return a;
@@ -1224,6 +1237,15 @@ ScoreGeom plan_score(int bhkv, int64_t n_keys, int L, int P, int G) {
   geo.seg_len = seg_len;
   geo.subs = (int)(segs * kScoreWaves);
   geo.sub_len = seg_len / kScoreWaves;
+  // unequal wave shares, in steps of kWaveStep keys out of S per wave. With
+  // 64 tables (16 steps per wave at 1M keys) the last group of four waves
+  // finished 27 us, about 7 steps' worth, after the first; shares {S+3,
+  // S+1, S-1, S-3} leave ~5 us and take 8 us off the kernel. With 32
+  // tables the groups end within ~3.6 us of each other and one step of
+  // skew made the kernel slower (no skew there).
+  const int S = (int)(geo.sub_len / kWaveStep);
+  geo.skew0 = L >= 64 ? (S * 3 + 8) / 16 * kWaveStep : 0;
+  geo.skew1 = L >= 64 ? S / 16 * kWaveStep : 0;
   return geo;
 }
 

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_hist_kernel(
 // per lane, so finding the next one's sub-list takes a step or two forward
 // (a binary search only when a loop starts over).
 struct RowLists {
-  const uint2* glob;      // row's list area (sub-list s at s * sub_len)
+  const uint2* glob;      // row's list area (sub-list s at sub_begin(s, ...))
   const uint2* cache;     // LDS copy of the first `cached` entries (order keys)
   uint32_t cached;
   const uint32_t* off;    // sub-list offsets in the concatenation (LDS)
@@ -77,6 +77,7 @@ struct RowLists {
   int64_t sub_len;
   bool score_bits;        // glob holds (score bits, index): map to order keys
   bool raw_cache;         // so does the LDS copy
+  int skew0 = 0, skew1 = 0;
   mutable int cur = -1;   // sub-list of the last position read from memory
   // element index in glob of position p (moves the cursor)
   __device__ __forceinline__ int64_t locate(uint32_t p) const {
@@ -89,7 +90,7 @@ struct RowLists {
       cur = lo;
     }
     while (cur + 1 < subs && off[cur + 1] <= p) ++cur;
-    return (int64_t)cur * sub_len + (p - off[cur]);
+    return sub_begin(cur, sub_len, skew0, skew1) + (p - off[cur]);
   }
   __device__ __forceinline__ uint2 from_memory(uint32_t p) const {
     uint2 e = glob[locate(p)];
@@ -162,7 +163,7 @@ __device__ uint32_t sublist_offsets(const uint32_t* cnt, int subs, uint32_t* off
 // fetches eight entries (located by binary search over the offsets) before
 // storing any, so the loads overlap.
 template <int NT>
-__device__ void cache_candidates(RowLists& rl, uint2* cache, uint32_t total) {
+__device__ __forceinline__ void cache_candidates(RowLists& rl, uint2* cache, uint32_t total) {
   const uint32_t cached = min(total, (uint32_t)kRefineCache);
   constexpr int kBatch = 8;
   for (uint32_t base = 0; base < cached; base += kBatch * NT) {
@@ -611,7 +612,8 @@ __global__ __launch_bounds__(kGatherThreads) void topk_gather_kernel(SelectArgs 
     len[q] = bc[sl];  // 0 past the row's last sub-list
     // (an empty sub-list may start past the row's end, e.g. in the last,
     // partial segment: its slot stands in for it, read but not used)
-    src[q] = a.lists + (int64_t)row * a.n + (len[q] > 0 ? (int64_t)(s0 + sl) * a.sub_len : 0);
+    src[q] = a.lists + (int64_t)row * a.n +
+             (len[q] > 0 ? sub_begin(s0 + sl, a.sub_len, a.skew0, a.skew1) : 0);
     dst[q] = a.spill + sr.start + off;
     off += len[q];
   }
@@ -751,7 +753,8 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
   const bool gathered = a.spill != nullptr && total <= sr.cap;  // block-uniform
   const uint32_t cached = min(total, (uint32_t)kRefineCache);
   unsigned char* cache_bytes = reinterpret_cast<unsigned char*>(sh.cache);
-  const RowLists rl{glob, sh.cache, cached, sh.off, a.subs, a.sub_len, true, false};
+  const RowLists rl{glob,      sh.cache, cached, sh.off,  a.subs,
+                    a.sub_len, true,     false,  a.skew0, a.skew1};
   const int tps = a.subs <= NT ? NT / a.subs : 1;  // threads per sub-list (short lists)
   uint32_t umax = 0;
   if (gathered) {
@@ -777,7 +780,7 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
     for (int t = threadIdx.x; t < a.subs * tps; t += NT) {
       const int sl = t / tps, r = t - sl * tps;
       const uint32_t o0 = sh.off[sl], n = sh.off[sl + 1] - o0;
-      const uint2* src = glob + (int64_t)sl * a.sub_len;
+      const uint2* src = glob + sub_begin(sl, a.sub_len, a.skew0, a.skew1);
       for (uint32_t j0 = r; j0 < n; j0 += tps * kShortBatch) {
         uint2 e[kShortBatch];
 #pragma unroll
@@ -816,7 +819,8 @@ __global__ __launch_bounds__(kRefineThreads) void topk_select_kernel(SelectArgs 
         const uint32_t o1 = min((uint32_t)__builtin_amdgcn_readlane((int)offv, k + 1), cached);
         const uint32_t dws = 2u * (o1 - o0);
         const uint32_t* src =
-            reinterpret_cast<const uint32_t*>(glob + (int64_t)(k0 + k) * a.sub_len);
+            reinterpret_cast<const uint32_t*>(glob + sub_begin(k0 + k, a.sub_len, a.skew0,
+                                                                 a.skew1));
         for (uint32_t d0 = 0; d0 < dws; d0 += 64) {  // wave-uniform
           if (d0 + lane < dws)
             __builtin_amdgcn_global_load_lds(

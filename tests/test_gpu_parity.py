@@ -968,6 +968,35 @@ def test_decode_many_sub_lists(with_rows):
         assert np.array_equal(idx_np[0, h], O.topk_indices(s_np[0, h], w.k)), f"head {h}"
 
 
+@pytest.mark.parametrize("N,k", [(2097152, 4096), (2092000, 500), (2092000, 16384)])
+def test_decode_unequal_wave_shares(N, k):
+    """64 tables, one KV head of about 2M keys: 256 score blocks of 8192
+    keys, whose 16 waves take unequal shares of 640, 512, 512 and 384 keys
+    (waves 0-3, 4-7, 8-11, 12-15). With N = 2092000 the last block holds
+    3000 keys, cut inside wave 4's share. Every score is written once (the
+    score rows equal socket_score's) and the selection, from short
+    sub-lists (k = 500) or gathered candidates (k = 16384), equals the
+    oracle's top-k of the GPU's own scores."""
+    w = W.custom_workload(B=1, Hq=4, Hkv=1, d=128, N=N, dtype="bf16", L=64, P=6,
+                          tau=0.2, k=k, lognormal_v=True, name="unequal_shares")
+    log(f"decode unequal wave shares N={N} k={k}")
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=17)
+    ids, vn = S.hash_keys(K, V, R, w.L, w.P)
+    idx = torch.empty((1, 4, w.kk), dtype=torch.int32, device=DEV)
+    sc = torch.empty((1, 4, w.N), dtype=torch.float32, device=DEV)
+    S.decode(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, idx_out=idx, scores_out=sc)
+    idx2 = torch.empty_like(idx)
+    S.decode(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, idx_out=idx2)
+    table = S.bucket_probs(Q, R, w.Hkv, w.L, w.P, w.tau)
+    sc_ref = S.score(table, ids, vn, w.Hq)
+    torch.cuda.synchronize()
+    assert torch.equal(sc, sc_ref)
+    assert torch.equal(idx, idx2)
+    s_np, idx_np = sc_ref.cpu().numpy(), idx.cpu().numpy()
+    for h in range(4):
+        assert np.array_equal(idx_np[0, h], O.topk_indices(s_np[0, h], w.k)), f"head {h}"
+
+
 @pytest.mark.parametrize("N", [6145, 8191])
 def test_decode_gathered_ragged_last_segment(N):
     """One query head, k = 6000 (the candidates are gathered): the last score
