@@ -211,10 +211,15 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
 }
 
 constexpr int kMergeMaxChunks = 1024;
+constexpr int kMergeRegChunks = 16;
 
 // Online-softmax merge of the chunk partials of one row, in chunk order.
-// All (m, l) pairs are staged in LDS first; the accumulator loads of the
-// chunks are independent, so they are issued back to back.
+// Up to kMergeRegChunks chunks (the sparse decode's 4-16): every thread
+// requests the (m, l) pair and its coordinate of every chunk at once, one
+// memory round trip, and merges them itself. More chunks (the dense
+// baseline): the (m, l) pairs are staged in LDS first, then the
+// accumulator loads, which are independent, are issued back to back. Both
+// take the same steps in the same order, so their results are equal.
 template <typename T, int D>
 __global__ __launch_bounds__(D) void attn_merge_kernel(
     const float* __restrict__ partial, int chunks,
@@ -225,6 +230,30 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(
   const int64_t row = blockIdx.x;
   const float* p = partial + row * chunks * (D + 2);
   const int t = threadIdx.x;
+  if (chunks <= kMergeRegChunks) {  // block-uniform
+    float m[kMergeRegChunks], l[kMergeRegChunks], a[kMergeRegChunks];
+#pragma unroll
+    for (int c = 0; c < kMergeRegChunks; ++c) {
+      const float* pc = p + (int64_t)min(c, chunks - 1) * (D + 2);
+      m[c] = pc[D];
+      l[c] = pc[D + 1];
+      a[c] = pc[t];
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < kMergeRegChunks; ++c)
+      if (c < chunks) mt = fmaxf(mt, m[c]);
+    float lt = 0.f, at = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMergeRegChunks; ++c)
+      if (c < chunks) {
+        const float w = m[c] == -INFINITY ? 0.f : expf(m[c] - mt);
+        lt = fmaf(w, l[c], lt);
+        at = fmaf(w, a[c], at);
+      }
+    T::store(out, row * D + t, at / lt);
+    return;
+  }
   for (int c = t; c < chunks; c += D) {
     sw[c] = p[c * (D + 2) + D];
     sl[c] = p[c * (D + 2) + D + 1];
