@@ -172,10 +172,10 @@ socket_status socket_hard_bucket_table(const void* Q, const void* R, socket_dtyp
  * The L probabilities are summed in float32 in a fixed order, then
  * multiplied by the value norm. With r = key index mod 16, when L is 16, 32
  * or 64 and the id rows are 16-byte aligned (this spreads LDS banks): for
- * P = 8, 32 or 16 tables and 4 query heads per block, table
- * 16c + (t + r) mod 16 at step 16c + t (t < 16: each run of 16 tables
- * rotated on its own); otherwise l = (t + r) mod L at step t. In all other
- * cases l = t.
+ * 4 query heads per block with P = 8 and 32 or 16 tables, or P = 6 and 64
+ * tables, table 16c + (t + r) mod 16 at step 16c + t (t < 16: each run of
+ * 16 tables rotated on its own); otherwise l = (t + r) mod L at step t. In
+ * all other cases l = t.
  */
 socket_status socket_score(const float* table, const uint8_t* ids,
                            const float* vnorm, int32_t B, int32_t Hq,

@@ -104,8 +104,8 @@ int score_pack(int L, int P, int G);
 // l = 16 c + (t' + r) mod 16 for t = 16 c + t' (each 16-table region
 // rotated on its own); else l = t
 bool score_rotated(const uint8_t* ids, int64_t stride, int L);
-// The rotated path keeps the table in 16-table regions (G = 4, P = 8,
-// L = 16 or 32).
+// The rotated path keeps the table in 16-table regions (G = 4; P = 8 with
+// L = 16 or 32, P = 6 with L = 64).
 bool score_region(int G, int P, int L);
 // LDS bytes of one score block (build: the block builds its table).
 size_t score_lds_bytes(int L, int P, int G, bool build);

@@ -154,12 +154,13 @@ __device__ __forceinline__ bool score_block_coords(int bhkv, int segs, int& bg,
   return true;
 }
 
-// Region layout of the LDS table (G = 4 query heads, P = 8, L = 16 or 32,
-// the rotated scorer): tables 16c .. 16c + 15 form region c at byte 65536 c;
-// in it, bucket u takes 256 bytes, 16 table slots of 16 bytes (the 4 heads'
-// probabilities). Float index of entry (u, l, j):
-__host__ __device__ __forceinline__ int region_index(int u, int l, int j) {
-  return (l >> 4) * 16384 + u * 64 + (l & 15) * 4 + j;
+// Region layout of the LDS table (G = 4 query heads, the rotated scorer;
+// P = 8 with L = 16 or 32, P = 6 with L = 64): tables 16c .. 16c + 15 form
+// region c at byte 2^P * 256 * c; in it, bucket u takes 256 bytes, 16 table
+// slots of 16 bytes (the 4 heads' probabilities). Float index of entry
+// (u, l, j):
+__host__ __device__ __forceinline__ int region_index(int u, int l, int j, int P) {
+  return (l >> 4) * (64 << P) + u * 64 + (l & 15) * 4 + j;
 }
 
 // The table of batch*KV head bg into LDS ([u][l][j], or the region layout
@@ -178,7 +179,7 @@ __device__ __forceinline__ void stage_table(float* tab, const float* table, int 
                        (bg % id_div) * G;
     for (int i = threadIdx.x; i < tsize; i += blockDim.x) {
       const int u = i / (L * G), l = (i / G) % L, j = i % G;
-      tab[REGION ? region_index(u, l, j) : i] = src[(int64_t)(i / G) * table_G + j];
+      tab[REGION ? region_index(u, l, j, P) : i] = src[(int64_t)(i / G) * table_G + j];
     }
   } else if (REGION) {
     // direct-to-LDS loads into the region layout: LDS slot f (16 bytes) of
@@ -194,7 +195,7 @@ __device__ __forceinline__ void stage_table(float* tab, const float* table, int 
       const int f0 = rr * per_round + (int)(threadIdx.x & ~63);  // wave-uniform
       const int f = f0 + lane;
       if (f0 < n4 && f < n4) {
-        const int c = f >> 12, u = (f >> 4) & 255, sl = f & 15;
+        const int c = f >> (P + 4), u = (f >> 4) & ((1 << P) - 1), sl = f & 15;
         __builtin_amdgcn_global_load_lds(
             (const void*)(src + u * L + c * 16 + sl),
             (__attribute__((address_space(3))) void*)(tab + (size_t)f0 * 4), 16, 0, 0);
@@ -555,7 +556,7 @@ __device__ __forceinline__ void store_table_share(const float* tab, const ScoreA
   const float4* src = reinterpret_cast<const float4*>(tab);
   for (int i = seg * per + (int)threadIdx.x; i < s1; i += kScoreThreads) {
     // slot i = u * L + l of the [u][l][j] layout the select kernel reads
-    dst[i] = REGION ? src[region_index(i / a.L, i % a.L, 0) / 4] : src[i];
+    dst[i] = REGION ? src[region_index(i / a.L, i % a.L, 0, a.P) / 4] : src[i];
   }
 }
 
@@ -880,20 +881,23 @@ struct RotScorer {
   }
 };
 
-// Rotated scorer over the region layout (G = 4 query heads, P = 8, L = 16
-// or 32): lane key n walks the 16 tables of each region c in the order
-// 16c + (t + r) mod 16, r = n mod 16 (the key's id row is rotated by r
-// bytes within each 16-byte half), so the 16 lanes the LDS serves together
-// hit 16 bank groups. One v_perm_b32 forms a lookup's LDS byte address
-// 65536 c + 256 u + 16 s: byte 1 the (rotated) id byte u, byte 0 the lane's
-// slot s = (t + r) mod 16 times 16 from a per-lane constant, byte 2 the
-// region bit from another constant (0 for region 0).
-template <int LW>
+// Rotated scorer over the region layout (G = 4 query heads; P = 8 with
+// L = 16 or 32, P = 6 with L = 64): lane key n walks the 16 tables of each
+// region c in the order 16c + (t + r) mod 16, r = n mod 16 (the key's id
+// row is rotated by r bytes within each 16-byte half), so the 16 lanes the
+// LDS serves together hit 16 bank groups. One v_perm_b32 forms a lookup's
+// LDS byte address 2^P * 256 * c + 256 u + 16 s: byte 1 the (rotated) id
+// byte u, byte 0 the lane's slot s = (t + r) mod 16 times 16 from a
+// per-lane constant; the region base is, for P = 8, byte 2 from another
+// constant (65536 for region 1), for P = 6 the read's immediate offset
+// (16384 c).
+template <int LW, int P>
 struct RegionScorer {
   static constexpr int G = 4;
   static constexpr int L = LW * 4;
   static constexpr int kChunk = 64 / G;  // lookups per dependency step
-  static_assert(LW == 4 || LW == 8, "16 or 32 tables");
+  static_assert((P == 8 && (LW == 4 || LW == 8)) || (P == 6 && LW == 16),
+                "P = 8 with 16 or 32 tables, P = 6 with 64 tables");
   __amdgpu_buffer_rsrc_t idseg, vseg;
   const float* tab;
   int we, wb;
@@ -959,6 +963,12 @@ struct RegionScorer {
 #pragma unroll
     for (int j = 0; j < G; ++j) acc[j] = 0.f;
     if (!valid) return;
+    if constexpr (P < 8) {
+      // P bits of every id byte: ids are < 2^P, so this never leaves the
+      // region (as the other scorers, which take P bits)
+#pragma unroll
+      for (int k = 0; k < LW; ++k) w[k] &= 0x01010101u * ((1u << P) - 1u);
+    }
     typedef float f32x4_t __attribute__((ext_vector_type(4)));
     // lookups in batches of kBatch, batch b + 1 requested before batch b is
     // added (as in RotScorer); the sums stay in table order
@@ -970,11 +980,14 @@ struct RegionScorer {
         const int t = b * kBatch + s;
         // byte selectors: 0-3 pick bytes of the slot word, 4-7 bytes of the
         // id word, 0x0c gives 0
-        const uint32_t addr =
-            t < 16 ? __builtin_amdgcn_perm(w[t >> 2], slot0[(t & 15) >> 2],
-                                           0x0c0c0000u | ((4u + (t & 3)) << 8) | (uint32_t)(t & 3))
-                   : __builtin_amdgcn_perm(w[t >> 2], slot1[(t & 15) >> 1],
-                                           0x0c020000u | ((4u + (t & 3)) << 8) | (uint32_t)(t & 1));
+        uint32_t addr;
+        if (P < 8 || t < 16)
+          addr = __builtin_amdgcn_perm(w[t >> 2], slot0[(t & 15) >> 2],
+                                       0x0c0c0000u | ((4u + (t & 3)) << 8) | (uint32_t)(t & 3)) +
+                 (P < 8 ? (uint32_t)(t >> 4) * (256u << P) : 0u);
+        else
+          addr = __builtin_amdgcn_perm(w[t >> 2], slot1[(t & 15) >> 1],
+                                       0x0c020000u | ((4u + (t & 3)) << 8) | (uint32_t)(t & 1));
         // the table is the block's dynamic LDS, which starts at LDS address 0
         // (the kernel has no static LDS; the host checks it before launching
         // this scorer): addr is the slot's absolute LDS address
@@ -1042,7 +1055,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_rot(ScoreArgs a) {
   if (!score_block_coords(a.bhkv, a.segs, bg, seg)) return;
   const WaveRange wr(a, seg);
   if constexpr (REGION) {
-    RegionScorer<LW> sc(a, bg, wr, tab);
+    // the region layouts: P = 8 with 16 or 32 tables, P = 6 with 64
+    RegionScorer<LW, LW == 16 ? 6 : 8> sc(a, bg, wr, tab);
     score_block<G, BUILD, true>(a, bg, seg, tab, sc, wr);
   } else {
     RotScorer<G, LW> sc(a, bg, wr, tab);
@@ -1078,6 +1092,7 @@ void set_lds_attributes() {
   if constexpr (G == 4) {
     const void* rf[] = {reinterpret_cast<const void*>(&score_kernel_rot<4, 4, false, true>),
                         reinterpret_cast<const void*>(&score_kernel_rot<4, 8, false, true>),
+                        reinterpret_cast<const void*>(&score_kernel_rot<4, 16, false, true>),
                         reinterpret_cast<const void*>(&score_kernel_rot<4, 4, true, true>),
                         reinterpret_cast<const void*>(&score_kernel_rot<4, 8, true, true>)};
     for (const void* f : rf)
@@ -1093,9 +1108,12 @@ void launch_score_rot(const ScoreArgs& a, int grid, size_t lds, hipStream_t stre
       if (a.L == 32)
         launch_kernel((score_kernel_rot<4, 8, BUILD, true>), dim3(grid), dim3(kScoreThreads), lds,
                       stream, a);
-      else
+      else if (a.L == 16)
         launch_kernel((score_kernel_rot<4, 4, BUILD, true>), dim3(grid), dim3(kScoreThreads), lds,
                       stream, a);
+      else if constexpr (!BUILD)  // L = 64 (P = 6: the table is never built in the block)
+        launch_kernel((score_kernel_rot<4, 16, false, true>), dim3(grid), dim3(kScoreThreads),
+                      lds, stream, a);
       return;
     }
   }
@@ -1189,6 +1207,7 @@ bool region_kernels_have_no_static_lds() {
   static const bool ok = [] {
     const void* fns[] = {reinterpret_cast<const void*>(&score_kernel_rot<4, 4, false, true>),
                          reinterpret_cast<const void*>(&score_kernel_rot<4, 8, false, true>),
+                         reinterpret_cast<const void*>(&score_kernel_rot<4, 16, false, true>),
                          reinterpret_cast<const void*>(&score_kernel_rot<4, 4, true, true>),
                          reinterpret_cast<const void*>(&score_kernel_rot<4, 8, true, true>)};
     for (const void* f : fns) {
@@ -1202,7 +1221,8 @@ bool region_kernels_have_no_static_lds() {
 }  // namespace
 
 bool score_region(int G, int P, int L) {
-  return G == 4 && P == 8 && (L == 16 || L == 32) && region_kernels_have_no_static_lds();
+  return G == 4 && ((P == 8 && (L == 16 || L == 32)) || (P == 6 && L == 64)) &&
+         region_kernels_have_no_static_lds();
 }
 
 bool score_rotated(const uint8_t* ids, int64_t stride, int L) {
