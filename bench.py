@@ -59,6 +59,8 @@ def parse():
                     help="leave out the soft-versus-hard LSH ranking comparison")
     ap.add_argument("--skip-other-configs", action="store_true",
                     help="leave out the 32K (eager and graphed) and 1M-key decode legs")
+    ap.add_argument("--skip-copy-reference", action="store_true",
+                    help="skip timing a plain 1 GiB device copy")
     ap.add_argument("--skip-fallback", action="store_true",
                     help="leave out the timing of the selection's full-row fallback")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -705,6 +707,33 @@ def main():
     if not args.skip_prefill_hash:
         prefill = prefill_hash(S, W, torch, dev)
 
+    # ---- a plain device-to-device copy of 1 GiB on the same GPU, for scale:
+    # the HBM rate a streaming copy reaches here (bytes read + written per
+    # second), beside the 8 TB/s published peak every fraction is taken of
+    copy_ref = None
+    if not args.skip_copy_reference:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        reps = 10
+        ev0.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        ev1.record()
+        torch.cuda.synchronize()
+        cms = ev0.elapsed_time(ev1) / reps
+        cbytes = 2 * src.numel() * 4
+        copy_ref = {
+            "bytes_per_copy": cbytes,
+            "ms": round(cms, 4),
+            "gbs": round(cbytes / (cms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(cbytes / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        }
+        del src, dst
+        torch.cuda.empty_cache()
+
 
     rec = {
         "metric": METRIC,
@@ -733,6 +762,7 @@ def main():
         "ranking_study": study,
         "group_shared_variant": group,
         "prefill_hash": prefill,
+        "hbm_copy_reference": copy_ref,
         "select_fallback": fallback,
         "other_configs": others,
         "cpu_baseline": cpu,
