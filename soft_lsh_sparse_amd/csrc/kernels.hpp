@@ -63,11 +63,12 @@ hipError_t launch_bucket_probs(const void* Q, const void* R, bool bf16, int B,
 // Launch geometry of the score kernel: segs blocks per (batch, KV head) of
 // seg_len keys each; every block's 16 waves own consecutive keys, sub_len
 // of them on average (subs = segs * 16 sub-lists per row when emitting
-// candidates). The shares are unequal: each SIMD serves its oldest wave
+// candidates). The shares can be unequal: each SIMD serves its oldest wave
 // first, so with equal shares waves 0-3 finish first and waves 12-15 last,
 // each group of four a few percent of the block's time after the one
-// before. Waves 4g..4g+3 therefore take sub_len + {skew0, skew1, -skew1,
-// -skew0}[g] keys (multiples of 128), which evens out their finish times.
+// before. Waves 4g..4g+3 take sub_len + {skew0, skew1, -skew1, -skew0}[g]
+// keys (multiples of 128; the plan sets a skew where it evens out the
+// finish times: 64 tables).
 struct ScoreGeom {
   int segs;
   int64_t seg_len;
