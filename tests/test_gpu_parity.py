@@ -973,7 +973,7 @@ def test_decode_unequal_wave_shares(N, k):
     """64 tables, one KV head of about 2M keys: 256 score blocks of 8192
     keys, whose 16 waves take unequal shares of 640, 512, 512 and 384 keys
     (waves 0-3, 4-7, 8-11, 12-15). With N = 2092000 the last block holds
-    3000 keys, cut inside wave 4's share. Every score is written once (the
+    3040 keys, cut inside wave 4's share. Every score is written once (the
     score rows equal socket_score's) and the selection, from short
     sub-lists (k = 500) or gathered candidates (k = 16384), equals the
     oracle's top-k of the GPU's own scores."""
@@ -995,6 +995,39 @@ def test_decode_unequal_wave_shares(N, k):
     s_np, idx_np = sc_ref.cpu().numpy(), idx.cpu().numpy()
     for h in range(4):
         assert np.array_equal(idx_np[0, h], O.topk_indices(s_np[0, h], w.k)), f"head {h}"
+
+
+def test_decode_group_shared_unequal_wave_shares():
+    """The group-shared decode with 64 tables of 6 bits over 2092000 keys of
+    one KV head: its score kernel (one summed row per KV head) takes the
+    same unequal wave shares, the last block cut inside wave 4's share. The
+    summed scores match the oracle's, the selection is the oracle's top-k of
+    the GPU's own scores (equal with and without score rows) and every head
+    attends over it."""
+    w = W.custom_workload(B=1, Hq=4, Hkv=1, d=128, N=2092000, dtype="bf16", L=64, P=6,
+                          tau=0.2, k=4096, lognormal_v=True, name="group_unequal_shares")
+    log("group-shared decode, unequal wave shares")
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=18)
+    ids, vn = S.hash_keys(K, V, R, w.L, w.P)
+    kk = w.kk
+    idx = torch.empty((1, 1, kk), dtype=torch.int32, device=DEV)
+    sc = torch.empty((1, 1, w.N), dtype=torch.float32, device=DEV)
+    out, _, _ = S.decode_group_shared(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, idx_out=idx,
+                                      scores_out=sc)
+    idx2 = torch.empty_like(idx)
+    S.decode_group_shared(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, idx_out=idx2)
+    torch.cuda.synchronize()
+    p = O.soft_bucket_probs(f64(Q), f64(R), w.L, w.P, tau32(w.tau))
+    ref_sc = O.group_scores(p, ids.cpu().numpy(), f64(vn), 4)
+    sc_np, idx_np = sc.cpu().numpy(), idx.cpu().numpy()
+    assert_close_rel(sc_np, ref_sc, 1e-5, 1e-30, "group scores")
+    assert np.array_equal(idx_np[0, 0], O.topk_indices(sc_np[0, 0], kk))
+    assert torch.equal(idx, idx2)
+    sel = idx[0, 0].long()
+    Kg = f64(K[0, 0][sel])[None, None]
+    Vg = f64(V[0, 0][sel])[None, None]
+    ref = O.subset_attention(f64(Q), Kg, Vg, np.tile(np.arange(kk), (1, 4, 1)), 4)
+    assert np.max(np.abs(f64(out) - ref)) <= 2e-2
 
 
 @pytest.mark.parametrize("N", [6145, 8191])
