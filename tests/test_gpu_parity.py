@@ -536,23 +536,24 @@ def test_decode_small_gqa_full():
     _check_decode(w)
 
 
-@pytest.mark.parametrize("Hq,Hkv,L,P", [
-    (8, 2, 16, 8),   # 16-table region layout, table built in the block
-    (8, 2, 16, 6),   # rotated 16 tables, two blocks per CU
-    (8, 2, 32, 6),   # rotated 32 tables, table from the table kernel
-    (8, 2, 64, 6),   # 64-table region layout (6 bits)
-    (4, 2, 32, 8),   # two query heads per block, table built in the block
-    (4, 4, 32, 8),   # one query head per block
+@pytest.mark.parametrize("Hq,Hkv,L,P,d", [
+    (8, 2, 16, 8, 128),   # 16-table region layout, table built in the block
+    (8, 2, 16, 6, 128),   # rotated 16 tables, two blocks per CU
+    (8, 2, 32, 6, 128),   # rotated 32 tables, table from the table kernel
+    (8, 2, 64, 6, 128),   # 64-table region layout (6 bits)
+    (4, 2, 32, 8, 128),   # two query heads per block, table built in the block
+    (4, 4, 32, 8, 128),   # one query head per block
+    (8, 2, 32, 8, 64),    # head dimension 64: the build's four-part projections
 ])
-def test_decode_scorer_layouts(Hq, Hkv, L, P):
+def test_decode_scorer_layouts(Hq, Hkv, L, P, d):
     """The decode through each score kernel layout (region or rotated
     order, table built in the block or copied from the table kernel, one,
-    two or four query heads per block): every row's scores, selection and
-    output against the oracle, over 20011 keys (several blocks, a ragged
-    last one)."""
-    w = W.custom_workload(B=2, Hq=Hq, Hkv=Hkv, d=128, N=20011, dtype="bf16", L=L, P=P,
+    two or four query heads per block, head dimension 128 or 64): every
+    row's scores, selection and output against the oracle, over 20011 keys
+    (several blocks, a ragged last one)."""
+    w = W.custom_workload(B=2, Hq=Hq, Hkv=Hkv, d=d, N=20011, dtype="bf16", L=L, P=P,
                           tau=0.3, k=700, outlier_channels=4, outlier_scale=8.0,
-                          lognormal_v=True, planted=16, name=f"layout_{Hq}_{Hkv}_{L}_{P}")
+                          lognormal_v=True, planted=16, name=f"layout_{Hq}_{Hkv}_{L}_{P}_{d}")
     log(f"decode {w.name}")
     _check_decode(w, seed=29)
 
