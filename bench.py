@@ -101,13 +101,16 @@ def kernel_bytes(w, names):
     table = w.B * w.Hkv * (2 ** w.P) * w.L * w.G * 4
     table_in = table if "bucket_probs_kernel" in names else rows * w.d * e + w.d * w.C * e
     partial = 0  # intermediates between two kernels are not counted
+    # the attention writes the output itself unless a merge kernel follows
+    out_bytes = 0 if "attn_merge_kernel" in names else rows * w.d * e
     return {
         "bucket_probs_kernel": rows * w.d * e + w.d * w.C * e + table,
         "score_kernel": keys * w.L + keys * 4 + table_in,
         "topk_gather_kernel": 0,  # moves candidates between two kernels only
         "topk_select_kernel": rows * kk * 4,
         "iota_rows_kernel": rows * kk * 4,
-        "sparse_attn_kernel": rows * kk * (2 * w.d * e + 4) + rows * w.d * e + partial,
+        "sparse_attn_kernel": rows * kk * (2 * w.d * e + 4) + rows * w.d * e + out_bytes
+        + partial,
         "attn_merge_kernel": rows * w.d * e,
     }
 

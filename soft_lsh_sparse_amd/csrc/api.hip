@@ -824,7 +824,8 @@ int32_t socket_decode_kernels(const uint8_t* ids, socket_dtype dtype, int32_t B,
     seq[n++] = "iota_rows_kernel";
   }
   seq[n++] = "sparse_attn_kernel";
-  seq[n++] = "attn_merge_kernel";
+  if (decode_layout(B, Hq, Hkv, d, n_keys, L, P, k).attn.chunks > 1)
+    seq[n++] = "attn_merge_kernel";
   if (names) {
     std::string joined;
     for (int i = 0; i < n; ++i) {

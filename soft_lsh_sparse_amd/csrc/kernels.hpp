@@ -208,11 +208,15 @@ int select_gather_blocks(int subs, int64_t kk);
 hipError_t launch_topk_select(const SelectArgs& a, int rows, hipStream_t stream);
 
 // ------------------------------------------------------- sparse attention
+// Chunk partials per row that one thread of the merge kernel combines from
+// registers (more chunks are staged in LDS).
+constexpr int kMergeRegChunks = 16;
 // Largest selection one attention row supports: 1024 chunks of 256 keys.
 constexpr int64_t kMaxSelected = 262144;
 struct AttnPlan {
   int B, Hq, Hkv, d;
   int64_t kk;
+  int waves;  // per block: 4, or 1 (64 keys per block) for short rows
   int keys_per_wave, chunk_keys, chunks;
   size_t partial_bytes;
 };

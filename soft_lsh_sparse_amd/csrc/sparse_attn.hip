@@ -30,8 +30,10 @@
 namespace socket_lsh {
 namespace {
 
-constexpr int kAttnThreads = 256;
-constexpr int kAttnWaves = kAttnThreads / 64;
+// Waves per block: 4, or 1 where 4-wave blocks would not give 512 blocks
+// (a CU pulls gathered rows at a limited rate, so short rows are spread
+// over more CUs).
+constexpr int kAttnWaves = 4;
 constexpr int kAttnLoads = 8;  // 16-byte loads per lane, tensor and batch
 
 template <typename T>
@@ -45,13 +47,17 @@ __device__ __forceinline__ void unpack16<F32>(const uint4& w, float* f) {
   unpack4_f32(w, f);
 }
 
-template <typename T, int D, int KPW>
-__global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
+// WAVES waves per block. DIRECT (one chunk per row): the block's merge is
+// the row's, and the output is written in the input dtype (the merge
+// kernel's arithmetic over a single chunk: at / lt).
+template <typename T, int D, int KPW, int WAVES, bool DIRECT>
+__global__ __launch_bounds__(WAVES * 64) void sparse_attn_kernel(
     const typename T::storage* __restrict__ Q,
     const typename T::storage* __restrict__ K,
     const typename T::storage* __restrict__ V, int Hq, int Hkv, int bhkv,
     int64_t stride, const int32_t* __restrict__ idx, int64_t kk, int chunks,
-    float* __restrict__ partial) {
+    float* __restrict__ partial, typename T::storage* __restrict__ final_out) {
+  constexpr int kAttnThreads = WAVES * 64;
   constexpr int EPL = 16 / T::bytes;  // elements per 16-byte load
   constexpr int LPR = D / EPL;        // lanes per key row
   constexpr int KPI = 64 / LPR;       // key rows per wave-wide load
@@ -60,9 +66,9 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
   constexpr int NB = KPW / KPB;       // batches per wave
   static_assert(NB * KPB == KPW && KPW % 64 == 0, "keys per wave");
   constexpr int NREG = KPW / 64;
-  constexpr int CHUNK = KPW * kAttnWaves;
-  __shared__ float sm_m[kAttnWaves], sm_l[kAttnWaves];
-  __shared__ float sm_acc[kAttnWaves][D];
+  constexpr int CHUNK = KPW * WAVES;
+  __shared__ float sm_m[WAVES], sm_l[WAVES];
+  __shared__ float sm_acc[WAVES][D];
 
   const int G = Hq / Hkv;
   const int per_group = G * chunks;
@@ -194,13 +200,17 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
   for (int t = threadIdx.x; t < D; t += kAttnThreads) {
     float mt = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) mt = fmaxf(mt, sm_m[w]);
+    for (int w = 0; w < WAVES; ++w) mt = fmaxf(mt, sm_m[w]);
     float lt = 0.f, at = 0.f;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) {
+    for (int w = 0; w < WAVES; ++w) {
       const float c = sm_m[w] == -INFINITY ? 0.f : expf(sm_m[w] - mt);
       lt = fmaf(c, sm_l[w], lt);
       at = fmaf(c, sm_acc[w][t], at);
+    }
+    if constexpr (DIRECT) {
+      T::store(final_out, row * D + t, at / lt);
+      continue;
     }
     out[t] = at;
     if (t == 0) {
@@ -211,7 +221,6 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
 }
 
 constexpr int kMergeMaxChunks = 1024;
-constexpr int kMergeRegChunks = 16;
 
 // Online-softmax merge of the chunk partials of one row, in chunk order.
 // Up to kMergeRegChunks chunks (the sparse decode's 4-16): every thread
@@ -277,7 +286,7 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(
   T::store(out, row * D + t, at / s_tot[0]);
 }
 
-template <typename T, int D, int KPW>
+template <typename T, int D, int KPW, int WAVES>
 hipError_t launch_attn_t(const void* Q, const void* K, const void* V,
                          const AttnPlan& plan, int64_t stride,
                          const int32_t* idx, void* out, float* partial,
@@ -287,10 +296,15 @@ hipError_t launch_attn_t(const void* Q, const void* K, const void* V,
   const int bhkv = plan.B * plan.Hkv;
   const int per_group = G * plan.chunks;
   const int grid = ((bhkv + 7) / 8) * 8 * per_group;
-  launch_kernel((sparse_attn_kernel<T, D, KPW>), dim3(grid),
-                     dim3(kAttnThreads), 0, stream, (const S*)Q, (const S*)K,
-                     (const S*)V, plan.Hq, plan.Hkv, bhkv, stride, idx,
-                     plan.kk, plan.chunks, partial);
+  if (plan.chunks == 1) {  // the block's merge is the row's: output written directly
+    launch_kernel((sparse_attn_kernel<T, D, KPW, WAVES, true>), dim3(grid), dim3(WAVES * 64),
+                  0, stream, (const S*)Q, (const S*)K, (const S*)V, plan.Hq, plan.Hkv, bhkv,
+                  stride, idx, plan.kk, 1, partial, (S*)out);
+    return hipGetLastError();
+  }
+  launch_kernel((sparse_attn_kernel<T, D, KPW, WAVES, false>), dim3(grid), dim3(WAVES * 64), 0,
+                stream, (const S*)Q, (const S*)K, (const S*)V, plan.Hq, plan.Hkv, bhkv, stride,
+                idx, plan.kk, plan.chunks, partial, nullptr);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   launch_kernel((attn_merge_kernel<T, D>), dim3(plan.B * plan.Hq),
@@ -303,13 +317,18 @@ hipError_t launch_attn_d(const void* Q, const void* K, const void* V,
                          const AttnPlan& plan, int64_t stride,
                          const int32_t* idx, void* out, float* partial,
                          hipStream_t stream) {
+  if (plan.waves == 1)  // 64 keys per block (plan_attn)
+    return launch_attn_t<T, D, 64, 1>(Q, K, V, plan, stride, idx, out, partial, stream);
   switch (plan.keys_per_wave) {
     case 256:
-      return launch_attn_t<T, D, 256>(Q, K, V, plan, stride, idx, out, partial, stream);
+      return launch_attn_t<T, D, 256, kAttnWaves>(Q, K, V, plan, stride, idx, out, partial,
+                                                  stream);
     case 128:
-      return launch_attn_t<T, D, 128>(Q, K, V, plan, stride, idx, out, partial, stream);
+      return launch_attn_t<T, D, 128, kAttnWaves>(Q, K, V, plan, stride, idx, out, partial,
+                                                  stream);
     default:
-      return launch_attn_t<T, D, 64>(Q, K, V, plan, stride, idx, out, partial, stream);
+      return launch_attn_t<T, D, 64, kAttnWaves>(Q, K, V, plan, stride, idx, out, partial,
+                                                 stream);
   }
 }
 
@@ -344,6 +363,7 @@ AttnPlan plan_attn(int B, int Hq, int Hkv, int d, int64_t kk) {
   p.d = d;
   p.kk = kk;
   const int64_t rows = (int64_t)B * Hq;
+  p.waves = kAttnWaves;
   // the most keys per wave that still give 512 blocks (two per CU)
   int kpw = 64;
   for (int cand : {256, 128}) {
@@ -353,9 +373,16 @@ AttnPlan plan_attn(int B, int Hq, int Hkv, int d, int64_t kk) {
       break;
     }
   }
+  int64_t chunks = (kk + kpw * kAttnWaves - 1) / (kpw * kAttnWaves);
+  const int64_t wave_chunks = (kk + 63) / 64;
+  if (rows * chunks < 512 && chunks > 1 && wave_chunks <= kMergeRegChunks) {
+    // one-wave blocks of 64 keys: up to 4x the blocks, merged from registers
+    p.waves = 1;
+    chunks = wave_chunks;
+  }
   p.keys_per_wave = kpw;
-  p.chunk_keys = kpw * kAttnWaves;
-  p.chunks = (int)((kk + p.chunk_keys - 1) / p.chunk_keys);
+  p.chunk_keys = kpw * p.waves;
+  p.chunks = (int)chunks;
   if (p.chunks < 1) p.chunks = 1;
   p.partial_bytes = (size_t)rows * p.chunks * (d + 2) * sizeof(float);
   return p;

@@ -221,6 +221,10 @@ def test_decode_kernel_sequence(lib):
     assert _kernels(lib, k=5461)[1] == ["score_kernel", "topk_select_kernel"] + tail
     assert _kernels(lib, k=131072) == (3, ["iota_rows_kernel"] + tail)
     assert _kernels(lib, k=131072, with_scores=1)[1] == ["score_kernel", "iota_rows_kernel"] + tail
+    # a row of one chunk (at most 256 keys with 4 waves): no merge kernel
+    assert _kernels(lib, B=1, Hq=1, Hkv=1, k=64)[1][-2:] == ["topk_select_kernel",
+                                                             "sparse_attn_kernel"]
+    assert _kernels(lib, B=1, Hq=1, Hkv=1, k=257)[1][-1] == "attn_merge_kernel"
     assert _kernels(lib, Hq=30)[0] == -1      # G not an integer
     assert _kernels(lib, cap=8)[0] == -2      # names do not fit
     assert lib.socket_decode_kernels(FAKE, _lib.DTYPE_BF16, 4, 32, 8, 128, 131072, 131072,

@@ -276,6 +276,15 @@ def test_topk_stage(rows, n, k, kind):
     (1, 4, 4, 64, 50, 50, "bf16"),
     (1, 2, 1, 128, 10, 1, "f32"),
     (2, 8, 1, 128, 700, 333, "f32"),
+    # the plan's routes: rows of one chunk write the output directly (the
+    # f32 and 50-key cases above); short rows in one-wave blocks of 64 keys
+    # (1000 and 333 keys above); 4-wave chunks merged from registers (8 and
+    # 10 chunks, ragged) or through LDS (more than 16 chunks)
+    (1, 4, 2, 64, 3000, 2048, "bf16"),
+    (1, 4, 1, 128, 8000, 2500, "bf16"),
+    (1, 4, 2, 64, 3000, 2049, "f32"),
+    (1, 2, 1, 128, 9000, 5000, "bf16"),
+    (1, 32, 8, 128, 40000, 6000, "bf16"),
 ])
 def test_sparse_attn_stage(B, Hq, Hkv, d, N, kk, dt):
     log(f"attn {(B, Hq, Hkv, d, N, kk, dt)}")
