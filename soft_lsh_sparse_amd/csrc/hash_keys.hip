@@ -631,7 +631,7 @@ __device__ __forceinline__ void hash_redo_block(
 // settle the listed signs, the next redo_blocks check the tiles for waves
 // whose list overflowed (disjoint rows: a tile belongs to one wave).
 template <int D>
-__global__ __launch_bounds__(256) void hash_settle_kernel(
+__global__ __launch_bounds__(256, 8) void hash_settle_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ R,
     const uint16_t* __restrict__ RT, int64_t n_keys, int64_t stride, int tph, int n_tiles,
     int parts, int L, int P, uint8_t* __restrict__ ids,
