@@ -31,6 +31,8 @@ if ROOT not in sys.path:
 
 METRIC = "decode tokens/s at 128K ctx (hash-score+top-k+sparse attn); % HBM peak"
 HBM_PEAK_GBS = 8000.0
+# LDS read peak of the chip: 128 bytes per clock per CU, 256 CUs, 2.4 GHz
+LDS_PEAK_GBS = 128 * 256 * 2.4
 
 
 def parse():
@@ -417,6 +419,21 @@ def decode_leg(lib, S, W, torch, w, dev, layers, queries, steps, warmup, stage_t
         "algorithmic_bytes_per_launch": kbytes[dom],
         "avg_launch_ms": round(kernel_ms[dom], 5),
     }
+    # the score kernel against its own bound, the LDS port: every key's L
+    # table lookups for the G query heads of its KV head (4 bytes each),
+    # over the kernel's mean duration, against 128 B/clk per CU
+    if "score_kernel" in kernel_ms:
+        lds_bytes = w.B * w.Hkv * w.N * w.L * w.G * 4
+        lds_gbs = lds_bytes / (kernel_ms["score_kernel"] * 1e-3) / 1e9
+        leg["score_lds_roofline"] = {
+            "bound": "lds",
+            "kernel": "score_kernel",
+            "achieved": round(lds_gbs, 1),
+            "peak": LDS_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(lds_gbs / LDS_PEAK_GBS, 4),
+            "lds_lookup_bytes_per_launch": lds_bytes,
+        }
     return leg
 
 
@@ -760,6 +777,7 @@ def main():
         "algorithmic_bytes_per_step": step_bytes,
         "kernel_ms": {k: round(v, 5) for k, v in kernel_ms.items()},
         "roofline": roofline,
+        "score_lds_roofline": leg.get("score_lds_roofline"),
         "dense_baseline": dense,
         "decode_loop": loop,
         "ranking_study": study,
