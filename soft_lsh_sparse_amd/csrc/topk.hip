@@ -35,6 +35,7 @@
 #include "radix.hpp"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace socket_lsh {
 namespace {
@@ -187,6 +188,8 @@ __device__ __forceinline__ void cache_candidates(RowLists& rl, uint2* cache, uin
 // below (entries read from memory then overlap instead of each waiting for
 // the one before it).
 constexpr int kPassBatch = 8;
+// memory entries per lane and batch when a pass collects the keys in play
+constexpr int kCollectMemKeys = 16;
 
 // Wave w's share [c0, c1) of positions 0 .. total: contiguous runs of a
 // multiple of 64 positions, in wave order (lane i reads positions c0 + i,
@@ -409,17 +412,28 @@ __device__ __forceinline__ bool select_range_and_emit(At at, uint32_t total, uin
   const int nbits = top;
   uint32_t prefix = 0, need = kk;  // x >> top == prefix for the keys still in play
   bool whole = false, first = true;
+  // Rows gathered into a run partly in memory: after the first pass the
+  // keys still in play (those of the bin holding the kk-th key, counted
+  // exactly by that pass) are collected into the sub-list offsets' LDS,
+  // which such rows no longer read, so the later passes read no memory.
+  const uint32_t* ck = nullptr;  // block-uniform
+  uint32_t nck = 0;
   do {  // block-uniform; at least one pass, which counts the entries reaching lo
     const int db = min(11, top), shift = top - db;
     const uint32_t dmask = (1u << db) - 1u;
     for (int i = threadIdx.x; i < kHistBins; i += NT) sh.h[i] = 0;
     __syncthreads();
-    for_all_keys<NT>(at, total, [&](uint32_t u, bool valid) {
+    auto count = [&](uint32_t u, bool valid) {
       if (!valid || u < lo) return;
       const uint32_t x = u - lo;
       if (top < nbits && (x >> top) != prefix) return;
       atomicAdd(&sh.h[(x >> shift) & dmask], 1u);
-    });
+    };
+    if (ck != nullptr) {
+      for (uint32_t p = threadIdx.x; p < nck; p += NT) count(ck[p], true);
+    } else {
+      for_all_keys<NT>(at, total, count);
+    }
     __syncthreads();
     find_threshold_bin<NT>(sh.h, need, sh.scratch, res);
     if (first && res[2] < kk) return false;
@@ -432,6 +446,35 @@ __device__ __forceinline__ bool select_range_and_emit(At at, uint32_t total, uin
     if (in_bin == need) {
       whole = true;
       break;
+    }
+    if constexpr (std::is_same<At, SpillAt>::value) {
+      if (ck == nullptr && top > 0 && total > at.split() && in_bin <= kMaxSelectSubLists + 1) {
+        uint32_t* keys = sh.off;
+        uint32_t* n_in = sh.scratch + 2 * (NT / 64 + 1);
+        if (threadIdx.x == 0) *n_in = 0u;
+        __syncthreads();
+        const uint32_t lane = threadIdx.x & 63;
+        auto put = [&](uint32_t u, bool valid) {
+          const bool keep = valid && u >= lo && ((u - lo) >> top) == prefix;
+          const uint64_t b = __ballot(keep);
+          if (b != 0) {  // wave-uniform
+            uint32_t base = 0u;
+            if (lane == 0) base = atomicAdd(n_in, (uint32_t)__popcll(b));
+            base = (uint32_t)__shfl((int)base, 0, 64);
+            if (keep) keys[base + lane_prefix(b)] = u;
+          }
+        };
+        // each wave's share of the LDS part and of the memory part, as in
+        // the passes (fewer memory loads per batch: the slot bookkeeping
+        // needs registers too)
+        const uint32_t mid = min(at.split(), total);
+        const WaveRun r0(mid, NT), r1(total - mid, NT);
+        for_keys<kPassBatch>(at, r0.c0, r0.c1, put);
+        for_keys<kCollectMemKeys>(at, mid + r1.c0, mid + r1.c1, put);
+        __syncthreads();  // the keys have landed
+        ck = keys;
+        nck = in_bin;
+      }
     }
   } while (top > 0);
   // whole: every key from the bin's lowest up; else top == 0 and prefix is
