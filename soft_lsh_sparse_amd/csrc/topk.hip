@@ -371,7 +371,8 @@ __device__ __forceinline__ SpillRow spill_row(int64_t n, int row) {
 // indices at positions given by block scans: o[0 .. kk) ascending.
 template <int NT, typename At>
 __device__ __forceinline__ void emit_in_order(At at, uint32_t total, uint32_t kk, uint32_t T,
-                                              uint32_t ties, RefineShared& sh, int32_t* o);
+                                              uint32_t ties, RefineShared& sh, int32_t* o,
+                                              bool counted = false);
 
 template <int NT, typename At>
 __device__ __forceinline__ void select_and_emit(At at, uint32_t total, uint32_t kk, int start_pass,
@@ -416,8 +417,14 @@ __device__ __forceinline__ bool select_range_and_emit(At at, uint32_t total, uin
   // keys still in play (those of the bin holding the kk-th key, counted
   // exactly by that pass) are collected into the sub-list offsets' LDS,
   // which such rows no longer read, so the later passes read no memory.
+  // Each collected key is stored as its x below bit ct (the bits above are
+  // cp, the same for all of them) tagged with its wave's chunk (bits 21..:
+  // 2 * wave + 0 for the LDS part, + 1 for the memory part), and each wave
+  // counts the keys of its chunks above the bin, so that the emit needs no
+  // counting pass of its own.
   const uint32_t* ck = nullptr;  // block-uniform
-  uint32_t nck = 0;
+  uint32_t nck = 0, cp = 0;
+  int ct = 0;
   do {  // block-uniform; at least one pass, which counts the entries reaching lo
     const int db = min(11, top), shift = top - db;
     const uint32_t dmask = (1u << db) - 1u;
@@ -430,7 +437,8 @@ __device__ __forceinline__ bool select_range_and_emit(At at, uint32_t total, uin
       atomicAdd(&sh.h[(x >> shift) & dmask], 1u);
     };
     if (ck != nullptr) {
-      for (uint32_t p = threadIdx.x; p < nck; p += NT) count(ck[p], true);
+      for (uint32_t p = threadIdx.x; p < nck; p += NT)
+        count(lo + ((cp << ct) | (ck[p] & ((1u << ct) - 1u))), true);
     } else {
       for_all_keys<NT>(at, total, count);
     }
@@ -453,33 +461,64 @@ __device__ __forceinline__ bool select_range_and_emit(At at, uint32_t total, uin
         uint32_t* n_in = sh.scratch + 2 * (NT / 64 + 1);
         if (threadIdx.x == 0) *n_in = 0u;
         __syncthreads();
-        const uint32_t lane = threadIdx.x & 63;
+        const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const uint32_t low = (1u << top) - 1u;  // top <= 21 after the first pass
+        uint32_t tag = 2u * wave, above = 0u;    // wave-uniform
         auto put = [&](uint32_t u, bool valid) {
-          const bool keep = valid && u >= lo && ((u - lo) >> top) == prefix;
+          const uint32_t x = u - lo;
+          const bool in = valid && u >= lo;
+          const bool keep = in && (x >> top) == prefix;
+          above += (uint32_t)__popcll(__ballot(in && (x >> top) > prefix));
           const uint64_t b = __ballot(keep);
           if (b != 0) {  // wave-uniform
             uint32_t base = 0u;
             if (lane == 0) base = atomicAdd(n_in, (uint32_t)__popcll(b));
             base = (uint32_t)__shfl((int)base, 0, 64);
-            if (keep) keys[base + lane_prefix(b)] = u;
+            if (keep) keys[base + lane_prefix(b)] = (tag << 21) | (x & low);
           }
         };
-        // each wave's share of the LDS part and of the memory part, as in
-        // the passes (fewer memory loads per batch: the slot bookkeeping
-        // needs registers too)
+        // each wave's chunk of the LDS part and of the memory part, as the
+        // emit takes them (fewer memory loads per batch than the passes:
+        // the slot bookkeeping needs registers too)
         const uint32_t mid = min(at.split(), total);
         const WaveRun r0(mid, NT), r1(total - mid, NT);
         for_keys<kPassBatch>(at, r0.c0, r0.c1, put);
+        if (lane == 0) sh.tmax[wave] = above;
+        tag += 1u;
+        above = 0u;
         for_keys<kCollectMemKeys>(at, mid + r1.c0, mid + r1.c1, put);
-        __syncthreads();  // the keys have landed
+        if (lane == 0) sh.cmax[wave] = above;
+        __syncthreads();  // the keys and counts have landed
         ck = keys;
         nck = in_bin;
+        cp = prefix;
+        ct = top;
       }
     }
   } while (top > 0);
   // whole: every key from the bin's lowest up; else top == 0 and prefix is
   // the kk-th key's x
-  emit_in_order<NT>(at, total, kk, lo + (prefix << top), whole ? 0xffffffffu : need, sh, o);
+  const uint32_t T = lo + (prefix << top), ties = whole ? 0xffffffffu : need;
+  if (ck != nullptr) {
+    // the emit's counts: each wave's keys above the collected bin, plus the
+    // collected keys above and equal to T by the chunk they came from
+    uint32_t* wc = sh.h;
+    for (int i = threadIdx.x; i < 4 * (NT / 64); i += NT) wc[i] = 0u;
+    __syncthreads();
+    for (uint32_t p = threadIdx.x; p < nck; p += NT) {
+      const uint32_t e = ck[p], u = lo + ((cp << ct) | (e & ((1u << ct) - 1u)));
+      const uint32_t w = (e >> 21) >> 1, part = (e >> 21) & 1u;
+      if (u > T) atomicAdd(&wc[4 * w + 2 * part], 1u);
+      else if (u == T) atomicAdd(&wc[4 * w + 2 * part + 1], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < NT / 64) {
+      wc[4 * threadIdx.x] += sh.tmax[threadIdx.x];
+      wc[4 * threadIdx.x + 2] += sh.cmax[threadIdx.x];
+    }
+    __syncthreads();
+  }
+  emit_in_order<NT>(at, total, kk, T, ties, sh, o, ck != nullptr);
   return true;
 }
 
@@ -519,34 +558,39 @@ __device__ __forceinline__ void emit_run(At at, uint32_t c0, uint32_t c1, uint32
 // chunks before each of its own (all of the LDS part's chunks come before
 // the memory part's), it knows how many keys precede the chunk in the
 // output and how many of the ties are taken before it, and writes the
-// indices it keeps at consecutive positions.
+// indices it keeps at consecutive positions. counted: the counts are
+// already in sh.h ([wave][gt in LDS part, eq, gt in memory part, eq]) and
+// visible to the block.
 template <int NT, typename At>
 __device__ __forceinline__ void emit_in_order(At at, uint32_t total, uint32_t kk, uint32_t T,
-                                              uint32_t ties, RefineShared& sh, int32_t* o) {
+                                              uint32_t ties, RefineShared& sh, int32_t* o,
+                                              bool counted) {
   constexpr int NW = NT / 64;
   const int wave = threadIdx.x >> 6;
   const uint32_t mid = min(at.split(), total);
   const WaveRun r0(mid, NT), r1(total - mid, NT);
   const uint32_t b0 = mid + r1.c0, b1 = mid + r1.c1;
-  uint32_t n_gt0 = 0, n_eq0 = 0, n_gt1 = 0, n_eq1 = 0;  // wave-uniform
-  auto count0 = [&](uint32_t u, bool valid) {
-    n_gt0 += (uint32_t)__popcll(__ballot(valid && u > T));
-    n_eq0 += (uint32_t)__popcll(__ballot(valid && u == T));
-  };
-  auto count1 = [&](uint32_t u, bool valid) {
-    n_gt1 += (uint32_t)__popcll(__ballot(valid && u > T));
-    n_eq1 += (uint32_t)__popcll(__ballot(valid && u == T));
-  };
-  for_keys<kPassBatch>(at, r0.c0, r0.c1, count0);
-  for_keys<At::kMemKeys>(at, b0, b1, count1);
   uint32_t* wc = sh.h;  // [NW][4]; the histogram is no longer read
-  if ((threadIdx.x & 63) == 0) {
-    wc[4 * wave] = n_gt0;
-    wc[4 * wave + 1] = n_eq0;
-    wc[4 * wave + 2] = n_gt1;
-    wc[4 * wave + 3] = n_eq1;
+  if (!counted) {  // block-uniform
+    uint32_t n_gt0 = 0, n_eq0 = 0, n_gt1 = 0, n_eq1 = 0;  // wave-uniform
+    auto count0 = [&](uint32_t u, bool valid) {
+      n_gt0 += (uint32_t)__popcll(__ballot(valid && u > T));
+      n_eq0 += (uint32_t)__popcll(__ballot(valid && u == T));
+    };
+    auto count1 = [&](uint32_t u, bool valid) {
+      n_gt1 += (uint32_t)__popcll(__ballot(valid && u > T));
+      n_eq1 += (uint32_t)__popcll(__ballot(valid && u == T));
+    };
+    for_keys<kPassBatch>(at, r0.c0, r0.c1, count0);
+    for_keys<At::kMemKeys>(at, b0, b1, count1);
+    if ((threadIdx.x & 63) == 0) {
+      wc[4 * wave] = n_gt0;
+      wc[4 * wave + 1] = n_eq0;
+      wc[4 * wave + 2] = n_gt1;
+      wc[4 * wave + 3] = n_eq1;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   uint32_t gt0 = 0, eq0 = 0, gt0_all = 0, eq0_all = 0, gt1 = 0, eq1 = 0;
   for (int w = 0; w < NW; ++w) {
     if (w < wave) {
