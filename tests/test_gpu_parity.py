@@ -941,6 +941,35 @@ def test_decode_gathered_ties(N, top):
         assert torch.equal(idx.cpu(), want), f"with_rows={with_rows}"
 
 
+def test_decode_gathered_ties_in_the_threshold_bin():
+    """64 value-norm levels of 625 keys each, spread over the index range by
+    a permutation (i * 7919 mod N), all keys in the same buckets: scores tie
+    exactly within a level. k = 20300 takes the 32 top levels whole and 300
+    of the next level's 625 tied keys, the lowest indices first. The
+    candidates (more than the 16K the select copies into LDS) are gathered,
+    and the threshold bin's 625 keys are collected into LDS after the first
+    radix pass, each tagged with the chunk it came from."""
+    N, levels, per, k = 40000, 64, 625, 20300
+    w = W.custom_workload(B=1, Hq=4, Hkv=1, d=128, N=N, dtype="bf16", L=32, P=8,
+                          tau=0.3, k=k, lognormal_v=False, name="tied_levels")
+    log(f"decode gathered ties in the threshold bin N={N} k={k}")
+    Q, K, V, R = W.make_decode_inputs(w, DEV, seed=14)
+    level = (np.arange(N, dtype=np.int64) * 7919 % N) // per
+    ids = torch.full((1, 1, N, w.L), 5, dtype=torch.uint8, device=DEV)
+    vn = torch.from_numpy((1.0 + level / levels).astype(np.float32)).view(1, 1, N).to(DEV)
+    top = np.nonzero(level >= levels // 2)[0]
+    tied = np.nonzero(level == levels // 2 - 1)[0][:k - len(top)]
+    want = np.sort(np.concatenate([top, tied])).astype(np.int32)
+    assert len(want) == k
+    for with_rows in (False, True):
+        idx = torch.empty((1, 4, k), dtype=torch.int32, device=DEV)
+        sc = torch.empty((1, 4, N), dtype=torch.float32, device=DEV) if with_rows else None
+        S.decode(Q, K, V, R, ids, vn, w.L, w.P, w.tau, w.k, idx_out=idx, scores_out=sc)
+        torch.cuda.synchronize()
+        for h in range(4):
+            assert np.array_equal(idx[0, h].cpu().numpy(), want), f"with_rows={with_rows} h={h}"
+
+
 @pytest.mark.parametrize("with_rows", [False, True])
 def test_decode_clustered_candidates(with_rows):
     """The first 4096 keys sit, in every table, in query head 0's most likely
